@@ -1,0 +1,191 @@
+"""Decoder-block operations in float64: forward and hand-written backward.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+Pages cited in this file:
+  [Review]  "MegaTrain: Full Precision Training of 100B+ Parameter Large
+            Language Models on a Single GPU Review", dimensionstp.github.io
+  [Lilting] "MegaTrainはシングルGPUで120BパラメータLLMをフル精度訓練する",
+            lilting.ch
+
+The pages train dense Qwen2.5 decoders ([Review] section 4-2, model list;
+[Lilting] section "ベンチマーク結果") but never spell the block out.  The
+reading taken is the standard pre-norm decoder those models use: RMSNorm ->
+causal grouped-query attention with rotary positions -> residual -> RMSNorm
+-> SwiGLU MLP -> residual, with no biases.  Conventions the pages leave open,
+and the reading taken for each:
+  * RMSNorm: eps inside the square root, statistics over the model dim.
+  * RoPE: "rotate-half" pairs (e, e + hd/2), angle s * base^(-2e/hd), with
+    s the position inside its own sequence.
+  * GQA: query head h reads key/value head h // (Hq / Hkv).
+  * attention: scale 1/sqrt(hd), causal mask s' <= s, no dropout.
+  * SwiGLU: silu(gate) * up, silu(z) = z / (1 + exp(-z)).
+  * loss: mean token cross-entropy over all B*S positions.
+
+Every function takes and returns float64 numpy arrays.  Token row t = b*S+s.
+"""
+import numpy as np
+
+
+# --------------------------------------------------------------------------
+# RMSNorm
+# --------------------------------------------------------------------------
+def rmsnorm_fwd(x, gamma, eps):
+    """n = gamma * x / sqrt(mean(x^2) + eps) per row.  Returns (n, rstd)."""
+    rstd = 1.0 / np.sqrt(np.mean(x * x, axis=-1) + eps)
+    n = x * rstd[..., None] * gamma
+    return n, rstd
+
+
+def rmsnorm_bwd(dn, x, gamma, rstd):
+    """Backward of ``rmsnorm_fwd``.  Returns (dx, dgamma).
+
+    With nh = x * rstd:  dx = rstd * (g - nh * mean(g * nh)),  g = dn * gamma;
+    dgamma = sum over rows of dn * nh.
+    """
+    nh = x * rstd[..., None]
+    g = dn * gamma
+    dx = rstd[..., None] * (g - nh * np.mean(g * nh, axis=-1, keepdims=True))
+    dgamma = np.sum((dn * nh).reshape(-1, x.shape[-1]), axis=0)
+    return dx, dgamma
+
+
+# --------------------------------------------------------------------------
+# Linear map y = x W^T with W stored [out x in]
+# --------------------------------------------------------------------------
+def linear_fwd(x, w):
+    return x @ w.T
+
+
+def linear_bwd(dy, x, w):
+    """Returns (dx, dw) for y = x W^T."""
+    return dy @ w, dy.T @ x
+
+
+# --------------------------------------------------------------------------
+# Rotary position embedding, rotate-half convention
+# --------------------------------------------------------------------------
+def rope_angles(seq, head_dim, base):
+    """theta[s, e] = s * base^(-2e/hd) for s < seq, e < hd/2."""
+    e = np.arange(head_dim // 2, dtype=np.float64)
+    inv_freq = base ** (-2.0 * e / head_dim)
+    s = np.arange(seq, dtype=np.float64)
+    return s[:, None] * inv_freq[None, :]
+
+
+def rope_rotate(z, theta):
+    """Rotate pairs (e, e+hd/2) of z [B, S, H, hd] by angle theta [S, hd/2]."""
+    half = z.shape[-1] // 2
+    c = np.cos(theta)[None, :, None, :]
+    s = np.sin(theta)[None, :, None, :]
+    lo, hi = z[..., :half], z[..., half:]
+    return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
+
+
+def rope_fwd(z, base):
+    """RoPE forward on z [B, S, H, hd]; position = index along S."""
+    return rope_rotate(z, rope_angles(z.shape[1], z.shape[-1], base))
+
+
+def rope_bwd(dz, base):
+    """RoPE backward: the transpose of a rotation is the rotation by -theta."""
+    return rope_rotate(dz, -rope_angles(dz.shape[1], dz.shape[-1], base))
+
+
+# --------------------------------------------------------------------------
+# Causal grouped-query attention, brute force S x S per head
+# --------------------------------------------------------------------------
+def _causal_mask(seq):
+    return np.tril(np.ones((seq, seq), dtype=bool))
+
+
+def attention_probs(q, k):
+    """P[b, h, s, s'] = softmax_{s'<=s}(q[b,s,h] . k[b,s',h//G] / sqrt(hd))."""
+    bsz, seq, hq, hd = q.shape
+    group = hq // k.shape[2]
+    kx = np.repeat(k, group, axis=2)                     # [B, S, Hq, hd]
+    scores = np.einsum("bshd,bthd->bhst", q, kx) / np.sqrt(hd)
+    scores = np.where(_causal_mask(seq)[None, None], scores, -np.inf)
+    scores = scores - scores.max(axis=-1, keepdims=True)
+    p = np.exp(scores)
+    return p / p.sum(axis=-1, keepdims=True)
+
+
+def attention_fwd(q, k, v):
+    """o [B, S, Hq, hd] for q [B,S,Hq,hd], k and v [B,S,Hkv,hd]."""
+    group = q.shape[2] // k.shape[2]
+    p = attention_probs(q, k)
+    vx = np.repeat(v, group, axis=2)
+    return np.einsum("bhst,bthd->bshd", p, vx)
+
+
+def attention_bwd(do, q, k, v):
+    """Returns (dq, dk, dv).
+
+    dP = dO V^T, D = rowsum(dO * O) = rowsum(P * dP), dS = P (dP - D),
+    dQ = dS K / sqrt(hd), dK = dS^T Q / sqrt(hd), dV = P^T dO; the key and
+    value gradients of a KV head are summed over the query heads of its group.
+    """
+    bsz, seq, hq, hd = q.shape
+    hkv = k.shape[2]
+    group = hq // hkv
+    p = attention_probs(q, k)
+    kx = np.repeat(k, group, axis=2)
+    vx = np.repeat(v, group, axis=2)
+    dp = np.einsum("bshd,bthd->bhst", do, vx)
+    dsum = np.sum(p * dp, axis=-1, keepdims=True)
+    ds = p * (dp - dsum)
+    scale = 1.0 / np.sqrt(hd)
+    dq = np.einsum("bhst,bthd->bshd", ds, kx) * scale
+    dkx = np.einsum("bhst,bshd->bthd", ds, q) * scale
+    dvx = np.einsum("bhst,bshd->bthd", p, do)
+    dk = dkx.reshape(bsz, seq, hkv, group, hd).sum(axis=3)
+    dv = dvx.reshape(bsz, seq, hkv, group, hd).sum(axis=3)
+    return dq, dk, dv
+
+
+# --------------------------------------------------------------------------
+# SwiGLU
+# --------------------------------------------------------------------------
+def sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def silu(z):
+    return z * sigmoid(z)
+
+
+def silu_grad(z):
+    """d silu / dz = sigma(z) * (1 + z * (1 - sigma(z)))."""
+    s = sigmoid(z)
+    return s * (1.0 + z * (1.0 - s))
+
+
+def swiglu_fwd(a, b):
+    """m = silu(a) * b, with a the gate projection and b the up projection."""
+    return silu(a) * b
+
+
+def swiglu_bwd(dm, a, b):
+    """Returns (da, db)."""
+    return dm * b * silu_grad(a), dm * silu(a)
+
+
+# --------------------------------------------------------------------------
+# Cross-entropy, mean over tokens
+# --------------------------------------------------------------------------
+def logsumexp(x):
+    mx = x.max(axis=-1, keepdims=True)
+    return (mx + np.log(np.sum(np.exp(x - mx), axis=-1, keepdims=True)))[..., 0]
+
+
+def cross_entropy(logits, labels):
+    """loss = mean_t [lse(logits_t) - logits_t[label_t]];
+    dlogits = (softmax(logits) - onehot(labels)) / T.  Returns (loss, dlogits)."""
+    t = logits.shape[0]
+    lse = logsumexp(logits)
+    picked = logits[np.arange(t), labels]
+    loss = float(np.mean(lse - picked))
+    dlogits = np.exp(logits - lse[:, None])
+    dlogits[np.arange(t), labels] -= 1.0
+    return loss, dlogits / t
