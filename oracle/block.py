@@ -104,11 +104,23 @@ def attention_probs(q, k):
     bsz, seq, hq, hd = q.shape
     group = hq // k.shape[2]
     kx = np.repeat(k, group, axis=2)                     # [B, S, Hq, hd]
-    scores = np.einsum("bshd,bthd->bhst", q, kx) / np.sqrt(hd)
+    scores = np.einsum("bshd,bthd->bhst", q, kx, optimize=True) / np.sqrt(hd)
     scores = np.where(_causal_mask(seq)[None, None], scores, -np.inf)
     scores = scores - scores.max(axis=-1, keepdims=True)
     p = np.exp(scores)
     return p / p.sum(axis=-1, keepdims=True)
+
+
+def attention_lse(q, k):
+    """lse[b, h, s] = log sum_{s'<=s} exp(q[b,s,h] . k[b,s',h//G] / sqrt(hd)),
+    the softmax normaliser a streaming attention keeps per query row."""
+    bsz, seq, hq, hd = q.shape
+    group = hq // k.shape[2]
+    kx = np.repeat(k, group, axis=2)
+    scores = np.einsum("bshd,bthd->bhst", q, kx, optimize=True) / np.sqrt(hd)
+    scores = np.where(_causal_mask(seq)[None, None], scores, -np.inf)
+    mx = scores.max(axis=-1, keepdims=True)
+    return (mx + np.log(np.exp(scores - mx).sum(axis=-1, keepdims=True)))[..., 0]
 
 
 def attention_fwd(q, k, v):
@@ -116,7 +128,7 @@ def attention_fwd(q, k, v):
     group = q.shape[2] // k.shape[2]
     p = attention_probs(q, k)
     vx = np.repeat(v, group, axis=2)
-    return np.einsum("bhst,bthd->bshd", p, vx)
+    return np.einsum("bhst,bthd->bshd", p, vx, optimize=True)
 
 
 def attention_bwd(do, q, k, v):
@@ -132,13 +144,13 @@ def attention_bwd(do, q, k, v):
     p = attention_probs(q, k)
     kx = np.repeat(k, group, axis=2)
     vx = np.repeat(v, group, axis=2)
-    dp = np.einsum("bshd,bthd->bhst", do, vx)
+    dp = np.einsum("bshd,bthd->bhst", do, vx, optimize=True)
     dsum = np.sum(p * dp, axis=-1, keepdims=True)
     ds = p * (dp - dsum)
     scale = 1.0 / np.sqrt(hd)
-    dq = np.einsum("bhst,bthd->bshd", ds, kx) * scale
-    dkx = np.einsum("bhst,bshd->bthd", ds, q) * scale
-    dvx = np.einsum("bhst,bshd->bthd", p, do)
+    dq = np.einsum("bhst,bthd->bshd", ds, kx, optimize=True) * scale
+    dkx = np.einsum("bhst,bshd->bthd", ds, q, optimize=True) * scale
+    dvx = np.einsum("bhst,bshd->bthd", p, do, optimize=True)
     dk = dkx.reshape(bsz, seq, hkv, group, hd).sum(axis=3)
     dv = dvx.reshape(bsz, seq, hkv, group, hd).sum(axis=3)
     return dq, dk, dv

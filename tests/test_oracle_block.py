@@ -135,6 +135,23 @@ def test_attention_zero_query_is_causal_prefix_mean():
     np.testing.assert_allclose(o[:, 0], np.repeat(v[:, 0], 2, axis=1), rtol=1e-14)
 
 
+def test_attention_lse_closed_forms():
+    # zero queries: every visible score is 0, so lse = log(number of keys seen)
+    q = np.zeros((1, 7, 2, 8))
+    k = rng.standard_normal((1, 7, 1, 8))
+    lse = block.attention_lse(q, k)
+    np.testing.assert_allclose(lse[0, 0], np.log(np.arange(1, 8)), rtol=1e-14)
+    # position 0 sees only key 0: lse = q0 . k0 / sqrt(hd)
+    q = rng.standard_normal((2, 5, 2, 16))
+    k = rng.standard_normal((2, 5, 2, 16))
+    lse = block.attention_lse(q, k)
+    np.testing.assert_allclose(lse[:, :, 0], np.einsum("bhd,bhd->bh", q[:, 0], k[:, 0]) / 4.0, rtol=1e-13)
+    # brute force on one row
+    s = 4
+    ref = math.log(sum(math.exp(float(q[1, s, 1] @ k[1, j, 1]) / 4.0) for j in range(s + 1)))
+    assert abs(lse[1, 1, s] - ref) < 1e-12
+
+
 def test_attention_brute_force_loops():
     bsz, seq, hq, hkv, hd = 1, 6, 3, 1, 4
     q = rng.standard_normal((bsz, seq, hq, hd))
