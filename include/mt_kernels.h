@@ -1,0 +1,93 @@
+/*
+ * mt_kernels.h -- test entries of libmt.so: one call per gfx950 kernel of
+ * the decoder block, on caller-owned device memory and a caller stream
+ * (hipStream_t passed as void*; NULL is the null stream).  They launch and
+ * return without synchronising.  Every call returns MT_OK, MT_E_INVAL for a
+ * shape the kernel does not support (checked before launching) or MT_E_HIP.
+ * bf16 tensors are uint16 bit patterns, row-major, 16-byte aligned; inner
+ * dimensions and leading dimensions are multiples of 8 elements.
+ *
+ * The operations follow the decoder block the pages train, a pre-norm
+ * Qwen2.5-style decoder ("MegaTrain ... Review", dimensionstp.github.io,
+ * section 4-2 model list); the block itself is not spelled out on the pages.
+ */
+#ifndef MT_KERNELS_H
+#define MT_KERNELS_H
+
+#include <stdint.h>
+
+#include "mt.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* C[M x N] = op(A) op(B), bf16 inputs, fp32 accumulation.
+ * layout 0 (NT): A [M x K] (lda), B [N x K] (ldb)   C = A B^T
+ * layout 1 (NN): A [M x K],       B [K x N]         C = A B
+ * layout 2 (TN): A [K x M],       B [K x N]         C = A^T B
+ * epi 0: C bf16 = acc; 1: C bf16 = acc + R (bf16, ldr); 2: C f32 = acc;
+ * 3: C f32 += acc; 4: C bf16 = acc + Cacc (f32, ldacc). */
+int mt_k_gemm(int32_t layout, int32_t epi, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+              int64_t ldc, const void* R, int64_t ldr, const void* Cacc, int64_t ldacc, int32_t M, int32_t N,
+              int32_t K, void* stream);
+
+/* RMSNorm: n = gamma * x / sqrt(mean(x^2) + eps) per row of x [T x d];
+ * rstd [T] f32 = 1/sqrt(mean(x^2) + eps). */
+int mt_k_rmsnorm_fwd(const void* x, const void* gamma, void* n, void* rstd, int32_t T, int32_t d, float eps,
+                     void* stream);
+/* dx = resid + rstd * (g - nh * mean(g * nh)), g = dn*gamma, nh = x*rstd
+ * (resid may be NULL); dgamma [d] bf16 = sum_t dn * nh, summed in a fixed
+ * order through `scratch` (f32, mt_k_rmsnorm_bwd_scratch_elems). */
+int64_t mt_k_rmsnorm_bwd_scratch_elems(int32_t T, int32_t d);
+int mt_k_rmsnorm_bwd(const void* dn, const void* x, const void* gamma, const void* rstd, const void* resid,
+                     void* dx, void* dgamma, void* scratch, int32_t T, int32_t d, void* stream);
+
+/* Rotary embedding, rotate-half pairs (e, e+hd/2), angle s*base^(-2e/hd)
+ * with s = t % S, in place on the first n_rot_heads heads of each row of
+ * qkv [T x ld]; dir +1 forward, -1 backward.  table: device scratch of
+ * S*hd/2 float2, filled by the call. */
+int mt_k_rope(void* qkv, int64_t ld, void* table, int32_t T, int32_t S, int32_t n_rot_heads, int32_t hd,
+              float base, int32_t dir, void* stream);
+
+/* SwiGLU on gu [T x 2F] = [gate | up]: m [T x F] = silu(gate) * up;
+ * backward dgu = [dm * up * silu'(gate) | dm * silu(gate)]. */
+int mt_k_swiglu_fwd(const void* gu, void* m, int32_t T, int32_t F, void* stream);
+int mt_k_swiglu_bwd(const void* dm, const void* gu, void* dgu, int32_t T, int32_t F, void* stream);
+
+/* Causal GQA attention on qkv [B*S x ld] (q heads at column 0, k heads at
+ * Hq*hd, v heads at (Hq+Hkv)*hd; query head h reads KV head h/(Hq/Hkv)),
+ * scale 1/sqrt(hd): o [B*S x ldo], lse [B x Hq x S] f32 (natural log).
+ * hd in {64, 128}. */
+int mt_k_attn_fwd(const void* qkv, int64_t ld, void* o, int64_t ldo, void* lse, int32_t B, int32_t S, int32_t Hq,
+                  int32_t Hkv, int32_t hd, void* stream);
+/* Backward: dqkv [B*S x ldd] gets dQ, dK, dV in the qkv column layout (the
+ * K and V gradients summed over each KV group, in a fixed order); dsum is
+ * f32 scratch [B x Hq x S]. */
+int mt_k_attn_bwd(const void* qkv, int64_t ld, const void* o, const void* dout, int64_t ldo, const void* lse,
+                  void* dsum, void* dqkv, int64_t ldd, int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t hd,
+                  void* stream);
+
+/* Cross-entropy of logits [Tc x V] f32 against int32 labels [Tc]:
+ * loss_rows [Tc] = logsumexp - logit[label]; dlogits [Tc x V] bf16 =
+ * (softmax - onehot) * inv_T.  mean: out[0] = sum(x[0..n)) / n. */
+int mt_k_ce(const void* logits, const void* labels, void* loss_rows, void* dlogits, int32_t Tc, int32_t V,
+            float inv_T, void* stream);
+int mt_k_mean(const void* x, void* out, int32_t n, void* stream);
+int mt_k_f32_to_bf16(const void* x, void* y, int64_t n, void* stream);
+
+/* Host (CPU) entries, no GPU needed. */
+/* The production host Adam over n elements of caller arrays: G <- gsrc,
+ * m, v, master updated in fp32 with bias corrections for `step`, W =
+ * bf16(master). */
+int mt_host_adam(uint16_t* w, uint16_t* g, float* master, float* m, float* v, const uint16_t* gsrc, int64_t n,
+                 int64_t step, float lr, float beta1, float beta2, float eps, int32_t threads);
+/* Initialise one unit tile (16 * mt_unit_elems bytes) as mt_init would. */
+int mt_host_init_unit(const mt_shape* shape, int32_t unit, uint64_t seed, float init_std, int32_t threads,
+                      void* tile, uint64_t tile_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MT_KERNELS_H */

@@ -1,0 +1,577 @@
+// Causal grouped-query flash attention for gfx950: forward (O and the
+// log-sum-exp), and a deterministic backward split into a dQ kernel and a
+// dK/dV kernel, neither using atomics.
+//
+// All contractions run on v_mfma_f32_32x32x16_bf16.  The MFMA writes element
+// r of lane l of a 32x32 result at row 8*(r/4) + 4*(l/32) + r%4, column l%32,
+// and takes its A operand as row l%32, k = 8*(l/32)..+7 and its B operand as
+// column l%32, same k.  The kernels exploit that:
+//  * forward and dQ compute S^T = K Q^T, so a lane owns one query (a column)
+//    and holds 16 of its scores in registers: the softmax state of a query
+//    lives in one lane (plus its partner lane l^32), no LDS reductions;
+//  * the probabilities then feed the next MFMA directly as its B operand,
+//    with the contraction index (keys) permuted the same way in the A
+//    operand, which is read from a transposed LDS image of V (or K);
+//  * dK/dV compute S = Q K^T instead, so a lane owns one key and the key
+//    gradients accumulate per lane over every query head of the KV group in
+//    a fixed order.
+// K/V (or Q/dO) tiles are staged in LDS twice-buffered: global loads of the
+// next tile are issued before the MFMAs on the current one.
+#include "kcommon.h"
+#include "kernels.h"
+
+namespace mt {
+namespace {
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+constexpr int BKV = 64;  // keys (or queries) per staged tile
+
+#define MFMA32(a, b, c) __builtin_amdgcn_mfma_f32_32x32x16_bf16((a), (b), (c), 0, 0, 0)
+
+// Row-major tile image [rows][HD] bf16 in 16-byte chunks, chunk index
+// XOR-swizzled with the row.
+template <int HD>
+struct RowTile {
+    static constexpr int NCH = HD / 8;
+    static constexpr int SW = (NCH < 16 ? NCH : 16) - 1;
+    __device__ static __forceinline__ int idx(int row, int chunk) { return row * NCH + (chunk ^ (row & SW)); }
+};
+// Transposed tile image [HD][64 positions] bf16 in 8-byte chunks of four
+// positions, chunk index XOR-swizzled with the d row.
+struct ColTile {
+    __device__ static __forceinline__ int idx(int d, int chunk4) { return d * 16 + (chunk4 ^ (d & 15)); }
+};
+
+__device__ __forceinline__ uint32_t h16(const uint4& v, int e) {
+    uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
+    return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
+}
+
+// A 4-position x 8-d block of a [pos x d] row-major source, kept in
+// registers and written out both as rows and transposed.
+struct Blk48 {
+    uint4 v[4];
+    __device__ __forceinline__ void load(const uint16_t* __restrict__ base, int64_t ld, int pos0,
+                                         int npos, int d0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int p = pos0 + j;
+            v[j] = p < npos ? *reinterpret_cast<const uint4*>(base + int64_t(p) * ld + d0)
+                            : make_uint4(0, 0, 0, 0);
+        }
+    }
+    template <int HD>
+    __device__ __forceinline__ void store_rows(uint4* __restrict__ lds, int prow0, int dchunk) const {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) lds[RowTile<HD>::idx(prow0 + j, dchunk)] = v[j];
+    }
+    __device__ __forceinline__ void store_cols(uint2* __restrict__ lds, int prow0, int d0) const {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            uint2 w;
+            w.x = h16(v[0], e) | (h16(v[1], e) << 16);
+            w.y = h16(v[2], e) | (h16(v[3], e) << 16);
+            lds[ColTile::idx(d0 + e, prow0 >> 2)] = w;
+        }
+    }
+};
+
+// Read an A operand (rows = d, k = 16 positions starting at 16*s2 of the
+// 32-position sub-tile t) from a transposed image, with the key permutation
+// that matches the accumulator layout: k-slot j of lane half hh is position
+// 4*hh + j (j < 4) or 8 + 4*hh + (j - 4).
+__device__ __forceinline__ bf16x8_t read_colT(const uint2* __restrict__ lds, int d, int t, int s2, int hh) {
+    const int c0 = 8 * t + 4 * s2 + hh;
+    const uint2 lo = lds[ColTile::idx(d, c0)];
+    const uint2 hi = lds[ColTile::idx(d, c0 + 2)];
+    return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+// Pack accumulator registers 8*s2..8*s2+7 into a bf16 B operand.
+__device__ __forceinline__ bf16x8_t pack_b(const float* v) {
+    return as_bf16x8(make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])));
+}
+
+// ----------------------------------------------------------- forward ------
+// Block: 4 waves x 32 queries of one (b, h); key tiles of 64.
+template <int HD>
+__global__ __launch_bounds__(256) void attn_fwd_k(AttnArgs a, int n_qt) {
+    constexpr int NS = HD / 16;   // k-steps over head dim
+    constexpr int ND = HD / 32;   // 32-wide d tiles
+    __shared__ uint4 Ks[2][BKV * HD / 8];
+    __shared__ uint2 Vt[2][HD * 16];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hh = lane >> 5, c = lane & 31;
+    const int qt = n_qt - 1 - int(blockIdx.x % n_qt);
+    const int bh = int(blockIdx.x / n_qt);
+    const int h = bh % a.Hq, b = bh / a.Hq;
+    const int hk = h / (a.Hq / a.Hkv);
+    const int S = a.S;
+    const int q0 = qt * 128;
+    const int qw = q0 + wave * 32;
+    const int q = qw + c;
+    const uint16_t* base = a.qkv + int64_t(b) * S * a.ld;
+    const int kcol = (a.Hq + hk) * HD, vcol = (a.Hq + a.Hkv + hk) * HD;
+
+    bf16x8_t qf[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (q < S) v = *reinterpret_cast<const uint4*>(base + int64_t(q) * a.ld + h * HD + (2 * s + hh) * 8);
+        qf[s] = as_bf16x8(v);
+    }
+
+    // Tile loaders: K as rows (HD/32 chunks per thread), V as 4x8 blocks.
+    constexpr int KCH = BKV * HD / 8 / 256;
+    uint4 kreg[KCH];
+    Blk48 vreg;
+    const bool vthread = tid < 2 * HD;  // (64/4) * (HD/8) blocks
+    const int vdg = tid % (HD / 8), vkg = tid / (HD / 8);
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            const int cc = tid + i * 256;
+            const int row = cc / (HD / 8), kc = cc % (HD / 8);
+            kreg[i] = (k0 + row < S) ? *reinterpret_cast<const uint4*>(base + int64_t(k0 + row) * a.ld + kcol + kc * 8)
+                                     : make_uint4(0, 0, 0, 0);
+        }
+        if (vthread) vreg.load(base + vcol, a.ld, k0 + 4 * vkg, S, 8 * vdg);
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            const int cc = tid + i * 256;
+            const int row = cc / (HD / 8), kc = cc % (HD / 8);
+            Ks[buf][RowTile<HD>::idx(row, kc)] = kreg[i];
+        }
+        if (vthread) vreg.store_cols(Vt[buf], 4 * vkg, 8 * vdg);
+    };
+
+    f32x16_t o[ND];
+#pragma unroll
+    for (int i = 0; i < ND; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
+    float m = -INFINITY, lsum = 0.f;
+    const float sc = LOG2E * rsqrtf(float(HD));
+
+    const int k_end = min(S, q0 + 128);
+    const int nkb = (k_end + BKV - 1) / BKV;
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int kb = 0; kb < nkb; ++kb) {
+        const int cur = kb & 1;
+        const int k0 = kb * BKV;
+        if (kb + 1 < nkb) gload(k0 + BKV);
+        if (k0 <= qw + 31) {
+            f32x16_t st[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) st[t][r] = 0.f;
+#pragma unroll
+                for (int s = 0; s < NS; ++s)
+                    st[t] = MFMA32(as_bf16x8(Ks[cur][RowTile<HD>::idx(32 * t + c, 2 * s + hh)]), qf[s], st[t]);
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
+                    const float v = (key > q || key >= S) ? -INFINITY : st[t][r] * sc;
+                    st[t][r] = v;
+                    mx = fmaxf(mx, v);
+                }
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float mn = fmaxf(m, mx);
+            const float alpha = (m == -INFINITY) ? 0.f : exp2f(m - mn);
+            m = mn;
+            float ps = 0.f;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float p = (mn == -INFINITY) ? 0.f : exp2f(st[t][r] - mn);
+                    st[t][r] = p;
+                    ps += p;
+                }
+            lsum = lsum * alpha + ps;
+#pragma unroll
+            for (int i = 0; i < ND; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+            bf16x8_t pb[2][2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    float tmp[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) tmp[j] = st[t][8 * s2 + j];
+                    pb[t][s2] = pack_b(tmp);
+                }
+#pragma unroll
+            for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2)
+                        o[dt] = MFMA32(read_colT(Vt[cur], 32 * dt + c, t, s2, hh), pb[t][s2], o[dt]);
+        }
+        if (kb + 1 < nkb) lstore(cur ^ 1);
+        __syncthreads();
+    }
+
+    const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+    if (q < S) {
+        const float inv = 1.0f / ltot;
+        uint16_t* orow = a.o + (int64_t(b) * S + q) * a.ldo + h * HD;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = 32 * dt + 8 * g + 4 * hh;
+                *reinterpret_cast<uint2*>(orow + d) =
+                    make_uint2(pack2(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv),
+                               pack2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv));
+            }
+        if (hh == 0) a.lse[(int64_t(b) * a.Hq + h) * S + q] = (m + log2f(ltot)) * LN2;
+    }
+}
+
+// ------------------------------------------------- D = rowsum(dO * O) -----
+template <int HD>
+__global__ void attn_dsum_k(AttnBwdArgs a) {
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t T = int64_t(a.B) * a.S;
+    if (i >= T * a.Hq) return;
+    const int h = int(i % a.Hq);
+    const int64_t t = i / a.Hq;
+    const uint4* o = reinterpret_cast<const uint4*>(a.o + t * a.ldo + h * HD);
+    const uint4* g = reinterpret_cast<const uint4*>(a.dout + t * a.ldo + h * HD);
+    float s = 0.f;
+#pragma unroll 4
+    for (int j = 0; j < HD / 8; ++j) {
+        float x[8], y[8];
+        unpack8(o[j], x);
+        unpack8(g[j], y);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) s += x[k] * y[k];
+    }
+    const int b = int(t / a.S), sq = int(t % a.S);
+    a.dsum[(int64_t(b) * a.Hq + h) * a.S + sq] = s;
+}
+
+// --------------------------------------------------------------- dQ -------
+template <int HD>
+__global__ __launch_bounds__(256) void attn_dq_k(AttnBwdArgs a, int n_qt) {
+    constexpr int NS = HD / 16, ND = HD / 32;
+    __shared__ uint4 Ks[2][BKV * HD / 8];
+    __shared__ uint4 Vs[2][BKV * HD / 8];
+    __shared__ uint2 Kt[2][HD * 16];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hh = lane >> 5, c = lane & 31;
+    const int qt = n_qt - 1 - int(blockIdx.x % n_qt);
+    const int bh = int(blockIdx.x / n_qt);
+    const int h = bh % a.Hq, b = bh / a.Hq;
+    const int hk = h / (a.Hq / a.Hkv);
+    const int S = a.S;
+    const int q0 = qt * 128, qw = q0 + wave * 32, q = qw + c;
+    const uint16_t* base = a.qkv + int64_t(b) * S * a.ld;
+    const uint16_t* dbase = a.dout + int64_t(b) * S * a.ldo;
+    const int kcol = (a.Hq + hk) * HD, vcol = (a.Hq + a.Hkv + hk) * HD;
+
+    bf16x8_t qf[NS], dof[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        uint4 v = make_uint4(0, 0, 0, 0), w = v;
+        if (q < S) {
+            v = *reinterpret_cast<const uint4*>(base + int64_t(q) * a.ld + h * HD + (2 * s + hh) * 8);
+            w = *reinterpret_cast<const uint4*>(dbase + int64_t(q) * a.ldo + h * HD + (2 * s + hh) * 8);
+        }
+        qf[s] = as_bf16x8(v);
+        dof[s] = as_bf16x8(w);
+    }
+    const int64_t st_off = (int64_t(b) * a.Hq + h) * S;
+    const float lse2 = q < S ? a.lse[st_off + q] * LOG2E : 0.f;
+    const float dq_d = q < S ? a.dsum[st_off + q] : 0.f;
+
+    // K blocks feed both the row image (scores) and the transposed image (dQ).
+    const int dg = tid % (HD / 8), kg = tid / (HD / 8);
+    const bool bthread = tid < 2 * HD;
+    Blk48 kreg, vreg;
+    auto gload = [&](int k0) {
+        if (bthread) {
+            kreg.load(base + kcol, a.ld, k0 + 4 * kg, S, 8 * dg);
+            vreg.load(base + vcol, a.ld, k0 + 4 * kg, S, 8 * dg);
+        }
+    };
+    auto lstore = [&](int buf) {
+        if (bthread) {
+            kreg.store_rows<HD>(Ks[buf], 4 * kg, dg);
+            kreg.store_cols(Kt[buf], 4 * kg, 8 * dg);
+            vreg.store_rows<HD>(Vs[buf], 4 * kg, dg);
+        }
+    };
+
+    f32x16_t acc[ND];
+#pragma unroll
+    for (int i = 0; i < ND; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+    const float sc = LOG2E * rsqrtf(float(HD));
+
+    const int k_end = min(S, q0 + 128);
+    const int nkb = (k_end + BKV - 1) / BKV;
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int kb = 0; kb < nkb; ++kb) {
+        const int cur = kb & 1;
+        const int k0 = kb * BKV;
+        if (kb + 1 < nkb) gload(k0 + BKV);
+        if (k0 <= qw + 31) {
+            f32x16_t st[2], dp[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) { st[t][r] = 0.f; dp[t][r] = 0.f; }
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    st[t] = MFMA32(as_bf16x8(Ks[cur][RowTile<HD>::idx(32 * t + c, 2 * s + hh)]), qf[s], st[t]);
+                    dp[t] = MFMA32(as_bf16x8(Vs[cur][RowTile<HD>::idx(32 * t + c, 2 * s + hh)]), dof[s], dp[t]);
+                }
+            }
+            bf16x8_t dsb[2][2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    float tmp[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int r = 8 * s2 + j;
+                        const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
+                        const float p = (key > q || key >= S) ? 0.f : exp2f(st[t][r] * sc - lse2);
+                        tmp[j] = p * (dp[t][r] - dq_d);
+                    }
+                    dsb[t][s2] = pack_b(tmp);
+                }
+#pragma unroll
+            for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2)
+                        acc[dt] = MFMA32(read_colT(Kt[cur], 32 * dt + c, t, s2, hh), dsb[t][s2], acc[dt]);
+        }
+        if (kb + 1 < nkb) lstore(cur ^ 1);
+        __syncthreads();
+    }
+    if (q < S) {
+        const float scale = rsqrtf(float(HD));
+        uint16_t* row = a.dqkv + (int64_t(b) * S + q) * a.ldd + h * HD;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = 32 * dt + 8 * g + 4 * hh;
+                *reinterpret_cast<uint2*>(row + d) =
+                    make_uint2(pack2(acc[dt][4 * g] * scale, acc[dt][4 * g + 1] * scale),
+                               pack2(acc[dt][4 * g + 2] * scale, acc[dt][4 * g + 3] * scale));
+            }
+    }
+}
+
+// ------------------------------------------------------------ dK, dV ------
+// Block: 4 waves x 32 keys of one (b, kv head); loops over the query heads
+// of the group and over 64-query tiles from the diagonal on.
+template <int HD>
+__global__ __launch_bounds__(256) void attn_dkdv_k(AttnBwdArgs a, int n_kt) {
+    constexpr int NS = HD / 16, ND = HD / 32;
+    __shared__ uint4 Qs[2][BKV * HD / 8];
+    __shared__ uint4 Ds[2][BKV * HD / 8];
+    __shared__ uint2 Qt[2][HD * 16];
+    __shared__ uint2 Dt[2][HD * 16];
+    __shared__ float Ls[2][BKV], Dd[2][BKV];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hh = lane >> 5, c = lane & 31;
+    const int kt = int(blockIdx.x % n_kt);
+    const int bk = int(blockIdx.x / n_kt);
+    const int hk = bk % a.Hkv, b = bk / a.Hkv;
+    const int G = a.Hq / a.Hkv;
+    const int S = a.S;
+    const int k0 = kt * 128, kw = k0 + wave * 32, key = kw + c;
+    const uint16_t* base = a.qkv + int64_t(b) * S * a.ld;
+    const uint16_t* dbase = a.dout + int64_t(b) * S * a.ldo;
+    const int kcol = (a.Hq + hk) * HD, vcol = (a.Hq + a.Hkv + hk) * HD;
+
+    bf16x8_t kf[NS], vf[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        uint4 v = make_uint4(0, 0, 0, 0), w = v;
+        if (key < S) {
+            v = *reinterpret_cast<const uint4*>(base + int64_t(key) * a.ld + kcol + (2 * s + hh) * 8);
+            w = *reinterpret_cast<const uint4*>(base + int64_t(key) * a.ld + vcol + (2 * s + hh) * 8);
+        }
+        kf[s] = as_bf16x8(v);
+        vf[s] = as_bf16x8(w);
+    }
+
+    const int dg = tid % (HD / 8), qg = tid / (HD / 8);
+    const bool bthread = tid < 2 * HD;
+    Blk48 qreg, dreg;
+    float lreg = 0.f, dreg_s = 0.f;
+    auto gload = [&](int h, int q0) {
+        if (bthread) {
+            qreg.load(base + h * HD, a.ld, q0 + 4 * qg, S, 8 * dg);
+            dreg.load(dbase + h * HD, a.ldo, q0 + 4 * qg, S, 8 * dg);
+        }
+        if (tid < BKV) {
+            const int64_t off = (int64_t(b) * a.Hq + h) * S;
+            const int qq = q0 + tid;
+            lreg = qq < S ? a.lse[off + qq] * LOG2E : 0.f;
+            dreg_s = qq < S ? a.dsum[off + qq] : 0.f;
+        }
+    };
+    auto lstore = [&](int buf) {
+        if (bthread) {
+            qreg.store_rows<HD>(Qs[buf], 4 * qg, dg);
+            qreg.store_cols(Qt[buf], 4 * qg, 8 * dg);
+            dreg.store_rows<HD>(Ds[buf], 4 * qg, dg);
+            dreg.store_cols(Dt[buf], 4 * qg, 8 * dg);
+        }
+        if (tid < BKV) {
+            Ls[buf][tid] = lreg;
+            Dd[buf][tid] = dreg_s;
+        }
+    };
+
+    f32x16_t dk[ND], dv[ND];
+#pragma unroll
+    for (int i = 0; i < ND; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { dk[i][r] = 0.f; dv[i][r] = 0.f; }
+    const float sc = LOG2E * rsqrtf(float(HD));
+
+    const int qb0 = k0 / BKV;
+    const int nqb = (S + BKV - 1) / BKV - qb0;  // per head
+    const int total = nqb * G;
+    if (total > 0) {
+        gload(hk * G, qb0 * BKV);
+        lstore(0);
+    }
+    __syncthreads();
+    for (int it = 0; it < total; ++it) {
+        const int cur = it & 1;
+        const int q0 = (qb0 + it % nqb) * BKV;
+        if (it + 1 < total) gload(hk * G + (it + 1) / nqb, (qb0 + (it + 1) % nqb) * BKV);
+        if (kw <= q0 + BKV - 1) {
+            f32x16_t st[2], dp[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) { st[t][r] = 0.f; dp[t][r] = 0.f; }
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    st[t] = MFMA32(as_bf16x8(Qs[cur][RowTile<HD>::idx(32 * t + c, 2 * s + hh)]), kf[s], st[t]);
+                    dp[t] = MFMA32(as_bf16x8(Ds[cur][RowTile<HD>::idx(32 * t + c, 2 * s + hh)]), vf[s], dp[t]);
+                }
+            }
+            bf16x8_t pb[2][2], dsb[2][2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    float tp[8], td[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int r = 8 * s2 + j;
+                        const int ql = 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
+                        const int qq = q0 + ql;
+                        const float p = (key > qq || qq >= S || key >= S)
+                                            ? 0.f : exp2f(st[t][r] * sc - Ls[cur][ql]);
+                        tp[j] = p;
+                        td[j] = p * (dp[t][r] - Dd[cur][ql]);
+                    }
+                    pb[t][s2] = pack_b(tp);
+                    dsb[t][s2] = pack_b(td);
+                }
+#pragma unroll
+            for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        dv[dt] = MFMA32(read_colT(Dt[cur], 32 * dt + c, t, s2, hh), pb[t][s2], dv[dt]);
+                        dk[dt] = MFMA32(read_colT(Qt[cur], 32 * dt + c, t, s2, hh), dsb[t][s2], dk[dt]);
+                    }
+        }
+        if (it + 1 < total) lstore(cur ^ 1);
+        __syncthreads();
+    }
+    if (key < S) {
+        const float scale = rsqrtf(float(HD));
+        uint16_t* row = a.dqkv + (int64_t(b) * S + key) * a.ldd;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = 32 * dt + 8 * g + 4 * hh;
+                *reinterpret_cast<uint2*>(row + kcol + d) =
+                    make_uint2(pack2(dk[dt][4 * g] * scale, dk[dt][4 * g + 1] * scale),
+                               pack2(dk[dt][4 * g + 2] * scale, dk[dt][4 * g + 3] * scale));
+                *reinterpret_cast<uint2*>(row + vcol + d) =
+                    make_uint2(pack2(dv[dt][4 * g], dv[dt][4 * g + 1]),
+                               pack2(dv[dt][4 * g + 2], dv[dt][4 * g + 3]));
+            }
+    }
+}
+
+bool attn_shape_ok(int B, int S, int Hq, int Hkv, int hd, int64_t ld, int64_t ldo) {
+    if (B <= 0 || S <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv) return false;
+    if (hd != 64 && hd != 128) return false;
+    if ((ld & 7) || (ldo & 7)) return false;
+    if (ld < int64_t(Hq + 2 * Hkv) * hd || ldo < int64_t(Hq) * hd) return false;
+    return true;
+}
+
+}  // namespace
+
+hipError_t attn_fwd(const AttnArgs& a, hipStream_t s) {
+    if (!attn_shape_ok(a.B, a.S, a.Hq, a.Hkv, a.hd, a.ld, a.ldo)) return hipErrorInvalidValue;
+    const int n_qt = (a.S + 127) / 128;
+    const dim3 grid(unsigned(int64_t(n_qt) * a.B * a.Hq));
+    if (a.hd == 128) attn_fwd_k<128><<<grid, 256, 0, s>>>(a, n_qt);
+    else attn_fwd_k<64><<<grid, 256, 0, s>>>(a, n_qt);
+    return hipGetLastError();
+}
+
+hipError_t attn_bwd(const AttnBwdArgs& a, hipStream_t s) {
+    if (!attn_shape_ok(a.B, a.S, a.Hq, a.Hkv, a.hd, a.ld, a.ldo)) return hipErrorInvalidValue;
+    if (a.ldd < int64_t(a.Hq + 2 * a.Hkv) * a.hd || (a.ldd & 7)) return hipErrorInvalidValue;
+    const int64_t rows = int64_t(a.B) * a.S * a.Hq;
+    const unsigned nb = unsigned((rows + 255) / 256);
+    const int n_qt = (a.S + 127) / 128;
+    const int n_kt = (a.S + 127) / 128;
+    const dim3 gq(unsigned(int64_t(n_qt) * a.B * a.Hq));
+    const dim3 gk(unsigned(int64_t(n_kt) * a.B * a.Hkv));
+    if (a.hd == 128) {
+        attn_dsum_k<128><<<nb, 256, 0, s>>>(a);
+        attn_dq_k<128><<<gq, 256, 0, s>>>(a, n_qt);
+        attn_dkdv_k<128><<<gk, 256, 0, s>>>(a, n_kt);
+    } else {
+        attn_dsum_k<64><<<nb, 256, 0, s>>>(a);
+        attn_dq_k<64><<<gq, 256, 0, s>>>(a, n_qt);
+        attn_dkdv_k<64><<<gk, 256, 0, s>>>(a, n_kt);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace mt

@@ -1,0 +1,397 @@
+// Memory-bound kernels of the decoder block on gfx950: RMSNorm forward and
+// backward, rotary embedding, SwiGLU forward and backward, the LM-head
+// cross-entropy, and small conversions.  All read and write bf16 in 16-byte
+// vectors (8 elements per lane), keep statistics in fp32 and reduce in a
+// fixed order, so every result is bit-reproducible run to run.
+#include "kcommon.h"
+#include "kernels.h"
+
+namespace mt {
+namespace {
+
+// ------------------------------------------------------------- RMSNorm ----
+// One wave per row, four rows per 256-thread block.
+__global__ __launch_bounds__(256) void rmsnorm_fwd_k(const uint4* __restrict__ x,
+                                                     const uint4* __restrict__ gamma,
+                                                     uint4* __restrict__ n, float* __restrict__ rstd,
+                                                     int T, int d, float eps) {
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= T) return;
+    const int nv = d >> 3;
+    const uint4* xr = x + int64_t(row) * nv;
+    float ss = 0.f;
+    for (int c = lane; c < nv; c += 64) {
+        float f[8];
+        unpack8(xr[c], f);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) ss += f[k] * f[k];
+    }
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / float(d) + eps);
+    uint4* nr = n + int64_t(row) * nv;
+    for (int c = lane; c < nv; c += 64) {
+        float f[8], g[8];
+        unpack8(xr[c], f);
+        unpack8(gamma[c], g);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) f[k] = (f[k] * r) * g[k];
+        nr[c] = pack8(f);
+    }
+    if (lane == 0) rstd[row] = r;
+}
+
+// Backward: each wave takes RPW consecutive rows; each lane accumulates the
+// gamma gradient of its columns in registers and writes one partial row per
+// wave; dgamma_reduce sums the partial rows in order.
+constexpr int RPW = 8;
+
+template <int NCL>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_k(const uint4* __restrict__ dn,
+                                                     const uint4* __restrict__ x,
+                                                     const uint4* __restrict__ gamma,
+                                                     const float* __restrict__ rstd,
+                                                     const uint4* __restrict__ resid,
+                                                     uint4* __restrict__ dx,
+                                                     float* __restrict__ partial, int T, int d) {
+    const int wave_id = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int nv = d >> 3;
+    float dg[NCL][8];
+#pragma unroll
+    for (int j = 0; j < NCL; ++j)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) dg[j][k] = 0.f;
+    float gm[NCL][8];
+#pragma unroll
+    for (int j = 0; j < NCL; ++j) {
+        int c = lane + 64 * j;
+        if (c < nv) unpack8(gamma[c], gm[j]);
+    }
+    const int row0 = wave_id * RPW;
+    for (int rr = 0; rr < RPW; ++rr) {
+        const int row = row0 + rr;
+        if (row >= T) break;
+        const float r = rstd[row];
+        const uint4* dnr = dn + int64_t(row) * nv;
+        const uint4* xr = x + int64_t(row) * nv;
+        float g[NCL][8], nh[NCL][8];
+        float dot = 0.f;
+#pragma unroll
+        for (int j = 0; j < NCL; ++j) {
+            int c = lane + 64 * j;
+            if (c < nv) {
+                float a[8], b[8];
+                unpack8(dnr[c], a);
+                unpack8(xr[c], b);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    nh[j][k] = b[k] * r;
+                    g[j][k] = a[k] * gm[j][k];
+                    dg[j][k] += a[k] * nh[j][k];
+                    dot += g[j][k] * nh[j][k];
+                }
+            }
+        }
+        dot = wave_sum(dot) / float(d);
+        uint4* dxr = dx + int64_t(row) * nv;
+        const uint4* rr_ = resid ? resid + int64_t(row) * nv : nullptr;
+#pragma unroll
+        for (int j = 0; j < NCL; ++j) {
+            int c = lane + 64 * j;
+            if (c < nv) {
+                float o[8], q[8];
+                if (rr_) unpack8(rr_[c], q);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    o[k] = r * (g[j][k] - nh[j][k] * dot);
+                    if (rr_) o[k] += q[k];
+                }
+                dxr[c] = pack8(o);
+            }
+        }
+    }
+    float* pr = partial + int64_t(wave_id) * d;
+#pragma unroll
+    for (int j = 0; j < NCL; ++j) {
+        int c = lane + 64 * j;
+        if (c < nv) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) pr[c * 8 + k] = dg[j][k];
+        }
+    }
+}
+
+__global__ void dgamma_reduce_k(const float* __restrict__ partial, int nrows, int d,
+                                uint16_t* __restrict__ dgamma) {
+    const int c = blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= d) return;
+    float s = 0.f;
+    for (int r = 0; r < nrows; ++r) s += partial[int64_t(r) * d + c];
+    dgamma[c] = f2bf(s);
+}
+
+// ---------------------------------------------------------------- RoPE ----
+__global__ void rope_table_k(float2* tab, int S, int half, int hd, double base) {
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= int64_t(S) * half) return;
+    const int s = int(i / half), e = int(i % half);
+    const double th = double(s) * pow(base, -2.0 * double(e) / double(hd));
+    tab[i] = make_float2(float(cos(th)), float(sin(th)));
+}
+
+// One thread rotates 8 pairs (e..e+7, e+half..e+half+7) of one head.
+__global__ void rope_apply_k(uint16_t* __restrict__ qkv, int64_t ld, const float2* __restrict__ tab,
+                             int T, int S, int nh, int hd, int dir) {
+    const int half = hd >> 1;
+    const int per_head = half >> 3;
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= int64_t(T) * nh * per_head) return;
+    const int e8 = int(i % per_head);
+    const int64_t th = i / per_head;
+    const int h = int(th % nh);
+    const int t = int(th / nh);
+    const int s = t % S;
+    uint16_t* base = qkv + int64_t(t) * ld + int64_t(h) * hd + e8 * 8;
+    uint4* plo = reinterpret_cast<uint4*>(base);
+    uint4* phi = reinterpret_cast<uint4*>(base + half);
+    float lo[8], hi[8], ol[8], oh[8];
+    unpack8(*plo, lo);
+    unpack8(*phi, hi);
+    const float2* tr = tab + int64_t(s) * half + e8 * 8;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const float2 cs = tr[k];
+        const float sn = dir > 0 ? cs.y : -cs.y;
+        ol[k] = lo[k] * cs.x - hi[k] * sn;
+        oh[k] = hi[k] * cs.x + lo[k] * sn;
+    }
+    *plo = pack8(ol);
+    *phi = pack8(oh);
+}
+
+// -------------------------------------------------------------- SwiGLU ----
+__device__ __forceinline__ float sigm(float z) { return 1.0f / (1.0f + expf(-z)); }
+
+__global__ void swiglu_fwd_k(const uint4* __restrict__ gu, uint4* __restrict__ m, int T, int F) {
+    const int fv = F >> 3;
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= int64_t(T) * fv) return;
+    const int64_t t = i / fv;
+    const int c = int(i % fv);
+    float a[8], b[8], o[8];
+    unpack8(gu[t * 2 * fv + c], a);
+    unpack8(gu[t * 2 * fv + fv + c], b);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o[k] = (a[k] * sigm(a[k])) * b[k];
+    m[t * fv + c] = pack8(o);
+}
+
+__global__ void swiglu_bwd_k(const uint4* __restrict__ dm, const uint4* __restrict__ gu,
+                             uint4* __restrict__ dgu, int T, int F) {
+    const int fv = F >> 3;
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= int64_t(T) * fv) return;
+    const int64_t t = i / fv;
+    const int c = int(i % fv);
+    float a[8], b[8], g[8], da[8], db[8];
+    unpack8(gu[t * 2 * fv + c], a);
+    unpack8(gu[t * 2 * fv + fv + c], b);
+    unpack8(dm[t * fv + c], g);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const float s = sigm(a[k]);
+        db[k] = g[k] * (a[k] * s);
+        da[k] = g[k] * b[k] * (s * (1.0f + a[k] * (1.0f - s)));
+    }
+    dgu[t * 2 * fv + c] = pack8(da);
+    dgu[t * 2 * fv + fv + c] = pack8(db);
+}
+
+// ------------------------------------------------------- Cross-entropy ----
+// One 256-thread block per token row.
+__global__ __launch_bounds__(256) void ce_k(const float* __restrict__ logits,
+                                            const int32_t* __restrict__ labels,
+                                            float* __restrict__ loss_rows,
+                                            uint16_t* __restrict__ dlogits, int V, float inv_T) {
+    const int row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const float* x = logits + int64_t(row) * V;
+    const float4* x4 = reinterpret_cast<const float4*>(x);
+    const int nv4 = V >> 2;
+    // Pass 1: running (max, sum of exp) per thread, then a fixed-order merge.
+    float mx = -INFINITY, sm = 0.f;
+    for (int c = tid; c < nv4; c += 256) {
+        const float4 v = x4[c];
+        const float vm = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
+        if (vm > mx) { sm *= expf(mx - vm); mx = vm; }
+        sm += expf(v.x - mx) + expf(v.y - mx) + expf(v.z - mx) + expf(v.w - mx);
+    }
+    __shared__ float smx[256], ssm[256];
+    smx[tid] = mx;
+    ssm[tid] = sm;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if (tid < o) {
+            const float m1 = smx[tid], m2 = smx[tid + o];
+            const float m = fmaxf(m1, m2);
+            const float s = (m1 == -INFINITY ? 0.f : ssm[tid] * expf(m1 - m)) +
+                            (m2 == -INFINITY ? 0.f : ssm[tid + o] * expf(m2 - m));
+            smx[tid] = m;
+            ssm[tid] = s;
+        }
+        __syncthreads();
+    }
+    const float lse = smx[0] + logf(ssm[0]);
+    const int lab = labels[row];
+    const bool lab_ok = lab >= 0 && lab < V;
+    if (tid == 0) loss_rows[row] = lab_ok ? lse - x[lab] : NAN;
+    // Pass 2: dlogits = (softmax - onehot) / T in bf16, 4 per thread-step.
+    uint2* d2 = reinterpret_cast<uint2*>(dlogits + int64_t(row) * V);
+    for (int c = tid; c < nv4; c += 256) {
+        const float4 v = x4[c];
+        float p0 = expf(v.x - lse), p1 = expf(v.y - lse), p2 = expf(v.z - lse), p3 = expf(v.w - lse);
+        const int b = c * 4;
+        if (lab == b) p0 -= 1.f;
+        if (lab == b + 1) p1 -= 1.f;
+        if (lab == b + 2) p2 -= 1.f;
+        if (lab == b + 3) p3 -= 1.f;
+        d2[c] = make_uint2(pack2(p0 * inv_T, p1 * inv_T), pack2(p2 * inv_T, p3 * inv_T));
+    }
+}
+
+__global__ __launch_bounds__(256) void mean_reduce_k(const float* __restrict__ x, float* out, int n) {
+    __shared__ float sh[256];
+    float s = 0.f;
+    for (int i = threadIdx.x; i < n; i += 256) s += x[i];
+    sh[threadIdx.x] = s;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if (threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) out[0] = sh[0] / float(n);
+}
+
+__global__ void f32_to_bf16_k(const float4* __restrict__ x, uint2* __restrict__ y, int64_t n4) {
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= n4) return;
+    const float4 v = x[i];
+    y[i] = make_uint2(pack2(v.x, v.y), pack2(v.z, v.w));
+}
+
+__global__ void fill_zero_k(uint4* __restrict__ p, int64_t n16) {
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < n16) p[i] = make_uint4(0, 0, 0, 0);
+}
+
+inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+inline unsigned blocks(int64_t n, int b) { return unsigned((n + b - 1) / b); }
+
+}  // namespace
+
+hipError_t rmsnorm_fwd(const uint16_t* x, const uint16_t* gamma, uint16_t* n, float* rstd, int T,
+                       int d, float eps, hipStream_t s) {
+    if (T < 0 || d <= 0 || (d & 7) || !al16(x) || !al16(gamma) || !al16(n)) return hipErrorInvalidValue;
+    if (T == 0) return hipSuccess;
+    rmsnorm_fwd_k<<<blocks(T, 4), 256, 0, s>>>(reinterpret_cast<const uint4*>(x),
+                                               reinterpret_cast<const uint4*>(gamma),
+                                               reinterpret_cast<uint4*>(n), rstd, T, d, eps);
+    return hipGetLastError();
+}
+
+int64_t rmsnorm_bwd_partial_elems(int T, int d) {
+    const int64_t waves = (int64_t(T) + RPW - 1) / RPW;
+    return ((waves + 3) / 4) * 4 * int64_t(d);
+}
+
+hipError_t rmsnorm_bwd(const uint16_t* dn, const uint16_t* x, const uint16_t* gamma,
+                       const float* rstd, const uint16_t* resid, uint16_t* dx, uint16_t* dgamma,
+                       float* partial, int T, int d, hipStream_t s) {
+    if (T <= 0 || d <= 0 || (d & 7) || d > 8192) return hipErrorInvalidValue;
+    if (!al16(dn) || !al16(x) || !al16(gamma) || !al16(dx) || (resid && !al16(resid)))
+        return hipErrorInvalidValue;
+    const int64_t waves = (int64_t(T) + RPW - 1) / RPW;
+    const unsigned nb = unsigned((waves + 3) / 4);
+    const int ncl = ((d >> 3) + 63) / 64;
+    auto U = [](const uint16_t* p) { return reinterpret_cast<const uint4*>(p); };
+    uint4* dxv = reinterpret_cast<uint4*>(dx);
+#define MT_RB(N)                                                                               \
+    rmsnorm_bwd_k<N><<<nb, 256, 0, s>>>(U(dn), U(x), U(gamma), rstd, resid ? U(resid) : nullptr, \
+                                        dxv, partial, T, d)
+    if (ncl <= 1) MT_RB(1);
+    else if (ncl <= 2) MT_RB(2);
+    else if (ncl <= 4) MT_RB(4);
+    else if (ncl <= 8) MT_RB(8);
+    else MT_RB(16);
+#undef MT_RB
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dgamma_reduce_k<<<blocks(d, 256), 256, 0, s>>>(partial, int(nb) * 4, d, dgamma);
+    return hipGetLastError();
+}
+
+hipError_t rope_table(float2* tab, int S, int hd, float base, hipStream_t s) {
+    if (S <= 0 || hd <= 0 || (hd & 15)) return hipErrorInvalidValue;
+    const int half = hd / 2;
+    rope_table_k<<<blocks(int64_t(S) * half, 256), 256, 0, s>>>(tab, S, half, hd, double(base));
+    return hipGetLastError();
+}
+
+hipError_t rope_apply(uint16_t* qkv, int64_t ld, const float2* tab, int T, int S, int nh, int hd,
+                      int dir, hipStream_t s) {
+    if (T < 0 || S <= 0 || nh <= 0 || (hd & 15) || (ld & 7) || !al16(qkv)) return hipErrorInvalidValue;
+    if (T == 0) return hipSuccess;
+    const int64_t n = int64_t(T) * nh * (hd / 16);
+    rope_apply_k<<<blocks(n, 256), 256, 0, s>>>(qkv, ld, tab, T, S, nh, hd, dir);
+    return hipGetLastError();
+}
+
+hipError_t swiglu_fwd(const uint16_t* gu, uint16_t* m, int T, int F, hipStream_t s) {
+    if (T < 0 || F <= 0 || (F & 7) || !al16(gu) || !al16(m)) return hipErrorInvalidValue;
+    if (T == 0) return hipSuccess;
+    swiglu_fwd_k<<<blocks(int64_t(T) * (F / 8), 256), 256, 0, s>>>(
+        reinterpret_cast<const uint4*>(gu), reinterpret_cast<uint4*>(m), T, F);
+    return hipGetLastError();
+}
+
+hipError_t swiglu_bwd(const uint16_t* dm, const uint16_t* gu, uint16_t* dgu, int T, int F,
+                      hipStream_t s) {
+    if (T < 0 || F <= 0 || (F & 7) || !al16(gu) || !al16(dm) || !al16(dgu)) return hipErrorInvalidValue;
+    if (T == 0) return hipSuccess;
+    swiglu_bwd_k<<<blocks(int64_t(T) * (F / 8), 256), 256, 0, s>>>(
+        reinterpret_cast<const uint4*>(dm), reinterpret_cast<const uint4*>(gu),
+        reinterpret_cast<uint4*>(dgu), T, F);
+    return hipGetLastError();
+}
+
+hipError_t ce_fwd_bwd(const float* logits, const int32_t* labels, float* loss_rows,
+                      uint16_t* dlogits, int Tc, int V, float inv_T, hipStream_t s) {
+    if (Tc < 0 || V <= 0 || (V & 7) || !al16(logits) || !al16(dlogits)) return hipErrorInvalidValue;
+    if (Tc == 0) return hipSuccess;
+    ce_k<<<Tc, 256, 0, s>>>(logits, labels, loss_rows, dlogits, V, inv_T);
+    return hipGetLastError();
+}
+
+hipError_t mean_reduce(const float* x, float* out, int n, hipStream_t s) {
+    if (n <= 0) return hipErrorInvalidValue;
+    mean_reduce_k<<<1, 256, 0, s>>>(x, out, n);
+    return hipGetLastError();
+}
+
+hipError_t f32_to_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t s) {
+    if (n < 0 || (n & 3) || !al16(x)) return hipErrorInvalidValue;
+    if (n == 0) return hipSuccess;
+    f32_to_bf16_k<<<blocks(n / 4, 256), 256, 0, s>>>(reinterpret_cast<const float4*>(x),
+                                                     reinterpret_cast<uint2*>(y), n / 4);
+    return hipGetLastError();
+}
+
+hipError_t fill_zero(void* p, int64_t bytes, hipStream_t s) {
+    if (bytes < 0 || (bytes & 15) || !al16(p)) return hipErrorInvalidValue;
+    if (bytes == 0) return hipSuccess;
+    fill_zero_k<<<blocks(bytes / 16, 256), 256, 0, s>>>(reinterpret_cast<uint4*>(p), bytes / 16);
+    return hipGetLastError();
+}
+
+}  // namespace mt

@@ -1,0 +1,1282 @@
+// The layer-streamed training step.
+//
+// Pages cited:
+//   [Review]  MegaTrain review, dimensionstp.github.io/study-concept/megatrain/
+//   [Hotdry]  MegaTrain checkpoint strategy and communication overlap, blog.hotdry.top
+//   [Lilting] MegaTrain article, lilting.ch
+//   [Peter]   MegaTrain translated abstract and technical details, peter-blog.pages.dev
+//   [Argon]   "Training 100B models on a single GPU ...", argonsys.com
+//
+// A step is a sequence of visits: forward of layers 0..L-1, the LM head
+// (forward and backward fused), then backward of layers L-1..0, each
+// backward visit first recomputing its layer's forward from the stored layer
+// input ([Review] 3-2 item 2; [Argon] "Block-Wise Recomputation", here with
+// a checkpoint interval of one layer).  Each visit binds a unit's weights:
+//   pack   host thread copies the unit's BF16 W from the pageable store into
+//          one of two pinned staging buffers ([Review] 3-2 item 4, JIT packing);
+//   H2D    weight stream copies staging -> a GPU weight slot after that slot
+//          is released, and records Weights-Ready ([Hotdry] "事件驱动同步协议");
+//   Bind   compute stream waits Weights-Ready and binds tensor views of the
+//          slot to the stateless layer template ([Lilting] "Stateless Layer
+//          Templates"; [Peter] stateless template section);
+//   G out  backward writes BF16 gradients into a gradient buffer and records
+//          Backward-Done; the gradient stream copies them into a free pinned
+//          slab and records Buffer-Free, and a host thread waits on the slab,
+//          unpacks it into the store and runs Adam for that unit ([Hotdry]
+//          K=12 slab pool and background CPU thread).
+// With two slots the H2D of visit i+1 overlaps the compute of visit i and the
+// D2H of visit i-1 ([Review] 3-2 item 3; [Peter] "管線雙緩衝執行引擎").
+// Layer inputs are checkpointed to pinned host memory on the gradient stream,
+// which is idle in forward, and copied back with the weights in backward.
+#include "engine.h"
+
+#include <chrono>
+#include <cstdlib>
+#include <cstring>
+#include <sys/mman.h>
+
+namespace mt {
+
+const char* site_name(int s) {
+    static const char* names[N_SITES] = {
+        "rms1_fwd", "gemm_qkv", "rope_fwd", "attn_fwd", "gemm_o", "rms2_fwd", "gemm_gateup",
+        "swiglu_fwd", "gemm_down",
+        "gemm_down_dx", "gemm_down_dw", "swiglu_bwd", "gemm_gateup_dx", "gemm_gateup_dw",
+        "rms2_bwd", "gemm_o_dx", "gemm_o_dw", "attn_bwd", "rope_bwd", "gemm_qkv_dx",
+        "gemm_qkv_dw", "rms1_bwd",
+        "head_rms_fwd", "head_logits", "head_ce", "head_dx", "head_dw", "head_rms_bwd",
+        "head_misc"};
+    return (s >= 0 && s < N_SITES) ? names[s] : nullptr;
+}
+
+LayerView bind_layer(const Layout& lay, void* base) {
+    const UnitLayout& u = lay.units[0];
+    uint16_t* b = static_cast<uint16_t*>(base);
+    return LayerView{b + u.t[T_G1].off, b + u.t[T_WQ].off, b + u.t[T_WO].off,
+                     b + u.t[T_G2].off, b + u.t[T_WG].off, b + u.t[T_WD].off};
+}
+HeadView bind_head(const Layout& lay, void* base) {
+    const UnitLayout& u = lay.units[lay.head()];
+    uint16_t* b = static_cast<uint16_t*>(base);
+    return HeadView{b + u.t[T_GF].off, b + u.t[T_EOUT].off};
+}
+
+namespace {
+
+using Clock = std::chrono::steady_clock;
+double ms_since(Clock::time_point t0) {
+    return std::chrono::duration<double, std::milli>(Clock::now() - t0).count();
+}
+uint64_t al256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+uint64_t al4k(uint64_t x) { return (x + 4095) & ~uint64_t(4095); }
+
+struct Ev {
+    hipEvent_t e = nullptr;
+    bool rec = false;
+};
+
+// Device arena plan; with base == nullptr only sizes are computed.
+struct ArenaPlan {
+    uint64_t slot_bytes = 0, total = 0;
+    int n_slots = 2, n_garea = 2;
+    std::vector<uint64_t> wslot, garea, resident;  // offsets
+    uint64_t ws_off = 0;
+};
+
+struct Carver {
+    uint64_t off = 0;
+    uint8_t* base = nullptr;
+    template <class T>
+    T* take(uint64_t bytes) {
+        const uint64_t o = off;
+        off = al256(off + bytes);
+        return base ? reinterpret_cast<T*>(base + o) : nullptr;
+    }
+};
+
+int64_t head_chunk_of(const mt_options& o, int64_t T) {
+    int64_t c = o.head_chunk > 0 ? o.head_chunk : std::min<int64_t>(T, 8192);
+    return std::max<int64_t>(1, std::min<int64_t>(c, T));
+}
+
+void plan_workspace(const Layout& lay, const mt_options& o, Carver& cv, Workspace& ws) {
+    const mt_shape& sh = lay.sh;
+    const int64_t T = int64_t(o.max_batch) * o.max_seq;
+    const int64_t d = sh.d_model, F = sh.ffn_dim, V = sh.vocab;
+    const int64_t nq = int64_t(sh.n_heads) * sh.head_dim;
+    const int64_t nqkv = int64_t(sh.n_heads + 2 * sh.n_kv_heads) * sh.head_dim;
+    const uint64_t td = uint64_t(T) * d * 2;
+    ws.maxT = T;
+    if (o.ckpt_on_host) {
+        ws.x[0] = cv.take<uint16_t>(td);
+        ws.x[1] = cv.take<uint16_t>(td);
+        ws.xc[0] = cv.take<uint16_t>(td);
+        ws.xc[1] = cv.take<uint16_t>(td);
+    } else {
+        ws.ckpt_dev = cv.take<uint16_t>(td * uint64_t(sh.n_layers + 1));
+    }
+    ws.n1 = cv.take<uint16_t>(td);
+    ws.h1 = cv.take<uint16_t>(td);
+    ws.n2 = cv.take<uint16_t>(td);
+    ws.qkv = cv.take<uint16_t>(uint64_t(T) * nqkv * 2);
+    ws.dqkv = cv.take<uint16_t>(uint64_t(T) * nqkv * 2);
+    ws.o = cv.take<uint16_t>(uint64_t(T) * nq * 2);
+    ws.dout = cv.take<uint16_t>(uint64_t(T) * nq * 2);
+    ws.gu = cv.take<uint16_t>(uint64_t(T) * 2 * F * 2);
+    ws.dgu = cv.take<uint16_t>(uint64_t(T) * 2 * F * 2);
+    ws.m = cv.take<uint16_t>(uint64_t(T) * F * 2);
+    ws.dm = cv.take<uint16_t>(uint64_t(T) * F * 2);
+    ws.dy[0] = cv.take<uint16_t>(td);
+    ws.dy[1] = cv.take<uint16_t>(td);
+    ws.dn = cv.take<uint16_t>(td);
+    ws.dh1 = cv.take<uint16_t>(td);
+    ws.rstd1 = cv.take<float>(uint64_t(T) * 4);
+    ws.rstd2 = cv.take<float>(uint64_t(T) * 4);
+    ws.lse = cv.take<float>(uint64_t(T) * sh.n_heads * 4);
+    ws.dsum = cv.take<float>(uint64_t(T) * sh.n_heads * 4);
+    ws.partial = cv.take<float>(uint64_t(rmsnorm_bwd_partial_elems(int(T), int(d))) * 4);
+    ws.rope_tab = cv.take<float2>(uint64_t(o.max_seq) * (sh.head_dim / 2) * 8);
+    ws.labels = cv.take<int32_t>(uint64_t(T) * 4);
+    const int64_t tc = head_chunk_of(o, T);
+    ws.head_chunk = tc;
+    ws.nf = cv.take<uint16_t>(td);
+    ws.dnf = cv.take<uint16_t>(td);
+    ws.rstdf = cv.take<float>(uint64_t(T) * 4);
+    ws.logits = cv.take<float>(uint64_t(tc) * V * 4);
+    ws.dlogits = cv.take<uint16_t>(uint64_t(tc) * V * 2);
+    ws.deout_acc = tc < T ? cv.take<float>(uint64_t(V) * d * 4) : nullptr;
+    ws.loss_rows = cv.take<float>(uint64_t(T) * 4);
+    ws.loss = cv.take<float>(256);
+}
+
+ArenaPlan plan_arena(const Layout& lay, const mt_options& o, uint8_t* base, Workspace* ws) {
+    ArenaPlan p;
+    p.slot_bytes = o.slot_bytes_override ? al4k(o.slot_bytes_override)
+                                         : al4k(uint64_t(lay.max_stream_elems) * 2);
+    p.n_slots = o.n_weight_slots;
+    const bool combined = o.slot_mode == 1;
+    p.n_garea = combined ? p.n_slots : 2;
+    Carver cv;
+    cv.base = base;
+    for (int s = 0; s < p.n_slots; ++s) {
+        p.wslot.push_back(cv.off);
+        cv.take<uint8_t>(p.slot_bytes);
+        if (combined) {
+            p.garea.push_back(cv.off);
+            cv.take<uint8_t>(p.slot_bytes);
+        }
+    }
+    if (!combined)
+        for (int g = 0; g < 2; ++g) {
+            p.garea.push_back(cv.off);
+            cv.take<uint8_t>(p.slot_bytes);
+        }
+    if (o.resident)
+        for (int u = 0; u <= lay.head(); ++u) {
+            p.resident.push_back(cv.off);
+            cv.take<uint8_t>(al4k(uint64_t(lay.units[u].elems) * 2));
+        }
+    p.ws_off = cv.off;
+    Workspace tmp;
+    Workspace& w = ws ? *ws : tmp;
+    if (o.workspace_bytes_override) {
+        Carver probe;
+        plan_workspace(lay, o, probe, tmp);
+        const uint64_t need = probe.off;
+        plan_workspace(lay, o, cv, w);
+        cv.off = p.ws_off + std::max<uint64_t>(need, o.workspace_bytes_override);
+    } else {
+        plan_workspace(lay, o, cv, w);
+    }
+    w.bytes = cv.off - p.ws_off;
+    p.total = cv.off;
+    return p;
+}
+
+struct PinnedPlan {
+    uint64_t staging = 0, slab = 0, ckpt = 0, io = 0, total = 0;
+};
+PinnedPlan plan_pinned(const Layout& lay, const mt_options& o, uint64_t slot_bytes) {
+    PinnedPlan p;
+    const uint64_t T = uint64_t(o.max_batch) * o.max_seq;
+    p.staging = o.pin_store ? 0 : 2 * slot_bytes;
+    p.slab = uint64_t(o.n_grad_slabs) * slot_bytes;
+    p.ckpt = o.ckpt_on_host ? al4k(T * lay.sh.d_model * 2) * lay.sh.n_layers : 0;
+    p.io = 2 * al4k(T * lay.sh.d_model * 2) + al4k(T * 4) + 4096;
+    p.total = p.staging + p.slab + p.ckpt + p.io;
+    return p;
+}
+
+int validate_options(const mt_options* o) {
+    if (!o) MT_FAIL(MT_E_INVAL, "options are NULL");
+    if (o->max_batch < 1 || o->max_seq < 1) MT_FAIL(MT_E_INVAL, "max_batch and max_seq must be >= 1");
+    if (int64_t(o->max_batch) * o->max_seq > (int64_t(1) << 30)) MT_FAIL(MT_E_INVAL, "max_batch*max_seq too large");
+    if (o->n_weight_slots < 1 || o->n_weight_slots > 4) MT_FAIL(MT_E_INVAL, "n_weight_slots must be 1..4");
+    if (o->n_grad_slabs < 1 || o->n_grad_slabs > 64) MT_FAIL(MT_E_INVAL, "n_grad_slabs must be 1..64");
+    if (o->slot_mode != 0 && o->slot_mode != 1) MT_FAIL(MT_E_INVAL, "slot_mode must be 0 or 1");
+    if (o->head_chunk < 0) MT_FAIL(MT_E_INVAL, "head_chunk must be >= 0");
+    if (!(o->lr >= 0.f) || !(o->beta1 >= 0.f && o->beta1 < 1.f) || !(o->beta2 >= 0.f && o->beta2 < 1.f) ||
+        !(o->adam_eps > 0.f))
+        MT_FAIL(MT_E_INVAL, "bad Adam hyper-parameters");
+    return MT_OK;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------
+struct Ctx {
+    Layout lay;
+    mt_options opt{};
+    ArenaPlan plan;
+    PinnedPlan pplan;
+    Workspace ws;
+    uint8_t* arena = nullptr;
+    uint64_t arena_bytes = 0;
+    // host
+    uint8_t* store = nullptr;
+    bool store_pinned = false;
+    uint8_t* staging[2] = {};
+    std::vector<uint8_t*> slabs;
+    uint8_t* ckpt_host = nullptr;
+    uint16_t *x0_pin = nullptr, *dx0_pin = nullptr;
+    int32_t* lab_pin = nullptr;
+    float* loss_pin = nullptr;
+    std::vector<uint8_t*> pinned_blocks;
+    std::vector<float> ein_acc;        // fp32 scatter accumulator [V x d]
+    std::vector<int32_t> ein_touched;  // rows with a non-zero gradient last step
+    // streams and events
+    hipStream_t st_c = nullptr, st_w = nullptr, st_g = nullptr;
+    bool own[3] = {false, false, false};
+    std::vector<Ev> wready, slot_free, bwd_done, buf_free, slab_done;
+    Ev staging_free[2], xc_free[2], ckpt_done[2], xready, emb_ready, fwd_ckpt_all, dx0_done, loss_done,
+        res_ready;
+    std::vector<hipEvent_t> tev;  // timing events
+    size_t tev_next = 0;
+    // host threads
+    std::unique_ptr<ThreadPool> pack_pool, adam_pool;
+    std::thread slab_thread;
+    std::mutex q_mu;
+    std::condition_variable q_cv, free_cv;
+    struct Job {
+        int unit, slab;
+        int64_t elems;
+    };
+    std::deque<Job> jobs;
+    std::vector<int> free_slabs;
+    bool stop = false;
+    int jobs_pending = 0;
+    int worker_status = MT_OK;
+    std::string worker_error;
+    double adam_ms_acc = 0.0, pack_ms = 0.0;
+    AdamStep cur_adam{};
+    // schedule state
+    std::vector<int> slot_unit;
+    int slot_ptr = 0, staging_ptr = 0;
+    int cached_rope_S = -1;
+    int64_t step = 0;
+    bool failed = false;
+    // fault injection (host side): "pack:<unit>" or "slab:<unit>"
+    int fault_pack = -1, fault_slab = -1;
+    // timing records
+    struct Interval {
+        hipEvent_t a, b;
+        int kind;  // 0 compute, 1 h2d, 2 d2h
+        uint64_t bytes;
+    };
+    std::vector<Interval> intervals;
+    struct SiteRec {
+        int site;
+        hipEvent_t a, b;
+    };
+    std::vector<SiteRec> site_recs;
+    hipEvent_t t_base = nullptr;
+    bool timing = true;
+
+    ~Ctx();
+    int init(const mt_shape& sh, const mt_options& o, void* arena, uint64_t bytes, void* const streams[3]);
+    int train_step(const int32_t* tokens, const int32_t* labels, int B, int S, float* loss, mt_stats* stats);
+    int layer_fwd(int layer, const void* x, void* y, int B, int S);
+    int layer_bwd(int layer, const void* x, const void* dy, void* dx, void* gtile, int B, int S);
+
+    // helpers
+    hipError_t rec(Ev& e, hipStream_t s) {
+        e.rec = true;
+        return hipEventRecord(e.e, s);
+    }
+    hipError_t wait(hipStream_t s, const Ev& e) { return e.rec ? hipStreamWaitEvent(s, e.e, 0) : hipSuccess; }
+    hipError_t hsync(const Ev& e) { return e.rec ? hipEventSynchronize(e.e) : hipSuccess; }
+    hipEvent_t next_tev() {
+        if (tev_next == tev.size()) {
+            hipEvent_t e;
+            if (hipEventCreate(&e) != hipSuccess) return nullptr;
+            tev.push_back(e);
+        }
+        return tev[tev_next++];
+    }
+    hipError_t h2d(void* dst, const void* src, uint64_t bytes, hipStream_t s) {
+        hipEvent_t a = timing ? next_tev() : nullptr, b = timing ? next_tev() : nullptr;
+        if (a) hipEventRecord(a, s);
+        hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, s);
+        if (b) hipEventRecord(b, s);
+        if (a && b) intervals.push_back({a, b, 1, bytes});
+        return e;
+    }
+    hipError_t d2h(void* dst, const void* src, uint64_t bytes, hipStream_t s) {
+        hipEvent_t a = timing ? next_tev() : nullptr, b = timing ? next_tev() : nullptr;
+        if (a) hipEventRecord(a, s);
+        hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, s);
+        if (b) hipEventRecord(b, s);
+        if (a && b) intervals.push_back({a, b, 2, bytes});
+        return e;
+    }
+    // kernel sites
+    template <class F>
+    hipError_t site(int id, F&& f) {
+        if (!opt.profile_kernels) return f();
+        hipEvent_t a = next_tev(), b = next_tev();
+        hipEventRecord(a, st_c);
+        hipError_t e = f();
+        hipEventRecord(b, st_c);
+        site_recs.push_back({id, a, b});
+        return e;
+    }
+    hipError_t fwd_layer(const LayerView& w, const uint16_t* x, uint16_t* y, int B, int S, bool need_y);
+    hipError_t bwd_layer(const LayerView& w, const LayerView& g, const uint16_t* x, const uint16_t* dy,
+                         uint16_t* dx, int B, int S);
+    hipError_t head(const HeadView& w, const HeadView& g, const uint16_t* xL, uint16_t* dy, int B, int S);
+    hipError_t ensure_rope(int S);
+    int pick_slot(int unit, bool* need_stream);
+    int stream_unit(int unit, int slot);
+    void slab_worker();
+    int acquire_slab();
+    void enqueue_job(int unit, int slab);
+    int drain_jobs();
+    int hip_fail(hipError_t e, const char* what) {
+        failed = true;
+        set_error(strfmt("HIP error '%s' in %s", hipGetErrorString(e), what));
+        return MT_E_HIP;
+    }
+};
+
+#define HIPC(expr)                                              \
+    do {                                                        \
+        hipError_t e_ = (expr);                                 \
+        if (e_ != hipSuccess) return hip_fail(e_, #expr);       \
+    } while (0)
+#define HIPR(expr)                                              \
+    do {                                                        \
+        hipError_t e_ = (expr);                                 \
+        if (e_ != hipSuccess) return e_;                        \
+    } while (0)
+
+// ---------------------------------------------------------------- init ----
+static uint8_t* pinned_alloc(Ctx* c, uint64_t bytes) {
+    if (bytes == 0) return nullptr;
+    void* p = nullptr;
+    if (hipHostMalloc(&p, bytes, hipHostMallocDefault) != hipSuccess || !p) return nullptr;
+    c->pinned_blocks.push_back(static_cast<uint8_t*>(p));
+    return static_cast<uint8_t*>(p);
+}
+
+int Ctx::init(const mt_shape& sh, const mt_options& o, void* arena_, uint64_t bytes,
+              void* const streams[3]) {
+    opt = o;
+    lay = make_layout(sh);
+    plan = plan_arena(lay, opt, nullptr, nullptr);
+    if (!arena_) MT_FAIL(MT_E_INVAL, "gpu_arena is NULL");
+    if (reinterpret_cast<uintptr_t>(arena_) & 255) MT_FAIL(MT_E_INVAL, "gpu_arena must be 256-byte aligned");
+    if (bytes < plan.total)
+        MT_FAIL(MT_E_NOMEM, "gpu arena of %llu bytes is smaller than the %llu needed",
+                (unsigned long long)bytes, (unsigned long long)plan.total);
+    if (plan.slot_bytes < uint64_t(lay.max_stream_elems) * 2)
+        MT_FAIL(MT_E_INVAL, "slot_bytes_override is below the largest unit (%lld bytes)",
+                (long long)(lay.max_stream_elems * 2));
+    arena = static_cast<uint8_t*>(arena_);
+    arena_bytes = bytes;
+    plan = plan_arena(lay, opt, arena, &ws);
+    pplan = plan_pinned(lay, opt, plan.slot_bytes);
+
+    if (const char* f = getenv("MT_FAULT")) {
+        if (!strncmp(f, "pack:", 5)) fault_pack = atoi(f + 5);
+        if (!strncmp(f, "slab:", 5)) fault_slab = atoi(f + 5);
+    }
+
+    // Host threads.
+    int nth = opt.host_threads > 0 ? opt.host_threads : int(std::thread::hardware_concurrency());
+    nth = std::max(1, nth);
+    const int npack = std::max(1, nth / 4);
+    pack_pool.reset(new ThreadPool(npack));
+    adam_pool.reset(new ThreadPool(std::max(1, nth - npack)));
+
+    // Host master store: pageable, huge pages where the kernel allows.
+    if (opt.pin_store) {
+        void* p = nullptr;
+        if (hipHostMalloc(&p, lay.store_bytes, hipHostMallocDefault) != hipSuccess || !p)
+            MT_FAIL(MT_E_NOMEM, "cannot allocate a pinned host store of %lld bytes", (long long)lay.store_bytes);
+        store = static_cast<uint8_t*>(p);
+        store_pinned = true;
+    } else {
+        void* p = mmap(nullptr, lay.store_bytes, PROT_READ | PROT_WRITE, MAP_PRIVATE | MAP_ANONYMOUS, -1, 0);
+        if (p == MAP_FAILED) MT_FAIL(MT_E_NOMEM, "cannot map a host store of %lld bytes", (long long)lay.store_bytes);
+        madvise(p, lay.store_bytes, MADV_HUGEPAGE);
+        store = static_cast<uint8_t*>(p);
+    }
+    {
+        ThreadPool init_pool(nth);
+        for (int u = 0; u < int(lay.units.size()); ++u) init_unit(init_pool, store, lay, u, opt.seed, opt.init_std);
+    }
+    ein_acc.assign(size_t(sh.vocab) * sh.d_model, 0.f);
+
+    // Pinned staging, slabs, checkpoint ring, I/O buffers.
+    if (!opt.pin_store) {
+        staging[0] = pinned_alloc(this, plan.slot_bytes);
+        staging[1] = pinned_alloc(this, plan.slot_bytes);
+        if (!staging[0] || !staging[1]) MT_FAIL(MT_E_NOMEM, "cannot allocate pinned staging buffers");
+    }
+    for (int k = 0; k < opt.n_grad_slabs; ++k) {
+        uint8_t* p = pinned_alloc(this, plan.slot_bytes);
+        if (!p) MT_FAIL(MT_E_NOMEM, "cannot allocate pinned gradient slab %d", k);
+        slabs.push_back(p);
+        free_slabs.push_back(k);
+    }
+    const uint64_t T = uint64_t(opt.max_batch) * opt.max_seq;
+    const uint64_t td = al4k(T * sh.d_model * 2);
+    if (opt.ckpt_on_host) {
+        ckpt_host = pinned_alloc(this, td * sh.n_layers);
+        if (!ckpt_host) MT_FAIL(MT_E_NOMEM, "cannot allocate the pinned checkpoint ring");
+    }
+    x0_pin = reinterpret_cast<uint16_t*>(pinned_alloc(this, td));
+    dx0_pin = reinterpret_cast<uint16_t*>(pinned_alloc(this, td));
+    lab_pin = reinterpret_cast<int32_t*>(pinned_alloc(this, al4k(T * 4)));
+    loss_pin = reinterpret_cast<float*>(pinned_alloc(this, 4096));
+    if (!x0_pin || !dx0_pin || !lab_pin || !loss_pin) MT_FAIL(MT_E_NOMEM, "cannot allocate pinned I/O buffers");
+
+    // Streams: the caller's, else our own (default priority, non-blocking).
+    hipStream_t* dst[3] = {&st_c, &st_w, &st_g};
+    for (int i = 0; i < 3; ++i) {
+        if (streams && streams[i]) {
+            *dst[i] = static_cast<hipStream_t>(streams[i]);
+        } else {
+            HIPC(hipStreamCreateWithFlags(dst[i], hipStreamNonBlocking));
+            own[i] = true;
+        }
+    }
+    auto mk = [&](Ev& e) { return hipEventCreateWithFlags(&e.e, hipEventDisableTiming); };
+    wready.resize(plan.n_slots);
+    slot_free.resize(plan.n_slots);
+    bwd_done.resize(plan.n_garea);
+    buf_free.resize(plan.n_garea);
+    slab_done.resize(opt.n_grad_slabs);
+    for (auto* v : {&wready, &slot_free, &bwd_done, &buf_free, &slab_done})
+        for (auto& e : *v) HIPC(mk(e));
+    for (Ev* e : {&staging_free[0], &staging_free[1], &xc_free[0], &xc_free[1], &ckpt_done[0], &ckpt_done[1],
+                  &xready, &emb_ready, &fwd_ckpt_all, &dx0_done, &loss_done, &res_ready})
+        HIPC(mk(*e));
+    HIPC(hipEventCreate(&t_base));
+    for (int i = 0; i < 1024; ++i) {
+        hipEvent_t e;
+        HIPC(hipEventCreate(&e));
+        tev.push_back(e);
+    }
+    slot_unit.assign(plan.n_slots, -1);
+
+    // Gradient areas: tensors never write their padding, so zero it once.
+    for (int g = 0; g < plan.n_garea; ++g) HIPC(fill_zero(arena + plan.garea[g], plan.slot_bytes, st_c));
+    HIPC(hipStreamSynchronize(st_c));
+    slab_thread = std::thread([this] { slab_worker(); });
+    return MT_OK;
+}
+
+Ctx::~Ctx() {
+    if (st_c) hipStreamSynchronize(st_c);
+    if (st_w) hipStreamSynchronize(st_w);
+    if (st_g) hipStreamSynchronize(st_g);
+    {
+        std::lock_guard<std::mutex> lk(q_mu);
+        stop = true;
+    }
+    q_cv.notify_all();
+    if (slab_thread.joinable()) slab_thread.join();
+    for (auto* v : {&wready, &slot_free, &bwd_done, &buf_free, &slab_done})
+        for (auto& e : *v)
+            if (e.e) hipEventDestroy(e.e);
+    for (Ev* e : {&staging_free[0], &staging_free[1], &xc_free[0], &xc_free[1], &ckpt_done[0], &ckpt_done[1],
+                  &xready, &emb_ready, &fwd_ckpt_all, &dx0_done, &loss_done, &res_ready})
+        if (e->e) hipEventDestroy(e->e);
+    for (auto e : tev) hipEventDestroy(e);
+    if (t_base) hipEventDestroy(t_base);
+    for (int i = 0; i < 3; ++i) {
+        hipStream_t s = i == 0 ? st_c : i == 1 ? st_w : st_g;
+        if (own[i] && s) hipStreamDestroy(s);
+    }
+    for (auto* p : pinned_blocks) hipHostFree(p);
+    if (store) {
+        if (store_pinned) hipHostFree(store);
+        else munmap(store, lay.store_bytes);
+    }
+}
+
+// ------------------------------------------------------- slab worker ----
+void Ctx::slab_worker() {
+    for (;;) {
+        Job j;
+        {
+            std::unique_lock<std::mutex> lk(q_mu);
+            q_cv.wait(lk, [&] { return stop || !jobs.empty(); });
+            if (jobs.empty()) return;
+            j = jobs.front();
+            jobs.pop_front();
+        }
+        int status = MT_OK;
+        std::string err;
+        hipError_t e = hipEventSynchronize(slab_done[j.slab].e);
+        if (e != hipSuccess) {
+            status = MT_E_HIP;
+            err = strfmt("HIP error '%s' waiting for gradient slab %d", hipGetErrorString(e), j.slab);
+        } else if (j.unit == fault_slab) {
+            status = MT_E_INTERNAL;
+            err = strfmt("injected slab-worker fault at unit %d", j.unit);
+        } else {
+            const auto t0 = Clock::now();
+            adam_unit(*adam_pool, tile_ptrs(store, lay, j.unit),
+                      reinterpret_cast<const uint16_t*>(slabs[j.slab]), j.elems, cur_adam);
+            const double ms = ms_since(t0);
+            std::lock_guard<std::mutex> lk(q_mu);
+            adam_ms_acc += ms;
+        }
+        {
+            std::lock_guard<std::mutex> lk(q_mu);
+            if (status != MT_OK && worker_status == MT_OK) {
+                worker_status = status;
+                worker_error = err;
+            }
+            free_slabs.push_back(j.slab);
+            --jobs_pending;
+        }
+        free_cv.notify_all();
+    }
+}
+
+int Ctx::acquire_slab() {
+    std::unique_lock<std::mutex> lk(q_mu);
+    free_cv.wait(lk, [&] { return !free_slabs.empty(); });
+    // Lowest index first keeps the slab order deterministic.
+    auto it = std::min_element(free_slabs.begin(), free_slabs.end());
+    const int k = *it;
+    free_slabs.erase(it);
+    return k;
+}
+
+void Ctx::enqueue_job(int unit, int slab) {
+    {
+        std::lock_guard<std::mutex> lk(q_mu);
+        jobs.push_back({unit, slab, lay.units[unit].elems});
+        ++jobs_pending;
+    }
+    q_cv.notify_one();
+}
+
+int Ctx::drain_jobs() {
+    std::unique_lock<std::mutex> lk(q_mu);
+    free_cv.wait(lk, [&] { return jobs_pending == 0; });
+    if (worker_status != MT_OK) {
+        failed = true;
+        set_error(worker_error);
+        const int s = worker_status;
+        worker_status = MT_OK;
+        return s;
+    }
+    return MT_OK;
+}
+
+// ------------------------------------------------------ layer template ----
+hipError_t Ctx::ensure_rope(int S) {
+    if (S == cached_rope_S) return hipSuccess;
+    cached_rope_S = S;
+    return rope_table(ws.rope_tab, S, lay.sh.head_dim, lay.sh.rope_base, st_c);
+}
+
+// Forward of one decoder layer on the compute stream.  With need_y false
+// (the recompute before backward) the last GEMM is skipped: backward needs
+// the intermediates, not the output.
+hipError_t Ctx::fwd_layer(const LayerView& w, const uint16_t* x, uint16_t* y, int B, int S, bool need_y) {
+    const mt_shape& sh = lay.sh;
+    const int T = B * S, d = sh.d_model, F = sh.ffn_dim;
+    const int nq = sh.n_heads * sh.head_dim;
+    const int nqkv = (sh.n_heads + 2 * sh.n_kv_heads) * sh.head_dim;
+    hipStream_t s = st_c;
+    HIPR(site(S_RMS1_FWD, [&] { return rmsnorm_fwd(x, w.g1, ws.n1, ws.rstd1, T, d, sh.rms_eps, s); }));
+    HIPR(site(S_GEMM_QKV, [&] {
+        GemmArgs a{ws.n1, d, w.wqkv, d, ws.qkv, nqkv, nullptr, 0, nullptr, 0, T, nqkv, d};
+        return gemm(GEMM_NT, EPI_BF16, a, s);
+    }));
+    HIPR(site(S_ROPE_FWD, [&] {
+        return rope_apply(ws.qkv, nqkv, ws.rope_tab, T, S, sh.n_heads + sh.n_kv_heads, sh.head_dim, +1, s);
+    }));
+    HIPR(site(S_ATTN_FWD, [&] {
+        AttnArgs a{ws.qkv, nqkv, ws.o, nq, ws.lse, B, S, sh.n_heads, sh.n_kv_heads, sh.head_dim};
+        return attn_fwd(a, s);
+    }));
+    HIPR(site(S_GEMM_O, [&] {
+        GemmArgs a{ws.o, nq, w.wo, nq, ws.h1, d, x, d, nullptr, 0, T, d, nq};
+        return gemm(GEMM_NT, EPI_BF16_RESID, a, s);
+    }));
+    HIPR(site(S_RMS2_FWD, [&] { return rmsnorm_fwd(ws.h1, w.g2, ws.n2, ws.rstd2, T, d, sh.rms_eps, s); }));
+    HIPR(site(S_GEMM_GATEUP, [&] {
+        GemmArgs a{ws.n2, d, w.wgu, d, ws.gu, 2 * F, nullptr, 0, nullptr, 0, T, 2 * F, d};
+        return gemm(GEMM_NT, EPI_BF16, a, s);
+    }));
+    HIPR(site(S_SWIGLU_FWD, [&] { return swiglu_fwd(ws.gu, ws.m, T, F, s); }));
+    if (need_y) {
+        HIPR(site(S_GEMM_DOWN, [&] {
+            GemmArgs a{ws.m, F, w.wd, F, y, d, ws.h1, d, nullptr, 0, T, d, F};
+            return gemm(GEMM_NT, EPI_BF16_RESID, a, s);
+        }));
+    }
+    return hipSuccess;
+}
+
+// Recompute, then backward of one decoder layer; writes dx and the layer's
+// BF16 gradients into the views g.
+hipError_t Ctx::bwd_layer(const LayerView& w, const LayerView& g, const uint16_t* x, const uint16_t* dy,
+                          uint16_t* dx, int B, int S) {
+    HIPR(fwd_layer(w, x, nullptr, B, S, false));
+    const mt_shape& sh = lay.sh;
+    const int T = B * S, d = sh.d_model, F = sh.ffn_dim;
+    const int nq = sh.n_heads * sh.head_dim;
+    const int nqkv = (sh.n_heads + 2 * sh.n_kv_heads) * sh.head_dim;
+    hipStream_t s = st_c;
+    // MLP
+    HIPR(site(S_GEMM_DOWN_DX, [&] {
+        GemmArgs a{dy, d, w.wd, F, ws.dm, F, nullptr, 0, nullptr, 0, T, F, d};
+        return gemm(GEMM_NN, EPI_BF16, a, s);
+    }));
+    HIPR(site(S_GEMM_DOWN_DW, [&] {
+        GemmArgs a{dy, d, ws.m, F, g.wd, F, nullptr, 0, nullptr, 0, d, F, T};
+        return gemm(GEMM_TN, EPI_BF16, a, s);
+    }));
+    HIPR(site(S_SWIGLU_BWD, [&] { return swiglu_bwd(ws.dm, ws.gu, ws.dgu, T, F, s); }));
+    HIPR(site(S_GEMM_GATEUP_DX, [&] {
+        GemmArgs a{ws.dgu, 2 * F, w.wgu, d, ws.dn, d, nullptr, 0, nullptr, 0, T, d, 2 * F};
+        return gemm(GEMM_NN, EPI_BF16, a, s);
+    }));
+    HIPR(site(S_GEMM_GATEUP_DW, [&] {
+        GemmArgs a{ws.dgu, 2 * F, ws.n2, d, g.wgu, d, nullptr, 0, nullptr, 0, 2 * F, d, T};
+        return gemm(GEMM_TN, EPI_BF16, a, s);
+    }));
+    HIPR(site(S_RMS2_BWD, [&] {
+        return rmsnorm_bwd(ws.dn, ws.h1, w.g2, ws.rstd2, dy, ws.dh1, g.g2, ws.partial, T, d, s);
+    }));
+    // attention
+    HIPR(site(S_GEMM_O_DX, [&] {
+        GemmArgs a{ws.dh1, d, w.wo, nq, ws.dout, nq, nullptr, 0, nullptr, 0, T, nq, d};
+        return gemm(GEMM_NN, EPI_BF16, a, s);
+    }));
+    HIPR(site(S_GEMM_O_DW, [&] {
+        GemmArgs a{ws.dh1, d, ws.o, nq, g.wo, nq, nullptr, 0, nullptr, 0, d, nq, T};
+        return gemm(GEMM_TN, EPI_BF16, a, s);
+    }));
+    HIPR(site(S_ATTN_BWD, [&] {
+        AttnBwdArgs a{ws.qkv, nqkv, ws.o, ws.dout, nq, ws.lse, ws.dsum, ws.dqkv, nqkv,
+                      B, S, sh.n_heads, sh.n_kv_heads, sh.head_dim};
+        return attn_bwd(a, s);
+    }));
+    HIPR(site(S_ROPE_BWD, [&] {
+        return rope_apply(ws.dqkv, nqkv, ws.rope_tab, T, S, sh.n_heads + sh.n_kv_heads, sh.head_dim, -1, s);
+    }));
+    HIPR(site(S_GEMM_QKV_DX, [&] {
+        GemmArgs a{ws.dqkv, nqkv, w.wqkv, d, ws.dn, d, nullptr, 0, nullptr, 0, T, d, nqkv};
+        return gemm(GEMM_NN, EPI_BF16, a, s);
+    }));
+    HIPR(site(S_GEMM_QKV_DW, [&] {
+        GemmArgs a{ws.dqkv, nqkv, ws.n1, d, g.wqkv, d, nullptr, 0, nullptr, 0, nqkv, d, T};
+        return gemm(GEMM_TN, EPI_BF16, a, s);
+    }));
+    HIPR(site(S_RMS1_BWD, [&] {
+        return rmsnorm_bwd(ws.dn, x, w.g1, ws.rstd1, ws.dh1, dx, g.g1, ws.partial, T, d, s);
+    }));
+    return hipSuccess;
+}
+
+// LM head, forward and backward fused over token chunks; writes dy (the
+// gradient of the last layer's output) and the head gradients into g.
+hipError_t Ctx::head(const HeadView& w, const HeadView& g, const uint16_t* xL, uint16_t* dy, int B, int S) {
+    const mt_shape& sh = lay.sh;
+    const int T = B * S, d = sh.d_model, V = sh.vocab;
+    hipStream_t s = st_c;
+    const int tc = int(std::min<int64_t>(ws.head_chunk, T));
+    const int nch = (T + tc - 1) / tc;
+    HIPR(site(S_HEAD_RMS_FWD, [&] { return rmsnorm_fwd(xL, w.gf, ws.nf, ws.rstdf, T, d, sh.rms_eps, s); }));
+    for (int c = 0; c < nch; ++c) {
+        const int r0 = c * tc, rows = std::min(tc, T - r0);
+        HIPR(site(S_HEAD_LOGITS, [&] {
+            GemmArgs a{ws.nf + int64_t(r0) * d, d, w.eout, d, ws.logits, V, nullptr, 0, nullptr, 0, rows, V, d};
+            return gemm(GEMM_NT, EPI_F32, a, s);
+        }));
+        HIPR(site(S_HEAD_CE, [&] {
+            return ce_fwd_bwd(ws.logits, ws.labels + r0, ws.loss_rows + r0, ws.dlogits, rows, V, 1.0f / float(T), s);
+        }));
+        HIPR(site(S_HEAD_DX, [&] {
+            GemmArgs a{ws.dlogits, V, w.eout, d, ws.dnf + int64_t(r0) * d, d, nullptr, 0, nullptr, 0, rows, d, V};
+            return gemm(GEMM_NN, EPI_BF16, a, s);
+        }));
+        HIPR(site(S_HEAD_DW, [&] {
+            GemmArgs a{ws.dlogits, V, ws.nf + int64_t(r0) * d, d, nullptr, d, nullptr, 0, nullptr, 0, V, d, rows};
+            GemmEpi epi;
+            if (nch == 1) { a.C = g.eout; epi = EPI_BF16; }
+            else if (c == 0) { a.C = ws.deout_acc; epi = EPI_F32; }
+            else if (c + 1 < nch) { a.C = ws.deout_acc; epi = EPI_F32_ACC; }
+            else { a.C = g.eout; a.Cacc = ws.deout_acc; a.ldacc = d; epi = EPI_BF16_ACCF32; }
+            return gemm(GEMM_TN, epi, a, s);
+        }));
+    }
+    HIPR(site(S_HEAD_RMS_BWD, [&] {
+        return rmsnorm_bwd(ws.dnf, xL, w.gf, ws.rstdf, nullptr, dy, g.gf, ws.partial, T, d, s);
+    }));
+    HIPR(site(S_HEAD_MISC, [&] { return mean_reduce(ws.loss_rows, ws.loss, T, s); }));
+    return hipSuccess;
+}
+
+// ------------------------------------------------------------ streaming ----
+int Ctx::pick_slot(int unit, bool* need_stream) {
+    for (int s = 0; s < plan.n_slots; ++s)
+        if (slot_unit[s] == unit) {
+            *need_stream = false;
+            slot_ptr = (s + 1) % plan.n_slots;
+            return s;
+        }
+    const int s = slot_ptr;
+    slot_ptr = (s + 1) % plan.n_slots;
+    *need_stream = true;
+    return s;
+}
+
+// Pack unit -> pinned staging (host), then H2D staging -> slot on the weight
+// stream once the slot is released.
+int Ctx::stream_unit(int unit, int slot) {
+    const uint64_t bytes = uint64_t(lay.units[unit].elems) * 2;
+    const uint8_t* src = store + lay.tile_off[unit];
+    if (unit == fault_pack) {
+        failed = true;
+        MT_FAIL(MT_E_INTERNAL, "injected pack fault at unit %d", unit);
+    }
+    HIPC(wait(st_w, slot_free[slot]));
+    if (store_pinned) {
+        HIPC(h2d(arena + plan.wslot[slot], src, bytes, st_w));
+    } else {
+        const int p = staging_ptr;
+        staging_ptr ^= 1;
+        HIPC(hsync(staging_free[p]));
+        const auto t0 = Clock::now();
+        parallel_copy(*pack_pool, staging[p], src, int64_t(bytes));
+        pack_ms += ms_since(t0);
+        HIPC(h2d(arena + plan.wslot[slot], staging[p], bytes, st_w));
+        HIPC(rec(staging_free[p], st_w));
+    }
+    slot_unit[slot] = unit;
+    return MT_OK;
+}
+
+// ------------------------------------------------------------ the step ----
+int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int B, int S, float* loss_out,
+                    mt_stats* stats) {
+    if (failed) MT_FAIL(MT_E_STATE, "context failed earlier");
+    if (!tokens || !labels || !loss_out) MT_FAIL(MT_E_INVAL, "tokens, labels and loss_out must not be NULL");
+    if (B < 1 || S < 1 || int64_t(B) * S > ws.maxT || S > opt.max_seq)
+        MT_FAIL(MT_E_INVAL, "batch %d x seq %d exceeds the workspace (max_batch*max_seq = %lld, max_seq = %d)",
+                B, S, (long long)ws.maxT, opt.max_seq);
+    const mt_shape& sh = lay.sh;
+    const int T = B * S, L = sh.n_layers, d = sh.d_model, V = sh.vocab;
+    for (int t = 0; t < T; ++t)
+        if (tokens[t] < 0 || tokens[t] >= V || labels[t] < 0 || labels[t] >= V)
+            MT_FAIL(MT_E_INVAL, "token or label at row %d outside [0, %d)", t, V);
+
+    const auto t_start = Clock::now();
+    tev_next = 0;
+    intervals.clear();
+    site_recs.clear();
+    adam_ms_acc = 0.0;
+    pack_ms = 0.0;
+    cur_adam = adam_step_params(opt, step + 1);
+    timing = true;
+    const uint64_t td = uint64_t(T) * d * 2;
+    const uint64_t td_al = al4k(uint64_t(ws.maxT) * d * 2);
+    HIPC(hipEventRecord(t_base, st_c));
+
+    // Labels and the embedding gather (host, exact) go up on the weight stream.
+    memcpy(lab_pin, labels, size_t(T) * 4);
+    HIPC(h2d(ws.labels, lab_pin, uint64_t(T) * 4, st_w));
+    {
+        const TilePtrs e = tile_ptrs(store, lay, lay.embed());
+        pack_pool->parallel_for(T, 64, [&](int64_t b, int64_t en) {
+            for (int64_t t = b; t < en; ++t)
+                memcpy(x0_pin + t * d, e.w + int64_t(tokens[t]) * d, size_t(d) * 2);
+        });
+    }
+    uint16_t* x_first = opt.ckpt_on_host ? ws.x[0] : ws.ckpt_dev;
+    HIPC(h2d(x_first, x0_pin, td, st_w));
+    HIPC(rec(emb_ready, st_w));
+    HIPC(ensure_rope(S));
+    if (opt.resident) {
+        // The comparison run: every unit's weights copied up once, no streaming.
+        for (int u = 0; u <= lay.head(); ++u) {
+            const uint64_t bytes = uint64_t(lay.units[u].elems) * 2;
+            HIPC(h2d(arena + plan.resident[u], store + lay.tile_off[u], bytes, st_w));
+        }
+    }
+
+    // Visits: forward 0..L-1, head, backward L-1..0.
+    const int nvis = 2 * L + 1;
+    int gnext = 0;
+    const bool combined = opt.slot_mode == 1;
+    double t_fwd = 0, t_head = 0;
+    hipEvent_t ph_fwd_end = nullptr, ph_head_end = nullptr, ph_bwd_end = nullptr;
+    for (int v = 0; v < nvis; ++v) {
+        const int kind = v < L ? 0 : (v == L ? 1 : 2);  // 0 fwd, 1 head, 2 bwd
+        const int unit = kind == 0 ? v : (kind == 1 ? lay.head() : 2 * L - v);
+        // Bind target: a streamed slot or the resident copy.
+        int slot = 0;
+        void* wbase;
+        if (opt.resident) {
+            wbase = arena + plan.resident[unit];
+        } else {
+            bool need = false;
+            slot = pick_slot(unit, &need);
+            if (need) {
+                const int r = stream_unit(unit, slot);
+                if (r != MT_OK) {
+                    drain_jobs();
+                    return r;
+                }
+            }
+            wbase = arena + plan.wslot[slot];
+        }
+        const int vb = v - L - 1;  // backward visit index
+        if (kind == 2 && opt.ckpt_on_host) {
+            if (vb == 0) HIPC(wait(st_w, fwd_ckpt_all));
+            HIPC(wait(st_w, xc_free[vb & 1]));
+            HIPC(h2d(ws.xc[vb & 1], ckpt_host + uint64_t(unit) * td_al, td, st_w));
+        }
+        Ev& wr = wready[slot];
+        HIPC(rec(wr, st_w));
+        HIPC(wait(st_c, wr));
+        hipEvent_t va = next_tev(), vz = next_tev();
+        HIPC(hipEventRecord(va, st_c));
+        if (kind == 0) {
+            const uint16_t* x = opt.ckpt_on_host ? ws.x[unit & 1] : ws.ckpt_dev + uint64_t(unit) * ws.maxT * d;
+            uint16_t* y = opt.ckpt_on_host ? ws.x[(unit + 1) & 1] : ws.ckpt_dev + uint64_t(unit + 1) * ws.maxT * d;
+            if (opt.ckpt_on_host) HIPC(wait(st_c, ckpt_done[(unit + 1) & 1]));
+            HIPC(fwd_layer(bind_layer(lay, wbase), x, y, B, S, true));
+            HIPC(hipEventRecord(vz, st_c));
+            intervals.push_back({va, vz, 0, 0});
+            HIPC(rec(slot_free[slot], st_c));
+            if (opt.ckpt_on_host) {
+                // Checkpoint the layer input on the gradient stream (idle in forward).
+                HIPC(wait(st_g, unit == 0 ? emb_ready : xready));
+                HIPC(d2h(ckpt_host + uint64_t(unit) * td_al, x, td, st_g));
+                HIPC(rec(ckpt_done[unit & 1], st_g));
+                HIPC(rec(xready, st_c));
+                if (unit == L - 1) HIPC(rec(fwd_ckpt_all, st_g));
+            }
+            if (unit == L - 1) {
+                ph_fwd_end = next_tev();
+                HIPC(hipEventRecord(ph_fwd_end, st_c));
+                t_fwd = ms_since(t_start);
+            }
+            continue;
+        }
+        // Head or backward: gradients go to a gradient area, then to a slab.
+        const int ga = combined ? slot : gnext;
+        if (!combined) gnext ^= 1;
+        HIPC(wait(st_c, buf_free[ga]));
+        void* gbase = arena + plan.garea[ga];
+        if (kind == 1) {
+            const uint16_t* xL = opt.ckpt_on_host ? ws.x[L & 1] : ws.ckpt_dev + uint64_t(L) * ws.maxT * d;
+            HIPC(head(bind_head(lay, wbase), bind_head(lay, gbase), xL, ws.dy[0], B, S));
+            HIPC(hipMemcpyAsync(loss_pin, ws.loss, 4, hipMemcpyDeviceToHost, st_c));
+            HIPC(rec(loss_done, st_c));
+        } else {
+            const uint16_t* x = opt.ckpt_on_host ? ws.xc[vb & 1] : ws.ckpt_dev + uint64_t(unit) * ws.maxT * d;
+            HIPC(bwd_layer(bind_layer(lay, wbase), bind_layer(lay, gbase), x, ws.dy[vb & 1], ws.dy[(vb + 1) & 1], B,
+                           S));
+            if (opt.ckpt_on_host) HIPC(rec(xc_free[vb & 1], st_c));
+        }
+        HIPC(hipEventRecord(vz, st_c));
+        intervals.push_back({va, vz, 0, 0});
+        if (!combined) HIPC(rec(slot_free[slot], st_c));
+        HIPC(rec(bwd_done[ga], st_c));
+        // Gradient offload: Backward-Done -> free slab -> Buffer-Free.
+        const int k = acquire_slab();
+        HIPC(wait(st_g, bwd_done[ga]));
+        HIPC(d2h(slabs[k], gbase, uint64_t(lay.units[unit].elems) * 2, st_g));
+        HIPC(rec(slab_done[k], st_g));
+        HIPC(rec(buf_free[ga], st_g));
+        if (combined) HIPC(rec(slot_free[slot], st_g));
+        enqueue_job(unit, k);
+        if (kind == 1) {
+            ph_head_end = next_tev();
+            HIPC(hipEventRecord(ph_head_end, st_c));
+            t_head = ms_since(t_start);
+        }
+    }
+    ph_bwd_end = next_tev();
+    HIPC(hipEventRecord(ph_bwd_end, st_c));
+    // Embedding backward on the host: dX0 down, scatter-add in token order.
+    const uint16_t* dx0 = ws.dy[L & 1];
+    HIPC(hipStreamWaitEvent(st_g, ph_bwd_end, 0));
+    HIPC(d2h(dx0_pin, dx0, td, st_g));
+    HIPC(rec(dx0_done, st_g));
+    HIPC(hsync(dx0_done));
+    const double t_bwd = ms_since(t_start);
+    {
+        const TilePtrs e = tile_ptrs(store, lay, lay.embed());
+        // Clear last step's rows, then accumulate this step's in fp32.
+        for (int32_t r : ein_touched) memset(e.g + int64_t(r) * d, 0, size_t(d) * 2);
+        std::vector<char> seen(size_t(V), 0);
+        ein_touched.clear();
+        for (int t = 0; t < T; ++t)
+            if (!seen[tokens[t]]) {
+                seen[tokens[t]] = 1;
+                ein_touched.push_back(tokens[t]);
+            }
+        float* acc = ein_acc.data();
+        adam_pool->parallel_for(d, 64, [&](int64_t c0, int64_t c1) {
+            for (int32_t r : ein_touched)
+                for (int64_t c = c0; c < c1; ++c) acc[int64_t(r) * d + c] = 0.f;
+            for (int t = 0; t < T; ++t) {
+                float* row = acc + int64_t(tokens[t]) * d;
+                const uint16_t* g = dx0_pin + int64_t(t) * d;
+                for (int64_t c = c0; c < c1; ++c) row[c] += bf16_to_f32(g[c]);
+            }
+            for (int32_t r : ein_touched)
+                for (int64_t c = c0; c < c1; ++c) e.g[int64_t(r) * d + c] = f32_to_bf16(acc[int64_t(r) * d + c]);
+        });
+        if (lay.embed() == fault_slab) {
+            drain_jobs();
+            failed = true;
+            MT_FAIL(MT_E_INTERNAL, "injected slab-worker fault at unit %d", lay.embed());
+        }
+        const auto t0 = Clock::now();
+        adam_unit(*adam_pool, e, e.g, lay.units[lay.embed()].elems, cur_adam);
+        std::lock_guard<std::mutex> lk(q_mu);
+        adam_ms_acc += ms_since(t0);
+    }
+    const int jr = drain_jobs();
+    HIPC(hsync(loss_done));
+    HIPC(hipStreamSynchronize(st_c));
+    HIPC(hipStreamSynchronize(st_w));
+    HIPC(hipStreamSynchronize(st_g));
+    if (jr != MT_OK) return jr;
+    *loss_out = *loss_pin;
+    ++step;
+    const double t_total = ms_since(t_start);
+
+    if (stats) {
+        memset(stats, 0, sizeof(*stats));
+        stats->step_ms = t_total;
+        auto el = [&](hipEvent_t a, hipEvent_t b) {
+            float ms = 0.f;
+            hipEventElapsedTime(&ms, a, b);
+            return double(ms);
+        };
+        if (ph_fwd_end && ph_head_end) {
+            stats->fwd_ms = el(t_base, ph_fwd_end);
+            stats->head_ms = el(ph_fwd_end, ph_head_end);
+            stats->bwd_ms = el(ph_head_end, ph_bwd_end);
+        }
+        stats->adam_tail_ms = t_total - t_bwd;
+        (void)t_fwd;
+        (void)t_head;
+        // Interval unions: compute C, copies X = H2D u D2H.
+        std::vector<std::pair<double, double>> C, X, H;
+        for (auto& iv : intervals) {
+            const double a = el(t_base, iv.a), b = el(t_base, iv.b);
+            if (iv.kind == 0) {
+                C.push_back({a, b});
+                stats->compute_busy_ms += b - a;
+            } else {
+                X.push_back({a, b});
+                if (iv.kind == 1) {
+                    H.push_back({a, b});
+                    stats->h2d_busy_ms += b - a;
+                    stats->h2d_bytes += iv.bytes;
+                } else {
+                    stats->d2h_busy_ms += b - a;
+                    stats->d2h_bytes += iv.bytes;
+                }
+            }
+        }
+        auto merge = [](std::vector<std::pair<double, double>> v) {
+            std::sort(v.begin(), v.end());
+            std::vector<std::pair<double, double>> out;
+            for (auto& p : v) {
+                if (!out.empty() && p.first <= out.back().second) out.back().second = std::max(out.back().second, p.second);
+                else out.push_back(p);
+            }
+            return out;
+        };
+        auto len = [](const std::vector<std::pair<double, double>>& v) {
+            double s = 0;
+            for (auto& p : v) s += p.second - p.first;
+            return s;
+        };
+        auto Cm = merge(C), Xm = merge(X), Hm = merge(H);
+        double inter = 0;
+        size_t i = 0, j = 0;
+        while (i < Cm.size() && j < Xm.size()) {
+            const double lo = std::max(Cm[i].first, Xm[j].first), hi = std::min(Cm[i].second, Xm[j].second);
+            if (hi > lo) inter += hi - lo;
+            if (Cm[i].second < Xm[j].second) ++i;
+            else ++j;
+        }
+        const double lc = len(Cm), lx = len(Xm);
+        stats->overlap_ratio = std::min(lc, lx) > 0 ? inter / std::min(lc, lx) : 0.0;
+        stats->pcie_busy_frac = t_total > 0 ? len(Hm) / t_total : 0.0;
+        stats->pack_ms = pack_ms;
+        stats->adam_ms = adam_ms_acc;
+        stats->gpu_arena_bytes = plan.total;
+        stats->pinned_bytes = pplan.total;
+        stats->host_store_bytes = uint64_t(lay.store_bytes);
+        if (opt.profile_kernels) {
+            stats->n_sites = N_SITES;
+            for (auto& r : site_recs) {
+                stats->site_ms[r.site] += el(r.a, r.b);
+                stats->site_launches[r.site] += 1;
+            }
+        }
+    }
+    return MT_OK;
+}
+
+// ------------------------------------------------------- test entries ----
+int Ctx::layer_fwd(int layer, const void* x, void* y, int B, int S) {
+    if (failed) MT_FAIL(MT_E_STATE, "context failed earlier");
+    if (layer < 0 || layer >= lay.L()) MT_FAIL(MT_E_INVAL, "layer %d out of range", layer);
+    if (!x || !y) MT_FAIL(MT_E_INVAL, "x and y must not be NULL");
+    if (B < 1 || S < 1 || int64_t(B) * S > ws.maxT || S > opt.max_seq) MT_FAIL(MT_E_INVAL, "batch x seq exceeds the workspace");
+    timing = false;
+    tev_next = 0;
+    HIPC(ensure_rope(S));
+    const int slot = 0;
+    slot_unit.assign(plan.n_slots, -1);
+    const int r = stream_unit(layer, slot);
+    if (r != MT_OK) return r;
+    HIPC(rec(wready[slot], st_w));
+    HIPC(wait(st_c, wready[slot]));
+    HIPC(fwd_layer(bind_layer(lay, arena + plan.wslot[slot]), static_cast<const uint16_t*>(x),
+                   static_cast<uint16_t*>(y), B, S, true));
+    HIPC(rec(slot_free[slot], st_c));
+    HIPC(hipStreamSynchronize(st_c));
+    HIPC(hipStreamSynchronize(st_w));
+    slot_unit.assign(plan.n_slots, -1);
+    return MT_OK;
+}
+
+int Ctx::layer_bwd(int layer, const void* x, const void* dy, void* dx, void* gtile, int B, int S) {
+    if (failed) MT_FAIL(MT_E_STATE, "context failed earlier");
+    if (layer < 0 || layer >= lay.L()) MT_FAIL(MT_E_INVAL, "layer %d out of range", layer);
+    if (!x || !dy || !dx || !gtile) MT_FAIL(MT_E_INVAL, "device pointers must not be NULL");
+    if (reinterpret_cast<uintptr_t>(gtile) & 15) MT_FAIL(MT_E_INVAL, "grad_tile_dev must be 16-byte aligned");
+    if (B < 1 || S < 1 || int64_t(B) * S > ws.maxT || S > opt.max_seq) MT_FAIL(MT_E_INVAL, "batch x seq exceeds the workspace");
+    timing = false;
+    tev_next = 0;
+    HIPC(ensure_rope(S));
+    const int slot = 0;
+    slot_unit.assign(plan.n_slots, -1);
+    const int r = stream_unit(layer, slot);
+    if (r != MT_OK) return r;
+    HIPC(rec(wready[slot], st_w));
+    HIPC(wait(st_c, wready[slot]));
+    HIPC(fill_zero(gtile, (uint64_t(lay.units[layer].elems) * 2 + 15) & ~uint64_t(15), st_c));
+    HIPC(bwd_layer(bind_layer(lay, arena + plan.wslot[slot]), bind_layer(lay, gtile),
+                   static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dy), static_cast<uint16_t*>(dx), B,
+                   S));
+    HIPC(rec(slot_free[slot], st_c));
+    HIPC(hipStreamSynchronize(st_c));
+    HIPC(hipStreamSynchronize(st_w));
+    slot_unit.assign(plan.n_slots, -1);
+    return MT_OK;
+}
+
+}  // namespace mt
+
+// ================================================================ C ABI ====
+using mt::Ctx;
+
+struct mt_ctx {
+    Ctx impl;
+};
+
+extern "C" {
+
+int mt_default_options(mt_options* o) {
+    if (!o) return MT_E_INVAL;
+    memset(o, 0, sizeof(*o));
+    o->max_batch = 1;
+    o->max_seq = 128;
+    o->n_weight_slots = 2;
+    o->n_grad_slabs = 12;
+    o->slot_mode = 0;
+    o->ckpt_on_host = 1;
+    o->resident = 0;
+    o->host_threads = 0;
+    o->head_chunk = 0;
+    o->profile_kernels = 0;
+    o->pin_store = 0;
+    o->lr = 1e-4f;
+    o->beta1 = 0.9f;
+    o->beta2 = 0.999f;
+    o->adam_eps = 1e-8f;
+    o->init_std = 0.02f;
+    o->seed = 1234;
+    return MT_OK;
+}
+
+int mt_workspace_bytes(const mt_shape* sh, const mt_options* o, uint64_t* gpu_arena, uint64_t* pinned,
+                       uint64_t* host_store) {
+    int r = mt::validate_shape(sh);
+    if (r != MT_OK) return r;
+    r = mt::validate_options(o);
+    if (r != MT_OK) return r;
+    const mt::Layout lay = mt::make_layout(*sh);
+    const mt::ArenaPlan p = mt::plan_arena(lay, *o, nullptr, nullptr);
+    const mt::PinnedPlan pp = mt::plan_pinned(lay, *o, p.slot_bytes);
+    if (gpu_arena) *gpu_arena = p.total;
+    if (pinned) *pinned = pp.total;
+    if (host_store) *host_store = uint64_t(lay.store_bytes);
+    return MT_OK;
+}
+
+int mt_init(const mt_shape* sh, const mt_options* o, void* gpu_arena, uint64_t arena_bytes,
+            void* const streams[3], mt_ctx** out) {
+    if (!out) {
+        mt::set_error("out is NULL");
+        return MT_E_INVAL;
+    }
+    *out = nullptr;
+    int r = mt::validate_shape(sh);
+    if (r != MT_OK) return r;
+    r = mt::validate_options(o);
+    if (r != MT_OK) return r;
+    mt_ctx* c = new (std::nothrow) mt_ctx;
+    if (!c) {
+        mt::set_error("out of host memory");
+        return MT_E_NOMEM;
+    }
+    try {
+        r = c->impl.init(*sh, *o, gpu_arena, arena_bytes, streams);
+    } catch (const std::bad_alloc&) {
+        mt::set_error("out of host memory during init");
+        r = MT_E_NOMEM;
+    } catch (...) {
+        mt::set_error("unexpected exception during init");
+        r = MT_E_INTERNAL;
+    }
+    if (r != MT_OK) {
+        delete c;
+        return r;
+    }
+    *out = c;
+    return MT_OK;
+}
+
+int mt_train_step(mt_ctx* c, const int32_t* tokens, const int32_t* labels, int32_t batch, int32_t seq,
+                  float* loss_out, mt_stats* stats) {
+    if (!c) {
+        mt::set_error("ctx is NULL");
+        return MT_E_INVAL;
+    }
+    try {
+        return c->impl.train_step(tokens, labels, batch, seq, loss_out, stats);
+    } catch (...) {
+        c->impl.failed = true;
+        mt::set_error("unexpected exception in mt_train_step");
+        return MT_E_INTERNAL;
+    }
+}
+
+int mt_layer_fwd(mt_ctx* c, int32_t layer, const void* x, void* y, int32_t batch, int32_t seq) {
+    if (!c) {
+        mt::set_error("ctx is NULL");
+        return MT_E_INVAL;
+    }
+    try {
+        return c->impl.layer_fwd(layer, x, y, batch, seq);
+    } catch (...) {
+        c->impl.failed = true;
+        mt::set_error("unexpected exception in mt_layer_fwd");
+        return MT_E_INTERNAL;
+    }
+}
+
+int mt_layer_bwd(mt_ctx* c, int32_t layer, const void* x, const void* dy, void* dx, void* gtile, int32_t batch,
+                 int32_t seq) {
+    if (!c) {
+        mt::set_error("ctx is NULL");
+        return MT_E_INVAL;
+    }
+    try {
+        return c->impl.layer_bwd(layer, x, dy, dx, gtile, batch, seq);
+    } catch (...) {
+        c->impl.failed = true;
+        mt::set_error("unexpected exception in mt_layer_bwd");
+        return MT_E_INTERNAL;
+    }
+}
+
+int mt_get_tensor(mt_ctx* c, int32_t unit, int32_t idx, int32_t which, void* dst, uint64_t bytes) {
+    if (!c || !dst) {
+        mt::set_error("ctx and host_dst must not be NULL");
+        return MT_E_INVAL;
+    }
+    const mt::Layout& lay = c->impl.lay;
+    if (unit < 0 || unit >= int(lay.units.size())) MT_FAIL(MT_E_INVAL, "unit %d out of range", unit);
+    const mt::UnitLayout& u = lay.units[unit];
+    if (idx < 0 || idx >= u.ntensors) MT_FAIL(MT_E_INVAL, "tensor %d out of range", idx);
+    if (which < MT_W || which > MT_V) MT_FAIL(MT_E_INVAL, "bad `which` %d", which);
+    const mt::TensorDesc& t = u.t[idx];
+    const uint64_t n = uint64_t(t.rows * t.cols), es = which <= MT_G ? 2 : 4;
+    if (bytes != n * es) MT_FAIL(MT_E_INVAL, "bytes %llu != %llu", (unsigned long long)bytes, (unsigned long long)(n * es));
+    const mt::TilePtrs p = mt::tile_ptrs(c->impl.store, lay, unit);
+    const void* src = which == MT_W ? static_cast<const void*>(p.w + t.off)
+                    : which == MT_G ? static_cast<const void*>(p.g + t.off)
+                    : which == MT_MASTER ? static_cast<const void*>(p.master + t.off)
+                    : which == MT_M ? static_cast<const void*>(p.m + t.off)
+                                    : static_cast<const void*>(p.v + t.off);
+    memcpy(dst, src, bytes);
+    return MT_OK;
+}
+
+int mt_set_tensor(mt_ctx* c, int32_t unit, int32_t idx, int32_t which, const void* srcp, uint64_t bytes) {
+    if (!c || !srcp) {
+        mt::set_error("ctx and host_src must not be NULL");
+        return MT_E_INVAL;
+    }
+    const mt::Layout& lay = c->impl.lay;
+    if (unit < 0 || unit >= int(lay.units.size())) MT_FAIL(MT_E_INVAL, "unit %d out of range", unit);
+    const mt::UnitLayout& u = lay.units[unit];
+    if (idx < 0 || idx >= u.ntensors) MT_FAIL(MT_E_INVAL, "tensor %d out of range", idx);
+    if (which < MT_W || which > MT_V) MT_FAIL(MT_E_INVAL, "bad `which` %d", which);
+    const mt::TensorDesc& t = u.t[idx];
+    const uint64_t n = uint64_t(t.rows * t.cols), es = which <= MT_G ? 2 : 4;
+    if (bytes != n * es) MT_FAIL(MT_E_INVAL, "bytes %llu != %llu", (unsigned long long)bytes, (unsigned long long)(n * es));
+    const mt::TilePtrs p = mt::tile_ptrs(c->impl.store, lay, unit);
+    void* dst = which == MT_W ? static_cast<void*>(p.w + t.off)
+              : which == MT_G ? static_cast<void*>(p.g + t.off)
+              : which == MT_MASTER ? static_cast<void*>(p.master + t.off)
+              : which == MT_M ? static_cast<void*>(p.m + t.off)
+                              : static_cast<void*>(p.v + t.off);
+    memcpy(dst, srcp, bytes);
+    return MT_OK;
+}
+
+int mt_step_count(mt_ctx* c, int64_t* out) {
+    if (!c || !out) return MT_E_INVAL;
+    *out = c->impl.step;
+    return MT_OK;
+}
+
+void mt_destroy(mt_ctx* c) { delete c; }
+
+}  // extern "C"
+

@@ -1,0 +1,58 @@
+// The streaming engine: context, device arena, streams and events, the
+// visit schedule of a step, the stateless layer template and its Bind.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <deque>
+#include <memory>
+
+#include "host.h"
+#include "kernels.h"
+
+namespace mt {
+
+// Kernel timing sites (profile_kernels).
+enum Site {
+    S_RMS1_FWD, S_GEMM_QKV, S_ROPE_FWD, S_ATTN_FWD, S_GEMM_O, S_RMS2_FWD, S_GEMM_GATEUP,
+    S_SWIGLU_FWD, S_GEMM_DOWN,
+    S_GEMM_DOWN_DX, S_GEMM_DOWN_DW, S_SWIGLU_BWD, S_GEMM_GATEUP_DX, S_GEMM_GATEUP_DW,
+    S_RMS2_BWD, S_GEMM_O_DX, S_GEMM_O_DW, S_ATTN_BWD, S_ROPE_BWD, S_GEMM_QKV_DX,
+    S_GEMM_QKV_DW, S_RMS1_BWD,
+    S_HEAD_RMS_FWD, S_HEAD_LOGITS, S_HEAD_CE, S_HEAD_DX, S_HEAD_DW, S_HEAD_RMS_BWD,
+    S_HEAD_MISC,
+    N_SITES
+};
+const char* site_name(int s);
+
+// Views of one decoder layer's tensors inside a weight slot (or a gradient
+// buffer): the Bind of a stateless template to streamed memory.
+struct LayerView {
+    uint16_t *g1, *wqkv, *wo, *g2, *wgu, *wd;
+};
+struct HeadView {
+    uint16_t *gf, *eout;
+};
+LayerView bind_layer(const Layout& lay, void* base);
+HeadView bind_head(const Layout& lay, void* base);
+
+// Device activations of one layer at the workspace's maximum token count.
+struct Workspace {
+    int64_t maxT = 0;
+    uint16_t *x[2] = {}, *xc[2] = {}, *xL = nullptr;
+    uint16_t* ckpt_dev = nullptr;  // [L+1][maxT x d] when checkpoints stay on the GPU
+    uint16_t *n1, *qkv, *o, *h1, *n2, *gu, *m;
+    float *rstd1, *rstd2, *lse;
+    uint16_t *dy[2], *dm, *dgu, *dn, *dh1, *dout, *dqkv;
+    float *dsum, *partial;
+    float2* rope_tab;
+    int32_t* labels;
+    // head
+    int64_t head_chunk = 0;
+    uint16_t *nf, *dnf, *dlogits;
+    float *rstdf, *logits, *deout_acc, *loss_rows, *loss;
+    uint64_t bytes = 0;
+};
+
+struct Ctx;
+
+}  // namespace mt

@@ -1,0 +1,274 @@
+// bf16 GEMM on gfx950 matrix cores (v_mfma_f32_32x32x16_bf16), fp32
+// accumulation, three operand layouts and five epilogues.
+//
+// The block linear maps of the decoder (fused QKV, O, fused gate|up, down,
+// LM head) and their backward passes are dense contractions, so they run on
+// MFMA.  Design:
+//  * block tile BM x BN with BK = 64, one LDS image per operand holding 64
+//    k-values per row (128 bytes, 8 chunks of 16 bytes); the chunk index is
+//    XOR-swizzled with (row & 7) so eight consecutive rows reading the same
+//    logical chunk hit eight different 16-byte bank groups;
+//  * operands stored k-contiguous ([rows x K]) are copied to LDS as they are;
+//    operands stored row-contiguous ([K x rows], the weight-gradient case)
+//    are transposed in registers, 4 k x 8 rows per thread, on the way in;
+//  * two LDS stages: the global loads of stage k+1 are issued before the
+//    MFMAs of stage k and written to the other LDS image after them, one
+//    barrier per stage;
+//  * blockIdx is remapped so that the tiles one XCD (every 8th block) runs
+//    are a contiguous range, then grouped 8 tiles deep along M, so tiles
+//    sharing A rows or B columns share that XCD's L2.
+#include "kcommon.h"
+#include "kernels.h"
+
+namespace mt {
+namespace {
+
+constexpr int BK = 64;
+
+__device__ __forceinline__ uint32_t half_of(const uint4& v, int e) {
+    uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
+    return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
+}
+
+// Tile loader for one operand: R rows of the tile (M or N side), 64 k.
+template <int R, int NT, bool KMAJOR>
+struct TileLoader {
+    // k-contiguous: R*8 chunks of 8 k; row-contiguous: 2R blocks of 4 k x 8 rows.
+    static constexpr int NCH = KMAJOR ? (R * 8) / NT : (2 * R) / NT;
+    static constexpr int NREG = KMAJOR ? NCH : NCH * 4;
+    static_assert(NCH >= 1, "tile too small for the thread count");
+    uint4 reg[NREG];
+
+    __device__ __forceinline__ void load(const uint16_t* __restrict__ base, int64_t ld, int row0,
+                                         int rows, int k0, int K, int tid) {
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        if constexpr (KMAJOR) {
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                int c = tid + i * NT;
+                int r = c >> 3, kc = c & 7;
+                int gr = row0 + r, gk = k0 + kc * 8;
+                reg[i] = (gr < rows && gk < K)
+                             ? *reinterpret_cast<const uint4*>(base + int64_t(gr) * ld + gk)
+                             : z;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                int c = tid + i * NT;
+                int mg = c % (R / 8), kg = c / (R / 8);
+                int gm = row0 + mg * 8;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    int gk = k0 + kg * 4 + j;
+                    reg[i * 4 + j] = (gk < K && gm < rows)
+                                         ? *reinterpret_cast<const uint4*>(base + int64_t(gk) * ld + gm)
+                                         : z;
+                }
+            }
+        }
+    }
+
+    // Write the registers into LDS image `lds` ([R][8] uint4, swizzled).
+    __device__ __forceinline__ void store(uint4* __restrict__ lds, int tid) const {
+        if constexpr (KMAJOR) {
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                int c = tid + i * NT;
+                int r = c >> 3, kc = c & 7;
+                lds[r * 8 + (kc ^ (r & 7))] = reg[i];
+            }
+        } else {
+            uint2* l2 = reinterpret_cast<uint2*>(lds);
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                int c = tid + i * NT;
+                int mg = c % (R / 8), kg = c / (R / 8);
+                int kc = kg >> 1, hf = kg & 1;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    int r = mg * 8 + e;
+                    uint2 v;
+                    v.x = half_of(reg[i * 4 + 0], e) | (half_of(reg[i * 4 + 1], e) << 16);
+                    v.y = half_of(reg[i * 4 + 2], e) | (half_of(reg[i * 4 + 3], e) << 16);
+                    l2[(r * 8 + (kc ^ (r & 7))) * 2 + hf] = v;
+                }
+            }
+        }
+    }
+};
+
+template <int BM, int BN, int WM, int WN, bool AK, bool BKM, int EPI>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs p, int tiles_m, int tiles_n) {
+    constexpr int NT = WM * WN * 64;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    static_assert(FM >= 1 && FN >= 1, "wave tile below 32x32");
+    __shared__ uint4 smem[2 * (BM + BN) * 8];
+    uint4* As = smem;
+    uint4* Bs = smem + 2 * BM * 8;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+
+    // XCD-aware remap, then group 8 tiles along M.
+    const int total = tiles_m * tiles_n;
+    int pid = blockIdx.x;
+    if ((total & 7) == 0) pid = (pid & 7) * (total >> 3) + (pid >> 3);
+    constexpr int GROUP = 8;
+    const int per_group = GROUP * tiles_n;
+    const int g = pid / per_group;
+    const int first_m = g * GROUP;
+    const int gsz = min(tiles_m - first_m, GROUP);
+    const int tm = first_m + (pid % per_group) % gsz;
+    const int tn = (pid % per_group) / gsz;
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const uint16_t* A = static_cast<const uint16_t*>(p.A);
+    const uint16_t* B = static_cast<const uint16_t*>(p.B);
+
+    TileLoader<BM, NT, AK> la;
+    TileLoader<BN, NT, BKM> lb;
+
+    f32x16_t acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int nk = (p.K + BK - 1) / BK;
+    la.load(A, p.lda, m0, p.M, 0, p.K, tid);
+    lb.load(B, p.ldb, n0, p.N, 0, p.K, tid);
+    la.store(As, tid);
+    lb.store(Bs, tid);
+    __syncthreads();
+
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        const bool more = kt + 1 < nk;
+        if (more) {
+            la.load(A, p.lda, m0, p.M, (kt + 1) * BK, p.K, tid);
+            lb.load(B, p.ldb, n0, p.N, (kt + 1) * BK, p.K, tid);
+        }
+        const uint4* a_l = As + cur * BM * 8;
+        const uint4* b_l = Bs + cur * BN * 8;
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            const int kc = ks * 2 + (lane >> 5);
+            bf16x8_t af[FM], bfr[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                int r = wm * TM + i * 32 + (lane & 31);
+                af[i] = as_bf16x8(a_l[r * 8 + (kc ^ (r & 7))]);
+            }
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                int r = wn * TN + j * 32 + (lane & 31);
+                bfr[j] = as_bf16x8(b_l[r * 8 + (kc ^ (r & 7))]);
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+        if (more) {
+            la.store(As + (cur ^ 1) * BM * 8, tid);
+            lb.store(Bs + (cur ^ 1) * BN * 8, tid);
+        }
+        __syncthreads();
+    }
+
+    // Epilogue.  Accumulator element r of lane l sits at row
+    // 8*(r/4) + 4*(l/32) + r%4 and column l%32 of its 32x32 tile.
+    const int col_l = lane & 31;
+    const int row_l = (lane >> 5) * 4;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int col = n0 + wn * TN + j * 32 + col_l;
+            if (col >= p.N) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm * TM + i * 32 + (r >> 2) * 8 + row_l + (r & 3);
+                if (row >= p.M) continue;
+                float v = acc[i][j][r];
+                if constexpr (EPI == EPI_BF16) {
+                    static_cast<uint16_t*>(p.C)[int64_t(row) * p.ldc + col] = f2bf(v);
+                } else if constexpr (EPI == EPI_BF16_RESID) {
+                    v += bf2f(static_cast<const uint16_t*>(p.R)[int64_t(row) * p.ldr + col]);
+                    static_cast<uint16_t*>(p.C)[int64_t(row) * p.ldc + col] = f2bf(v);
+                } else if constexpr (EPI == EPI_F32) {
+                    static_cast<float*>(p.C)[int64_t(row) * p.ldc + col] = v;
+                } else if constexpr (EPI == EPI_F32_ACC) {
+                    float* c = static_cast<float*>(p.C) + int64_t(row) * p.ldc + col;
+                    *c = *c + v;
+                } else {
+                    v += p.Cacc[int64_t(row) * p.ldacc + col];
+                    static_cast<uint16_t*>(p.C)[int64_t(row) * p.ldc + col] = f2bf(v);
+                }
+            }
+        }
+    }
+}
+
+template <int BM, int BN, int WM, int WN, bool AK, bool BKM>
+hipError_t launch_epi(GemmEpi epi, const GemmArgs& a, hipStream_t s) {
+    const int tm = (a.M + BM - 1) / BM, tn = (a.N + BN - 1) / BN;
+    dim3 grid(tm * tn), block(WM * WN * 64);
+    switch (epi) {
+        case EPI_BF16:
+            gemm_kernel<BM, BN, WM, WN, AK, BKM, EPI_BF16><<<grid, block, 0, s>>>(a, tm, tn); break;
+        case EPI_BF16_RESID:
+            gemm_kernel<BM, BN, WM, WN, AK, BKM, EPI_BF16_RESID><<<grid, block, 0, s>>>(a, tm, tn); break;
+        case EPI_F32:
+            gemm_kernel<BM, BN, WM, WN, AK, BKM, EPI_F32><<<grid, block, 0, s>>>(a, tm, tn); break;
+        case EPI_F32_ACC:
+            gemm_kernel<BM, BN, WM, WN, AK, BKM, EPI_F32_ACC><<<grid, block, 0, s>>>(a, tm, tn); break;
+        case EPI_BF16_ACCF32:
+            gemm_kernel<BM, BN, WM, WN, AK, BKM, EPI_BF16_ACCF32><<<grid, block, 0, s>>>(a, tm, tn); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <bool AK, bool BKM>
+hipError_t launch_layout(GemmEpi epi, const GemmArgs& a, hipStream_t s) {
+    // Large problems: 256x256 tiles, 8 waves of 128x64.  Small ones (fewer
+    // than ~2 tiles per CU): 128x128 tiles, 4 waves of 64x64.
+    const int64_t big_tiles = int64_t((a.M + 255) / 256) * ((a.N + 255) / 256);
+    if (big_tiles >= 512) return launch_epi<256, 256, 2, 4, AK, BKM>(epi, a, s);
+    return launch_epi<128, 128, 2, 2, AK, BKM>(epi, a, s);
+}
+
+}  // namespace
+
+hipError_t gemm(GemmLayout lay, GemmEpi epi, const GemmArgs& a, hipStream_t s) {
+    if (a.M <= 0 || a.N <= 0 || a.K <= 0) return hipErrorInvalidValue;
+    if (!a.A || !a.B || !a.C) return hipErrorInvalidValue;
+    // 16-byte vector loads: the contiguous dimension and every leading
+    // dimension must be multiples of 8 elements, base pointers 16-byte aligned.
+    auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+    if (!al16(a.A) || !al16(a.B) || (a.lda & 7) || (a.ldb & 7)) return hipErrorInvalidValue;
+    const bool ak = lay != GEMM_TN, bk = lay == GEMM_NT;
+    if (ak ? (a.K & 7) : (a.M & 7)) return hipErrorInvalidValue;
+    if (bk ? (a.K & 7) : (a.N & 7)) return hipErrorInvalidValue;
+    if (ak ? a.lda < a.K : a.lda < a.M) return hipErrorInvalidValue;
+    if (bk ? a.ldb < a.K : a.ldb < a.N) return hipErrorInvalidValue;
+    if (a.ldc < a.N) return hipErrorInvalidValue;
+    if (epi == EPI_BF16_RESID && (!a.R || a.ldr < a.N)) return hipErrorInvalidValue;
+    if (epi == EPI_BF16_ACCF32 && (!a.Cacc || a.ldacc < a.N)) return hipErrorInvalidValue;
+    switch (lay) {
+        case GEMM_NT: return launch_layout<true, true>(epi, a, s);
+        case GEMM_NN: return launch_layout<true, false>(epi, a, s);
+        case GEMM_TN: return launch_layout<false, false>(epi, a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace mt

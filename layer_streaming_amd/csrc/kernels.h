@@ -1,0 +1,93 @@
+// Host-side launchers of the gfx950 kernels.  Every launcher checks the
+// shapes it relies on, enqueues on `stream` and returns hipSuccess or the
+// error of the launch; hipErrorInvalidValue means a shape the kernel does not
+// support (the caller maps it to MT_E_INVAL before any device work).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mt {
+
+// ---------------------------------------------------------------- GEMM ----
+// C[M x N] = op(A) op(B) with fp32 accumulation on bf16 MFMA.
+//   NT: A [M x K] row-major (lda), B [N x K] row-major (ldb)  -> X W^T
+//   NN: A [M x K] row-major,       B [K x N] row-major          -> dY W
+//   TN: A [K x M] row-major,       B [K x N] row-major          -> dY^T X
+enum GemmLayout { GEMM_NT = 0, GEMM_NN = 1, GEMM_TN = 2 };
+// Epilogues: what is written to C.
+enum GemmEpi {
+    EPI_BF16 = 0,        // C(bf16) = acc
+    EPI_BF16_RESID = 1,  // C(bf16) = acc + R(bf16)
+    EPI_F32 = 2,         // C(f32)  = acc
+    EPI_F32_ACC = 3,     // C(f32) += acc
+    EPI_BF16_ACCF32 = 4, // C(bf16) = acc + Cacc(f32)
+};
+struct GemmArgs {
+    const void* A; int64_t lda;
+    const void* B; int64_t ldb;
+    void* C; int64_t ldc;
+    const void* R; int64_t ldr;       // residual, EPI_BF16_RESID
+    const float* Cacc; int64_t ldacc; // fp32 partial sum, EPI_BF16_ACCF32
+    int M, N, K;
+};
+hipError_t gemm(GemmLayout lay, GemmEpi epi, const GemmArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------- RMSNorm ----
+// n = gamma * x * rstd, rstd = 1/sqrt(mean(x^2)+eps); x, n, gamma bf16.
+hipError_t rmsnorm_fwd(const uint16_t* x, const uint16_t* gamma, uint16_t* n, float* rstd, int T,
+                       int d, float eps, hipStream_t s);
+// dx = resid + rstd*(g - nh*mean(g*nh)), g = dn*gamma, nh = x*rstd (resid may be null);
+// dgamma = sum_t dn*nh written as bf16 (two-stage, fixed order).  `partial` is
+// fp32 scratch of rmsnorm_bwd_partial_elems(T, d) elements.
+hipError_t rmsnorm_bwd(const uint16_t* dn, const uint16_t* x, const uint16_t* gamma,
+                       const float* rstd, const uint16_t* resid, uint16_t* dx, uint16_t* dgamma,
+                       float* partial, int T, int d, hipStream_t s);
+int64_t rmsnorm_bwd_partial_elems(int T, int d);
+
+// ---------------------------------------------------------------- RoPE ----
+// Table of cos/sin [S x hd/2] (float2), angle s*base^(-2e/hd) in double.
+hipError_t rope_table(float2* tab, int S, int hd, float base, hipStream_t s);
+// Rotate the first n_rot_heads heads of every row of qkv [T x ld] in place,
+// position s = t % S; dir = +1 forward, -1 backward (rotation by -theta).
+hipError_t rope_apply(uint16_t* qkv, int64_t ld, const float2* tab, int T, int S, int n_rot_heads,
+                      int hd, int dir, hipStream_t s);
+
+// -------------------------------------------------------------- SwiGLU ----
+// gu [T x 2F] = [gate | up] -> m [T x F] = silu(gate) * up.
+hipError_t swiglu_fwd(const uint16_t* gu, uint16_t* m, int T, int F, hipStream_t s);
+// dgu [T x 2F] = [dm*up*silu'(gate) | dm*silu(gate)].
+hipError_t swiglu_bwd(const uint16_t* dm, const uint16_t* gu, uint16_t* dgu, int T, int F,
+                      hipStream_t s);
+
+// ----------------------------------------------------------- Attention ----
+// qkv [B*S x ld]: q heads at column 0, k heads at Hq*hd, v heads at (Hq+Hkv)*hd.
+struct AttnArgs {
+    const uint16_t* qkv; int64_t ld;
+    uint16_t* o; int64_t ldo;   // [B*S x Hq*hd]
+    float* lse;                 // [B x Hq x S], natural-log sum-exp of scaled scores
+    int B, S, Hq, Hkv, hd;
+};
+hipError_t attn_fwd(const AttnArgs& a, hipStream_t s);
+struct AttnBwdArgs {
+    const uint16_t* qkv; int64_t ld;
+    const uint16_t* o; const uint16_t* dout; int64_t ldo;
+    const float* lse;
+    float* dsum;                // scratch [B x Hq x S]: rowsum(dO * O)
+    uint16_t* dqkv; int64_t ldd; // output, same column layout as qkv
+    int B, S, Hq, Hkv, hd;
+};
+hipError_t attn_bwd(const AttnBwdArgs& a, hipStream_t s);
+
+// ------------------------------------------------------- Cross-entropy ----
+// logits f32 [Tc x V], labels int32 [Tc] -> loss_rows[Tc] = lse - logit[label],
+// dlogits bf16 [Tc x V] = (softmax - onehot) * inv_T.
+hipError_t ce_fwd_bwd(const float* logits, const int32_t* labels, float* loss_rows,
+                      uint16_t* dlogits, int Tc, int V, float inv_T, hipStream_t s);
+// out[0] = sum(x[0..n)) / n in a fixed order (one block).
+hipError_t mean_reduce(const float* x, float* out, int n, hipStream_t s);
+
+// --------------------------------------------------------------- misc -----
+hipError_t f32_to_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t s);
+hipError_t fill_zero(void* p, int64_t bytes, hipStream_t s);
+
+}  // namespace mt

@@ -1,0 +1,58 @@
+"""Helpers for the GPU parity tests: device buffers of bf16 bit patterns,
+comparison metrics.  Arithmetic of the method lives in oracle/ (reference)
+and libmt.so (under test), never here."""
+import sys
+
+import numpy as np
+
+TOL = 1e-2  # normwise relative error bound on activations, loss and gradients
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def bits_of(x):
+    """bf16 bit patterns of float32 values that are exactly representable."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0), "value not exactly representable in bf16"
+    return (u >> 16).astype(np.uint16)
+
+
+def widen(bits):
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def dev_bits(x_f32):
+    import torch
+    return torch.from_numpy(bits_of(x_f32).view(np.int16)).cuda()
+
+
+def dev_zeros_bits(shape):
+    import torch
+    return torch.zeros(shape, dtype=torch.int16, device="cuda")
+
+
+def host_f32(t):
+    """Device tensor of bf16 bits (int16) -> float32 numpy."""
+    return widen(t.cpu().numpy().view(np.uint16))
+
+
+def rel_err(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref)
+    if den == 0.0:
+        return float(np.linalg.norm(got))
+    return float(np.linalg.norm(got - ref) / den)
+
+
+def assert_close(got, ref, name, tol=TOL):
+    e = rel_err(got, ref)
+    mx = float(np.max(np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64)))) if np.size(ref) else 0.0
+    log(f"  {name}: normwise rel err {e:.3e} (max abs {mx:.3e})")
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    assert e <= tol, f"{name}: normwise relative error {e:.3e} > {tol}"
+    return e

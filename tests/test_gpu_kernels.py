@@ -1,0 +1,236 @@
+"""Kernel-level parity: each gfx950 kernel (through the C ABI test entries)
+against the float64 oracle on the same seeded bf16 inputs, at sizes that span
+several tiles with ragged tails.  Bound: normwise relative error <= 1e-2."""
+import math
+
+import numpy as np
+import pytest
+
+from layer_streaming_amd import synth
+from oracle import block
+from tests.gpu_util import assert_close, dev_bits, dev_zeros_bits, host_f32, log
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from layer_streaming_amd import mt  # noqa: E402
+
+RNG = np.random.default_rng(1234)
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ GEMM --
+GEMM_SHAPES = [(200, 136, 72), (520, 392, 264), (136, 264, 1000), (4096, 8192, 64), (64, 8, 8), (13, 24, 40)]
+
+
+@pytest.mark.parametrize("layout", [0, 1, 2], ids=["NT", "NN", "TN"])
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_gemm_layouts(layout, M, N, K):
+    if layout == 2 and M % 8:
+        pytest.skip("TN reads A row-contiguous along M: M must be a multiple of 8")
+    log(f"gemm layout={layout} M={M} N={N} K={K}")
+    a_shape = (M, K) if layout in (0, 1) else (K, M)
+    b_shape = (N, K) if layout == 0 else (K, N)
+    A = synth.bf16_exact_normal(RNG, a_shape)
+    B = synth.bf16_exact_normal(RNG, b_shape)
+    opA = A if layout in (0, 1) else A.T
+    opB = B.T if layout == 0 else B
+    ref = opA.astype(np.float64) @ opB.astype(np.float64)
+    dA, dB = dev_bits(A), dev_bits(B)
+    dC = dev_zeros_bits((M, N))
+    mt.check(mt.lib.mt_k_gemm(layout, 0, dA.data_ptr(), a_shape[1], dB.data_ptr(), b_shape[1], dC.data_ptr(), N,
+                              None, 0, None, 0, M, N, K, _stream()), "gemm")
+    _sync()
+    assert_close(host_f32(dC), ref, "C")
+
+
+def test_gemm_epilogues():
+    M, N, K = 300, 264, 136
+    log(f"gemm epilogues M={M} N={N} K={K}")
+    A = synth.bf16_exact_normal(RNG, (M, K))
+    B = synth.bf16_exact_normal(RNG, (N, K))
+    R = synth.bf16_exact_normal(RNG, (M, N))
+    ref = A.astype(np.float64) @ B.astype(np.float64).T
+    dA, dB, dR = dev_bits(A), dev_bits(B), dev_bits(R)
+    s = _stream()
+    # residual
+    dC = dev_zeros_bits((M, N))
+    mt.check(mt.lib.mt_k_gemm(0, 1, dA.data_ptr(), K, dB.data_ptr(), K, dC.data_ptr(), N, dR.data_ptr(), N,
+                              None, 0, M, N, K, s))
+    _sync()
+    assert_close(host_f32(dC), ref + R, "C+R")
+    # fp32 out, then fp32 accumulate twice, then bf16 from the fp32 partial
+    c32 = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+    mt.check(mt.lib.mt_k_gemm(0, 2, dA.data_ptr(), K, dB.data_ptr(), K, c32.data_ptr(), N, None, 0, None, 0,
+                              M, N, K, s))
+    _sync()
+    assert_close(c32.cpu().numpy(), ref, "C f32", tol=1e-5)
+    mt.check(mt.lib.mt_k_gemm(0, 3, dA.data_ptr(), K, dB.data_ptr(), K, c32.data_ptr(), N, None, 0, None, 0,
+                              M, N, K, s))
+    _sync()
+    assert_close(c32.cpu().numpy(), 2 * ref, "C f32 += ", tol=1e-5)
+    dC2 = dev_zeros_bits((M, N))
+    mt.check(mt.lib.mt_k_gemm(0, 4, dA.data_ptr(), K, dB.data_ptr(), K, dC2.data_ptr(), N, None, 0,
+                              c32.data_ptr(), N, M, N, K, s))
+    _sync()
+    assert_close(host_f32(dC2), 3 * ref, "C bf16 from f32 partial")
+
+
+def test_gemm_rejects_misaligned_shapes():
+    A = dev_zeros_bits((16, 16))
+    r = mt.lib.mt_k_gemm(0, 0, A.data_ptr(), 12, A.data_ptr(), 16, A.data_ptr(), 16, None, 0, None, 0,
+                         16, 16, 12, _stream())
+    assert r == mt.MT_E_INVAL
+
+
+# --------------------------------------------------------------- RMSNorm --
+@pytest.mark.parametrize("T,d", [(37, 256), (130, 3584), (9, 8192), (1, 64)])
+def test_rmsnorm_fwd_bwd(T, d):
+    log(f"rmsnorm T={T} d={d}")
+    eps = 1e-6
+    x = synth.bf16_exact_normal(RNG, (T, d))
+    g = synth.bf16_exact_normal(RNG, (d,), std=0.2, mean=1.0)
+    dn = synth.bf16_exact_normal(RNG, (T, d))
+    res = synth.bf16_exact_normal(RNG, (T, d))
+    dx_, n_, dg_ = dev_bits(x), dev_zeros_bits((T, d)), dev_zeros_bits((d,))
+    rstd = torch.zeros(T, dtype=torch.float32, device="cuda")
+    dgam, ddn, dres = dev_bits(g), dev_bits(dn), dev_bits(res)
+    s = _stream()
+    mt.check(mt.lib.mt_k_rmsnorm_fwd(dx_.data_ptr(), dgam.data_ptr(), n_.data_ptr(), rstd.data_ptr(), T, d, eps, s))
+    scratch = torch.zeros(int(mt.lib.mt_k_rmsnorm_bwd_scratch_elems(T, d)), dtype=torch.float32, device="cuda")
+    ddx = dev_zeros_bits((T, d))
+    mt.check(mt.lib.mt_k_rmsnorm_bwd(ddn.data_ptr(), dx_.data_ptr(), dgam.data_ptr(), rstd.data_ptr(),
+                                     dres.data_ptr(), ddx.data_ptr(), dg_.data_ptr(), scratch.data_ptr(), T, d, s))
+    _sync()
+    xd = x.astype(np.float64)
+    n_ref, r_ref = block.rmsnorm_fwd(xd, g.astype(np.float64), eps)
+    assert_close(host_f32(n_), n_ref, "n")
+    assert_close(rstd.cpu().numpy(), r_ref, "rstd", tol=1e-5)
+    dx_ref, dg_ref = block.rmsnorm_bwd(dn.astype(np.float64), xd, g.astype(np.float64), r_ref)
+    assert_close(host_f32(ddx), dx_ref + res, "dx")
+    assert_close(host_f32(dg_), dg_ref, "dgamma")
+
+
+# ------------------------------------------------------------------ RoPE --
+@pytest.mark.parametrize("hd", [64, 128])
+def test_rope_fwd_bwd(hd):
+    B, S, hq, hkv = 2, 100, 4, 2
+    log(f"rope hd={hd}")
+    ld = (hq + 2 * hkv) * hd
+    T = B * S
+    qkv = synth.bf16_exact_normal(RNG, (T, ld))
+    dq = dev_bits(qkv)
+    tab = torch.zeros(S * hd // 2 * 2, dtype=torch.float32, device="cuda")
+    mt.check(mt.lib.mt_k_rope(dq.data_ptr(), ld, tab.data_ptr(), T, S, hq + hkv, hd, 10000.0, 1, _stream()))
+    _sync()
+    got = host_f32(dq)
+    rot = qkv[:, :(hq + hkv) * hd].astype(np.float64).reshape(B, S, hq + hkv, hd)
+    ref = block.rope_fwd(rot, 10000.0).reshape(T, -1)
+    assert_close(got[:, :(hq + hkv) * hd], ref, "rope fwd")
+    np.testing.assert_array_equal(got[:, (hq + hkv) * hd:], qkv[:, (hq + hkv) * hd:])
+    dq2 = dev_bits(qkv)
+    mt.check(mt.lib.mt_k_rope(dq2.data_ptr(), ld, tab.data_ptr(), T, S, hq + hkv, hd, 10000.0, -1, _stream()))
+    _sync()
+    ref_b = block.rope_bwd(rot, 10000.0).reshape(T, -1)
+    assert_close(host_f32(dq2)[:, :(hq + hkv) * hd], ref_b, "rope bwd")
+
+
+def test_rope_long_positions():
+    """Angles up to 131071 rad: the table is computed in float64."""
+    B, S, h, hd = 1, 131072, 1, 128
+    log("rope long S=131072")
+    qkv = synth.bf16_exact_normal(RNG, (S, 3 * hd))
+    dq = dev_bits(qkv)
+    tab = torch.zeros(S * hd, dtype=torch.float32, device="cuda")
+    mt.check(mt.lib.mt_k_rope(dq.data_ptr(), 3 * hd, tab.data_ptr(), S, S, 1, hd, 10000.0, 1, _stream()))
+    _sync()
+    got = host_f32(dq)[:, :hd]
+    ref = block.rope_fwd(qkv[:, :hd].astype(np.float64).reshape(1, S, 1, hd), 10000.0).reshape(S, hd)
+    assert_close(got, ref, "rope fwd long")
+
+
+# ---------------------------------------------------------------- SwiGLU --
+@pytest.mark.parametrize("T,F", [(50, 688), (7, 18944)])
+def test_swiglu_fwd_bwd(T, F):
+    log(f"swiglu T={T} F={F}")
+    gu = synth.bf16_exact_normal(RNG, (T, 2 * F), std=2.0)
+    dm = synth.bf16_exact_normal(RNG, (T, F))
+    dgu_, dm_, m_, dgo = dev_bits(gu), dev_bits(dm), dev_zeros_bits((T, F)), dev_zeros_bits((T, 2 * F))
+    s = _stream()
+    mt.check(mt.lib.mt_k_swiglu_fwd(dgu_.data_ptr(), m_.data_ptr(), T, F, s))
+    mt.check(mt.lib.mt_k_swiglu_bwd(dm_.data_ptr(), dgu_.data_ptr(), dgo.data_ptr(), T, F, s))
+    _sync()
+    a, b = gu[:, :F].astype(np.float64), gu[:, F:].astype(np.float64)
+    assert_close(host_f32(m_), block.swiglu_fwd(a, b), "m")
+    da, db = block.swiglu_bwd(dm.astype(np.float64), a, b)
+    got = host_f32(dgo)
+    assert_close(got[:, :F], da, "dgate")
+    assert_close(got[:, F:], db, "dup")
+
+
+# ------------------------------------------------------------- Attention --
+ATTN_CASES = [(2, 200, 4, 2, 64), (1, 300, 7, 1, 128), (2, 128, 4, 4, 128), (1, 1, 2, 1, 64),
+              (1, 65, 2, 2, 128), (1, 1024, 28, 4, 128)]
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,hd", ATTN_CASES)
+def test_attention_fwd_bwd(B, S, Hq, Hkv, hd):
+    log(f"attention B={B} S={S} Hq={Hq} Hkv={Hkv} hd={hd}")
+    T = B * S
+    ld = (Hq + 2 * Hkv) * hd
+    nq = Hq * hd
+    qkv = synth.bf16_exact_normal(RNG, (T, ld))
+    dout = synth.bf16_exact_normal(RNG, (T, nq))
+    d_qkv, d_do = dev_bits(qkv), dev_bits(dout)
+    d_o = dev_zeros_bits((T, nq))
+    lse = torch.zeros(B * Hq * S, dtype=torch.float32, device="cuda")
+    dsum = torch.zeros(B * Hq * S, dtype=torch.float32, device="cuda")
+    d_dqkv = dev_zeros_bits((T, ld))
+    s = _stream()
+    mt.check(mt.lib.mt_k_attn_fwd(d_qkv.data_ptr(), ld, d_o.data_ptr(), nq, lse.data_ptr(), B, S, Hq, Hkv, hd, s))
+    mt.check(mt.lib.mt_k_attn_bwd(d_qkv.data_ptr(), ld, d_o.data_ptr(), d_do.data_ptr(), nq, lse.data_ptr(),
+                                  dsum.data_ptr(), d_dqkv.data_ptr(), ld, B, S, Hq, Hkv, hd, s))
+    _sync()
+    x = qkv.astype(np.float64).reshape(B, S, Hq + 2 * Hkv, hd)
+    q, k, v = x[:, :, :Hq], x[:, :, Hq:Hq + Hkv], x[:, :, Hq + Hkv:]
+    o_ref = block.attention_fwd(q, k, v)
+    o_gpu = host_f32(d_o)
+    assert_close(o_gpu, o_ref.reshape(T, nq), "o")
+    lse_ref = block.attention_lse(q, k)   # [B, Hq, S]
+    assert_close(lse.cpu().numpy().reshape(B, Hq, S), lse_ref, "lse", tol=1e-4)
+    # Backward from the GPU's own (bf16) O, as the kernel sees it.
+    dq, dk, dv = block.attention_bwd(dout.astype(np.float64).reshape(B, S, Hq, hd), q, k, v)
+    g = host_f32(d_dqkv).reshape(B, S, Hq + 2 * Hkv, hd)
+    assert_close(g[:, :, :Hq], dq, "dq")
+    assert_close(g[:, :, Hq:Hq + Hkv], dk, "dk")
+    assert_close(g[:, :, Hq + Hkv:], dv, "dv")
+
+
+# --------------------------------------------------------- Cross-entropy --
+@pytest.mark.parametrize("Tc,V", [(37, 1024), (3, 152064)])
+def test_cross_entropy(Tc, V):
+    log(f"ce Tc={Tc} V={V}")
+    logits = (RNG.standard_normal((Tc, V)) * 2).astype(np.float32)
+    labels = RNG.integers(0, V, size=Tc).astype(np.int32)
+    dl = torch.from_numpy(logits).cuda()
+    dlab = torch.from_numpy(labels).cuda()
+    rows = torch.zeros(Tc, dtype=torch.float32, device="cuda")
+    dlog = dev_zeros_bits((Tc, V))
+    out = torch.zeros(1, dtype=torch.float32, device="cuda")
+    s = _stream()
+    mt.check(mt.lib.mt_k_ce(dl.data_ptr(), dlab.data_ptr(), rows.data_ptr(), dlog.data_ptr(), Tc, V, 1.0 / Tc, s))
+    mt.check(mt.lib.mt_k_mean(rows.data_ptr(), out.data_ptr(), Tc, s))
+    _sync()
+    loss, dref = block.cross_entropy(logits.astype(np.float64), labels)
+    assert abs(out.item() - loss) / abs(loss) < 1e-5
+    assert_close(host_f32(dlog), dref, "dlogits")
