@@ -216,16 +216,19 @@ def adam_update(master, m, v, grad, step, lr, beta1, beta2, eps):
     """One Adam step.
 
     Inputs master, m, v are float32 arrays (the FP32 state), grad holds the
-    BF16 gradient values (as float32), step t >= 1.  The update is computed
-    in float64, hyper-parameters included (bias corrections 1 - beta^t too);
-    the new state is stored back in float32, the state's precision.  Returns
-    (master, m, v, w) with w = bf16_RNE(master).
+    BF16 gradient values (as float32), step t >= 1.  Hyper-parameters are
+    the float32 values a caller hands the library (0.999 is 0.99900001287...);
+    from those, everything (1 - beta, the bias corrections 1 - beta^t, the
+    update) is computed in float64, and the new state is stored back in
+    float32, the state's precision.  Returns (master, m, v, w) with
+    w = bf16_RNE(master).
 
         m <- b1 m + (1 - b1) g
         v <- b2 v + (1 - b2) g^2
         master <- master - lr * (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps)
     """
-    b1, b2 = float(beta1), float(beta2)
+    b1, b2 = float(np.float32(beta1)), float(np.float32(beta2))
+    lr, eps = float(np.float32(lr)), float(np.float32(eps))
     bc1 = 1.0 - b1 ** step
     bc2 = 1.0 - b2 ** step
     g = grad.astype(np.float64)
@@ -233,7 +236,7 @@ def adam_update(master, m, v, grad, step, lr, beta1, beta2, eps):
     v_new = (b2 * v.astype(np.float64) + (1.0 - b2) * g * g).astype(np.float32)
     mhat = m_new.astype(np.float64) / bc1
     vhat = v_new.astype(np.float64) / bc2
-    upd = float(lr) * mhat / (np.sqrt(vhat) + float(eps))
+    upd = lr * mhat / (np.sqrt(vhat) + eps)
     master_new = (master.astype(np.float64) - upd).astype(np.float32)
     return master_new, m_new, v_new, round_bf16(master_new)
 

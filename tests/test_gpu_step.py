@@ -1,0 +1,239 @@
+"""Layer- and step-level parity of the streamed GPU path against the oracle,
+plus bit-identity of results across streaming configurations.
+
+Weights come from the library's own seeded init and are read back through
+mt_get_tensor, so the oracle computes on exactly the values the GPU used.
+Bound: normwise relative error <= 1e-2 per tensor (loss, dx, every gradient).
+"""
+import numpy as np
+import pytest
+
+from layer_streaming_amd import synth
+from oracle import step as ostep
+from oracle.bf16 import round_bf16
+from tests.gpu_util import assert_close, dev_bits, dev_zeros_bits, host_f32, log, widen
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from layer_streaming_amd import mt  # noqa: E402
+
+CFG1 = dict(n_layers=2, d_model=256, n_heads=4, n_kv_heads=4, head_dim=64, ffn_dim=688, vocab=1024)
+GQA = dict(n_layers=2, d_model=256, n_heads=4, n_kv_heads=2, head_dim=64, ffn_dim=688, vocab=1024)
+HD128 = dict(n_layers=1, d_model=256, n_heads=2, n_kv_heads=1, head_dim=128, ffn_dim=512, vocab=512)
+
+
+def make_ctx(shape_kw, max_batch, max_seq, **opts):
+    sh = mt.make_shape(**shape_kw)
+    o = mt.default_options(max_batch=max_batch, max_seq=max_seq, host_threads=8, **opts)
+    arena_bytes, _, _ = mt.workspace_bytes(sh, o)
+    arena = torch.empty(arena_bytes, dtype=torch.uint8, device="cuda")
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    ctx = mt.Context(sh, o, arena.data_ptr(), arena_bytes, [s.cuda_stream for s in streams])
+    ctx._keep = (arena, streams)
+    return ctx
+
+
+def oracle_shape(kw):
+    return ostep.Shape(**kw)
+
+
+def read_params(ctx, kw):
+    L = kw["n_layers"]
+    layers = []
+    for i in range(L):
+        layers.append({n: widen(ctx.get_tensor(i, j, mt.MT_W)).astype(np.float64)
+                       for j, n in enumerate(ostep.LAYER_TENSORS)})
+    head = {n: widen(ctx.get_tensor(L, j, mt.MT_W)).astype(np.float64) for j, n in enumerate(ostep.HEAD_TENSORS)}
+    return {"layers": layers, "head": head, "e_in": widen(ctx.get_tensor(L + 1, 0, mt.MT_W)).astype(np.float64)}
+
+
+def read_all(ctx, kw, which):
+    L = kw["n_layers"]
+    out = []
+    for u in range(L + 2):
+        n = 9 if u < L else (2 if u == L else 1)
+        for j in range(n):
+            out.append(((u, j), ctx.get_tensor(u, j, which).copy()))
+    return out
+
+
+# ----------------------------------------------------------- layer level --
+@pytest.mark.parametrize("kw,B,S", [(GQA, 2, 72), (HD128, 1, 130), (CFG1, 1, 1)])
+def test_layer_fwd_bwd_parity(kw, B, S):
+    log(f"layer fwd/bwd {kw} B={B} S={S}")
+    ctx = make_ctx(kw, B, S)
+    sh = oracle_shape(kw)
+    T, d = B * S, kw["d_model"]
+    rng = np.random.default_rng(99)
+    x = synth.bf16_exact_normal(rng, (T, d))
+    dy = synth.bf16_exact_normal(rng, (T, d), std=0.1)
+    dx_, dy_ = dev_bits(x), dev_bits(dy)
+    y_, dxo = dev_zeros_bits((T, d)), dev_zeros_bits((T, d))
+    gtile = dev_zeros_bits((mt.unit_elems(ctx.shape, 0),))
+    ctx.layer_fwd(0, dx_.data_ptr(), y_.data_ptr(), B, S)
+    ctx.layer_bwd(0, dx_.data_ptr(), dy_.data_ptr(), dxo.data_ptr(), gtile.data_ptr(), B, S)
+    torch.cuda.synchronize()
+    w = read_params(ctx, kw)["layers"][0]
+    y_ref, cache = ostep.layer_fwd(x.astype(np.float64), w, sh, B, S)
+    assert_close(host_f32(y_), y_ref, "y")
+    dx_ref, g_ref = ostep.layer_bwd(dy.astype(np.float64), cache, w, sh, B, S)
+    assert_close(host_f32(dxo), dx_ref, "dx")
+    gt = host_f32(gtile)
+    for j, n in enumerate(ostep.LAYER_TENSORS):
+        info = mt.tensor_desc(ctx.shape, 0, j)
+        sl = gt[info["offset"]: info["offset"] + info["rows"] * info["cols"]].reshape(g_ref[n].shape)
+        assert_close(sl, g_ref[n], f"d{n}")
+    ctx.close()
+
+
+# ------------------------------------------------------------ full step --
+@pytest.mark.parametrize("kw,B,S", [(CFG1, 2, 128), (GQA, 3, 40), (HD128, 1, 1)])
+def test_train_step_parity(kw, B, S):
+    log(f"train step {kw} B={B} S={S}")
+    ctx = make_ctx(kw, B, S)
+    sh = oracle_shape(kw)
+    tokens, labels = synth.tokens_labels(synth.SEED_TOKENS, B, S, kw["vocab"])
+    params = read_params(ctx, kw)
+    masters0 = read_all(ctx, kw, mt.MT_MASTER)
+    loss, st = ctx.train_step(tokens, labels)
+    log(f"  loss gpu {loss:.6f}  step {st.step_ms:.1f} ms")
+    loss_ref, g_ref = ostep.grads_monolithic(params, tokens, labels, sh)
+    assert abs(loss - loss_ref) / abs(loss_ref) <= 1e-2, (loss, loss_ref)
+    L = kw["n_layers"]
+    for i in range(L):
+        for j, n in enumerate(ostep.LAYER_TENSORS):
+            assert_close(widen(ctx.get_tensor(i, j, mt.MT_G)), g_ref["layers"][i][n], f"L{i}.d{n}")
+    for j, n in enumerate(ostep.HEAD_TENSORS):
+        assert_close(widen(ctx.get_tensor(L, j, mt.MT_G)), g_ref["head"][n], f"head.d{n}")
+    assert_close(widen(ctx.get_tensor(L + 1, 0, mt.MT_G)), g_ref["e_in"], "d_e_in")
+    # The host Adam consumed exactly the gradients the store now holds.
+    for (u, j), m0 in masters0:
+        g = widen(ctx.get_tensor(u, j, mt.MT_G))
+        z = np.zeros_like(m0)
+        mst, m, v, w = ostep.adam_update(m0, z, z, g, 1, 1e-4, 0.9, 0.999, 1e-8)
+        got = ctx.get_tensor(u, j, mt.MT_MASTER)
+        ulp = np.spacing(np.abs(mst)).astype(np.float64)
+        err = np.abs(got.astype(np.float64) - mst.astype(np.float64))
+        assert np.all(err <= np.maximum(2 * ulp, 1e-10)), (u, j, float(err.max()))
+        np.testing.assert_allclose(ctx.get_tensor(u, j, mt.MT_M), m, rtol=1e-6, atol=1e-30)
+        np.testing.assert_allclose(ctx.get_tensor(u, j, mt.MT_V), v, rtol=1e-6, atol=1e-30)
+        assert np.array_equal(widen(ctx.get_tensor(u, j, mt.MT_W)), round_bf16(got))
+    assert ctx.step_count() == 1
+    ctx.close()
+
+
+def test_multi_chunk_head_parity():
+    """LM head over several token chunks (fp32 accumulation of dE_out)."""
+    kw, B, S = CFG1, 2, 128
+    log("multi-chunk head")
+    ctx = make_ctx(kw, B, S, head_chunk=48)
+    tokens, labels = synth.tokens_labels(7, B, S, kw["vocab"])
+    params = read_params(ctx, kw)
+    loss, _ = ctx.train_step(tokens, labels)
+    loss_ref, g_ref = ostep.grads_monolithic(params, tokens, labels, oracle_shape(kw))
+    assert abs(loss - loss_ref) / abs(loss_ref) <= 1e-2
+    L = kw["n_layers"]
+    assert_close(widen(ctx.get_tensor(L, 1, mt.MT_G)), g_ref["head"]["e_out"], "head.de_out")
+    assert_close(widen(ctx.get_tensor(0, 1, mt.MT_G)), g_ref["layers"][0]["wq"], "L0.dwq")
+    ctx.close()
+
+
+# ------------------------------------------------------- bit identity ----
+VARIANTS = [dict(resident=1), dict(n_weight_slots=1), dict(n_weight_slots=3), dict(n_grad_slabs=1),
+            dict(slot_mode=1), dict(ckpt_on_host=0), dict(host_threads=3), dict(pin_store=1)]
+
+
+def _run_two_steps(kw, B, S, **opts):
+    ctx = make_ctx(kw, B, S, **opts)
+    losses = []
+    for k in range(2):
+        tokens, labels = synth.tokens_labels(100 + k, B, S, kw["vocab"])
+        losses.append(ctx.train_step(tokens, labels)[0])
+    state = [(key, which, a) for which in (mt.MT_W, mt.MT_G, mt.MT_MASTER, mt.MT_M, mt.MT_V)
+             for key, a in read_all(ctx, kw, which)]
+    ctx.close()
+    return losses, state
+
+
+@pytest.fixture(scope="module")
+def baseline_run():
+    return _run_two_steps(GQA, 2, 64)
+
+
+@pytest.mark.parametrize("opts", VARIANTS, ids=lambda o: ",".join(f"{k}={v}" for k, v in o.items()))
+def test_streamed_configurations_bit_identical(baseline_run, opts):
+    log(f"bit identity vs default streaming: {opts}")
+    base_losses, base_state = baseline_run
+    losses, state = _run_two_steps(GQA, 2, 64, **opts)
+    assert [np.float32(x).tobytes() for x in losses] == [np.float32(x).tobytes() for x in base_losses]
+    for (k1, w1, a1), (k2, w2, a2) in zip(base_state, state):
+        assert k1 == k2 and w1 == w2
+        assert np.array_equal(a1.view(np.uint8), a2.view(np.uint8)), (k1, w1)
+
+
+def test_loss_decreases_over_steps_on_fixed_batch():
+    log("loss decreases on a repeated batch")
+    kw = CFG1
+    ctx = make_ctx(kw, 2, 64, )
+    tokens, labels = synth.tokens_labels(5, 2, 64, kw["vocab"])
+    losses = [ctx.train_step(tokens, labels)[0] for _ in range(4)]
+    log(f"  losses {losses}")
+    assert losses[-1] < losses[0]
+    ctx.close()
+
+
+# ------------------------------------------------------------ errors ------
+def test_invalid_tokens_rejected_before_device_work():
+    ctx = make_ctx(CFG1, 1, 16)
+    tokens, labels = synth.tokens_labels(1, 1, 16, 1024)
+    tokens[0, 3] = 1024
+    with pytest.raises(mt.MTError) as e:
+        ctx.train_step(tokens, labels)
+    assert e.value.status == mt.MT_E_INVAL
+    # the context is still usable
+    tokens[0, 3] = 5
+    loss, _ = ctx.train_step(tokens, labels)
+    assert np.isfinite(loss)
+    with pytest.raises(mt.MTError) as e:
+        ctx.train_step(np.zeros((2, 16), np.int32), np.zeros((2, 16), np.int32))
+    assert e.value.status == mt.MT_E_INVAL
+    ctx.close()
+
+
+def test_arena_too_small_is_nomem():
+    sh = mt.make_shape(**CFG1)
+    o = mt.default_options(max_batch=1, max_seq=16)
+    need, _, _ = mt.workspace_bytes(sh, o)
+    arena = torch.empty(need, dtype=torch.uint8, device="cuda")
+    with pytest.raises(mt.MTError) as e:
+        mt.Context(sh, o, arena.data_ptr(), need - 4096)
+    assert e.value.status == mt.MT_E_NOMEM
+
+
+def test_injected_slab_worker_fault_is_reported(monkeypatch):
+    """A host worker failure (forced from the host) ends the step with an
+    error, joins cleanly and marks the context failed."""
+    monkeypatch.setenv("MT_FAULT", "slab:1")
+    ctx = make_ctx(CFG1, 1, 16)
+    tokens, labels = synth.tokens_labels(1, 1, 16, 1024)
+    with pytest.raises(mt.MTError) as e:
+        ctx.train_step(tokens, labels)
+    assert e.value.status == mt.MT_E_INTERNAL
+    with pytest.raises(mt.MTError) as e:
+        ctx.train_step(tokens, labels)
+    assert e.value.status == mt.MT_E_STATE
+    ctx.close()
+
+
+def test_injected_pack_fault_is_reported(monkeypatch):
+    monkeypatch.setenv("MT_FAULT", "pack:0")
+    ctx = make_ctx(CFG1, 1, 16)
+    tokens, labels = synth.tokens_labels(1, 1, 16, 1024)
+    with pytest.raises(mt.MTError) as e:
+        ctx.train_step(tokens, labels)
+    assert e.value.status == mt.MT_E_INTERNAL
+    ctx.close()

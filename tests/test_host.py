@@ -1,0 +1,187 @@
+"""CPU tests of the library's host side and its C ABI surface (no GPU):
+exported symbols, argument validation, tile layout, store sizing, the
+production host Adam against the oracle's, and the seeded weight init."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from layer_streaming_amd import mt
+from oracle import step as ostep
+from oracle.bf16 import round_bf16
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CFG1 = mt.make_shape(2, 256, 4, 4, 64, 688, 1024)
+QWEN7 = mt.make_shape(28, 3584, 28, 4, 128, 18944, 152064)
+QWEN14 = mt.make_shape(48, 5120, 40, 8, 128, 13824, 152064)
+
+
+def _declared_functions():
+    names = set()
+    for h in ("mt.h", "mt_kernels.h"):
+        src = open(os.path.join(ROOT, "include", h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(mt_[a-z_0-9]+)\s*\(", src, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 30
+    for n in sorted(names):
+        assert hasattr(mt.lib, n), n
+    assert names == set(mt.EXPORTED), names ^ set(mt.EXPORTED)
+
+
+def test_strerror_and_status_codes():
+    for s in (mt.MT_OK, mt.MT_E_INVAL, mt.MT_E_NOMEM, mt.MT_E_HIP, mt.MT_E_STATE, mt.MT_E_INTERNAL):
+        assert mt.lib.mt_strerror(s)
+    assert mt.lib.mt_strerror(-99) == b"unknown status"
+
+
+def test_tensor_layout_contiguity_and_alignment():
+    sh = QWEN7
+    d, hq, hkv, f = 3584, 28 * 128, 4 * 128, 18944
+    t = [mt.tensor_desc(sh, 0, j) for j in range(9)]
+    assert [x["name"] for x in t] == ["g1", "wq", "wk", "wv", "wo", "g2", "wg", "wu", "wd"]
+    assert t[2]["offset"] == t[1]["offset"] + hq * d          # wq|wk|wv contiguous
+    assert t[3]["offset"] == t[2]["offset"] + hkv * d
+    assert t[7]["offset"] == t[6]["offset"] + f * d           # wg|wu contiguous
+    for x in t:
+        assert x["offset"] % 8 == 0
+    for j in (0, 1, 4, 5, 6, 8):
+        assert t[j]["offset"] % 128 == 0                      # 256-byte aligned
+    assert (t[4]["rows"], t[4]["cols"]) == (d, hq)
+    assert (t[8]["rows"], t[8]["cols"]) == (d, f)
+    h = [mt.tensor_desc(sh, 28, j) for j in range(2)]
+    assert h[1]["name"] == "e_out" and (h[1]["rows"], h[1]["cols"]) == (152064, d)
+    assert mt.tensor_desc(sh, 29, 0)["name"] == "e_in"
+    assert mt.unit_tensors(sh, 0) == 9 and mt.unit_tensors(sh, 28) == 2 and mt.unit_tensors(sh, 29) == 1
+    # no two tensors overlap and the region covers them
+    ends = sorted((x["offset"], x["offset"] + x["rows"] * x["cols"]) for x in t)
+    for (a0, a1), (b0, b1) in zip(ends, ends[1:]):
+        assert a1 <= b0
+    assert ends[-1][1] <= mt.unit_elems(sh, 0)
+
+
+def test_host_store_is_sixteen_bytes_per_parameter():
+    o = mt.default_options(max_batch=8, max_seq=1024)
+    for sh, n in ((QWEN7, 7_615_487_488), (QWEN14, 14_769_689_600)):
+        _, _, store = mt.workspace_bytes(sh, o)
+        # padding to 256-byte tensors and 4 KiB tiles adds well under 0.01 %
+        assert n * 16 <= store <= n * 16 * 1.0001
+    _, _, store = mt.workspace_bytes(QWEN7, o)
+    assert abs(store / 1e9 - 121.85) < 0.05                     # the pages' ~122 GB
+
+
+def test_gpu_working_set_does_not_grow_with_depth():
+    o = mt.default_options(max_batch=4, max_seq=2048)
+    arenas = set()
+    for L in (4, 8, 16, 24):
+        sh = mt.make_shape(L, 8192, 64, 8, 128, 28672, 128256)
+        a, pinned, _ = mt.workspace_bytes(sh, o)
+        arenas.add(a)
+    assert len(arenas) == 1
+    # with checkpoints kept on the GPU the arena grows with depth instead
+    o2 = mt.default_options(max_batch=4, max_seq=2048, ckpt_on_host=0)
+    a4 = mt.workspace_bytes(mt.make_shape(4, 8192, 64, 8, 128, 28672, 128256), o2)[0]
+    a8 = mt.workspace_bytes(mt.make_shape(8, 8192, 64, 8, 128, 28672, 128256), o2)[0]
+    assert a8 > a4
+
+
+def test_workspace_bytes_deterministic_and_overridable():
+    o = mt.default_options(max_batch=8, max_seq=1024)
+    a1 = mt.workspace_bytes(QWEN7, o)
+    a2 = mt.workspace_bytes(QWEN7, o)
+    assert a1 == a2
+    o.workspace_bytes_override = a1[0] * 2
+    assert mt.workspace_bytes(QWEN7, o)[0] > a1[0]
+
+
+@pytest.mark.parametrize("field,value", [("d_model", 100), ("head_dim", 96), ("n_kv_heads", 3),
+                                         ("vocab", 0), ("n_layers", 0)])
+def test_bad_shapes_rejected(field, value):
+    sh = mt.make_shape(2, 256, 4, 4, 64, 688, 1024)
+    setattr(sh, field, value)
+    a, p, h = C.c_uint64(), C.c_uint64(), C.c_uint64()
+    o = mt.default_options()
+    r = mt.lib.mt_workspace_bytes(C.byref(sh), C.byref(o), C.byref(a), C.byref(p), C.byref(h))
+    assert r == mt.MT_E_INVAL
+    assert mt.lib.mt_last_error()
+
+
+@pytest.mark.parametrize("field,value", [("n_weight_slots", 0), ("n_weight_slots", 5), ("n_grad_slabs", 0),
+                                         ("slot_mode", 2), ("max_batch", 0), ("beta1", 1.0)])
+def test_bad_options_rejected(field, value):
+    o = mt.default_options()
+    setattr(o, field, value)
+    a, p, h = C.c_uint64(), C.c_uint64(), C.c_uint64()
+    assert mt.lib.mt_workspace_bytes(C.byref(CFG1), C.byref(o), C.byref(a), C.byref(p), C.byref(h)) == mt.MT_E_INVAL
+
+
+def test_init_rejects_null_arena_before_device_work():
+    o = mt.default_options(max_batch=1, max_seq=16)
+    ptr = C.c_void_p()
+    r = mt.lib.mt_init(C.byref(CFG1), C.byref(o), None, 0, None, C.byref(ptr))
+    assert r == mt.MT_E_INVAL and not ptr.value
+
+
+# ------------------------------------------------------------ host Adam ---
+@pytest.mark.parametrize("step", [1, 2, 7])
+def test_host_adam_matches_oracle(step):
+    rng = np.random.default_rng(step)
+    n = 100_003
+    master = rng.standard_normal(n).astype(np.float32) * 0.05
+    m = (rng.standard_normal(n) * 1e-4).astype(np.float32) if step > 1 else np.zeros(n, np.float32)
+    v = (np.abs(rng.standard_normal(n)) * 1e-8).astype(np.float32) if step > 1 else np.zeros(n, np.float32)
+    g = round_bf16((rng.standard_normal(n) * 1e-3).astype(np.float32))
+    g[:100] = 0.0
+    gbits = (g.view(np.uint32) >> 16).astype(np.uint16)
+    w = np.zeros(n, np.uint16)
+    gst = np.zeros(n, np.uint16)
+    pm, pmm, pv = master.copy(), m.copy(), v.copy()
+    r = mt.lib.mt_host_adam(w.ctypes.data, gst.ctypes.data, pm.ctypes.data, pmm.ctypes.data, pv.ctypes.data,
+                            gbits.ctypes.data, n, step, 1e-4, 0.9, 0.999, 1e-8, 4)
+    assert r == mt.MT_OK
+    om, omm, ov, ow = ostep.adam_update(master, m, v, g, step, 1e-4, 0.9, 0.999, 1e-8)
+    ulp = np.spacing(np.abs(om)).astype(np.float64)
+    assert np.all(np.abs(pm.astype(np.float64) - om) <= np.maximum(2 * ulp, 1e-6 * 1e-4))
+    # b1*m + (1-b1)*g can cancel: allow ~2 ulp of the operands' scale
+    np.testing.assert_allclose(pmm, omm, rtol=2e-6, atol=2e-11)
+    np.testing.assert_allclose(pv, ov, rtol=2e-6, atol=2e-15)
+    assert np.array_equal(gst, gbits)
+    assert np.array_equal((w.astype(np.uint32) << 16).view(np.float32), round_bf16(pm))
+
+
+# ------------------------------------------------------------------ init --
+def _init_tile(sh, unit, seed, threads):
+    n = mt.unit_elems(sh, unit)
+    buf = np.zeros(16 * n, np.uint8)
+    assert mt.lib.mt_host_init_unit(C.byref(sh), unit, seed, 0.02, threads, buf.ctypes.data, buf.nbytes) == 0
+    return buf, n
+
+
+def test_init_is_deterministic_across_thread_counts_and_statistically_normal():
+    b1, n = _init_tile(CFG1, 0, 1234, 1)
+    b2, _ = _init_tile(CFG1, 0, 1234, 7)
+    assert np.array_equal(b1, b2)
+    b3, _ = _init_tile(CFG1, 0, 1235, 2)
+    assert not np.array_equal(b1, b3)
+    w = b1[: 2 * n].view(np.uint16)
+    master = b1[4 * n: 8 * n].view(np.float32)
+    assert np.array_equal((w.astype(np.uint32) << 16).view(np.float32), master)   # master = W
+    assert np.all(b1[2 * n: 4 * n] == 0) and np.all(b1[8 * n:] == 0)             # G, m, v zero
+    for j in range(9):
+        t = mt.tensor_desc(CFG1, 0, j)
+        x = master[t["offset"]: t["offset"] + t["rows"] * t["cols"]].astype(np.float64)
+        if t["rows"] == 1:
+            assert np.all(x == 1.0)
+        else:
+            assert abs(x.mean()) < 3 * 0.02 / np.sqrt(x.size) + 1e-6
+            assert abs(x.std() / 0.02 - 1) < 0.02
+            # normal, not uniform: kurtosis ~ 3
+            k = np.mean((x - x.mean()) ** 4) / x.var() ** 2
+            assert abs(k - 3.0) < 0.15

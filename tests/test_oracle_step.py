@@ -275,8 +275,9 @@ def test_adam_first_step_closed_form():
     ulp = np.spacing(np.abs(expect).astype(np.float32)).astype(np.float64)
     assert np.all(err <= np.maximum(4 * ulp, 1e-6 * lr))
     assert np.array_equal(mast[:50], theta[:50])
-    np.testing.assert_allclose(m, 0.1 * gd, rtol=1e-6)
-    np.testing.assert_allclose(v, 0.001 * gd * gd, rtol=1e-6)
+    # (1 - beta) of the float32 hyper-parameters the library receives
+    np.testing.assert_allclose(m, (1 - float(np.float32(0.9))) * gd, rtol=1e-6)
+    np.testing.assert_allclose(v, (1 - float(np.float32(0.999))) * gd * gd, rtol=1e-6)
     assert np.array_equal(w, round_bf16(mast))
 
 
@@ -286,7 +287,9 @@ def test_adam_two_steps_closed_form():
     theta = rng.standard_normal(n).astype(np.float32)
     g1 = round_bf16((rng.standard_normal(n) * 1e-2).astype(np.float32)).astype(np.float64)
     g2 = round_bf16((rng.standard_normal(n) * 1e-2).astype(np.float32)).astype(np.float64)
-    b1, b2, lr, eps = 0.9, 0.999, 1e-3, 1e-8
+    # hyper-parameters as the float32 values the library receives
+    b1, b2 = float(np.float32(0.9)), float(np.float32(0.999))
+    lr, eps = float(np.float32(1e-3)), float(np.float32(1e-8))
     st = (theta, np.zeros(n, np.float32), np.zeros(n, np.float32))
     st = step.adam_update(*st, g1.astype(np.float32), 1, lr, b1, b2, eps)[:3]
     mast, m, v, _ = step.adam_update(*st, g2.astype(np.float32), 2, lr, b1, b2, eps)
