@@ -1,0 +1,235 @@
+"""Benchmark of the layer-streamed training step on one MI355X.
+
+Workload: a 7B-shaped decoder (28 layers, d_model 3584, 28 query / 4 KV heads
+of 128, SwiGLU ffn 18944, vocab 152064, untied embeddings), batch 8 x seq
+1024 of seeded uniform token ids, weights N(0, 0.02^2) in bf16 from seed 1234,
+host store of 16 bytes per parameter.  One step = streamed forward of every
+layer, the fused LM head, recompute + backward of every layer with gradient
+offload, and the host Adam over all 7.6B parameters (synchronous).
+
+Prints ONE JSON line on stdout (progress goes to stderr):
+  value            whole-step training tokens/s (inputs resident on the host
+                   store and in pinned memory, as the step consumes them)
+  roofline         the dominant kernel (fused gate|up GEMM, bf16 MFMA):
+                   algorithmic FLOPs per launch / mean launch time, timed live
+                   with HIP events on the compute stream over the timed steps
+  cpu_baseline     the CPU oracle on the host cores, on a bounded sample of the
+                   same workload, extrapolated to a full step
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "training tokens/sec + MFMA util & PCIe H2D/D2H GB/s overlap, 1×MI355X"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+PCIE_GEN5_X16_GBS = 64.0
+
+SHAPES = {
+    "7b": dict(n_layers=28, d_model=3584, n_heads=28, n_kv_heads=4, head_dim=128, ffn_dim=18944, vocab=152064,
+               batch=8, seq=1024,
+               workload="7B-shaped decoder, 28 layers, d_model 3584, 28q/4kv heads x 128, ffn 18944, "
+                        "vocab 152064, batch 8 x seq 1024, layer-streamed train step with host Adam"),
+    "tiny": dict(n_layers=2, d_model=256, n_heads=4, n_kv_heads=4, head_dim=64, ffn_dim=688, vocab=1024,
+                 batch=2, seq=128,
+                 workload="tiny decoder, 2 layers, d_model 256, 4 heads x 64, ffn 688, vocab 1024, "
+                          "batch 2 x seq 128"),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gemm_flops(cfg, T):
+    """Algorithmic FLOPs of every GEMM site per launch (2*M*N*K)."""
+    d, F, V = cfg["d_model"], cfg["ffn_dim"], cfg["vocab"]
+    nq = cfg["n_heads"] * cfg["head_dim"]
+    nqkv = (cfg["n_heads"] + 2 * cfg["n_kv_heads"]) * cfg["head_dim"]
+    f = {
+        "gemm_qkv": 2 * T * nqkv * d, "gemm_o": 2 * T * d * nq, "gemm_gateup": 2 * T * 2 * F * d,
+        "gemm_down": 2 * T * d * F,
+        "gemm_down_dx": 2 * T * F * d, "gemm_down_dw": 2 * d * F * T,
+        "gemm_gateup_dx": 2 * T * d * 2 * F, "gemm_gateup_dw": 2 * 2 * F * d * T,
+        "gemm_o_dx": 2 * T * nq * d, "gemm_o_dw": 2 * d * nq * T,
+        "gemm_qkv_dx": 2 * T * d * nqkv, "gemm_qkv_dw": 2 * nqkv * d * T,
+    }
+    return f
+
+
+def model_flops_per_step(cfg, T, S):
+    """6 * params * tokens for the matmuls plus causal attention (fwd 2 matmuls
+    of 2*S/2*hd per query-head on average, x3 for fwd+bwd); recompute excluded."""
+    L, d, F, V = cfg["n_layers"], cfg["d_model"], cfg["ffn_dim"], cfg["vocab"]
+    hq, hkv, hd = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    p_lin = d * hq * hd + 2 * d * hkv * hd + hq * hd * d + 3 * d * F
+    attn_fwd = 2 * 2 * T * hq * hd * (S + 1) / 2
+    return 6 * p_lin * L * T + 6 * T * d * V + 3 * attn_fwd * L
+
+
+def cpu_baseline(ctx, cfg, mt):
+    """Time the oracle (float64 numpy, all host cores) on a bounded sample:
+    one decoder layer (forward, recompute, backward) and the LM head at
+    B=1 x S=1024 tokens of the workload's shapes, and Adam over a 16M-element
+    slice; extrapolate to the full step (L layers, head, Adam over all
+    parameters) in the metric's unit."""
+    from oracle import step as ostep
+    from layer_streaming_amd import synth
+    sh = ostep.Shape(cfg["n_layers"], cfg["d_model"], cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"],
+                     cfg["ffn_dim"], cfg["vocab"])
+    widen = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    w = {n: widen(ctx.get_tensor(0, j, mt.MT_W)) for j, n in enumerate(ostep.LAYER_TENSORS)}
+    L = cfg["n_layers"]
+    hw = {n: widen(ctx.get_tensor(L, j, mt.MT_W)) for j, n in enumerate(ostep.HEAD_TENSORS)}
+    Bs, Ss = 1, min(1024, cfg["seq"])
+    Ts = Bs * Ss
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((Ts, sh.d_model)) * 0.02
+    dy = rng.standard_normal((Ts, sh.d_model)) * 1e-4
+    _, labels = synth.tokens_labels(synth.SEED_TOKENS, Bs, Ss, sh.vocab)
+    t0 = time.perf_counter()
+    ostep.layer_fwd(x, w, sh, Bs, Ss)                     # forward
+    _, c = ostep.layer_fwd(x, w, sh, Bs, Ss)              # recompute
+    ostep.layer_bwd(dy, c, w, sh, Bs, Ss)                 # backward
+    t_layer = time.perf_counter() - t0
+    log(f"cpu oracle: layer fwd+recompute+bwd at T={Ts}: {t_layer:.2f} s")
+    t0 = time.perf_counter()
+    ostep.head_fwd_bwd(x, hw, labels.reshape(-1), sh)
+    t_head = time.perf_counter() - t0
+    log(f"cpu oracle: head fwd+bwd at T={Ts}: {t_head:.2f} s")
+    n = 1 << 24
+    st = [rng.standard_normal(n).astype(np.float32) for _ in range(4)]
+    t0 = time.perf_counter()
+    ostep.adam_update(st[0], st[1], np.abs(st[2]), st[3], 1, 1e-4, 0.9, 0.999, 1e-8)
+    t_adam = (time.perf_counter() - t0) * sh.n_params() / n
+    log(f"cpu oracle: Adam over {sh.n_params() / 1e9:.2f}B params (from a {n} sample): {t_adam:.2f} s")
+    T = cfg["batch"] * cfg["seq"]
+    t_step = (L * t_layer + t_head) * (T / Ts) + t_adam
+    cores = len(os.sched_getaffinity(0))
+    return {"value": T / t_step, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"float64 numpy oracle: one decoder layer (fwd, recompute, bwd) and the LM head at 1x{Ss} "
+                      f"tokens, Adam over a 16M-element slice; step extrapolated as L*layer + head scaled to "
+                      f"{T} tokens + Adam over all parameters ({t_step:.1f} s per step)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="7b", choices=sorted(SHAPES))
+    ap.add_argument("--no-profile", action="store_true", help="skip per-kernel HIP event timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--host-threads", type=int, default=0)
+    ap.add_argument("--slots", type=int, default=2)
+    ap.add_argument("--slabs", type=int, default=12)
+    ap.add_argument("--slot-mode", type=int, default=0)
+    ap.add_argument("--resident", type=int, default=0)
+    ap.add_argument("--pin-store", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build streams one model through one MI355X; "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from layer_streaming_amd import mt, synth
+    cfg = SHAPES[args.config]
+    B, S = cfg["batch"], cfg["seq"]
+    T = B * S
+    shape = mt.make_shape(cfg["n_layers"], cfg["d_model"], cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"],
+                          cfg["ffn_dim"], cfg["vocab"])
+    opt = mt.default_options(max_batch=B, max_seq=S, profile_kernels=0 if args.no_profile else 1,
+                             host_threads=args.host_threads, n_weight_slots=args.slots, n_grad_slabs=args.slabs,
+                             slot_mode=args.slot_mode, resident=args.resident, pin_store=args.pin_store,
+                             seed=synth.SEED_WEIGHTS)
+    arena_bytes, pinned_bytes, store_bytes = mt.workspace_bytes(shape, opt)
+    log(f"arena {arena_bytes / 1e9:.2f} GB, pinned {pinned_bytes / 1e9:.2f} GB, store {store_bytes / 1e9:.2f} GB")
+    torch.cuda.init()
+    free0, _ = torch.cuda.mem_get_info()
+    arena = torch.empty(arena_bytes, dtype=torch.uint8, device="cuda")
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    t0 = time.time()
+    ctx = mt.Context(shape, opt, arena.data_ptr(), arena_bytes, [s.cuda_stream for s in streams])
+    log(f"init (host store + seeded weights) {time.time() - t0:.1f} s")
+    tokens, labels = synth.tokens_labels(synth.SEED_TOKENS, B, S, cfg["vocab"])
+
+    for i in range(args.warmup):
+        loss, st = ctx.train_step(tokens, labels)
+        log(f"warmup {i}: loss {loss:.4f} step {st.step_ms:.0f} ms")
+    torch.cuda.synchronize()
+    stats = []
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        loss, st = ctx.train_step(tokens, labels)
+        stats.append(mt.stats_dict(st))
+        log(f"step {i}: loss {loss:.4f} step {st.step_ms:.0f} ms (fwd {st.fwd_ms:.0f} head {st.head_ms:.0f} "
+            f"bwd {st.bwd_ms:.0f} adam tail {st.adam_tail_ms:.0f}; adam busy {st.adam_ms:.0f}, "
+            f"pack {st.pack_ms:.0f}; overlap {st.overlap_ratio:.2f})")
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = T * args.steps / elapsed
+
+    out = {"metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_per_step, 2), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": cfg["workload"], "global_batch": B, "seq_len": S, "layers": cfg["n_layers"],
+                      "parallelism": "single GPU, layer-streamed", "weight_slots": args.slots,
+                      "grad_slabs": args.slabs, "slot_mode": args.slot_mode, "resident": args.resident}}
+    mf = model_flops_per_step(cfg, T, S)
+    out["model_tflops_per_s"] = round(mf / (ms_per_step / 1e3) / 1e12, 2)
+
+    # Transfer and overlap figures (device clock, averaged over timed steps).
+    h2d_b = np.mean([s["h2d_bytes"] for s in stats])
+    h2d_ms = np.mean([s["h2d_busy_ms"] for s in stats])
+    d2h_b = np.mean([s["d2h_bytes"] for s in stats])
+    d2h_ms = np.mean([s["d2h_busy_ms"] for s in stats])
+    out["pcie"] = {"h2d_GBps": round(h2d_b / (h2d_ms / 1e3) / 1e9, 2) if h2d_ms else None,
+                   "d2h_GBps": round(d2h_b / (d2h_ms / 1e3) / 1e9, 2) if d2h_ms else None,
+                   "h2d_GB_per_step": round(h2d_b / 1e9, 3), "d2h_GB_per_step": round(d2h_b / 1e9, 3),
+                   "peak_GBps": PCIE_GEN5_X16_GBS,
+                   "h2d_busy_frac_of_step": round(float(np.mean([s["pcie_busy_frac"] for s in stats])), 3),
+                   "overlap_ratio": round(float(np.mean([s["overlap_ratio"] for s in stats])), 3)}
+    out["phases_ms"] = {k: round(float(np.mean([s[k] for s in stats])), 1)
+                        for k in ("fwd_ms", "head_ms", "bwd_ms", "adam_tail_ms", "compute_busy_ms",
+                                  "adam_ms", "pack_ms")}
+    out["memory"] = {"gpu_arena_bytes": int(stats[0]["gpu_arena_bytes"]),
+                     "gpu_mem_used_delta_bytes": int(free0 - torch.cuda.mem_get_info()[0]),
+                     "pinned_bytes": int(stats[0]["pinned_bytes"]),
+                     "host_store_bytes": int(stats[0]["host_store_bytes"])}
+    if not args.no_profile:
+        sites = {}
+        for s in stats:
+            for k, v in s["sites"].items():
+                a = sites.setdefault(k, [0.0, 0])
+                a[0] += v["ms"]
+                a[1] += v["launches"]
+        fl = gemm_flops(cfg, T)
+        g_ms = sum(sites[k][0] for k in fl if k in sites)
+        g_fl = sum(fl[k] * sites[k][1] for k in fl if k in sites)
+        out["mfma_util_block_gemms"] = round(g_fl / (g_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4) if g_ms else None
+        out["kernel_ms_per_step"] = {k: round(v[0] / len(stats), 3) for k, v in sorted(sites.items())}
+        dom = "gemm_gateup"
+        ms, n = sites[dom]
+        avg_ms = ms / n
+        achieved = fl[dom] / (avg_ms / 1e3) / 1e12
+        out["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                           "traffic": None, "avg_launch_ms": round(avg_ms, 4), "launches": n,
+                           "flops_per_launch": fl[dom]}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(ctx, cfg, mt)
+    ctx.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

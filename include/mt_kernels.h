@@ -27,21 +27,22 @@ extern "C" {
  * layout 1 (NN): A [M x K],       B [K x N]         C = A B
  * layout 2 (TN): A [K x M],       B [K x N]         C = A^T B
  * epi 0: C bf16 = acc; 1: C bf16 = acc + R (bf16, ldr); 2: C f32 = acc;
- * 3: C f32 += acc; 4: C bf16 = acc + Cacc (f32, ldacc). */
+ * 3: C f32 += acc; 4: C bf16 = acc + Cacc (f32, ldacc); 5: C f32 = acc + R
+ * (bf16); 6: C bf16 = acc + R (f32). */
 int mt_k_gemm(int32_t layout, int32_t epi, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
               int64_t ldc, const void* R, int64_t ldr, const void* Cacc, int64_t ldacc, int32_t M, int32_t N,
               int32_t K, void* stream);
 
-/* RMSNorm: n = gamma * x / sqrt(mean(x^2) + eps) per row of x [T x d];
- * rstd [T] f32 = 1/sqrt(mean(x^2) + eps). */
-int mt_k_rmsnorm_fwd(const void* x, const void* gamma, void* n, void* rstd, int32_t T, int32_t d, float eps,
-                     void* stream);
+/* RMSNorm: n = gamma * x / sqrt(mean(x^2) + eps) per row of x [T x d]
+ * (x bf16, or f32 when x_f32 != 0); rstd [T] f32 = 1/sqrt(mean(x^2) + eps). */
+int mt_k_rmsnorm_fwd(const void* x, int32_t x_f32, const void* gamma, void* n, void* rstd, int32_t T, int32_t d,
+                     float eps, void* stream);
 /* dx = resid + rstd * (g - nh * mean(g * nh)), g = dn*gamma, nh = x*rstd
  * (resid may be NULL); dgamma [d] bf16 = sum_t dn * nh, summed in a fixed
  * order through `scratch` (f32, mt_k_rmsnorm_bwd_scratch_elems). */
 int64_t mt_k_rmsnorm_bwd_scratch_elems(int32_t T, int32_t d);
-int mt_k_rmsnorm_bwd(const void* dn, const void* x, const void* gamma, const void* rstd, const void* resid,
-                     void* dx, void* dgamma, void* scratch, int32_t T, int32_t d, void* stream);
+int mt_k_rmsnorm_bwd(const void* dn, const void* x, int32_t x_f32, const void* gamma, const void* rstd,
+                     const void* resid, void* dx, void* dgamma, void* scratch, int32_t T, int32_t d, void* stream);
 
 /* Rotary embedding, rotate-half pairs (e, e+hd/2), angle s*base^(-2e/hd)
  * with s = t % S, in place on the first n_rot_heads heads of each row of

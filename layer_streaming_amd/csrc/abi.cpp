@@ -70,21 +70,21 @@ static int kst(hipError_t e, const char* what) {
 int mt_k_gemm(int32_t layout, int32_t epi, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
               int64_t ldc, const void* R, int64_t ldr, const void* Cacc, int64_t ldacc, int32_t M, int32_t N,
               int32_t K, void* stream) {
-    if (layout < 0 || layout > 2 || epi < 0 || epi > 4) MT_FAIL(MT_E_INVAL, "bad layout or epilogue");
+    if (layout < 0 || layout > 2 || epi < 0 || epi > 6) MT_FAIL(MT_E_INVAL, "bad layout or epilogue");
     mt::GemmArgs a{A, lda, B, ldb, C, ldc, R, ldr, static_cast<const float*>(Cacc), ldacc, M, N, K};
     return kst(mt::gemm(mt::GemmLayout(layout), mt::GemmEpi(epi), a, S_(stream)), "gemm");
 }
 
-int mt_k_rmsnorm_fwd(const void* x, const void* gamma, void* n, void* rstd, int32_t T, int32_t d, float eps,
-                     void* stream) {
-    return kst(mt::rmsnorm_fwd(U16(x), U16(gamma), U16(n), F32(rstd), T, d, eps, S_(stream)), "rmsnorm_fwd");
+int mt_k_rmsnorm_fwd(const void* x, int32_t x_f32, const void* gamma, void* n, void* rstd, int32_t T, int32_t d,
+                     float eps, void* stream) {
+    return kst(mt::rmsnorm_fwd(x, x_f32 != 0, U16(gamma), U16(n), F32(rstd), T, d, eps, S_(stream)), "rmsnorm_fwd");
 }
 
 int64_t mt_k_rmsnorm_bwd_scratch_elems(int32_t T, int32_t d) { return mt::rmsnorm_bwd_partial_elems(T, d); }
 
-int mt_k_rmsnorm_bwd(const void* dn, const void* x, const void* gamma, const void* rstd, const void* resid,
-                     void* dx, void* dgamma, void* scratch, int32_t T, int32_t d, void* stream) {
-    return kst(mt::rmsnorm_bwd(U16(dn), U16(x), U16(gamma), F32(rstd), resid ? U16(resid) : nullptr, U16(dx),
+int mt_k_rmsnorm_bwd(const void* dn, const void* x, int32_t x_f32, const void* gamma, const void* rstd,
+                     const void* resid, void* dx, void* dgamma, void* scratch, int32_t T, int32_t d, void* stream) {
+    return kst(mt::rmsnorm_bwd(U16(dn), x, x_f32 != 0, U16(gamma), F32(rstd), resid ? U16(resid) : nullptr, U16(dx),
                                U16(dgamma), F32(scratch), T, d, S_(stream)),
                "rmsnorm_bwd");
 }

@@ -10,8 +10,21 @@ namespace mt {
 namespace {
 
 // ------------------------------------------------------------- RMSNorm ----
+// The input of a norm is bf16 (layer inputs) or fp32 (the residual stream
+// inside a layer); eight elements at a time either way.
+__device__ __forceinline__ void load8(const uint16_t* __restrict__ row, int c, float* f) {
+    unpack8(reinterpret_cast<const uint4*>(row)[c], f);
+}
+__device__ __forceinline__ void load8(const float* __restrict__ row, int c, float* f) {
+    const float4 a = reinterpret_cast<const float4*>(row)[2 * c];
+    const float4 b = reinterpret_cast<const float4*>(row)[2 * c + 1];
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
 // One wave per row, four rows per 256-thread block.
-__global__ __launch_bounds__(256) void rmsnorm_fwd_k(const uint4* __restrict__ x,
+template <class TX>
+__global__ __launch_bounds__(256) void rmsnorm_fwd_k(const TX* __restrict__ x,
                                                      const uint4* __restrict__ gamma,
                                                      uint4* __restrict__ n, float* __restrict__ rstd,
                                                      int T, int d, float eps) {
@@ -19,11 +32,11 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_k(const uint4* __restrict__ x
     const int lane = threadIdx.x & 63;
     if (row >= T) return;
     const int nv = d >> 3;
-    const uint4* xr = x + int64_t(row) * nv;
+    const TX* xr = x + int64_t(row) * d;
     float ss = 0.f;
     for (int c = lane; c < nv; c += 64) {
         float f[8];
-        unpack8(xr[c], f);
+        load8(xr, c, f);
 #pragma unroll
         for (int k = 0; k < 8; ++k) ss += f[k] * f[k];
     }
@@ -32,7 +45,7 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_k(const uint4* __restrict__ x
     uint4* nr = n + int64_t(row) * nv;
     for (int c = lane; c < nv; c += 64) {
         float f[8], g[8];
-        unpack8(xr[c], f);
+        load8(xr, c, f);
         unpack8(gamma[c], g);
 #pragma unroll
         for (int k = 0; k < 8; ++k) f[k] = (f[k] * r) * g[k];
@@ -46,9 +59,9 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_k(const uint4* __restrict__ x
 // wave; dgamma_reduce sums the partial rows in order.
 constexpr int RPW = 8;
 
-template <int NCL>
+template <int NCL, class TX>
 __global__ __launch_bounds__(256) void rmsnorm_bwd_k(const uint4* __restrict__ dn,
-                                                     const uint4* __restrict__ x,
+                                                     const TX* __restrict__ x,
                                                      const uint4* __restrict__ gamma,
                                                      const float* __restrict__ rstd,
                                                      const uint4* __restrict__ resid,
@@ -74,7 +87,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_k(const uint4* __restrict__ d
         if (row >= T) break;
         const float r = rstd[row];
         const uint4* dnr = dn + int64_t(row) * nv;
-        const uint4* xr = x + int64_t(row) * nv;
+        const TX* xr = x + int64_t(row) * d;
         float g[NCL][8], nh[NCL][8];
         float dot = 0.f;
 #pragma unroll
@@ -83,7 +96,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_k(const uint4* __restrict__ d
             if (c < nv) {
                 float a[8], b[8];
                 unpack8(dnr[c], a);
-                unpack8(xr[c], b);
+                load8(xr, c, b);
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
                     nh[j][k] = b[k] * r;
@@ -290,13 +303,17 @@ inline unsigned blocks(int64_t n, int b) { return unsigned((n + b - 1) / b); }
 
 }  // namespace
 
-hipError_t rmsnorm_fwd(const uint16_t* x, const uint16_t* gamma, uint16_t* n, float* rstd, int T,
+hipError_t rmsnorm_fwd(const void* x, bool x_f32, const uint16_t* gamma, uint16_t* n, float* rstd, int T,
                        int d, float eps, hipStream_t s) {
     if (T < 0 || d <= 0 || (d & 7) || !al16(x) || !al16(gamma) || !al16(n)) return hipErrorInvalidValue;
     if (T == 0) return hipSuccess;
-    rmsnorm_fwd_k<<<blocks(T, 4), 256, 0, s>>>(reinterpret_cast<const uint4*>(x),
-                                               reinterpret_cast<const uint4*>(gamma),
-                                               reinterpret_cast<uint4*>(n), rstd, T, d, eps);
+    const uint4* g = reinterpret_cast<const uint4*>(gamma);
+    uint4* nv = reinterpret_cast<uint4*>(n);
+    if (x_f32)
+        rmsnorm_fwd_k<float><<<blocks(T, 4), 256, 0, s>>>(static_cast<const float*>(x), g, nv, rstd, T, d, eps);
+    else
+        rmsnorm_fwd_k<uint16_t><<<blocks(T, 4), 256, 0, s>>>(static_cast<const uint16_t*>(x), g, nv, rstd, T, d,
+                                                              eps);
     return hipGetLastError();
 }
 
@@ -305,7 +322,18 @@ int64_t rmsnorm_bwd_partial_elems(int T, int d) {
     return ((waves + 3) / 4) * 4 * int64_t(d);
 }
 
-hipError_t rmsnorm_bwd(const uint16_t* dn, const uint16_t* x, const uint16_t* gamma,
+template <class TX>
+static void rmsnorm_bwd_launch(int ncl, unsigned nb, const uint4* dn, const TX* x, const uint4* g,
+                               const float* rstd, const uint4* resid, uint4* dx, float* partial, int T, int d,
+                               hipStream_t s) {
+    if (ncl <= 1) rmsnorm_bwd_k<1, TX><<<nb, 256, 0, s>>>(dn, x, g, rstd, resid, dx, partial, T, d);
+    else if (ncl <= 2) rmsnorm_bwd_k<2, TX><<<nb, 256, 0, s>>>(dn, x, g, rstd, resid, dx, partial, T, d);
+    else if (ncl <= 4) rmsnorm_bwd_k<4, TX><<<nb, 256, 0, s>>>(dn, x, g, rstd, resid, dx, partial, T, d);
+    else if (ncl <= 8) rmsnorm_bwd_k<8, TX><<<nb, 256, 0, s>>>(dn, x, g, rstd, resid, dx, partial, T, d);
+    else rmsnorm_bwd_k<16, TX><<<nb, 256, 0, s>>>(dn, x, g, rstd, resid, dx, partial, T, d);
+}
+
+hipError_t rmsnorm_bwd(const uint16_t* dn, const void* x, bool x_f32, const uint16_t* gamma,
                        const float* rstd, const uint16_t* resid, uint16_t* dx, uint16_t* dgamma,
                        float* partial, int T, int d, hipStream_t s) {
     if (T <= 0 || d <= 0 || (d & 7) || d > 8192) return hipErrorInvalidValue;
@@ -316,15 +344,13 @@ hipError_t rmsnorm_bwd(const uint16_t* dn, const uint16_t* x, const uint16_t* ga
     const int ncl = ((d >> 3) + 63) / 64;
     auto U = [](const uint16_t* p) { return reinterpret_cast<const uint4*>(p); };
     uint4* dxv = reinterpret_cast<uint4*>(dx);
-#define MT_RB(N)                                                                               \
-    rmsnorm_bwd_k<N><<<nb, 256, 0, s>>>(U(dn), U(x), U(gamma), rstd, resid ? U(resid) : nullptr, \
-                                        dxv, partial, T, d)
-    if (ncl <= 1) MT_RB(1);
-    else if (ncl <= 2) MT_RB(2);
-    else if (ncl <= 4) MT_RB(4);
-    else if (ncl <= 8) MT_RB(8);
-    else MT_RB(16);
-#undef MT_RB
+    const uint4* rv = resid ? U(resid) : nullptr;
+    if (x_f32)
+        rmsnorm_bwd_launch<float>(ncl, nb, U(dn), static_cast<const float*>(x), U(gamma), rstd, rv, dxv, partial,
+                                  T, d, s);
+    else
+        rmsnorm_bwd_launch<uint16_t>(ncl, nb, U(dn), static_cast<const uint16_t*>(x), U(gamma), rstd, rv, dxv,
+                                     partial, T, d, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     dgamma_reduce_k<<<blocks(d, 256), 256, 0, s>>>(partial, int(nb) * 4, d, dgamma);

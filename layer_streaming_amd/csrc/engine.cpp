@@ -116,7 +116,7 @@ void plan_workspace(const Layout& lay, const mt_options& o, Carver& cv, Workspac
         ws.ckpt_dev = cv.take<uint16_t>(td * uint64_t(sh.n_layers + 1));
     }
     ws.n1 = cv.take<uint16_t>(td);
-    ws.h1 = cv.take<uint16_t>(td);
+    ws.h1 = cv.take<float>(td * 2);
     ws.n2 = cv.take<uint16_t>(td);
     ws.qkv = cv.take<uint16_t>(uint64_t(T) * nqkv * 2);
     ws.dqkv = cv.take<uint16_t>(uint64_t(T) * nqkv * 2);
@@ -605,7 +605,7 @@ hipError_t Ctx::fwd_layer(const LayerView& w, const uint16_t* x, uint16_t* y, in
     const int nq = sh.n_heads * sh.head_dim;
     const int nqkv = (sh.n_heads + 2 * sh.n_kv_heads) * sh.head_dim;
     hipStream_t s = st_c;
-    HIPR(site(S_RMS1_FWD, [&] { return rmsnorm_fwd(x, w.g1, ws.n1, ws.rstd1, T, d, sh.rms_eps, s); }));
+    HIPR(site(S_RMS1_FWD, [&] { return rmsnorm_fwd(x, false, w.g1, ws.n1, ws.rstd1, T, d, sh.rms_eps, s); }));
     HIPR(site(S_GEMM_QKV, [&] {
         GemmArgs a{ws.n1, d, w.wqkv, d, ws.qkv, nqkv, nullptr, 0, nullptr, 0, T, nqkv, d};
         return gemm(GEMM_NT, EPI_BF16, a, s);
@@ -619,9 +619,9 @@ hipError_t Ctx::fwd_layer(const LayerView& w, const uint16_t* x, uint16_t* y, in
     }));
     HIPR(site(S_GEMM_O, [&] {
         GemmArgs a{ws.o, nq, w.wo, nq, ws.h1, d, x, d, nullptr, 0, T, d, nq};
-        return gemm(GEMM_NT, EPI_BF16_RESID, a, s);
+        return gemm(GEMM_NT, EPI_F32_RESID, a, s);
     }));
-    HIPR(site(S_RMS2_FWD, [&] { return rmsnorm_fwd(ws.h1, w.g2, ws.n2, ws.rstd2, T, d, sh.rms_eps, s); }));
+    HIPR(site(S_RMS2_FWD, [&] { return rmsnorm_fwd(ws.h1, true, w.g2, ws.n2, ws.rstd2, T, d, sh.rms_eps, s); }));
     HIPR(site(S_GEMM_GATEUP, [&] {
         GemmArgs a{ws.n2, d, w.wgu, d, ws.gu, 2 * F, nullptr, 0, nullptr, 0, T, 2 * F, d};
         return gemm(GEMM_NT, EPI_BF16, a, s);
@@ -630,7 +630,7 @@ hipError_t Ctx::fwd_layer(const LayerView& w, const uint16_t* x, uint16_t* y, in
     if (need_y) {
         HIPR(site(S_GEMM_DOWN, [&] {
             GemmArgs a{ws.m, F, w.wd, F, y, d, ws.h1, d, nullptr, 0, T, d, F};
-            return gemm(GEMM_NT, EPI_BF16_RESID, a, s);
+            return gemm(GEMM_NT, EPI_BF16_RESID32, a, s);
         }));
     }
     return hipSuccess;
@@ -665,7 +665,7 @@ hipError_t Ctx::bwd_layer(const LayerView& w, const LayerView& g, const uint16_t
         return gemm(GEMM_TN, EPI_BF16, a, s);
     }));
     HIPR(site(S_RMS2_BWD, [&] {
-        return rmsnorm_bwd(ws.dn, ws.h1, w.g2, ws.rstd2, dy, ws.dh1, g.g2, ws.partial, T, d, s);
+        return rmsnorm_bwd(ws.dn, ws.h1, true, w.g2, ws.rstd2, dy, ws.dh1, g.g2, ws.partial, T, d, s);
     }));
     // attention
     HIPR(site(S_GEMM_O_DX, [&] {
@@ -693,7 +693,7 @@ hipError_t Ctx::bwd_layer(const LayerView& w, const LayerView& g, const uint16_t
         return gemm(GEMM_TN, EPI_BF16, a, s);
     }));
     HIPR(site(S_RMS1_BWD, [&] {
-        return rmsnorm_bwd(ws.dn, x, w.g1, ws.rstd1, ws.dh1, dx, g.g1, ws.partial, T, d, s);
+        return rmsnorm_bwd(ws.dn, x, false, w.g1, ws.rstd1, ws.dh1, dx, g.g1, ws.partial, T, d, s);
     }));
     return hipSuccess;
 }
@@ -706,7 +706,7 @@ hipError_t Ctx::head(const HeadView& w, const HeadView& g, const uint16_t* xL, u
     hipStream_t s = st_c;
     const int tc = int(std::min<int64_t>(ws.head_chunk, T));
     const int nch = (T + tc - 1) / tc;
-    HIPR(site(S_HEAD_RMS_FWD, [&] { return rmsnorm_fwd(xL, w.gf, ws.nf, ws.rstdf, T, d, sh.rms_eps, s); }));
+    HIPR(site(S_HEAD_RMS_FWD, [&] { return rmsnorm_fwd(xL, false, w.gf, ws.nf, ws.rstdf, T, d, sh.rms_eps, s); }));
     for (int c = 0; c < nch; ++c) {
         const int r0 = c * tc, rows = std::min(tc, T - r0);
         HIPR(site(S_HEAD_LOGITS, [&] {
@@ -731,7 +731,7 @@ hipError_t Ctx::head(const HeadView& w, const HeadView& g, const uint16_t* xL, u
         }));
     }
     HIPR(site(S_HEAD_RMS_BWD, [&] {
-        return rmsnorm_bwd(ws.dnf, xL, w.gf, ws.rstdf, nullptr, dy, g.gf, ws.partial, T, d, s);
+        return rmsnorm_bwd(ws.dnf, xL, false, w.gf, ws.rstdf, nullptr, dy, g.gf, ws.partial, T, d, s);
     }));
     HIPR(site(S_HEAD_MISC, [&] { return mean_reduce(ws.loss_rows, ws.loss, T, s); }));
     return hipSuccess;

@@ -40,7 +40,8 @@ struct Workspace {
     int64_t maxT = 0;
     uint16_t *x[2] = {}, *xc[2] = {}, *xL = nullptr;
     uint16_t* ckpt_dev = nullptr;  // [L+1][maxT x d] when checkpoints stay on the GPU
-    uint16_t *n1, *qkv, *o, *h1, *n2, *gu, *m;
+    uint16_t *n1, *qkv, *o, *n2, *gu, *m;
+    float* h1;  // residual stream inside a layer, kept in fp32
     float *rstd1, *rstd2, *lse;
     uint16_t *dy[2], *dm, *dgu, *dn, *dh1, *dout, *dqkv;
     float *dsum, *partial;

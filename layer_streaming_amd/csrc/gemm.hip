@@ -208,6 +208,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs p, int tile
                 } else if constexpr (EPI == EPI_F32_ACC) {
                     float* c = static_cast<float*>(p.C) + int64_t(row) * p.ldc + col;
                     *c = *c + v;
+                } else if constexpr (EPI == EPI_F32_RESID) {
+                    v += bf2f(static_cast<const uint16_t*>(p.R)[int64_t(row) * p.ldr + col]);
+                    static_cast<float*>(p.C)[int64_t(row) * p.ldc + col] = v;
+                } else if constexpr (EPI == EPI_BF16_RESID32) {
+                    v += static_cast<const float*>(p.R)[int64_t(row) * p.ldr + col];
+                    static_cast<uint16_t*>(p.C)[int64_t(row) * p.ldc + col] = f2bf(v);
                 } else {
                     v += p.Cacc[int64_t(row) * p.ldacc + col];
                     static_cast<uint16_t*>(p.C)[int64_t(row) * p.ldc + col] = f2bf(v);
@@ -232,6 +238,10 @@ hipError_t launch_epi(GemmEpi epi, const GemmArgs& a, hipStream_t s) {
             gemm_kernel<BM, BN, WM, WN, AK, BKM, EPI_F32_ACC><<<grid, block, 0, s>>>(a, tm, tn); break;
         case EPI_BF16_ACCF32:
             gemm_kernel<BM, BN, WM, WN, AK, BKM, EPI_BF16_ACCF32><<<grid, block, 0, s>>>(a, tm, tn); break;
+        case EPI_F32_RESID:
+            gemm_kernel<BM, BN, WM, WN, AK, BKM, EPI_F32_RESID><<<grid, block, 0, s>>>(a, tm, tn); break;
+        case EPI_BF16_RESID32:
+            gemm_kernel<BM, BN, WM, WN, AK, BKM, EPI_BF16_RESID32><<<grid, block, 0, s>>>(a, tm, tn); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -261,7 +271,8 @@ hipError_t gemm(GemmLayout lay, GemmEpi epi, const GemmArgs& a, hipStream_t s) {
     if (ak ? a.lda < a.K : a.lda < a.M) return hipErrorInvalidValue;
     if (bk ? a.ldb < a.K : a.ldb < a.N) return hipErrorInvalidValue;
     if (a.ldc < a.N) return hipErrorInvalidValue;
-    if (epi == EPI_BF16_RESID && (!a.R || a.ldr < a.N)) return hipErrorInvalidValue;
+    if ((epi == EPI_BF16_RESID || epi == EPI_F32_RESID || epi == EPI_BF16_RESID32) && (!a.R || a.ldr < a.N))
+        return hipErrorInvalidValue;
     if (epi == EPI_BF16_ACCF32 && (!a.Cacc || a.ldacc < a.N)) return hipErrorInvalidValue;
     switch (lay) {
         case GEMM_NT: return launch_layout<true, true>(epi, a, s);

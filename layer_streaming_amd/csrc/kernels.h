@@ -21,25 +21,28 @@ enum GemmEpi {
     EPI_F32 = 2,         // C(f32)  = acc
     EPI_F32_ACC = 3,     // C(f32) += acc
     EPI_BF16_ACCF32 = 4, // C(bf16) = acc + Cacc(f32)
+    EPI_F32_RESID = 5,   // C(f32)  = acc + R(bf16)
+    EPI_BF16_RESID32 = 6,// C(bf16) = acc + R(f32)
 };
 struct GemmArgs {
     const void* A; int64_t lda;
     const void* B; int64_t ldb;
     void* C; int64_t ldc;
-    const void* R; int64_t ldr;       // residual, EPI_BF16_RESID
+    const void* R; int64_t ldr;       // residual (EPI_*RESID*)
     const float* Cacc; int64_t ldacc; // fp32 partial sum, EPI_BF16_ACCF32
     int M, N, K;
 };
 hipError_t gemm(GemmLayout lay, GemmEpi epi, const GemmArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------- RMSNorm ----
-// n = gamma * x * rstd, rstd = 1/sqrt(mean(x^2)+eps); x, n, gamma bf16.
-hipError_t rmsnorm_fwd(const uint16_t* x, const uint16_t* gamma, uint16_t* n, float* rstd, int T,
+// n = gamma * x * rstd, rstd = 1/sqrt(mean(x^2)+eps); x bf16 or fp32 (x_f32),
+// n and gamma bf16.
+hipError_t rmsnorm_fwd(const void* x, bool x_f32, const uint16_t* gamma, uint16_t* n, float* rstd, int T,
                        int d, float eps, hipStream_t s);
 // dx = resid + rstd*(g - nh*mean(g*nh)), g = dn*gamma, nh = x*rstd (resid may be null);
 // dgamma = sum_t dn*nh written as bf16 (two-stage, fixed order).  `partial` is
 // fp32 scratch of rmsnorm_bwd_partial_elems(T, d) elements.
-hipError_t rmsnorm_bwd(const uint16_t* dn, const uint16_t* x, const uint16_t* gamma,
+hipError_t rmsnorm_bwd(const uint16_t* dn, const void* x, bool x_f32, const uint16_t* gamma,
                        const float* rstd, const uint16_t* resid, uint16_t* dx, uint16_t* dgamma,
                        float* partial, int T, int d, hipStream_t s);
 int64_t rmsnorm_bwd_partial_elems(int T, int d);

@@ -84,6 +84,17 @@ def test_gemm_epilogues():
                               c32.data_ptr(), N, M, N, K, s))
     _sync()
     assert_close(host_f32(dC2), 3 * ref, "C bf16 from f32 partial")
+    # fp32 residual stream: C f32 = acc + R bf16, then C bf16 = acc + R f32
+    h32 = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+    mt.check(mt.lib.mt_k_gemm(0, 5, dA.data_ptr(), K, dB.data_ptr(), K, h32.data_ptr(), N, dR.data_ptr(), N,
+                              None, 0, M, N, K, s))
+    _sync()
+    assert_close(h32.cpu().numpy(), ref + R, "C f32 = acc + R bf16", tol=1e-5)
+    dC3 = dev_zeros_bits((M, N))
+    mt.check(mt.lib.mt_k_gemm(0, 6, dA.data_ptr(), K, dB.data_ptr(), K, dC3.data_ptr(), N, h32.data_ptr(), N,
+                              None, 0, M, N, K, s))
+    _sync()
+    assert_close(host_f32(dC3), 2 * ref + R, "C bf16 = acc + R f32")
 
 
 def test_gemm_rejects_misaligned_shapes():
@@ -94,22 +105,29 @@ def test_gemm_rejects_misaligned_shapes():
 
 
 # --------------------------------------------------------------- RMSNorm --
-@pytest.mark.parametrize("T,d", [(37, 256), (130, 3584), (9, 8192), (1, 64)])
-def test_rmsnorm_fwd_bwd(T, d):
-    log(f"rmsnorm T={T} d={d}")
+@pytest.mark.parametrize("T,d,x_f32", [(37, 256, 0), (130, 3584, 0), (9, 8192, 0), (1, 64, 0), (130, 3584, 1),
+                                       (21, 256, 1)])
+def test_rmsnorm_fwd_bwd(T, d, x_f32):
+    log(f"rmsnorm T={T} d={d} x_f32={x_f32}")
     eps = 1e-6
-    x = synth.bf16_exact_normal(RNG, (T, d))
+    if x_f32:
+        x = RNG.standard_normal((T, d)).astype(np.float32)
+        dx_ = torch.from_numpy(x).cuda()
+    else:
+        x = synth.bf16_exact_normal(RNG, (T, d))
+        dx_ = dev_bits(x)
     g = synth.bf16_exact_normal(RNG, (d,), std=0.2, mean=1.0)
     dn = synth.bf16_exact_normal(RNG, (T, d))
     res = synth.bf16_exact_normal(RNG, (T, d))
-    dx_, n_, dg_ = dev_bits(x), dev_zeros_bits((T, d)), dev_zeros_bits((d,))
+    n_, dg_ = dev_zeros_bits((T, d)), dev_zeros_bits((d,))
     rstd = torch.zeros(T, dtype=torch.float32, device="cuda")
     dgam, ddn, dres = dev_bits(g), dev_bits(dn), dev_bits(res)
     s = _stream()
-    mt.check(mt.lib.mt_k_rmsnorm_fwd(dx_.data_ptr(), dgam.data_ptr(), n_.data_ptr(), rstd.data_ptr(), T, d, eps, s))
+    mt.check(mt.lib.mt_k_rmsnorm_fwd(dx_.data_ptr(), x_f32, dgam.data_ptr(), n_.data_ptr(), rstd.data_ptr(), T, d,
+                                     eps, s))
     scratch = torch.zeros(int(mt.lib.mt_k_rmsnorm_bwd_scratch_elems(T, d)), dtype=torch.float32, device="cuda")
     ddx = dev_zeros_bits((T, d))
-    mt.check(mt.lib.mt_k_rmsnorm_bwd(ddn.data_ptr(), dx_.data_ptr(), dgam.data_ptr(), rstd.data_ptr(),
+    mt.check(mt.lib.mt_k_rmsnorm_bwd(ddn.data_ptr(), dx_.data_ptr(), x_f32, dgam.data_ptr(), rstd.data_ptr(),
                                      dres.data_ptr(), ddx.data_ptr(), dg_.data_ptr(), scratch.data_ptr(), T, d, s))
     _sync()
     xd = x.astype(np.float64)
