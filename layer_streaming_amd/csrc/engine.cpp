@@ -792,6 +792,10 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int B, int S, 
             MT_FAIL(MT_E_INVAL, "token or label at row %d outside [0, %d)", t, V);
 
     const auto t_start = Clock::now();
+    // Adam rewrote every unit's weights after the last step: no slot holds
+    // current weights any more.
+    slot_unit.assign(plan.n_slots, -1);
+    slot_ptr = 0;
     tev_next = 0;
     intervals.clear();
     site_recs.clear();
