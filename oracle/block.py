@@ -156,6 +156,60 @@ def attention_bwd(do, q, k, v):
     return dq, dk, dv
 
 
+def attention_group_rows(q, k, v, do, rows_q, rows_k, block=1024):
+    """The same attention, forward and backward, for one KV group of one
+    sequence at lengths where the S x S matrices do not fit: q and do are
+    [S, G, hd] (the group's G query heads), k and v [S, hd].  Returns o, lse
+    and dq at query rows ``rows_q`` ([len, G, hd], [len, G], [len, G, hd]) and
+    dk, dv at key rows ``rows_k`` ([len, hd], summed over the group).
+
+    Exact float64 definition, computed in row blocks: pass 1 gets lse_s and
+    o_s for every row s (softmax over keys s' <= s), hence D_s = do_s . o_s;
+    then dq_s = sum_{s'<=s} P_ss' (dP_ss' - D_s) k_s' / sqrt(hd) and
+    dk_j = sum_{s>=j} P_sj (dP_sj - D_s) q_s / sqrt(hd), dv_j = sum_{s>=j} P_sj do_s.
+    """
+    seq, grp, hd = q.shape
+    sc = 1.0 / np.sqrt(hd)
+    lse = np.empty((seq, grp))
+    o = np.empty((seq, grp, hd))
+    # Row s's lse and o depend on keys <= s only, so pass 1 is needed just for
+    # the sampled query rows and for every row at or after the first sampled key.
+    rows_q = np.asarray(rows_q)
+    rows_k = np.asarray(rows_k)
+    need = np.zeros(seq, dtype=bool)
+    need[rows_q] = True
+    if len(rows_k):
+        need[int(rows_k.min()):] = True
+    for r0 in range(0, seq, block):
+        r1 = min(seq, r0 + block)
+        if not need[r0:r1].any():
+            continue
+        for g in range(grp):
+            s = (q[r0:r1, g] @ k[:r1].T) * sc                       # [rows, keys]
+            s = np.where(np.arange(r1)[None, :] <= np.arange(r0, r1)[:, None], s, -np.inf)
+            mx = s.max(axis=1, keepdims=True)
+            p = np.exp(s - mx)
+            den = p.sum(axis=1, keepdims=True)
+            lse[r0:r1, g] = (mx + np.log(den))[:, 0]
+            o[r0:r1, g] = (p / den) @ v[:r1]
+    dsum = np.einsum("sgd,sgd->sg", do, o)
+    dq = np.zeros((len(rows_q), grp, hd))
+    for i, s_ in enumerate(rows_q):
+        for g in range(grp):
+            p = np.exp(k[: s_ + 1] @ q[s_, g] * sc - lse[s_, g])
+            dp = v[: s_ + 1] @ do[s_, g]
+            dq[i, g] = (p * (dp - dsum[s_, g])) @ k[: s_ + 1] * sc
+    dk = np.zeros((len(rows_k), hd))
+    dv = np.zeros((len(rows_k), hd))
+    for i, j in enumerate(rows_k):
+        for g in range(grp):
+            p = np.exp(q[j:, g] @ k[j] * sc - lse[j:, g])               # P_sj for s >= j
+            dp = do[j:, g] @ v[j]
+            dk[i] += (p * (dp - dsum[j:, g])) @ q[j:, g] * sc
+            dv[i] += p @ do[j:, g]
+    return o[rows_q], lse[rows_q], dq, dk, dv
+
+
 # --------------------------------------------------------------------------
 # SwiGLU
 # --------------------------------------------------------------------------

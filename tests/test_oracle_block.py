@@ -180,6 +180,25 @@ def test_attention_matches_torch_sdpa_float64():
     np.testing.assert_allclose(o, ref.permute(0, 2, 1, 3).numpy(), rtol=1e-11, atol=1e-13)
 
 
+def test_attention_group_rows_equals_full_attention():
+    """The blocked row-sampled form against the S x S form on one KV group."""
+    seq, grp, hd = 70, 3, 16
+    q = rng.standard_normal((1, seq, grp, hd))
+    k = rng.standard_normal((1, seq, 1, hd))
+    v = rng.standard_normal((1, seq, 1, hd))
+    do = rng.standard_normal((1, seq, grp, hd))
+    o = block.attention_fwd(q, k, v)[0]
+    lse = block.attention_lse(q, k)[0]                     # [grp, seq]
+    dq, dk, dv = block.attention_bwd(do, q, k, v)
+    rq, rk = [0, 5, 31, 32, 69], [0, 1, 40, 69]
+    o2, lse2, dq2, dk2, dv2 = block.attention_group_rows(q[0], k[0, :, 0], v[0, :, 0], do[0], rq, rk, block=16)
+    np.testing.assert_allclose(o2, o[rq], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse2, lse[:, rq].T, rtol=1e-12)
+    np.testing.assert_allclose(dq2, dq[0, rq], rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(dk2, dk[0, rk, 0], rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(dv2, dv[0, rk, 0], rtol=1e-10, atol=1e-13)
+
+
 def test_attention_gqa_equals_mha_with_replicated_kv():
     bsz, seq, hq, hkv, hd = 1, 7, 6, 2, 8
     q = rng.standard_normal((bsz, seq, hq, hd))
