@@ -180,18 +180,18 @@ def attention_group_rows(q, k, v, do, rows_q, rows_k, block=1024):
     need[rows_q] = True
     if len(rows_k):
         need[int(rows_k.min()):] = True
-    for r0 in range(0, seq, block):
-        r1 = min(seq, r0 + block)
-        if not need[r0:r1].any():
-            continue
+    idx = np.nonzero(need)[0]
+    for c0 in range(0, len(idx), block):
+        rows = idx[c0:c0 + block]
+        r1 = int(rows[-1]) + 1
         for g in range(grp):
-            s = (q[r0:r1, g] @ k[:r1].T) * sc                       # [rows, keys]
-            s = np.where(np.arange(r1)[None, :] <= np.arange(r0, r1)[:, None], s, -np.inf)
+            s = (q[rows, g] @ k[:r1].T) * sc                        # [rows, keys]
+            s = np.where(np.arange(r1)[None, :] <= rows[:, None], s, -np.inf)
             mx = s.max(axis=1, keepdims=True)
             p = np.exp(s - mx)
             den = p.sum(axis=1, keepdims=True)
-            lse[r0:r1, g] = (mx + np.log(den))[:, 0]
-            o[r0:r1, g] = (p / den) @ v[:r1]
+            lse[rows, g] = (mx + np.log(den))[:, 0]
+            o[rows, g] = (p / den) @ v[:r1]
     dsum = np.einsum("sgd,sgd->sg", do, o)
     dq = np.zeros((len(rows_q), grp, hd))
     for i, s_ in enumerate(rows_q):
