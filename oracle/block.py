@@ -99,36 +99,60 @@ def _causal_mask(seq):
     return np.tril(np.ones((seq, seq), dtype=bool))
 
 
+def _group_scores(q, k, b, j, group):
+    """Scores of KV group j of sequence b: s[g, s, s'] = q[b,s,jG+g] . k[b,s',j]
+    / sqrt(hd), causal (-inf above the diagonal).  [G, S, S]."""
+    seq, hd = q.shape[1], q.shape[3]
+    qg = np.ascontiguousarray(q[b, :, j * group:(j + 1) * group].transpose(1, 0, 2))   # [G, S, hd]
+    s = (qg @ k[b, :, j].T) / np.sqrt(hd)
+    return np.where(_causal_mask(seq)[None], s, -np.inf)
+
+
+def _group_probs(q, k, b, j, group):
+    s = _group_scores(q, k, b, j, group)
+    s = s - s.max(axis=-1, keepdims=True)
+    p = np.exp(s)
+    return p / p.sum(axis=-1, keepdims=True)
+
+
 def attention_probs(q, k):
     """P[b, h, s, s'] = softmax_{s'<=s}(q[b,s,h] . k[b,s',h//G] / sqrt(hd))."""
-    bsz, seq, hq, hd = q.shape
-    group = hq // k.shape[2]
-    kx = np.repeat(k, group, axis=2)                     # [B, S, Hq, hd]
-    scores = np.einsum("bshd,bthd->bhst", q, kx, optimize=True) / np.sqrt(hd)
-    scores = np.where(_causal_mask(seq)[None, None], scores, -np.inf)
-    scores = scores - scores.max(axis=-1, keepdims=True)
-    p = np.exp(scores)
-    return p / p.sum(axis=-1, keepdims=True)
+    bsz, seq, hq, _ = q.shape
+    hkv = k.shape[2]
+    group = hq // hkv
+    p = np.empty((bsz, hq, seq, seq))
+    for b in range(bsz):
+        for j in range(hkv):
+            p[b, j * group:(j + 1) * group] = _group_probs(q, k, b, j, group)
+    return p
 
 
 def attention_lse(q, k):
     """lse[b, h, s] = log sum_{s'<=s} exp(q[b,s,h] . k[b,s',h//G] / sqrt(hd)),
     the softmax normaliser a streaming attention keeps per query row."""
-    bsz, seq, hq, hd = q.shape
-    group = hq // k.shape[2]
-    kx = np.repeat(k, group, axis=2)
-    scores = np.einsum("bshd,bthd->bhst", q, kx, optimize=True) / np.sqrt(hd)
-    scores = np.where(_causal_mask(seq)[None, None], scores, -np.inf)
-    mx = scores.max(axis=-1, keepdims=True)
-    return (mx + np.log(np.exp(scores - mx).sum(axis=-1, keepdims=True)))[..., 0]
+    bsz, seq, hq, _ = q.shape
+    hkv = k.shape[2]
+    group = hq // hkv
+    out = np.empty((bsz, hq, seq))
+    for b in range(bsz):
+        for j in range(hkv):
+            s = _group_scores(q, k, b, j, group)
+            mx = s.max(axis=-1, keepdims=True)
+            out[b, j * group:(j + 1) * group] = (mx + np.log(np.exp(s - mx).sum(axis=-1, keepdims=True)))[..., 0]
+    return out
 
 
 def attention_fwd(q, k, v):
     """o [B, S, Hq, hd] for q [B,S,Hq,hd], k and v [B,S,Hkv,hd]."""
-    group = q.shape[2] // k.shape[2]
-    p = attention_probs(q, k)
-    vx = np.repeat(v, group, axis=2)
-    return np.einsum("bhst,bthd->bshd", p, vx, optimize=True)
+    bsz, seq, hq, hd = q.shape
+    hkv = k.shape[2]
+    group = hq // hkv
+    o = np.empty((bsz, seq, hq, hd))
+    for b in range(bsz):
+        for j in range(hkv):
+            p = _group_probs(q, k, b, j, group)                 # [G, S, S]
+            o[b, :, j * group:(j + 1) * group] = (p @ v[b, :, j]).transpose(1, 0, 2)
+    return o
 
 
 def attention_bwd(do, q, k, v):
@@ -141,18 +165,22 @@ def attention_bwd(do, q, k, v):
     bsz, seq, hq, hd = q.shape
     hkv = k.shape[2]
     group = hq // hkv
-    p = attention_probs(q, k)
-    kx = np.repeat(k, group, axis=2)
-    vx = np.repeat(v, group, axis=2)
-    dp = np.einsum("bshd,bthd->bhst", do, vx, optimize=True)
-    dsum = np.sum(p * dp, axis=-1, keepdims=True)
-    ds = p * (dp - dsum)
     scale = 1.0 / np.sqrt(hd)
-    dq = np.einsum("bhst,bthd->bshd", ds, kx, optimize=True) * scale
-    dkx = np.einsum("bhst,bshd->bthd", ds, q, optimize=True) * scale
-    dvx = np.einsum("bhst,bshd->bthd", p, do, optimize=True)
-    dk = dkx.reshape(bsz, seq, hkv, group, hd).sum(axis=3)
-    dv = dvx.reshape(bsz, seq, hkv, group, hd).sum(axis=3)
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    for b in range(bsz):
+        for j in range(hkv):
+            hs = slice(j * group, (j + 1) * group)
+            p = _group_probs(q, k, b, j, group)                 # [G, S, S]
+            dog = np.ascontiguousarray(do[b, :, hs].transpose(1, 0, 2))      # [G, S, hd]
+            qg = np.ascontiguousarray(q[b, :, hs].transpose(1, 0, 2))
+            dp = dog @ v[b, :, j].T                              # [G, S, S]
+            dsum = np.sum(p * dp, axis=-1, keepdims=True)
+            ds = p * (dp - dsum)
+            dq[b, :, hs] = (ds @ k[b, :, j]).transpose(1, 0, 2) * scale
+            dk[b, :, j] = np.einsum("gst,gsd->td", ds, qg, optimize=True) * scale
+            dv[b, :, j] = np.einsum("gst,gsd->td", p, dog, optimize=True)
     return dq, dk, dv
 
 
