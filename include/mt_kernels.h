@@ -28,15 +28,17 @@ extern "C" {
  * layout 2 (TN): A [K x M],       B [K x N]         C = A^T B
  * epi 0: C bf16 = acc; 1: C bf16 = acc + R (bf16, ldr); 2: C f32 = acc;
  * 3: C f32 += acc; 4: C bf16 = acc + Cacc (f32, ldacc); 5: C f32 = acc + R
- * (bf16); 6: C bf16 = acc + R (f32). */
+ * (bf16); 6: C bf16 = acc + R (f32); 7: A and B are fp16 (not bf16), C f32 =
+ * acc, layout 0 only. */
 int mt_k_gemm(int32_t layout, int32_t epi, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
               int64_t ldc, const void* R, int64_t ldr, const void* Cacc, int64_t ldacc, int32_t M, int32_t N,
               int32_t K, void* stream);
 
 /* RMSNorm: n = gamma * x / sqrt(mean(x^2) + eps) per row of x [T x d]
- * (x bf16, or f32 when x_f32 != 0); rstd [T] f32 = 1/sqrt(mean(x^2) + eps). */
-int mt_k_rmsnorm_fwd(const void* x, int32_t x_f32, const void* gamma, void* n, void* rstd, int32_t T, int32_t d,
-                     float eps, void* stream);
+ * (x bf16, or f32 when x_f32 != 0); rstd [T] f32 = 1/sqrt(mean(x^2) + eps).
+ * n_f16 (may be NULL) receives n rounded to fp16 instead of bf16. */
+int mt_k_rmsnorm_fwd(const void* x, int32_t x_f32, const void* gamma, void* n, void* n_f16, void* rstd, int32_t T,
+                     int32_t d, float eps, void* stream);
 /* dx = resid + rstd * (g - nh * mean(g * nh)), g = dn*gamma, nh = x*rstd
  * (resid may be NULL); dgamma [d] bf16 = sum_t dn * nh, summed in a fixed
  * order through `scratch` (f32, mt_k_rmsnorm_bwd_scratch_elems). */
@@ -50,6 +52,14 @@ int mt_k_rmsnorm_bwd(const void* dn, const void* x, int32_t x_f32, const void* g
  * S*hd/2 float2, filled by the call. */
 int mt_k_rope(void* qkv, int64_t ld, void* table, int32_t T, int32_t S, int32_t n_rot_heads, int32_t hd,
               float base, int32_t dir, void* stream);
+/* Forward rotary embedding on the f32 QKV projection in [T x ldin] (n_heads
+ * heads of hd): the first n_rot_heads heads (q and k) are rotated in f32 and
+ * written as fp16, the others (v) as bf16, to out [T x ldout].  Same angles
+ * and table as mt_k_rope. */
+int mt_k_qkv_rope_cvt(const void* in, int64_t ldin, void* out, int64_t ldout, void* table, int32_t T, int32_t S,
+                      int32_t n_rot_heads, int32_t n_heads, int32_t hd, float base, void* stream);
+/* y[i] = fp16(x[i]) for bf16 x, n a multiple of 8. */
+int mt_k_bf16_to_f16(const void* x, void* y, int64_t n, void* stream);
 
 /* SwiGLU on gu [T x 2F] = [gate | up]: m [T x F] = silu(gate) * up;
  * backward dgu = [dm * up * silu'(gate) | dm * silu(gate)]. */
@@ -59,6 +69,7 @@ int mt_k_swiglu_bwd(const void* dm, const void* gu, void* dgu, int32_t T, int32_
 /* Causal GQA attention on qkv [B*S x ld] (q heads at column 0, k heads at
  * Hq*hd, v heads at (Hq+Hkv)*hd; query head h reads KV head h/(Hq/Hkv)),
  * scale 1/sqrt(hd): o [B*S x ldo], lse [B x Hq x S] f32 (natural log).
+ * q and k are fp16, v, o, dout and dqkv bf16.
  * hd in {64, 128}. */
 int mt_k_attn_fwd(const void* qkv, int64_t ld, void* o, int64_t ldo, void* lse, int32_t B, int32_t S, int32_t Hq,
                   int32_t Hkv, int32_t hd, void* stream);

@@ -70,14 +70,16 @@ static int kst(hipError_t e, const char* what) {
 int mt_k_gemm(int32_t layout, int32_t epi, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
               int64_t ldc, const void* R, int64_t ldr, const void* Cacc, int64_t ldacc, int32_t M, int32_t N,
               int32_t K, void* stream) {
-    if (layout < 0 || layout > 2 || epi < 0 || epi > 6) MT_FAIL(MT_E_INVAL, "bad layout or epilogue");
+    if (layout < 0 || layout > 2 || epi < 0 || epi > 7) MT_FAIL(MT_E_INVAL, "bad layout or epilogue");
     mt::GemmArgs a{A, lda, B, ldb, C, ldc, R, ldr, static_cast<const float*>(Cacc), ldacc, M, N, K};
     return kst(mt::gemm(mt::GemmLayout(layout), mt::GemmEpi(epi), a, S_(stream)), "gemm");
 }
 
-int mt_k_rmsnorm_fwd(const void* x, int32_t x_f32, const void* gamma, void* n, void* rstd, int32_t T, int32_t d,
-                     float eps, void* stream) {
-    return kst(mt::rmsnorm_fwd(x, x_f32 != 0, U16(gamma), U16(n), F32(rstd), T, d, eps, S_(stream)), "rmsnorm_fwd");
+int mt_k_rmsnorm_fwd(const void* x, int32_t x_f32, const void* gamma, void* n, void* n_f16, void* rstd, int32_t T,
+                     int32_t d, float eps, void* stream) {
+    return kst(mt::rmsnorm_fwd(x, x_f32 != 0, U16(gamma), U16(n), n_f16 ? U16(n_f16) : nullptr, F32(rstd), T, d, eps,
+                               S_(stream)),
+               "rmsnorm_fwd");
 }
 
 int64_t mt_k_rmsnorm_bwd_scratch_elems(int32_t T, int32_t d) { return mt::rmsnorm_bwd_partial_elems(T, d); }
@@ -95,6 +97,19 @@ int mt_k_rope(void* qkv, int64_t ld, void* table, int32_t T, int32_t S, int32_t 
     if (e != hipSuccess) return kst(e, "rope_table");
     return kst(mt::rope_apply(U16(qkv), ld, static_cast<float2*>(table), T, S, n_rot_heads, hd, dir, S_(stream)),
                "rope_apply");
+}
+
+int mt_k_qkv_rope_cvt(const void* in, int64_t ldin, void* out, int64_t ldout, void* table, int32_t T, int32_t S,
+                      int32_t n_rot_heads, int32_t n_heads, int32_t hd, float base, void* stream) {
+    hipError_t e = mt::rope_table(static_cast<float2*>(table), S, hd, base, S_(stream));
+    if (e != hipSuccess) return kst(e, "rope_table");
+    return kst(mt::qkv_rope_cvt(F32(in), ldin, U16(out), ldout, static_cast<float2*>(table), T, S, n_rot_heads,
+                                n_heads, hd, S_(stream)),
+               "qkv_rope_cvt");
+}
+
+int mt_k_bf16_to_f16(const void* x, void* y, int64_t n, void* stream) {
+    return kst(mt::bf16_to_f16(U16(x), U16(y), n, S_(stream)), "bf16_to_f16");
 }
 
 int mt_k_swiglu_fwd(const void* gu, void* m, int32_t T, int32_t F, void* stream) {

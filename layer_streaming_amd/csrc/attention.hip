@@ -2,7 +2,10 @@
 // log-sum-exp), and a deterministic backward split into a dQ kernel and a
 // dK/dV kernel, neither using atomics.
 //
-// All contractions run on v_mfma_f32_32x32x16_bf16.  The MFMA writes element
+// q and k arrive in fp16, v, dO and O in bf16.  The score products Q K^T run
+// on v_mfma_f32_32x32x16_f16, every other contraction on the bf16 form; the
+// fp16 q/k tiles that feed a gradient product are rounded to bf16 when staged.
+// Both MFMA forms share one register layout.  The MFMA writes element
 // r of lane l of a 32x32 result at row 8*(r/4) + 4*(l/32) + r%4, column l%32,
 // and takes its A operand as row l%32, k = 8*(l/32)..+7 and its B operand as
 // column l%32, same k.  The kernels exploit that:
@@ -28,6 +31,11 @@ constexpr float LN2 = 0.6931471805599453f;
 constexpr int BKV = 64;  // keys (or queries) per staged tile
 
 #define MFMA32(a, b, c) __builtin_amdgcn_mfma_f32_32x32x16_bf16((a), (b), (c), 0, 0, 0)
+// Scores from fp16 q and k (the logit path is kept in fp16: its rounding
+// error enters the softmax in proportion to the logits' size).
+#define MFMA32H(a, b, c) __builtin_amdgcn_mfma_f32_32x32x16_f16((a), (b), (c), 0, 0, 0)
+
+__device__ __forceinline__ uint32_t h2b(uint32_t h) { return f2bf(h2f(uint16_t(h))); }
 
 // Row-major tile image [rows][HD] bf16 in 16-byte chunks, chunk index
 // XOR-swizzled with the row.
@@ -66,12 +74,17 @@ struct Blk48 {
 #pragma unroll
         for (int j = 0; j < 4; ++j) lds[RowTile<HD>::idx(prow0 + j, dchunk)] = v[j];
     }
+    // FROM_F16: the source holds fp16; the transposed image is written as bf16
+    // (it feeds a bf16 product of the gradient path).
+    template <bool FROM_F16 = false>
     __device__ __forceinline__ void store_cols(uint2* __restrict__ lds, int prow0, int d0) const {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
+            uint32_t x0 = h16(v[0], e), x1 = h16(v[1], e), x2 = h16(v[2], e), x3 = h16(v[3], e);
+            if constexpr (FROM_F16) { x0 = h2b(x0); x1 = h2b(x1); x2 = h2b(x2); x3 = h2b(x3); }
             uint2 w;
-            w.x = h16(v[0], e) | (h16(v[1], e) << 16);
-            w.y = h16(v[2], e) | (h16(v[3], e) << 16);
+            w.x = x0 | (x1 << 16);
+            w.y = x2 | (x3 << 16);
             lds[ColTile::idx(d0 + e, prow0 >> 2)] = w;
         }
     }
@@ -115,12 +128,12 @@ __global__ __launch_bounds__(256) void attn_fwd_k(AttnArgs a, int n_qt) {
     const uint16_t* base = a.qkv + int64_t(b) * S * a.ld;
     const int kcol = (a.Hq + hk) * HD, vcol = (a.Hq + a.Hkv + hk) * HD;
 
-    bf16x8_t qf[NS];
+    f16x8_t qf[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         uint4 v = make_uint4(0, 0, 0, 0);
         if (q < S) v = *reinterpret_cast<const uint4*>(base + int64_t(q) * a.ld + h * HD + (2 * s + hh) * 8);
-        qf[s] = as_bf16x8(v);
+        qf[s] = as_f16x8(v);
     }
 
     // Tile loaders: K as rows (HD/32 chunks per thread), V as 4x8 blocks.
@@ -174,7 +187,7 @@ __global__ __launch_bounds__(256) void attn_fwd_k(AttnArgs a, int n_qt) {
                 for (int r = 0; r < 16; ++r) st[t][r] = 0.f;
 #pragma unroll
                 for (int s = 0; s < NS; ++s)
-                    st[t] = MFMA32(as_bf16x8(Ks[cur][RowTile<HD>::idx(32 * t + c, 2 * s + hh)]), qf[s], st[t]);
+                    st[t] = MFMA32H(as_f16x8(Ks[cur][RowTile<HD>::idx(32 * t + c, 2 * s + hh)]), qf[s], st[t]);
             }
             float mx = -INFINITY;
 #pragma unroll
@@ -286,7 +299,8 @@ __global__ __launch_bounds__(256) void attn_dq_k(AttnBwdArgs a, int n_qt) {
     const uint16_t* dbase = a.dout + int64_t(b) * S * a.ldo;
     const int kcol = (a.Hq + hk) * HD, vcol = (a.Hq + a.Hkv + hk) * HD;
 
-    bf16x8_t qf[NS], dof[NS];
+    f16x8_t qf[NS];
+    bf16x8_t dof[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         uint4 v = make_uint4(0, 0, 0, 0), w = v;
@@ -294,7 +308,7 @@ __global__ __launch_bounds__(256) void attn_dq_k(AttnBwdArgs a, int n_qt) {
             v = *reinterpret_cast<const uint4*>(base + int64_t(q) * a.ld + h * HD + (2 * s + hh) * 8);
             w = *reinterpret_cast<const uint4*>(dbase + int64_t(q) * a.ldo + h * HD + (2 * s + hh) * 8);
         }
-        qf[s] = as_bf16x8(v);
+        qf[s] = as_f16x8(v);
         dof[s] = as_bf16x8(w);
     }
     const int64_t st_off = (int64_t(b) * a.Hq + h) * S;
@@ -314,7 +328,7 @@ __global__ __launch_bounds__(256) void attn_dq_k(AttnBwdArgs a, int n_qt) {
     auto lstore = [&](int buf) {
         if (bthread) {
             kreg.store_rows<HD>(Ks[buf], 4 * kg, dg);
-            kreg.store_cols(Kt[buf], 4 * kg, 8 * dg);
+            kreg.store_cols<true>(Kt[buf], 4 * kg, 8 * dg);
             vreg.store_rows<HD>(Vs[buf], 4 * kg, dg);
         }
     };
@@ -343,7 +357,7 @@ __global__ __launch_bounds__(256) void attn_dq_k(AttnBwdArgs a, int n_qt) {
                 for (int r = 0; r < 16; ++r) { st[t][r] = 0.f; dp[t][r] = 0.f; }
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
-                    st[t] = MFMA32(as_bf16x8(Ks[cur][RowTile<HD>::idx(32 * t + c, 2 * s + hh)]), qf[s], st[t]);
+                    st[t] = MFMA32H(as_f16x8(Ks[cur][RowTile<HD>::idx(32 * t + c, 2 * s + hh)]), qf[s], st[t]);
                     dp[t] = MFMA32(as_bf16x8(Vs[cur][RowTile<HD>::idx(32 * t + c, 2 * s + hh)]), dof[s], dp[t]);
                 }
             }
@@ -412,7 +426,8 @@ __global__ __launch_bounds__(256) void attn_dkdv_k(AttnBwdArgs a, int n_kt) {
     const uint16_t* dbase = a.dout + int64_t(b) * S * a.ldo;
     const int kcol = (a.Hq + hk) * HD, vcol = (a.Hq + a.Hkv + hk) * HD;
 
-    bf16x8_t kf[NS], vf[NS];
+    f16x8_t kf[NS];
+    bf16x8_t vf[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         uint4 v = make_uint4(0, 0, 0, 0), w = v;
@@ -420,7 +435,7 @@ __global__ __launch_bounds__(256) void attn_dkdv_k(AttnBwdArgs a, int n_kt) {
             v = *reinterpret_cast<const uint4*>(base + int64_t(key) * a.ld + kcol + (2 * s + hh) * 8);
             w = *reinterpret_cast<const uint4*>(base + int64_t(key) * a.ld + vcol + (2 * s + hh) * 8);
         }
-        kf[s] = as_bf16x8(v);
+        kf[s] = as_f16x8(v);
         vf[s] = as_bf16x8(w);
     }
 
@@ -443,7 +458,7 @@ __global__ __launch_bounds__(256) void attn_dkdv_k(AttnBwdArgs a, int n_kt) {
     auto lstore = [&](int buf) {
         if (bthread) {
             qreg.store_rows<HD>(Qs[buf], 4 * qg, dg);
-            qreg.store_cols(Qt[buf], 4 * qg, 8 * dg);
+            qreg.store_cols<true>(Qt[buf], 4 * qg, 8 * dg);
             dreg.store_rows<HD>(Ds[buf], 4 * qg, dg);
             dreg.store_cols(Dt[buf], 4 * qg, 8 * dg);
         }
@@ -480,7 +495,7 @@ __global__ __launch_bounds__(256) void attn_dkdv_k(AttnBwdArgs a, int n_kt) {
                 for (int r = 0; r < 16; ++r) { st[t][r] = 0.f; dp[t][r] = 0.f; }
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
-                    st[t] = MFMA32(as_bf16x8(Qs[cur][RowTile<HD>::idx(32 * t + c, 2 * s + hh)]), kf[s], st[t]);
+                    st[t] = MFMA32H(as_f16x8(Qs[cur][RowTile<HD>::idx(32 * t + c, 2 * s + hh)]), kf[s], st[t]);
                     dp[t] = MFMA32(as_bf16x8(Ds[cur][RowTile<HD>::idx(32 * t + c, 2 * s + hh)]), vf[s], dp[t]);
                 }
             }

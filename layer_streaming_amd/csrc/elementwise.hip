@@ -26,8 +26,8 @@ __device__ __forceinline__ void load8(const float* __restrict__ row, int c, floa
 template <class TX>
 __global__ __launch_bounds__(256) void rmsnorm_fwd_k(const TX* __restrict__ x,
                                                      const uint4* __restrict__ gamma,
-                                                     uint4* __restrict__ n, float* __restrict__ rstd,
-                                                     int T, int d, float eps) {
+                                                     uint4* __restrict__ n, uint4* __restrict__ n16,
+                                                     float* __restrict__ rstd, int T, int d, float eps) {
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= T) return;
@@ -43,6 +43,7 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_k(const TX* __restrict__ x,
     ss = wave_sum(ss);
     const float r = 1.0f / sqrtf(ss / float(d) + eps);
     uint4* nr = n + int64_t(row) * nv;
+    uint4* nh = n16 ? n16 + int64_t(row) * nv : nullptr;
     for (int c = lane; c < nv; c += 64) {
         float f[8], g[8];
         load8(xr, c, f);
@@ -50,6 +51,7 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_k(const TX* __restrict__ x,
 #pragma unroll
         for (int k = 0; k < 8; ++k) f[k] = (f[k] * r) * g[k];
         nr[c] = pack8(f);
+        if (nh) nh[c] = pack8h(f);
     }
     if (lane == 0) rstd[row] = r;
 }
@@ -183,6 +185,60 @@ __global__ void rope_apply_k(uint16_t* __restrict__ qkv, int64_t ld, const float
     *phi = pack8(oh);
 }
 
+// Rotary embedding on the fp32 output of the QKV projection, written as the
+// 2-byte operands of attention: rotated q and k heads in fp16, v in bf16.
+__global__ void qkv_rope_cvt_k(const float* __restrict__ in, int64_t ldin, uint16_t* __restrict__ out,
+                               int64_t ldout, const float2* __restrict__ tab, int T, int S, int nrot, int nall,
+                               int hd) {
+    const int half = hd >> 1, per_head = half >> 3;
+    const int64_t n_rot_items = int64_t(T) * nrot * per_head;
+    const int64_t n_v_items = int64_t(T) * (nall - nrot) * (hd >> 3);
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < n_rot_items) {
+        const int e8 = int(i % per_head);
+        const int64_t th = i / per_head;
+        const int h = int(th % nrot);
+        const int t = int(th / nrot);
+        const int s = t % S;
+        const float* src = in + int64_t(t) * ldin + int64_t(h) * hd + e8 * 8;
+        float lo[8], hi[8], ol[8], oh[8];
+        const float4* s4 = reinterpret_cast<const float4*>(src);
+        const float4* h4 = reinterpret_cast<const float4*>(src + half);
+        *reinterpret_cast<float4*>(lo) = s4[0];
+        *reinterpret_cast<float4*>(lo + 4) = s4[1];
+        *reinterpret_cast<float4*>(hi) = h4[0];
+        *reinterpret_cast<float4*>(hi + 4) = h4[1];
+        const float2* tr = tab + int64_t(s) * half + e8 * 8;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float2 cs = tr[k];
+            ol[k] = lo[k] * cs.x - hi[k] * cs.y;
+            oh[k] = hi[k] * cs.x + lo[k] * cs.y;
+        }
+        uint16_t* dst = out + int64_t(t) * ldout + int64_t(h) * hd + e8 * 8;
+        *reinterpret_cast<uint4*>(dst) = pack8h(ol);
+        *reinterpret_cast<uint4*>(dst + half) = pack8h(oh);
+    } else if (i < n_rot_items + n_v_items) {
+        const int64_t j = i - n_rot_items;
+        const int vw = (nall - nrot) * hd;
+        const int c8 = int(j % (vw >> 3));
+        const int t = int(j / (vw >> 3));
+        const float* src = in + int64_t(t) * ldin + int64_t(nrot) * hd + c8 * 8;
+        float f[8];
+        *reinterpret_cast<float4*>(f) = reinterpret_cast<const float4*>(src)[0];
+        *reinterpret_cast<float4*>(f + 4) = reinterpret_cast<const float4*>(src)[1];
+        *reinterpret_cast<uint4*>(out + int64_t(t) * ldout + int64_t(nrot) * hd + c8 * 8) = pack8(f);
+    }
+}
+
+__global__ void bf16_to_f16_k(const uint4* __restrict__ in, uint4* __restrict__ out, int64_t n8) {
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= n8) return;
+    float f[8];
+    unpack8(in[i], f);
+    out[i] = pack8h(f);
+}
+
 // -------------------------------------------------------------- SwiGLU ----
 __device__ __forceinline__ float sigm(float z) { return 1.0f / (1.0f + expf(-z)); }
 
@@ -303,17 +359,38 @@ inline unsigned blocks(int64_t n, int b) { return unsigned((n + b - 1) / b); }
 
 }  // namespace
 
-hipError_t rmsnorm_fwd(const void* x, bool x_f32, const uint16_t* gamma, uint16_t* n, float* rstd, int T,
-                       int d, float eps, hipStream_t s) {
-    if (T < 0 || d <= 0 || (d & 7) || !al16(x) || !al16(gamma) || !al16(n)) return hipErrorInvalidValue;
+hipError_t rmsnorm_fwd(const void* x, bool x_f32, const uint16_t* gamma, uint16_t* n, uint16_t* n_f16,
+                       float* rstd, int T, int d, float eps, hipStream_t s) {
+    if (T < 0 || d <= 0 || (d & 7) || !al16(x) || !al16(gamma) || !al16(n) || (n_f16 && !al16(n_f16)))
+        return hipErrorInvalidValue;
     if (T == 0) return hipSuccess;
     const uint4* g = reinterpret_cast<const uint4*>(gamma);
     uint4* nv = reinterpret_cast<uint4*>(n);
+    uint4* nh = reinterpret_cast<uint4*>(n_f16);
     if (x_f32)
-        rmsnorm_fwd_k<float><<<blocks(T, 4), 256, 0, s>>>(static_cast<const float*>(x), g, nv, rstd, T, d, eps);
+        rmsnorm_fwd_k<float><<<blocks(T, 4), 256, 0, s>>>(static_cast<const float*>(x), g, nv, nh, rstd, T, d, eps);
     else
-        rmsnorm_fwd_k<uint16_t><<<blocks(T, 4), 256, 0, s>>>(static_cast<const uint16_t*>(x), g, nv, rstd, T, d,
-                                                              eps);
+        rmsnorm_fwd_k<uint16_t><<<blocks(T, 4), 256, 0, s>>>(static_cast<const uint16_t*>(x), g, nv, nh, rstd, T,
+                                                              d, eps);
+    return hipGetLastError();
+}
+
+hipError_t qkv_rope_cvt(const float* in, int64_t ldin, uint16_t* out, int64_t ldout, const float2* tab, int T,
+                        int S, int n_rot_heads, int n_heads, int hd, hipStream_t s) {
+    if (T < 0 || S <= 0 || n_rot_heads < 0 || n_heads < n_rot_heads || (hd & 15) || (ldin & 3) || (ldout & 7) ||
+        ldin < int64_t(n_heads) * hd || ldout < int64_t(n_heads) * hd || !al16(in) || !al16(out))
+        return hipErrorInvalidValue;
+    if (T == 0) return hipSuccess;
+    const int64_t n = int64_t(T) * n_rot_heads * (hd / 16) + int64_t(T) * (n_heads - n_rot_heads) * (hd / 8);
+    qkv_rope_cvt_k<<<blocks(n, 256), 256, 0, s>>>(in, ldin, out, ldout, tab, T, S, n_rot_heads, n_heads, hd);
+    return hipGetLastError();
+}
+
+hipError_t bf16_to_f16(const uint16_t* in, uint16_t* out, int64_t n, hipStream_t s) {
+    if (n < 0 || (n & 7) || !al16(in) || !al16(out)) return hipErrorInvalidValue;
+    if (n == 0) return hipSuccess;
+    bf16_to_f16_k<<<blocks(n / 8, 256), 256, 0, s>>>(reinterpret_cast<const uint4*>(in),
+                                                     reinterpret_cast<uint4*>(out), n / 8);
     return hipGetLastError();
 }
 

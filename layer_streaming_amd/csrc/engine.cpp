@@ -116,6 +116,9 @@ void plan_workspace(const Layout& lay, const mt_options& o, Carver& cv, Workspac
         ws.ckpt_dev = cv.take<uint16_t>(td * uint64_t(sh.n_layers + 1));
     }
     ws.n1 = cv.take<uint16_t>(td);
+    ws.n1h = cv.take<uint16_t>(td);
+    ws.w16 = cv.take<uint16_t>(uint64_t(nqkv) * d * 2);
+    ws.qkv32 = cv.take<float>(uint64_t(T) * nqkv * 4);
     ws.h1 = cv.take<float>(td * 2);
     ws.n2 = cv.take<uint16_t>(td);
     ws.qkv = cv.take<uint16_t>(uint64_t(T) * nqkv * 2);
@@ -404,9 +407,11 @@ int Ctx::init(const mt_shape& sh, const mt_options& o, void* arena_, uint64_t by
     // Host threads.
     int nth = opt.host_threads > 0 ? opt.host_threads : int(std::thread::hardware_concurrency());
     nth = std::max(1, nth);
+    // Adam is the host's bandwidth-bound bulk (30 B/param) and gets every
+    // thread; packing runs in short bursts on a quarter of them besides.
     const int npack = std::max(1, nth / 4);
     pack_pool.reset(new ThreadPool(npack));
-    adam_pool.reset(new ThreadPool(std::max(1, nth - npack)));
+    adam_pool.reset(new ThreadPool(nth));
 
     // Host master store: pageable, huge pages where the kernel allows.
     if (opt.pin_store) {
@@ -605,13 +610,19 @@ hipError_t Ctx::fwd_layer(const LayerView& w, const uint16_t* x, uint16_t* y, in
     const int nq = sh.n_heads * sh.head_dim;
     const int nqkv = (sh.n_heads + 2 * sh.n_kv_heads) * sh.head_dim;
     hipStream_t s = st_c;
-    HIPR(site(S_RMS1_FWD, [&] { return rmsnorm_fwd(x, false, w.g1, ws.n1, ws.rstd1, T, d, sh.rms_eps, s); }));
+    // Logit path in fp16: n1 and Wqkv go to the QKV product as fp16 (a bf16
+    // value in fp16's normal range converts exactly; smaller ones keep an
+    // absolute error under 2^-25), the projection comes back in fp32, RoPE
+    // rotates it in fp32 and q, k are stored as fp16, v as bf16.
+    HIPR(site(S_RMS1_FWD, [&] { return rmsnorm_fwd(x, false, w.g1, ws.n1, ws.n1h, ws.rstd1, T, d, sh.rms_eps, s); }));
     HIPR(site(S_GEMM_QKV, [&] {
-        GemmArgs a{ws.n1, d, w.wqkv, d, ws.qkv, nqkv, nullptr, 0, nullptr, 0, T, nqkv, d};
-        return gemm(GEMM_NT, EPI_BF16, a, s);
+        HIPR(bf16_to_f16(w.wqkv, ws.w16, int64_t(nqkv) * d, s));
+        GemmArgs a{ws.n1h, d, ws.w16, d, ws.qkv32, nqkv, nullptr, 0, nullptr, 0, T, nqkv, d};
+        return gemm(GEMM_NT, EPI_F32_F16IN, a, s);
     }));
     HIPR(site(S_ROPE_FWD, [&] {
-        return rope_apply(ws.qkv, nqkv, ws.rope_tab, T, S, sh.n_heads + sh.n_kv_heads, sh.head_dim, +1, s);
+        return qkv_rope_cvt(ws.qkv32, nqkv, ws.qkv, nqkv, ws.rope_tab, T, S, sh.n_heads + sh.n_kv_heads,
+                            sh.n_heads + 2 * sh.n_kv_heads, sh.head_dim, s);
     }));
     HIPR(site(S_ATTN_FWD, [&] {
         AttnArgs a{ws.qkv, nqkv, ws.o, nq, ws.lse, B, S, sh.n_heads, sh.n_kv_heads, sh.head_dim};
@@ -621,7 +632,7 @@ hipError_t Ctx::fwd_layer(const LayerView& w, const uint16_t* x, uint16_t* y, in
         GemmArgs a{ws.o, nq, w.wo, nq, ws.h1, d, x, d, nullptr, 0, T, d, nq};
         return gemm(GEMM_NT, EPI_F32_RESID, a, s);
     }));
-    HIPR(site(S_RMS2_FWD, [&] { return rmsnorm_fwd(ws.h1, true, w.g2, ws.n2, ws.rstd2, T, d, sh.rms_eps, s); }));
+    HIPR(site(S_RMS2_FWD, [&] { return rmsnorm_fwd(ws.h1, true, w.g2, ws.n2, nullptr, ws.rstd2, T, d, sh.rms_eps, s); }));
     HIPR(site(S_GEMM_GATEUP, [&] {
         GemmArgs a{ws.n2, d, w.wgu, d, ws.gu, 2 * F, nullptr, 0, nullptr, 0, T, 2 * F, d};
         return gemm(GEMM_NT, EPI_BF16, a, s);
@@ -706,7 +717,7 @@ hipError_t Ctx::head(const HeadView& w, const HeadView& g, const uint16_t* xL, u
     hipStream_t s = st_c;
     const int tc = int(std::min<int64_t>(ws.head_chunk, T));
     const int nch = (T + tc - 1) / tc;
-    HIPR(site(S_HEAD_RMS_FWD, [&] { return rmsnorm_fwd(xL, false, w.gf, ws.nf, ws.rstdf, T, d, sh.rms_eps, s); }));
+    HIPR(site(S_HEAD_RMS_FWD, [&] { return rmsnorm_fwd(xL, false, w.gf, ws.nf, nullptr, ws.rstdf, T, d, sh.rms_eps, s); }));
     for (int c = 0; c < nch; ++c) {
         const int r0 = c * tc, rows = std::min(tc, T - r0);
         HIPR(site(S_HEAD_LOGITS, [&] {

@@ -42,6 +42,9 @@ struct Workspace {
     uint16_t* ckpt_dev = nullptr;  // [L+1][maxT x d] when checkpoints stay on the GPU
     uint16_t *n1, *qkv, *o, *n2, *gu, *m;
     float* h1;  // residual stream inside a layer, kept in fp32
+    // logit path: fp16 copies of n1 and Wqkv, fp32 QKV projection before RoPE
+    uint16_t *n1h, *w16;
+    float* qkv32;
     float *rstd1, *rstd2, *lse;
     uint16_t *dy[2], *dm, *dgu, *dn, *dh1, *dout, *dqkv;
     float *dsum, *partial;

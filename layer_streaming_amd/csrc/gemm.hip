@@ -6,8 +6,8 @@
 // MFMA.  Design:
 //  * block tile BM x BN with BK = 64, one LDS image per operand holding 64
 //    k-values per row (128 bytes, 8 chunks of 16 bytes); the chunk index is
-//    XOR-swizzled with (row & 7) so eight consecutive rows reading the same
-//    logical chunk hit eight different 16-byte bank groups;
+//    XOR-swizzled with the row so both the MFMA fragment reads and the
+//    transposing writes spread over all bank groups;
 //  * operands stored k-contiguous ([rows x K]) are copied to LDS as they are;
 //    operands stored row-contiguous ([K x rows], the weight-gradient case)
 //    are transposed in registers, 4 k x 8 rows per thread, on the way in;
@@ -25,6 +25,12 @@ namespace {
 
 constexpr int BK = 64;
 
+// Physical 16-byte chunk of logical chunk kc in LDS row r is kc ^ swz(r).
+// Mixing bits 3..5 of the row in keeps both the MFMA reads (32 consecutive
+// rows, one chunk) and the transposing writes (rows 8 apart, one chunk)
+// spread over all eight chunk positions.
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
 __device__ __forceinline__ uint32_t half_of(const uint4& v, int e) {
     uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
     return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
@@ -38,45 +44,56 @@ struct TileLoader {
     static constexpr int NREG = KMAJOR ? NCH : NCH * 4;
     static_assert(NCH >= 1, "tile too small for the thread count");
     uint4 reg[NREG];
+    uint32_t ok[NREG];  // all-ones for lanes inside the matrix, else zero
 
+    // Every lane issues its loads unconditionally from an address clamped into
+    // the matrix; lanes outside it zero their registers when the data is
+    // consumed.  (A conditional load would make the loads wait one by one.)
     __device__ __forceinline__ void load(const uint16_t* __restrict__ base, int64_t ld, int row0,
                                          int rows, int k0, int K, int tid) {
-        const uint4 z = make_uint4(0, 0, 0, 0);
         if constexpr (KMAJOR) {
 #pragma unroll
             for (int i = 0; i < NCH; ++i) {
-                int c = tid + i * NT;
-                int r = c >> 3, kc = c & 7;
-                int gr = row0 + r, gk = k0 + kc * 8;
-                reg[i] = (gr < rows && gk < K)
-                             ? *reinterpret_cast<const uint4*>(base + int64_t(gr) * ld + gk)
-                             : z;
+                const int c = tid + i * NT;
+                const int r = c >> 3, kc = c & 7;
+                const int gr = row0 + r, gk = k0 + kc * 8;
+                ok[i] = (gr < rows && gk < K) ? 0xFFFFFFFFu : 0u;
+                const int cr = min(gr, rows - 1), ck = min(gk, K - 8);
+                reg[i] = *reinterpret_cast<const uint4*>(base + int64_t(cr) * ld + ck);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < NCH; ++i) {
-                int c = tid + i * NT;
-                int mg = c % (R / 8), kg = c / (R / 8);
-                int gm = row0 + mg * 8;
+                const int c = tid + i * NT;
+                const int mg = c % (R / 8), kg = c / (R / 8);
+                const int gm = row0 + mg * 8;
+                const int cm = min(gm, rows - 8);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    int gk = k0 + kg * 4 + j;
-                    reg[i * 4 + j] = (gk < K && gm < rows)
-                                         ? *reinterpret_cast<const uint4*>(base + int64_t(gk) * ld + gm)
-                                         : z;
+                    const int gk = k0 + kg * 4 + j;
+                    ok[i * 4 + j] = (gk < K && gm < rows) ? 0xFFFFFFFFu : 0u;
+                    const int ck = min(gk, K - 1);
+                    reg[i * 4 + j] = *reinterpret_cast<const uint4*>(base + int64_t(ck) * ld + cm);
                 }
             }
         }
     }
 
     // Write the registers into LDS image `lds` ([R][8] uint4, swizzled).
-    __device__ __forceinline__ void store(uint4* __restrict__ lds, int tid) const {
+    __device__ __forceinline__ void store(uint4* __restrict__ lds, int tid) {
+#pragma unroll
+        for (int i = 0; i < NREG; ++i) {
+            reg[i].x &= ok[i];
+            reg[i].y &= ok[i];
+            reg[i].z &= ok[i];
+            reg[i].w &= ok[i];
+        }
         if constexpr (KMAJOR) {
 #pragma unroll
             for (int i = 0; i < NCH; ++i) {
                 int c = tid + i * NT;
                 int r = c >> 3, kc = c & 7;
-                lds[r * 8 + (kc ^ (r & 7))] = reg[i];
+                lds[r * 8 + (kc ^ swz(r))] = reg[i];
             }
         } else {
             uint2* l2 = reinterpret_cast<uint2*>(lds);
@@ -91,7 +108,7 @@ struct TileLoader {
                     uint2 v;
                     v.x = half_of(reg[i * 4 + 0], e) | (half_of(reg[i * 4 + 1], e) << 16);
                     v.y = half_of(reg[i * 4 + 2], e) | (half_of(reg[i * 4 + 3], e) << 16);
-                    l2[(r * 8 + (kc ^ (r & 7))) * 2 + hf] = v;
+                    l2[(r * 8 + (kc ^ swz(r))) * 2 + hf] = v;
                 }
             }
         }
@@ -159,22 +176,28 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs p, int tile
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
             const int kc = ks * 2 + (lane >> 5);
-            bf16x8_t af[FM], bfr[FN];
+            uint4 af[FM], bfr[FN];
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
                 int r = wm * TM + i * 32 + (lane & 31);
-                af[i] = as_bf16x8(a_l[r * 8 + (kc ^ (r & 7))]);
+                af[i] = a_l[r * 8 + (kc ^ swz(r))];
             }
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 int r = wn * TN + j * 32 + (lane & 31);
-                bfr[j] = as_bf16x8(b_l[r * 8 + (kc ^ (r & 7))]);
+                bfr[j] = b_l[r * 8 + (kc ^ swz(r))];
             }
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < FN; ++j) {
+                    if constexpr (EPI == EPI_F32_F16IN)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(af[i]), as_f16x8(bfr[j]),
+                                                                           acc[i][j], 0, 0, 0);
+                    else
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[i]), as_bf16x8(bfr[j]),
+                                                                            acc[i][j], 0, 0, 0);
+                }
         }
         if (more) {
             la.store(As + (cur ^ 1) * BM * 8, tid);
@@ -203,7 +226,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs p, int tile
                 } else if constexpr (EPI == EPI_BF16_RESID) {
                     v += bf2f(static_cast<const uint16_t*>(p.R)[int64_t(row) * p.ldr + col]);
                     static_cast<uint16_t*>(p.C)[int64_t(row) * p.ldc + col] = f2bf(v);
-                } else if constexpr (EPI == EPI_F32) {
+                } else if constexpr (EPI == EPI_F32 || EPI == EPI_F32_F16IN) {
                     static_cast<float*>(p.C)[int64_t(row) * p.ldc + col] = v;
                 } else if constexpr (EPI == EPI_F32_ACC) {
                     float* c = static_cast<float*>(p.C) + int64_t(row) * p.ldc + col;
@@ -242,6 +265,12 @@ hipError_t launch_epi(GemmEpi epi, const GemmArgs& a, hipStream_t s) {
             gemm_kernel<BM, BN, WM, WN, AK, BKM, EPI_F32_RESID><<<grid, block, 0, s>>>(a, tm, tn); break;
         case EPI_BF16_RESID32:
             gemm_kernel<BM, BN, WM, WN, AK, BKM, EPI_BF16_RESID32><<<grid, block, 0, s>>>(a, tm, tn); break;
+        case EPI_F32_F16IN:
+            if constexpr (AK && BKM) {
+                gemm_kernel<BM, BN, WM, WN, AK, BKM, EPI_F32_F16IN><<<grid, block, 0, s>>>(a, tm, tn);
+                break;
+            }
+            return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -251,8 +280,12 @@ template <bool AK, bool BKM>
 hipError_t launch_layout(GemmEpi epi, const GemmArgs& a, hipStream_t s) {
     // Large problems: 256x256 tiles, 8 waves of 128x64.  Small ones (fewer
     // than ~2 tiles per CU): 128x128 tiles, 4 waves of 64x64.
+    // Measured on MI355X at the 7B shapes: 256x256 with 8 waves wins whenever
+    // the grid has at least one tile per CU (a 1.75-wave grid of big tiles
+    // still beats 7 waves of 128x128); 4 waves of 128x128 each lose latency
+    // hiding at one wave per SIMD.
     const int64_t big_tiles = int64_t((a.M + 255) / 256) * ((a.N + 255) / 256);
-    if (big_tiles >= 512) return launch_epi<256, 256, 2, 4, AK, BKM>(epi, a, s);
+    if (big_tiles >= 256) return launch_epi<256, 256, 2, 4, AK, BKM>(epi, a, s);
     return launch_epi<128, 128, 2, 2, AK, BKM>(epi, a, s);
 }
 
@@ -274,6 +307,8 @@ hipError_t gemm(GemmLayout lay, GemmEpi epi, const GemmArgs& a, hipStream_t s) {
     if ((epi == EPI_BF16_RESID || epi == EPI_F32_RESID || epi == EPI_BF16_RESID32) && (!a.R || a.ldr < a.N))
         return hipErrorInvalidValue;
     if (epi == EPI_BF16_ACCF32 && (!a.Cacc || a.ldacc < a.N)) return hipErrorInvalidValue;
+    if (epi == EPI_F32_F16IN && lay != GEMM_NT) return hipErrorInvalidValue;
+    if (int(epi) < 0 || int(epi) > int(EPI_F32_F16IN)) return hipErrorInvalidValue;
     switch (lay) {
         case GEMM_NT: return launch_layout<true, true>(epi, a, s);
         case GEMM_NN: return launch_layout<true, false>(epi, a, s);

@@ -5,8 +5,14 @@
 #include <stdint.h>
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// fp16 <-> float (hardware conversion, round to nearest even).
+__device__ __forceinline__ float h2f(uint16_t h) { return float(__builtin_bit_cast(_Float16, h)); }
+__device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, _Float16(f)); }
+__device__ __forceinline__ f16x8_t as_f16x8(const uint4& v) { return __builtin_bit_cast(f16x8_t, v); }
 
 // bf16 -> float is exact: the bf16 bits are the top half of the float.
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
@@ -47,4 +53,14 @@ __device__ __forceinline__ float wave_max(float v) {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
     return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// 8 fp16 in a uint4 <-> floats.
+__device__ __forceinline__ void unpack8h(const uint4& v, float* f) {
+    f[0] = h2f(v.x & 0xFFFF); f[1] = h2f(v.x >> 16); f[2] = h2f(v.y & 0xFFFF); f[3] = h2f(v.y >> 16);
+    f[4] = h2f(v.z & 0xFFFF); f[5] = h2f(v.z >> 16); f[6] = h2f(v.w & 0xFFFF); f[7] = h2f(v.w >> 16);
+}
+__device__ __forceinline__ uint4 pack8h(const float* f) {
+    auto p = [](float a, float b) { return uint32_t(f2h(a)) | (uint32_t(f2h(b)) << 16); };
+    return make_uint4(p(f[0], f[1]), p(f[2], f[3]), p(f[4], f[5]), p(f[6], f[7]));
 }

@@ -23,6 +23,7 @@ enum GemmEpi {
     EPI_BF16_ACCF32 = 4, // C(bf16) = acc + Cacc(f32)
     EPI_F32_RESID = 5,   // C(f32)  = acc + R(bf16)
     EPI_BF16_RESID32 = 6,// C(bf16) = acc + R(f32)
+    EPI_F32_F16IN = 7,   // operands fp16 (not bf16), C(f32) = acc; NT layout only
 };
 struct GemmArgs {
     const void* A; int64_t lda;
@@ -36,9 +37,9 @@ hipError_t gemm(GemmLayout lay, GemmEpi epi, const GemmArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------- RMSNorm ----
 // n = gamma * x * rstd, rstd = 1/sqrt(mean(x^2)+eps); x bf16 or fp32 (x_f32),
-// n and gamma bf16.
-hipError_t rmsnorm_fwd(const void* x, bool x_f32, const uint16_t* gamma, uint16_t* n, float* rstd, int T,
-                       int d, float eps, hipStream_t s);
+// n and gamma bf16; n_f16 (may be null) receives the same values in fp16.
+hipError_t rmsnorm_fwd(const void* x, bool x_f32, const uint16_t* gamma, uint16_t* n, uint16_t* n_f16,
+                       float* rstd, int T, int d, float eps, hipStream_t s);
 // dx = resid + rstd*(g - nh*mean(g*nh)), g = dn*gamma, nh = x*rstd (resid may be null);
 // dgamma = sum_t dn*nh written as bf16 (two-stage, fixed order).  `partial` is
 // fp32 scratch of rmsnorm_bwd_partial_elems(T, d) elements.
@@ -54,6 +55,13 @@ hipError_t rope_table(float2* tab, int S, int hd, float base, hipStream_t s);
 // position s = t % S; dir = +1 forward, -1 backward (rotation by -theta).
 hipError_t rope_apply(uint16_t* qkv, int64_t ld, const float2* tab, int T, int S, int n_rot_heads,
                       int hd, int dir, hipStream_t s);
+// From the fp32 QKV projection in [T x ldin] (n_heads heads of hd): rotate the
+// first n_rot_heads (q and k) and write them as fp16, the rest (v) as bf16,
+// into out [T x ldout] (the attention operand buffer).
+hipError_t qkv_rope_cvt(const float* in, int64_t ldin, uint16_t* out, int64_t ldout, const float2* tab, int T,
+                        int S, int n_rot_heads, int n_heads, int hd, hipStream_t s);
+// Elementwise bf16 -> fp16 (n a multiple of 8).
+hipError_t bf16_to_f16(const uint16_t* in, uint16_t* out, int64_t n, hipStream_t s);
 
 // -------------------------------------------------------------- SwiGLU ----
 // gu [T x 2F] = [gate | up] -> m [T x F] = silu(gate) * up.
@@ -63,7 +71,8 @@ hipError_t swiglu_bwd(const uint16_t* dm, const uint16_t* gu, uint16_t* dgu, int
                       hipStream_t s);
 
 // ----------------------------------------------------------- Attention ----
-// qkv [B*S x ld]: q heads at column 0, k heads at Hq*hd, v heads at (Hq+Hkv)*hd.
+// qkv [B*S x ld]: q heads at column 0, k heads at Hq*hd, v heads at (Hq+Hkv)*hd;
+// q and k are fp16 (the logit path), v bf16.  o, dout and dqkv are bf16.
 struct AttnArgs {
     const uint16_t* qkv; int64_t ld;
     uint16_t* o; int64_t ldo;   // [B*S x Hq*hd]

@@ -77,7 +77,7 @@ _SIGS = {
     # test entries
     "mt_k_gemm": (C.c_int, [C.c_int32, C.c_int32, _P, C.c_int64, _P, C.c_int64, _P, C.c_int64, _P, C.c_int64,
                             _P, C.c_int64, C.c_int32, C.c_int32, C.c_int32, _P]),
-    "mt_k_rmsnorm_fwd": (C.c_int, [_P, C.c_int32, _P, _P, _P, C.c_int32, C.c_int32, C.c_float, _P]),
+    "mt_k_rmsnorm_fwd": (C.c_int, [_P, C.c_int32, _P, _P, _P, _P, C.c_int32, C.c_int32, C.c_float, _P]),
     "mt_k_rmsnorm_bwd_scratch_elems": (C.c_int64, [C.c_int32, C.c_int32]),
     "mt_k_rmsnorm_bwd": (C.c_int, [_P, _P, C.c_int32, _P, _P, _P, _P, _P, _P, C.c_int32, C.c_int32, _P]),
     "mt_k_rope": (C.c_int, [_P, C.c_int64, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_float, C.c_int32,
@@ -91,6 +91,9 @@ _SIGS = {
     "mt_k_ce": (C.c_int, [_P, _P, _P, _P, C.c_int32, C.c_int32, C.c_float, _P]),
     "mt_k_mean": (C.c_int, [_P, _P, C.c_int32, _P]),
     "mt_k_f32_to_bf16": (C.c_int, [_P, _P, C.c_int64, _P]),
+    "mt_k_qkv_rope_cvt": (C.c_int, [_P, C.c_int64, _P, C.c_int64, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                    C.c_int32, C.c_float, _P]),
+    "mt_k_bf16_to_f16": (C.c_int, [_P, _P, C.c_int64, _P]),
     "mt_host_adam": (C.c_int, [_P, _P, _P, _P, _P, _P, C.c_int64, C.c_int64, C.c_float, C.c_float, C.c_float,
                                C.c_float, C.c_int32]),
     "mt_host_init_unit": (C.c_int, [C.POINTER(mt_shape), C.c_int32, C.c_uint64, C.c_float, C.c_int32, _P,

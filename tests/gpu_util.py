@@ -40,6 +40,23 @@ def host_f32(t):
     return widen(t.cpu().numpy().view(np.uint16))
 
 
+def f16_exact(x):
+    """The float32 values as float16, asserting that none changes."""
+    h = np.asarray(x, dtype=np.float32).astype(np.float16)
+    assert np.array_equal(h.astype(np.float32), np.asarray(x, dtype=np.float32)), "value not exact in fp16"
+    return h
+
+
+def dev_f16(x_f16):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x_f16, dtype=np.float16).view(np.int16)).cuda()
+
+
+def host_f16(t):
+    """Device tensor of fp16 bits (int16) -> float32 numpy."""
+    return t.cpu().numpy().view(np.float16).astype(np.float32)
+
+
 def rel_err(got, ref):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
@@ -56,3 +73,17 @@ def assert_close(got, ref, name, tol=TOL):
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
     assert e <= tol, f"{name}: normwise relative error {e:.3e} > {tol}"
     return e
+
+
+def attn_inputs(rng, T, Hq, Hkv, hd, qk_std=1.0):
+    """qkv [T x (Hq+2Hkv)hd] as the attention kernels take it: q and k as fp16
+    (normal, std qk_std), v as bf16 (standard normal).  Returns the values
+    (float32) and the device bit patterns (int16)."""
+    import torch
+    from layer_streaming_amd import synth
+    nr = (Hq + Hkv) * hd
+    qk = (qk_std * rng.standard_normal((T, nr))).astype(np.float16)
+    v = synth.bf16_exact_normal(rng, (T, Hkv * hd))
+    bits = np.concatenate([qk.view(np.uint16), (v.view(np.uint32) >> 16).astype(np.uint16)], axis=1)
+    vals = np.concatenate([qk.astype(np.float32), v], axis=1)
+    return vals, torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()

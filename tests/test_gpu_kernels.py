@@ -8,7 +8,8 @@ import pytest
 
 from layer_streaming_amd import synth
 from oracle import block
-from tests.gpu_util import assert_close, dev_bits, dev_zeros_bits, host_f32, log
+from oracle.bf16 import bf16_bits
+from tests.gpu_util import assert_close, attn_inputs, dev_bits, dev_f16, dev_zeros_bits, host_f16, host_f32, log
 
 pytestmark = pytest.mark.gpu
 
@@ -104,6 +105,24 @@ def test_gemm_rejects_misaligned_shapes():
     assert r == mt.MT_E_INVAL
 
 
+@pytest.mark.parametrize("M,N,K", [(200, 136, 72), (520, 4608, 264), (8192, 1536, 512)])
+def test_gemm_f16_operands(M, N, K):
+    """Epilogue 7: fp16 operands (the QKV projection of the logit path), f32 out."""
+    log(f"gemm f16 M={M} N={N} K={K}")
+    A = RNG.standard_normal((M, K)).astype(np.float16)
+    B = (0.02 * RNG.standard_normal((N, K))).astype(np.float16)
+    ref = A.astype(np.float64) @ B.astype(np.float64).T
+    dA, dB = dev_f16(A), dev_f16(B)
+    dC = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+    mt.check(mt.lib.mt_k_gemm(0, 7, dA.data_ptr(), K, dB.data_ptr(), K, dC.data_ptr(), N, None, 0, None, 0,
+                              M, N, K, _stream()), "gemm f16")
+    _sync()
+    assert_close(dC.cpu().numpy(), ref, "C", tol=1e-5)
+    r = mt.lib.mt_k_gemm(1, 7, dA.data_ptr(), K, dB.data_ptr(), N, dC.data_ptr(), N, None, 0, None, 0,
+                         M, N, K, _stream())
+    assert r == mt.MT_E_INVAL
+
+
 # --------------------------------------------------------------- RMSNorm --
 @pytest.mark.parametrize("T,d,x_f32", [(37, 256, 0), (130, 3584, 0), (9, 8192, 0), (1, 64, 0), (130, 3584, 1),
                                        (21, 256, 1)])
@@ -119,12 +138,12 @@ def test_rmsnorm_fwd_bwd(T, d, x_f32):
     g = synth.bf16_exact_normal(RNG, (d,), std=0.2, mean=1.0)
     dn = synth.bf16_exact_normal(RNG, (T, d))
     res = synth.bf16_exact_normal(RNG, (T, d))
-    n_, dg_ = dev_zeros_bits((T, d)), dev_zeros_bits((d,))
+    n_, dg_, nh_ = dev_zeros_bits((T, d)), dev_zeros_bits((d,)), dev_zeros_bits((T, d))
     rstd = torch.zeros(T, dtype=torch.float32, device="cuda")
     dgam, ddn, dres = dev_bits(g), dev_bits(dn), dev_bits(res)
     s = _stream()
-    mt.check(mt.lib.mt_k_rmsnorm_fwd(dx_.data_ptr(), x_f32, dgam.data_ptr(), n_.data_ptr(), rstd.data_ptr(), T, d,
-                                     eps, s))
+    mt.check(mt.lib.mt_k_rmsnorm_fwd(dx_.data_ptr(), x_f32, dgam.data_ptr(), n_.data_ptr(), nh_.data_ptr(),
+                                     rstd.data_ptr(), T, d, eps, s))
     scratch = torch.zeros(int(mt.lib.mt_k_rmsnorm_bwd_scratch_elems(T, d)), dtype=torch.float32, device="cuda")
     ddx = dev_zeros_bits((T, d))
     mt.check(mt.lib.mt_k_rmsnorm_bwd(ddn.data_ptr(), dx_.data_ptr(), x_f32, dgam.data_ptr(), rstd.data_ptr(),
@@ -133,6 +152,7 @@ def test_rmsnorm_fwd_bwd(T, d, x_f32):
     xd = x.astype(np.float64)
     n_ref, r_ref = block.rmsnorm_fwd(xd, g.astype(np.float64), eps)
     assert_close(host_f32(n_), n_ref, "n")
+    assert_close(host_f16(nh_), n_ref, "n (fp16)", tol=1e-3)
     assert_close(rstd.cpu().numpy(), r_ref, "rstd", tol=1e-5)
     dx_ref, dg_ref = block.rmsnorm_bwd(dn.astype(np.float64), xd, g.astype(np.float64), r_ref)
     assert_close(host_f32(ddx), dx_ref + res, "dx")
@@ -177,6 +197,31 @@ def test_rope_long_positions():
     assert_close(got, ref, "rope fwd long")
 
 
+@pytest.mark.parametrize("hd,S", [(64, 100), (128, 100), (128, 131072)])
+def test_qkv_rope_cvt(hd, S):
+    """Forward RoPE on the f32 projection: q, k rotated and stored fp16, v
+    rounded to bf16 (bit-exact against round-to-nearest-even)."""
+    hq, hkv = (4, 2) if S < 1000 else (1, 1)
+    B = 2 if S < 1000 else 1
+    log(f"qkv_rope_cvt hd={hd} S={S}")
+    ld = (hq + 2 * hkv) * hd
+    T = B * S
+    x = RNG.standard_normal((T, ld)).astype(np.float32)
+    dx = torch.from_numpy(x).cuda()
+    out = dev_zeros_bits((T, ld))
+    tab = torch.zeros(S * hd, dtype=torch.float32, device="cuda")
+    mt.check(mt.lib.mt_k_qkv_rope_cvt(dx.data_ptr(), ld, out.data_ptr(), ld, tab.data_ptr(), T, S, hq + hkv,
+                                      hq + 2 * hkv, hd, 10000.0, _stream()))
+    _sync()
+    nr = (hq + hkv) * hd
+    got_qk = host_f16(out)[:, :nr]
+    rot = x[:, :nr].astype(np.float64).reshape(B, S, hq + hkv, hd)
+    ref = block.rope_fwd(rot, 10000.0).reshape(T, nr)
+    assert_close(got_qk, ref, "q, k (fp16)", tol=1e-3)
+    got_v = out.cpu().numpy().view(np.uint16)[:, nr:]
+    np.testing.assert_array_equal(got_v, bf16_bits(x[:, nr:]))
+
+
 # ---------------------------------------------------------------- SwiGLU --
 @pytest.mark.parametrize("T,F", [(50, 688), (7, 18944)])
 def test_swiglu_fwd_bwd(T, F):
@@ -203,13 +248,23 @@ ATTN_CASES = [(2, 200, 4, 2, 64), (1, 300, 7, 1, 128), (2, 128, 4, 4, 128), (1, 
 
 @pytest.mark.parametrize("B,S,Hq,Hkv,hd", ATTN_CASES)
 def test_attention_fwd_bwd(B, S, Hq, Hkv, hd):
-    log(f"attention B={B} S={S} Hq={Hq} Hkv={Hkv} hd={hd}")
+    _attention_case(B, S, Hq, Hkv, hd, 1.0)
+
+
+def test_attention_sharp_logits():
+    """q, k with std 2 (logits of std 4): a peaked softmax, where the logit
+    path's rounding matters most."""
+    _attention_case(1, 700, 8, 2, 128, 2.0)
+
+
+def _attention_case(B, S, Hq, Hkv, hd, qk_std):
+    log(f"attention B={B} S={S} Hq={Hq} Hkv={Hkv} hd={hd} qk_std={qk_std}")
     T = B * S
     ld = (Hq + 2 * Hkv) * hd
     nq = Hq * hd
-    qkv = synth.bf16_exact_normal(RNG, (T, ld))
+    qkv, d_qkv = attn_inputs(RNG, T, Hq, Hkv, hd, qk_std)
     dout = synth.bf16_exact_normal(RNG, (T, nq))
-    d_qkv, d_do = dev_bits(qkv), dev_bits(dout)
+    d_do = dev_bits(dout)
     d_o = dev_zeros_bits((T, nq))
     lse = torch.zeros(B * Hq * S, dtype=torch.float32, device="cuda")
     dsum = torch.zeros(B * Hq * S, dtype=torch.float32, device="cuda")

@@ -11,7 +11,7 @@ import pytest
 from layer_streaming_amd import synth
 from oracle import step as ostep
 from oracle.bf16 import round_bf16
-from tests.gpu_util import assert_close, dev_bits, dev_zeros_bits, host_f32, log, widen
+from tests.gpu_util import TOL, assert_close, dev_bits, dev_zeros_bits, host_f32, log, widen
 
 pytestmark = pytest.mark.gpu
 
@@ -108,8 +108,8 @@ def _cmp_units(ctx, kw, g_ref, per_tensor):
         got_all, ref_all = [], []
         for j, n in enumerate(names):
             got = widen(ctx.get_tensor(u, j, mt.MT_G))
-            if per_tensor:
-                assert_close(got, ref[n], f"{tag}.d{n}")
+            # per tensor: asserted where per_tensor, else reported
+            assert_close(got, ref[n], f"{tag}.d{n}", tol=TOL if per_tensor else np.inf)
             got_all.append(got.reshape(-1))
             ref_all.append(np.asarray(ref[n]).reshape(-1))
         assert_close(np.concatenate(got_all), np.concatenate(ref_all), f"{tag} gradient tile")
