@@ -23,8 +23,10 @@ CXX_SOURCES = ["host.cpp", "engine.cpp", "abi.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
 HIP_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# host code: no FMA contraction, so the scalar and vector forms of the host
+# Adam round identically
 CXX_FLAGS = ["-x", "c++", "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include", "-march=x86-64-v3",
-             "-pthread"]
+             "-ffp-contract=off", "-pthread"]
 
 
 def _compile(src, flags):

@@ -4,6 +4,7 @@
 //   [Review]  MegaTrain review, dimensionstp.github.io/study-concept/megatrain/
 //   [Hotdry]  MegaTrain checkpoint strategy and communication overlap, blog.hotdry.top
 //   [Lilting] MegaTrain article, lilting.ch
+#include <immintrin.h>
 #include <math.h>
 #include <stdarg.h>
 #include <string.h>
@@ -160,12 +161,33 @@ void ThreadPool::parallel_for(int64_t n, int64_t grain,
     fn_ = nullptr;
 }
 
+// Copy into a buffer the CPU does not read back (a pinned staging buffer the
+// DMA engine drains): streaming stores skip the read-for-ownership of every
+// destination line, a third of a plain copy's memory traffic.
+static void nt_copy(char* dst, const char* src, int64_t n) {
+    const int64_t head = std::min<int64_t>(n, int64_t((32 - (reinterpret_cast<uintptr_t>(dst) & 31)) & 31));
+    memcpy(dst, src, size_t(head));
+    int64_t i = head;
+    for (; i + 128 <= n; i += 128) {
+        const __m256i a = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(src + i));
+        const __m256i b = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(src + i + 32));
+        const __m256i c = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(src + i + 64));
+        const __m256i d = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(src + i + 96));
+        _mm256_stream_si256(reinterpret_cast<__m256i*>(dst + i), a);
+        _mm256_stream_si256(reinterpret_cast<__m256i*>(dst + i + 32), b);
+        _mm256_stream_si256(reinterpret_cast<__m256i*>(dst + i + 64), c);
+        _mm256_stream_si256(reinterpret_cast<__m256i*>(dst + i + 96), d);
+    }
+    memcpy(dst + i, src + i, size_t(n - i));
+    _mm_sfence();  // drain the write-combining buffers before the copy is reported done
+}
+
 void parallel_copy(ThreadPool& pool, void* dst, const void* src, int64_t bytes) {
-    const int64_t unit = 1 << 16;
+    const int64_t unit = 1 << 20;
     const int64_t nblk = (bytes + unit - 1) / unit;
-    pool.parallel_for(nblk, 32, [&](int64_t b, int64_t e) {
+    pool.parallel_for(nblk, 1, [&](int64_t b, int64_t e) {
         const int64_t lo = b * unit, hi = std::min(bytes, e * unit);
-        memcpy(static_cast<char*>(dst) + lo, static_cast<const char*>(src) + lo, size_t(hi - lo));
+        nt_copy(static_cast<char*>(dst) + lo, static_cast<const char*>(src) + lo, hi - lo);
     });
 }
 
@@ -249,6 +271,36 @@ AdamStep adam_step_params(const mt_options& o, int64_t t) {
     return a;
 }
 
+// 8 bf16 <-> 8 fp32, the conversions of bf16_to_f32 / f32_to_bf16 (round to
+// nearest even, NaN kept quiet) lane by lane.
+static inline __m256 bf16x8_to_f32(__m128i h) {
+    return _mm256_castsi256_ps(_mm256_slli_epi32(_mm256_cvtepu16_epi32(h), 16));
+}
+static inline __m128i f32x8_to_bf16(__m256 x) {
+    const __m256i u = _mm256_castps_si256(x);
+    const __m256i lsb = _mm256_and_si256(_mm256_srli_epi32(u, 16), _mm256_set1_epi32(1));
+    __m256i r = _mm256_srli_epi32(_mm256_add_epi32(_mm256_add_epi32(u, _mm256_set1_epi32(0x7FFF)), lsb), 16);
+    const __m256i is_nan =
+        _mm256_cmpgt_epi32(_mm256_and_si256(u, _mm256_set1_epi32(0x7FFFFFFF)), _mm256_set1_epi32(0x7F800000));
+    r = _mm256_blendv_epi8(r, _mm256_or_si256(_mm256_srli_epi32(u, 16), _mm256_set1_epi32(0x40)), is_nan);
+    // every lane is in [0, 0xFFFF], so the saturating pack is exact
+    const __m256i p = _mm256_permute4x64_epi64(_mm256_packus_epi32(r, r), 0x08);
+    return _mm256_castsi256_si128(p);
+}
+
+// One Adam element; the vector loop below performs the same fp32 operations
+// in the same order (no contraction into FMA), so results are bit-identical.
+static inline void adam_one(const AdamStep& a, uint16_t gb, float& M, float& V, float& th, uint16_t& W) {
+    const float g = bf16_to_f32(gb);
+    const float mi = a.b1 * M + a.omb1 * g;
+    const float vi = a.b2 * V + a.omb2 * (g * g);
+    M = mi;
+    V = vi;
+    const float upd = a.lr * (mi / a.bc1) / (sqrtf(vi / a.bc2) + a.eps);
+    th = th - upd;
+    W = f32_to_bf16(th);
+}
+
 void adam_range(const TilePtrs& p, const uint16_t* gsrc, int64_t b, int64_t e, const AdamStep& a) {
     const bool copy_g = gsrc != p.g;
     uint16_t* __restrict__ G = p.g;
@@ -257,18 +309,41 @@ void adam_range(const TilePtrs& p, const uint16_t* gsrc, int64_t b, int64_t e, c
     float* __restrict__ Vv = p.v;
     float* __restrict__ th = p.master;
     uint16_t* __restrict__ W = p.w;
-    for (int64_t i = b; i < e; ++i) {
-        const uint16_t gb = gs[i];
-        if (copy_g) G[i] = gb;
-        const float g = bf16_to_f32(gb);
-        const float mi = a.b1 * M[i] + a.omb1 * g;
-        const float vi = a.b2 * Vv[i] + a.omb2 * (g * g);
-        M[i] = mi;
-        Vv[i] = vi;
-        const float upd = a.lr * (mi / a.bc1) / (sqrtf(vi / a.bc2) + a.eps);
-        const float t = th[i] - upd;
-        th[i] = t;
-        W[i] = f32_to_bf16(t);
+    int64_t i = b;
+    // scalar head up to 16-byte alignment of W (G shares it in practice; if
+    // not, the whole range stays scalar)
+    while (i < e && (reinterpret_cast<uintptr_t>(W + i) & 15)) {
+        if (copy_g) G[i] = gs[i];
+        adam_one(a, gs[i], M[i], Vv[i], th[i], W[i]);
+        ++i;
+    }
+    const bool vec = !copy_g || (reinterpret_cast<uintptr_t>(G + i) & 15) == 0;
+    if (vec) {
+        const __m256 b1 = _mm256_set1_ps(a.b1), b2 = _mm256_set1_ps(a.b2);
+        const __m256 omb1 = _mm256_set1_ps(a.omb1), omb2 = _mm256_set1_ps(a.omb2);
+        const __m256 lr = _mm256_set1_ps(a.lr), bc1 = _mm256_set1_ps(a.bc1), bc2 = _mm256_set1_ps(a.bc2);
+        const __m256 eps = _mm256_set1_ps(a.eps);
+        for (; i + 8 <= e; i += 8) {
+            const __m128i gb = _mm_loadu_si128(reinterpret_cast<const __m128i*>(gs + i));
+            // G and W are not read again by this pass: streaming stores
+            if (copy_g) _mm_stream_si128(reinterpret_cast<__m128i*>(G + i), gb);
+            const __m256 g = bf16x8_to_f32(gb);
+            const __m256 mi = _mm256_add_ps(_mm256_mul_ps(b1, _mm256_loadu_ps(M + i)), _mm256_mul_ps(omb1, g));
+            const __m256 vi =
+                _mm256_add_ps(_mm256_mul_ps(b2, _mm256_loadu_ps(Vv + i)), _mm256_mul_ps(omb2, _mm256_mul_ps(g, g)));
+            _mm256_storeu_ps(M + i, mi);
+            _mm256_storeu_ps(Vv + i, vi);
+            const __m256 den = _mm256_add_ps(_mm256_sqrt_ps(_mm256_div_ps(vi, bc2)), eps);
+            const __m256 upd = _mm256_div_ps(_mm256_mul_ps(lr, _mm256_div_ps(mi, bc1)), den);
+            const __m256 t = _mm256_sub_ps(_mm256_loadu_ps(th + i), upd);
+            _mm256_storeu_ps(th + i, t);
+            _mm_stream_si128(reinterpret_cast<__m128i*>(W + i), f32x8_to_bf16(t));
+        }
+        _mm_sfence();
+    }
+    for (; i < e; ++i) {
+        if (copy_g) G[i] = gs[i];
+        adam_one(a, gs[i], M[i], Vv[i], th[i], W[i]);
     }
 }
 

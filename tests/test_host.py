@@ -156,6 +156,38 @@ def test_host_adam_matches_oracle(step):
     assert np.array_equal((w.astype(np.uint32) << 16).view(np.float32), round_bf16(pm))
 
 
+@pytest.mark.parametrize("off", [0, 3])
+def test_host_adam_vector_path_bit_identical_to_single_elements(off):
+    """The host Adam's 8-wide loop against one call per element (which never
+    reaches the vector loop), on arrays starting at an unaligned offset, with
+    NaN, inf and zero gradients mixed in."""
+    rng = np.random.default_rng(11 + off)
+    n = 2_051
+
+    def arrays():
+        r = np.random.default_rng(5)
+        mas = (r.standard_normal(n + off) * 0.05).astype(np.float32)
+        mm = (r.standard_normal(n + off) * 1e-4).astype(np.float32)
+        vv = (np.abs(r.standard_normal(n + off)) * 1e-8).astype(np.float32)
+        return mas, mm, vv, np.zeros(n + off, np.uint16), np.zeros(n + off, np.uint16)
+
+    g = round_bf16((rng.standard_normal(n) * 1e-3).astype(np.float32))
+    g[[5, 17, 100]] = [np.nan, np.inf, 0.0]
+    gbits = np.zeros(n + off, np.uint16)
+    gbits[off:] = (g.view(np.uint32) >> 16).astype(np.uint16)
+    a = arrays()
+    b = arrays()
+    ptr = lambda x, i=off: x.ctypes.data + i * x.itemsize  # noqa: E731
+    assert mt.lib.mt_host_adam(ptr(a[3]), ptr(a[4]), ptr(a[0]), ptr(a[1]), ptr(a[2]), ptr(gbits), n, 3, 1e-4,
+                               0.9, 0.999, 1e-8, 3) == mt.MT_OK
+    for i in range(n):
+        j = off + i
+        assert mt.lib.mt_host_adam(ptr(b[3], j), ptr(b[4], j), ptr(b[0], j), ptr(b[1], j), ptr(b[2], j),
+                                   ptr(gbits, j), 1, 3, 1e-4, 0.9, 0.999, 1e-8, 1) == mt.MT_OK
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+
+
 # ------------------------------------------------------------------ init --
 def _init_tile(sh, unit, seed, threads):
     n = mt.unit_elems(sh, unit)
