@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libmt.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 
-HIP_SOURCES = ["gemm.hip", "attention.hip", "elementwise.hip"]
+HIP_SOURCES = ["gemm.hip", "gemm_nt.hip", "attention.hip", "elementwise.hip"]
 CXX_SOURCES = ["host.cpp", "engine.cpp", "abi.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]

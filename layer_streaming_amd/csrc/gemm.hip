@@ -309,6 +309,10 @@ hipError_t gemm(GemmLayout lay, GemmEpi epi, const GemmArgs& a, hipStream_t s) {
     if (epi == EPI_BF16_ACCF32 && (!a.Cacc || a.ldacc < a.N)) return hipErrorInvalidValue;
     if (epi == EPI_F32_F16IN && lay != GEMM_NT) return hipErrorInvalidValue;
     if (int(epi) < 0 || int(epi) > int(EPI_F32_F16IN)) return hipErrorInvalidValue;
+    if (lay == GEMM_NT) {
+        const hipError_t e = gemm_nt_direct(epi, a, s);
+        if (e != hipErrorNotSupported) return e;
+    }
     switch (lay) {
         case GEMM_NT: return launch_layout<true, true>(epi, a, s);
         case GEMM_NN: return launch_layout<true, false>(epi, a, s);

@@ -1,0 +1,375 @@
+// NT GEMM (C = A B^T, both operands k-contiguous) for gfx950 with the tile
+// loads going straight from global memory into LDS.
+//
+// This is the layout of every forward projection of the decoder (fused QKV,
+// O, fused gate|up, down, LM head).  Design:
+//  * buffer_load_dwordx4 ... lds moves each 16-byte chunk from global memory
+//    into LDS without passing through registers: no staging VGPRs and no LDS
+//    store instructions.  One wave instruction fills 1 KB of LDS (64 lanes x
+//    16 bytes, in lane order), i.e. 16 tile rows of 32 k; each lane fetches
+//    the global chunk that the XOR swizzle places at its LDS slot;
+//  * k-tiles of 32 in four LDS stages, loads issued three tiles ahead, so a
+//    load has three tiles of MFMA work to arrive in; one barrier per tile,
+//    whose wait counts only the loads of the tile about to be read;
+//  * per block, buffer resources based at the block's first row bound the
+//    reads: chunks past the last valid row, and k-chunks past K (given an
+//    offset beyond the resource), read as zero, so edge tiles need no clamped
+//    addresses or masks;
+//  * fragments are double-buffered in registers: the LDS reads of the next
+//    16-deep k-step are issued before the MFMAs of the current one, and the
+//    last step of a tile runs its MFMAs after the barrier, behind the first
+//    reads of the next tile;
+//  * the MFMA takes the B fragment as its first operand, so a lane's
+//    accumulator holds 4 consecutive output columns of one row and the
+//    epilogue stores 8 or 16 bytes per lane.
+#include "kcommon.h"
+#include "kernels.h"
+
+namespace mt {
+namespace {
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+constexpr int BK = 32;                 // k per tile; an LDS row is 64 bytes
+constexpr uint32_t OOB = 0x80000000u;  // beyond every resource's extent
+
+// Physical chunk (of four 16-byte chunks) of logical chunk c in LDS row r.
+// The LDS serves a 128-bit read 16 lanes (256 bytes, all 64 banks) per
+// cycle; 16 consecutive rows span four 256-byte lines, and mixing row bits
+// 2..3 into the chunk gives them 16 distinct bank positions (measured: the
+// bits-1..2 variant doubles the LDS cycles through conflicts).
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+
+// Buffer resource (gfx9 layout): base, stride 0, extent in bytes, and the
+// default data-format word.  Reads at offsets >= extent return zero.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4_t r;
+    r.x = int(uint32_t(a));
+    r.y = int(uint32_t(a >> 32) & 0xFFFFu);
+    r.z = int(bytes);
+    r.w = 0x00020000;
+    return r;
+}
+
+// 16 bytes per lane from the buffer at byte offset voff into LDS at
+// lds_addr + 16 * lane.  Issued as inline assembly: the compiler then does
+// not treat every later LDS read as a possible reader of this load (it cannot
+// tell the stages apart) and does not insert waits for it; the kernel waits
+// on vmcnt itself.
+__device__ __forceinline__ void dma16(i32x4_t rs, uint32_t lds_addr, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_addr), "v"(voff), "s"(rs)
+                 : "memory");
+}
+
+template <int V> struct IntC { static constexpr int value = V; };
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(IntC<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+// Block barrier without the full memory fence of __syncthreads (which would
+// also wait for the loads still in flight for later tiles); LDS reads done.
+// The lgkmcnt(0) wait goes through the builtin (gfx9 encoding: vmcnt 63,
+// expcnt 7, lgkmcnt 0) so that the compiler knows the earlier fragment reads
+// have completed and adds no waits of its own after the barrier.
+__device__ __forceinline__ void barrier_lds() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Loads of one operand's ROWS x 32 tile by NW waves: NI wave instructions
+// each, instruction i of wave w covering tile rows 16*(i*NW + w) .. +15.
+template <int ROWS, int NW>
+struct DirectLoader {
+    static constexpr int NI = ROWS / (16 * NW);
+    static_assert(NI >= 1 && ROWS % (16 * NW) == 0, "tile rows must cover the waves");
+    uint32_t off[NI];  // byte offset of the lane's chunk at k = 0
+    int kk[NI];        // its first k within the tile
+
+    __device__ __forceinline__ void init(int lane, int wave, int64_t ld) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int r = (i * NW + wave) * 16 + (lane >> 2);
+            const int c = (lane & 3) ^ swz(r);
+            off[i] = uint32_t((int64_t(r) * ld + c * 8) * 2);
+            kk[i] = c * 8;
+        }
+    }
+    // Instruction i of this wave for the tile at k0.
+    __device__ __forceinline__ void issue_one(int i, i32x4_t rs, uint4* stage, int wave, int k0, int K) const {
+        const uint32_t base = uint32_t(reinterpret_cast<uintptr_t>((lds_ptr_t)stage));
+        uint32_t v = off[i] + uint32_t(k0) * 2u;
+        if (k0 + kk[i] >= K) v = OOB;
+        dma16(rs, __builtin_amdgcn_readfirstlane(base + uint32_t(i * NW + wave) * 1024u), v);
+    }
+    __device__ __forceinline__ void issue(i32x4_t rs, uint4* stage, int wave, int k0, int K) const {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) issue_one(i, rs, stage, wave, k0, K);
+    }
+};
+
+// Fragments of one 16-deep k-step: the wave's FM A row-blocks and FN B
+// row-blocks of 32, lane l holding row l%32, k = 8*(l/32)..+7 of the step.
+template <int FM, int FN, int TM, int TN>
+__device__ __forceinline__ void read_frags(const uint4* __restrict__ a_l, const uint4* __restrict__ b_l, int ks,
+                                           int wm, int wn, int lane, uint4 (&fa)[FM], uint4 (&fb)[FN]) {
+    const int kc = ks * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int r = wm * TM + i * 32 + (lane & 31);
+        fa[i] = a_l[r * 4 + (kc ^ swz(r))];
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int r = wn * TN + j * 32 + (lane & 31);
+        fb[j] = b_l[r * 4 + (kc ^ swz(r))];
+    }
+}
+
+// MFMAs number q0 .. q0+NQ-1 of a k-step, in (i, j) row-major order.
+template <int FM, int FN, bool F16, int Q0, int NQ>
+__device__ __forceinline__ void mma_part(const uint4 (&fa)[FM], const uint4 (&fb)[FN], f32x16_t (&acc)[FM][FN]) {
+#pragma unroll
+    for (int q = Q0; q < Q0 + NQ; ++q) {
+        const int i = q / FN, j = q % FN;
+        if constexpr (F16)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(fb[j]), as_f16x8(fa[i]), acc[i][j], 0, 0, 0);
+        else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fb[j]), as_bf16x8(fa[i]), acc[i][j], 0, 0, 0);
+    }
+}
+
+template <int FM, int FN, bool F16>
+__device__ __forceinline__ void mma_frags(const uint4 (&fa)[FM], const uint4 (&fb)[FN], f32x16_t (&acc)[FM][FN]) {
+    mma_part<FM, FN, F16, 0, FM * FN>(fa, fb, acc);
+}
+
+// Epilogue of 4 consecutive columns col..col+3 of one row.
+template <int EPI>
+__device__ __forceinline__ void store4(const GemmArgs& p, int row, int col, const float* v) {
+    const int64_t ci = int64_t(row) * p.ldc + col;
+    if (col + 4 <= p.N) {
+        float w[4] = {v[0], v[1], v[2], v[3]};
+        if constexpr (EPI == EPI_BF16_RESID || EPI == EPI_F32_RESID) {
+            const uint2 r = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.R) + int64_t(row) * p.ldr + col);
+            w[0] += bflo(r.x); w[1] += bfhi(r.x); w[2] += bflo(r.y); w[3] += bfhi(r.y);
+        } else if constexpr (EPI == EPI_BF16_RESID32) {
+            const float4 r = *reinterpret_cast<const float4*>(static_cast<const float*>(p.R) + int64_t(row) * p.ldr + col);
+            w[0] += r.x; w[1] += r.y; w[2] += r.z; w[3] += r.w;
+        } else if constexpr (EPI == EPI_BF16_ACCF32) {
+            const float4 r = *reinterpret_cast<const float4*>(p.Cacc + int64_t(row) * p.ldacc + col);
+            w[0] += r.x; w[1] += r.y; w[2] += r.z; w[3] += r.w;
+        } else if constexpr (EPI == EPI_F32_ACC) {
+            const float4 r = *reinterpret_cast<const float4*>(static_cast<const float*>(p.C) + ci);
+            w[0] += r.x; w[1] += r.y; w[2] += r.z; w[3] += r.w;
+        }
+        if constexpr (EPI == EPI_F32 || EPI == EPI_F32_F16IN || EPI == EPI_F32_ACC || EPI == EPI_F32_RESID)
+            *reinterpret_cast<float4*>(static_cast<float*>(p.C) + ci) = make_float4(w[0], w[1], w[2], w[3]);
+        else
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.C) + ci) = make_uint2(pack2(w[0], w[1]), pack2(w[2], w[3]));
+        return;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int c = col + e;
+        if (c >= p.N) break;
+        float w = v[e];
+        if constexpr (EPI == EPI_BF16_RESID || EPI == EPI_F32_RESID)
+            w += bf2f(static_cast<const uint16_t*>(p.R)[int64_t(row) * p.ldr + c]);
+        else if constexpr (EPI == EPI_BF16_RESID32)
+            w += static_cast<const float*>(p.R)[int64_t(row) * p.ldr + c];
+        else if constexpr (EPI == EPI_BF16_ACCF32)
+            w += p.Cacc[int64_t(row) * p.ldacc + c];
+        else if constexpr (EPI == EPI_F32_ACC)
+            w += static_cast<const float*>(p.C)[ci + e];
+        if constexpr (EPI == EPI_F32 || EPI == EPI_F32_F16IN || EPI == EPI_F32_ACC || EPI == EPI_F32_RESID)
+            static_cast<float*>(p.C)[ci + e] = w;
+        else
+            static_cast<uint16_t*>(p.C)[ci + e] = f2bf(w);
+    }
+}
+
+template <int BM, int BN, int WM, int WN, int EPI>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_nt_k(GemmArgs p, int tiles_m, int tiles_n) {
+    constexpr int NW = WM * WN;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr bool F16 = EPI == EPI_F32_F16IN;
+    // four stages, one array each, so that the compiler can tell the LDS
+    // reads of one stage from the loads in flight into another
+    __shared__ uint4 As0[BM * 4], As1[BM * 4], As2[BM * 4], As3[BM * 4];
+    __shared__ uint4 Bs0[BN * 4], Bs1[BN * 4], Bs2[BN * 4], Bs3[BN * 4];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+
+    // Blocks dispatched to one XCD (every 8th) take a contiguous range of
+    // tiles, grouped 8 deep along M so neighbours share A rows and B rows.
+    const int total = tiles_m * tiles_n;
+    int pid = blockIdx.x;
+    if ((total & 7) == 0) pid = (pid & 7) * (total >> 3) + (pid >> 3);
+    constexpr int GROUP = 8;
+    const int per_group = GROUP * tiles_n;
+    const int g = pid / per_group;
+    const int first_m = g * GROUP;
+    const int gsz = min(tiles_m - first_m, GROUP);
+    const int tm = first_m + (pid % per_group) % gsz;
+    const int tn = (pid % per_group) / gsz;
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int rows_a = min(BM, p.M - m0), rows_b = min(BN, p.N - n0);
+    const auto ra = make_rsrc(static_cast<const uint16_t*>(p.A) + int64_t(m0) * p.lda,
+                              uint32_t((int64_t(rows_a - 1) * p.lda + p.K) * 2));
+    const auto rb = make_rsrc(static_cast<const uint16_t*>(p.B) + int64_t(n0) * p.ldb,
+                              uint32_t((int64_t(rows_b - 1) * p.ldb + p.K) * 2));
+    DirectLoader<BM, NW> la;
+    DirectLoader<BN, NW> lb;
+    la.init(lane, wave, p.lda);
+    lb.init(lane, wave, p.ldb);
+    constexpr int NIT = DirectLoader<BM, NW>::NI + DirectLoader<BN, NW>::NI;  // loads per wave per tile
+
+    f32x16_t acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int nk = (p.K + BK - 1) / BK;
+    uint4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+
+#define ISSUE(SA, SB, T)                         \
+    la.issue(ra, SA, wave, (T) * BK, p.K);      \
+    lb.issue(rb, SB, wave, (T) * BK, p.K);      \
+    __builtin_amdgcn_sched_barrier(0)
+#define RD(SA, SB, KS, FA, FB) read_frags<FM, FN, TM, TN>(SA, SB, KS, wm, wn, lane, FA, FB)
+#define MM(FA, FB) mma_frags<FM, FN, F16>(FA, FB, acc)
+// The loads of a tile are spread over the MFMAs of the tile three earlier:
+// NIT/2 with each of its two k-steps, one per MG MFMAs, so the wave never
+// stalls on a full address FIFO with MFMAs left to issue.
+    constexpr int NIA = DirectLoader<BM, NW>::NI;
+    constexpr int HALF = NIT / 2;
+    constexpr int MG = FM * FN / HALF;
+    static_assert(NIT % 2 == 0 && (FM * FN) % HALF == 0, "load interleave");
+// Wait until tile T's loads have landed (those of tile T+1 and the first
+// half of tile T+2 may still be in flight), then a block barrier.
+#define WAIT_TILE(T)                                  \
+    do {                                              \
+        const int later = min(nk - 1 - (T), 2);       \
+        if (later >= 2) wait_vmem<NIT + HALF>();      \
+        else if (later == 1) wait_vmem<NIT>();        \
+        else wait_vmem<0>();                          \
+        barrier_lds();                                \
+    } while (0)
+#define LOAD_ONE(g, XA, XB, T)                                                           \
+    if constexpr ((g) < NIA) la.issue_one((g), ra, XA, wave, (T) * BK, p.K);             \
+    else lb.issue_one((g) - NIA, rb, XB, wave, (T) * BK, p.K)
+// Half h of a k-step's MFMAs interleaved with half h of tile T3's loads.
+#define MM_LOADS(FA, FB, h, XA, XB, T3, do_load)                                         \
+    static_for<0, HALF>([&](auto g_) {                                                   \
+        constexpr int g = decltype(g_)::value;                                           \
+        if (do_load) { LOAD_ONE((h) * HALF + g, XA, XB, T3); }                           \
+        mma_part<FM, FN, F16, g * MG, MG>(FA, FB, acc);                                  \
+        __builtin_amdgcn_sched_barrier(0);                                               \
+    })
+// Tile T in stage (SA, SB): read step 1 while step 0 multiplies, barrier,
+// read step 0 of tile T+1 from (NA, NB) while step 1 multiplies; the loads
+// of tile T+3 into stage (XA, XB) ride along.
+#define TILE(T, SA, SB, NA, NB, XA, XB)                                    \
+    if ((T) < nk) {                                                        \
+        const bool ld3 = (T) + 3 < nk;                                     \
+        RD(SA, SB, 1, fa1, fb1);                                           \
+        __builtin_amdgcn_sched_barrier(0);                                 \
+        MM_LOADS(fa0, fb0, 0, XA, XB, (T) + 3, ld3);                       \
+        WAIT_TILE((T) + 1);                                                \
+        if ((T) + 1 < nk) { RD(NA, NB, 0, fa0, fb0); }                     \
+        __builtin_amdgcn_sched_barrier(0);                                 \
+        MM_LOADS(fa1, fb1, 1, XA, XB, (T) + 3, ld3);                       \
+    }
+
+    ISSUE(As0, Bs0, 0);
+    if (nk > 1) { ISSUE(As1, Bs1, 1); }
+    if (nk > 2) { ISSUE(As2, Bs2, 2); }
+    WAIT_TILE(0);
+    RD(As0, Bs0, 0, fa0, fb0);
+    for (int t = 0; t < nk; t += 4) {
+        TILE(t, As0, Bs0, As1, Bs1, As3, Bs3)
+        TILE(t + 1, As1, Bs1, As2, Bs2, As0, Bs0)
+        TILE(t + 2, As2, Bs2, As3, Bs3, As1, Bs1)
+        TILE(t + 3, As3, Bs3, As0, Bs0, As2, Bs2)
+    }
+#undef TILE
+#undef MM_LOADS
+#undef LOAD_ONE
+#undef WAIT_TILE
+#undef MM
+#undef RD
+#undef ISSUE
+
+    // acc[i][j] element r of lane l: row m0 + wm*TM + 32i + l%32, column
+    // n0 + wn*TN + 32j + 8*(r/4) + 4*(l/32) + r%4.
+    const int ml = lane & 31, nq = (lane >> 5) * 4;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int row = m0 + wm * TM + i * 32 + ml;
+        if (row >= p.M) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int col = n0 + wn * TN + j * 32 + 8 * q + nq;
+                if (col >= p.N) continue;
+                const float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                store4<EPI>(p, row, col, v);
+            }
+    }
+}
+
+template <int BM, int BN, int WM, int WN>
+hipError_t launch(GemmEpi epi, const GemmArgs& a, hipStream_t s) {
+    const int tm = (a.M + BM - 1) / BM, tn = (a.N + BN - 1) / BN;
+    const dim3 grid(tm * tn), block(WM * WN * 64);
+    switch (epi) {
+        case EPI_BF16: gemm_nt_k<BM, BN, WM, WN, EPI_BF16><<<grid, block, 0, s>>>(a, tm, tn); break;
+        case EPI_BF16_RESID: gemm_nt_k<BM, BN, WM, WN, EPI_BF16_RESID><<<grid, block, 0, s>>>(a, tm, tn); break;
+        case EPI_F32: gemm_nt_k<BM, BN, WM, WN, EPI_F32><<<grid, block, 0, s>>>(a, tm, tn); break;
+        case EPI_F32_ACC: gemm_nt_k<BM, BN, WM, WN, EPI_F32_ACC><<<grid, block, 0, s>>>(a, tm, tn); break;
+        case EPI_BF16_ACCF32: gemm_nt_k<BM, BN, WM, WN, EPI_BF16_ACCF32><<<grid, block, 0, s>>>(a, tm, tn); break;
+        case EPI_F32_RESID: gemm_nt_k<BM, BN, WM, WN, EPI_F32_RESID><<<grid, block, 0, s>>>(a, tm, tn); break;
+        case EPI_BF16_RESID32: gemm_nt_k<BM, BN, WM, WN, EPI_BF16_RESID32><<<grid, block, 0, s>>>(a, tm, tn); break;
+        case EPI_F32_F16IN: gemm_nt_k<BM, BN, WM, WN, EPI_F32_F16IN><<<grid, block, 0, s>>>(a, tm, tn); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+inline bool al16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; }
+
+}  // namespace
+
+hipError_t gemm_nt_direct(GemmEpi epi, const GemmArgs& a, hipStream_t s) {
+    // Preconditions beyond gemm()'s checks: 4-column epilogue vectors stay
+    // aligned, and a block's rows x ld fit the 31-bit buffer offsets.
+    const bool resid = epi == EPI_BF16_RESID || epi == EPI_F32_RESID || epi == EPI_BF16_RESID32;
+    if ((a.ldc & 3) || !al16(a.C)) return hipErrorNotSupported;
+    if (resid && ((a.ldr & 3) || !al16(a.R))) return hipErrorNotSupported;
+    if (epi == EPI_BF16_ACCF32 && ((a.ldacc & 3) || !al16(a.Cacc))) return hipErrorNotSupported;
+    if (a.lda > (int64_t(1) << 21) || a.ldb > (int64_t(1) << 21)) return hipErrorNotSupported;
+    const int64_t big_tiles = int64_t((a.M + 255) / 256) * ((a.N + 255) / 256);
+    if (big_tiles >= 256) return launch<256, 256, 2, 4>(epi, a, s);
+    return launch<128, 128, 2, 2>(epi, a, s);
+}
+
+}  // namespace mt

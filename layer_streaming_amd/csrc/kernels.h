@@ -34,6 +34,10 @@ struct GemmArgs {
     int M, N, K;
 };
 hipError_t gemm(GemmLayout lay, GemmEpi epi, const GemmArgs& a, hipStream_t s);
+// The NT path with direct global->LDS tile loads (called by gemm() after its
+// checks); hipErrorNotSupported when its alignment or size preconditions
+// fail, and gemm() then uses the generic kernel.
+hipError_t gemm_nt_direct(GemmEpi epi, const GemmArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------- RMSNorm ----
 // n = gamma * x * rstd, rstd = 1/sqrt(mean(x^2)+eps); x bf16 or fp32 (x_f32),
