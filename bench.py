@@ -133,6 +133,10 @@ def main():
     ap.add_argument("--slot-mode", type=int, default=0)
     ap.add_argument("--resident", type=int, default=0)
     ap.add_argument("--pin-store", type=int, default=0)
+    ap.add_argument("--pin-weights", type=int, default=0)
+    ap.add_argument("--cross-step", type=int, default=0,
+                    help="1: the next step's forward overlaps this step's Adam tail (same results); on a host "
+                         "whose memory bandwidth the Adam already fills this is slower, so it is off by default")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build streams one model through one MI355X; "
@@ -149,7 +153,7 @@ def main():
     opt = mt.default_options(max_batch=B, max_seq=S, profile_kernels=0 if args.no_profile else 1,
                              host_threads=args.host_threads, n_weight_slots=args.slots, n_grad_slabs=args.slabs,
                              slot_mode=args.slot_mode, resident=args.resident, pin_store=args.pin_store,
-                             seed=synth.SEED_WEIGHTS)
+                             cross_step=args.cross_step, pin_weights=args.pin_weights, seed=synth.SEED_WEIGHTS)
     arena_bytes, pinned_bytes, store_bytes = mt.workspace_bytes(shape, opt)
     log(f"arena {arena_bytes / 1e9:.2f} GB, pinned {pinned_bytes / 1e9:.2f} GB, store {store_bytes / 1e9:.2f} GB")
     torch.cuda.init()
@@ -164,6 +168,7 @@ def main():
     for i in range(args.warmup):
         loss, st = ctx.train_step(tokens, labels)
         log(f"warmup {i}: loss {loss:.4f} step {st.step_ms:.0f} ms")
+    ctx.sync()  # queued host updates (cross_step) land before the clock starts
     torch.cuda.synchronize()
     stats = []
     t0 = time.perf_counter()
@@ -172,7 +177,8 @@ def main():
         stats.append(mt.stats_dict(st))
         log(f"step {i}: loss {loss:.4f} step {st.step_ms:.0f} ms (fwd {st.fwd_ms:.0f} head {st.head_ms:.0f} "
             f"bwd {st.bwd_ms:.0f} adam tail {st.adam_tail_ms:.0f}; adam busy {st.adam_ms:.0f}, "
-            f"pack {st.pack_ms:.0f}; overlap {st.overlap_ratio:.2f})")
+            f"pack {st.pack_ms:.0f}; waited for adam {st.adam_wait_ms:.0f}; overlap {st.overlap_ratio:.2f})")
+    ctx.sync()  # every step's host Adam is inside the timed region
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
@@ -183,7 +189,8 @@ def main():
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": cfg["workload"], "global_batch": B, "seq_len": S, "layers": cfg["n_layers"],
                       "parallelism": "single GPU, layer-streamed", "weight_slots": args.slots,
-                      "grad_slabs": args.slabs, "slot_mode": args.slot_mode, "resident": args.resident}}
+                      "grad_slabs": args.slabs, "slot_mode": args.slot_mode, "resident": args.resident,
+                      "cross_step": args.cross_step, "pin_weights": args.pin_weights}}
     mf = model_flops_per_step(cfg, T, S)
     out["model_tflops_per_s"] = round(mf / (ms_per_step / 1e3) / 1e12, 2)
 
@@ -200,7 +207,7 @@ def main():
                    "overlap_ratio": round(float(np.mean([s["overlap_ratio"] for s in stats])), 3)}
     out["phases_ms"] = {k: round(float(np.mean([s[k] for s in stats])), 1)
                         for k in ("fwd_ms", "head_ms", "bwd_ms", "adam_tail_ms", "compute_busy_ms",
-                                  "adam_ms", "pack_ms")}
+                                  "adam_ms", "adam_wait_ms", "pack_ms")}
     out["memory"] = {"gpu_arena_bytes": int(stats[0]["gpu_arena_bytes"]),
                      "gpu_mem_used_delta_bytes": int(free0 - torch.cuda.mem_get_info()[0]),
                      "pinned_bytes": int(stats[0]["pinned_bytes"]),

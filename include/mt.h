@@ -90,6 +90,16 @@ typedef struct mt_options {
     int32_t pin_store;           /* 1: allocate the host store page-locked, so H2D reads it
                                     directly instead of packing into staging; 0 (default): pageable
                                     store plus two pinned staging buffers, as on the pages */
+    int32_t cross_step;          /* 1: mt_train_step returns once the loss is known and every
+                                    unit's Adam is queued; Adam runs on, lowest unit first, and the
+                                    next step streams a unit only after its update has landed
+                                    (the next forward overlaps the Adam tail).  Same results as 0.
+                                    mt_sync, and every entry that reads or writes the store, wait
+                                    for the queued updates first.  0 (default): synchronous step */
+    int32_t pin_weights;         /* 1: the W regions of all units live in one page-locked block
+                                    (2 B/param), so StreamIn copies straight from it with no pack;
+                                    G and the optimizer state stay in the pageable tiles.  0
+                                    (default): W inside each pageable tile, packed into staging */
     uint64_t slot_bytes_override;      /* 0: largest unit's weight bytes */
     uint64_t workspace_bytes_override; /* 0: computed from max_batch*max_seq */
     float lr, beta1, beta2, adam_eps;  /* 1e-4, 0.9, 0.999, 1e-8 */
@@ -106,6 +116,8 @@ typedef struct mt_stats {
     double compute_busy_ms; /* sum of compute-stream visit spans (device clock) */
     double h2d_busy_ms, d2h_busy_ms;   /* sum of copy durations (device clock) */
     double pack_ms, adam_ms;           /* host worker busy time */
+    double adam_wait_ms;               /* time this step waited for the previous step's Adam
+                                          (cross_step) */
     double overlap_ratio;   /* |compute ∩ copies| / min(|compute|, |copies|) */
     double pcie_busy_frac;  /* |H2D| / step time */
     uint64_t h2d_bytes, d2h_bytes;
@@ -147,11 +159,17 @@ int mt_init(const mt_shape* shape, const mt_options* opt, void* gpu_arena, uint6
  * (row t = b*seq + s; copied during the call).  Runs the streamed forward,
  * the fused LM head, the recomputing backward and the host Adam (step count
  * advanced by one), then returns the mean token cross-entropy in *loss_out.
- * Synchronous: all Adam work has finished on return.  stats_out may be
- * NULL.  Errors: MT_E_INVAL (shape beyond max_batch*max_seq, token or label
+ * Synchronous unless opt->cross_step: all Adam work has finished on return.
+ * With cross_step the updates of this step may still be running on return
+ * (mt_sync waits for them).  stats_out may be NULL.  Errors: MT_E_INVAL (shape beyond max_batch*max_seq, token or label
  * outside [0, vocab), NULL pointers), MT_E_HIP, MT_E_INTERNAL, MT_E_STATE. */
 int mt_train_step(mt_ctx* ctx, const int32_t* tokens, const int32_t* labels, int32_t batch,
                   int32_t seq, float* loss_out, mt_stats* stats_out);
+
+/* Wait until every queued host Adam update has been applied to the store
+ * (a no-op for synchronous steps).  Returns the first error a host worker
+ * met since the last call (MT_E_HIP, MT_E_INTERNAL), else MT_OK. */
+int mt_sync(mt_ctx* ctx);
 
 /* Test entry: forward of decoder layer `layer` on caller-owned device
  * buffers x_dev, y_dev (BF16 [batch*seq x d_model] row-major).  Streams the

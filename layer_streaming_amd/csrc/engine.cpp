@@ -197,16 +197,17 @@ ArenaPlan plan_arena(const Layout& lay, const mt_options& o, uint8_t* base, Work
 }
 
 struct PinnedPlan {
-    uint64_t staging = 0, slab = 0, ckpt = 0, io = 0, total = 0;
+    uint64_t staging = 0, slab = 0, ckpt = 0, io = 0, weights = 0, total = 0;
 };
 PinnedPlan plan_pinned(const Layout& lay, const mt_options& o, uint64_t slot_bytes) {
     PinnedPlan p;
     const uint64_t T = uint64_t(o.max_batch) * o.max_seq;
-    p.staging = o.pin_store ? 0 : 2 * slot_bytes;
+    p.staging = (o.pin_store || o.pin_weights) ? 0 : 2 * slot_bytes;
+    p.weights = o.pin_weights ? uint64_t(lay.w_bytes) : 0;
     p.slab = uint64_t(o.n_grad_slabs) * slot_bytes;
     p.ckpt = o.ckpt_on_host ? al4k(T * lay.sh.d_model * 2) * lay.sh.n_layers : 0;
     p.io = 2 * al4k(T * lay.sh.d_model * 2) + al4k(T * 4) + 4096;
-    p.total = p.staging + p.slab + p.ckpt + p.io;
+    p.total = p.staging + p.slab + p.ckpt + p.io + p.weights;
     return p;
 }
 
@@ -218,6 +219,9 @@ int validate_options(const mt_options* o) {
     if (o->n_grad_slabs < 1 || o->n_grad_slabs > 64) MT_FAIL(MT_E_INVAL, "n_grad_slabs must be 1..64");
     if (o->slot_mode != 0 && o->slot_mode != 1) MT_FAIL(MT_E_INVAL, "slot_mode must be 0 or 1");
     if (o->head_chunk < 0) MT_FAIL(MT_E_INVAL, "head_chunk must be >= 0");
+    if (o->cross_step != 0 && o->cross_step != 1) MT_FAIL(MT_E_INVAL, "cross_step must be 0 or 1");
+    if (o->pin_weights != 0 && o->pin_weights != 1) MT_FAIL(MT_E_INVAL, "pin_weights must be 0 or 1");
+    if (o->pin_weights && o->pin_store) MT_FAIL(MT_E_INVAL, "pin_weights and pin_store exclude each other");
     if (!(o->lr >= 0.f) || !(o->beta1 >= 0.f && o->beta1 < 1.f) || !(o->beta2 >= 0.f && o->beta2 < 1.f) ||
         !(o->adam_eps > 0.f))
         MT_FAIL(MT_E_INVAL, "bad Adam hyper-parameters");
@@ -238,6 +242,7 @@ struct Ctx {
     // host
     uint8_t* store = nullptr;
     bool store_pinned = false;
+    uint8_t* wblock = nullptr;  // page-locked W regions (pin_weights)
     uint8_t* staging[2] = {};
     std::vector<uint8_t*> slabs;
     uint8_t* ckpt_host = nullptr;
@@ -260,11 +265,17 @@ struct Ctx {
     std::thread slab_thread;
     std::mutex q_mu;
     std::condition_variable q_cv, free_cv;
+    // One host Adam update of a unit; slab < 0: the gradient is already in
+    // the store's G region (the input embedding).  Carries its own step's
+    // hyper-parameters: with cross_step it may run during the next step.
     struct Job {
         int unit, slab;
         int64_t elems;
+        AdamStep a;
     };
     std::deque<Job> jobs;
+    std::vector<int64_t> adam_gen;  // updates applied per unit
+    double adam_wait_ms = 0.0;
     std::vector<int> free_slabs;
     bool stop = false;
     int jobs_pending = 0;
@@ -354,6 +365,7 @@ struct Ctx {
     int acquire_slab();
     void enqueue_job(int unit, int slab);
     int drain_jobs();
+    int wait_adam(int unit);
     int hip_fail(hipError_t e, const char* what) {
         failed = true;
         set_error(strfmt("HIP error '%s' in %s", hipGetErrorString(e), what));
@@ -426,14 +438,22 @@ int Ctx::init(const mt_shape& sh, const mt_options& o, void* arena_, uint64_t by
         madvise(p, lay.store_bytes, MADV_HUGEPAGE);
         store = static_cast<uint8_t*>(p);
     }
+    if (opt.pin_weights) {
+        void* p = nullptr;
+        if (hipHostMalloc(&p, lay.w_bytes, hipHostMallocDefault) != hipSuccess || !p)
+            MT_FAIL(MT_E_NOMEM, "cannot allocate a pinned weight block of %lld bytes", (long long)lay.w_bytes);
+        wblock = static_cast<uint8_t*>(p);
+    }
     {
         ThreadPool init_pool(nth);
-        for (int u = 0; u < int(lay.units.size()); ++u) init_unit(init_pool, store, lay, u, opt.seed, opt.init_std);
+        for (int u = 0; u < int(lay.units.size()); ++u)
+            init_unit(init_pool, store, lay, u, opt.seed, opt.init_std, wblock);
     }
     ein_acc.assign(size_t(sh.vocab) * sh.d_model, 0.f);
+    adam_gen.assign(lay.units.size(), 0);
 
     // Pinned staging, slabs, checkpoint ring, I/O buffers.
-    if (!opt.pin_store) {
+    if (!opt.pin_store && !opt.pin_weights) {
         staging[0] = pinned_alloc(this, plan.slot_bytes);
         staging[1] = pinned_alloc(this, plan.slot_bytes);
         if (!staging[0] || !staging[1]) MT_FAIL(MT_E_NOMEM, "cannot allocate pinned staging buffers");
@@ -519,6 +539,7 @@ Ctx::~Ctx() {
         if (store_pinned) hipHostFree(store);
         else munmap(store, lay.store_bytes);
     }
+    if (wblock) hipHostFree(wblock);
 }
 
 // ------------------------------------------------------- slab worker ----
@@ -529,12 +550,17 @@ void Ctx::slab_worker() {
             std::unique_lock<std::mutex> lk(q_mu);
             q_cv.wait(lk, [&] { return stop || !jobs.empty(); });
             if (jobs.empty()) return;
-            j = jobs.front();
-            jobs.pop_front();
+            // The next forward needs the input embedding first, then the
+            // layers in order, then the head: lowest rank first.
+            auto rank = [&](const Job& x) { return x.unit == lay.embed() ? -1 : x.unit; };
+            auto it = std::min_element(jobs.begin(), jobs.end(),
+                                       [&](const Job& x, const Job& y) { return rank(x) < rank(y); });
+            j = *it;
+            jobs.erase(it);
         }
         int status = MT_OK;
         std::string err;
-        hipError_t e = hipEventSynchronize(slab_done[j.slab].e);
+        hipError_t e = j.slab >= 0 ? hipEventSynchronize(slab_done[j.slab].e) : hipSuccess;
         if (e != hipSuccess) {
             status = MT_E_HIP;
             err = strfmt("HIP error '%s' waiting for gradient slab %d", hipGetErrorString(e), j.slab);
@@ -543,8 +569,9 @@ void Ctx::slab_worker() {
             err = strfmt("injected slab-worker fault at unit %d", j.unit);
         } else {
             const auto t0 = Clock::now();
-            adam_unit(*adam_pool, tile_ptrs(store, lay, j.unit),
-                      reinterpret_cast<const uint16_t*>(slabs[j.slab]), j.elems, cur_adam);
+            const TilePtrs tp = tile_ptrs(store, lay, j.unit, wblock);
+            adam_unit(*adam_pool, tp, j.slab >= 0 ? reinterpret_cast<const uint16_t*>(slabs[j.slab]) : tp.g,
+                      j.elems, j.a);
             const double ms = ms_since(t0);
             std::lock_guard<std::mutex> lk(q_mu);
             adam_ms_acc += ms;
@@ -555,7 +582,8 @@ void Ctx::slab_worker() {
                 worker_status = status;
                 worker_error = err;
             }
-            free_slabs.push_back(j.slab);
+            if (j.slab >= 0) free_slabs.push_back(j.slab);
+            ++adam_gen[j.unit];
             --jobs_pending;
         }
         free_cv.notify_all();
@@ -575,10 +603,28 @@ int Ctx::acquire_slab() {
 void Ctx::enqueue_job(int unit, int slab) {
     {
         std::lock_guard<std::mutex> lk(q_mu);
-        jobs.push_back({unit, slab, lay.units[unit].elems});
+        jobs.push_back({unit, slab, lay.units[unit].elems, cur_adam});
         ++jobs_pending;
     }
     q_cv.notify_one();
+}
+
+// Block until `unit` carries every update of the steps run so far (with
+// cross_step the previous step's may still be queued).  A worker error
+// fails the context.
+int Ctx::wait_adam(int unit) {
+    std::unique_lock<std::mutex> lk(q_mu);
+    const auto t0 = Clock::now();
+    free_cv.wait(lk, [&] { return adam_gen[unit] >= step || worker_status != MT_OK; });
+    adam_wait_ms += ms_since(t0);
+    if (worker_status != MT_OK) {
+        failed = true;
+        set_error(worker_error);
+        const int s = worker_status;
+        worker_status = MT_OK;
+        return s;
+    }
+    return MT_OK;
 }
 
 int Ctx::drain_jobs() {
@@ -766,13 +812,15 @@ int Ctx::pick_slot(int unit, bool* need_stream) {
 // stream once the slot is released.
 int Ctx::stream_unit(int unit, int slot) {
     const uint64_t bytes = uint64_t(lay.units[unit].elems) * 2;
-    const uint8_t* src = store + lay.tile_off[unit];
+    const uint8_t* src = wblock ? wblock + lay.w_off[unit] : store + lay.tile_off[unit];
     if (unit == fault_pack) {
         failed = true;
         MT_FAIL(MT_E_INTERNAL, "injected pack fault at unit %d", unit);
     }
+    const int wa = wait_adam(unit);
+    if (wa != MT_OK) return wa;
     HIPC(wait(st_w, slot_free[slot]));
-    if (store_pinned) {
+    if (store_pinned || wblock) {
         HIPC(h2d(arena + plan.wslot[slot], src, bytes, st_w));
     } else {
         const int p = staging_ptr;
@@ -810,7 +858,11 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int B, int S, 
     tev_next = 0;
     intervals.clear();
     site_recs.clear();
-    adam_ms_acc = 0.0;
+    {
+        std::lock_guard<std::mutex> lk(q_mu);
+        adam_ms_acc = 0.0;
+        adam_wait_ms = 0.0;
+    }
     pack_ms = 0.0;
     cur_adam = adam_step_params(opt, step + 1);
     timing = true;
@@ -822,7 +874,10 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int B, int S, 
     memcpy(lab_pin, labels, size_t(T) * 4);
     HIPC(h2d(ws.labels, lab_pin, uint64_t(T) * 4, st_w));
     {
-        const TilePtrs e = tile_ptrs(store, lay, lay.embed());
+        // The previous step's update of E_in (queued with cross_step) first.
+        const int we = wait_adam(lay.embed());
+        if (we != MT_OK) return we;
+        const TilePtrs e = tile_ptrs(store, lay, lay.embed(), wblock);
         pack_pool->parallel_for(T, 64, [&](int64_t b, int64_t en) {
             for (int64_t t = b; t < en; ++t)
                 memcpy(x0_pin + t * d, e.w + int64_t(tokens[t]) * d, size_t(d) * 2);
@@ -835,8 +890,10 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int B, int S, 
     if (opt.resident) {
         // The comparison run: every unit's weights copied up once, no streaming.
         for (int u = 0; u <= lay.head(); ++u) {
+            const int wa = wait_adam(u);
+            if (wa != MT_OK) return wa;
             const uint64_t bytes = uint64_t(lay.units[u].elems) * 2;
-            HIPC(h2d(arena + plan.resident[u], store + lay.tile_off[u], bytes, st_w));
+            HIPC(h2d(arena + plan.resident[u], wblock ? wblock + lay.w_off[u] : store + lay.tile_off[u], bytes, st_w));
         }
     }
 
@@ -944,7 +1001,7 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int B, int S, 
     HIPC(hsync(dx0_done));
     const double t_bwd = ms_since(t_start);
     {
-        const TilePtrs e = tile_ptrs(store, lay, lay.embed());
+        const TilePtrs e = tile_ptrs(store, lay, lay.embed(), wblock);
         // Clear last step's rows, then accumulate this step's in fp32.
         for (int32_t r : ein_touched) memset(e.g + int64_t(r) * d, 0, size_t(d) * 2);
         std::vector<char> seen(size_t(V), 0);
@@ -955,7 +1012,7 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int B, int S, 
                 ein_touched.push_back(tokens[t]);
             }
         float* acc = ein_acc.data();
-        adam_pool->parallel_for(d, 64, [&](int64_t c0, int64_t c1) {
+        pack_pool->parallel_for(d, 64, [&](int64_t c0, int64_t c1) {
             for (int32_t r : ein_touched)
                 for (int64_t c = c0; c < c1; ++c) acc[int64_t(r) * d + c] = 0.f;
             for (int t = 0; t < T; ++t) {
@@ -971,12 +1028,22 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int B, int S, 
             failed = true;
             MT_FAIL(MT_E_INTERNAL, "injected slab-worker fault at unit %d", lay.embed());
         }
-        const auto t0 = Clock::now();
-        adam_unit(*adam_pool, e, e.g, lay.units[lay.embed()].elems, cur_adam);
-        std::lock_guard<std::mutex> lk(q_mu);
-        adam_ms_acc += ms_since(t0);
+        enqueue_job(lay.embed(), -1);
     }
-    const int jr = drain_jobs();
+    // Synchronous step: every update lands before returning.  cross_step:
+    // they run on; report a worker error that has already happened.
+    int jr = MT_OK;
+    if (!opt.cross_step) {
+        jr = drain_jobs();
+    } else {
+        std::lock_guard<std::mutex> lk(q_mu);
+        if (worker_status != MT_OK) {
+            failed = true;
+            set_error(worker_error);
+            jr = worker_status;
+            worker_status = MT_OK;
+        }
+    }
     HIPC(hsync(loss_done));
     HIPC(hipStreamSynchronize(st_c));
     HIPC(hipStreamSynchronize(st_w));
@@ -1048,7 +1115,11 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int B, int S, 
         stats->overlap_ratio = std::min(lc, lx) > 0 ? inter / std::min(lc, lx) : 0.0;
         stats->pcie_busy_frac = t_total > 0 ? len(Hm) / t_total : 0.0;
         stats->pack_ms = pack_ms;
-        stats->adam_ms = adam_ms_acc;
+        {
+            std::lock_guard<std::mutex> lk(q_mu);
+            stats->adam_ms = adam_ms_acc;
+            stats->adam_wait_ms = adam_wait_ms;
+        }
         stats->gpu_arena_bytes = plan.total;
         stats->pinned_bytes = pplan.total;
         stats->host_store_bytes = uint64_t(lay.store_bytes);
@@ -1138,6 +1209,8 @@ int mt_default_options(mt_options* o) {
     o->head_chunk = 0;
     o->profile_kernels = 0;
     o->pin_store = 0;
+    o->cross_step = 0;
+    o->pin_weights = 0;
     o->lr = 1e-4f;
     o->beta1 = 0.9f;
     o->beta2 = 0.999f;
@@ -1252,7 +1325,9 @@ int mt_get_tensor(mt_ctx* c, int32_t unit, int32_t idx, int32_t which, void* dst
     const mt::TensorDesc& t = u.t[idx];
     const uint64_t n = uint64_t(t.rows * t.cols), es = which <= MT_G ? 2 : 4;
     if (bytes != n * es) MT_FAIL(MT_E_INVAL, "bytes %llu != %llu", (unsigned long long)bytes, (unsigned long long)(n * es));
-    const mt::TilePtrs p = mt::tile_ptrs(c->impl.store, lay, unit);
+    const int ds = c->impl.drain_jobs();  // updates still queued by a cross-step train step
+    if (ds != MT_OK) return ds;
+    const mt::TilePtrs p = mt::tile_ptrs(c->impl.store, lay, unit, c->impl.wblock);
     const void* src = which == MT_W ? static_cast<const void*>(p.w + t.off)
                     : which == MT_G ? static_cast<const void*>(p.g + t.off)
                     : which == MT_MASTER ? static_cast<const void*>(p.master + t.off)
@@ -1275,7 +1350,9 @@ int mt_set_tensor(mt_ctx* c, int32_t unit, int32_t idx, int32_t which, const voi
     const mt::TensorDesc& t = u.t[idx];
     const uint64_t n = uint64_t(t.rows * t.cols), es = which <= MT_G ? 2 : 4;
     if (bytes != n * es) MT_FAIL(MT_E_INVAL, "bytes %llu != %llu", (unsigned long long)bytes, (unsigned long long)(n * es));
-    const mt::TilePtrs p = mt::tile_ptrs(c->impl.store, lay, unit);
+    const int ds = c->impl.drain_jobs();
+    if (ds != MT_OK) return ds;
+    const mt::TilePtrs p = mt::tile_ptrs(c->impl.store, lay, unit, c->impl.wblock);
     void* dst = which == MT_W ? static_cast<void*>(p.w + t.off)
               : which == MT_G ? static_cast<void*>(p.g + t.off)
               : which == MT_MASTER ? static_cast<void*>(p.master + t.off)
@@ -1283,6 +1360,14 @@ int mt_set_tensor(mt_ctx* c, int32_t unit, int32_t idx, int32_t which, const voi
                               : static_cast<void*>(p.v + t.off);
     memcpy(dst, srcp, bytes);
     return MT_OK;
+}
+
+int mt_sync(mt_ctx* c) {
+    if (!c) {
+        mt::set_error("ctx is NULL");
+        return MT_E_INVAL;
+    }
+    return c->impl.drain_jobs();
 }
 
 int mt_step_count(mt_ctx* c, int64_t* out) {

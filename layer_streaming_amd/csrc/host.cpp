@@ -91,6 +91,12 @@ Layout make_layout(const mt_shape& sh) {
         off += (u.tile_bytes() + 4095) & ~int64_t(4095);
     }
     lay.store_bytes = off;
+    int64_t woff = 0;
+    for (auto& u : lay.units) {
+        lay.w_off.push_back(woff);
+        woff += (u.elems * 2 + 4095) & ~int64_t(4095);
+    }
+    lay.w_bytes = woff;
     lay.max_stream_elems = std::max(ly.elems, hd.elems);
     int64_t per_layer = 0;
     for (int i = 0; i < 9; ++i) per_layer += ly.t[i].rows * ly.t[i].cols;
@@ -204,9 +210,9 @@ static constexpr uint64_t GOLDEN = 0x9E3779B97F4A7C15ull;
 static inline uint64_t splitmix_at(uint64_t key, uint64_t n) { return splitmix_mix(key + (n + 1) * GOLDEN); }
 
 void init_unit(ThreadPool& pool, uint8_t* store, const Layout& lay, int unit, uint64_t seed,
-               float std_) {
+               float std_, uint8_t* wblock) {
     const UnitLayout& u = lay.units[unit];
-    const TilePtrs p = tile_ptrs(store, lay, unit);
+    const TilePtrs p = tile_ptrs(store, lay, unit, wblock);
     const int64_t n = u.elems;
     // Zero everything first (padding included), in parallel: first touch.
     pool.parallel_for(n, 1 << 16, [&](int64_t b, int64_t e) {

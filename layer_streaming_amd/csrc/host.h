@@ -55,6 +55,10 @@ struct Layout {
     std::vector<UnitLayout> units;   // L layers, head, embedding
     std::vector<int64_t> tile_off;   // byte offset of each tile in the store
     int64_t store_bytes = 0;
+    // With the weights kept apart in one page-locked block: byte offset of
+    // each unit's W region in that block, and its size.
+    std::vector<int64_t> w_off;
+    int64_t w_bytes = 0;
     int64_t max_stream_elems = 0;    // largest streamed unit (layers, head)
     int64_t n_params = 0;            // unpadded parameter count
     int L() const { return sh.n_layers; }
@@ -64,7 +68,8 @@ struct Layout {
 int validate_shape(const mt_shape* sh);
 Layout make_layout(const mt_shape& sh);
 
-// Host pointers into a unit tile.
+// Host pointers into a unit tile.  With `wblock` (the page-locked weight
+// block) W points there instead of into the tile.
 struct TilePtrs {
     uint16_t* w;
     uint16_t* g;
@@ -72,11 +77,11 @@ struct TilePtrs {
     float* m;
     float* v;
 };
-inline TilePtrs tile_ptrs(uint8_t* store, const Layout& lay, int unit) {
+inline TilePtrs tile_ptrs(uint8_t* store, const Layout& lay, int unit, uint8_t* wblock = nullptr) {
     uint8_t* b = store + lay.tile_off[unit];
     const int64_t n = lay.units[unit].elems;
     TilePtrs p;
-    p.w = reinterpret_cast<uint16_t*>(b);
+    p.w = reinterpret_cast<uint16_t*>(wblock ? wblock + lay.w_off[unit] : b);
     p.g = reinterpret_cast<uint16_t*>(b + 2 * n);
     p.master = reinterpret_cast<float*>(b + 4 * n);
     p.m = reinterpret_cast<float*>(b + 8 * n);
@@ -132,7 +137,7 @@ void parallel_copy(ThreadPool& pool, void* dst, const void* src, int64_t bytes);
 // SplitMix64 stream per tensor and Box-Muller, rounded to bf16; gains 1.0;
 // master = W; G = m = v = 0; padding 0.
 void init_unit(ThreadPool& pool, uint8_t* store, const Layout& lay, int unit, uint64_t seed,
-               float std_);
+               float std_, uint8_t* wblock = nullptr);
 
 // Adam hyper-parameters for one step (bias corrections already computed).
 struct AdamStep {

@@ -32,7 +32,8 @@ class mt_options(C.Structure):
     _fields_ = [("max_batch", C.c_int32), ("max_seq", C.c_int32), ("n_weight_slots", C.c_int32),
                 ("n_grad_slabs", C.c_int32), ("slot_mode", C.c_int32), ("ckpt_on_host", C.c_int32),
                 ("resident", C.c_int32), ("host_threads", C.c_int32), ("head_chunk", C.c_int32),
-                ("profile_kernels", C.c_int32), ("pin_store", C.c_int32),
+                ("profile_kernels", C.c_int32), ("pin_store", C.c_int32), ("cross_step", C.c_int32),
+                ("pin_weights", C.c_int32),
                 ("slot_bytes_override", C.c_uint64), ("workspace_bytes_override", C.c_uint64),
                 ("lr", C.c_float), ("beta1", C.c_float), ("beta2", C.c_float), ("adam_eps", C.c_float),
                 ("init_std", C.c_float), ("seed", C.c_uint64)]
@@ -42,7 +43,8 @@ class mt_stats(C.Structure):
     _fields_ = [("step_ms", C.c_double), ("fwd_ms", C.c_double), ("head_ms", C.c_double),
                 ("bwd_ms", C.c_double), ("adam_tail_ms", C.c_double), ("compute_busy_ms", C.c_double),
                 ("h2d_busy_ms", C.c_double), ("d2h_busy_ms", C.c_double), ("pack_ms", C.c_double),
-                ("adam_ms", C.c_double), ("overlap_ratio", C.c_double), ("pcie_busy_frac", C.c_double),
+                ("adam_ms", C.c_double), ("adam_wait_ms", C.c_double), ("overlap_ratio", C.c_double),
+                ("pcie_busy_frac", C.c_double),
                 ("h2d_bytes", C.c_uint64), ("d2h_bytes", C.c_uint64), ("gpu_arena_bytes", C.c_uint64),
                 ("pinned_bytes", C.c_uint64), ("host_store_bytes", C.c_uint64), ("n_sites", C.c_int32),
                 ("site_ms", C.c_double * MT_MAX_SITES), ("site_launches", C.c_uint64 * MT_MAX_SITES)]
@@ -70,6 +72,7 @@ _SIGS = {
     "mt_get_tensor": (C.c_int, [_P, C.c_int32, C.c_int32, C.c_int32, _P, C.c_uint64]),
     "mt_set_tensor": (C.c_int, [_P, C.c_int32, C.c_int32, C.c_int32, _P, C.c_uint64]),
     "mt_step_count": (C.c_int, [_P, C.POINTER(C.c_int64)]),
+    "mt_sync": (C.c_int, [_P]),
     "mt_site_name": (C.c_char_p, [C.c_int32]),
     "mt_destroy": (None, [_P]),
     "mt_strerror": (C.c_char_p, [C.c_int]),
@@ -226,6 +229,9 @@ class Context:
         dt = np.uint16 if which in (MT_W, MT_G) else np.float32
         a = np.ascontiguousarray(arr, dtype=dt)
         check(lib.mt_set_tensor(self._ptr, unit, idx, which, a.ctypes.data, a.nbytes), "mt_set_tensor")
+
+    def sync(self):
+        check(lib.mt_sync(self._ptr), "mt_sync")
 
     def step_count(self):
         v = C.c_int64()

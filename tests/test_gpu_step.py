@@ -163,7 +163,9 @@ def test_multi_chunk_head_parity():
 
 # ------------------------------------------------------- bit identity ----
 VARIANTS = [dict(resident=1), dict(n_weight_slots=1), dict(n_weight_slots=3), dict(n_grad_slabs=1),
-            dict(slot_mode=1), dict(ckpt_on_host=0), dict(host_threads=3), dict(pin_store=1)]
+            dict(slot_mode=1), dict(ckpt_on_host=0), dict(host_threads=3), dict(pin_store=1),
+            dict(cross_step=1), dict(cross_step=1, n_grad_slabs=1), dict(cross_step=1, resident=1),
+            dict(pin_weights=1), dict(pin_weights=1, cross_step=1)]
 
 
 def _run_two_steps(kw, B, S, **opts):
@@ -242,6 +244,27 @@ def test_injected_slab_worker_fault_is_reported(monkeypatch):
     with pytest.raises(mt.MTError) as e:
         ctx.train_step(tokens, labels)
     assert e.value.status == mt.MT_E_INTERNAL
+    with pytest.raises(mt.MTError) as e:
+        ctx.train_step(tokens, labels)
+    assert e.value.status == mt.MT_E_STATE
+    ctx.close()
+
+
+def test_injected_slab_worker_fault_with_cross_step(monkeypatch):
+    """With cross_step the failing update may land after mt_train_step has
+    returned: then mt_sync reports it; either way the context is failed."""
+    monkeypatch.setenv("MT_FAULT", "slab:1")
+    ctx = make_ctx(CFG1, 1, 16, cross_step=1)
+    tokens, labels = synth.tokens_labels(1, 1, 16, 1024)
+    statuses = []
+    for call in (lambda: ctx.train_step(tokens, labels), ctx.sync):
+        try:
+            call()
+            statuses.append(mt.MT_OK)
+        except mt.MTError as e:
+            statuses.append(e.status)
+    log(f"  statuses {statuses}")
+    assert mt.MT_E_INTERNAL in statuses
     with pytest.raises(mt.MTError) as e:
         ctx.train_step(tokens, labels)
     assert e.value.status == mt.MT_E_STATE
