@@ -550,11 +550,15 @@ void Ctx::slab_worker() {
             std::unique_lock<std::mutex> lk(q_mu);
             q_cv.wait(lk, [&] { return stop || !jobs.empty(); });
             if (jobs.empty()) return;
-            // The next forward needs the input embedding first, then the
-            // layers in order, then the head: lowest rank first.
+            // Synchronous steps: arrival order, which frees the slabs in the
+            // order the backward needs them.  cross_step: the next forward
+            // needs the input embedding first, then the layers in order,
+            // then the head, so the lowest rank goes first.
             auto rank = [&](const Job& x) { return x.unit == lay.embed() ? -1 : x.unit; };
-            auto it = std::min_element(jobs.begin(), jobs.end(),
-                                       [&](const Job& x, const Job& y) { return rank(x) < rank(y); });
+            auto it = !opt.cross_step ? jobs.begin()
+                                      : std::min_element(jobs.begin(), jobs.end(), [&](const Job& x, const Job& y) {
+                                            return rank(x) < rank(y);
+                                        });
             j = *it;
             jobs.erase(it);
         }
