@@ -44,6 +44,27 @@ SHAPES = {
 }
 
 
+# HBM bytes per launch of the dominant kernel (the gate|up GEMM at the 7B
+# shape) from two rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE), each scaled
+# by the same counter's reading for a 1 GiB device copy; see
+# profiles/gemm_gateup_traffic_7b.md.  Valid only for the kernel source it was
+# taken on: reported as null once that file changes.
+TRAFFIC = {"source": "layer_streaming_amd/csrc/gemm_nt.hip",
+           "sha256": "0307c32f1be5fb112dfb08bbd0eb4987b477e0d4b5dff3a94637de1302881148",
+           "fetch_bytes": 3317995274, "write_bytes": 683473451}
+
+
+def traffic_bytes():
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, TRAFFIC["source"]), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != TRAFFIC["sha256"]:
+                return None
+    except OSError:
+        return None
+    return TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -64,6 +85,38 @@ def gemm_flops(cfg, T):
     return f
 
 
+def head_gemm_flops(cfg, T):
+    """The LM head's three products over all token chunks (one launch each per chunk)."""
+    return 2 * T * cfg["vocab"] * cfg["d_model"]
+
+
+def hbm_bytes(cfg, T):
+    """Algorithmic HBM bytes per launch of the bandwidth-bound kernel sites."""
+    d, F = cfg["d_model"], cfg["ffn_dim"]
+    nqkv = (cfg["n_heads"] + 2 * cfg["n_kv_heads"]) * cfg["head_dim"]
+    return {
+        "rms1_fwd": T * d * 2 + 2 * T * d * 2 + T * 4,     # x in; n (bf16) and n (fp16) out; rstd
+        "rms2_fwd": T * d * 4 + T * d * 2 + T * 4,         # fp32 h1 in; n2 out; rstd
+        "rope_fwd": T * nqkv * 4 + T * nqkv * 2,           # fp32 projection in; q, k fp16 and v bf16 out
+        "swiglu_fwd": T * 2 * F * 2 + T * F * 2,           # gate|up in; m out
+        "swiglu_bwd": T * F * 2 + T * 2 * F * 2 + T * 2 * F * 2,  # dm, gate|up in; dgate|dup out
+    }
+
+
+def host_bytes_per_step(cfg, T):
+    """Host DRAM bytes one synchronous step moves: Adam 30 B/param over every
+    unit, the pack (read W, streaming write to staging) and the DMA read of
+    staging for the forward and the backward visit of every streamed unit,
+    the DMA write of every streamed unit's gradient, the checkpoint ring out
+    and back in, and the embedding rows."""
+    L, d, F, V = cfg["n_layers"], cfg["d_model"], cfg["ffn_dim"], cfg["vocab"]
+    hq, hkv, hd = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    p_layer = d * hq * hd + 2 * d * hkv * hd + hq * hd * d + 3 * d * F + 2 * d
+    streamed = L * p_layer + V * d + d
+    p_embed = V * d
+    return 30 * (streamed + p_embed) + 2 * (4 + 2) * streamed + 2 * streamed + 2 * L * T * d * 2 + 2 * T * d * 2
+
+
 def model_flops_per_step(cfg, T, S):
     """6 * params * tokens for the matmuls plus causal attention (fwd 2 matmuls
     of 2*S/2*hd per query-head on average, x3 for fwd+bwd); recompute excluded."""
@@ -72,6 +125,23 @@ def model_flops_per_step(cfg, T, S):
     p_lin = d * hq * hd + 2 * d * hkv * hd + hq * hd * d + 3 * d * F
     attn_fwd = 2 * 2 * T * hq * hd * (S + 1) / 2
     return 6 * p_lin * L * T + 6 * T * d * V + 3 * attn_fwd * L
+
+
+def host_adam_probe(mt, n=256 << 20):
+    """Host DRAM rate the library's Adam reaches on its own (all threads,
+    30 B/param), the yardstick for the step's host traffic."""
+    w = np.zeros(n, np.uint16)
+    g = np.zeros(n, np.uint16)
+    gs = np.full(n, 0x3A83, np.uint16)
+    ms, m, v = np.ones(n, np.float32), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    best = 1e9
+    for _ in range(3):
+        t0 = time.perf_counter()
+        mt.check(mt.lib.mt_host_adam(w.ctypes.data, g.ctypes.data, ms.ctypes.data, m.ctypes.data, v.ctypes.data,
+                                     gs.ctypes.data, n, 1, 1e-4, 0.9, 0.999, 1e-8, min(16, os.cpu_count() or 1)),
+                 "mt_host_adam")
+        best = min(best, time.perf_counter() - t0)
+    return round(30 * n / best / 1e9, 1)
 
 
 def cpu_baseline(ctx, cfg, mt):
@@ -193,6 +263,15 @@ def main():
                       "cross_step": args.cross_step, "pin_weights": args.pin_weights}}
     mf = model_flops_per_step(cfg, T, S)
     out["model_tflops_per_s"] = round(mf / (ms_per_step / 1e3) / 1e12, 2)
+    # hardware FLOPs add the recomputed forward of every layer (the down GEMM
+    # is not recomputed: backward needs its input, not its output)
+    fl0 = gemm_flops(cfg, T)
+    recompute = cfg["n_layers"] * (fl0["gemm_qkv"] + fl0["gemm_o"] + fl0["gemm_gateup"] +
+                                   2 * 2 * T * cfg["n_heads"] * cfg["head_dim"] * (S + 1) / 2)
+    out["hw_tflops_per_s"] = round((mf + recompute) / (ms_per_step / 1e3) / 1e12, 2)
+    hb_step = host_bytes_per_step(cfg, T)
+    out["host_memory"] = {"bytes_per_step": int(hb_step), "achieved_GBps": round(hb_step / (ms_per_step / 1e3) / 1e9, 1),
+                          "adam_alone_GBps": host_adam_probe(mt)}
 
     # Transfer and overlap figures (device clock, averaged over timed steps).
     h2d_b = np.mean([s["h2d_bytes"] for s in stats])
@@ -224,13 +303,22 @@ def main():
         g_fl = sum(fl[k] * sites[k][1] for k in fl if k in sites)
         out["mfma_util_block_gemms"] = round(g_fl / (g_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4) if g_ms else None
         out["kernel_ms_per_step"] = {k: round(v[0] / len(stats), 3) for k, v in sorted(sites.items())}
+        out["gemm_tflops"] = {k: round(fl[k] * sites[k][1] / (sites[k][0] / 1e3) / 1e12, 1)
+                              for k in fl if k in sites and sites[k][0] > 0}
+        hf = head_gemm_flops(cfg, T)
+        for k in ("head_logits", "head_dx", "head_dw"):
+            if k in sites and sites[k][0] > 0:
+                out["gemm_tflops"][k] = round(hf * len(stats) / (sites[k][0] / 1e3) / 1e12, 1)
+        hb = hbm_bytes(cfg, T)
+        out["hbm_kernels_GBps"] = {k: round(hb[k] * sites[k][1] / (sites[k][0] / 1e3) / 1e9, 1)
+                                   for k in hb if k in sites and sites[k][0] > 0}
         dom = "gemm_gateup"
         ms, n = sites[dom]
         avg_ms = ms / n
         achieved = fl[dom] / (avg_ms / 1e3) / 1e12
         out["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                           "traffic": None, "avg_launch_ms": round(avg_ms, 4), "launches": n,
+                           "traffic": traffic_bytes(), "avg_launch_ms": round(avg_ms, 4), "launches": n,
                            "flops_per_launch": fl[dom]}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(ctx, cfg, mt)
