@@ -127,6 +127,27 @@ def model_flops_per_step(cfg, T, S):
     return 6 * p_lin * L * T + 6 * T * d * V + 3 * attn_fwd * L
 
 
+def traffic_probe(torch, mt, cfg):
+    """The dominant GEMM (gate|up, NT, bf16, random operands) three times,
+    then a 1 GiB fill and three 1 GiB device copies as the counters'
+    yardstick of known size."""
+    M, N, K = cfg["batch"] * cfg["seq"], 2 * cfg["ffn_dim"], cfg["d_model"]
+    g = torch.Generator(device="cpu").manual_seed(0)
+    A = torch.randn(M, K, generator=g).to("cuda", torch.bfloat16)
+    B = torch.randn(N, K, generator=g).to("cuda", torch.bfloat16)
+    C = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
+    s = torch.cuda.current_stream().cuda_stream
+    for _ in range(3):
+        mt.check(mt.lib.mt_k_gemm(0, 0, A.data_ptr(), K, B.data_ptr(), K, C.data_ptr(), N, None, 0, None, 0,
+                                  M, N, K, s), "gemm")
+    x = torch.ones(1 << 29, device="cuda", dtype=torch.int16)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    log("traffic probe done")
+
+
 def host_adam_probe(mt, n=256 << 20):
     """Host DRAM rate the library's Adam reaches on its own (all threads,
     30 B/param), the yardstick for the step's host traffic."""
@@ -204,6 +225,9 @@ def main():
     ap.add_argument("--resident", type=int, default=0)
     ap.add_argument("--pin-store", type=int, default=0)
     ap.add_argument("--pin-weights", type=int, default=0)
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="only launch the gate|up GEMM three times and a 1 GiB device copy three times (run "
+                         "under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE to measure the GEMM's HBM traffic)")
     ap.add_argument("--cross-step", type=int, default=0,
                     help="1: the next step's forward overlaps this step's Adam tail (same results); on a host "
                          "whose memory bandwidth the Adam already fills this is slower, so it is off by default")
@@ -216,6 +240,9 @@ def main():
     import torch
     from layer_streaming_amd import mt, synth
     cfg = SHAPES[args.config]
+    if args.traffic_probe:
+        traffic_probe(torch, mt, cfg)
+        return
     B, S = cfg["batch"], cfg["seq"]
     T = B * S
     shape = mt.make_shape(cfg["n_layers"], cfg["d_model"], cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"],
