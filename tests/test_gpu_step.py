@@ -94,12 +94,11 @@ def test_layer_fwd_bwd_parity(kw, B, S):
 # ------------------------------------------------------------ full step --
 # Gradients are compared per streamed unit (a layer's, the head's and the
 # embedding's whole BF16 gradient tile, the granularity gradients leave the
-# GPU in) on every workload, and per tensor on the tiny-LM workload itself
-# (2 layers, d 256, MHA 4x64, ffn 688, vocab 1024, batch 2 x seq 128).  All
-# at normwise relative error <= 1e-2.  On the other shapes the attention
-# projections' gradients (dWq, dWk) sit at the bf16-operand rounding floor,
-# 1.0-1.1e-2 per tensor, which a float64 emulation of the same rounding
-# points reproduces (see the design notes), so they are bounded per unit.
+# GPU in) on every workload, and per tensor on all but the GQA B3 x S40
+# shape, all at normwise relative error <= 1e-2.  There the attention query
+# projection's gradient of layer 1 sits at the floor of the remaining bf16
+# roundings (1.000e-2 measured), so that shape is bounded per unit and its
+# per-tensor errors are logged.
 def _cmp_units(ctx, kw, g_ref, per_tensor):
     L = kw["n_layers"]
     units = [(i, ostep.LAYER_TENSORS, g_ref["layers"][i], f"L{i}") for i in range(L)]
@@ -116,7 +115,7 @@ def _cmp_units(ctx, kw, g_ref, per_tensor):
 
 
 @pytest.mark.parametrize("kw,B,S,per_tensor", [(CFG1, 2, 128, True), (GQA, 3, 40, False),
-                                               (HD128, 2, 100, False), (HD128, 1, 1, True)])
+                                               (HD128, 2, 100, True), (HD128, 1, 1, True)])
 def test_train_step_parity(kw, B, S, per_tensor):
     log(f"train step {kw} B={B} S={S}")
     ctx = make_ctx(kw, B, S)
@@ -157,7 +156,7 @@ def test_multi_chunk_head_parity():
     assert abs(loss - loss_ref) / abs(loss_ref) <= 1e-2
     L = kw["n_layers"]
     assert_close(widen(ctx.get_tensor(L, 1, mt.MT_G)), g_ref["head"]["e_out"], "head.de_out")
-    _cmp_units(ctx, kw, g_ref, per_tensor=False)
+    _cmp_units(ctx, kw, g_ref, per_tensor=True)
     ctx.close()
 
 
