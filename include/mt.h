@@ -96,6 +96,12 @@ typedef struct mt_options {
                                     (the next forward overlaps the Adam tail).  Same results as 0.
                                     mt_sync, and every entry that reads or writes the store, wait
                                     for the queued updates first.  0 (default): synchronous step */
+    int32_t ckpt_interval;       /* k >= 1: the forward keeps every k-th layer input (layers 0, k,
+                                    2k, ...); the backward restores a block's first input, re-runs
+                                    the forward of the block's first k-1 layers to rebuild the
+                                    others, then runs the block's backward ([Argon] block-wise
+                                    recomputation).  1 (default): every layer's input.  k > 1 needs
+                                    ckpt_on_host = 1 */
     int32_t pin_weights;         /* 1: the W regions of all units live in one page-locked block
                                     (2 B/param), so StreamIn copies straight from it with no pack;
                                     G and the optimizer state stay in the pageable tiles.  0

@@ -99,6 +99,13 @@ int64_t head_chunk_of(const mt_options& o, int64_t T) {
     return std::max<int64_t>(1, std::min<int64_t>(c, T));
 }
 
+// Checkpoint interval, capped at the depth, and the host ring entries it needs.
+int ckpt_k(const mt_options& o, const mt_shape& sh) { return std::max(1, std::min(o.ckpt_interval, sh.n_layers)); }
+int ckpt_slots(const mt_options& o, const mt_shape& sh) {
+    const int k = ckpt_k(o, sh);
+    return (sh.n_layers + k - 1) / k;
+}
+
 void plan_workspace(const Layout& lay, const mt_options& o, Carver& cv, Workspace& ws) {
     const mt_shape& sh = lay.sh;
     const int64_t T = int64_t(o.max_batch) * o.max_seq;
@@ -110,8 +117,8 @@ void plan_workspace(const Layout& lay, const mt_options& o, Carver& cv, Workspac
     if (o.ckpt_on_host) {
         ws.x[0] = cv.take<uint16_t>(td);
         ws.x[1] = cv.take<uint16_t>(td);
-        ws.xc[0] = cv.take<uint16_t>(td);
-        ws.xc[1] = cv.take<uint16_t>(td);
+        ws.xc.assign(size_t(2 * ckpt_k(o, sh)), nullptr);
+        for (auto& b : ws.xc) b = cv.take<uint16_t>(td);
     } else {
         ws.ckpt_dev = cv.take<uint16_t>(td * uint64_t(sh.n_layers + 1));
     }
@@ -205,7 +212,7 @@ PinnedPlan plan_pinned(const Layout& lay, const mt_options& o, uint64_t slot_byt
     p.staging = (o.pin_store || o.pin_weights) ? 0 : 2 * slot_bytes;
     p.weights = o.pin_weights ? uint64_t(lay.w_bytes) : 0;
     p.slab = uint64_t(o.n_grad_slabs) * slot_bytes;
-    p.ckpt = o.ckpt_on_host ? al4k(T * lay.sh.d_model * 2) * lay.sh.n_layers : 0;
+    p.ckpt = o.ckpt_on_host ? al4k(T * lay.sh.d_model * 2) * ckpt_slots(o, lay.sh) : 0;
     p.io = 2 * al4k(T * lay.sh.d_model * 2) + al4k(T * 4) + 4096;
     p.total = p.staging + p.slab + p.ckpt + p.io + p.weights;
     return p;
@@ -220,6 +227,8 @@ int validate_options(const mt_options* o) {
     if (o->slot_mode != 0 && o->slot_mode != 1) MT_FAIL(MT_E_INVAL, "slot_mode must be 0 or 1");
     if (o->head_chunk < 0) MT_FAIL(MT_E_INVAL, "head_chunk must be >= 0");
     if (o->cross_step != 0 && o->cross_step != 1) MT_FAIL(MT_E_INVAL, "cross_step must be 0 or 1");
+    if (o->ckpt_interval < 1) MT_FAIL(MT_E_INVAL, "ckpt_interval must be >= 1");
+    if (o->ckpt_interval > 1 && !o->ckpt_on_host) MT_FAIL(MT_E_INVAL, "ckpt_interval > 1 needs ckpt_on_host = 1");
     if (o->pin_weights != 0 && o->pin_weights != 1) MT_FAIL(MT_E_INVAL, "pin_weights must be 0 or 1");
     if (o->pin_weights && o->pin_store) MT_FAIL(MT_E_INVAL, "pin_weights and pin_store exclude each other");
     if (!(o->lr >= 0.f) || !(o->beta1 >= 0.f && o->beta1 < 1.f) || !(o->beta2 >= 0.f && o->beta2 < 1.f) ||
@@ -467,7 +476,7 @@ int Ctx::init(const mt_shape& sh, const mt_options& o, void* arena_, uint64_t by
     const uint64_t T = uint64_t(opt.max_batch) * opt.max_seq;
     const uint64_t td = al4k(T * sh.d_model * 2);
     if (opt.ckpt_on_host) {
-        ckpt_host = pinned_alloc(this, td * sh.n_layers);
+        ckpt_host = pinned_alloc(this, td * uint64_t(ckpt_slots(opt, sh)));
         if (!ckpt_host) MT_FAIL(MT_E_NOMEM, "cannot allocate the pinned checkpoint ring");
     }
     x0_pin = reinterpret_cast<uint16_t*>(pinned_alloc(this, td));
@@ -901,15 +910,30 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int B, int S, 
         }
     }
 
-    // Visits: forward 0..L-1, head, backward L-1..0.
-    const int nvis = 2 * L + 1;
-    int gnext = 0;
+    // The visit schedule: forward 0..L-1 (every k-th layer input checkpointed),
+    // the head, then per checkpoint block from the top: restore the block's
+    // first input, re-run the forward of its first k-1 layers to rebuild the
+    // other inputs, and run the block's backward from its last layer down.
+    // With k = 1 this is forward 0..L-1, head, backward L-1..0.
+    enum { V_FWD, V_HEAD, V_REFWD, V_BWD };
+    struct Visit {
+        int kind, unit, block, pos;  // block: backward block counter; pos: the layer's index in its block
+    };
+    const int K = opt.ckpt_on_host ? ckpt_k(opt, sh) : 1;
+    std::vector<Visit> sched;
+    for (int l = 0; l < L; ++l) sched.push_back({V_FWD, l, 0, 0});
+    sched.push_back({V_HEAD, lay.head(), 0, 0});
+    for (int j = (L + K - 1) / K - 1, bi = 0; j >= 0; --j, ++bi) {
+        const int b0 = j * K, e0 = std::min(b0 + K - 1, L - 1);
+        for (int i = b0; i < e0; ++i) sched.push_back({V_REFWD, i, bi, i - b0});
+        for (int l = e0; l >= b0; --l) sched.push_back({V_BWD, l, bi, l - b0});
+    }
+    int gnext = 0, nbwd = 0, restored = -1;
     const bool combined = opt.slot_mode == 1;
     double t_fwd = 0, t_head = 0;
     hipEvent_t ph_fwd_end = nullptr, ph_head_end = nullptr, ph_bwd_end = nullptr;
-    for (int v = 0; v < nvis; ++v) {
-        const int kind = v < L ? 0 : (v == L ? 1 : 2);  // 0 fwd, 1 head, 2 bwd
-        const int unit = kind == 0 ? v : (kind == 1 ? lay.head() : 2 * L - v);
+    for (const Visit& vs : sched) {
+        const int kind = vs.kind, unit = vs.unit;
         // Bind target: a streamed slot or the resident copy.
         int slot = 0;
         void* wbase;
@@ -927,18 +951,21 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int B, int S, 
             }
             wbase = arena + plan.wslot[slot];
         }
-        const int vb = v - L - 1;  // backward visit index
-        if (kind == 2 && opt.ckpt_on_host) {
-            if (vb == 0) HIPC(wait(st_w, fwd_ckpt_all));
-            HIPC(wait(st_w, xc_free[vb & 1]));
-            HIPC(h2d(ws.xc[vb & 1], ckpt_host + uint64_t(unit) * td_al, td, st_w));
+        const int bank = vs.block & 1;
+        uint16_t* const* xb = opt.ckpt_on_host ? ws.xc.data() + size_t(bank) * K : nullptr;
+        if ((kind == V_REFWD || kind == V_BWD) && opt.ckpt_on_host && vs.block != restored) {
+            // Restore the block's first input from the host ring.
+            restored = vs.block;
+            if (vs.block == 0) HIPC(wait(st_w, fwd_ckpt_all));
+            HIPC(wait(st_w, xc_free[bank]));
+            HIPC(h2d(xb[0], ckpt_host + uint64_t(unit / K) * td_al, td, st_w));
         }
         Ev& wr = wready[slot];
         HIPC(rec(wr, st_w));
         HIPC(wait(st_c, wr));
         hipEvent_t va = next_tev(), vz = next_tev();
         HIPC(hipEventRecord(va, st_c));
-        if (kind == 0) {
+        if (kind == V_FWD) {
             const uint16_t* x = opt.ckpt_on_host ? ws.x[unit & 1] : ws.ckpt_dev + uint64_t(unit) * ws.maxT * d;
             uint16_t* y = opt.ckpt_on_host ? ws.x[(unit + 1) & 1] : ws.ckpt_dev + uint64_t(unit + 1) * ws.maxT * d;
             if (opt.ckpt_on_host) HIPC(wait(st_c, ckpt_done[(unit + 1) & 1]));
@@ -948,9 +975,11 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int B, int S, 
             HIPC(rec(slot_free[slot], st_c));
             if (opt.ckpt_on_host) {
                 // Checkpoint the layer input on the gradient stream (idle in forward).
-                HIPC(wait(st_g, unit == 0 ? emb_ready : xready));
-                HIPC(d2h(ckpt_host + uint64_t(unit) * td_al, x, td, st_g));
-                HIPC(rec(ckpt_done[unit & 1], st_g));
+                if (unit % K == 0) {
+                    HIPC(wait(st_g, unit == 0 ? emb_ready : xready));
+                    HIPC(d2h(ckpt_host + uint64_t(unit / K) * td_al, x, td, st_g));
+                    HIPC(rec(ckpt_done[unit & 1], st_g));
+                }
                 HIPC(rec(xready, st_c));
                 if (unit == L - 1) HIPC(rec(fwd_ckpt_all, st_g));
             }
@@ -961,21 +990,31 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int B, int S, 
             }
             continue;
         }
+        if (kind == V_REFWD) {
+            // Rebuild the next layer's input inside the block's bank.
+            HIPC(fwd_layer(bind_layer(lay, wbase), xb[vs.pos], xb[vs.pos + 1], B, S, true));
+            HIPC(hipEventRecord(vz, st_c));
+            intervals.push_back({va, vz, 0, 0});
+            HIPC(rec(slot_free[slot], st_c));
+            continue;
+        }
         // Head or backward: gradients go to a gradient area, then to a slab.
         const int ga = combined ? slot : gnext;
         if (!combined) gnext ^= 1;
         HIPC(wait(st_c, buf_free[ga]));
         void* gbase = arena + plan.garea[ga];
-        if (kind == 1) {
+        if (kind == V_HEAD) {
             const uint16_t* xL = opt.ckpt_on_host ? ws.x[L & 1] : ws.ckpt_dev + uint64_t(L) * ws.maxT * d;
             HIPC(head(bind_head(lay, wbase), bind_head(lay, gbase), xL, ws.dy[0], B, S));
             HIPC(hipMemcpyAsync(loss_pin, ws.loss, 4, hipMemcpyDeviceToHost, st_c));
             HIPC(rec(loss_done, st_c));
         } else {
-            const uint16_t* x = opt.ckpt_on_host ? ws.xc[vb & 1] : ws.ckpt_dev + uint64_t(unit) * ws.maxT * d;
-            HIPC(bwd_layer(bind_layer(lay, wbase), bind_layer(lay, gbase), x, ws.dy[vb & 1], ws.dy[(vb + 1) & 1], B,
-                           S));
-            if (opt.ckpt_on_host) HIPC(rec(xc_free[vb & 1], st_c));
+            const uint16_t* x = opt.ckpt_on_host ? xb[vs.pos] : ws.ckpt_dev + uint64_t(unit) * ws.maxT * d;
+            HIPC(bwd_layer(bind_layer(lay, wbase), bind_layer(lay, gbase), x, ws.dy[nbwd & 1], ws.dy[(nbwd + 1) & 1],
+                           B, S));
+            ++nbwd;
+            // The block's bank is free once its first layer's backward ran.
+            if (opt.ckpt_on_host && vs.pos == 0) HIPC(rec(xc_free[bank], st_c));
         }
         HIPC(hipEventRecord(vz, st_c));
         intervals.push_back({va, vz, 0, 0});
@@ -989,7 +1028,7 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int B, int S, 
         HIPC(rec(buf_free[ga], st_g));
         if (combined) HIPC(rec(slot_free[slot], st_g));
         enqueue_job(unit, k);
-        if (kind == 1) {
+        if (kind == V_HEAD) {
             ph_head_end = next_tev();
             HIPC(hipEventRecord(ph_head_end, st_c));
             t_head = ms_since(t_start);
@@ -1214,6 +1253,7 @@ int mt_default_options(mt_options* o) {
     o->profile_kernels = 0;
     o->pin_store = 0;
     o->cross_step = 0;
+    o->ckpt_interval = 1;
     o->pin_weights = 0;
     o->lr = 1e-4f;
     o->beta1 = 0.9f;

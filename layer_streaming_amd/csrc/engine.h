@@ -5,6 +5,7 @@
 
 #include <deque>
 #include <memory>
+#include <vector>
 
 #include "host.h"
 #include "kernels.h"
@@ -38,7 +39,10 @@ HeadView bind_head(const Layout& lay, void* base);
 // Device activations of one layer at the workspace's maximum token count.
 struct Workspace {
     int64_t maxT = 0;
-    uint16_t *x[2] = {}, *xc[2] = {}, *xL = nullptr;
+    uint16_t *x[2] = {}, *xL = nullptr;
+    // Backward inputs with checkpoints on the host: two banks of k buffers
+    // (k = checkpoint interval), bank b buffer i = input of a block's layer i.
+    std::vector<uint16_t*> xc;
     uint16_t* ckpt_dev = nullptr;  // [L+1][maxT x d] when checkpoints stay on the GPU
     uint16_t *n1, *qkv, *o, *n2, *gu, *m;
     float* h1;  // residual stream inside a layer, kept in fp32

@@ -195,6 +195,32 @@ def test_streamed_configurations_bit_identical(baseline_run, opts):
         assert np.array_equal(a1.view(np.uint8), a2.view(np.uint8)), (k1, w1)
 
 
+DEEP = dict(n_layers=5, d_model=256, n_heads=4, n_kv_heads=2, head_dim=64, ffn_dim=688, vocab=1024)
+
+
+@pytest.fixture(scope="module")
+def deep_baseline_run():
+    return _run_two_steps(DEEP, 2, 64)
+
+
+@pytest.mark.parametrize("opts", [dict(ckpt_interval=2), dict(ckpt_interval=3), dict(ckpt_interval=5),
+                                  dict(ckpt_interval=7), dict(ckpt_interval=2, n_weight_slots=1),
+                                  dict(ckpt_interval=3, cross_step=1)],
+                         ids=lambda o: ",".join(f"{k}={v}" for k, v in o.items()))
+def test_checkpoint_interval_bit_identical(deep_baseline_run, opts):
+    """Block-wise recomputation (every k-th layer input kept, the block's
+    other inputs rebuilt by re-running its forward) changes where the inputs
+    come from, not their values: 5 layers in blocks of 2, 3, 5 and 7 (capped
+    at the depth) give the per-layer-checkpoint results bit for bit."""
+    log(f"checkpoint interval vs every layer: {opts}")
+    base_losses, base_state = deep_baseline_run
+    losses, state = _run_two_steps(DEEP, 2, 64, **opts)
+    assert [np.float32(x).tobytes() for x in losses] == [np.float32(x).tobytes() for x in base_losses]
+    for (k1, w1, a1), (k2, w2, a2) in zip(base_state, state):
+        assert k1 == k2 and w1 == w2
+        assert np.array_equal(a1.view(np.uint8), a2.view(np.uint8)), (k1, w1)
+
+
 def test_loss_decreases_over_steps_on_fixed_batch():
     log("loss decreases on a repeated batch")
     kw = CFG1

@@ -114,12 +114,34 @@ def test_bad_shapes_rejected(field, value):
 
 
 @pytest.mark.parametrize("field,value", [("n_weight_slots", 0), ("n_weight_slots", 5), ("n_grad_slabs", 0),
-                                         ("slot_mode", 2), ("max_batch", 0), ("beta1", 1.0)])
+                                         ("slot_mode", 2), ("max_batch", 0), ("beta1", 1.0), ("ckpt_interval", 0),
+                                         ("cross_step", 2), ("pin_weights", 2)])
 def test_bad_options_rejected(field, value):
     o = mt.default_options()
     setattr(o, field, value)
     a, p, h = C.c_uint64(), C.c_uint64(), C.c_uint64()
     assert mt.lib.mt_workspace_bytes(C.byref(CFG1), C.byref(o), C.byref(a), C.byref(p), C.byref(h)) == mt.MT_E_INVAL
+
+
+def test_option_conflicts_rejected():
+    for kw in (dict(ckpt_interval=2, ckpt_on_host=0), dict(pin_weights=1, pin_store=1)):
+        o = mt.default_options(**kw)
+        a, p, h = C.c_uint64(), C.c_uint64(), C.c_uint64()
+        assert mt.lib.mt_workspace_bytes(C.byref(CFG1), C.byref(o), C.byref(a), C.byref(p), C.byref(h)) == mt.MT_E_INVAL
+
+
+def test_checkpoint_interval_trades_pinned_ring_for_arena_banks():
+    """Interval k keeps ceil(L/k) layer inputs in the pinned ring and 2k input
+    buffers in the GPU arena (two banks of a block's inputs)."""
+    sh = mt.make_shape(6, 256, 4, 4, 64, 688, 1024)
+    td = 2 * 64 * 256 * 2  # max_batch 2 x max_seq 64 tokens x d 256, bf16 (a 4 KiB multiple)
+    sizes = {}
+    for k in (1, 2, 3, 6, 9):
+        sizes[k] = mt.workspace_bytes(sh, mt.default_options(max_batch=2, max_seq=64, ckpt_interval=k))
+    for k, kk in ((2, 2), (3, 3), (6, 6), (9, 6)):
+        a, p, _ = sizes[k]
+        assert sizes[1][1] - p == (6 - (6 + kk - 1) // kk) * td  # fewer ring entries
+        assert a - sizes[1][0] >= 2 * (kk - 1) * td and a - sizes[1][0] < 2 * (kk - 1) * td + 4 * 4096
 
 
 def test_init_rejects_null_arena_before_device_work():
