@@ -281,10 +281,12 @@ struct Ctx {
         int unit, slab;
         int64_t elems;
         AdamStep a;
+        int64_t step_id;  // the step (1-based) whose gradient this is
     };
     std::deque<Job> jobs;
     std::vector<int64_t> adam_gen;  // updates applied per unit
     double adam_wait_ms = 0.0;
+    int64_t bwd_complete = 0;  // last step whose backward has handed over every gradient
     std::vector<int> free_slabs;
     bool stop = false;
     int jobs_pending = 0;
@@ -559,15 +561,18 @@ void Ctx::slab_worker() {
             std::unique_lock<std::mutex> lk(q_mu);
             q_cv.wait(lk, [&] { return stop || !jobs.empty(); });
             if (jobs.empty()) return;
-            // Synchronous steps: arrival order, which frees the slabs in the
-            // order the backward needs them.  cross_step: the next forward
-            // needs the input embedding first, then the layers in order,
-            // then the head, so the lowest rank goes first.
+            // While the backward runs: arrival order, which frees the slabs
+            // in the order the backward needs them.  With cross_step, once a
+            // step's backward is over its remaining updates go lowest rank
+            // first: the next forward needs the input embedding, then the
+            // layers in order, then the head.
             auto rank = [&](const Job& x) { return x.unit == lay.embed() ? -1 : x.unit; };
-            auto it = !opt.cross_step ? jobs.begin()
-                                      : std::min_element(jobs.begin(), jobs.end(), [&](const Job& x, const Job& y) {
-                                            return rank(x) < rank(y);
-                                        });
+            auto it = jobs.begin();
+            if (opt.cross_step && jobs.front().step_id <= bwd_complete)
+                it = std::min_element(jobs.begin(), jobs.end(), [&](const Job& x, const Job& y) {
+                    return (x.step_id <= bwd_complete ? rank(x) : INT32_MAX) <
+                           (y.step_id <= bwd_complete ? rank(y) : INT32_MAX);
+                });
             j = *it;
             jobs.erase(it);
         }
@@ -616,7 +621,7 @@ int Ctx::acquire_slab() {
 void Ctx::enqueue_job(int unit, int slab) {
     {
         std::lock_guard<std::mutex> lk(q_mu);
-        jobs.push_back({unit, slab, lay.units[unit].elems, cur_adam});
+        jobs.push_back({unit, slab, lay.units[unit].elems, cur_adam, step + 1});
         ++jobs_pending;
     }
     q_cv.notify_one();
@@ -1033,6 +1038,10 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int B, int S, 
             HIPC(hipEventRecord(ph_head_end, st_c));
             t_head = ms_since(t_start);
         }
+    }
+    {
+        std::lock_guard<std::mutex> lk(q_mu);
+        bwd_complete = step + 1;
     }
     ph_bwd_end = next_tev();
     HIPC(hipEventRecord(ph_bwd_end, st_c));
