@@ -116,3 +116,89 @@ def test_attention_long_context_sampled():
     assert_close(g_g[rows_q, :Hq], np.concatenate(dq_ref, axis=1), "dq (sampled rows, all heads)")
     assert_close(g_g[rows_k, Hq], dk_ref, "dk (sampled keys, KV head 0)")
     assert_close(g_g[rows_k, Hq + Hkv], dv_ref, "dv (sampled keys, KV head 0)")
+
+
+# ------------------------------------------------- full steps at full size --
+# Whole training steps at the long-context shape (8 layers of the 7B layer,
+# B1 x S131072) and the 70B-layer shape (4 layers of d 8192, 64q/8kv, ffn
+# 28672, vocab 128256, B4 x S2048).  The oracle cannot run these steps, so
+# they are checked through properties that hold at any size:
+#  * the loss at initialisation: with gains 1 the final norm's rows have unit
+#    mean square, so each logit is a sum over d of N(0, 0.02^2) weights times
+#    unit-RMS activations, and over V >> 1 vocabulary rows the log-sum-exp
+#    concentrates at ln V + s^2/2 with s^2 = d * 0.02^2, while the label's
+#    logit averages 0 over the batch;
+#  * every gradient and updated state finite, and the gradients not all zero;
+#  * the host Adam the step ran equals the oracle's Adam applied to the very
+#    gradients the store holds, on sampled elements of the first layer and
+#    the head (within 2 ulp of fp32, or 1e-10 near zero);
+#  * a second run with other streaming options (checkpoint interval, slots)
+#    gives the same loss and the same gradients and weights, bit for bit.
+def _digest(a):
+    import hashlib
+    return hashlib.blake2b(np.ascontiguousarray(a).view(np.uint8), digest_size=16).hexdigest()
+
+
+def _full_step(kw, B, S, opts, check_adam):
+    sh = mt.make_shape(**kw)
+    o = mt.default_options(max_batch=B, max_seq=S, host_threads=16, **opts)
+    arena_bytes, _, _ = mt.workspace_bytes(sh, o)
+    arena = torch.empty(arena_bytes, dtype=torch.uint8, device="cuda")
+    ctx = mt.Context(sh, o, arena.data_ptr(), arena_bytes)
+    L = kw["n_layers"]
+    rng = np.random.default_rng(31)
+    samples = {}
+    if check_adam:
+        for unit, j in ((0, 1), (L, 1)):  # Wq of layer 0, E_out of the head
+            ms = ctx.get_tensor(unit, j, mt.MT_MASTER).reshape(-1)
+            idx = rng.choice(ms.size, size=20000, replace=False)
+            samples[(unit, j)] = (idx, ms[idx].copy())
+            del ms
+    tokens, labels = synth.tokens_labels(synth.SEED_TOKENS, B, S, kw["vocab"])
+    log(f"  step ({opts}) ...")
+    loss, st = ctx.train_step(tokens, labels)
+    log(f"  loss {loss:.5f}, step {st.step_ms:.0f} ms")
+    digests = {}
+    nonzero = 0
+    for unit in range(L + 2):
+        for j in range(mt.unit_tensors(sh, unit)):
+            g = widen(ctx.get_tensor(unit, j, mt.MT_G))
+            assert np.all(np.isfinite(g)), (unit, j)
+            nonzero += int(np.count_nonzero(g))
+            digests[(unit, j, "G")] = _digest(g)
+            w = ctx.get_tensor(unit, j, mt.MT_W)
+            digests[(unit, j, "W")] = _digest(w)
+            del g, w
+    assert nonzero > 0
+    for (unit, j), (idx, m0) in samples.items():
+        g = widen(ctx.get_tensor(unit, j, mt.MT_G)).reshape(-1)[idx]
+        got = ctx.get_tensor(unit, j, mt.MT_MASTER).reshape(-1)[idx]
+        ref, _, _, _ = ostep.adam_update(m0, np.zeros_like(m0), np.zeros_like(m0), g, 1, o.lr, o.beta1, o.beta2,
+                                         o.adam_eps)
+        # fp32 state: 2 ulp of the result, or the fp32 rounding of the update
+        # itself (|update| ~ lr) where the result is near zero
+        ulp = np.spacing(np.abs(ref)).astype(np.float64)
+        err = np.abs(got.astype(np.float64) - ref.astype(np.float64))
+        assert np.all(err <= np.maximum(2 * ulp, 1e-10)), (unit, j, float(err.max()))
+    ctx.close()
+    del arena
+    torch.cuda.empty_cache()
+    return loss, digests
+
+
+@pytest.mark.parametrize("name", ["long_context", "70b_layer_x4"])
+def test_full_size_step_properties(name):
+    if name == "long_context":
+        kw = dict(n_layers=8, d_model=3584, n_heads=28, n_kv_heads=4, head_dim=128, ffn_dim=18944, vocab=152064)
+        B, S, alt = 1, 131072, dict(ckpt_interval=4, n_weight_slots=3)
+    else:
+        kw = dict(n_layers=4, d_model=8192, n_heads=64, n_kv_heads=8, head_dim=128, ffn_dim=28672, vocab=128256)
+        B, S, alt = 4, 2048, dict(n_weight_slots=3, slot_mode=1)
+    log(f"full-size step {name}: {kw} B={B} S={S}")
+    loss, dig = _full_step(kw, B, S, {}, check_adam=True)
+    expect = np.log(kw["vocab"]) + kw["d_model"] * 0.02 ** 2 / 2
+    log(f"  loss {loss:.5f} vs ln V + d*0.02^2/2 = {expect:.5f}")
+    assert abs(loss - expect) < 0.05
+    loss2, dig2 = _full_step(kw, B, S, alt, check_adam=False)
+    assert np.float32(loss).tobytes() == np.float32(loss2).tobytes()
+    assert dig == dig2
