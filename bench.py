@@ -148,6 +148,34 @@ def traffic_probe(torch, mt, cfg):
     log("traffic probe done")
 
 
+def ablations(torch, mt, shape, cfg, args, tokens, labels, base_value):
+    """The cheap ablations: the same workload with one weight slot (no
+    prefetch), one gradient slab, and W and G sharing combined slots."""
+    from layer_streaming_amd import synth
+    B, S = cfg["batch"], cfg["seq"]
+    res = {}
+    for name, kw in (("one_weight_slot", dict(n_weight_slots=1)), ("one_grad_slab", dict(n_grad_slabs=1)),
+                     ("combined_slots", dict(slot_mode=1))):
+        opt = mt.default_options(max_batch=B, max_seq=S, host_threads=args.host_threads, seed=synth.SEED_WEIGHTS,
+                                 **kw)
+        arena_bytes, _, _ = mt.workspace_bytes(shape, opt)
+        arena = torch.empty(arena_bytes, dtype=torch.uint8, device="cuda")
+        ctx = mt.Context(shape, opt, arena.data_ptr(), arena_bytes)
+        ctx.train_step(tokens, labels)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(2):
+            ctx.train_step(tokens, labels)
+        torch.cuda.synchronize()
+        v = 2 * B * S / (time.perf_counter() - t0)
+        res[name] = {"value": round(v, 1), "vs_default": round(v / base_value, 3)}
+        log(f"ablation {name}: {v:.0f} tokens/s ({v / base_value:.3f} of the default)")
+        ctx.close()
+        del arena
+        torch.cuda.empty_cache()
+    return res
+
+
 def host_adam_probe(mt, n=256 << 20):
     """Host DRAM rate the library's Adam reaches on its own (all threads,
     30 B/param), the yardstick for the step's host traffic."""
@@ -225,6 +253,9 @@ def main():
     ap.add_argument("--resident", type=int, default=0)
     ap.add_argument("--pin-store", type=int, default=0)
     ap.add_argument("--pin-weights", type=int, default=0)
+    ap.add_argument("--ablations", action="store_true",
+                    help="after the timed run, time 2 steps each with one weight slot, one gradient slab and "
+                         "combined W/G slots (the pages' ablations), reported as tokens/s and ratio")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only launch the gate|up GEMM three times and a 1 GiB device copy three times (run "
                          "under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE to measure the GEMM's HBM traffic)")
@@ -310,7 +341,12 @@ def main():
                    "h2d_GB_per_step": round(h2d_b / 1e9, 3), "d2h_GB_per_step": round(d2h_b / 1e9, 3),
                    "peak_GBps": PCIE_GEN5_X16_GBS,
                    "h2d_busy_frac_of_step": round(float(np.mean([s["pcie_busy_frac"] for s in stats])), 3),
-                   "overlap_ratio": round(float(np.mean([s["overlap_ratio"] for s in stats])), 3)}
+                   "overlap_ratio": round(float(np.mean([s["overlap_ratio"] for s in stats])), 3),
+                   "overlap_by_phase": {ph: round(float(np.mean([s["overlap_phase"][i] for s in stats])), 3)
+                                        for i, ph in enumerate(("fwd", "head", "bwd"))},
+                   "exposed_transfer_ms_by_phase": {ph: round(float(np.mean([s["exposed_transfer_ms"][i]
+                                                                             for s in stats])), 1)
+                                                    for i, ph in enumerate(("fwd", "head", "bwd"))}}
     out["phases_ms"] = {k: round(float(np.mean([s[k] for s in stats])), 1)
                         for k in ("fwd_ms", "head_ms", "bwd_ms", "adam_tail_ms", "compute_busy_ms",
                                   "adam_ms", "adam_wait_ms", "pack_ms")}
@@ -350,6 +386,9 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(ctx, cfg, mt)
     ctx.close()
+    del arena
+    if args.ablations:
+        out["ablations"] = ablations(torch, mt, shape, cfg, args, tokens, labels, T / (ms_per_step / 1e3))
     print(json.dumps(out), flush=True)
 
 

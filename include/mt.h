@@ -126,6 +126,8 @@ typedef struct mt_stats {
                                           (cross_step) */
     double overlap_ratio;   /* |compute ∩ copies| / min(|compute|, |copies|) */
     double pcie_busy_frac;  /* |H2D| / step time */
+    double overlap_phase[3];        /* overlap_ratio within the forward, the head, the backward */
+    double exposed_transfer_ms[3];  /* |copies \ compute| per phase (device clock) */
     uint64_t h2d_bytes, d2h_bytes;
     uint64_t gpu_arena_bytes, pinned_bytes, host_store_bytes;
     int32_t n_sites;                       /* kernel sites timed (profile_kernels) */
@@ -215,6 +217,11 @@ int mt_set_tensor(mt_ctx* ctx, int32_t unit, int32_t idx, int32_t which, const v
 
 /* Adam step count already applied (0 after init). */
 int mt_step_count(mt_ctx* ctx, int64_t* out);
+
+/* sizeof the ABI structs as this library was built, for bindings to check
+ * their mirrors: which 0 mt_shape, 1 mt_options, 2 mt_stats,
+ * 3 mt_tensor_info; -1 for another value. */
+int64_t mt_abi_sizeof(int32_t which);
 
 /* Name of a kernel timing site of mt_stats (NULL if out of range). */
 const char* mt_site_name(int32_t site);

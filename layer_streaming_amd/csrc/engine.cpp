@@ -1155,17 +1155,41 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int B, int S, 
             return s;
         };
         auto Cm = merge(C), Xm = merge(X), Hm = merge(H);
-        double inter = 0;
-        size_t i = 0, j = 0;
-        while (i < Cm.size() && j < Xm.size()) {
-            const double lo = std::max(Cm[i].first, Xm[j].first), hi = std::min(Cm[i].second, Xm[j].second);
-            if (hi > lo) inter += hi - lo;
-            if (Cm[i].second < Xm[j].second) ++i;
-            else ++j;
-        }
+        auto intersect = [](const std::vector<std::pair<double, double>>& A,
+                            const std::vector<std::pair<double, double>>& Bv) {
+            double r = 0;
+            size_t i = 0, j = 0;
+            while (i < A.size() && j < Bv.size()) {
+                const double lo = std::max(A[i].first, Bv[j].first), hi = std::min(A[i].second, Bv[j].second);
+                if (hi > lo) r += hi - lo;
+                if (A[i].second < Bv[j].second) ++i;
+                else ++j;
+            }
+            return r;
+        };
+        auto clip = [](const std::vector<std::pair<double, double>>& v, double lo, double hi) {
+            std::vector<std::pair<double, double>> out;
+            for (auto& p : v) {
+                const double a = std::max(p.first, lo), b = std::min(p.second, hi);
+                if (b > a) out.push_back({a, b});
+            }
+            return out;
+        };
+        const double inter = intersect(Cm, Xm);
         const double lc = len(Cm), lx = len(Xm);
         stats->overlap_ratio = std::min(lc, lx) > 0 ? inter / std::min(lc, lx) : 0.0;
         stats->pcie_busy_frac = t_total > 0 ? len(Hm) / t_total : 0.0;
+        // The same per phase (forward, head, backward), and the transfer time
+        // no compute hides, |X \ C|.
+        if (ph_fwd_end && ph_head_end && ph_bwd_end) {
+            const double edges[4] = {0.0, el(t_base, ph_fwd_end), el(t_base, ph_head_end), el(t_base, ph_bwd_end)};
+            for (int p = 0; p < 3; ++p) {
+                const auto Cp = clip(Cm, edges[p], edges[p + 1]), Xp = clip(Xm, edges[p], edges[p + 1]);
+                const double ip = intersect(Cp, Xp), lcp = len(Cp), lxp = len(Xp);
+                stats->overlap_phase[p] = std::min(lcp, lxp) > 0 ? ip / std::min(lcp, lxp) : 0.0;
+                stats->exposed_transfer_ms[p] = lxp - ip;
+            }
+        }
         stats->pack_ms = pack_ms;
         {
             std::lock_guard<std::mutex> lk(q_mu);
@@ -1421,6 +1445,16 @@ int mt_sync(mt_ctx* c) {
         return MT_E_INVAL;
     }
     return c->impl.drain_jobs();
+}
+
+int64_t mt_abi_sizeof(int32_t which) {
+    switch (which) {
+        case 0: return int64_t(sizeof(mt_shape));
+        case 1: return int64_t(sizeof(mt_options));
+        case 2: return int64_t(sizeof(mt_stats));
+        case 3: return int64_t(sizeof(mt_tensor_info));
+        default: return -1;
+    }
 }
 
 int mt_step_count(mt_ctx* c, int64_t* out) {

@@ -45,7 +45,8 @@ class mt_stats(C.Structure):
                 ("bwd_ms", C.c_double), ("adam_tail_ms", C.c_double), ("compute_busy_ms", C.c_double),
                 ("h2d_busy_ms", C.c_double), ("d2h_busy_ms", C.c_double), ("pack_ms", C.c_double),
                 ("adam_ms", C.c_double), ("adam_wait_ms", C.c_double), ("overlap_ratio", C.c_double),
-                ("pcie_busy_frac", C.c_double),
+                ("pcie_busy_frac", C.c_double), ("overlap_phase", C.c_double * 3),
+                ("exposed_transfer_ms", C.c_double * 3),
                 ("h2d_bytes", C.c_uint64), ("d2h_bytes", C.c_uint64), ("gpu_arena_bytes", C.c_uint64),
                 ("pinned_bytes", C.c_uint64), ("host_store_bytes", C.c_uint64), ("n_sites", C.c_int32),
                 ("site_ms", C.c_double * MT_MAX_SITES), ("site_launches", C.c_uint64 * MT_MAX_SITES)]
@@ -74,6 +75,7 @@ _SIGS = {
     "mt_set_tensor": (C.c_int, [_P, C.c_int32, C.c_int32, C.c_int32, _P, C.c_uint64]),
     "mt_step_count": (C.c_int, [_P, C.POINTER(C.c_int64)]),
     "mt_sync": (C.c_int, [_P]),
+    "mt_abi_sizeof": (C.c_int64, [C.c_int32]),
     "mt_site_name": (C.c_char_p, [C.c_int32]),
     "mt_destroy": (None, [_P]),
     "mt_strerror": (C.c_char_p, [C.c_int]),
@@ -242,7 +244,10 @@ class Context:
 
 def stats_dict(st):
     names = site_names()
-    d = {k: getattr(st, k) for k, _ in mt_stats._fields_ if k not in ("site_ms", "site_launches")}
+    d = {k: getattr(st, k) for k, _ in mt_stats._fields_
+         if k not in ("site_ms", "site_launches", "overlap_phase", "exposed_transfer_ms")}
+    d["overlap_phase"] = list(st.overlap_phase)
+    d["exposed_transfer_ms"] = list(st.exposed_transfer_ms)
     d["sites"] = {names[i]: {"ms": st.site_ms[i], "launches": st.site_launches[i]}
                   for i in range(min(st.n_sites, len(names)))}
     return d

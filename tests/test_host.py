@@ -36,6 +36,12 @@ def test_library_exports_every_declared_symbol():
     assert names == set(mt.EXPORTED), names ^ set(mt.EXPORTED)
 
 
+def test_python_mirrors_match_the_abi_structs():
+    for which, cls in enumerate((mt.mt_shape, mt.mt_options, mt.mt_stats, mt.mt_tensor_info)):
+        assert mt.lib.mt_abi_sizeof(which) == C.sizeof(cls), cls.__name__
+    assert mt.lib.mt_abi_sizeof(7) == -1
+
+
 def test_strerror_and_status_codes():
     for s in (mt.MT_OK, mt.MT_E_INVAL, mt.MT_E_NOMEM, mt.MT_E_HIP, mt.MT_E_STATE, mt.MT_E_INTERNAL):
         assert mt.lib.mt_strerror(s)
