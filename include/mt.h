@@ -53,6 +53,7 @@ extern "C" {
 #define MT_E_HIP (-3)      /* a HIP runtime call failed                     */
 #define MT_E_STATE (-4)    /* the context failed earlier                    */
 #define MT_E_INTERNAL (-5) /* a host worker failed                          */
+#define MT_E_IO (-6)       /* a checkpoint file could not be written or read */
 
 /* Which copy of a tensor mt_get_tensor / mt_set_tensor address. */
 #define MT_W 0      /* BF16 weight (uint16 bit patterns)            */
@@ -217,6 +218,23 @@ int mt_set_tensor(mt_ctx* ctx, int32_t unit, int32_t idx, int32_t which, const v
 
 /* Adam step count already applied (0 after init). */
 int mt_step_count(mt_ctx* ctx, int64_t* out);
+
+/* Checkpoint shards ([Hotdry] checkpoint sharding and restore): write every
+ * unit's whole tile (W, G, master, m, v) and the step count to one file per
+ * unit, dir/unit_NNNNN.mtt, after waiting for queued host updates.  The
+ * directory is created if missing; files are written under a temporary name
+ * and renamed.  Errors: MT_E_INVAL, MT_E_IO, MT_E_STATE. */
+int mt_checkpoint_save(mt_ctx* ctx, const char* dir);
+
+/* Restore a context of the same shape from mt_checkpoint_save's files: every
+ * header is checked (format, unit, shape, size, one step count for all) before
+ * anything is read, then the tiles are loaded now (lazy = 0) or each when the
+ * step first needs it (lazy = 1: the embedding before the gather, a layer or
+ * the head before it is streamed, any unit before mt_get/set_tensor).  The
+ * step count continues from the saved one.  A checksum mismatch found while
+ * loading fails the context (MT_E_IO, then MT_E_STATE).  Errors: MT_E_INVAL
+ * (NULL, other shape), MT_E_IO. */
+int mt_checkpoint_restore(mt_ctx* ctx, const char* dir, int32_t lazy);
 
 /* sizeof the ABI structs as this library was built, for bindings to check
  * their mirrors: which 0 mt_shape, 1 mt_options, 2 mt_stats,

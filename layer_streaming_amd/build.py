@@ -19,7 +19,7 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 
 HIP_SOURCES = ["gemm.hip", "gemm_nt.hip", "attention.hip", "elementwise.hip"]
-CXX_SOURCES = ["host.cpp", "engine.cpp", "abi.cpp"]
+CXX_SOURCES = ["host.cpp", "shard.cpp", "engine.cpp", "abi.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
 HIP_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -17,6 +17,7 @@ const char* mt_strerror(int s) {
         case MT_E_HIP: return "HIP runtime error";
         case MT_E_STATE: return "context failed earlier";
         case MT_E_INTERNAL: return "host worker failure";
+        case MT_E_IO: return "checkpoint file I/O error";
         default: return "unknown status";
     }
 }

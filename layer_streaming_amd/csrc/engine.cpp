@@ -261,6 +261,8 @@ struct Ctx {
     std::vector<uint8_t*> pinned_blocks;
     std::vector<float> ein_acc;        // fp32 scatter accumulator [V x d]
     std::vector<int32_t> ein_touched;  // rows with a non-zero gradient last step
+    bool ein_clear_all = false;        // after a restore: the whole E_in gradient is stale
+    std::vector<std::string> lazy_dir; // per unit: checkpoint directory still to load from (lazy restore)
     // streams and events
     hipStream_t st_c = nullptr, st_w = nullptr, st_g = nullptr;
     bool own[3] = {false, false, false};
@@ -377,6 +379,9 @@ struct Ctx {
     void enqueue_job(int unit, int slab);
     int drain_jobs();
     int wait_adam(int unit);
+    int ensure_loaded(int unit);
+    int checkpoint_save(const std::string& dir);
+    int checkpoint_restore(const std::string& dir, bool lazy);
     int hip_fail(hipError_t e, const char* what) {
         failed = true;
         set_error(strfmt("HIP error '%s' in %s", hipGetErrorString(e), what));
@@ -658,6 +663,67 @@ int Ctx::drain_jobs() {
     return MT_OK;
 }
 
+// ------------------------------------------------- checkpoint shards ----
+// Load a unit whose shard a lazy restore left pending.
+int Ctx::ensure_loaded(int unit) {
+    if (lazy_dir.empty() || lazy_dir[unit].empty()) return MT_OK;
+    const std::string dir = lazy_dir[unit];
+    lazy_dir[unit].clear();
+    const int r = load_shard(*pack_pool, dir, tile_ptrs(store, lay, unit, wblock), lay, unit);
+    if (r != MT_OK) failed = true;
+    return r;
+}
+
+int Ctx::checkpoint_save(const std::string& dir) {
+    if (failed) MT_FAIL(MT_E_STATE, "context failed earlier");
+    const int ds = drain_jobs();
+    if (ds != MT_OK) return ds;
+    for (int u = 0; u < int(lay.units.size()); ++u) {
+        int r = ensure_loaded(u);
+        if (r == MT_OK) r = save_shard(*pack_pool, dir, tile_ptrs(store, lay, u, wblock), lay, u, step);
+        if (r != MT_OK) return r;
+    }
+    return MT_OK;
+}
+
+int Ctx::checkpoint_restore(const std::string& dir, bool lazy) {
+    if (failed) MT_FAIL(MT_E_STATE, "context failed earlier");
+    const int ds = drain_jobs();
+    if (ds != MT_OK) return ds;
+    // Every header first: nothing is overwritten unless all shards fit.
+    const int nu = int(lay.units.size());
+    int64_t s0 = -1;
+    for (int u = 0; u < nu; ++u) {
+        int64_t su = 0;
+        const int r = check_shard(dir, lay, u, &su);
+        if (r != MT_OK) return r;
+        if (u == 0) s0 = su;
+        else if (su != s0) MT_FAIL(MT_E_IO, "shards of %s come from different steps (%lld, %lld)", dir.c_str(),
+                                   (long long)s0, (long long)su);
+    }
+    lazy_dir.assign(size_t(nu), std::string());
+    for (int u = 0; u < nu; ++u) {
+        if (lazy) {
+            lazy_dir[u] = dir;
+            continue;
+        }
+        const int r = load_shard(*pack_pool, dir, tile_ptrs(store, lay, u, wblock), lay, u);
+        if (r != MT_OK) {
+            failed = true;
+            return r;
+        }
+    }
+    step = s0;
+    {
+        std::lock_guard<std::mutex> lk(q_mu);
+        adam_gen.assign(size_t(nu), s0);
+    }
+    slot_unit.assign(plan.n_slots, -1);
+    ein_touched.clear();
+    ein_clear_all = true;
+    return MT_OK;
+}
+
 // ------------------------------------------------------ layer template ----
 hipError_t Ctx::ensure_rope(int S) {
     if (S == cached_rope_S) return hipSuccess;
@@ -835,6 +901,8 @@ int Ctx::stream_unit(int unit, int slot) {
         failed = true;
         MT_FAIL(MT_E_INTERNAL, "injected pack fault at unit %d", unit);
     }
+    const int el = ensure_loaded(unit);
+    if (el != MT_OK) return el;
     const int wa = wait_adam(unit);
     if (wa != MT_OK) return wa;
     HIPC(wait(st_w, slot_free[slot]));
@@ -892,6 +960,8 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int B, int S, 
     memcpy(lab_pin, labels, size_t(T) * 4);
     HIPC(h2d(ws.labels, lab_pin, uint64_t(T) * 4, st_w));
     {
+        const int le = ensure_loaded(lay.embed());
+        if (le != MT_OK) return le;
         // The previous step's update of E_in (queued with cross_step) first.
         const int we = wait_adam(lay.embed());
         if (we != MT_OK) return we;
@@ -908,6 +978,8 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int B, int S, 
     if (opt.resident) {
         // The comparison run: every unit's weights copied up once, no streaming.
         for (int u = 0; u <= lay.head(); ++u) {
+            const int lu = ensure_loaded(u);
+            if (lu != MT_OK) return lu;
             const int wa = wait_adam(u);
             if (wa != MT_OK) return wa;
             const uint64_t bytes = uint64_t(lay.units[u].elems) * 2;
@@ -1055,6 +1127,8 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int B, int S, 
     {
         const TilePtrs e = tile_ptrs(store, lay, lay.embed(), wblock);
         // Clear last step's rows, then accumulate this step's in fp32.
+        if (ein_clear_all) memset(e.g, 0, size_t(V) * d * 2);
+        ein_clear_all = false;
         for (int32_t r : ein_touched) memset(e.g + int64_t(r) * d, 0, size_t(d) * 2);
         std::vector<char> seen(size_t(V), 0);
         ein_touched.clear();
@@ -1404,6 +1478,8 @@ int mt_get_tensor(mt_ctx* c, int32_t unit, int32_t idx, int32_t which, void* dst
     if (bytes != n * es) MT_FAIL(MT_E_INVAL, "bytes %llu != %llu", (unsigned long long)bytes, (unsigned long long)(n * es));
     const int ds = c->impl.drain_jobs();  // updates still queued by a cross-step train step
     if (ds != MT_OK) return ds;
+    const int ls = c->impl.ensure_loaded(unit);  // a shard still pending after a lazy restore
+    if (ls != MT_OK) return ls;
     const mt::TilePtrs p = mt::tile_ptrs(c->impl.store, lay, unit, c->impl.wblock);
     const void* src = which == MT_W ? static_cast<const void*>(p.w + t.off)
                     : which == MT_G ? static_cast<const void*>(p.g + t.off)
@@ -1429,6 +1505,8 @@ int mt_set_tensor(mt_ctx* c, int32_t unit, int32_t idx, int32_t which, const voi
     if (bytes != n * es) MT_FAIL(MT_E_INVAL, "bytes %llu != %llu", (unsigned long long)bytes, (unsigned long long)(n * es));
     const int ds = c->impl.drain_jobs();
     if (ds != MT_OK) return ds;
+    const int ls = c->impl.ensure_loaded(unit);
+    if (ls != MT_OK) return ls;
     const mt::TilePtrs p = mt::tile_ptrs(c->impl.store, lay, unit, c->impl.wblock);
     void* dst = which == MT_W ? static_cast<void*>(p.w + t.off)
               : which == MT_G ? static_cast<void*>(p.g + t.off)
@@ -1445,6 +1523,33 @@ int mt_sync(mt_ctx* c) {
         return MT_E_INVAL;
     }
     return c->impl.drain_jobs();
+}
+
+int mt_checkpoint_save(mt_ctx* c, const char* dir) {
+    if (!c || !dir || !*dir) {
+        mt::set_error("ctx and dir must not be NULL or empty");
+        return MT_E_INVAL;
+    }
+    try {
+        return c->impl.checkpoint_save(dir);
+    } catch (...) {
+        mt::set_error("unexpected exception in mt_checkpoint_save");
+        return MT_E_INTERNAL;
+    }
+}
+
+int mt_checkpoint_restore(mt_ctx* c, const char* dir, int32_t lazy) {
+    if (!c || !dir || !*dir) {
+        mt::set_error("ctx and dir must not be NULL or empty");
+        return MT_E_INVAL;
+    }
+    try {
+        return c->impl.checkpoint_restore(dir, lazy != 0);
+    } catch (...) {
+        c->impl.failed = true;
+        mt::set_error("unexpected exception in mt_checkpoint_restore");
+        return MT_E_INTERNAL;
+    }
 }
 
 int64_t mt_abi_sizeof(int32_t which) {

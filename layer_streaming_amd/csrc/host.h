@@ -151,4 +151,11 @@ void adam_range(const TilePtrs& p, const uint16_t* gsrc, int64_t b, int64_t e, c
 void adam_unit(ThreadPool& pool, const TilePtrs& p, const uint16_t* gsrc, int64_t n,
                const AdamStep& a);
 
+// ------------------------------------------------- checkpoint shards ----
+std::string shard_path(const std::string& dir, int unit);
+int save_shard(ThreadPool& pool, const std::string& dir, const TilePtrs& t, const Layout& lay, int unit,
+               int64_t step);
+int check_shard(const std::string& dir, const Layout& lay, int unit, int64_t* step);
+int load_shard(ThreadPool& pool, const std::string& dir, const TilePtrs& t, const Layout& lay, int unit);
+
 }  // namespace mt

@@ -17,7 +17,7 @@ if not os.path.exists(_LIB_PATH):
     raise ImportError(f"{_LIB_PATH} is not built; run `python -m layer_streaming_amd.build`")
 lib = C.CDLL(_LIB_PATH)
 
-MT_OK, MT_E_INVAL, MT_E_NOMEM, MT_E_HIP, MT_E_STATE, MT_E_INTERNAL = 0, -1, -2, -3, -4, -5
+MT_OK, MT_E_INVAL, MT_E_NOMEM, MT_E_HIP, MT_E_STATE, MT_E_INTERNAL, MT_E_IO = 0, -1, -2, -3, -4, -5, -6
 MT_W, MT_G, MT_MASTER, MT_M, MT_V = 0, 1, 2, 3, 4
 MT_MAX_SITES = 48
 
@@ -75,6 +75,8 @@ _SIGS = {
     "mt_set_tensor": (C.c_int, [_P, C.c_int32, C.c_int32, C.c_int32, _P, C.c_uint64]),
     "mt_step_count": (C.c_int, [_P, C.POINTER(C.c_int64)]),
     "mt_sync": (C.c_int, [_P]),
+    "mt_checkpoint_save": (C.c_int, [_P, C.c_char_p]),
+    "mt_checkpoint_restore": (C.c_int, [_P, C.c_char_p, C.c_int32]),
     "mt_abi_sizeof": (C.c_int64, [C.c_int32]),
     "mt_site_name": (C.c_char_p, [C.c_int32]),
     "mt_destroy": (None, [_P]),
@@ -235,6 +237,12 @@ class Context:
 
     def sync(self):
         check(lib.mt_sync(self._ptr), "mt_sync")
+
+    def checkpoint_save(self, path):
+        check(lib.mt_checkpoint_save(self._ptr, os.fsencode(path)), "mt_checkpoint_save")
+
+    def checkpoint_restore(self, path, lazy=False):
+        check(lib.mt_checkpoint_restore(self._ptr, os.fsencode(path), 1 if lazy else 0), "mt_checkpoint_restore")
 
     def step_count(self):
         v = C.c_int64()
