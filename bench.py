@@ -50,8 +50,8 @@ SHAPES = {
 # profiles/gemm_gateup_traffic_7b.md.  Valid only for the kernel source it was
 # taken on: reported as null once that file changes.
 TRAFFIC = {"source": "layer_streaming_amd/csrc/gemm_nt.hip",
-           "sha256": "0307c32f1be5fb112dfb08bbd0eb4987b477e0d4b5dff3a94637de1302881148",
-           "fetch_bytes": 3317992844, "write_bytes": 695424717}
+           "sha256": "6c6dbe1f3ef43c0fca55a7790898be3e9515cd7cd8e320b59e1a3e2ee89379b4",
+           "fetch_bytes": 3317989356, "write_bytes": 690056704}
 
 
 def traffic_bytes():
