@@ -47,20 +47,23 @@ SHAPES = {
 # HBM bytes per launch of the dominant kernel (the gate|up GEMM at the 7B
 # shape) from two rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE), each scaled
 # by the same counter's reading for a 1 GiB device copy; see
-# profiles/gemm_gateup_traffic_7b.md.  Valid only for the kernel source it was
-# taken on: reported as null once that file changes.
-TRAFFIC = {"source": "layer_streaming_amd/csrc/gemm_nt.hip",
-           "sha256": "6c6dbe1f3ef43c0fca55a7790898be3e9515cd7cd8e320b59e1a3e2ee89379b4",
-           "fetch_bytes": 3317989356, "write_bytes": 690056704}
+# profiles/gemm_gateup_traffic_7b.md.  Valid only for the kernel sources it was
+# taken on (sha256 over the files in order): reported as null once they change.
+TRAFFIC = {"sources": ["layer_streaming_amd/csrc/gemm_nt.hip", "layer_streaming_amd/csrc/kcommon.h"],
+           "sha256": "e25e77bfba310585be5eb6190e19d1949c491add75f4ef6171b641b1e0b75f33",
+           "fetch_bytes": 3317797202, "write_bytes": 638521504}
 
 
 def traffic_bytes():
     import hashlib
+    h = hashlib.sha256()
     try:
-        with open(os.path.join(ROOT, TRAFFIC["source"]), "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest() != TRAFFIC["sha256"]:
-                return None
+        for src in TRAFFIC["sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
     except OSError:
+        return None
+    if h.hexdigest() != TRAFFIC["sha256"]:
         return None
     return TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
 

@@ -19,15 +19,14 @@ __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(uint3
 __device__ __forceinline__ float bflo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bfhi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// float -> bf16, IEEE round to nearest, ties to even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint16_t f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return uint16_t((u >> 16) | 0x40u);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return uint16_t(u >> 16);
-}
+// float -> bf16, IEEE round to nearest, ties to even; NaN stays a NaN.  The
+// conversion is gfx950's v_cvt_pk_bf16_f32 (one instruction per two values).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, __bf16(f)); }
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    return uint32_t(f2bf(lo)) | (uint32_t(f2bf(hi)) << 16);
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Unpack 8 bf16 held in a uint4 into floats.

@@ -307,3 +307,32 @@ def test_cross_entropy(Tc, V):
     loss, dref = block.cross_entropy(logits.astype(np.float64), labels)
     assert abs(out.item() - loss) / abs(loss) < 1e-5
     assert_close(host_f32(dlog), dref, "dlogits")
+
+
+# ------------------------------------------------------ fp32 -> bf16 RNE --
+def test_f32_to_bf16_round_to_nearest_even():
+    """The device conversion used by every bf16 output against the IEEE
+    definition (oracle bf16_bits): values over the whole exponent range, all
+    rounding cases of the low half (below, at and above the tie, odd and even
+    kept bit), signed zeros and infinities bit for bit; NaN stays NaN."""
+    rng = np.random.default_rng(7)
+    hi = rng.integers(0, 1 << 16, size=1 << 16, dtype=np.uint32)
+    hi = hi[((hi >> 7) & 0xFF) != 0xFF]                          # finite high halves
+    lows = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF], np.uint32)
+    u = ((hi[:, None] << 16) | lows[None, :]).reshape(-1)
+    special = np.array([0x00000000, 0x80000000, 0x7F800000, 0xFF800000, 0x7F7FFFFF, 0x00000001, 0x007FFFFF,
+                        0x00800000, 0x7FC00000, 0x7F800001, 0xFFC12345], np.uint32)
+    u = np.concatenate([u, special, np.zeros((-(u.size + special.size)) % 4, np.uint32)])
+    x = u.view(np.float32)
+    dx = torch.from_numpy(x).cuda()
+    dy = torch.zeros(x.size, dtype=torch.int16, device="cuda")
+    mt.check(mt.lib.mt_k_f32_to_bf16(dx.data_ptr(), dy.data_ptr(), x.size, _stream()))
+    _sync()
+    got = dy.cpu().numpy().view(np.uint16)
+    ref = bf16_bits(x)
+    nan = np.isnan(x)
+    # below fp32's normal range the hardware may flush; everything else exact
+    sub = (np.abs(x) < np.float32(1.1754944e-38)) & (x != 0)
+    keep = ~nan & ~sub
+    assert np.array_equal(got[keep], ref[keep]), int(np.sum(got[keep] != ref[keep]))
+    assert np.all(np.isnan((got[nan].astype(np.uint32) << 16).view(np.float32)))
