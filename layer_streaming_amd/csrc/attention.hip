@@ -189,34 +189,48 @@ __global__ __launch_bounds__(256) void attn_fwd_k(AttnArgs a, int n_qt) {
                 for (int s = 0; s < NS; ++s)
                     st[t] = MFMA32H(as_f16x8(Ks[cur][RowTile<HD>::idx(32 * t + c, 2 * s + hh)]), qf[s], st[t]);
             }
+            // Raw scores; the scale goes into the exponent's FMA.  A tile
+            // every query of the wave sees whole (below the diagonal, inside
+            // the sequence) needs no mask.
+            const bool full = k0 + BKV - 1 <= qw && k0 + BKV <= S;
             float mx = -INFINITY;
+            if (full) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+                for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
-                    const float v = (key > q || key >= S) ? -INFINITY : st[t][r] * sc;
-                    st[t][r] = v;
-                    mx = fmaxf(mx, v);
-                }
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[t][r]);
+            } else {
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
+                        if (key > q || key >= S) st[t][r] = -INFINITY;
+                        mx = fmaxf(mx, st[t][r]);
+                    }
+            }
             mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float mn = fmaxf(m, mx);
+            const float mn = fmaxf(m, mx * sc);  // running max of the scaled scores (log2 units)
             const float alpha = (m == -INFINITY) ? 0.f : exp2f(m - mn);
             m = mn;
+            const float nb = (mn == -INFINITY) ? 0.f : -mn;  // masked scores give exp2(-inf) = 0
             float ps = 0.f;
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float p = (mn == -INFINITY) ? 0.f : exp2f(st[t][r] - mn);
+                    const float p = exp2f(fmaf(st[t][r], sc, nb));
                     st[t][r] = p;
                     ps += p;
                 }
             lsum = lsum * alpha + ps;
+            // Rescale the output only when some lane's maximum moved.
+            if (__ballot(alpha != 1.0f)) {
 #pragma unroll
-            for (int i = 0; i < ND; ++i)
+                for (int i = 0; i < ND; ++i)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+                    for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+            }
             bf16x8_t pb[2][2];
 #pragma unroll
             for (int t = 0; t < 2; ++t)
@@ -362,6 +376,8 @@ __global__ __launch_bounds__(256) void attn_dq_k(AttnBwdArgs a, int n_qt) {
                 }
             }
             bf16x8_t dsb[2][2];
+            // a tile every query of the wave sees whole needs no mask
+            const bool full = k0 + BKV - 1 <= qw && k0 + BKV <= S;
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -370,8 +386,11 @@ __global__ __launch_bounds__(256) void attn_dq_k(AttnBwdArgs a, int n_qt) {
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
                         const int r = 8 * s2 + j;
-                        const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
-                        const float p = (key > q || key >= S) ? 0.f : exp2f(st[t][r] * sc - lse2);
+                        float p = exp2f(fmaf(st[t][r], sc, -lse2));
+                        if (!full) {
+                            const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
+                            if (key > q || key >= S) p = 0.f;
+                        }
                         tmp[j] = p * (dp[t][r] - dq_d);
                     }
                     dsb[t][s2] = pack_b(tmp);
@@ -500,6 +519,9 @@ __global__ __launch_bounds__(256) void attn_dkdv_k(AttnBwdArgs a, int n_kt) {
                 }
             }
             bf16x8_t pb[2][2], dsb[2][2];
+            // every key of the wave before every query of the tile, all inside
+            // the sequence: no mask
+            const bool full = kw + 31 <= q0 && q0 + BKV <= S && kw + 32 <= S;
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -509,9 +531,11 @@ __global__ __launch_bounds__(256) void attn_dkdv_k(AttnBwdArgs a, int n_kt) {
                     for (int j = 0; j < 8; ++j) {
                         const int r = 8 * s2 + j;
                         const int ql = 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
-                        const int qq = q0 + ql;
-                        const float p = (key > qq || qq >= S || key >= S)
-                                            ? 0.f : exp2f(st[t][r] * sc - Ls[cur][ql]);
+                        float p = exp2f(fmaf(st[t][r], sc, -Ls[cur][ql]));
+                        if (!full) {
+                            const int qq = q0 + ql;
+                            if (key > qq || qq >= S || key >= S) p = 0.f;
+                        }
                         tp[j] = p;
                         td[j] = p * (dp[t][r] - Dd[cur][ql]);
                     }
