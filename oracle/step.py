@@ -283,3 +283,88 @@ def train_step(store, tokens, labels, sh, step, lr=1e-4, beta1=0.9,
             t["master"], t["m"], t["v"], t["w"] = adam_update(
                 t["master"], t["m"], t["v"], g, step, lr, beta1, beta2, eps)
     return loss, gstore
+
+
+# --------------------------------------------------------------------------
+# Gradient accumulation over micro-batches
+# --------------------------------------------------------------------------
+def accumulate_bf16(acc, g):
+    """acc + g for two arrays of BF16 values, rounded once to BF16 (RNE).
+
+    The host keeps the accumulated gradient in the BF16 G region of each
+    tile ([Review] 3-2 item 1: the host holds parameters, the accumulated
+    gradient and the optimizer state; [Hotdry] "三层 CUDA Stream 流水线与双缓冲调度":
+    the CPU thread unpacks each slab and accumulates it into the master
+    store).  The sum of two BF16 values is computed exactly in float64;
+    float32 then holds it exactly, or within far less than half a BF16 unit
+    of the larger operand, so a single BF16 rounding follows."""
+    s = acc.astype(np.float64) + g.astype(np.float64)
+    return round_bf16(s.astype(np.float32))
+
+
+def grads_accumulated(params, tokens, labels, sh, n_staging=2):
+    """float64 gradients of the mean cross-entropy over every token of the
+    micro-batches tokens[j] (shape [n, B, S]), without BF16 rounding: the
+    sum over j of each micro-batch's gradient times 1/n.  Returns
+    (loss, grads) like ``grads_streamed``."""
+    n = tokens.shape[0]
+    total, loss = None, 0.0
+    for j in range(n):
+        lj, gj = grads_streamed(params, tokens[j], labels[j], sh, n_staging)
+        loss += lj / n
+        gj = _scale_tree(gj, 1.0 / n)
+        total = gj if total is None else _add_tree(total, gj)
+    return loss, total
+
+
+def _scale_tree(tree, s):
+    return {"layers": [{k: v * s for k, v in u.items()} for u in tree["layers"]],
+            "head": {k: v * s for k, v in tree["head"].items()},
+            "e_in": tree["e_in"] * s}
+
+
+def _add_tree(a, b):
+    return {"layers": [{k: ua[k] + ub[k] for k in ua} for ua, ub in zip(a["layers"], b["layers"])],
+            "head": {k: a["head"][k] + b["head"][k] for k in a["head"]},
+            "e_in": a["e_in"] + b["e_in"]}
+
+
+def train_step_accum(store, tokens, labels, sh, step, lr=1e-4, beta1=0.9,
+                     beta2=0.999, eps=1e-8, n_staging=2):
+    """One optimizer step over n micro-batches (tokens, labels [n, B, S]).
+
+    Every micro-batch runs the whole streamed forward and backward with the
+    weights of the step's start; its gradient of the mean loss over all
+    n*B*S tokens (the micro-batch's own gradient times 1/n) is rounded to
+    BF16, the precision gradients stream out in, and summed into the BF16
+    accumulator in micro-batch order with one rounding per addition
+    (``accumulate_bf16``).  Adam then runs once on the accumulated gradient.
+    The loss is the mean over all tokens.  With n = 1 this is ``train_step``.
+    Returns (loss, accumulated BF16 gradients as float32 in store layout)."""
+    n = tokens.shape[0]
+    params = params_from_store(store)
+    units = [("layers", i) for i in range(sh.n_layers)] + [("head", None), ("e_in", None)]
+
+    def unit_of(tree, kind, i):
+        return tree[kind][i] if kind == "layers" else tree[kind]
+
+    gstore = None
+    loss = 0.0
+    for j in range(n):
+        lj, gr = grads_streamed(params, tokens[j], labels[j], sh, n_staging)
+        loss += lj / n
+        gj = {"layers": [dict() for _ in range(sh.n_layers)], "head": {}, "e_in": {}}
+        for kind, i in units:
+            g_unit = unit_of(gr, kind, i) if kind != "e_in" else {"e_in": gr["e_in"]}
+            for name, g in g_unit.items():
+                gb = round_bf16((g / n).astype(np.float32))
+                if gstore is not None:
+                    gb = accumulate_bf16(unit_of(gstore, kind, i)[name], gb)
+                unit_of(gj, kind, i)[name] = gb
+        gstore = gj
+    for kind, i in units:
+        for name, t in unit_of(store, kind, i).items():
+            g = unit_of(gstore, kind, i)[name]
+            t["master"], t["m"], t["v"], t["w"] = adam_update(
+                t["master"], t["m"], t["v"], g, step, lr, beta1, beta2, eps)
+    return loss, gstore

@@ -328,3 +328,110 @@ def test_parameter_counts_and_host_store_bytes():
     assert abs(qwen7.n_params() * 16 / 1e9 - 122) < 0.5
     assert abs(qwen14.n_params() * 16 / 1e9 - 235) < 1.5
     assert CFG1.n_params() == 2 * 791_040 + 256 + 2 * 1024 * 256
+
+
+# ------------------------------------------- gradient accumulation (P10) --
+def _bf16_grid_neighbours(x):
+    """The two bf16 values around a float64 x (exact, via float32 bits)."""
+    f = np.float32(x)
+    bits = int(np.array(f).view(np.uint32))
+    lo_bits = bits & 0xFFFF0000
+    lo = float(np.array(lo_bits, dtype=np.uint32).view(np.float32))
+    hi = float(np.array((lo_bits + 0x10000) & 0xFFFFFFFF, dtype=np.uint32).view(np.float32))
+    return lo, hi
+
+
+def test_accumulate_bf16_is_one_rounding_of_the_exact_sum():
+    """Brute force against the definition: the exact sum (Fractions) rounded
+    to the nearer bf16 neighbour, ties to the even one."""
+    from fractions import Fraction
+    rng = np.random.default_rng(4)
+    a = round_bf16(rng.standard_normal(4000).astype(np.float32))
+    b = round_bf16((rng.standard_normal(4000) * np.exp2(rng.integers(-30, 30, 4000))).astype(np.float32))
+    # ties: b equal to half a bf16 unit of a, with a's last bit odd and even
+    ta = round_bf16(np.float32(1.0) + np.arange(1, 33, dtype=np.float32) * np.float32(2.0 ** -7))
+    tb = np.full(32, 2.0 ** -8, dtype=np.float32)
+    a, b = np.concatenate([a, ta]), np.concatenate([b, tb])
+    got = step.accumulate_bf16(a, b)
+    for x, y, g in zip(a, b, got):
+        s = Fraction(float(x)) + Fraction(float(y))
+        lo, hi = _bf16_grid_neighbours(float(s))
+        if s < 0:
+            lo, hi = sorted(_bf16_grid_neighbours(float(s)))
+        lo, hi = min(lo, hi), max(lo, hi)
+        if Fraction(lo) == s:
+            want = lo
+        elif Fraction(hi) == s:
+            want = hi
+        else:
+            dlo, dhi = s - Fraction(lo), Fraction(hi) - s
+            if dlo != dhi:
+                want = lo if dlo < dhi else hi
+            else:
+                lob = int(np.array(np.float32(lo)).view(np.uint32)) >> 16
+                want = lo if lob % 2 == 0 else hi
+        assert float(g) == want, (x, y, g, want)
+
+
+def test_accumulated_gradient_equals_the_full_batch_gradient():
+    """Two micro-batches of B sequences give the gradient of one batch of 2B
+    sequences (the mean over every token), before any rounding."""
+    sh = TINY
+    params = random_params(sh, seed=31)
+    ta, la = synth.tokens_labels(41, 2, 5, sh.vocab)
+    tb, lb = synth.tokens_labels(42, 2, 5, sh.vocab)
+    loss_acc, g_acc = step.grads_accumulated(params, np.stack([ta, tb]), np.stack([la, lb]), sh)
+    loss_full, g_full = step.grads_monolithic(params, np.concatenate([ta, tb]), np.concatenate([la, lb]), sh)
+    assert abs(loss_acc - loss_full) <= 1e-13 * abs(loss_full)
+    for key, _ in _all_tensors(params):
+        ga, gf = _get(g_acc, key), _get(g_full, key)
+        assert np.max(np.abs(ga - gf)) <= 1e-12 * max(np.max(np.abs(gf)), 1e-300), key
+
+
+def test_one_micro_batch_is_the_plain_step():
+    sh = TINY
+    params = random_params(sh, seed=12)
+    tokens, labels = synth.tokens_labels(8, 2, 5, sh.vocab)
+    s1, s2 = _store_from(params, sh), _store_from(params, sh)
+    l1, g1 = step.train_step(s1, tokens, labels, sh, step=1)
+    l2, g2 = step.train_step_accum(s2, tokens[None], labels[None], sh, step=1)
+    assert l1 == l2
+    for a, b in zip(_leaves(s1), _leaves(s2)):
+        assert np.array_equal(a, b)
+
+
+def test_identical_micro_batches_equal_one_step_bit_for_bit():
+    """n copies of one micro-batch: each gradient is the plain one times 1/n
+    (a power of two here, exact), the BF16 sums are exact, so the update is
+    the plain step's bit for bit."""
+    sh = TINY
+    params = random_params(sh, seed=13)
+    tokens, labels = synth.tokens_labels(9, 2, 5, sh.vocab)
+    for n in (2, 4):
+        s1, s2 = _store_from(params, sh), _store_from(params, sh)
+        l1, g1 = step.train_step(s1, tokens, labels, sh, step=1)
+        l2, g2 = step.train_step_accum(s2, np.stack([tokens] * n), np.stack([labels] * n), sh, step=1)
+        assert l1 == l2
+        for a, b in zip(_leaves(s1), _leaves(s2)):
+            assert np.array_equal(a, b)
+
+
+def test_accumulation_adds_in_micro_batch_order_with_one_rounding_each():
+    """Planted values: the accumulated G of three micro-batches is
+    bf16(bf16(g0 + g1) + g2) of the per-micro-batch BF16 gradients."""
+    sh = TINY
+    params = random_params(sh, seed=14)
+    toks = [synth.tokens_labels(50 + j, 1, 6, sh.vocab) for j in range(3)]
+    tokens = np.stack([t for t, _ in toks])
+    labels = np.stack([l for _, l in toks])
+    store = _store_from(params, sh)
+    _, gacc = step.train_step_accum(store, tokens, labels, sh, step=1)
+    p = step.params_from_store(_store_from(params, sh))
+    per = [step.grads_streamed(p, tokens[j], labels[j], sh)[1] for j in range(3)]
+    for key, _ in _all_tensors(params):
+        gb = [round_bf16((_get(g, key) / 3).astype(np.float32)) for g in per]
+        want = round_bf16((round_bf16((gb[0].astype(np.float64) + gb[1]).astype(np.float32))
+                           .astype(np.float64) + gb[2]).astype(np.float32))
+        kind, i, k = key
+        got = gacc["layers"][i][k] if kind == "layers" else gacc[kind][k]
+        assert np.array_equal(got, want), key
