@@ -175,6 +175,26 @@ int mt_init(const mt_shape* shape, const mt_options* opt, void* gpu_arena, uint6
 int mt_train_step(mt_ctx* ctx, const int32_t* tokens, const int32_t* labels, int32_t batch,
                   int32_t seq, float* loss_out, mt_stats* stats_out);
 
+#define MT_MAX_MICRO 4096
+
+/* One optimizer step over n_micro micro-batches: tokens and labels are
+ * [n_micro x batch x seq] int32 (micro-batch j at offset j*batch*seq).
+ * The host keeps the accumulated gradient in each tile's BF16 G region
+ * ([Review] 3-2 item 1: parameters, the accumulated gradient and the
+ * optimizer state live on the host; [Hotdry] "三层 CUDA Stream 流水线与双缓冲调度":
+ * the CPU thread unpacks each slab and accumulates it into the master store).
+ * Every micro-batch runs the whole streamed forward, head and recomputing
+ * backward with the step's weights; its gradient is that of the mean loss
+ * over all n_micro*batch*seq tokens, streamed out in BF16; the host stores
+ * the first micro-batch's gradient into G and adds each later one into G
+ * (fp32 add, one BF16 rounding, in micro-batch order); after the last one,
+ * each unit's Adam runs once on G.  *loss_out is the mean cross-entropy over
+ * all tokens.  n_micro = 1 is mt_train_step.  Synchronicity, stats and
+ * errors as mt_train_step, plus MT_E_INVAL for n_micro outside
+ * [1, MT_MAX_MICRO]; stats phase times are summed over the micro-batches. */
+int mt_train_step_accum(mt_ctx* ctx, const int32_t* tokens, const int32_t* labels, int32_t n_micro,
+                        int32_t batch, int32_t seq, float* loss_out, mt_stats* stats_out);
+
 /* Wait until every queued host Adam update has been applied to the store
  * (a no-op for synchronous steps).  Returns the first error a host worker
  * met since the last call (MT_E_HIP, MT_E_INTERNAL), else MT_OK. */

@@ -94,6 +94,9 @@ int mt_k_f32_to_bf16(const void* x, void* y, int64_t n, void* stream);
  * bf16(master). */
 int mt_host_adam(uint16_t* w, uint16_t* g, float* master, float* m, float* v, const uint16_t* gsrc, int64_t n,
                  int64_t step, float lr, float beta1, float beta2, float eps, int32_t threads);
+/* The production gradient accumulation of micro-batch steps over n elements:
+ * g[i] <- bf16_RNE(f32(g[i]) + f32(src[i])). */
+int mt_host_accum(uint16_t* g, const uint16_t* src, int64_t n, int32_t threads);
 /* Initialise one unit tile (16 * mt_unit_elems bytes) as mt_init would. */
 int mt_host_init_unit(const mt_shape* shape, int32_t unit, uint64_t seed, float init_std, int32_t threads,
                       void* tile, uint64_t tile_bytes);

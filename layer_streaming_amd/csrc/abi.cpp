@@ -166,6 +166,14 @@ int mt_host_adam(uint16_t* w, uint16_t* g, float* master, float* m, float* v, co
     return MT_OK;
 }
 
+// Host gradient accumulation on caller arrays (no GPU).
+int mt_host_accum(uint16_t* g, const uint16_t* src, int64_t n, int32_t threads) {
+    if (!g || !src || n < 0) MT_FAIL(MT_E_INVAL, "bad host accumulation arguments");
+    mt::ThreadPool pool(threads > 0 ? threads : 1);
+    mt::accum_unit(pool, g, src, n);
+    return MT_OK;
+}
+
 // Host init of one synthetic tensor stream, for tests of determinism.
 int mt_host_init_unit(const mt_shape* sh, int32_t unit, uint64_t seed, float std_, int32_t threads, void* tile,
                       uint64_t tile_bytes) {

@@ -261,6 +261,7 @@ struct Ctx {
     std::vector<uint8_t*> pinned_blocks;
     std::vector<float> ein_acc;        // fp32 scatter accumulator [V x d]
     std::vector<int32_t> ein_touched;  // rows with a non-zero gradient last step
+    std::vector<char> ein_seen;        // rows touched so far in this step
     bool ein_clear_all = false;        // after a restore: the whole E_in gradient is stale
     std::vector<std::string> lazy_dir; // per unit: checkpoint directory still to load from (lazy restore)
     // streams and events
@@ -276,14 +277,19 @@ struct Ctx {
     std::thread slab_thread;
     std::mutex q_mu;
     std::condition_variable q_cv, free_cv;
-    // One host Adam update of a unit; slab < 0: the gradient is already in
-    // the store's G region (the input embedding).  Carries its own step's
+    // One host job on a unit's gradient; slab < 0: the gradient is already
+    // in the store's G region (the input embedding).  Carries its own step's
     // hyper-parameters: with cross_step it may run during the next step.
+    // Modes: a one-micro-batch step copies the slab into G and runs Adam;
+    // with micro-batches the first stores the slab into G, the middle ones
+    // accumulate into G, the last accumulates and runs Adam.
+    enum { JOB_ADAM, JOB_STORE, JOB_ACCUM, JOB_ACCUM_ADAM };
     struct Job {
         int unit, slab;
         int64_t elems;
         AdamStep a;
         int64_t step_id;  // the step (1-based) whose gradient this is
+        int mode;
     };
     std::deque<Job> jobs;
     std::vector<int64_t> adam_gen;  // updates applied per unit
@@ -321,7 +327,8 @@ struct Ctx {
 
     ~Ctx();
     int init(const mt_shape& sh, const mt_options& o, void* arena, uint64_t bytes, void* const streams[3]);
-    int train_step(const int32_t* tokens, const int32_t* labels, int B, int S, float* loss, mt_stats* stats);
+    int train_step(const int32_t* tokens, const int32_t* labels, int n_micro, int B, int S, float* loss,
+                   mt_stats* stats);
     int layer_fwd(int layer, const void* x, void* y, int B, int S);
     int layer_bwd(int layer, const void* x, const void* dy, void* dx, void* gtile, int B, int S);
 
@@ -370,13 +377,14 @@ struct Ctx {
     hipError_t fwd_layer(const LayerView& w, const uint16_t* x, uint16_t* y, int B, int S, bool need_y);
     hipError_t bwd_layer(const LayerView& w, const LayerView& g, const uint16_t* x, const uint16_t* dy,
                          uint16_t* dx, int B, int S);
-    hipError_t head(const HeadView& w, const HeadView& g, const uint16_t* xL, uint16_t* dy, int B, int S);
+    hipError_t head(const HeadView& w, const HeadView& g, const uint16_t* xL, uint16_t* dy, int B, int S,
+                    float inv_tokens);
     hipError_t ensure_rope(int S);
     int pick_slot(int unit, bool* need_stream);
     int stream_unit(int unit, int slot);
     void slab_worker();
     int acquire_slab();
-    void enqueue_job(int unit, int slab);
+    void enqueue_job(int unit, int slab, int mode);
     int drain_jobs();
     int wait_adam(int unit);
     int ensure_loaded(int unit);
@@ -593,8 +601,15 @@ void Ctx::slab_worker() {
         } else {
             const auto t0 = Clock::now();
             const TilePtrs tp = tile_ptrs(store, lay, j.unit, wblock);
-            adam_unit(*adam_pool, tp, j.slab >= 0 ? reinterpret_cast<const uint16_t*>(slabs[j.slab]) : tp.g,
-                      j.elems, j.a);
+            const uint16_t* src = j.slab >= 0 ? reinterpret_cast<const uint16_t*>(slabs[j.slab]) : tp.g;
+            switch (j.mode) {
+                case JOB_ADAM: adam_unit(*adam_pool, tp, src, j.elems, j.a); break;
+                case JOB_STORE: parallel_copy(*adam_pool, tp.g, src, j.elems * 2); break;
+                case JOB_ACCUM: accum_unit(*adam_pool, tp.g, src, j.elems); break;
+                default:
+                    accum_unit(*adam_pool, tp.g, src, j.elems);
+                    adam_unit(*adam_pool, tp, tp.g, j.elems, j.a);
+            }
             const double ms = ms_since(t0);
             std::lock_guard<std::mutex> lk(q_mu);
             adam_ms_acc += ms;
@@ -606,7 +621,7 @@ void Ctx::slab_worker() {
                 worker_error = err;
             }
             if (j.slab >= 0) free_slabs.push_back(j.slab);
-            ++adam_gen[j.unit];
+            if (j.mode == JOB_ADAM || j.mode == JOB_ACCUM_ADAM) ++adam_gen[j.unit];
             --jobs_pending;
         }
         free_cv.notify_all();
@@ -623,10 +638,10 @@ int Ctx::acquire_slab() {
     return k;
 }
 
-void Ctx::enqueue_job(int unit, int slab) {
+void Ctx::enqueue_job(int unit, int slab, int mode) {
     {
         std::lock_guard<std::mutex> lk(q_mu);
-        jobs.push_back({unit, slab, lay.units[unit].elems, cur_adam, step + 1});
+        jobs.push_back({unit, slab, lay.units[unit].elems, cur_adam, step + 1, mode});
         ++jobs_pending;
     }
     q_cv.notify_one();
@@ -841,7 +856,8 @@ hipError_t Ctx::bwd_layer(const LayerView& w, const LayerView& g, const uint16_t
 
 // LM head, forward and backward fused over token chunks; writes dy (the
 // gradient of the last layer's output) and the head gradients into g.
-hipError_t Ctx::head(const HeadView& w, const HeadView& g, const uint16_t* xL, uint16_t* dy, int B, int S) {
+hipError_t Ctx::head(const HeadView& w, const HeadView& g, const uint16_t* xL, uint16_t* dy, int B, int S,
+                     float inv_tokens) {
     const mt_shape& sh = lay.sh;
     const int T = B * S, d = sh.d_model, V = sh.vocab;
     hipStream_t s = st_c;
@@ -855,7 +871,7 @@ hipError_t Ctx::head(const HeadView& w, const HeadView& g, const uint16_t* xL, u
             return gemm(GEMM_NT, EPI_F32, a, s);
         }));
         HIPR(site(S_HEAD_CE, [&] {
-            return ce_fwd_bwd(ws.logits, ws.labels + r0, ws.loss_rows + r0, ws.dlogits, rows, V, 1.0f / float(T), s);
+            return ce_fwd_bwd(ws.logits, ws.labels + r0, ws.loss_rows + r0, ws.dlogits, rows, V, inv_tokens, s);
         }));
         HIPR(site(S_HEAD_DX, [&] {
             GemmArgs a{ws.dlogits, V, w.eout, d, ws.dnf + int64_t(r0) * d, d, nullptr, 0, nullptr, 0, rows, d, V};
@@ -923,18 +939,20 @@ int Ctx::stream_unit(int unit, int slot) {
 }
 
 // ------------------------------------------------------------ the step ----
-int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int B, int S, float* loss_out,
+int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, int B, int S, float* loss_out,
                     mt_stats* stats) {
     if (failed) MT_FAIL(MT_E_STATE, "context failed earlier");
     if (!tokens || !labels || !loss_out) MT_FAIL(MT_E_INVAL, "tokens, labels and loss_out must not be NULL");
     if (B < 1 || S < 1 || int64_t(B) * S > ws.maxT || S > opt.max_seq)
         MT_FAIL(MT_E_INVAL, "batch %d x seq %d exceeds the workspace (max_batch*max_seq = %lld, max_seq = %d)",
                 B, S, (long long)ws.maxT, opt.max_seq);
+    if (n_micro < 1 || n_micro > MT_MAX_MICRO)
+        MT_FAIL(MT_E_INVAL, "n_micro = %d outside [1, %d]", n_micro, MT_MAX_MICRO);
     const mt_shape& sh = lay.sh;
     const int T = B * S, L = sh.n_layers, d = sh.d_model, V = sh.vocab;
-    for (int t = 0; t < T; ++t)
+    for (int64_t t = 0; t < int64_t(n_micro) * T; ++t)
         if (tokens[t] < 0 || tokens[t] >= V || labels[t] < 0 || labels[t] >= V)
-            MT_FAIL(MT_E_INVAL, "token or label at row %d outside [0, %d)", t, V);
+            MT_FAIL(MT_E_INVAL, "token or label at row %lld outside [0, %d)", (long long)t, V);
 
     const auto t_start = Clock::now();
     // Adam rewrote every unit's weights after the last step: no slot holds
@@ -954,26 +972,11 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int B, int S, 
     timing = true;
     const uint64_t td = uint64_t(T) * d * 2;
     const uint64_t td_al = al4k(uint64_t(ws.maxT) * d * 2);
+    // Each micro-batch's loss gradient is that of the mean over all n*B*S
+    // tokens: 1/(n T) (a power-of-two multiple of 1/T's rounding when n is a
+    // power of two).
+    const float inv_tokens = 1.0f / float(int64_t(n_micro) * T);
     HIPC(hipEventRecord(t_base, st_c));
-
-    // Labels and the embedding gather (host, exact) go up on the weight stream.
-    memcpy(lab_pin, labels, size_t(T) * 4);
-    HIPC(h2d(ws.labels, lab_pin, uint64_t(T) * 4, st_w));
-    {
-        const int le = ensure_loaded(lay.embed());
-        if (le != MT_OK) return le;
-        // The previous step's update of E_in (queued with cross_step) first.
-        const int we = wait_adam(lay.embed());
-        if (we != MT_OK) return we;
-        const TilePtrs e = tile_ptrs(store, lay, lay.embed(), wblock);
-        pack_pool->parallel_for(T, 64, [&](int64_t b, int64_t en) {
-            for (int64_t t = b; t < en; ++t)
-                memcpy(x0_pin + t * d, e.w + int64_t(tokens[t]) * d, size_t(d) * 2);
-        });
-    }
-    uint16_t* x_first = opt.ckpt_on_host ? ws.x[0] : ws.ckpt_dev;
-    HIPC(h2d(x_first, x0_pin, td, st_w));
-    HIPC(rec(emb_ready, st_w));
     HIPC(ensure_rope(S));
     if (opt.resident) {
         // The comparison run: every unit's weights copied up once, no streaming.
@@ -991,7 +994,8 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int B, int S, 
     // the head, then per checkpoint block from the top: restore the block's
     // first input, re-run the forward of its first k-1 layers to rebuild the
     // other inputs, and run the block's backward from its last layer down.
-    // With k = 1 this is forward 0..L-1, head, backward L-1..0.
+    // With k = 1 this is forward 0..L-1, head, backward L-1..0.  Every
+    // micro-batch of the step runs the whole schedule with the same weights.
     enum { V_FWD, V_HEAD, V_REFWD, V_BWD };
     struct Visit {
         int kind, unit, block, pos;  // block: backward block counter; pos: the layer's index in its block
@@ -1005,157 +1009,210 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int B, int S, 
         for (int i = b0; i < e0; ++i) sched.push_back({V_REFWD, i, bi, i - b0});
         for (int l = e0; l >= b0; --l) sched.push_back({V_BWD, l, bi, l - b0});
     }
-    int gnext = 0, nbwd = 0, restored = -1;
     const bool combined = opt.slot_mode == 1;
-    double t_fwd = 0, t_head = 0;
-    hipEvent_t ph_fwd_end = nullptr, ph_head_end = nullptr, ph_bwd_end = nullptr;
-    for (const Visit& vs : sched) {
-        const int kind = vs.kind, unit = vs.unit;
-        // Bind target: a streamed slot or the resident copy.
-        int slot = 0;
-        void* wbase;
-        if (opt.resident) {
-            wbase = arena + plan.resident[unit];
-        } else {
-            bool need = false;
-            slot = pick_slot(unit, &need);
-            if (need) {
-                const int r = stream_unit(unit, slot);
-                if (r != MT_OK) {
-                    drain_jobs();
-                    return r;
+    // Phase edges per micro-batch: start, end of forward, of the head, of the backward.
+    struct Phases {
+        hipEvent_t start, fwd, head, bwd;
+    };
+    std::vector<Phases> phases;
+    double loss_sum = 0.0;
+    double t_bwd = 0.0;
+    for (int mb = 0; mb < n_micro; ++mb) {
+        const int32_t* tk = tokens + int64_t(mb) * T;
+        const int32_t* lb = labels + int64_t(mb) * T;
+        const int mode = n_micro == 1        ? JOB_ADAM
+                         : mb == 0           ? JOB_STORE
+                         : mb + 1 < n_micro ? JOB_ACCUM
+                                             : JOB_ACCUM_ADAM;
+        Phases ph{mb == 0 ? t_base : phases.back().bwd, nullptr, nullptr, nullptr};
+        // The previous micro-batch's use of the labels and input buffers is over.
+        if (mb > 0) HIPC(hipStreamWaitEvent(st_w, ph.start, 0));
+
+        // Labels and the embedding gather (host, exact) go up on the weight stream.
+        memcpy(lab_pin, lb, size_t(T) * 4);
+        HIPC(h2d(ws.labels, lab_pin, uint64_t(T) * 4, st_w));
+        {
+            const int le = ensure_loaded(lay.embed());
+            if (le != MT_OK) return le;
+            // The previous step's update of E_in (queued with cross_step) first.
+            const int we = wait_adam(lay.embed());
+            if (we != MT_OK) return we;
+            const TilePtrs e = tile_ptrs(store, lay, lay.embed(), wblock);
+            pack_pool->parallel_for(T, 64, [&](int64_t b, int64_t en) {
+                for (int64_t t = b; t < en; ++t)
+                    memcpy(x0_pin + t * d, e.w + int64_t(tk[t]) * d, size_t(d) * 2);
+            });
+        }
+        uint16_t* x_first = opt.ckpt_on_host ? ws.x[0] : ws.ckpt_dev;
+        HIPC(h2d(x_first, x0_pin, td, st_w));
+        HIPC(rec(emb_ready, st_w));
+
+        int gnext = 0, nbwd = 0, restored = -1;
+        for (const Visit& vs : sched) {
+            const int kind = vs.kind, unit = vs.unit;
+            // Bind target: a streamed slot or the resident copy.
+            int slot = 0;
+            void* wbase;
+            if (opt.resident) {
+                wbase = arena + plan.resident[unit];
+            } else {
+                bool need = false;
+                slot = pick_slot(unit, &need);
+                if (need) {
+                    const int r = stream_unit(unit, slot);
+                    if (r != MT_OK) {
+                        drain_jobs();
+                        return r;
+                    }
                 }
+                wbase = arena + plan.wslot[slot];
             }
-            wbase = arena + plan.wslot[slot];
-        }
-        const int bank = vs.block & 1;
-        uint16_t* const* xb = opt.ckpt_on_host ? ws.xc.data() + size_t(bank) * K : nullptr;
-        if ((kind == V_REFWD || kind == V_BWD) && opt.ckpt_on_host && vs.block != restored) {
-            // Restore the block's first input from the host ring.
-            restored = vs.block;
-            if (vs.block == 0) HIPC(wait(st_w, fwd_ckpt_all));
-            HIPC(wait(st_w, xc_free[bank]));
-            HIPC(h2d(xb[0], ckpt_host + uint64_t(unit / K) * td_al, td, st_w));
-        }
-        Ev& wr = wready[slot];
-        HIPC(rec(wr, st_w));
-        HIPC(wait(st_c, wr));
-        hipEvent_t va = next_tev(), vz = next_tev();
-        HIPC(hipEventRecord(va, st_c));
-        if (kind == V_FWD) {
-            const uint16_t* x = opt.ckpt_on_host ? ws.x[unit & 1] : ws.ckpt_dev + uint64_t(unit) * ws.maxT * d;
-            uint16_t* y = opt.ckpt_on_host ? ws.x[(unit + 1) & 1] : ws.ckpt_dev + uint64_t(unit + 1) * ws.maxT * d;
-            if (opt.ckpt_on_host) HIPC(wait(st_c, ckpt_done[(unit + 1) & 1]));
-            HIPC(fwd_layer(bind_layer(lay, wbase), x, y, B, S, true));
+            const int bank = vs.block & 1;
+            uint16_t* const* xb = opt.ckpt_on_host ? ws.xc.data() + size_t(bank) * K : nullptr;
+            if ((kind == V_REFWD || kind == V_BWD) && opt.ckpt_on_host && vs.block != restored) {
+                // Restore the block's first input from the host ring.
+                restored = vs.block;
+                if (vs.block == 0) HIPC(wait(st_w, fwd_ckpt_all));
+                HIPC(wait(st_w, xc_free[bank]));
+                HIPC(h2d(xb[0], ckpt_host + uint64_t(unit / K) * td_al, td, st_w));
+            }
+            Ev& wr = wready[slot];
+            HIPC(rec(wr, st_w));
+            HIPC(wait(st_c, wr));
+            hipEvent_t va = next_tev(), vz = next_tev();
+            HIPC(hipEventRecord(va, st_c));
+            if (kind == V_FWD) {
+                const uint16_t* x = opt.ckpt_on_host ? ws.x[unit & 1] : ws.ckpt_dev + uint64_t(unit) * ws.maxT * d;
+                uint16_t* y =
+                    opt.ckpt_on_host ? ws.x[(unit + 1) & 1] : ws.ckpt_dev + uint64_t(unit + 1) * ws.maxT * d;
+                if (opt.ckpt_on_host) HIPC(wait(st_c, ckpt_done[(unit + 1) & 1]));
+                HIPC(fwd_layer(bind_layer(lay, wbase), x, y, B, S, true));
+                HIPC(hipEventRecord(vz, st_c));
+                intervals.push_back({va, vz, 0, 0});
+                HIPC(rec(slot_free[slot], st_c));
+                if (opt.ckpt_on_host) {
+                    // Checkpoint the layer input on the gradient stream (idle in forward).
+                    if (unit % K == 0) {
+                        HIPC(wait(st_g, unit == 0 ? emb_ready : xready));
+                        HIPC(d2h(ckpt_host + uint64_t(unit / K) * td_al, x, td, st_g));
+                        HIPC(rec(ckpt_done[unit & 1], st_g));
+                    }
+                    HIPC(rec(xready, st_c));
+                    if (unit == L - 1) HIPC(rec(fwd_ckpt_all, st_g));
+                }
+                if (unit == L - 1) {
+                    ph.fwd = next_tev();
+                    HIPC(hipEventRecord(ph.fwd, st_c));
+                }
+                continue;
+            }
+            if (kind == V_REFWD) {
+                // Rebuild the next layer's input inside the block's bank.
+                HIPC(fwd_layer(bind_layer(lay, wbase), xb[vs.pos], xb[vs.pos + 1], B, S, true));
+                HIPC(hipEventRecord(vz, st_c));
+                intervals.push_back({va, vz, 0, 0});
+                HIPC(rec(slot_free[slot], st_c));
+                continue;
+            }
+            // Head or backward: gradients go to a gradient area, then to a slab.
+            const int ga = combined ? slot : gnext;
+            if (!combined) gnext ^= 1;
+            HIPC(wait(st_c, buf_free[ga]));
+            void* gbase = arena + plan.garea[ga];
+            if (kind == V_HEAD) {
+                const uint16_t* xL = opt.ckpt_on_host ? ws.x[L & 1] : ws.ckpt_dev + uint64_t(L) * ws.maxT * d;
+                HIPC(head(bind_head(lay, wbase), bind_head(lay, gbase), xL, ws.dy[0], B, S, inv_tokens));
+                HIPC(hipMemcpyAsync(loss_pin, ws.loss, 4, hipMemcpyDeviceToHost, st_c));
+                HIPC(rec(loss_done, st_c));
+            } else {
+                const uint16_t* x = opt.ckpt_on_host ? xb[vs.pos] : ws.ckpt_dev + uint64_t(unit) * ws.maxT * d;
+                HIPC(bwd_layer(bind_layer(lay, wbase), bind_layer(lay, gbase), x, ws.dy[nbwd & 1],
+                               ws.dy[(nbwd + 1) & 1], B, S));
+                ++nbwd;
+                // The block's bank is free once its first layer's backward ran.
+                if (opt.ckpt_on_host && vs.pos == 0) HIPC(rec(xc_free[bank], st_c));
+            }
             HIPC(hipEventRecord(vz, st_c));
             intervals.push_back({va, vz, 0, 0});
-            HIPC(rec(slot_free[slot], st_c));
-            if (opt.ckpt_on_host) {
-                // Checkpoint the layer input on the gradient stream (idle in forward).
-                if (unit % K == 0) {
-                    HIPC(wait(st_g, unit == 0 ? emb_ready : xready));
-                    HIPC(d2h(ckpt_host + uint64_t(unit / K) * td_al, x, td, st_g));
-                    HIPC(rec(ckpt_done[unit & 1], st_g));
-                }
-                HIPC(rec(xready, st_c));
-                if (unit == L - 1) HIPC(rec(fwd_ckpt_all, st_g));
+            if (!combined) HIPC(rec(slot_free[slot], st_c));
+            HIPC(rec(bwd_done[ga], st_c));
+            // Gradient offload: Backward-Done -> free slab -> Buffer-Free.
+            const int k = acquire_slab();
+            HIPC(wait(st_g, bwd_done[ga]));
+            HIPC(d2h(slabs[k], gbase, uint64_t(lay.units[unit].elems) * 2, st_g));
+            HIPC(rec(slab_done[k], st_g));
+            HIPC(rec(buf_free[ga], st_g));
+            if (combined) HIPC(rec(slot_free[slot], st_g));
+            enqueue_job(unit, k, mode);
+            if (kind == V_HEAD) {
+                ph.head = next_tev();
+                HIPC(hipEventRecord(ph.head, st_c));
             }
-            if (unit == L - 1) {
-                ph_fwd_end = next_tev();
-                HIPC(hipEventRecord(ph_fwd_end, st_c));
-                t_fwd = ms_since(t_start);
-            }
-            continue;
         }
-        if (kind == V_REFWD) {
-            // Rebuild the next layer's input inside the block's bank.
-            HIPC(fwd_layer(bind_layer(lay, wbase), xb[vs.pos], xb[vs.pos + 1], B, S, true));
-            HIPC(hipEventRecord(vz, st_c));
-            intervals.push_back({va, vz, 0, 0});
-            HIPC(rec(slot_free[slot], st_c));
-            continue;
+        if (mb + 1 == n_micro) {
+            std::lock_guard<std::mutex> lk(q_mu);
+            bwd_complete = step + 1;
         }
-        // Head or backward: gradients go to a gradient area, then to a slab.
-        const int ga = combined ? slot : gnext;
-        if (!combined) gnext ^= 1;
-        HIPC(wait(st_c, buf_free[ga]));
-        void* gbase = arena + plan.garea[ga];
-        if (kind == V_HEAD) {
-            const uint16_t* xL = opt.ckpt_on_host ? ws.x[L & 1] : ws.ckpt_dev + uint64_t(L) * ws.maxT * d;
-            HIPC(head(bind_head(lay, wbase), bind_head(lay, gbase), xL, ws.dy[0], B, S));
-            HIPC(hipMemcpyAsync(loss_pin, ws.loss, 4, hipMemcpyDeviceToHost, st_c));
-            HIPC(rec(loss_done, st_c));
-        } else {
-            const uint16_t* x = opt.ckpt_on_host ? xb[vs.pos] : ws.ckpt_dev + uint64_t(unit) * ws.maxT * d;
-            HIPC(bwd_layer(bind_layer(lay, wbase), bind_layer(lay, gbase), x, ws.dy[nbwd & 1], ws.dy[(nbwd + 1) & 1],
-                           B, S));
-            ++nbwd;
-            // The block's bank is free once its first layer's backward ran.
-            if (opt.ckpt_on_host && vs.pos == 0) HIPC(rec(xc_free[bank], st_c));
-        }
-        HIPC(hipEventRecord(vz, st_c));
-        intervals.push_back({va, vz, 0, 0});
-        if (!combined) HIPC(rec(slot_free[slot], st_c));
-        HIPC(rec(bwd_done[ga], st_c));
-        // Gradient offload: Backward-Done -> free slab -> Buffer-Free.
-        const int k = acquire_slab();
-        HIPC(wait(st_g, bwd_done[ga]));
-        HIPC(d2h(slabs[k], gbase, uint64_t(lay.units[unit].elems) * 2, st_g));
-        HIPC(rec(slab_done[k], st_g));
-        HIPC(rec(buf_free[ga], st_g));
-        if (combined) HIPC(rec(slot_free[slot], st_g));
-        enqueue_job(unit, k);
-        if (kind == V_HEAD) {
-            ph_head_end = next_tev();
-            HIPC(hipEventRecord(ph_head_end, st_c));
-            t_head = ms_since(t_start);
-        }
-    }
-    {
-        std::lock_guard<std::mutex> lk(q_mu);
-        bwd_complete = step + 1;
-    }
-    ph_bwd_end = next_tev();
-    HIPC(hipEventRecord(ph_bwd_end, st_c));
-    // Embedding backward on the host: dX0 down, scatter-add in token order.
-    const uint16_t* dx0 = ws.dy[L & 1];
-    HIPC(hipStreamWaitEvent(st_g, ph_bwd_end, 0));
-    HIPC(d2h(dx0_pin, dx0, td, st_g));
-    HIPC(rec(dx0_done, st_g));
-    HIPC(hsync(dx0_done));
-    const double t_bwd = ms_since(t_start);
-    {
+        ph.bwd = next_tev();
+        HIPC(hipEventRecord(ph.bwd, st_c));
+        phases.push_back(ph);
+        // Embedding backward on the host: dX0 down, scatter-add in token order.
+        const uint16_t* dx0 = ws.dy[L & 1];
+        HIPC(hipStreamWaitEvent(st_g, ph.bwd, 0));
+        HIPC(d2h(dx0_pin, dx0, td, st_g));
+        HIPC(rec(dx0_done, st_g));
+        HIPC(hsync(dx0_done));
+        HIPC(hsync(loss_done));
+        loss_sum += double(*loss_pin);
+        t_bwd = ms_since(t_start);
         const TilePtrs e = tile_ptrs(store, lay, lay.embed(), wblock);
-        // Clear last step's rows, then accumulate this step's in fp32.
-        if (ein_clear_all) memset(e.g, 0, size_t(V) * d * 2);
-        ein_clear_all = false;
-        for (int32_t r : ein_touched) memset(e.g + int64_t(r) * d, 0, size_t(d) * 2);
-        std::vector<char> seen(size_t(V), 0);
-        ein_touched.clear();
-        for (int t = 0; t < T; ++t)
-            if (!seen[tokens[t]]) {
-                seen[tokens[t]] = 1;
-                ein_touched.push_back(tokens[t]);
-            }
+        if (mb == 0) {
+            // Clear last step's rows; rows not listed are zero.
+            if (ein_clear_all) memset(e.g, 0, size_t(V) * d * 2);
+            ein_clear_all = false;
+            for (int32_t r : ein_touched) memset(e.g + int64_t(r) * d, 0, size_t(d) * 2);
+            ein_touched.clear();
+            ein_seen.assign(size_t(V), 0);
+        }
+        // This micro-batch's distinct rows, summed in fp32 in token order,
+        // rounded to bf16 once, then stored (first micro-batch) or added into G
+        // with one more rounding (the others), as the slab jobs do.
+        std::vector<int32_t> rows;
+        {
+            std::vector<char> seen(size_t(V), 0);
+            for (int t = 0; t < T; ++t)
+                if (!seen[tk[t]]) {
+                    seen[tk[t]] = 1;
+                    rows.push_back(tk[t]);
+                    if (!ein_seen[tk[t]]) {
+                        ein_seen[tk[t]] = 1;
+                        ein_touched.push_back(tk[t]);
+                    }
+                }
+        }
         float* acc = ein_acc.data();
         pack_pool->parallel_for(d, 64, [&](int64_t c0, int64_t c1) {
-            for (int32_t r : ein_touched)
+            for (int32_t r : rows)
                 for (int64_t c = c0; c < c1; ++c) acc[int64_t(r) * d + c] = 0.f;
             for (int t = 0; t < T; ++t) {
-                float* row = acc + int64_t(tokens[t]) * d;
+                float* row = acc + int64_t(tk[t]) * d;
                 const uint16_t* g = dx0_pin + int64_t(t) * d;
                 for (int64_t c = c0; c < c1; ++c) row[c] += bf16_to_f32(g[c]);
             }
-            for (int32_t r : ein_touched)
-                for (int64_t c = c0; c < c1; ++c) e.g[int64_t(r) * d + c] = f32_to_bf16(acc[int64_t(r) * d + c]);
+            for (int32_t r : rows)
+                for (int64_t c = c0; c < c1; ++c) {
+                    uint16_t& gr = e.g[int64_t(r) * d + c];
+                    const uint16_t v = f32_to_bf16(acc[int64_t(r) * d + c]);
+                    gr = mb == 0 ? v : f32_to_bf16(bf16_to_f32(gr) + bf16_to_f32(v));
+                }
         });
-        if (lay.embed() == fault_slab) {
-            drain_jobs();
-            failed = true;
-            MT_FAIL(MT_E_INTERNAL, "injected slab-worker fault at unit %d", lay.embed());
-        }
-        enqueue_job(lay.embed(), -1);
     }
+    if (lay.embed() == fault_slab) {
+        drain_jobs();
+        failed = true;
+        MT_FAIL(MT_E_INTERNAL, "injected slab-worker fault at unit %d", lay.embed());
+    }
+    enqueue_job(lay.embed(), -1, JOB_ADAM);
     // Synchronous step: every update lands before returning.  cross_step:
     // they run on; report a worker error that has already happened.
     int jr = MT_OK;
@@ -1175,7 +1232,7 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int B, int S, 
     HIPC(hipStreamSynchronize(st_w));
     HIPC(hipStreamSynchronize(st_g));
     if (jr != MT_OK) return jr;
-    *loss_out = *loss_pin;
+    *loss_out = float(loss_sum / n_micro);  // mean over every token of the step
     ++step;
     const double t_total = ms_since(t_start);
 
@@ -1187,14 +1244,12 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int B, int S, 
             hipEventElapsedTime(&ms, a, b);
             return double(ms);
         };
-        if (ph_fwd_end && ph_head_end) {
-            stats->fwd_ms = el(t_base, ph_fwd_end);
-            stats->head_ms = el(ph_fwd_end, ph_head_end);
-            stats->bwd_ms = el(ph_head_end, ph_bwd_end);
+        for (const Phases& ph : phases) {
+            stats->fwd_ms += el(ph.start, ph.fwd);
+            stats->head_ms += el(ph.fwd, ph.head);
+            stats->bwd_ms += el(ph.head, ph.bwd);
         }
         stats->adam_tail_ms = t_total - t_bwd;
-        (void)t_fwd;
-        (void)t_head;
         // Interval unions: compute C, copies X = H2D u D2H.
         std::vector<std::pair<double, double>> C, X, H;
         for (auto& iv : intervals) {
@@ -1255,14 +1310,21 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int B, int S, 
         stats->pcie_busy_frac = t_total > 0 ? len(Hm) / t_total : 0.0;
         // The same per phase (forward, head, backward), and the transfer time
         // no compute hides, |X \ C|.
-        if (ph_fwd_end && ph_head_end && ph_bwd_end) {
-            const double edges[4] = {0.0, el(t_base, ph_fwd_end), el(t_base, ph_head_end), el(t_base, ph_bwd_end)};
+        // Summed over the micro-batches' windows of each phase.
+        double ip[3] = {}, lcp[3] = {}, lxp[3] = {};
+        for (const Phases& ph : phases) {
+            const double edges[4] = {el(t_base, ph.start), el(t_base, ph.fwd), el(t_base, ph.head),
+                                     el(t_base, ph.bwd)};
             for (int p = 0; p < 3; ++p) {
                 const auto Cp = clip(Cm, edges[p], edges[p + 1]), Xp = clip(Xm, edges[p], edges[p + 1]);
-                const double ip = intersect(Cp, Xp), lcp = len(Cp), lxp = len(Xp);
-                stats->overlap_phase[p] = std::min(lcp, lxp) > 0 ? ip / std::min(lcp, lxp) : 0.0;
-                stats->exposed_transfer_ms[p] = lxp - ip;
+                ip[p] += intersect(Cp, Xp);
+                lcp[p] += len(Cp);
+                lxp[p] += len(Xp);
             }
+        }
+        for (int p = 0; p < 3; ++p) {
+            stats->overlap_phase[p] = std::min(lcp[p], lxp[p]) > 0 ? ip[p] / std::min(lcp[p], lxp[p]) : 0.0;
+            stats->exposed_transfer_ms[p] = lxp[p] - ip[p];
         }
         stats->pack_ms = pack_ms;
         {
@@ -1426,10 +1488,25 @@ int mt_train_step(mt_ctx* c, const int32_t* tokens, const int32_t* labels, int32
         return MT_E_INVAL;
     }
     try {
-        return c->impl.train_step(tokens, labels, batch, seq, loss_out, stats);
+        return c->impl.train_step(tokens, labels, 1, batch, seq, loss_out, stats);
     } catch (...) {
         c->impl.failed = true;
         mt::set_error("unexpected exception in mt_train_step");
+        return MT_E_INTERNAL;
+    }
+}
+
+int mt_train_step_accum(mt_ctx* c, const int32_t* tokens, const int32_t* labels, int32_t n_micro, int32_t batch,
+                        int32_t seq, float* loss_out, mt_stats* stats) {
+    if (!c) {
+        mt::set_error("ctx is NULL");
+        return MT_E_INVAL;
+    }
+    try {
+        return c->impl.train_step(tokens, labels, n_micro, batch, seq, loss_out, stats);
+    } catch (...) {
+        c->impl.failed = true;
+        mt::set_error("unexpected exception in mt_train_step_accum");
         return MT_E_INTERNAL;
     }
 }

@@ -358,4 +358,28 @@ void adam_unit(ThreadPool& pool, const TilePtrs& p, const uint16_t* gsrc, int64_
     pool.parallel_for(n, 1 << 15, [&](int64_t b, int64_t e) { adam_range(p, gsrc, b, e, a); });
 }
 
+// Gradient accumulation into the host G ([Review] 3-2 item 1: the host holds
+// the accumulated gradient; [Hotdry] "三层 CUDA Stream 流水线与双缓冲调度": the
+// CPU thread unpacks each slab and accumulates it into the master store).
+// G <- bf16_RNE(f32(G) + f32(src)): the sum of two bf16 values is exact in
+// fp32 whenever it can round differently, so this is one rounding of the
+// exact sum.  The vector loop does the same operations lane by lane.
+void accum_range(uint16_t* G, const uint16_t* src, int64_t b, int64_t e) {
+    int64_t i = b;
+    while (i < e && (reinterpret_cast<uintptr_t>(G + i) & 15)) {
+        G[i] = f32_to_bf16(bf16_to_f32(G[i]) + bf16_to_f32(src[i]));
+        ++i;
+    }
+    for (; i + 8 <= e; i += 8) {
+        const __m256 a = bf16x8_to_f32(_mm_load_si128(reinterpret_cast<const __m128i*>(G + i)));
+        const __m256 c = bf16x8_to_f32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(src + i)));
+        _mm_store_si128(reinterpret_cast<__m128i*>(G + i), f32x8_to_bf16(_mm256_add_ps(a, c)));
+    }
+    for (; i < e; ++i) G[i] = f32_to_bf16(bf16_to_f32(G[i]) + bf16_to_f32(src[i]));
+}
+
+void accum_unit(ThreadPool& pool, uint16_t* G, const uint16_t* src, int64_t n) {
+    pool.parallel_for(n, 1 << 15, [&](int64_t b, int64_t e) { accum_range(G, src, b, e); });
+}
+
 }  // namespace mt

@@ -150,6 +150,9 @@ AdamStep adam_step_params(const mt_options& o, int64_t t);
 void adam_range(const TilePtrs& p, const uint16_t* gsrc, int64_t b, int64_t e, const AdamStep& a);
 void adam_unit(ThreadPool& pool, const TilePtrs& p, const uint16_t* gsrc, int64_t n,
                const AdamStep& a);
+// G <- bf16(G + src) elementwise (gradient accumulation across micro-batches).
+void accum_range(uint16_t* G, const uint16_t* src, int64_t b, int64_t e);
+void accum_unit(ThreadPool& pool, uint16_t* G, const uint16_t* src, int64_t n);
 
 // ------------------------------------------------- checkpoint shards ----
 std::string shard_path(const std::string& dir, int unit);

@@ -20,6 +20,7 @@ lib = C.CDLL(_LIB_PATH)
 MT_OK, MT_E_INVAL, MT_E_NOMEM, MT_E_HIP, MT_E_STATE, MT_E_INTERNAL, MT_E_IO = 0, -1, -2, -3, -4, -5, -6
 MT_W, MT_G, MT_MASTER, MT_M, MT_V = 0, 1, 2, 3, 4
 MT_MAX_SITES = 48
+MT_MAX_MICRO = 4096
 
 
 class mt_shape(C.Structure):
@@ -66,6 +67,8 @@ _SIGS = {
                           C.POINTER(_P)]),
     "mt_train_step": (C.c_int, [_P, C.POINTER(C.c_int32), C.POINTER(C.c_int32), C.c_int32, C.c_int32,
                                 C.POINTER(C.c_float), C.POINTER(mt_stats)]),
+    "mt_train_step_accum": (C.c_int, [_P, C.POINTER(C.c_int32), C.POINTER(C.c_int32), C.c_int32, C.c_int32,
+                                      C.c_int32, C.POINTER(C.c_float), C.POINTER(mt_stats)]),
     "mt_layer_fwd": (C.c_int, [_P, C.c_int32, _P, _P, C.c_int32, C.c_int32]),
     "mt_layer_bwd": (C.c_int, [_P, C.c_int32, _P, _P, _P, _P, C.c_int32, C.c_int32]),
     "mt_tensor_desc": (C.c_int, [C.POINTER(mt_shape), C.c_int32, C.c_int32, C.POINTER(mt_tensor_info)]),
@@ -104,6 +107,7 @@ _SIGS = {
     "mt_k_bf16_to_f16": (C.c_int, [_P, _P, C.c_int64, _P]),
     "mt_host_adam": (C.c_int, [_P, _P, _P, _P, _P, _P, C.c_int64, C.c_int64, C.c_float, C.c_float, C.c_float,
                                C.c_float, C.c_int32]),
+    "mt_host_accum": (C.c_int, [_P, _P, C.c_int64, C.c_int32]),
     "mt_host_init_unit": (C.c_int, [C.POINTER(mt_shape), C.c_int32, C.c_uint64, C.c_float, C.c_int32, _P,
                                     C.c_uint64]),
 }
@@ -214,6 +218,18 @@ class Context:
         check(lib.mt_train_step(self._ptr, tokens.ctypes.data_as(C.POINTER(C.c_int32)),
                                 labels.ctypes.data_as(C.POINTER(C.c_int32)), b, s, C.byref(loss),
                                 C.byref(st) if st is not None else None), "mt_train_step")
+        return loss.value, st
+
+    def train_step_accum(self, tokens, labels, stats=True):
+        """tokens, labels: [n_micro, batch, seq]."""
+        tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+        labels = np.ascontiguousarray(labels, dtype=np.int32)
+        n, b, s = tokens.shape
+        loss = C.c_float()
+        st = mt_stats() if stats else None
+        check(lib.mt_train_step_accum(self._ptr, tokens.ctypes.data_as(C.POINTER(C.c_int32)),
+                                      labels.ctypes.data_as(C.POINTER(C.c_int32)), n, b, s, C.byref(loss),
+                                      C.byref(st) if st is not None else None), "mt_train_step_accum")
         return loss.value, st
 
     def layer_fwd(self, layer, x_ptr, y_ptr, batch, seq):

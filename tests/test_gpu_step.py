@@ -221,6 +221,123 @@ def test_checkpoint_interval_bit_identical(deep_baseline_run, opts):
         assert np.array_equal(a1.view(np.uint8), a2.view(np.uint8)), (k1, w1)
 
 
+# -------------------------------------------- gradient accumulation ----
+def _micro_batches(kw, n, B, S, seed0):
+    tl = [synth.tokens_labels(seed0 + j, B, S, kw["vocab"]) for j in range(n)]
+    return np.stack([t for t, _ in tl]), np.stack([lb for _, lb in tl])
+
+
+def test_accumulated_step_parity():
+    """Three micro-batches, one optimizer step, against the oracle: the loss
+    over every token, the accumulated gradients, and Adam run once on them."""
+    kw, B, S, n = CFG1, 1, 96, 3
+    log(f"accumulated step {n} x B={B} S={S}")
+    ctx = make_ctx(kw, B, S)
+    tokens, labels = _micro_batches(kw, n, B, S, 300)
+    params = read_params(ctx, kw)
+    masters0 = read_all(ctx, kw, mt.MT_MASTER)
+    loss, st = ctx.train_step_accum(tokens, labels)
+    log(f"  loss gpu {loss:.6f}  step {st.step_ms:.1f} ms")
+    loss_ref, g_ref = ostep.grads_accumulated(params, tokens, labels, oracle_shape(kw))
+    assert abs(loss - loss_ref) / abs(loss_ref) <= 1e-2, (loss, loss_ref)
+    _cmp_units(ctx, kw, g_ref, per_tensor=True)
+    for (u, j), m0 in masters0:
+        g = widen(ctx.get_tensor(u, j, mt.MT_G))
+        z = np.zeros_like(m0)
+        mst, m, v, w = ostep.adam_update(m0, z, z, g, 1, 1e-4, 0.9, 0.999, 1e-8)
+        got = ctx.get_tensor(u, j, mt.MT_MASTER)
+        err = np.abs(got.astype(np.float64) - mst.astype(np.float64))
+        assert np.all(err <= np.maximum(2 * np.spacing(np.abs(mst)).astype(np.float64), 1e-10)), (u, j)
+        np.testing.assert_allclose(ctx.get_tensor(u, j, mt.MT_M), m, rtol=1e-6, atol=1e-30)
+    assert ctx.step_count() == 1
+    ctx.close()
+
+
+def test_accumulation_is_the_bf16_sum_of_separate_micro_batch_gradients():
+    """Two micro-batches give, bit for bit, the one-rounding BF16 sum of half
+    the gradients two fresh contexts compute for each micro-batch alone (the
+    loss scale 1/(2T) is exactly half of 1/T, and every gradient is linear in
+    it), which pins the host accumulation of every unit, the input embedding
+    included."""
+    kw, B, S = GQA, 2, 48
+    log("accumulation vs separate micro-batch gradients")
+    tokens, labels = _micro_batches(kw, 2, B, S, 400)
+    sep = []
+    for j in range(2):
+        c = make_ctx(kw, B, S)
+        c.train_step(tokens[j], labels[j])
+        sep.append([a for _, a in read_all(c, kw, mt.MT_G)])
+        c.close()
+    ctx = make_ctx(kw, B, S)
+    ctx.train_step_accum(tokens, labels)
+    got = read_all(ctx, kw, mt.MT_G)
+    ctx.close()
+    for (key, g), g0, g1 in zip(got, sep[0], sep[1]):
+        want = ostep.accumulate_bf16(widen(g0) * 0.5, widen(g1) * 0.5)
+        assert np.array_equal(widen(g), want), key
+
+
+def test_identical_micro_batches_equal_one_micro_batch_bit_for_bit():
+    kw, B, S = GQA, 2, 64
+    log("n identical micro-batches vs one")
+    base_losses, base_state = _run_two_steps(kw, B, S)
+    for n in (2, 4):
+        ctx = make_ctx(kw, B, S)
+        losses = []
+        for k in range(2):
+            t, lb = synth.tokens_labels(100 + k, B, S, kw["vocab"])
+            losses.append(ctx.train_step_accum(np.stack([t] * n), np.stack([lb] * n))[0])
+        state = _state(ctx, kw)
+        ctx.close()
+        assert [np.float32(x).tobytes() for x in losses] == [np.float32(x).tobytes() for x in base_losses]
+        for (k1, w1, a1), (k2, w2, a2) in zip(base_state, state):
+            assert np.array_equal(a1.view(np.uint8), a2.view(np.uint8)), (n, k1, w1)
+
+
+def _run_two_accum_steps(kw, B, S, n, **opts):
+    ctx = make_ctx(kw, B, S, **opts)
+    losses = []
+    for k in range(2):
+        t, lb = _micro_batches(kw, n, B, S, 500 + 10 * k)
+        losses.append(ctx.train_step_accum(t, lb)[0])
+    state = _state(ctx, kw)
+    ctx.close()
+    return losses, state
+
+
+@pytest.fixture(scope="module")
+def accum_baseline_run():
+    return _run_two_accum_steps(DEEP, 1, 64, 3)
+
+
+@pytest.mark.parametrize("opts", [dict(cross_step=1), dict(n_grad_slabs=1), dict(n_weight_slots=1),
+                                  dict(ckpt_interval=2), dict(resident=1), dict(slot_mode=1),
+                                  dict(cross_step=1, n_grad_slabs=1, ckpt_interval=3)],
+                         ids=lambda o: ",".join(f"{k}={v}" for k, v in o.items()))
+def test_accumulated_steps_bit_identical_across_streaming_options(accum_baseline_run, opts):
+    log(f"accumulated steps vs default streaming: {opts}")
+    base_losses, base_state = accum_baseline_run
+    losses, state = _run_two_accum_steps(DEEP, 1, 64, 3, **opts)
+    assert [np.float32(x).tobytes() for x in losses] == [np.float32(x).tobytes() for x in base_losses]
+    for (k1, w1, a1), (k2, w2, a2) in zip(base_state, state):
+        assert k1 == k2 and w1 == w2
+        assert np.array_equal(a1.view(np.uint8), a2.view(np.uint8)), (k1, w1)
+
+
+def test_bad_micro_batch_count_rejected():
+    kw, B, S = CFG1, 1, 16
+    ctx = make_ctx(kw, B, S)
+    t, lb = synth.tokens_labels(1, B, S, kw["vocab"])
+    for n in (0, mt.MT_MAX_MICRO + 1):
+        r = mt.lib.mt_train_step_accum(ctx._ptr, t.ctypes.data_as(mt.C.POINTER(mt.C.c_int32)),
+                                       lb.ctypes.data_as(mt.C.POINTER(mt.C.c_int32)), n, B, S,
+                                       mt.C.byref(mt.C.c_float()), None)
+        assert r == mt.MT_E_INVAL
+    assert ctx.step_count() == 0
+    ctx.train_step(t, lb)  # the context is still usable
+    ctx.close()
+
+
 # ----------------------------------------------------- checkpoint shards --
 def _state(ctx, kw):
     return [(key, which, a) for which in (mt.MT_W, mt.MT_G, mt.MT_MASTER, mt.MT_M, mt.MT_V)

@@ -40,6 +40,10 @@ def test_python_mirrors_match_the_abi_structs():
     for which, cls in enumerate((mt.mt_shape, mt.mt_options, mt.mt_stats, mt.mt_tensor_info)):
         assert mt.lib.mt_abi_sizeof(which) == C.sizeof(cls), cls.__name__
     assert mt.lib.mt_abi_sizeof(7) == -1
+    # constants the binding mirrors from the header
+    hdr = open(os.path.join(ROOT, "include", "mt.h")).read()
+    for name in ("MT_MAX_SITES", "MT_MAX_MICRO"):
+        assert int(re.search(rf"#define {name} (\d+)", hdr).group(1)) == getattr(mt, name), name
 
 
 def test_strerror_and_status_codes():
@@ -214,6 +218,32 @@ def test_host_adam_vector_path_bit_identical_to_single_elements(off):
                                    ptr(gbits, j), 1, 3, 1e-4, 0.9, 0.999, 1e-8, 1) == mt.MT_OK
     for x, y in zip(a, b):
         assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+
+
+@pytest.mark.parametrize("off", [0, 3])
+def test_host_accumulation_matches_oracle_bit_for_bit(off):
+    """The production G accumulation of micro-batch steps against the
+    oracle's one-rounding BF16 sum: random magnitudes over 60 binades, exact
+    ties (half a BF16 unit added to odd and even values), zeros, infinities,
+    both signs; an unaligned start exercises the scalar head and tail."""
+    rng = np.random.default_rng(40 + off)
+    n = 4_099
+    a = round_bf16((rng.standard_normal(n) * np.exp2(rng.integers(-30, 30, n))).astype(np.float32))
+    b = round_bf16((rng.standard_normal(n) * np.exp2(rng.integers(-30, 30, n))).astype(np.float32))
+    k = np.arange(64, dtype=np.float32)
+    a[:64] = round_bf16(np.float32(1.0) + k * np.float32(2.0 ** -7))
+    b[:64] = np.where(k % 3 == 0, -2.0 ** -8, 2.0 ** -8).astype(np.float32)
+    a[64:70] = [0.0, -0.0, np.inf, -np.inf, 1.0, 3.0]
+    b[64:70] = [-0.0, -0.0, 1.0, -2.0, -1.0, -3.0]
+    bits = lambda x: (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)  # noqa: E731
+    g = np.zeros(n + off, np.uint16)
+    src = np.zeros(n + off, np.uint16)
+    g[off:], src[off:] = bits(a), bits(b)
+    ptr = lambda x: x.ctypes.data + off * 2  # noqa: E731
+    assert mt.lib.mt_host_accum(ptr(g), ptr(src), n, 3) == mt.MT_OK
+    want = bits(ostep.accumulate_bf16(a, b))
+    assert np.array_equal(g[off:], want)
+    assert mt.lib.mt_host_accum(None, ptr(src), n, 1) == mt.MT_E_INVAL
 
 
 # ------------------------------------------------------------------ init --
