@@ -106,18 +106,22 @@ def hbm_bytes(cfg, T):
     }
 
 
-def host_bytes_per_step(cfg, T):
-    """Host DRAM bytes one synchronous step moves: Adam 30 B/param over every
-    unit, the pack (read W, streaming write to staging) and the DMA read of
-    staging for the forward and the backward visit of every streamed unit,
-    the DMA write of every streamed unit's gradient, the checkpoint ring out
-    and back in, and the embedding rows."""
+def host_bytes_per_step(cfg, T, n_micro=1):
+    """Host DRAM bytes one synchronous step moves.  Per micro-batch: the pack
+    (read W, streaming write to staging) and the DMA read of staging for the
+    forward and the backward visit of every streamed unit, the DMA write of
+    every streamed unit's gradient, the checkpoint ring out and back in, and
+    the embedding rows.  Per optimizer step and parameter: Adam's 30 B with
+    one micro-batch; with n > 1 the first stores the slab into G (4 B), each
+    middle one adds into G (6 B), the last adds and runs Adam (34 B)."""
     L, d, F, V = cfg["n_layers"], cfg["d_model"], cfg["ffn_dim"], cfg["vocab"]
     hq, hkv, hd = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]
     p_layer = d * hq * hd + 2 * d * hkv * hd + hq * hd * d + 3 * d * F + 2 * d
     streamed = L * p_layer + V * d + d
     p_embed = V * d
-    return 30 * (streamed + p_embed) + 2 * (4 + 2) * streamed + 2 * streamed + 2 * L * T * d * 2 + 2 * T * d * 2
+    per_param = 30 if n_micro == 1 else 4 + 6 * (n_micro - 2) + 34
+    per_micro = 2 * (4 + 2) * streamed + 2 * streamed + 2 * L * T * d * 2 + 2 * T * d * 2
+    return per_param * (streamed + p_embed) + n_micro * per_micro
 
 
 def model_flops_per_step(cfg, T, S):
@@ -262,10 +266,16 @@ def main():
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only launch the gate|up GEMM three times and a 1 GiB device copy three times (run "
                          "under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE to measure the GEMM's HBM traffic)")
+    ap.add_argument("--own-streams", action="store_true",
+                    help="let the library create its three streams instead of passing torch's")
+    ap.add_argument("--micro", type=int, default=1,
+                    help="micro-batches of batch x seq per optimizer step (gradient accumulation on the host)")
     ap.add_argument("--cross-step", type=int, default=0,
                     help="1: the next step's forward overlaps this step's Adam tail (same results); on a host "
                          "whose memory bandwidth the Adam already fills this is slower, so it is off by default")
     args = ap.parse_args()
+    if args.micro < 1 or (args.micro > 1 and (args.ablations or args.traffic_probe)):
+        ap.error("--micro must be >= 1, and 1 with --ablations or --traffic-probe")
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build streams one model through one MI355X; "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
@@ -292,19 +302,27 @@ def main():
     arena = torch.empty(arena_bytes, dtype=torch.uint8, device="cuda")
     streams = [torch.cuda.Stream() for _ in range(3)]
     t0 = time.time()
-    ctx = mt.Context(shape, opt, arena.data_ptr(), arena_bytes, [s.cuda_stream for s in streams])
+    ctx = mt.Context(shape, opt, arena.data_ptr(), arena_bytes,
+                     (None, None, None) if args.own_streams else [s.cuda_stream for s in streams])
     log(f"init (host store + seeded weights) {time.time() - t0:.1f} s")
     tokens, labels = synth.tokens_labels(synth.SEED_TOKENS, B, S, cfg["vocab"])
+    nm = args.micro
+    if nm > 1:
+        tl = [synth.tokens_labels(synth.SEED_TOKENS + j, B, S, cfg["vocab"]) for j in range(nm)]
+        mtok, mlab = np.stack([t for t, _ in tl]), np.stack([lb for _, lb in tl])
+
+    def one_step():
+        return ctx.train_step(tokens, labels) if nm == 1 else ctx.train_step_accum(mtok, mlab)
 
     for i in range(args.warmup):
-        loss, st = ctx.train_step(tokens, labels)
+        loss, st = one_step()
         log(f"warmup {i}: loss {loss:.4f} step {st.step_ms:.0f} ms")
     ctx.sync()  # queued host updates (cross_step) land before the clock starts
     torch.cuda.synchronize()
     stats = []
     t0 = time.perf_counter()
     for i in range(args.steps):
-        loss, st = ctx.train_step(tokens, labels)
+        loss, st = one_step()
         stats.append(mt.stats_dict(st))
         log(f"step {i}: loss {loss:.4f} step {st.step_ms:.0f} ms (fwd {st.fwd_ms:.0f} head {st.head_ms:.0f} "
             f"bwd {st.bwd_ms:.0f} adam tail {st.adam_tail_ms:.0f}; adam busy {st.adam_ms:.0f}, "
@@ -313,24 +331,25 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
-    value = T * args.steps / elapsed
+    value = nm * T * args.steps / elapsed
 
     out = {"metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 2), "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-           "config": {"workload": cfg["workload"], "global_batch": B, "seq_len": S, "layers": cfg["n_layers"],
+           "config": {"workload": cfg["workload"], "global_batch": nm * B, "micro_batches": nm, "seq_len": S,
+                      "layers": cfg["n_layers"],
                       "parallelism": "single GPU, layer-streamed", "weight_slots": args.slots,
                       "grad_slabs": args.slabs, "slot_mode": args.slot_mode, "resident": args.resident,
                       "cross_step": args.cross_step, "pin_weights": args.pin_weights}}
-    mf = model_flops_per_step(cfg, T, S)
+    mf = nm * model_flops_per_step(cfg, T, S)
     out["model_tflops_per_s"] = round(mf / (ms_per_step / 1e3) / 1e12, 2)
     # hardware FLOPs add the recomputed forward of every layer (the down GEMM
     # is not recomputed: backward needs its input, not its output)
     fl0 = gemm_flops(cfg, T)
     recompute = cfg["n_layers"] * (fl0["gemm_qkv"] + fl0["gemm_o"] + fl0["gemm_gateup"] +
                                    2 * 2 * T * cfg["n_heads"] * cfg["head_dim"] * (S + 1) / 2)
-    out["hw_tflops_per_s"] = round((mf + recompute) / (ms_per_step / 1e3) / 1e12, 2)
-    hb_step = host_bytes_per_step(cfg, T)
+    out["hw_tflops_per_s"] = round((mf + nm * recompute) / (ms_per_step / 1e3) / 1e12, 2)
+    hb_step = host_bytes_per_step(cfg, T, nm)
     out["host_memory"] = {"bytes_per_step": int(hb_step), "achieved_GBps": round(hb_step / (ms_per_step / 1e3) / 1e9, 1),
                           "adam_alone_GBps": host_adam_probe(mt)}
 
@@ -374,7 +393,7 @@ def main():
         hf = head_gemm_flops(cfg, T)
         for k in ("head_logits", "head_dx", "head_dw"):
             if k in sites and sites[k][0] > 0:
-                out["gemm_tflops"][k] = round(hf * len(stats) / (sites[k][0] / 1e3) / 1e12, 1)
+                out["gemm_tflops"][k] = round(hf * nm * len(stats) / (sites[k][0] / 1e3) / 1e12, 1)
         hb = hbm_bytes(cfg, T)
         out["hbm_kernels_GBps"] = {k: round(hb[k] * sites[k][1] / (sites[k][0] / 1e3) / 1e9, 1)
                                    for k in hb if k in sites and sites[k][0] > 0}

@@ -171,7 +171,12 @@ int mt_init(const mt_shape* shape, const mt_options* opt, void* gpu_arena, uint6
  * Synchronous unless opt->cross_step: all Adam work has finished on return.
  * With cross_step the updates of this step may still be running on return
  * (mt_sync waits for them).  stats_out may be NULL.  Errors: MT_E_INVAL (shape beyond max_batch*max_seq, token or label
- * outside [0, vocab), NULL pointers), MT_E_HIP, MT_E_INTERNAL, MT_E_STATE. */
+ * outside [0, vocab), NULL pointers), MT_E_HIP, MT_E_INTERNAL, MT_E_STATE.
+ * Debugging aid: with the environment variable MT_TRACE=<path> set when the
+ * context is created, every step appends its intervals (compute visits with
+ * their kind and unit, H2D and D2H copies with their bytes; device-clock ms
+ * from the step's first event) to <path> as CSV lines
+ * step,kind,visit,unit,start_ms,end_ms,bytes. */
 int mt_train_step(mt_ctx* ctx, const int32_t* tokens, const int32_t* labels, int32_t batch,
                   int32_t seq, float* loss_out, mt_stats* stats_out);
 

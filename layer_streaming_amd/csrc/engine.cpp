@@ -310,13 +310,55 @@ struct Ctx {
     bool failed = false;
     // fault injection (host side): "pack:<unit>" or "slab:<unit>"
     int fault_pack = -1, fault_slab = -1;
+    std::string trace_path;  // MT_TRACE: append every step's intervals as CSV
+    struct HostRec {
+        const char* what;
+        int unit, aux;
+        Clock::time_point a, b;
+    };
+    std::vector<HostRec> host_recs;  // host-side spans of the step (MT_TRACE)
+    Clock::time_point step_clock0;
+    void host_rec(const char* what, int unit, int aux, Clock::time_point a) {
+        if (trace_path.empty()) return;
+        std::lock_guard<std::mutex> lk(trace_mu);
+        host_recs.push_back({what, unit, aux, a, Clock::now()});
+    }
+    std::mutex trace_mu;
+    // Gradient offload thread.  It takes Backward-Done'd gradient areas in
+    // visit order, acquires a slab, and issues each D2H only once the
+    // previous one has completed: a D2H queued behind another one still in
+    // flight was measured to run at a quarter of the link rate.  The compute
+    // thread never blocks on the offload; it waits only until the request
+    // that last used a gradient area (or, combined, a slot) has been issued,
+    // so that the Buffer-Free event it then waits on is the right one.
+    struct OffReq {
+        int unit, ga, slot, mode;  // slot >= 0: combined W/G slot released after the copy
+        void* gbase;
+        uint64_t bytes;
+    };
+    std::thread off_thread;
+    std::mutex off_mu;
+    std::condition_variable off_cv;
+    std::deque<OffReq> off_q;
+    int64_t off_submitted = 0, off_issued = 0;
+    bool off_stop = false;
+    int off_status = MT_OK;
+    std::string off_error;
+    std::vector<hipEvent_t> off_tev;
+    size_t off_tev_next = 0;
+    std::vector<int64_t> ga_last_req, slot_last_req;
+    int off_prev_slab = -1;
+    void offload_worker();
+    int wait_offload(int64_t seq);
     // timing records
     struct Interval {
         hipEvent_t a, b;
         int kind;  // 0 compute, 1 h2d, 2 d2h
         uint64_t bytes;
+        int visit = -1, unit = -1;  // compute: the visit kind and unit
     };
     std::vector<Interval> intervals;
+    std::vector<Interval> off_intervals;  // gradient copies, filled by the offload thread
     struct SiteRec {
         int site;
         hipEvent_t a, b;
@@ -435,6 +477,7 @@ int Ctx::init(const mt_shape& sh, const mt_options& o, void* arena_, uint64_t by
     plan = plan_arena(lay, opt, arena, &ws);
     pplan = plan_pinned(lay, opt, plan.slot_bytes);
 
+    if (const char* f = getenv("MT_TRACE")) trace_path = f;
     if (const char* f = getenv("MT_FAULT")) {
         if (!strncmp(f, "pack:", 5)) fault_pack = atoi(f + 5);
         if (!strncmp(f, "slab:", 5)) fault_slab = atoi(f + 5);
@@ -532,11 +575,29 @@ int Ctx::init(const mt_shape& sh, const mt_options& o, void* arena_, uint64_t by
     // Gradient areas: tensors never write their padding, so zero it once.
     for (int g = 0; g < plan.n_garea; ++g) HIPC(fill_zero(arena + plan.garea[g], plan.slot_bytes, st_c));
     HIPC(hipStreamSynchronize(st_c));
+    ga_last_req.assign(plan.n_garea, -1);
+    slot_last_req.assign(plan.n_slots, -1);
+    for (int i = 0; i < 256; ++i) {
+        hipEvent_t e;
+        HIPC(hipEventCreate(&e));
+        off_tev.push_back(e);
+    }
     slab_thread = std::thread([this] { slab_worker(); });
+    off_thread = std::thread([this] { offload_worker(); });
     return MT_OK;
 }
 
 Ctx::~Ctx() {
+    // The offload thread first (pending requests dropped; the one in hand may
+    // still need a slab from the slab worker), then the streams, then the
+    // slab worker.
+    {
+        std::lock_guard<std::mutex> lk(off_mu);
+        off_stop = true;
+        off_q.clear();
+    }
+    off_cv.notify_all();
+    if (off_thread.joinable()) off_thread.join();
     if (st_c) hipStreamSynchronize(st_c);
     if (st_w) hipStreamSynchronize(st_w);
     if (st_g) hipStreamSynchronize(st_g);
@@ -546,6 +607,7 @@ Ctx::~Ctx() {
     }
     q_cv.notify_all();
     if (slab_thread.joinable()) slab_thread.join();
+    for (auto e : off_tev) hipEventDestroy(e);
     for (auto* v : {&wready, &slot_free, &bwd_done, &buf_free, &slab_done})
         for (auto& e : *v)
             if (e.e) hipEventDestroy(e.e);
@@ -611,6 +673,7 @@ void Ctx::slab_worker() {
                     adam_unit(*adam_pool, tp, tp.g, j.elems, j.a);
             }
             const double ms = ms_since(t0);
+            host_rec("host_job", j.unit, j.mode * 100 + j.slab, t0);
             std::lock_guard<std::mutex> lk(q_mu);
             adam_ms_acc += ms;
         }
@@ -628,13 +691,81 @@ void Ctx::slab_worker() {
     }
 }
 
+// ------------------------------------------------- gradient offload ----
+void Ctx::offload_worker() {
+    for (;;) {
+        OffReq r;
+        {
+            std::unique_lock<std::mutex> lk(off_mu);
+            off_cv.wait(lk, [&] { return off_stop || !off_q.empty(); });
+            if (off_q.empty()) return;
+            r = off_q.front();
+            off_q.pop_front();
+        }
+        const int k = acquire_slab();
+        hipError_t e = hipSuccess;
+        // One gradient copy in flight at a time (the previous slab's copy
+        // cannot have been re-recorded: only this thread acquires slabs).
+        if (off_prev_slab >= 0) e = hsync(slab_done[off_prev_slab]);
+        off_prev_slab = k;
+        hipEvent_t a = nullptr, b = nullptr;
+        if (e == hipSuccess) e = hipStreamWaitEvent(st_g, bwd_done[r.ga].e, 0);
+        if (e == hipSuccess && timing && off_tev_next + 2 <= off_tev.size()) {
+            a = off_tev[off_tev_next++];
+            b = off_tev[off_tev_next++];
+            e = hipEventRecord(a, st_g);
+        }
+        if (e == hipSuccess) e = hipMemcpyAsync(slabs[k], r.gbase, r.bytes, hipMemcpyDeviceToHost, st_g);
+        if (e == hipSuccess && b) e = hipEventRecord(b, st_g);
+        if (e == hipSuccess) e = rec(slab_done[k], st_g);
+        if (e == hipSuccess) e = rec(buf_free[r.ga], st_g);
+        if (e == hipSuccess && r.slot >= 0) e = rec(slot_free[r.slot], st_g);
+        // The job is queued before the request counts as issued, so a
+        // compute thread that saw every request issued also sees its job.
+        if (e == hipSuccess) {
+            enqueue_job(r.unit, k, r.mode);
+        } else {
+            std::lock_guard<std::mutex> lk(q_mu);
+            free_slabs.push_back(k);
+            free_cv.notify_all();
+        }
+        {
+            std::lock_guard<std::mutex> lk(off_mu);
+            if (a && b && e == hipSuccess) off_intervals.push_back({a, b, 2, r.bytes, -1, k});
+            if (e != hipSuccess && off_status == MT_OK) {
+                off_status = MT_E_HIP;
+                off_error = strfmt("HIP error '%s' offloading the gradient of unit %d", hipGetErrorString(e), r.unit);
+            }
+            ++off_issued;
+        }
+        off_cv.notify_all();
+    }
+}
+
+// Block until offload request `seq` (0-based; < 0: none) has been issued.
+int Ctx::wait_offload(int64_t seq) {
+    std::unique_lock<std::mutex> lk(off_mu);
+    off_cv.wait(lk, [&] { return off_issued > seq || off_status != MT_OK; });
+    if (off_status != MT_OK) {
+        failed = true;
+        set_error(off_error);
+        return off_status;
+    }
+    return MT_OK;
+}
+
 int Ctx::acquire_slab() {
-    std::unique_lock<std::mutex> lk(q_mu);
-    free_cv.wait(lk, [&] { return !free_slabs.empty(); });
-    // Lowest index first keeps the slab order deterministic.
-    auto it = std::min_element(free_slabs.begin(), free_slabs.end());
-    const int k = *it;
-    free_slabs.erase(it);
+    const auto t0 = Clock::now();
+    int k;
+    {
+        std::unique_lock<std::mutex> lk(q_mu);
+        free_cv.wait(lk, [&] { return !free_slabs.empty(); });
+        // Lowest index first keeps the slab order deterministic.
+        auto it = std::min_element(free_slabs.begin(), free_slabs.end());
+        k = *it;
+        free_slabs.erase(it);
+    }
+    host_rec("host_slab_wait", -1, k, t0);
     return k;
 }
 
@@ -921,16 +1052,21 @@ int Ctx::stream_unit(int unit, int slot) {
     if (el != MT_OK) return el;
     const int wa = wait_adam(unit);
     if (wa != MT_OK) return wa;
+    const int wo = wait_offload(slot_last_req[slot]);  // combined slots: released by the offload
+    if (wo != MT_OK) return wo;
     HIPC(wait(st_w, slot_free[slot]));
     if (store_pinned || wblock) {
         HIPC(h2d(arena + plan.wslot[slot], src, bytes, st_w));
     } else {
         const int p = staging_ptr;
         staging_ptr ^= 1;
+        const auto tw = Clock::now();
         HIPC(hsync(staging_free[p]));
+        host_rec("host_staging_wait", unit, p, tw);
         const auto t0 = Clock::now();
         parallel_copy(*pack_pool, staging[p], src, int64_t(bytes));
         pack_ms += ms_since(t0);
+        host_rec("host_pack", unit, p, t0);
         HIPC(h2d(arena + plan.wslot[slot], staging[p], bytes, st_w));
         HIPC(rec(staging_free[p], st_w));
     }
@@ -955,6 +1091,11 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
             MT_FAIL(MT_E_INVAL, "token or label at row %lld outside [0, %d)", (long long)t, V);
 
     const auto t_start = Clock::now();
+    step_clock0 = t_start;
+    {
+        std::lock_guard<std::mutex> lk(trace_mu);
+        host_recs.clear();
+    }
     // Adam rewrote every unit's weights after the last step: no slot holds
     // current weights any more.
     slot_unit.assign(plan.n_slots, -1);
@@ -962,6 +1103,12 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
     tev_next = 0;
     intervals.clear();
     site_recs.clear();
+    {
+        // The offload thread is idle between steps: every request was issued.
+        std::lock_guard<std::mutex> lk(off_mu);
+        off_tev_next = 0;
+        off_intervals.clear();
+    }
     {
         std::lock_guard<std::mutex> lk(q_mu);
         adam_ms_acc = 0.0;
@@ -1079,6 +1226,16 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
             Ev& wr = wready[slot];
             HIPC(rec(wr, st_w));
             HIPC(wait(st_c, wr));
+            // Head and backward write a gradient area: wait until its last
+            // offload is done (Buffer-Free) before the visit's clock starts.
+            int ga = 0;
+            if (kind == V_HEAD || kind == V_BWD) {
+                ga = combined ? slot : gnext;
+                if (!combined) gnext ^= 1;
+                const int wo = wait_offload(ga_last_req[ga]);
+                if (wo != MT_OK) return wo;
+                HIPC(wait(st_c, buf_free[ga]));
+            }
             hipEvent_t va = next_tev(), vz = next_tev();
             HIPC(hipEventRecord(va, st_c));
             if (kind == V_FWD) {
@@ -1088,7 +1245,7 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
                 if (opt.ckpt_on_host) HIPC(wait(st_c, ckpt_done[(unit + 1) & 1]));
                 HIPC(fwd_layer(bind_layer(lay, wbase), x, y, B, S, true));
                 HIPC(hipEventRecord(vz, st_c));
-                intervals.push_back({va, vz, 0, 0});
+                intervals.push_back({va, vz, 0, 0, kind, unit});
                 HIPC(rec(slot_free[slot], st_c));
                 if (opt.ckpt_on_host) {
                     // Checkpoint the layer input on the gradient stream (idle in forward).
@@ -1110,14 +1267,11 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
                 // Rebuild the next layer's input inside the block's bank.
                 HIPC(fwd_layer(bind_layer(lay, wbase), xb[vs.pos], xb[vs.pos + 1], B, S, true));
                 HIPC(hipEventRecord(vz, st_c));
-                intervals.push_back({va, vz, 0, 0});
+                intervals.push_back({va, vz, 0, 0, kind, unit});
                 HIPC(rec(slot_free[slot], st_c));
                 continue;
             }
             // Head or backward: gradients go to a gradient area, then to a slab.
-            const int ga = combined ? slot : gnext;
-            if (!combined) gnext ^= 1;
-            HIPC(wait(st_c, buf_free[ga]));
             void* gbase = arena + plan.garea[ga];
             if (kind == V_HEAD) {
                 const uint16_t* xL = opt.ckpt_on_host ? ws.x[L & 1] : ws.ckpt_dev + uint64_t(L) * ws.maxT * d;
@@ -1133,21 +1287,26 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
                 if (opt.ckpt_on_host && vs.pos == 0) HIPC(rec(xc_free[bank], st_c));
             }
             HIPC(hipEventRecord(vz, st_c));
-            intervals.push_back({va, vz, 0, 0});
+            intervals.push_back({va, vz, 0, 0, kind, unit});
             if (!combined) HIPC(rec(slot_free[slot], st_c));
             HIPC(rec(bwd_done[ga], st_c));
             // Gradient offload: Backward-Done -> free slab -> Buffer-Free.
-            const int k = acquire_slab();
-            HIPC(wait(st_g, bwd_done[ga]));
-            HIPC(d2h(slabs[k], gbase, uint64_t(lay.units[unit].elems) * 2, st_g));
-            HIPC(rec(slab_done[k], st_g));
-            HIPC(rec(buf_free[ga], st_g));
-            if (combined) HIPC(rec(slot_free[slot], st_g));
-            enqueue_job(unit, k, mode);
+            {
+                std::lock_guard<std::mutex> lk(off_mu);
+                off_q.push_back({unit, ga, combined ? slot : -1, mode, gbase, uint64_t(lay.units[unit].elems) * 2});
+                ga_last_req[ga] = off_submitted;
+                if (combined) slot_last_req[slot] = off_submitted;
+                ++off_submitted;
+            }
+            off_cv.notify_all();
             if (kind == V_HEAD) {
                 ph.head = next_tev();
                 HIPC(hipEventRecord(ph.head, st_c));
             }
+        }
+        {
+            const int wo = wait_offload(off_submitted - 1);  // every gradient copy issued
+            if (wo != MT_OK) return wo;
         }
         if (mb + 1 == n_micro) {
             std::lock_guard<std::mutex> lk(q_mu);
@@ -1232,9 +1391,37 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
     HIPC(hipStreamSynchronize(st_w));
     HIPC(hipStreamSynchronize(st_g));
     if (jr != MT_OK) return jr;
+    {
+        std::lock_guard<std::mutex> lk(off_mu);
+        intervals.insert(intervals.end(), off_intervals.begin(), off_intervals.end());
+    }
     *loss_out = float(loss_sum / n_micro);  // mean over every token of the step
     ++step;
     const double t_total = ms_since(t_start);
+    if (!trace_path.empty()) {
+        // Debugging aid: every interval of the step on the device clock,
+        // relative to the step's first event.
+        if (FILE* f = fopen(trace_path.c_str(), "a")) {
+            for (const Interval& iv : intervals) {
+                float a = 0.f, b = 0.f;
+                hipEventElapsedTime(&a, t_base, iv.a);
+                hipEventElapsedTime(&b, t_base, iv.b);
+                static const char* names[] = {"fwd", "head", "refwd", "bwd"};
+                fprintf(f, "%lld,%s,%s,%d,%.4f,%.4f,%llu\n", (long long)step,
+                        iv.kind == 0 ? "compute" : iv.kind == 1 ? "h2d" : "d2h",
+                        iv.kind == 0 ? names[iv.visit] : "-", iv.unit, a, b, (unsigned long long)iv.bytes);
+            }
+            // Host spans on the host clock from the step's start (the device
+            // clock starts within microseconds of it: the GPU is idle then).
+            std::lock_guard<std::mutex> lk(trace_mu);
+            for (const HostRec& h : host_recs) {
+                const double a = std::chrono::duration<double, std::milli>(h.a - step_clock0).count();
+                const double b = std::chrono::duration<double, std::milli>(h.b - step_clock0).count();
+                fprintf(f, "%lld,%s,%d,%d,%.4f,%.4f,0\n", (long long)step, h.what, h.aux, h.unit, a, b);
+            }
+            fclose(f);
+        }
+    }
 
     if (stats) {
         memset(stats, 0, sizeof(*stats));
