@@ -164,15 +164,17 @@ def ablations(torch, mt, shape, cfg, args, tokens, labels, base_value):
     for name, kw in (("one_weight_slot", dict(n_weight_slots=1)), ("one_grad_slab", dict(n_grad_slabs=1)),
                      ("combined_slots", dict(slot_mode=1))):
         opt = mt.default_options(max_batch=B, max_seq=S, host_threads=args.host_threads, seed=synth.SEED_WEIGHTS,
-                                 **kw)
+                                 cross_step=args.cross_step, pin_weights=args.pin_weights, **kw)
         arena_bytes, _, _ = mt.workspace_bytes(shape, opt)
         arena = torch.empty(arena_bytes, dtype=torch.uint8, device="cuda")
         ctx = mt.Context(shape, opt, arena.data_ptr(), arena_bytes)
         ctx.train_step(tokens, labels)
+        ctx.sync()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(2):
             ctx.train_step(tokens, labels)
+        ctx.sync()
         torch.cuda.synchronize()
         v = 2 * B * S / (time.perf_counter() - t0)
         res[name] = {"value": round(v, 1), "vs_default": round(v / base_value, 3)}
@@ -259,7 +261,8 @@ def main():
     ap.add_argument("--slot-mode", type=int, default=0)
     ap.add_argument("--resident", type=int, default=0)
     ap.add_argument("--pin-store", type=int, default=0)
-    ap.add_argument("--pin-weights", type=int, default=0)
+    ap.add_argument("--pin-weights", type=int, default=1,
+                    help="1 (default): W regions in one page-locked block, streamed with no pack copy")
     ap.add_argument("--ablations", action="store_true",
                     help="after the timed run, time 2 steps each with one weight slot, one gradient slab and "
                          "combined W/G slots (the pages' ablations), reported as tokens/s and ratio")
@@ -270,9 +273,9 @@ def main():
                     help="let the library create its three streams instead of passing torch's")
     ap.add_argument("--micro", type=int, default=1,
                     help="micro-batches of batch x seq per optimizer step (gradient accumulation on the host)")
-    ap.add_argument("--cross-step", type=int, default=0,
-                    help="1: the next step's forward overlaps this step's Adam tail (same results); on a host "
-                         "whose memory bandwidth the Adam already fills this is slower, so it is off by default")
+    ap.add_argument("--cross-step", type=int, default=1,
+                    help="1 (default): the next step's forward overlaps this step's Adam tail (same results); "
+                         "0: every step synchronous")
     args = ap.parse_args()
     if args.micro < 1 or (args.micro > 1 and (args.ablations or args.traffic_probe)):
         ap.error("--micro must be >= 1, and 1 with --ablations or --traffic-probe")

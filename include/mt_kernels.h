@@ -87,6 +87,10 @@ int mt_k_ce(const void* logits, const void* labels, void* loss_rows, void* dlogi
             float inv_T, void* stream);
 int mt_k_mean(const void* x, void* out, int32_t n, void* stream);
 int mt_k_f32_to_bf16(const void* x, void* y, int64_t n, void* stream);
+/* Transpose of an R x C matrix of 16-bit elements: dst[c*ldd + r] = src[r*lds + c]
+ * (the backward products take both operands reduction-contiguous).  Errors:
+ * MT_E_INVAL for negative sizes, lds < C or ldd < R. */
+int mt_k_transpose16(const void* src, int64_t lds, void* dst, int64_t ldd, int32_t R, int32_t C, void* stream);
 
 /* Host (CPU) entries, no GPU needed. */
 /* The production host Adam over n elements of caller arrays: G <- gsrc,

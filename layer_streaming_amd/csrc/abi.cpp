@@ -145,6 +145,10 @@ int mt_k_mean(const void* x, void* out, int32_t n, void* stream) {
     return kst(mt::mean_reduce(F32(x), F32(out), n, S_(stream)), "mean_reduce");
 }
 
+int mt_k_transpose16(const void* src, int64_t lds, void* dst, int64_t ldd, int32_t R, int32_t C, void* stream) {
+    return kst(mt::transpose16(U16(src), lds, U16(dst), ldd, R, C, S_(stream)), "transpose16");
+}
+
 int mt_k_f32_to_bf16(const void* x, void* y, int64_t n, void* stream) {
     return kst(mt::f32_to_bf16(F32(x), U16(y), n, S_(stream)), "f32_to_bf16");
 }

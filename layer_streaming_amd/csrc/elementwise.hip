@@ -349,6 +349,50 @@ __global__ void f32_to_bf16_k(const float4* __restrict__ x, uint2* __restrict__ 
     y[i] = make_uint2(pack2(v.x, v.y), pack2(v.z, v.w));
 }
 
+// 16-bit element e (0..7, compile-time after unrolling) of a uint4.
+__device__ __forceinline__ uint32_t h16of(const uint4& v, int e) {
+    const uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
+    return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
+}
+
+// dst[c][r] = src[r][c] for bf16 (any 16-bit) matrices.  One wave per
+// 64 x 64 tile; lane (tx, ty) = (lane % 8, lane / 8) moves the 8 x 8 block at
+// rows 8 ty.., columns 8 tx..: eight 16-byte row loads, a transpose in
+// registers, eight 16-byte row stores.  Eight lanes cover 128 contiguous
+// bytes of a source row on load and of a destination row on store.  VEC: rows
+// of both matrices start 16-byte aligned; blocks that cross the matrix edge,
+// and every block when !VEC, go element by element.
+template <bool VEC>
+__global__ __launch_bounds__(256) void transpose16_k(const uint16_t* __restrict__ src, int64_t lds,
+                                                     uint16_t* __restrict__ dst, int64_t ldd, int R, int C,
+                                                     int tiles_c, int64_t n_tiles) {
+    const int lane = threadIdx.x & 63;
+    const int64_t tile = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (tile >= n_tiles) return;
+    const int r = int(tile / tiles_c) * 64 + 8 * (lane >> 3);
+    const int c = int(tile % tiles_c) * 64 + 8 * (lane & 7);
+    if (r >= R || c >= C) return;
+    if (VEC && r + 8 <= R && c + 8 <= C) {
+        uint4 in[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) in[i] = *reinterpret_cast<const uint4*>(src + int64_t(r + i) * lds + c);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            uint32_t w[4];
+#pragma unroll
+            for (int i = 0; i < 8; i += 2) {
+                const uint32_t a = h16of(in[i], j), b = h16of(in[i + 1], j);
+                w[i >> 1] = a | (b << 16);
+            }
+            *reinterpret_cast<uint4*>(dst + int64_t(c + j) * ldd + r) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+        return;
+    }
+    const int nr = min(8, R - r), nc = min(8, C - c);
+    for (int i = 0; i < nr; ++i)
+        for (int j = 0; j < nc; ++j) dst[int64_t(c + j) * ldd + r + i] = src[int64_t(r + i) * lds + c + j];
+}
+
 __global__ void fill_zero_k(uint4* __restrict__ p, int64_t n16) {
     const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i < n16) p[i] = make_uint4(0, 0, 0, 0);
@@ -487,6 +531,21 @@ hipError_t f32_to_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t s) {
     if (n == 0) return hipSuccess;
     f32_to_bf16_k<<<blocks(n / 4, 256), 256, 0, s>>>(reinterpret_cast<const float4*>(x),
                                                      reinterpret_cast<uint2*>(y), n / 4);
+    return hipGetLastError();
+}
+
+hipError_t transpose16(const uint16_t* src, int64_t lds, uint16_t* dst, int64_t ldd, int R, int C, hipStream_t s) {
+    if (R < 0 || C < 0 || !src || !dst || lds < C || ldd < R) return hipErrorInvalidValue;
+    if (R == 0 || C == 0) return hipSuccess;
+    const int tiles_c = (C + 63) / 64;
+    const int64_t n_tiles = int64_t((R + 63) / 64) * tiles_c;
+    const int64_t nb = (n_tiles + 3) / 4;
+    if (nb > INT32_MAX) return hipErrorInvalidValue;
+    const bool vec = (lds % 8) == 0 && (ldd % 8) == 0 && al16(src) && al16(dst);
+    if (vec)
+        transpose16_k<true><<<unsigned(nb), 256, 0, s>>>(src, lds, dst, ldd, R, C, tiles_c, n_tiles);
+    else
+        transpose16_k<false><<<unsigned(nb), 256, 0, s>>>(src, lds, dst, ldd, R, C, tiles_c, n_tiles);
     return hipGetLastError();
 }
 

@@ -140,6 +140,15 @@ void plan_workspace(const Layout& lay, const mt_options& o, Carver& cv, Workspac
     ws.dy[1] = cv.take<uint16_t>(td);
     ws.dn = cv.take<uint16_t>(td);
     ws.dh1 = cv.take<uint16_t>(td);
+    {
+        const uint64_t T8 = uint64_t((T + 7) & ~int64_t(7));  // token rows padded for the dW products
+        const uint64_t ta = uint64_t(std::max({d, 2 * F, nqkv})) * T8;
+        const uint64_t tb = std::max({uint64_t(F) * std::max<uint64_t>(T8, uint64_t(2 * d)),
+                                      uint64_t(std::max(nq, nqkv)) * std::max<uint64_t>(T8, uint64_t(d)),
+                                      uint64_t(d) * T8});
+        ws.tA = cv.take<uint16_t>(ta * 2);
+        ws.tB = cv.take<uint16_t>(tb * 2);
+    }
     ws.rstd1 = cv.take<float>(uint64_t(T) * 4);
     ws.rstd2 = cv.take<float>(uint64_t(T) * 4);
     ws.lse = cv.take<float>(uint64_t(T) * sh.n_heads * 4);
@@ -421,6 +430,10 @@ struct Ctx {
                          uint16_t* dx, int B, int S);
     hipError_t head(const HeadView& w, const HeadView& g, const uint16_t* xL, uint16_t* dy, int B, int S,
                     float inv_tokens);
+    hipError_t gemm_nn_t(const uint16_t* A, int64_t lda, const uint16_t* Bm, int64_t ldb, uint16_t* C, int64_t ldc,
+                         int M, int N, int K);
+    hipError_t gemm_tn_t(const uint16_t* A, int64_t lda, const uint16_t* Bm, int64_t ldb, uint16_t* C, int64_t ldc,
+                         int M, int N, int K);
     hipError_t ensure_rope(int S);
     int pick_slot(int unit, bool* need_stream);
     int stream_unit(int unit, int slot);
@@ -933,36 +946,21 @@ hipError_t Ctx::bwd_layer(const LayerView& w, const LayerView& g, const uint16_t
     const int nq = sh.n_heads * sh.head_dim;
     const int nqkv = (sh.n_heads + 2 * sh.n_kv_heads) * sh.head_dim;
     hipStream_t s = st_c;
+    // Every backward product runs as an NT product on operands made
+    // reduction-contiguous by a transpose (HBM-bound, a few percent of the
+    // product's time); dX = dY W and dW = dY^T X.
     // MLP
-    HIPR(site(S_GEMM_DOWN_DX, [&] {
-        GemmArgs a{dy, d, w.wd, F, ws.dm, F, nullptr, 0, nullptr, 0, T, F, d};
-        return gemm(GEMM_NN, EPI_BF16, a, s);
-    }));
-    HIPR(site(S_GEMM_DOWN_DW, [&] {
-        GemmArgs a{dy, d, ws.m, F, g.wd, F, nullptr, 0, nullptr, 0, d, F, T};
-        return gemm(GEMM_TN, EPI_BF16, a, s);
-    }));
+    HIPR(site(S_GEMM_DOWN_DX, [&] { return gemm_nn_t(dy, d, w.wd, F, ws.dm, F, T, F, d); }));
+    HIPR(site(S_GEMM_DOWN_DW, [&] { return gemm_tn_t(dy, d, ws.m, F, g.wd, F, d, F, T); }));
     HIPR(site(S_SWIGLU_BWD, [&] { return swiglu_bwd(ws.dm, ws.gu, ws.dgu, T, F, s); }));
-    HIPR(site(S_GEMM_GATEUP_DX, [&] {
-        GemmArgs a{ws.dgu, 2 * F, w.wgu, d, ws.dn, d, nullptr, 0, nullptr, 0, T, d, 2 * F};
-        return gemm(GEMM_NN, EPI_BF16, a, s);
-    }));
-    HIPR(site(S_GEMM_GATEUP_DW, [&] {
-        GemmArgs a{ws.dgu, 2 * F, ws.n2, d, g.wgu, d, nullptr, 0, nullptr, 0, 2 * F, d, T};
-        return gemm(GEMM_TN, EPI_BF16, a, s);
-    }));
+    HIPR(site(S_GEMM_GATEUP_DX, [&] { return gemm_nn_t(ws.dgu, 2 * F, w.wgu, d, ws.dn, d, T, d, 2 * F); }));
+    HIPR(site(S_GEMM_GATEUP_DW, [&] { return gemm_tn_t(ws.dgu, 2 * F, ws.n2, d, g.wgu, d, 2 * F, d, T); }));
     HIPR(site(S_RMS2_BWD, [&] {
         return rmsnorm_bwd(ws.dn, ws.h1, true, w.g2, ws.rstd2, dy, ws.dh1, g.g2, ws.partial, T, d, s);
     }));
     // attention
-    HIPR(site(S_GEMM_O_DX, [&] {
-        GemmArgs a{ws.dh1, d, w.wo, nq, ws.dout, nq, nullptr, 0, nullptr, 0, T, nq, d};
-        return gemm(GEMM_NN, EPI_BF16, a, s);
-    }));
-    HIPR(site(S_GEMM_O_DW, [&] {
-        GemmArgs a{ws.dh1, d, ws.o, nq, g.wo, nq, nullptr, 0, nullptr, 0, d, nq, T};
-        return gemm(GEMM_TN, EPI_BF16, a, s);
-    }));
+    HIPR(site(S_GEMM_O_DX, [&] { return gemm_nn_t(ws.dh1, d, w.wo, nq, ws.dout, nq, T, nq, d); }));
+    HIPR(site(S_GEMM_O_DW, [&] { return gemm_tn_t(ws.dh1, d, ws.o, nq, g.wo, nq, d, nq, T); }));
     HIPR(site(S_ATTN_BWD, [&] {
         AttnBwdArgs a{ws.qkv, nqkv, ws.o, ws.dout, nq, ws.lse, ws.dsum, ws.dqkv, nqkv,
                       B, S, sh.n_heads, sh.n_kv_heads, sh.head_dim};
@@ -971,18 +969,36 @@ hipError_t Ctx::bwd_layer(const LayerView& w, const LayerView& g, const uint16_t
     HIPR(site(S_ROPE_BWD, [&] {
         return rope_apply(ws.dqkv, nqkv, ws.rope_tab, T, S, sh.n_heads + sh.n_kv_heads, sh.head_dim, -1, s);
     }));
-    HIPR(site(S_GEMM_QKV_DX, [&] {
-        GemmArgs a{ws.dqkv, nqkv, w.wqkv, d, ws.dn, d, nullptr, 0, nullptr, 0, T, d, nqkv};
-        return gemm(GEMM_NN, EPI_BF16, a, s);
-    }));
-    HIPR(site(S_GEMM_QKV_DW, [&] {
-        GemmArgs a{ws.dqkv, nqkv, ws.n1, d, g.wqkv, d, nullptr, 0, nullptr, 0, nqkv, d, T};
-        return gemm(GEMM_TN, EPI_BF16, a, s);
-    }));
+    HIPR(site(S_GEMM_QKV_DX, [&] { return gemm_nn_t(ws.dqkv, nqkv, w.wqkv, d, ws.dn, d, T, d, nqkv); }));
+    HIPR(site(S_GEMM_QKV_DW, [&] { return gemm_tn_t(ws.dqkv, nqkv, ws.n1, d, g.wqkv, d, nqkv, d, T); }));
     HIPR(site(S_RMS1_BWD, [&] {
         return rmsnorm_bwd(ws.dn, x, false, w.g1, ws.rstd1, ws.dh1, dx, g.g1, ws.partial, T, d, s);
     }));
     return hipSuccess;
+}
+
+// C[M x N] = A[M x K] B[K x N] (B row-major): B transposed into tB, then NT.
+hipError_t Ctx::gemm_nn_t(const uint16_t* A, int64_t lda, const uint16_t* Bm, int64_t ldb, uint16_t* C, int64_t ldc,
+                          int M, int N, int K) {
+    HIPR(transpose16(Bm, ldb, ws.tB, K, K, N, st_c));
+    GemmArgs a{A, lda, ws.tB, K, C, ldc, nullptr, 0, nullptr, 0, M, N, K};
+    return gemm(GEMM_NT, EPI_BF16, a, st_c);
+}
+
+// C[M x N] = A^T B with A stored [K x M] and B [K x N]: both transposed, then
+// NT.  K (the tokens) is padded to a multiple of 8 with zero columns, which
+// add nothing.
+hipError_t Ctx::gemm_tn_t(const uint16_t* A, int64_t lda, const uint16_t* Bm, int64_t ldb, uint16_t* C, int64_t ldc,
+                          int M, int N, int K) {
+    const int Kp = (K + 7) & ~7;
+    if (Kp != K) {
+        HIPR(fill_zero(ws.tA, int64_t(M) * Kp * 2, st_c));
+        HIPR(fill_zero(ws.tB, int64_t(N) * Kp * 2, st_c));
+    }
+    HIPR(transpose16(A, lda, ws.tA, Kp, K, M, st_c));
+    HIPR(transpose16(Bm, ldb, ws.tB, Kp, K, N, st_c));
+    GemmArgs a{ws.tA, Kp, ws.tB, Kp, C, ldc, nullptr, 0, nullptr, 0, M, N, Kp};
+    return gemm(GEMM_NT, EPI_BF16, a, st_c);
 }
 
 // LM head, forward and backward fused over token chunks; writes dy (the

@@ -51,6 +51,8 @@ struct Workspace {
     float* qkv32;
     float *rstd1, *rstd2, *lse;
     uint16_t *dy[2], *dm, *dgu, *dn, *dh1, *dout, *dqkv;
+    // reduction-contiguous copies of the backward products' operands
+    uint16_t *tA, *tB;
     float *dsum, *partial;
     float2* rope_tab;
     int32_t* labels;

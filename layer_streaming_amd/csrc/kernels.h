@@ -105,5 +105,7 @@ hipError_t mean_reduce(const float* x, float* out, int n, hipStream_t s);
 // --------------------------------------------------------------- misc -----
 hipError_t f32_to_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t s);
 hipError_t fill_zero(void* p, int64_t bytes, hipStream_t s);
+// dst[c * ldd + r] = src[r * lds + c] for an R x C matrix of 16-bit elements.
+hipError_t transpose16(const uint16_t* src, int64_t lds, uint16_t* dst, int64_t ldd, int R, int C, hipStream_t s);
 
 }  // namespace mt

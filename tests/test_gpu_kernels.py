@@ -336,3 +336,23 @@ def test_f32_to_bf16_round_to_nearest_even():
     keep = ~nan & ~sub
     assert np.array_equal(got[keep], ref[keep]), int(np.sum(got[keep] != ref[keep]))
     assert np.all(np.isnan((got[nan].astype(np.uint32) << 16).view(np.float32)))
+
+
+@pytest.mark.parametrize("R,C,pad_s,pad_d", [(64, 64, 0, 0), (130, 77, 3, 5), (1000, 520, 8, 0),
+                                              (1, 1, 0, 0), (8192, 200, 0, 0), (200, 8192, 0, 8), (71, 64, 0, 1)])
+def test_transpose16_bit_exact(R, C, pad_s, pad_d):
+    """The transpose feeding the backward products moves bit patterns: exact,
+    including ragged edges (vector interior, element-wise border) and leading
+    dimensions that rule the vector path out; the padding is left alone."""
+    log(f"transpose16 {R}x{C} pad {pad_s},{pad_d}")
+    rng = np.random.default_rng(R * 7 + C)
+    lds, ldd = C + pad_s, R + pad_d
+    src = rng.integers(0, 1 << 16, size=(R, lds), dtype=np.uint16)
+    dsrc = torch.from_numpy(src.view(np.int16)).cuda()
+    ddst = torch.full((C, ldd), 0x1234, dtype=torch.int16, device="cuda")
+    mt.check(mt.lib.mt_k_transpose16(dsrc.data_ptr(), lds, ddst.data_ptr(), ldd, R, C, _stream()))
+    _sync()
+    got = ddst.cpu().numpy().view(np.uint16)
+    assert np.array_equal(got[:, :R], src[:, :C].T)
+    assert np.all(got[:, R:] == 0x1234)
+    assert mt.lib.mt_k_transpose16(dsrc.data_ptr(), lds, ddst.data_ptr(), R - 1, R, C, _stream()) == mt.MT_E_INVAL
