@@ -137,13 +137,26 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_k(const uint4* __restrict__ d
     }
 }
 
-__global__ void dgamma_reduce_k(const float* __restrict__ partial, int nrows, int d,
-                                uint16_t* __restrict__ dgamma) {
-    const int c = blockIdx.x * blockDim.x + threadIdx.x;
-    if (c >= d) return;
+// 64 columns per block, 16 waves: wave w sums partial rows w, w+16, ... of
+// its lane's column (coalesced 256-byte row segments), then wave 0 adds the
+// 16 sums in wave order: a fixed order, so the result is deterministic.
+__global__ __launch_bounds__(1024) void dgamma_reduce_k(const float* __restrict__ partial, int nrows, int d,
+                                                        uint16_t* __restrict__ dgamma) {
+    __shared__ float red[16][64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int c = blockIdx.x * 64 + lane;
     float s = 0.f;
-    for (int r = 0; r < nrows; ++r) s += partial[int64_t(r) * d + c];
-    dgamma[c] = f2bf(s);
+    if (c < d)
+#pragma unroll 8
+        for (int r = w; r < nrows; r += 16) s += partial[int64_t(r) * d + c];
+    red[w][lane] = s;
+    __syncthreads();
+    if (w == 0 && c < d) {
+        float t = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) t += red[i][lane];
+        dgamma[c] = f2bf(t);
+    }
 }
 
 // ---------------------------------------------------------------- RoPE ----
@@ -474,7 +487,7 @@ hipError_t rmsnorm_bwd(const uint16_t* dn, const void* x, bool x_f32, const uint
                                      partial, T, d, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dgamma_reduce_k<<<blocks(d, 256), 256, 0, s>>>(partial, int(nb) * 4, d, dgamma);
+    dgamma_reduce_k<<<(d + 63) / 64, 1024, 0, s>>>(partial, int(nb) * 4, d, dgamma);
     return hipGetLastError();
 }
 
