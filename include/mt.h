@@ -107,6 +107,15 @@ typedef struct mt_options {
                                     (2 B/param), so StreamIn copies straight from it with no pack;
                                     G and the optimizer state stay in the pageable tiles.  0
                                     (default): W inside each pageable tile, packed into staging */
+    int32_t head_vocab_chunk;    /* the LM head streamed in chunks of E_out rows, so the weight
+                                    slots are sized to the largest decoder layer instead of the
+                                    head: a forward pass over the chunks keeps a running
+                                    logsumexp per token, a backward pass (chunks in reverse order)
+                                    recomputes each chunk's logits and forms its gradients; each
+                                    chunk's gradient is offloaded and updated on its own ([Hotdry]
+                                    staging buffers sized to the largest layer).  0 (default): the
+                                    head is one unit; -1: rows per chunk chosen so a chunk fits the
+                                    largest decoder layer's slot; k > 0 (a multiple of 8): k rows */
     uint64_t slot_bytes_override;      /* 0: largest unit's weight bytes */
     uint64_t workspace_bytes_override; /* 0: computed from max_batch*max_seq */
     float lr, beta1, beta2, adam_eps;  /* 1e-4, 0.9, 0.999, 1e-8 */

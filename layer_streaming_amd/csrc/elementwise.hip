@@ -342,6 +342,85 @@ __global__ __launch_bounds__(256) void ce_k(const float* __restrict__ logits,
     }
 }
 
+// Cross-entropy over vocabulary chunks (the LM head streamed in row chunks
+// of E_out).  Forward, per row: the chunk's (max, sum of exp) merged into the
+// running (m, l) of the chunks before it, and the label's logit picked up by
+// the chunk that holds it.  After the last chunk, LSE = m + log l and the
+// row's loss LSE - z.  Backward: dlogits = (exp(x - LSE) - onehot) / T.
+__global__ __launch_bounds__(256) void ce_chunk_fwd_k(const float* __restrict__ logits,
+                                                      const int32_t* __restrict__ labels, int Vc, int v0,
+                                                      int first, float* __restrict__ m, float* __restrict__ l,
+                                                      float* __restrict__ z) {
+    const int row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const float* x = logits + int64_t(row) * Vc;
+    const float4* x4 = reinterpret_cast<const float4*>(x);
+    const int nv4 = Vc >> 2;
+    float mx = -INFINITY, sm = 0.f;
+    for (int c = tid; c < nv4; c += 256) {
+        const float4 v = x4[c];
+        const float vm = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
+        if (vm > mx) { sm *= expf(mx - vm); mx = vm; }
+        sm += expf(v.x - mx) + expf(v.y - mx) + expf(v.z - mx) + expf(v.w - mx);
+    }
+    __shared__ float smx[256], ssm[256];
+    smx[tid] = mx;
+    ssm[tid] = sm;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if (tid < o) {
+            const float m1 = smx[tid], m2 = smx[tid + o];
+            const float mm = fmaxf(m1, m2);
+            const float s = (m1 == -INFINITY ? 0.f : ssm[tid] * expf(m1 - mm)) +
+                            (m2 == -INFINITY ? 0.f : ssm[tid + o] * expf(m2 - mm));
+            smx[tid] = mm;
+            ssm[tid] = s;
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        float M = first ? -INFINITY : m[row], L = first ? 0.f : l[row];
+        const float cm = smx[0], cs = ssm[0];
+        const float nm = fmaxf(M, cm);
+        L = (M == -INFINITY ? 0.f : L * expf(M - nm)) + (cm == -INFINITY ? 0.f : cs * expf(cm - nm));
+        m[row] = nm;
+        l[row] = L;
+        const int lab = labels[row] - v0;
+        if (lab >= 0 && lab < Vc) z[row] = x[lab];
+    }
+}
+
+__global__ void ce_chunk_final_k(const float* __restrict__ m, const float* __restrict__ l,
+                                 const float* __restrict__ z, float* __restrict__ lse,
+                                 float* __restrict__ loss_rows, int T) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= T) return;
+    const float s = m[t] + logf(l[t]);
+    lse[t] = s;
+    loss_rows[t] = s - z[t];
+}
+
+__global__ __launch_bounds__(256) void ce_chunk_bwd_k(const float* __restrict__ logits,
+                                                      const int32_t* __restrict__ labels,
+                                                      const float* __restrict__ lse, int Vc, int v0,
+                                                      uint16_t* __restrict__ dlogits, float inv_T) {
+    const int row = blockIdx.x;
+    const float4* x4 = reinterpret_cast<const float4*>(logits + int64_t(row) * Vc);
+    uint2* d2 = reinterpret_cast<uint2*>(dlogits + int64_t(row) * Vc);
+    const float s = lse[row];
+    const int lab = labels[row] - v0;
+    for (int c = threadIdx.x; c < (Vc >> 2); c += 256) {
+        const float4 v = x4[c];
+        float p0 = expf(v.x - s), p1 = expf(v.y - s), p2 = expf(v.z - s), p3 = expf(v.w - s);
+        const int b = c * 4;
+        if (lab == b) p0 -= 1.f;
+        if (lab == b + 1) p1 -= 1.f;
+        if (lab == b + 2) p2 -= 1.f;
+        if (lab == b + 3) p3 -= 1.f;
+        d2[c] = make_uint2(pack2(p0 * inv_T, p1 * inv_T), pack2(p2 * inv_T, p3 * inv_T));
+    }
+}
+
 __global__ __launch_bounds__(256) void mean_reduce_k(const float* __restrict__ x, float* out, int n) {
     __shared__ float sh[256];
     float s = 0.f;
@@ -544,6 +623,30 @@ hipError_t f32_to_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t s) {
     if (n == 0) return hipSuccess;
     f32_to_bf16_k<<<blocks(n / 4, 256), 256, 0, s>>>(reinterpret_cast<const float4*>(x),
                                                      reinterpret_cast<uint2*>(y), n / 4);
+    return hipGetLastError();
+}
+
+hipError_t ce_chunk_fwd(const float* logits, const int32_t* labels, int rows, int Vc, int v0, bool first, float* m,
+                        float* l, float* z, hipStream_t s) {
+    if (rows < 0 || Vc <= 0 || (Vc & 7) || !al16(logits)) return hipErrorInvalidValue;
+    if (rows == 0) return hipSuccess;
+    ce_chunk_fwd_k<<<rows, 256, 0, s>>>(logits, labels, Vc, v0, first ? 1 : 0, m, l, z);
+    return hipGetLastError();
+}
+
+hipError_t ce_chunk_final(const float* m, const float* l, const float* z, float* lse, float* loss_rows, int T,
+                          hipStream_t s) {
+    if (T < 0) return hipErrorInvalidValue;
+    if (T == 0) return hipSuccess;
+    ce_chunk_final_k<<<blocks(T, 256), 256, 0, s>>>(m, l, z, lse, loss_rows, T);
+    return hipGetLastError();
+}
+
+hipError_t ce_chunk_bwd(const float* logits, const int32_t* labels, const float* lse, int rows, int Vc, int v0,
+                        uint16_t* dlogits, float inv_T, hipStream_t s) {
+    if (rows < 0 || Vc <= 0 || (Vc & 7) || !al16(logits) || !al16(dlogits)) return hipErrorInvalidValue;
+    if (rows == 0) return hipSuccess;
+    ce_chunk_bwd_k<<<rows, 256, 0, s>>>(logits, labels, lse, Vc, v0, dlogits, inv_T);
     return hipGetLastError();
 }
 

@@ -99,6 +99,44 @@ int64_t head_chunk_of(const mt_options& o, int64_t T) {
     return std::max<int64_t>(1, std::min<int64_t>(c, T));
 }
 
+// The LM head's E_out in row chunks (head_vocab_chunk != 0).  Chunk c covers
+// the head tile's elements [start, start + elems): chunk 0 also holds gf and
+// the padding before E_out, so every element the head updates is in exactly
+// one chunk.  Empty when the head streams as one unit.
+struct HeadChunk {
+    int64_t start, elems;  // head-tile element range
+    int row0, rows;        // vocabulary rows of E_out
+};
+std::vector<HeadChunk> head_chunks(const Layout& lay, const mt_options& o) {
+    std::vector<HeadChunk> v;
+    if (o.head_vocab_chunk == 0) return v;
+    const int64_t d = lay.sh.d_model, V = lay.sh.vocab;
+    const int64_t e0 = lay.units[lay.head()].t[T_EOUT].off;
+    int64_t rows = o.head_vocab_chunk;
+    if (rows < 0) {
+        int64_t lmax = 0;
+        for (int l = 0; l < lay.L(); ++l) lmax = std::max(lmax, lay.units[l].elems);
+        rows = std::max<int64_t>(8, ((lmax - e0) / d) & ~int64_t(7));
+    }
+    rows = std::min(rows, V);
+    for (int64_t r = 0; r < V; r += rows) {
+        const int64_t n = std::min(rows, V - r);
+        const int64_t start = r == 0 ? 0 : e0 + r * d;
+        v.push_back({start, e0 + (r + n) * d - start, int(r), int(n)});
+    }
+    return v;
+}
+
+// Elements of the largest block a weight slot receives.
+int64_t stream_elems_max(const Layout& lay, const mt_options& o) {
+    const auto ch = head_chunks(lay, o);
+    if (ch.empty()) return lay.max_stream_elems;
+    int64_t m = 0;
+    for (int l = 0; l < lay.L(); ++l) m = std::max(m, lay.units[l].elems);
+    for (const HeadChunk& c : ch) m = std::max(m, c.elems);
+    return m;
+}
+
 // Checkpoint interval, capped at the depth, and the host ring entries it needs.
 int ckpt_k(const mt_options& o, const mt_shape& sh) { return std::max(1, std::min(o.ckpt_interval, sh.n_layers)); }
 int ckpt_slots(const mt_options& o, const mt_shape& sh) {
@@ -161,9 +199,21 @@ void plan_workspace(const Layout& lay, const mt_options& o, Carver& cv, Workspac
     ws.nf = cv.take<uint16_t>(td);
     ws.dnf = cv.take<uint16_t>(td);
     ws.rstdf = cv.take<float>(uint64_t(T) * 4);
-    ws.logits = cv.take<float>(uint64_t(tc) * V * 4);
-    ws.dlogits = cv.take<uint16_t>(uint64_t(tc) * V * 2);
-    ws.deout_acc = tc < T ? cv.take<float>(uint64_t(V) * d * 4) : nullptr;
+    // Vocabulary columns one logits block holds: all of V, or one E_out chunk.
+    int64_t vc = V;
+    const auto hch = head_chunks(lay, o);
+    if (!hch.empty()) {
+        vc = 0;
+        for (const HeadChunk& c : hch) vc = std::max<int64_t>(vc, c.rows);
+        ws.dnf_acc = cv.take<float>(uint64_t(T) * d * 4);
+        ws.ce_m = cv.take<float>(uint64_t(T) * 4);
+        ws.ce_l = cv.take<float>(uint64_t(T) * 4);
+        ws.ce_z = cv.take<float>(uint64_t(T) * 4);
+        ws.ce_lse = cv.take<float>(uint64_t(T) * 4);
+    }
+    ws.logits = cv.take<float>(uint64_t(tc) * vc * 4);
+    ws.dlogits = cv.take<uint16_t>(uint64_t(tc) * vc * 2);
+    ws.deout_acc = tc < T ? cv.take<float>(uint64_t(vc) * d * 4) : nullptr;
     ws.loss_rows = cv.take<float>(uint64_t(T) * 4);
     ws.loss = cv.take<float>(256);
 }
@@ -171,7 +221,7 @@ void plan_workspace(const Layout& lay, const mt_options& o, Carver& cv, Workspac
 ArenaPlan plan_arena(const Layout& lay, const mt_options& o, uint8_t* base, Workspace* ws) {
     ArenaPlan p;
     p.slot_bytes = o.slot_bytes_override ? al4k(o.slot_bytes_override)
-                                         : al4k(uint64_t(lay.max_stream_elems) * 2);
+                                         : al4k(uint64_t(stream_elems_max(lay, o)) * 2);
     p.n_slots = o.n_weight_slots;
     const bool combined = o.slot_mode == 1;
     p.n_garea = combined ? p.n_slots : 2;
@@ -240,6 +290,8 @@ int validate_options(const mt_options* o) {
     if (o->ckpt_interval > 1 && !o->ckpt_on_host) MT_FAIL(MT_E_INVAL, "ckpt_interval > 1 needs ckpt_on_host = 1");
     if (o->pin_weights != 0 && o->pin_weights != 1) MT_FAIL(MT_E_INVAL, "pin_weights must be 0 or 1");
     if (o->pin_weights && o->pin_store) MT_FAIL(MT_E_INVAL, "pin_weights and pin_store exclude each other");
+    if (o->head_vocab_chunk < -1 || (o->head_vocab_chunk > 0 && (o->head_vocab_chunk & 7)))
+        MT_FAIL(MT_E_INVAL, "head_vocab_chunk must be -1, 0 or a positive multiple of 8");
     if (!(o->lr >= 0.f) || !(o->beta1 >= 0.f && o->beta1 < 1.f) || !(o->beta2 >= 0.f && o->beta2 < 1.f) ||
         !(o->adam_eps > 0.f))
         MT_FAIL(MT_E_INVAL, "bad Adam hyper-parameters");
@@ -299,6 +351,8 @@ struct Ctx {
         AdamStep a;
         int64_t step_id;  // the step (1-based) whose gradient this is
         int mode;
+        int64_t off = 0;    // first tile element (a head chunk starts inside the tile)
+        bool last = true;   // completes the unit's update of this step
     };
     std::deque<Job> jobs;
     std::vector<int64_t> adam_gen;  // updates applied per unit
@@ -344,6 +398,8 @@ struct Ctx {
         int unit, ga, slot, mode;  // slot >= 0: combined W/G slot released after the copy
         void* gbase;
         uint64_t bytes;
+        int64_t off = 0;   // first tile element of the copied range
+        bool last = true;  // the unit's last range this step
     };
     std::thread off_thread;
     std::mutex off_mu;
@@ -430,16 +486,22 @@ struct Ctx {
                          uint16_t* dx, int B, int S);
     hipError_t head(const HeadView& w, const HeadView& g, const uint16_t* xL, uint16_t* dy, int B, int S,
                     float inv_tokens);
+    hipError_t head_chunk_fwd(const HeadChunk& ch, bool first, bool last, const void* wbase, const uint16_t* xL,
+                              int B, int S);
+    hipError_t head_chunk_bwd(const HeadChunk& ch, bool first, bool last, const void* wbase, void* gbase,
+                              const uint16_t* xL, uint16_t* dy, int B, int S, float inv_tokens);
     hipError_t gemm_nn_t(const uint16_t* A, int64_t lda, const uint16_t* Bm, int64_t ldb, uint16_t* C, int64_t ldc,
                          int M, int N, int K);
     hipError_t gemm_tn_t(const uint16_t* A, int64_t lda, const uint16_t* Bm, int64_t ldb, uint16_t* C, int64_t ldc,
                          int M, int N, int K);
     hipError_t ensure_rope(int S);
     int pick_slot(int unit, bool* need_stream);
-    int stream_unit(int unit, int slot);
+    // Stream W of `unit` (elements [e0, e0 + n), n < 0: all) into `slot`; the
+    // slot then holds block `id` (id < 0: the unit).
+    int stream_unit(int unit, int slot, int id = -1, int64_t e0 = 0, int64_t n = -1);
     void slab_worker();
     int acquire_slab();
-    void enqueue_job(int unit, int slab, int mode);
+    void enqueue_job(int unit, int slab, int mode, int64_t off = 0, int64_t elems = -1, bool last = true);
     int drain_jobs();
     int wait_adam(int unit);
     int ensure_loaded(int unit);
@@ -482,9 +544,9 @@ int Ctx::init(const mt_shape& sh, const mt_options& o, void* arena_, uint64_t by
     if (bytes < plan.total)
         MT_FAIL(MT_E_NOMEM, "gpu arena of %llu bytes is smaller than the %llu needed",
                 (unsigned long long)bytes, (unsigned long long)plan.total);
-    if (plan.slot_bytes < uint64_t(lay.max_stream_elems) * 2)
-        MT_FAIL(MT_E_INVAL, "slot_bytes_override is below the largest unit (%lld bytes)",
-                (long long)(lay.max_stream_elems * 2));
+    if (plan.slot_bytes < uint64_t(stream_elems_max(lay, opt)) * 2)
+        MT_FAIL(MT_E_INVAL, "slot_bytes_override is below the largest streamed block (%lld bytes)",
+                (long long)(stream_elems_max(lay, opt) * 2));
     arena = static_cast<uint8_t*>(arena_);
     arena_bytes = bytes;
     plan = plan_arena(lay, opt, arena, &ws);
@@ -675,7 +737,12 @@ void Ctx::slab_worker() {
             err = strfmt("injected slab-worker fault at unit %d", j.unit);
         } else {
             const auto t0 = Clock::now();
-            const TilePtrs tp = tile_ptrs(store, lay, j.unit, wblock);
+            TilePtrs tp = tile_ptrs(store, lay, j.unit, wblock);
+            tp.w += j.off;
+            tp.g += j.off;
+            tp.master += j.off;
+            tp.m += j.off;
+            tp.v += j.off;
             const uint16_t* src = j.slab >= 0 ? reinterpret_cast<const uint16_t*>(slabs[j.slab]) : tp.g;
             switch (j.mode) {
                 case JOB_ADAM: adam_unit(*adam_pool, tp, src, j.elems, j.a); break;
@@ -697,7 +764,7 @@ void Ctx::slab_worker() {
                 worker_error = err;
             }
             if (j.slab >= 0) free_slabs.push_back(j.slab);
-            if (j.mode == JOB_ADAM || j.mode == JOB_ACCUM_ADAM) ++adam_gen[j.unit];
+            if (j.last && (j.mode == JOB_ADAM || j.mode == JOB_ACCUM_ADAM)) ++adam_gen[j.unit];
             --jobs_pending;
         }
         free_cv.notify_all();
@@ -736,7 +803,7 @@ void Ctx::offload_worker() {
         // The job is queued before the request counts as issued, so a
         // compute thread that saw every request issued also sees its job.
         if (e == hipSuccess) {
-            enqueue_job(r.unit, k, r.mode);
+            enqueue_job(r.unit, k, r.mode, r.off, int64_t(r.bytes / 2), r.last);
         } else {
             std::lock_guard<std::mutex> lk(q_mu);
             free_slabs.push_back(k);
@@ -782,10 +849,10 @@ int Ctx::acquire_slab() {
     return k;
 }
 
-void Ctx::enqueue_job(int unit, int slab, int mode) {
+void Ctx::enqueue_job(int unit, int slab, int mode, int64_t off, int64_t elems, bool last) {
     {
         std::lock_guard<std::mutex> lk(q_mu);
-        jobs.push_back({unit, slab, lay.units[unit].elems, cur_adam, step + 1, mode});
+        jobs.push_back({unit, slab, elems < 0 ? lay.units[unit].elems : elems, cur_adam, step + 1, mode, off, last});
         ++jobs_pending;
     }
     q_cv.notify_one();
@@ -977,6 +1044,97 @@ hipError_t Ctx::bwd_layer(const LayerView& w, const LayerView& g, const uint16_t
     return hipSuccess;
 }
 
+// The head streamed in E_out row chunks ([Hotdry]: the pinned staging
+// buffers match the largest layer; here the largest decoder layer, not the
+// head).  Forward over the chunks in order: nf once (chunk 0 carries gf), the
+// logits of every token chunk against the chunk's rows, the running
+// logsumexp per token; after the last chunk the loss rows and the loss.
+hipError_t Ctx::head_chunk_fwd(const HeadChunk& ch, bool first, bool last, const void* wbase, const uint16_t* xL,
+                               int B, int S) {
+    const mt_shape& sh = lay.sh;
+    const int T = B * S, d = sh.d_model;
+    hipStream_t s = st_c;
+    const UnitLayout& hu = lay.units[lay.head()];
+    const uint16_t* w = static_cast<const uint16_t*>(wbase);
+    const uint16_t* E = w + (hu.t[T_EOUT].off + int64_t(ch.row0) * d - ch.start);
+    if (first)
+        HIPR(site(S_HEAD_RMS_FWD, [&] {
+            return rmsnorm_fwd(xL, false, w + hu.t[T_GF].off, ws.nf, nullptr, ws.rstdf, T, d, sh.rms_eps, s);
+        }));
+    const int tc = int(std::min<int64_t>(ws.head_chunk, T));
+    for (int r0 = 0; r0 < T; r0 += tc) {
+        const int rows = std::min(tc, T - r0);
+        HIPR(site(S_HEAD_LOGITS, [&] {
+            GemmArgs a{ws.nf + int64_t(r0) * d, d, E, d, ws.logits, ch.rows, nullptr, 0, nullptr, 0, rows, ch.rows, d};
+            return gemm(GEMM_NT, EPI_F32, a, s);
+        }));
+        HIPR(site(S_HEAD_CE, [&] {
+            return ce_chunk_fwd(ws.logits, ws.labels + r0, rows, ch.rows, ch.row0, first, ws.ce_m + r0,
+                                ws.ce_l + r0, ws.ce_z + r0, s);
+        }));
+    }
+    if (last) {
+        HIPR(site(S_HEAD_CE, [&] { return ce_chunk_final(ws.ce_m, ws.ce_l, ws.ce_z, ws.ce_lse, ws.loss_rows, T, s); }));
+        HIPR(site(S_HEAD_MISC, [&] { return mean_reduce(ws.loss_rows, ws.loss, T, s); }));
+    }
+    return hipSuccess;
+}
+
+// Backward over the chunks in reverse order (the last forward chunk is still
+// in its slot): the chunk's logits again, dlogits = (softmax - onehot) / T,
+// dnf summed over the chunks in fp32, the chunk's dE_out summed over token
+// chunks in fp32 and written as bf16 into the gradient area (element i of the
+// area = element start + i of the head tile); after chunk 0, the last, the
+// final RMSNorm backward writes dy and dgf.
+hipError_t Ctx::head_chunk_bwd(const HeadChunk& ch, bool first, bool last, const void* wbase, void* gbase,
+                               const uint16_t* xL, uint16_t* dy, int B, int S, float inv_tokens) {
+    const mt_shape& sh = lay.sh;
+    const int T = B * S, d = sh.d_model;
+    hipStream_t s = st_c;
+    const UnitLayout& hu = lay.units[lay.head()];
+    const int64_t eoff = hu.t[T_EOUT].off + int64_t(ch.row0) * d - ch.start;
+    const uint16_t* w = static_cast<const uint16_t*>(wbase);
+    uint16_t* g = static_cast<uint16_t*>(gbase);
+    const uint16_t* E = w + eoff;
+    uint16_t* gE = g + eoff;
+    const int tc = int(std::min<int64_t>(ws.head_chunk, T));
+    const int nch = (T + tc - 1) / tc;
+    for (int c = 0; c < nch; ++c) {
+        const int r0 = c * tc, rows = std::min(tc, T - r0);
+        HIPR(site(S_HEAD_LOGITS, [&] {
+            GemmArgs a{ws.nf + int64_t(r0) * d, d, E, d, ws.logits, ch.rows, nullptr, 0, nullptr, 0, rows, ch.rows, d};
+            return gemm(GEMM_NT, EPI_F32, a, s);
+        }));
+        HIPR(site(S_HEAD_CE, [&] {
+            return ce_chunk_bwd(ws.logits, ws.labels + r0, ws.ce_lse + r0, rows, ch.rows, ch.row0, ws.dlogits,
+                                inv_tokens, s);
+        }));
+        HIPR(site(S_HEAD_DX, [&] {
+            GemmArgs a{ws.dlogits, ch.rows, E, d, ws.dnf_acc + int64_t(r0) * d, d, nullptr, 0, nullptr, 0,
+                       rows, d, ch.rows};
+            return gemm(GEMM_NN, first ? EPI_F32 : EPI_F32_ACC, a, s);
+        }));
+        HIPR(site(S_HEAD_DW, [&] {
+            GemmArgs a{ws.dlogits, ch.rows, ws.nf + int64_t(r0) * d, d, nullptr, d, nullptr, 0, nullptr, 0,
+                       ch.rows, d, rows};
+            GemmEpi epi;
+            if (nch == 1) { a.C = gE; epi = EPI_BF16; }
+            else if (c == 0) { a.C = ws.deout_acc; epi = EPI_F32; }
+            else if (c + 1 < nch) { a.C = ws.deout_acc; epi = EPI_F32_ACC; }
+            else { a.C = gE; a.Cacc = ws.deout_acc; a.ldacc = d; epi = EPI_BF16_ACCF32; }
+            return gemm(GEMM_TN, epi, a, s);
+        }));
+    }
+    if (last) {
+        HIPR(site(S_HEAD_RMS_BWD, [&] {
+            HIPR(f32_to_bf16(ws.dnf_acc, ws.dnf, int64_t(T) * d, s));
+            return rmsnorm_bwd(ws.dnf, xL, false, w + hu.t[T_GF].off, ws.rstdf, nullptr, dy, g + hu.t[T_GF].off,
+                               ws.partial, T, d, s);
+        }));
+    }
+    return hipSuccess;
+}
+
 // C[M x N] = A[M x K] B[K x N] (B row-major): B transposed into tB, then NT.
 hipError_t Ctx::gemm_nn_t(const uint16_t* A, int64_t lda, const uint16_t* Bm, int64_t ldb, uint16_t* C, int64_t ldc,
                           int M, int N, int K) {
@@ -1057,9 +1215,9 @@ int Ctx::pick_slot(int unit, bool* need_stream) {
 
 // Pack unit -> pinned staging (host), then H2D staging -> slot on the weight
 // stream once the slot is released.
-int Ctx::stream_unit(int unit, int slot) {
-    const uint64_t bytes = uint64_t(lay.units[unit].elems) * 2;
-    const uint8_t* src = wblock ? wblock + lay.w_off[unit] : store + lay.tile_off[unit];
+int Ctx::stream_unit(int unit, int slot, int id, int64_t e0, int64_t n) {
+    const uint64_t bytes = uint64_t(n < 0 ? lay.units[unit].elems : n) * 2;
+    const uint8_t* src = (wblock ? wblock + lay.w_off[unit] : store + lay.tile_off[unit]) + e0 * 2;
     if (unit == fault_pack) {
         failed = true;
         MT_FAIL(MT_E_INTERNAL, "injected pack fault at unit %d", unit);
@@ -1086,7 +1244,7 @@ int Ctx::stream_unit(int unit, int slot) {
         HIPC(h2d(arena + plan.wslot[slot], staging[p], bytes, st_w));
         HIPC(rec(staging_free[p], st_w));
     }
-    slot_unit[slot] = unit;
+    slot_unit[slot] = id < 0 ? unit : id;
     return MT_OK;
 }
 
@@ -1159,14 +1317,23 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
     // other inputs, and run the block's backward from its last layer down.
     // With k = 1 this is forward 0..L-1, head, backward L-1..0.  Every
     // micro-batch of the step runs the whole schedule with the same weights.
-    enum { V_FWD, V_HEAD, V_REFWD, V_BWD };
+    enum { V_FWD, V_HEAD, V_REFWD, V_BWD, V_HFWD, V_HBWD };
     struct Visit {
         int kind, unit, block, pos;  // block: backward block counter; pos: the layer's index in its block
+                                     // (head chunk visits: the chunk)
     };
     const int K = opt.ckpt_on_host ? ckpt_k(opt, sh) : 1;
+    const std::vector<HeadChunk> hch = head_chunks(lay, opt);
+    const int NV = int(hch.size());
     std::vector<Visit> sched;
     for (int l = 0; l < L; ++l) sched.push_back({V_FWD, l, 0, 0});
-    sched.push_back({V_HEAD, lay.head(), 0, 0});
+    if (hch.empty()) {
+        sched.push_back({V_HEAD, lay.head(), 0, 0});
+    } else {
+        // The head in E_out chunks: forward in order, backward in reverse.
+        for (int c = 0; c < NV; ++c) sched.push_back({V_HFWD, lay.head(), 0, c});
+        for (int c = NV - 1; c >= 0; --c) sched.push_back({V_HBWD, lay.head(), 0, c});
+    }
     for (int j = (L + K - 1) / K - 1, bi = 0; j >= 0; --j, ++bi) {
         const int b0 = j * K, e0 = std::min(b0 + K - 1, L - 1);
         for (int i = b0; i < e0; ++i) sched.push_back({V_REFWD, i, bi, i - b0});
@@ -1213,16 +1380,19 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
         int gnext = 0, nbwd = 0, restored = -1;
         for (const Visit& vs : sched) {
             const int kind = vs.kind, unit = vs.unit;
+            const bool hchunk = kind == V_HFWD || kind == V_HBWD;
+            const HeadChunk* ch = hchunk ? &hch[size_t(vs.pos)] : nullptr;
             // Bind target: a streamed slot or the resident copy.
             int slot = 0;
             void* wbase;
             if (opt.resident) {
-                wbase = arena + plan.resident[unit];
+                wbase = arena + plan.resident[unit] + (ch ? ch->start * 2 : 0);
             } else {
                 bool need = false;
-                slot = pick_slot(unit, &need);
+                const int id = ch ? lay.embed() + 1 + vs.pos : unit;  // slot contents: unit or head chunk
+                slot = pick_slot(id, &need);
                 if (need) {
-                    const int r = stream_unit(unit, slot);
+                    const int r = ch ? stream_unit(unit, slot, id, ch->start, ch->elems) : stream_unit(unit, slot);
                     if (r != MT_OK) {
                         drain_jobs();
                         return r;
@@ -1245,7 +1415,7 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
             // Head and backward write a gradient area: wait until its last
             // offload is done (Buffer-Free) before the visit's clock starts.
             int ga = 0;
-            if (kind == V_HEAD || kind == V_BWD) {
+            if (kind == V_HEAD || kind == V_BWD || kind == V_HBWD) {
                 ga = combined ? slot : gnext;
                 if (!combined) gnext ^= 1;
                 const int wo = wait_offload(ga_last_req[ga]);
@@ -1279,6 +1449,18 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
                 }
                 continue;
             }
+            if (kind == V_HFWD) {
+                const uint16_t* xL = opt.ckpt_on_host ? ws.x[L & 1] : ws.ckpt_dev + uint64_t(L) * ws.maxT * d;
+                HIPC(head_chunk_fwd(*ch, vs.pos == 0, vs.pos == NV - 1, wbase, xL, B, S));
+                if (vs.pos == NV - 1) {
+                    HIPC(hipMemcpyAsync(loss_pin, ws.loss, 4, hipMemcpyDeviceToHost, st_c));
+                    HIPC(rec(loss_done, st_c));
+                }
+                HIPC(hipEventRecord(vz, st_c));
+                intervals.push_back({va, vz, 0, 0, kind, unit});
+                HIPC(rec(slot_free[slot], st_c));
+                continue;
+            }
             if (kind == V_REFWD) {
                 // Rebuild the next layer's input inside the block's bank.
                 HIPC(fwd_layer(bind_layer(lay, wbase), xb[vs.pos], xb[vs.pos + 1], B, S, true));
@@ -1294,6 +1476,10 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
                 HIPC(head(bind_head(lay, wbase), bind_head(lay, gbase), xL, ws.dy[0], B, S, inv_tokens));
                 HIPC(hipMemcpyAsync(loss_pin, ws.loss, 4, hipMemcpyDeviceToHost, st_c));
                 HIPC(rec(loss_done, st_c));
+            } else if (kind == V_HBWD) {
+                const uint16_t* xL = opt.ckpt_on_host ? ws.x[L & 1] : ws.ckpt_dev + uint64_t(L) * ws.maxT * d;
+                HIPC(head_chunk_bwd(*ch, vs.pos == NV - 1, vs.pos == 0, wbase, gbase, xL, ws.dy[0], B, S,
+                                    inv_tokens));
             } else {
                 const uint16_t* x = opt.ckpt_on_host ? xb[vs.pos] : ws.ckpt_dev + uint64_t(unit) * ws.maxT * d;
                 HIPC(bwd_layer(bind_layer(lay, wbase), bind_layer(lay, gbase), x, ws.dy[nbwd & 1],
@@ -1309,13 +1495,17 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
             // Gradient offload: Backward-Done -> free slab -> Buffer-Free.
             {
                 std::lock_guard<std::mutex> lk(off_mu);
-                off_q.push_back({unit, ga, combined ? slot : -1, mode, gbase, uint64_t(lay.units[unit].elems) * 2});
+                if (ch)  // one head chunk: its element range of the head tile
+                    off_q.push_back({unit, ga, combined ? slot : -1, mode, gbase, uint64_t(ch->elems) * 2, ch->start,
+                                     vs.pos == 0});
+                else
+                    off_q.push_back({unit, ga, combined ? slot : -1, mode, gbase, uint64_t(lay.units[unit].elems) * 2});
                 ga_last_req[ga] = off_submitted;
                 if (combined) slot_last_req[slot] = off_submitted;
                 ++off_submitted;
             }
             off_cv.notify_all();
-            if (kind == V_HEAD) {
+            if (kind == V_HEAD || (kind == V_HBWD && vs.pos == 0)) {
                 ph.head = next_tev();
                 HIPC(hipEventRecord(ph.head, st_c));
             }
@@ -1422,7 +1612,7 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
                 float a = 0.f, b = 0.f;
                 hipEventElapsedTime(&a, t_base, iv.a);
                 hipEventElapsedTime(&b, t_base, iv.b);
-                static const char* names[] = {"fwd", "head", "refwd", "bwd"};
+                static const char* names[] = {"fwd", "head", "refwd", "bwd", "hfwd", "hbwd"};
                 fprintf(f, "%lld,%s,%s,%d,%.4f,%.4f,%llu\n", (long long)step,
                         iv.kind == 0 ? "compute" : iv.kind == 1 ? "h2d" : "d2h",
                         iv.kind == 0 ? names[iv.visit] : "-", iv.unit, a, b, (unsigned long long)iv.bytes);
@@ -1627,6 +1817,7 @@ int mt_default_options(mt_options* o) {
     o->cross_step = 0;
     o->ckpt_interval = 1;
     o->pin_weights = 0;
+    o->head_vocab_chunk = 0;
     o->lr = 1e-4f;
     o->beta1 = 0.9f;
     o->beta2 = 0.999f;

@@ -60,6 +60,9 @@ struct Workspace {
     int64_t head_chunk = 0;
     uint16_t *nf, *dnf, *dlogits;
     float *rstdf, *logits, *deout_acc, *loss_rows, *loss;
+    // head streamed in E_out row chunks: fp32 dnf accumulated over the
+    // chunks, running max / sum of exp / label logit / LSE per token
+    float *dnf_acc = nullptr, *ce_m = nullptr, *ce_l = nullptr, *ce_z = nullptr, *ce_lse = nullptr;
     uint64_t bytes = 0;
 };
 

@@ -101,6 +101,16 @@ hipError_t ce_fwd_bwd(const float* logits, const int32_t* labels, float* loss_ro
                       uint16_t* dlogits, int Tc, int V, float inv_T, hipStream_t s);
 // out[0] = sum(x[0..n)) / n in a fixed order (one block).
 hipError_t mean_reduce(const float* x, float* out, int n, hipStream_t s);
+// Cross-entropy over vocabulary chunks of Vc (a multiple of 8) columns
+// starting at vocabulary row v0: merge the chunk into the running (m, l) per
+// row (first: start afresh) and pick the label's logit into z; final: LSE and
+// loss per row; bwd: dlogits = (exp(x - LSE) - onehot) * inv_T in bf16.
+hipError_t ce_chunk_fwd(const float* logits, const int32_t* labels, int rows, int Vc, int v0, bool first, float* m,
+                        float* l, float* z, hipStream_t s);
+hipError_t ce_chunk_final(const float* m, const float* l, const float* z, float* lse, float* loss_rows, int T,
+                          hipStream_t s);
+hipError_t ce_chunk_bwd(const float* logits, const int32_t* labels, const float* lse, int rows, int Vc, int v0,
+                        uint16_t* dlogits, float inv_T, hipStream_t s);
 
 // --------------------------------------------------------------- misc -----
 hipError_t f32_to_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t s);

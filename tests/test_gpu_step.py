@@ -221,6 +221,86 @@ def test_checkpoint_interval_bit_identical(deep_baseline_run, opts):
         assert np.array_equal(a1.view(np.uint8), a2.view(np.uint8)), (k1, w1)
 
 
+# ------------------------------------------- vocabulary-chunked head ----
+BIGV = dict(n_layers=2, d_model=256, n_heads=4, n_kv_heads=2, head_dim=64, ffn_dim=688, vocab=8192)
+
+
+@pytest.mark.parametrize("kw,B,S,opts", [(CFG1, 2, 128, dict(head_vocab_chunk=256)),
+                                         (CFG1, 2, 128, dict(head_vocab_chunk=264, head_chunk=48)),
+                                         (BIGV, 1, 96, dict(head_vocab_chunk=-1))],
+                         ids=["4chunks", "ragged+tokenchunks", "auto"])
+def test_vocab_chunked_head_step_parity(kw, B, S, opts):
+    """The head streamed in E_out row chunks (online logsumexp over a forward
+    pass, logits recomputed in a reverse backward pass, each chunk's gradient
+    offloaded and updated on its own) against the oracle: loss, every
+    gradient and the Adam update of the head."""
+    log(f"vocab-chunked head {kw['vocab']} {opts}")
+    ctx = make_ctx(kw, B, S, **opts)
+    tokens, labels = synth.tokens_labels(17, B, S, kw["vocab"])
+    params = read_params(ctx, kw)
+    masters0 = read_all(ctx, kw, mt.MT_MASTER)
+    loss, _ = ctx.train_step(tokens, labels)
+    loss_ref, g_ref = ostep.grads_monolithic(params, tokens, labels, oracle_shape(kw))
+    assert abs(loss - loss_ref) / abs(loss_ref) <= 1e-2, (loss, loss_ref)
+    _cmp_units(ctx, kw, g_ref, per_tensor=True)
+    L = kw["n_layers"]
+    for (u, j), m0 in masters0:
+        if u != L:
+            continue
+        g = widen(ctx.get_tensor(u, j, mt.MT_G))
+        z = np.zeros_like(m0)
+        mst, _, _, _ = ostep.adam_update(m0, z, z, g, 1, 1e-4, 0.9, 0.999, 1e-8)
+        got = ctx.get_tensor(u, j, mt.MT_MASTER)
+        err = np.abs(got.astype(np.float64) - mst.astype(np.float64))
+        assert np.all(err <= np.maximum(2 * np.spacing(np.abs(mst)).astype(np.float64), 1e-10)), (u, j)
+    ctx.close()
+
+
+def test_vocab_chunked_head_slots_sized_to_the_layer():
+    """With automatic chunking the weight slots (and so the arena) hold the
+    largest decoder layer, not the head."""
+    sh = mt.make_shape(**BIGV)
+    whole = mt.workspace_bytes(sh, mt.default_options(max_batch=1, max_seq=96))
+    chunked = mt.workspace_bytes(sh, mt.default_options(max_batch=1, max_seq=96, head_vocab_chunk=-1))
+    assert chunked[1] < whole[1]  # pinned: staging and slabs are slot-sized
+
+
+@pytest.fixture(scope="module")
+def chunked_baseline_run():
+    return _run_two_steps(BIGV, 1, 64, head_vocab_chunk=-1)
+
+
+@pytest.mark.parametrize("opts", [dict(resident=1), dict(n_weight_slots=1), dict(n_weight_slots=3),
+                                  dict(slot_mode=1), dict(cross_step=1, n_grad_slabs=1), dict(pin_weights=1),
+                                  dict(ckpt_interval=2)],
+                         ids=lambda o: ",".join(f"{k}={v}" for k, v in o.items()))
+def test_vocab_chunked_head_bit_identical_across_streaming_options(chunked_baseline_run, opts):
+    log(f"chunked head vs default streaming: {opts}")
+    base_losses, base_state = chunked_baseline_run
+    losses, state = _run_two_steps(BIGV, 1, 64, head_vocab_chunk=-1, **opts)
+    assert [np.float32(x).tobytes() for x in losses] == [np.float32(x).tobytes() for x in base_losses]
+    for (k1, w1, a1), (k2, w2, a2) in zip(base_state, state):
+        assert k1 == k2 and w1 == w2
+        assert np.array_equal(a1.view(np.uint8), a2.view(np.uint8)), (k1, w1)
+
+
+def test_vocab_chunked_head_with_micro_batches():
+    """Chunked head under gradient accumulation: two identical micro-batches
+    give the one-micro-batch step bit for bit."""
+    kw, B, S = BIGV, 1, 64
+    base_losses, base_state = _run_two_steps(kw, B, S, head_vocab_chunk=-1)
+    ctx = make_ctx(kw, B, S, head_vocab_chunk=-1)
+    losses = []
+    for k in range(2):
+        t, lb = synth.tokens_labels(100 + k, B, S, kw["vocab"])
+        losses.append(ctx.train_step_accum(np.stack([t] * 2), np.stack([lb] * 2))[0])
+    state = _state(ctx, kw)
+    ctx.close()
+    assert [np.float32(x).tobytes() for x in losses] == [np.float32(x).tobytes() for x in base_losses]
+    for (k1, w1, a1), (k2, w2, a2) in zip(base_state, state):
+        assert np.array_equal(a1.view(np.uint8), a2.view(np.uint8)), (k1, w1)
+
+
 # -------------------------------------------- gradient accumulation ----
 def _micro_batches(kw, n, B, S, seed0):
     tl = [synth.tokens_labels(seed0 + j, B, S, kw["vocab"]) for j in range(n)]

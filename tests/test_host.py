@@ -125,7 +125,8 @@ def test_bad_shapes_rejected(field, value):
 
 @pytest.mark.parametrize("field,value", [("n_weight_slots", 0), ("n_weight_slots", 5), ("n_grad_slabs", 0),
                                          ("slot_mode", 2), ("max_batch", 0), ("beta1", 1.0), ("ckpt_interval", 0),
-                                         ("cross_step", 2), ("pin_weights", 2)])
+                                         ("cross_step", 2), ("pin_weights", 2), ("head_vocab_chunk", -2),
+                                         ("head_vocab_chunk", 12)])
 def test_bad_options_rejected(field, value):
     o = mt.default_options()
     setattr(o, field, value)
@@ -138,6 +139,22 @@ def test_option_conflicts_rejected():
         o = mt.default_options(**kw)
         a, p, h = C.c_uint64(), C.c_uint64(), C.c_uint64()
         assert mt.lib.mt_workspace_bytes(C.byref(CFG1), C.byref(o), C.byref(a), C.byref(p), C.byref(h)) == mt.MT_E_INVAL
+
+
+def test_vocab_chunked_head_sizes_slots_to_the_decoder_layer():
+    """head_vocab_chunk=-1 streams E_out in row chunks no larger than the
+    largest decoder layer: at the 7B shape the four slot-sized arena buffers
+    and the 14 slot-sized pinned buffers shrink from the head's 1.09 GB to the
+    layer's 466 MB (minus the chunked head's own fp32 buffers)."""
+    o0 = mt.default_options(max_batch=8, max_seq=1024)
+    o1 = mt.default_options(max_batch=8, max_seq=1024, head_vocab_chunk=-1)
+    a0, p0, h0 = mt.workspace_bytes(QWEN7, o0)
+    a1, p1, h1 = mt.workspace_bytes(QWEN7, o1)
+    layer_b = mt.unit_elems(QWEN7, 0) * 2
+    head_b = mt.unit_elems(QWEN7, 28) * 2
+    assert h1 == h0
+    assert abs((p0 - p1) - 14 * (head_b - layer_b)) < 14 * 8192
+    assert a1 < a0 - 2 * (head_b - layer_b)
 
 
 def test_checkpoint_interval_trades_pinned_ring_for_arena_banks():
