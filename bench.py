@@ -269,6 +269,9 @@ def main():
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only launch the gate|up GEMM three times and a 1 GiB device copy three times (run "
                          "under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE to measure the GEMM's HBM traffic)")
+    ap.add_argument("--head-vocab-chunk", type=int, default=-1,
+                    help="stream the LM head in E_out row chunks; -1 (default): chunks sized to the largest "
+                         "decoder layer, so every slot is layer-sized; 0: the head as one unit")
     ap.add_argument("--own-streams", action="store_true",
                     help="let the library create its three streams instead of passing torch's")
     ap.add_argument("--micro", type=int, default=1,
@@ -297,7 +300,8 @@ def main():
     opt = mt.default_options(max_batch=B, max_seq=S, profile_kernels=0 if args.no_profile else 1,
                              host_threads=args.host_threads, n_weight_slots=args.slots, n_grad_slabs=args.slabs,
                              slot_mode=args.slot_mode, resident=args.resident, pin_store=args.pin_store,
-                             cross_step=args.cross_step, pin_weights=args.pin_weights, seed=synth.SEED_WEIGHTS)
+                             cross_step=args.cross_step, pin_weights=args.pin_weights,
+                             head_vocab_chunk=args.head_vocab_chunk, seed=synth.SEED_WEIGHTS)
     arena_bytes, pinned_bytes, store_bytes = mt.workspace_bytes(shape, opt)
     log(f"arena {arena_bytes / 1e9:.2f} GB, pinned {pinned_bytes / 1e9:.2f} GB, store {store_bytes / 1e9:.2f} GB")
     torch.cuda.init()
@@ -343,7 +347,8 @@ def main():
                       "layers": cfg["n_layers"],
                       "parallelism": "single GPU, layer-streamed", "weight_slots": args.slots,
                       "grad_slabs": args.slabs, "slot_mode": args.slot_mode, "resident": args.resident,
-                      "cross_step": args.cross_step, "pin_weights": args.pin_weights}}
+                      "cross_step": args.cross_step, "pin_weights": args.pin_weights,
+                      "head_vocab_chunk": args.head_vocab_chunk}}
     mf = nm * model_flops_per_step(cfg, T, S)
     out["model_tflops_per_s"] = round(mf / (ms_per_step / 1e3) / 1e12, 2)
     # hardware FLOPs add the recomputed forward of every layer (the down GEMM
