@@ -31,6 +31,10 @@ constexpr float LN2 = 0.6931471805599453f;
 constexpr int BKV = 64;  // keys (or queries) per staged tile
 
 #define MFMA32(a, b, c) __builtin_amdgcn_mfma_f32_32x32x16_bf16((a), (b), (c), 0, 0, 0)
+// 2^x on the hardware instruction alone: results below 2^-126 (probabilities
+// that add nothing at fp32 precision) flush to zero instead of being formed
+// as denormals, which costs the library form four more instructions.
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 // Scores from fp16 q and k (the logit path is kept in fp16: its rounding
 // error enters the softmax in proportion to the logits' size).
 #define MFMA32H(a, b, c) __builtin_amdgcn_mfma_f32_32x32x16_f16((a), (b), (c), 0, 0, 0)
@@ -211,7 +215,7 @@ __global__ __launch_bounds__(256) void attn_fwd_k(AttnArgs a, int n_qt) {
             }
             mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
             const float mn = fmaxf(m, mx * sc);  // running max of the scaled scores (log2 units)
-            const float alpha = (m == -INFINITY) ? 0.f : exp2f(m - mn);
+            const float alpha = (m == -INFINITY) ? 0.f : ex2(m - mn);
             m = mn;
             const float nb = (mn == -INFINITY) ? 0.f : -mn;  // masked scores give exp2(-inf) = 0
             float ps = 0.f;
@@ -219,7 +223,7 @@ __global__ __launch_bounds__(256) void attn_fwd_k(AttnArgs a, int n_qt) {
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float p = exp2f(fmaf(st[t][r], sc, nb));
+                    const float p = ex2(fmaf(st[t][r], sc, nb));
                     st[t][r] = p;
                     ps += p;
                 }
@@ -251,6 +255,234 @@ __global__ __launch_bounds__(256) void attn_fwd_k(AttnArgs a, int n_qt) {
         }
         if (kb + 1 < nkb) lstore(cur ^ 1);
         __syncthreads();
+    }
+
+    const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+    if (q < S) {
+        const float inv = 1.0f / ltot;
+        uint16_t* orow = a.o + (int64_t(b) * S + q) * a.ldo + h * HD;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = 32 * dt + 8 * g + 4 * hh;
+                *reinterpret_cast<uint2*>(orow + d) =
+                    make_uint2(pack2(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv),
+                               pack2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv));
+            }
+        if (hh == 0) a.lse[(int64_t(b) * a.Hq + h) * S + q] = (m + log2f(ltot)) * LN2;
+    }
+}
+
+// ------------------------------------------- forward, direct-load form ----
+// K and V tiles go from global memory straight into LDS
+// (`buffer_load_dwordx4 ... lds`: no staging registers, no LDS stores), both
+// row-major with 16-byte chunks XOR-swizzled by aswz(row).  K fragments are
+// read as rows; the transposed V fragments of the P.V product come from
+// ds_read_b64_tr_b16, which hands lane i of a 16-lane group element i of
+// the four rows the group addresses.  The swizzle serves both reads without
+// bank conflicts: 16 consecutive rows of one chunk (K) and 4 rows x 4
+// chunks (V^T, 32 lanes per cycle) each land on distinct banks.  No staging
+// registers and a small register set let two blocks share a CU, so one
+// wave's softmax runs while the other's products do.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+// Buffer resource (gfx9 layout): base, stride 0, extent in bytes, the
+// default data-format word.  Reads at offsets >= extent return zero.
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    i32x4_t r;
+    r.x = int(uint32_t(p));
+    r.y = int(uint32_t(p >> 32) & 0xFFFFu);
+    r.z = int(bytes);
+    r.w = 0x00020000;
+    return r;
+}
+// 16 bytes per lane from the buffer at byte offset voff into LDS at
+// lds_addr + 16 * lane (inline assembly, so the compiler adds no waits for it
+// before unrelated LDS reads; the kernel waits on vmcnt itself).
+__device__ __forceinline__ void dma16(i32x4_t rs, uint32_t lds_addr, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_addr), "v"(voff), "s"(rs)
+                 : "memory");
+}
+__device__ __forceinline__ void wait_vmem0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Block barrier after this wave's loads landed (vmcnt) and its LDS reads
+// completed (lgkmcnt through the builtin, so the compiler knows).
+__device__ __forceinline__ void barrier_tile() {
+    wait_vmem0();
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+template <int HD>
+__device__ __forceinline__ int aswz(int r) {
+    if constexpr (HD == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return uint32_t(reinterpret_cast<uintptr_t>((lds_ptr_t)p));
+}
+
+template <int HD>
+__global__ __launch_bounds__(256, 2) void attn_fwd2_k(AttnArgs a, int n_qt) {
+    constexpr int NS = HD / 16, ND = HD / 32, NCH = HD / 8;
+    constexpr int TILE = BKV * NCH;  // 16-byte chunks per tile
+    constexpr int NI = TILE / 256;   // wave instructions per tile and operand
+    constexpr int RB = NCH * 16;     // bytes per LDS row
+    __shared__ uint4 Ks[2][TILE];
+    __shared__ uint4 Vs[2][TILE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hh = lane >> 5, c = lane & 31;
+    const int qt = n_qt - 1 - int(blockIdx.x % n_qt);
+    const int bh = int(blockIdx.x / n_qt);
+    const int h = bh % a.Hq, b = bh / a.Hq;
+    const int hk = h / (a.Hq / a.Hkv);
+    const int S = a.S;
+    const int q0 = qt * 128;
+    const int qw = q0 + wave * 32;
+    const int q = qw + c;
+    const uint16_t* base = a.qkv + int64_t(b) * S * a.ld;
+
+    f16x8_t qf[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (q < S) v = *reinterpret_cast<const uint4*>(base + int64_t(q) * a.ld + h * HD + (2 * s + hh) * 8);
+        qf[s] = as_f16x8(v);
+    }
+
+    // Loads: instruction i of wave w fills chunks (4 i + w) * 64 + lane of the
+    // tile; the lane fetches the logical chunk the swizzle places there.
+    const uint32_t ext = uint32_t((int64_t(S - 1) * a.ld + HD) * 2);
+    const i32x4_t rk = make_rsrc(base + (a.Hq + hk) * HD, ext);
+    const i32x4_t rv = make_rsrc(base + (a.Hq + a.Hkv + hk) * HD, ext);
+    uint32_t doff[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int p = (4 * i + wave) * 64 + lane;
+        const int row = p / NCH;
+        const int lc = (p % NCH) ^ aswz<HD>(row);
+        doff[i] = uint32_t((int64_t(row) * a.ld + lc * 8) * 2);
+    }
+    auto issue = [&](int k0, int buf) {
+        const uint32_t kof = uint32_t(int64_t(k0) * a.ld * 2);
+        const uint32_t kl = lds_addr(&Ks[buf][0]), vl = lds_addr(&Vs[buf][0]);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const uint32_t la = uint32_t((4 * i + wave) * 1024);
+            dma16(rk, __builtin_amdgcn_readfirstlane(kl + la), doff[i] + kof);
+            dma16(rv, __builtin_amdgcn_readfirstlane(vl + la), doff[i] + kof);
+        }
+    };
+    // K fragment (row 32 t + c, logical chunk 2 s + hh): byte offset in a tile.
+    auto koff = [&](int t, int s) { return (32 * t + c) * RB + (((2 * s + hh) ^ aswz<HD>(32 * t + c)) * 16); };
+    // V^T fragment for d-tile dt, keys 32 t + 16 s2 + 4 hh + 8 e2 .. +3: the
+    // lane addresses row (j / 4) of its group's four rows, 8 bytes at column
+    // dbase + 4 (j % 4); lane i then holds column dbase + i of the four rows.
+    const int j = lane & 15, g16 = (lane >> 4) & 1;
+    auto voff = [&](int dt, int t, int s2, int e2) {
+        const int row = 32 * t + 16 * s2 + 8 * e2 + 4 * hh + (j >> 2);
+        const int col = 32 * dt + 16 * g16 + 4 * (j & 3);
+        return row * RB + (((col >> 3) ^ aswz<HD>(row)) * 16) + (col & 7) * 2;
+    };
+
+    f32x16_t o[ND];
+#pragma unroll
+    for (int i = 0; i < ND; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
+    float m = -INFINITY, lsum = 0.f;
+    const float sc = LOG2E * rsqrtf(float(HD));
+
+    const int k_end = min(S, q0 + 128);
+    const int nkb = (k_end + BKV - 1) / BKV;
+    issue(0, 0);
+    barrier_tile();
+    for (int kb = 0; kb < nkb; ++kb) {
+        const int cur = kb & 1;
+        const int k0 = kb * BKV;
+        if (kb + 1 < nkb) issue(k0 + BKV, cur ^ 1);
+        if (k0 <= qw + 31) {
+            const char* kt = reinterpret_cast<const char*>(&Ks[cur][0]);
+            const char* vt = reinterpret_cast<const char*>(&Vs[cur][0]);
+            f32x16_t st[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) st[t][r] = 0.f;
+#pragma unroll
+                for (int s = 0; s < NS; ++s)
+                    st[t] = MFMA32H(as_f16x8(*reinterpret_cast<const uint4*>(kt + koff(t, s))), qf[s], st[t]);
+            }
+            const bool full = k0 + BKV - 1 <= qw && k0 + BKV <= S;
+            float mx = -INFINITY;
+            if (full) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[t][r]);
+            } else {
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
+                        if (key > q || key >= S) st[t][r] = -INFINITY;
+                        mx = fmaxf(mx, st[t][r]);
+                    }
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float mn = fmaxf(m, mx * sc);
+            const float alpha = (m == -INFINITY) ? 0.f : ex2(m - mn);
+            m = mn;
+            const float nb = (mn == -INFINITY) ? 0.f : -mn;
+            float ps = 0.f;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float p = ex2(fmaf(st[t][r], sc, nb));
+                    st[t][r] = p;
+                    ps += p;
+                }
+            lsum = lsum * alpha + ps;
+            if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+                for (int i = 0; i < ND; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+            }
+            bf16x8_t pb[2][2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    float tmp[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) tmp[e] = st[t][8 * s2 + e];
+                    pb[t][s2] = pack_b(tmp);
+                }
+#pragma unroll
+            for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) i16x4_t*)(lds_ptr_t)(vt + voff(dt, t, s2, 0)));
+                        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) i16x4_t*)(lds_ptr_t)(vt + voff(dt, t, s2, 1)));
+                        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+                        o[dt] = MFMA32(as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y)), pb[t][s2], o[dt]);
+                    }
+        }
+        barrier_tile();
     }
 
     const float ltot = lsum + __shfl_xor(lsum, 32, 64);
@@ -386,7 +618,7 @@ __global__ __launch_bounds__(256) void attn_dq_k(AttnBwdArgs a, int n_qt) {
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
                         const int r = 8 * s2 + j;
-                        float p = exp2f(fmaf(st[t][r], sc, -lse2));
+                        float p = ex2(fmaf(st[t][r], sc, -lse2));
                         if (!full) {
                             const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
                             if (key > q || key >= S) p = 0.f;
@@ -531,7 +763,7 @@ __global__ __launch_bounds__(256) void attn_dkdv_k(AttnBwdArgs a, int n_kt) {
                     for (int j = 0; j < 8; ++j) {
                         const int r = 8 * s2 + j;
                         const int ql = 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
-                        float p = exp2f(fmaf(st[t][r], sc, -Ls[cur][ql]));
+                        float p = ex2(fmaf(st[t][r], sc, -Ls[cur][ql]));
                         if (!full) {
                             const int qq = q0 + ql;
                             if (key > qq || qq >= S || key >= S) p = 0.f;
@@ -587,8 +819,16 @@ hipError_t attn_fwd(const AttnArgs& a, hipStream_t s) {
     if (!attn_shape_ok(a.B, a.S, a.Hq, a.Hkv, a.hd, a.ld, a.ldo)) return hipErrorInvalidValue;
     const int n_qt = (a.S + 127) / 128;
     const dim3 grid(unsigned(int64_t(n_qt) * a.B * a.Hq));
-    if (a.hd == 128) attn_fwd_k<128><<<grid, 256, 0, s>>>(a, n_qt);
-    else attn_fwd_k<64><<<grid, 256, 0, s>>>(a, n_qt);
+    // The direct-load kernel addresses one sequence's K (or V) rows through a
+    // 32-bit buffer extent.
+    const bool direct = int64_t(a.S) * a.ld * 2 < (int64_t(1) << 32);
+    if (direct) {
+        if (a.hd == 128) attn_fwd2_k<128><<<grid, 256, 0, s>>>(a, n_qt);
+        else attn_fwd2_k<64><<<grid, 256, 0, s>>>(a, n_qt);
+    } else {
+        if (a.hd == 128) attn_fwd_k<128><<<grid, 256, 0, s>>>(a, n_qt);
+        else attn_fwd_k<64><<<grid, 256, 0, s>>>(a, n_qt);
+    }
     return hipGetLastError();
 }
 
