@@ -54,10 +54,13 @@ int mt_k_rope(void* qkv, int64_t ld, void* table, int32_t T, int32_t S, int32_t 
               float base, int32_t dir, void* stream);
 /* Forward rotary embedding on the f32 QKV projection in [T x ldin] (n_heads
  * heads of hd): the first n_rot_heads heads (q and k) are rotated in f32 and
- * written as fp16, the others (v) as bf16, to out [T x ldout].  Same angles
- * and table as mt_k_rope. */
-int mt_k_qkv_rope_cvt(const void* in, int64_t ldin, void* out, int64_t ldout, void* table, int32_t T, int32_t S,
-                      int32_t n_rot_heads, int32_t n_heads, int32_t hd, float base, void* stream);
+ * written as fp16, the others (v) as bf16, to out [T x ldout]; out_bf16 (may
+ * be NULL) [T x ld_bf16] also gets the rotated heads in bf16 (the attention
+ * backward's gradient products take them in that form).  Same angles and
+ * table as mt_k_rope. */
+int mt_k_qkv_rope_cvt(const void* in, int64_t ldin, void* out, int64_t ldout, void* out_bf16, int64_t ld_bf16,
+                      void* table, int32_t T, int32_t S, int32_t n_rot_heads, int32_t n_heads, int32_t hd, float base,
+                      void* stream);
 /* y[i] = fp16(x[i]) for bf16 x, n a multiple of 8. */
 int mt_k_bf16_to_f16(const void* x, void* y, int64_t n, void* stream);
 
@@ -75,10 +78,13 @@ int mt_k_attn_fwd(const void* qkv, int64_t ld, void* o, int64_t ldo, void* lse, 
                   int32_t Hkv, int32_t hd, void* stream);
 /* Backward: dqkv [B*S x ldd] gets dQ, dK, dV in the qkv column layout (the
  * K and V gradients summed over each KV group, in a fixed order); dsum is
- * f32 scratch [B x Hq x S]. */
+ * f32 scratch [B x Hq x S].  qk_bf16 (may be NULL): bf16 copy of the rotated
+ * q and k heads [B*S x ld_bf16] (k after the Hq query heads), which lets the
+ * kernels load every tile straight into LDS; NULL: they round the fp16 q and
+ * k to bf16 themselves. */
 int mt_k_attn_bwd(const void* qkv, int64_t ld, const void* o, const void* dout, int64_t ldo, const void* lse,
                   void* dsum, void* dqkv, int64_t ldd, int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t hd,
-                  void* stream);
+                  const void* qk_bf16, int64_t ld_bf16, void* stream);
 
 /* Cross-entropy of logits [Tc x V] f32 against int32 labels [Tc]:
  * loss_rows [Tc] = logsumexp - logit[label]; dlogits [Tc x V] bf16 =

@@ -100,12 +100,13 @@ int mt_k_rope(void* qkv, int64_t ld, void* table, int32_t T, int32_t S, int32_t 
                "rope_apply");
 }
 
-int mt_k_qkv_rope_cvt(const void* in, int64_t ldin, void* out, int64_t ldout, void* table, int32_t T, int32_t S,
-                      int32_t n_rot_heads, int32_t n_heads, int32_t hd, float base, void* stream) {
+int mt_k_qkv_rope_cvt(const void* in, int64_t ldin, void* out, int64_t ldout, void* out_bf16, int64_t ld_bf16,
+                      void* table, int32_t T, int32_t S, int32_t n_rot_heads, int32_t n_heads, int32_t hd, float base,
+                      void* stream) {
     hipError_t e = mt::rope_table(static_cast<float2*>(table), S, hd, base, S_(stream));
     if (e != hipSuccess) return kst(e, "rope_table");
-    return kst(mt::qkv_rope_cvt(F32(in), ldin, U16(out), ldout, static_cast<float2*>(table), T, S, n_rot_heads,
-                                n_heads, hd, S_(stream)),
+    return kst(mt::qkv_rope_cvt(F32(in), ldin, U16(out), ldout, static_cast<uint16_t*>(out_bf16), ld_bf16,
+                                static_cast<float2*>(table), T, S, n_rot_heads, n_heads, hd, S_(stream)),
                "qkv_rope_cvt");
 }
 
@@ -129,8 +130,9 @@ int mt_k_attn_fwd(const void* qkv, int64_t ld, void* o, int64_t ldo, void* lse, 
 
 int mt_k_attn_bwd(const void* qkv, int64_t ld, const void* o, const void* dout, int64_t ldo, const void* lse,
                   void* dsum, void* dqkv, int64_t ldd, int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t hd,
-                  void* stream) {
-    mt::AttnBwdArgs a{U16(qkv), ld, U16(o), U16(dout), ldo, F32(lse), F32(dsum), U16(dqkv), ldd, B, S, Hq, Hkv, hd};
+                  const void* qk_bf16, int64_t ld_bf16, void* stream) {
+    mt::AttnBwdArgs a{U16(qkv), ld, U16(o), U16(dout), ldo, F32(lse), F32(dsum), U16(dqkv), ldd, B, S, Hq, Hkv, hd,
+                      static_cast<const uint16_t*>(qk_bf16), ld_bf16};
     return kst(mt::attn_bwd(a, S_(stream)), "attn_bwd");
 }
 

@@ -502,6 +502,326 @@ __global__ __launch_bounds__(256, 2) void attn_fwd2_k(AttnArgs a, int n_qt) {
     }
 }
 
+// ------------------------------------- backward, direct-load forms -----
+// Offsets of the DMA chunks of a 64-row tile: instruction i of wave w fills
+// tile chunks (4 i + w) * 64 + lane with the logical chunk the swizzle puts
+// there, from rows that are ld elements apart.
+template <int HD, int NI>
+__device__ __forceinline__ void tile_offsets(uint32_t (&off)[NI], int wave, int lane, int64_t ld) {
+    constexpr int NCH = HD / 8;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int p = (4 * i + wave) * 64 + lane;
+        const int row = p / NCH;
+        const int lc = (p % NCH) ^ aswz<HD>(row);
+        off[i] = uint32_t((int64_t(row) * ld + lc * 8) * 2);
+    }
+}
+template <int NI>
+__device__ __forceinline__ void tile_issue(i32x4_t rs, const uint32_t (&off)[NI], uint32_t rowoff, uint32_t lds,
+                                           int wave) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+        dma16(rs, __builtin_amdgcn_readfirstlane(lds + uint32_t((4 * i + wave) * 1024)), off[i] + rowoff);
+}
+// Row fragment (row, logical chunk) of a swizzled tile.
+template <int HD>
+__device__ __forceinline__ uint4 tile_row(const uint4* t, int row, int ch) {
+    return t[row * (HD / 8) + (ch ^ aswz<HD>(row))];
+}
+// Transposed fragment: 8 elements of column (32 dt + lane % 32), rows
+// 32 t + 16 s2 + 4 hh + {0..3} and + 8 + {0..3}, the key/query permutation of
+// the accumulator layout (the lane addresses one 8-byte piece of its group's
+// four rows; ds_read_b64_tr_b16 hands lane i column i of them).
+template <int HD>
+__device__ __forceinline__ bf16x8_t tile_colT(const uint4* t, int dt, int tt, int s2, int lane) {
+    constexpr int RB = HD / 8 * 16;
+    const int j = lane & 15, g16 = (lane >> 4) & 1, hh = lane >> 5;
+    const int col = 32 * dt + 16 * g16 + 4 * (j & 3);
+    const char* base = reinterpret_cast<const char*>(t);
+    uint2 r[2];
+#pragma unroll
+    for (int e2 = 0; e2 < 2; ++e2) {
+        const int row = 32 * tt + 16 * s2 + 8 * e2 + 4 * hh + (j >> 2);
+        const int off = row * RB + (((col >> 3) ^ aswz<HD>(row)) * 16) + (col & 7) * 2;
+        const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(lds_ptr_t)(base + off));
+        r[e2] = __builtin_bit_cast(uint2, v);
+    }
+    return as_bf16x8(make_uint4(r[0].x, r[0].y, r[1].x, r[1].y));
+}
+
+// dQ: block = 4 waves x 32 queries of one (b, h); key tiles of 64 staged as
+// fp16 K rows (scores), bf16 K (read transposed for dQ) and bf16 V rows.
+template <int HD>
+__global__ __launch_bounds__(256) void attn_dq2_k(AttnBwdArgs a, int n_qt) {
+    constexpr int NS = HD / 16, ND = HD / 32, NCH = HD / 8;
+    constexpr int TILE = BKV * NCH, NI = TILE / 256;
+    __shared__ uint4 Kh[2][TILE];
+    __shared__ uint4 Kb[2][TILE];
+    __shared__ uint4 Vs[2][TILE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hh = lane >> 5, c = lane & 31;
+    const int qt = n_qt - 1 - int(blockIdx.x % n_qt);
+    const int bh = int(blockIdx.x / n_qt);
+    const int h = bh % a.Hq, b = bh / a.Hq;
+    const int hk = h / (a.Hq / a.Hkv);
+    const int S = a.S;
+    const int q0 = qt * 128, qw = q0 + wave * 32, q = qw + c;
+    const uint16_t* base = a.qkv + int64_t(b) * S * a.ld;
+    const uint16_t* bbase = a.qkb + int64_t(b) * S * a.ldb;
+    const uint16_t* dbase = a.dout + int64_t(b) * S * a.ldo;
+
+    f16x8_t qf[NS];
+    bf16x8_t dof[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        uint4 v = make_uint4(0, 0, 0, 0), w = v;
+        if (q < S) {
+            v = *reinterpret_cast<const uint4*>(base + int64_t(q) * a.ld + h * HD + (2 * s + hh) * 8);
+            w = *reinterpret_cast<const uint4*>(dbase + int64_t(q) * a.ldo + h * HD + (2 * s + hh) * 8);
+        }
+        qf[s] = as_f16x8(v);
+        dof[s] = as_bf16x8(w);
+    }
+    const int64_t st_off = (int64_t(b) * a.Hq + h) * S;
+    const float lse2 = q < S ? a.lse[st_off + q] * LOG2E : 0.f;
+    const float dq_d = q < S ? a.dsum[st_off + q] : 0.f;
+
+    const i32x4_t rkh = make_rsrc(base + (a.Hq + hk) * HD, uint32_t((int64_t(S - 1) * a.ld + HD) * 2));
+    const i32x4_t rv = make_rsrc(base + (a.Hq + a.Hkv + hk) * HD, uint32_t((int64_t(S - 1) * a.ld + HD) * 2));
+    const i32x4_t rkb = make_rsrc(bbase + (a.Hq + hk) * HD, uint32_t((int64_t(S - 1) * a.ldb + HD) * 2));
+    uint32_t offa[NI], offb[NI];
+    tile_offsets<HD>(offa, wave, lane, a.ld);
+    tile_offsets<HD>(offb, wave, lane, a.ldb);
+    auto issue = [&](int k0, int buf) {
+        tile_issue(rkh, offa, uint32_t(int64_t(k0) * a.ld * 2), lds_addr(&Kh[buf][0]), wave);
+        tile_issue(rv, offa, uint32_t(int64_t(k0) * a.ld * 2), lds_addr(&Vs[buf][0]), wave);
+        tile_issue(rkb, offb, uint32_t(int64_t(k0) * a.ldb * 2), lds_addr(&Kb[buf][0]), wave);
+    };
+
+    f32x16_t acc[ND];
+#pragma unroll
+    for (int i = 0; i < ND; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+    const float sc = LOG2E * rsqrtf(float(HD));
+
+    const int k_end = min(S, q0 + 128);
+    const int nkb = (k_end + BKV - 1) / BKV;
+    issue(0, 0);
+    barrier_tile();
+    for (int kb = 0; kb < nkb; ++kb) {
+        const int cur = kb & 1;
+        const int k0 = kb * BKV;
+        if (kb + 1 < nkb) issue(k0 + BKV, cur ^ 1);
+        if (k0 <= qw + 31) {
+            f32x16_t st[2], dp[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) { st[t][r] = 0.f; dp[t][r] = 0.f; }
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    st[t] = MFMA32H(as_f16x8(tile_row<HD>(Kh[cur], 32 * t + c, 2 * s + hh)), qf[s], st[t]);
+                    dp[t] = MFMA32(as_bf16x8(tile_row<HD>(Vs[cur], 32 * t + c, 2 * s + hh)), dof[s], dp[t]);
+                }
+            }
+            bf16x8_t dsb[2][2];
+            const bool full = k0 + BKV - 1 <= qw && k0 + BKV <= S;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    float tmp[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int r = 8 * s2 + j;
+                        float p = ex2(fmaf(st[t][r], sc, -lse2));
+                        if (!full) {
+                            const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
+                            if (key > q || key >= S) p = 0.f;
+                        }
+                        tmp[j] = p * (dp[t][r] - dq_d);
+                    }
+                    dsb[t][s2] = pack_b(tmp);
+                }
+#pragma unroll
+            for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2)
+                        acc[dt] = MFMA32(tile_colT<HD>(Kb[cur], dt, t, s2, lane), dsb[t][s2], acc[dt]);
+        }
+        barrier_tile();
+    }
+    if (q < S) {
+        const float scale = rsqrtf(float(HD));
+        uint16_t* row = a.dqkv + (int64_t(b) * S + q) * a.ldd + h * HD;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = 32 * dt + 8 * g + 4 * hh;
+                *reinterpret_cast<uint2*>(row + d) =
+                    make_uint2(pack2(acc[dt][4 * g] * scale, acc[dt][4 * g + 1] * scale),
+                               pack2(acc[dt][4 * g + 2] * scale, acc[dt][4 * g + 3] * scale));
+            }
+    }
+}
+
+// dK, dV: block = 4 waves x 32 keys of one (b, kv head); query tiles of 64
+// over the group's heads, staged as fp16 Q rows (scores), bf16 Q (read
+// transposed for dK) and bf16 dO (rows for dP, transposed for dV).
+template <int HD>
+__global__ __launch_bounds__(256) void attn_dkdv2_k(AttnBwdArgs a, int n_kt) {
+    constexpr int NS = HD / 16, ND = HD / 32, NCH = HD / 8;
+    constexpr int TILE = BKV * NCH, NI = TILE / 256;
+    __shared__ uint4 Qh[2][TILE];
+    __shared__ uint4 Qb[2][TILE];
+    __shared__ uint4 Ds[2][TILE];
+    __shared__ float Ls[2][BKV], Dd[2][BKV];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hh = lane >> 5, c = lane & 31;
+    const int kt = int(blockIdx.x % n_kt);
+    const int bk = int(blockIdx.x / n_kt);
+    const int hk = bk % a.Hkv, b = bk / a.Hkv;
+    const int G = a.Hq / a.Hkv;
+    const int S = a.S;
+    const int k0 = kt * 128, kw = k0 + wave * 32, key = kw + c;
+    const uint16_t* base = a.qkv + int64_t(b) * S * a.ld;
+    const uint16_t* bbase = a.qkb + int64_t(b) * S * a.ldb;
+    const uint16_t* dbase = a.dout + int64_t(b) * S * a.ldo;
+    const int kcol = (a.Hq + hk) * HD, vcol = (a.Hq + a.Hkv + hk) * HD;
+
+    f16x8_t kf[NS];
+    bf16x8_t vf[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        uint4 v = make_uint4(0, 0, 0, 0), w = v;
+        if (key < S) {
+            v = *reinterpret_cast<const uint4*>(base + int64_t(key) * a.ld + kcol + (2 * s + hh) * 8);
+            w = *reinterpret_cast<const uint4*>(base + int64_t(key) * a.ld + vcol + (2 * s + hh) * 8);
+        }
+        kf[s] = as_f16x8(v);
+        vf[s] = as_bf16x8(w);
+    }
+
+    uint32_t offa[NI], offb[NI], offd[NI];
+    tile_offsets<HD>(offa, wave, lane, a.ld);
+    tile_offsets<HD>(offb, wave, lane, a.ldb);
+    tile_offsets<HD>(offd, wave, lane, a.ldo);
+    const uint32_t exa = uint32_t((int64_t(S - 1) * a.ld + HD) * 2);
+    const uint32_t exb = uint32_t((int64_t(S - 1) * a.ldb + HD) * 2);
+    const uint32_t exd = uint32_t((int64_t(S - 1) * a.ldo + HD) * 2);
+    float lreg = 0.f, dreg = 0.f;
+    auto issue = [&](int hq, int q0, int buf) {
+        tile_issue(make_rsrc(base + hq * HD, exa), offa, uint32_t(int64_t(q0) * a.ld * 2), lds_addr(&Qh[buf][0]),
+                   wave);
+        tile_issue(make_rsrc(bbase + hq * HD, exb), offb, uint32_t(int64_t(q0) * a.ldb * 2),
+                   lds_addr(&Qb[buf][0]), wave);
+        tile_issue(make_rsrc(dbase + hq * HD, exd), offd, uint32_t(int64_t(q0) * a.ldo * 2),
+                   lds_addr(&Ds[buf][0]), wave);
+        if (tid < BKV) {
+            const int64_t off = (int64_t(b) * a.Hq + hq) * S;
+            const int qq = q0 + tid;
+            lreg = qq < S ? a.lse[off + qq] * LOG2E : 0.f;
+            dreg = qq < S ? a.dsum[off + qq] : 0.f;
+        }
+    };
+
+    f32x16_t dk[ND], dv[ND];
+#pragma unroll
+    for (int i = 0; i < ND; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { dk[i][r] = 0.f; dv[i][r] = 0.f; }
+    const float sc = LOG2E * rsqrtf(float(HD));
+
+    const int qb0 = k0 / BKV;
+    const int nqb = (S + BKV - 1) / BKV - qb0;  // per head
+    const int total = nqb * G;
+    if (total > 0) {
+        issue(hk * G, qb0 * BKV, 0);
+        if (tid < BKV) {
+            Ls[0][tid] = lreg;
+            Dd[0][tid] = dreg;
+        }
+    }
+    barrier_tile();
+    for (int it = 0; it < total; ++it) {
+        const int cur = it & 1;
+        const int q0 = (qb0 + it % nqb) * BKV;
+        if (it + 1 < total) issue(hk * G + (it + 1) / nqb, (qb0 + (it + 1) % nqb) * BKV, cur ^ 1);
+        if (kw <= q0 + BKV - 1) {
+            f32x16_t st[2], dp[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) { st[t][r] = 0.f; dp[t][r] = 0.f; }
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    st[t] = MFMA32H(as_f16x8(tile_row<HD>(Qh[cur], 32 * t + c, 2 * s + hh)), kf[s], st[t]);
+                    dp[t] = MFMA32(as_bf16x8(tile_row<HD>(Ds[cur], 32 * t + c, 2 * s + hh)), vf[s], dp[t]);
+                }
+            }
+            bf16x8_t pb[2][2], dsb[2][2];
+            const bool full = kw + 31 <= q0 && q0 + BKV <= S && kw + 32 <= S;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    float tp[8], td[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int r = 8 * s2 + j;
+                        const int ql = 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
+                        float p = ex2(fmaf(st[t][r], sc, -Ls[cur][ql]));
+                        if (!full) {
+                            const int qq = q0 + ql;
+                            if (key > qq || qq >= S || key >= S) p = 0.f;
+                        }
+                        tp[j] = p;
+                        td[j] = p * (dp[t][r] - Dd[cur][ql]);
+                    }
+                    pb[t][s2] = pack_b(tp);
+                    dsb[t][s2] = pack_b(td);
+                }
+#pragma unroll
+            for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        dv[dt] = MFMA32(tile_colT<HD>(Ds[cur], dt, t, s2, lane), pb[t][s2], dv[dt]);
+                        dk[dt] = MFMA32(tile_colT<HD>(Qb[cur], dt, t, s2, lane), dsb[t][s2], dk[dt]);
+                    }
+        }
+        if (it + 1 < total && tid < BKV) {
+            Ls[cur ^ 1][tid] = lreg;
+            Dd[cur ^ 1][tid] = dreg;
+        }
+        barrier_tile();
+    }
+    if (key < S) {
+        const float scale = rsqrtf(float(HD));
+        uint16_t* row = a.dqkv + (int64_t(b) * S + key) * a.ldd;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = 32 * dt + 8 * g + 4 * hh;
+                *reinterpret_cast<uint2*>(row + kcol + d) =
+                    make_uint2(pack2(dk[dt][4 * g] * scale, dk[dt][4 * g + 1] * scale),
+                               pack2(dk[dt][4 * g + 2] * scale, dk[dt][4 * g + 3] * scale));
+                *reinterpret_cast<uint2*>(row + vcol + d) =
+                    make_uint2(pack2(dv[dt][4 * g], dv[dt][4 * g + 1]), pack2(dv[dt][4 * g + 2], dv[dt][4 * g + 3]));
+            }
+    }
+}
+
 // ------------------------------------------------- D = rowsum(dO * O) -----
 template <int HD>
 __global__ void attn_dsum_k(AttnBwdArgs a) {
@@ -841,6 +1161,22 @@ hipError_t attn_bwd(const AttnBwdArgs& a, hipStream_t s) {
     const int n_kt = (a.S + 127) / 128;
     const dim3 gq(unsigned(int64_t(n_qt) * a.B * a.Hq));
     const dim3 gk(unsigned(int64_t(n_kt) * a.B * a.Hkv));
+    const int64_t lim = int64_t(1) << 32;  // 32-bit buffer extents of one sequence's rows
+    const bool direct = a.qkb && a.ldb >= int64_t(a.Hq + a.Hkv) * a.hd && (a.ldb & 7) == 0 &&
+                        int64_t(a.S) * a.ld * 2 < lim && int64_t(a.S) * a.ldb * 2 < lim &&
+                        int64_t(a.S) * a.ldo * 2 < lim;
+    if (direct) {
+        if (a.hd == 128) {
+            attn_dsum_k<128><<<nb, 256, 0, s>>>(a);
+            attn_dq2_k<128><<<gq, 256, 0, s>>>(a, n_qt);
+            attn_dkdv2_k<128><<<gk, 256, 0, s>>>(a, n_kt);
+        } else {
+            attn_dsum_k<64><<<nb, 256, 0, s>>>(a);
+            attn_dq2_k<64><<<gq, 256, 0, s>>>(a, n_qt);
+            attn_dkdv2_k<64><<<gk, 256, 0, s>>>(a, n_kt);
+        }
+        return hipGetLastError();
+    }
     if (a.hd == 128) {
         attn_dsum_k<128><<<nb, 256, 0, s>>>(a);
         attn_dq_k<128><<<gq, 256, 0, s>>>(a, n_qt);

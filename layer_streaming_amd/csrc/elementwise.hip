@@ -201,8 +201,8 @@ __global__ void rope_apply_k(uint16_t* __restrict__ qkv, int64_t ld, const float
 // Rotary embedding on the fp32 output of the QKV projection, written as the
 // 2-byte operands of attention: rotated q and k heads in fp16, v in bf16.
 __global__ void qkv_rope_cvt_k(const float* __restrict__ in, int64_t ldin, uint16_t* __restrict__ out,
-                               int64_t ldout, const float2* __restrict__ tab, int T, int S, int nrot, int nall,
-                               int hd) {
+                               int64_t ldout, uint16_t* __restrict__ outb, int64_t ldb,
+                               const float2* __restrict__ tab, int T, int S, int nrot, int nall, int hd) {
     const int half = hd >> 1, per_head = half >> 3;
     const int64_t n_rot_items = int64_t(T) * nrot * per_head;
     const int64_t n_v_items = int64_t(T) * (nall - nrot) * (hd >> 3);
@@ -231,6 +231,11 @@ __global__ void qkv_rope_cvt_k(const float* __restrict__ in, int64_t ldin, uint1
         uint16_t* dst = out + int64_t(t) * ldout + int64_t(h) * hd + e8 * 8;
         *reinterpret_cast<uint4*>(dst) = pack8h(ol);
         *reinterpret_cast<uint4*>(dst + half) = pack8h(oh);
+        if (outb) {  // bf16 copy of the rotated q / k for the gradient products
+            uint16_t* db = outb + int64_t(t) * ldb + int64_t(h) * hd + e8 * 8;
+            *reinterpret_cast<uint4*>(db) = pack8(ol);
+            *reinterpret_cast<uint4*>(db + half) = pack8(oh);
+        }
     } else if (i < n_rot_items + n_v_items) {
         const int64_t j = i - n_rot_items;
         const int vw = (nall - nrot) * hd;
@@ -511,14 +516,16 @@ hipError_t rmsnorm_fwd(const void* x, bool x_f32, const uint16_t* gamma, uint16_
     return hipGetLastError();
 }
 
-hipError_t qkv_rope_cvt(const float* in, int64_t ldin, uint16_t* out, int64_t ldout, const float2* tab, int T,
-                        int S, int n_rot_heads, int n_heads, int hd, hipStream_t s) {
+hipError_t qkv_rope_cvt(const float* in, int64_t ldin, uint16_t* out, int64_t ldout, uint16_t* outb, int64_t ldb,
+                        const float2* tab, int T, int S, int n_rot_heads, int n_heads, int hd, hipStream_t s) {
     if (T < 0 || S <= 0 || n_rot_heads < 0 || n_heads < n_rot_heads || (hd & 15) || (ldin & 3) || (ldout & 7) ||
         ldin < int64_t(n_heads) * hd || ldout < int64_t(n_heads) * hd || !al16(in) || !al16(out))
         return hipErrorInvalidValue;
+    if (outb && ((ldb & 7) || ldb < int64_t(n_rot_heads) * hd || !al16(outb))) return hipErrorInvalidValue;
     if (T == 0) return hipSuccess;
     const int64_t n = int64_t(T) * n_rot_heads * (hd / 16) + int64_t(T) * (n_heads - n_rot_heads) * (hd / 8);
-    qkv_rope_cvt_k<<<blocks(n, 256), 256, 0, s>>>(in, ldin, out, ldout, tab, T, S, n_rot_heads, n_heads, hd);
+    qkv_rope_cvt_k<<<blocks(n, 256), 256, 0, s>>>(in, ldin, out, ldout, outb, ldb, tab, T, S, n_rot_heads, n_heads,
+                                                   hd);
     return hipGetLastError();
 }
 

@@ -167,6 +167,7 @@ void plan_workspace(const Layout& lay, const mt_options& o, Carver& cv, Workspac
     ws.h1 = cv.take<float>(td * 2);
     ws.n2 = cv.take<uint16_t>(td);
     ws.qkv = cv.take<uint16_t>(uint64_t(T) * nqkv * 2);
+    ws.qkb = cv.take<uint16_t>(uint64_t(T) * (sh.n_heads + sh.n_kv_heads) * sh.head_dim * 2);
     ws.dqkv = cv.take<uint16_t>(uint64_t(T) * nqkv * 2);
     ws.o = cv.take<uint16_t>(uint64_t(T) * nq * 2);
     ws.dout = cv.take<uint16_t>(uint64_t(T) * nq * 2);
@@ -977,8 +978,10 @@ hipError_t Ctx::fwd_layer(const LayerView& w, const uint16_t* x, uint16_t* y, in
         return gemm(GEMM_NT, EPI_F32_F16IN, a, s);
     }));
     HIPR(site(S_ROPE_FWD, [&] {
-        return qkv_rope_cvt(ws.qkv32, nqkv, ws.qkv, nqkv, ws.rope_tab, T, S, sh.n_heads + sh.n_kv_heads,
-                            sh.n_heads + 2 * sh.n_kv_heads, sh.head_dim, s);
+        // The recompute (no y) feeds the backward: it also keeps q, k in bf16.
+        const int64_t nr = int64_t(sh.n_heads + sh.n_kv_heads) * sh.head_dim;
+        return qkv_rope_cvt(ws.qkv32, nqkv, ws.qkv, nqkv, need_y ? nullptr : ws.qkb, nr, ws.rope_tab, T, S,
+                            sh.n_heads + sh.n_kv_heads, sh.n_heads + 2 * sh.n_kv_heads, sh.head_dim, s);
     }));
     HIPR(site(S_ATTN_FWD, [&] {
         AttnArgs a{ws.qkv, nqkv, ws.o, nq, ws.lse, B, S, sh.n_heads, sh.n_kv_heads, sh.head_dim};
@@ -1030,7 +1033,8 @@ hipError_t Ctx::bwd_layer(const LayerView& w, const LayerView& g, const uint16_t
     HIPR(site(S_GEMM_O_DW, [&] { return gemm_tn_t(ws.dh1, d, ws.o, nq, g.wo, nq, d, nq, T); }));
     HIPR(site(S_ATTN_BWD, [&] {
         AttnBwdArgs a{ws.qkv, nqkv, ws.o, ws.dout, nq, ws.lse, ws.dsum, ws.dqkv, nqkv,
-                      B, S, sh.n_heads, sh.n_kv_heads, sh.head_dim};
+                      B, S, sh.n_heads, sh.n_kv_heads, sh.head_dim,
+                      ws.qkb, int64_t(sh.n_heads + sh.n_kv_heads) * sh.head_dim};
         return attn_bwd(a, s);
     }));
     HIPR(site(S_ROPE_BWD, [&] {

@@ -45,6 +45,7 @@ struct Workspace {
     std::vector<uint16_t*> xc;
     uint16_t* ckpt_dev = nullptr;  // [L+1][maxT x d] when checkpoints stay on the GPU
     uint16_t *n1, *qkv, *o, *n2, *gu, *m;
+    uint16_t* qkb;  // bf16 copy of the rotated q and k (recompute), for the attention backward
     float* h1;  // residual stream inside a layer, kept in fp32
     // logit path: fp16 copies of n1 and Wqkv, fp32 QKV projection before RoPE
     uint16_t *n1h, *w16;

@@ -62,8 +62,8 @@ hipError_t rope_apply(uint16_t* qkv, int64_t ld, const float2* tab, int T, int S
 // From the fp32 QKV projection in [T x ldin] (n_heads heads of hd): rotate the
 // first n_rot_heads (q and k) and write them as fp16, the rest (v) as bf16,
 // into out [T x ldout] (the attention operand buffer).
-hipError_t qkv_rope_cvt(const float* in, int64_t ldin, uint16_t* out, int64_t ldout, const float2* tab, int T,
-                        int S, int n_rot_heads, int n_heads, int hd, hipStream_t s);
+hipError_t qkv_rope_cvt(const float* in, int64_t ldin, uint16_t* out, int64_t ldout, uint16_t* outb, int64_t ldb,
+                        const float2* tab, int T, int S, int n_rot_heads, int n_heads, int hd, hipStream_t s);
 // Elementwise bf16 -> fp16 (n a multiple of 8).
 hipError_t bf16_to_f16(const uint16_t* in, uint16_t* out, int64_t n, hipStream_t s);
 
@@ -91,6 +91,10 @@ struct AttnBwdArgs {
     float* dsum;                // scratch [B x Hq x S]: rowsum(dO * O)
     uint16_t* dqkv; int64_t ldd; // output, same column layout as qkv
     int B, S, Hq, Hkv, hd;
+    // Optional bf16 copy of the rotated q and k, [B*S x (Hq+Hkv)*hd] (k after
+    // the Hq query heads), for the gradient products; null: the kernels round
+    // the fp16 q and k to bf16 themselves (staging through registers).
+    const uint16_t* qkb = nullptr; int64_t ldb = 0;
 };
 hipError_t attn_bwd(const AttnBwdArgs& a, hipStream_t s);
 

@@ -98,13 +98,13 @@ _SIGS = {
     "mt_k_attn_fwd": (C.c_int, [_P, C.c_int64, _P, C.c_int64, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                 C.c_int32, _P]),
     "mt_k_attn_bwd": (C.c_int, [_P, C.c_int64, _P, _P, C.c_int64, _P, _P, _P, C.c_int64, C.c_int32, C.c_int32,
-                                C.c_int32, C.c_int32, C.c_int32, _P]),
+                                C.c_int32, C.c_int32, C.c_int32, _P, C.c_int64, _P]),
     "mt_k_ce": (C.c_int, [_P, _P, _P, _P, C.c_int32, C.c_int32, C.c_float, _P]),
     "mt_k_mean": (C.c_int, [_P, _P, C.c_int32, _P]),
     "mt_k_f32_to_bf16": (C.c_int, [_P, _P, C.c_int64, _P]),
     "mt_k_transpose16": (C.c_int, [_P, C.c_int64, _P, C.c_int64, C.c_int32, C.c_int32, _P]),
-    "mt_k_qkv_rope_cvt": (C.c_int, [_P, C.c_int64, _P, C.c_int64, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
-                                    C.c_int32, C.c_float, _P]),
+    "mt_k_qkv_rope_cvt": (C.c_int, [_P, C.c_int64, _P, C.c_int64, _P, C.c_int64, _P, C.c_int32, C.c_int32,
+                                    C.c_int32, C.c_int32, C.c_int32, C.c_float, _P]),
     "mt_k_bf16_to_f16": (C.c_int, [_P, _P, C.c_int64, _P]),
     "mt_host_adam": (C.c_int, [_P, _P, _P, _P, _P, _P, C.c_int64, C.c_int64, C.c_float, C.c_float, C.c_float,
                                C.c_float, C.c_int32]),

@@ -16,6 +16,7 @@ import pytest
 
 from layer_streaming_amd import synth
 from oracle import block, step as ostep
+from oracle.bf16 import bf16_bits
 from tests.gpu_util import assert_close, attn_inputs, dev_bits, dev_zeros_bits, host_f32, log, widen
 
 pytestmark = pytest.mark.gpu
@@ -88,8 +89,10 @@ def test_attention_long_context_sampled():
     d_dqkv = dev_zeros_bits((S, ld))
     s = torch.cuda.current_stream().cuda_stream
     mt.check(mt.lib.mt_k_attn_fwd(d_qkv.data_ptr(), ld, d_o.data_ptr(), nq, lse.data_ptr(), B, S, Hq, Hkv, hd, s))
+    nr = (Hq + Hkv) * hd  # the bf16 copy of q, k the engine's recompute writes
+    d_qkb = dev_bits(widen(bf16_bits(qkv[:, :nr])))
     mt.check(mt.lib.mt_k_attn_bwd(d_qkv.data_ptr(), ld, d_o.data_ptr(), d_do.data_ptr(), nq, lse.data_ptr(),
-                                  dsum.data_ptr(), d_dqkv.data_ptr(), ld, B, S, Hq, Hkv, hd, s))
+                                  dsum.data_ptr(), d_dqkv.data_ptr(), ld, B, S, Hq, Hkv, hd, d_qkb.data_ptr(), nr, s))
     torch.cuda.synchronize()
     o_g = host_f32(d_o).reshape(S, Hq, hd)
     g_g = host_f32(d_dqkv).reshape(S, Hq + 2 * Hkv, hd)

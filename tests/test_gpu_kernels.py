@@ -9,7 +9,8 @@ import pytest
 from layer_streaming_amd import synth
 from oracle import block
 from oracle.bf16 import bf16_bits
-from tests.gpu_util import assert_close, attn_inputs, dev_bits, dev_f16, dev_zeros_bits, host_f16, host_f32, log
+from tests.gpu_util import (assert_close, attn_inputs, dev_bits, dev_f16, dev_zeros_bits, host_f16, host_f32, log,
+                            widen)
 
 pytestmark = pytest.mark.gpu
 
@@ -199,8 +200,9 @@ def test_rope_long_positions():
 
 @pytest.mark.parametrize("hd,S", [(64, 100), (128, 100), (128, 131072)])
 def test_qkv_rope_cvt(hd, S):
-    """Forward RoPE on the f32 projection: q, k rotated and stored fp16, v
-    rounded to bf16 (bit-exact against round-to-nearest-even)."""
+    """Forward RoPE on the f32 projection: q, k rotated and stored fp16 (and
+    bf16 in a second buffer), v rounded to bf16 (bit-exact against
+    round-to-nearest-even)."""
     hq, hkv = (4, 2) if S < 1000 else (1, 1)
     B = 2 if S < 1000 else 1
     log(f"qkv_rope_cvt hd={hd} S={S}")
@@ -209,17 +211,25 @@ def test_qkv_rope_cvt(hd, S):
     x = RNG.standard_normal((T, ld)).astype(np.float32)
     dx = torch.from_numpy(x).cuda()
     out = dev_zeros_bits((T, ld))
-    tab = torch.zeros(S * hd, dtype=torch.float32, device="cuda")
-    mt.check(mt.lib.mt_k_qkv_rope_cvt(dx.data_ptr(), ld, out.data_ptr(), ld, tab.data_ptr(), T, S, hq + hkv,
-                                      hq + 2 * hkv, hd, 10000.0, _stream()))
-    _sync()
     nr = (hq + hkv) * hd
+    outb = dev_zeros_bits((T, nr))
+    tab = torch.zeros(S * hd, dtype=torch.float32, device="cuda")
+    mt.check(mt.lib.mt_k_qkv_rope_cvt(dx.data_ptr(), ld, out.data_ptr(), ld, outb.data_ptr(), nr, tab.data_ptr(), T,
+                                      S, hq + hkv, hq + 2 * hkv, hd, 10000.0, _stream()))
+    _sync()
     got_qk = host_f16(out)[:, :nr]
     rot = x[:, :nr].astype(np.float64).reshape(B, S, hq + hkv, hd)
     ref = block.rope_fwd(rot, 10000.0).reshape(T, nr)
     assert_close(got_qk, ref, "q, k (fp16)", tol=1e-3)
+    assert_close(host_f32(outb), ref, "q, k (bf16)", tol=5e-3)
     got_v = out.cpu().numpy().view(np.uint16)[:, nr:]
     np.testing.assert_array_equal(got_v, bf16_bits(x[:, nr:]))
+    # without the bf16 copy: same fp16 output
+    out2 = dev_zeros_bits((T, ld))
+    mt.check(mt.lib.mt_k_qkv_rope_cvt(dx.data_ptr(), ld, out2.data_ptr(), ld, None, 0, tab.data_ptr(), T, S,
+                                      hq + hkv, hq + 2 * hkv, hd, 10000.0, _stream()))
+    _sync()
+    assert torch.equal(out, out2)
 
 
 # ---------------------------------------------------------------- SwiGLU --
@@ -247,18 +257,22 @@ ATTN_CASES = [(2, 200, 4, 2, 64), (1, 300, 7, 1, 128), (2, 128, 4, 4, 128), (1, 
 
 
 @pytest.mark.parametrize("B,S,Hq,Hkv,hd", ATTN_CASES)
-def test_attention_fwd_bwd(B, S, Hq, Hkv, hd):
-    _attention_case(B, S, Hq, Hkv, hd, 1.0)
+@pytest.mark.parametrize("qkb", [True, False], ids=["direct", "staged"])
+def test_attention_fwd_bwd(B, S, Hq, Hkv, hd, qkb):
+    """Forward, then backward in both forms: tiles loaded straight into LDS
+    with the bf16 copy of q and k, or staged through registers rounding the
+    fp16 q and k."""
+    _attention_case(B, S, Hq, Hkv, hd, 1.0, qkb)
 
 
 def test_attention_sharp_logits():
     """q, k with std 2 (logits of std 4): a peaked softmax, where the logit
     path's rounding matters most."""
-    _attention_case(1, 700, 8, 2, 128, 2.0)
+    _attention_case(1, 700, 8, 2, 128, 2.0, True)
 
 
-def _attention_case(B, S, Hq, Hkv, hd, qk_std):
-    log(f"attention B={B} S={S} Hq={Hq} Hkv={Hkv} hd={hd} qk_std={qk_std}")
+def _attention_case(B, S, Hq, Hkv, hd, qk_std, with_qkb):
+    log(f"attention B={B} S={S} Hq={Hq} Hkv={Hkv} hd={hd} qk_std={qk_std} qkb={with_qkb}")
     T = B * S
     ld = (Hq + 2 * Hkv) * hd
     nq = Hq * hd
@@ -271,8 +285,11 @@ def _attention_case(B, S, Hq, Hkv, hd, qk_std):
     d_dqkv = dev_zeros_bits((T, ld))
     s = _stream()
     mt.check(mt.lib.mt_k_attn_fwd(d_qkv.data_ptr(), ld, d_o.data_ptr(), nq, lse.data_ptr(), B, S, Hq, Hkv, hd, s))
+    nr = (Hq + Hkv) * hd
+    d_qkb = dev_bits(widen(bf16_bits(qkv[:, :nr]))) if with_qkb else None
     mt.check(mt.lib.mt_k_attn_bwd(d_qkv.data_ptr(), ld, d_o.data_ptr(), d_do.data_ptr(), nq, lse.data_ptr(),
-                                  dsum.data_ptr(), d_dqkv.data_ptr(), ld, B, S, Hq, Hkv, hd, s))
+                                  dsum.data_ptr(), d_dqkv.data_ptr(), ld, B, S, Hq, Hkv, hd,
+                                  d_qkb.data_ptr() if with_qkb else None, nr if with_qkb else 0, s))
     _sync()
     x = qkv.astype(np.float64).reshape(B, S, Hq + 2 * Hkv, hd)
     q, k, v = x[:, :, :Hq], x[:, :, Hq:Hq + Hkv], x[:, :, Hq + Hkv:]
