@@ -41,6 +41,14 @@ SHAPES = {
                  batch=2, seq=128,
                  workload="tiny decoder, 2 layers, d_model 256, 4 heads x 64, ffn 688, vocab 1024, "
                           "batch 2 x seq 128"),
+    "long": dict(n_layers=8, d_model=3584, n_heads=28, n_kv_heads=4, head_dim=128, ffn_dim=18944, vocab=152064,
+                 batch=1, seq=131072,
+                 workload="long-context step: 8 layers of the 7B-shaped layer, batch 1 x seq 131072, causal, "
+                          "layer-streamed with host Adam"),
+    "70b_x4": dict(n_layers=4, d_model=8192, n_heads=64, n_kv_heads=8, head_dim=128, ffn_dim=28672, vocab=128256,
+                   batch=4, seq=2048,
+                   workload="70B-layer-shaped decoder, 4 layers, d_model 8192, 64q/8kv heads x 128, ffn 28672, "
+                            "vocab 128256, batch 4 x seq 2048, layer-streamed train step with host Adam"),
 }
 
 
@@ -54,8 +62,12 @@ TRAFFIC = {"sources": ["layer_streaming_amd/csrc/gemm_nt.hip", "layer_streaming_
            "fetch_bytes": 3317797202, "write_bytes": 638521504}
 
 
-def traffic_bytes():
+def traffic_bytes(config):
+    """Measured HBM bytes per gate|up launch: only for the shape and the
+    kernel sources the counters were taken on."""
     import hashlib
+    if config != "7b":
+        return None
     h = hashlib.sha256()
     try:
         for src in TRAFFIC["sources"]:
@@ -411,7 +423,8 @@ def main():
         achieved = fl[dom] / (avg_ms / 1e3) / 1e12
         out["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                           "traffic": traffic_bytes(), "avg_launch_ms": round(avg_ms, 4), "launches": n,
+                           "traffic": traffic_bytes(args.config), "avg_launch_ms": round(avg_ms, 4),
+                           "launches": n,
                            "flops_per_launch": fl[dom]}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(ctx, cfg, mt)
