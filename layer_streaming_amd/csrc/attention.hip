@@ -29,6 +29,9 @@ namespace {
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr int BKV = 64;  // keys (or queries) per staged tile
+#ifndef MT_ATTN_SPLIT
+#define MT_ATTN_SPLIT 0  // 1: dK and dV of the direct-load backward in two launches
+#endif
 
 #define MFMA32(a, b, c) __builtin_amdgcn_mfma_f32_32x32x16_bf16((a), (b), (c), 0, 0, 0)
 // 2^x on the hardware instruction alone: results below 2^-126 (probabilities
@@ -674,15 +677,19 @@ __global__ __launch_bounds__(256) void attn_dq2_k(AttnBwdArgs a, int n_qt) {
 
 // dK, dV: block = 4 waves x 32 keys of one (b, kv head); query tiles of 64
 // over the group's heads, staged as fp16 Q rows (scores), bf16 Q (read
-// transposed for dK) and bf16 dO (rows for dP, transposed for dV).
-template <int HD>
-__global__ __launch_bounds__(256) void attn_dkdv2_k(AttnBwdArgs a, int n_kt) {
+// transposed for dK) and bf16 dO (rows for dP, transposed for dV).  MODE 0
+// computes both; MODE 1 dK only and MODE 2 dV only (P and dO, no dP), for a
+// split into two launches with fewer registers each.
+template <int HD, int MODE>
+__global__ __launch_bounds__(256, MODE == 2 ? 2 : 1) void attn_dkdv2_k(AttnBwdArgs a, int n_kt) {
+    constexpr bool WK = MODE != 2, WV = MODE != 1;  // dK, dV wanted
     constexpr int NS = HD / 16, ND = HD / 32, NCH = HD / 8;
     constexpr int TILE = BKV * NCH, NI = TILE / 256;
     __shared__ uint4 Qh[2][TILE];
-    __shared__ uint4 Qb[2][TILE];
+    __shared__ uint4 Qb[WK ? 2 : 1][WK ? TILE : 1];
     __shared__ uint4 Ds[2][TILE];
-    __shared__ float Ls[2][BKV], Dd[2][BKV];
+    __shared__ __align__(16) float Ls[2][BKV];
+    __shared__ __align__(16) float Dd[2][BKV];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hh = lane >> 5, c = lane & 31;
@@ -698,21 +705,22 @@ __global__ __launch_bounds__(256) void attn_dkdv2_k(AttnBwdArgs a, int n_kt) {
     const int kcol = (a.Hq + hk) * HD, vcol = (a.Hq + a.Hkv + hk) * HD;
 
     f16x8_t kf[NS];
-    bf16x8_t vf[NS];
+    bf16x8_t vf[WK ? NS : 1];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-        uint4 v = make_uint4(0, 0, 0, 0), w = v;
-        if (key < S) {
-            v = *reinterpret_cast<const uint4*>(base + int64_t(key) * a.ld + kcol + (2 * s + hh) * 8);
-            w = *reinterpret_cast<const uint4*>(base + int64_t(key) * a.ld + vcol + (2 * s + hh) * 8);
-        }
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (key < S) v = *reinterpret_cast<const uint4*>(base + int64_t(key) * a.ld + kcol + (2 * s + hh) * 8);
         kf[s] = as_f16x8(v);
-        vf[s] = as_bf16x8(w);
+        if constexpr (WK) {
+            uint4 w = make_uint4(0, 0, 0, 0);
+            if (key < S) w = *reinterpret_cast<const uint4*>(base + int64_t(key) * a.ld + vcol + (2 * s + hh) * 8);
+            vf[s] = as_bf16x8(w);
+        }
     }
 
     uint32_t offa[NI], offb[NI], offd[NI];
     tile_offsets<HD>(offa, wave, lane, a.ld);
-    tile_offsets<HD>(offb, wave, lane, a.ldb);
+    if constexpr (WK) tile_offsets<HD>(offb, wave, lane, a.ldb);
     tile_offsets<HD>(offd, wave, lane, a.ldo);
     const uint32_t exa = uint32_t((int64_t(S - 1) * a.ld + HD) * 2);
     const uint32_t exb = uint32_t((int64_t(S - 1) * a.ldb + HD) * 2);
@@ -721,15 +729,16 @@ __global__ __launch_bounds__(256) void attn_dkdv2_k(AttnBwdArgs a, int n_kt) {
     auto issue = [&](int hq, int q0, int buf) {
         tile_issue(make_rsrc(base + hq * HD, exa), offa, uint32_t(int64_t(q0) * a.ld * 2), lds_addr(&Qh[buf][0]),
                    wave);
-        tile_issue(make_rsrc(bbase + hq * HD, exb), offb, uint32_t(int64_t(q0) * a.ldb * 2),
-                   lds_addr(&Qb[buf][0]), wave);
+        if constexpr (WK)
+            tile_issue(make_rsrc(bbase + hq * HD, exb), offb, uint32_t(int64_t(q0) * a.ldb * 2),
+                       lds_addr(&Qb[buf][0]), wave);
         tile_issue(make_rsrc(dbase + hq * HD, exd), offd, uint32_t(int64_t(q0) * a.ldo * 2),
                    lds_addr(&Ds[buf][0]), wave);
         if (tid < BKV) {
             const int64_t off = (int64_t(b) * a.Hq + hq) * S;
             const int qq = q0 + tid;
             lreg = qq < S ? a.lse[off + qq] * LOG2E : 0.f;
-            dreg = qq < S ? a.dsum[off + qq] : 0.f;
+            if constexpr (WK) dreg = qq < S ? a.dsum[off + qq] : 0.f;
         }
     };
 
@@ -764,7 +773,8 @@ __global__ __launch_bounds__(256) void attn_dkdv2_k(AttnBwdArgs a, int n_kt) {
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
                     st[t] = MFMA32H(as_f16x8(tile_row<HD>(Qh[cur], 32 * t + c, 2 * s + hh)), kf[s], st[t]);
-                    dp[t] = MFMA32(as_bf16x8(tile_row<HD>(Ds[cur], 32 * t + c, 2 * s + hh)), vf[s], dp[t]);
+                    if constexpr (WK)
+                        dp[t] = MFMA32(as_bf16x8(tile_row<HD>(Ds[cur], 32 * t + c, 2 * s + hh)), vf[s], dp[t]);
                 }
             }
             bf16x8_t pb[2][2], dsb[2][2];
@@ -775,19 +785,26 @@ __global__ __launch_bounds__(256) void attn_dkdv2_k(AttnBwdArgs a, int n_kt) {
                 for (int s2 = 0; s2 < 2; ++s2) {
                     float tp[8], td[8];
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const int r = 8 * s2 + j;
-                        const int ql = 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
-                        float p = ex2(fmaf(st[t][r], sc, -Ls[cur][ql]));
-                        if (!full) {
-                            const int qq = q0 + ql;
-                            if (key > qq || qq >= S || key >= S) p = 0.f;
+                    for (int g4 = 0; g4 < 2; ++g4) {
+                        // four consecutive queries' statistics in one 16-byte read each
+                        const int qb = 32 * t + 8 * (2 * s2 + g4) + 4 * hh;
+                        float lv[4], dv4[4];
+                        *reinterpret_cast<float4*>(lv) = *reinterpret_cast<const float4*>(&Ls[cur][qb]);
+                        if constexpr (WK) *reinterpret_cast<float4*>(dv4) = *reinterpret_cast<const float4*>(&Dd[cur][qb]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int j = 4 * g4 + e, r = 8 * s2 + j;
+                            float p = ex2(fmaf(st[t][r], sc, -lv[e]));
+                            if (!full) {
+                                const int qq = q0 + qb + e;
+                                if (key > qq || qq >= S || key >= S) p = 0.f;
+                            }
+                            tp[j] = p;
+                            if constexpr (WK) td[j] = p * (dp[t][r] - dv4[e]);
                         }
-                        tp[j] = p;
-                        td[j] = p * (dp[t][r] - Dd[cur][ql]);
                     }
-                    pb[t][s2] = pack_b(tp);
-                    dsb[t][s2] = pack_b(td);
+                    if constexpr (WV) pb[t][s2] = pack_b(tp);
+                    if constexpr (WK) dsb[t][s2] = pack_b(td);
                 }
 #pragma unroll
             for (int dt = 0; dt < ND; ++dt)
@@ -795,8 +812,9 @@ __global__ __launch_bounds__(256) void attn_dkdv2_k(AttnBwdArgs a, int n_kt) {
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
                     for (int s2 = 0; s2 < 2; ++s2) {
-                        dv[dt] = MFMA32(tile_colT<HD>(Ds[cur], dt, t, s2, lane), pb[t][s2], dv[dt]);
-                        dk[dt] = MFMA32(tile_colT<HD>(Qb[cur], dt, t, s2, lane), dsb[t][s2], dk[dt]);
+                        if constexpr (WV) dv[dt] = MFMA32(tile_colT<HD>(Ds[cur], dt, t, s2, lane), pb[t][s2], dv[dt]);
+                        if constexpr (WK)
+                            dk[dt] = MFMA32(tile_colT<HD>(Qb[cur], dt, t, s2, lane), dsb[t][s2], dk[dt]);
                     }
         }
         if (it + 1 < total && tid < BKV) {
@@ -813,10 +831,12 @@ __global__ __launch_bounds__(256) void attn_dkdv2_k(AttnBwdArgs a, int n_kt) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int d = 32 * dt + 8 * g + 4 * hh;
-                *reinterpret_cast<uint2*>(row + kcol + d) =
-                    make_uint2(pack2(dk[dt][4 * g] * scale, dk[dt][4 * g + 1] * scale),
-                               pack2(dk[dt][4 * g + 2] * scale, dk[dt][4 * g + 3] * scale));
-                *reinterpret_cast<uint2*>(row + vcol + d) =
+                if constexpr (WK)
+                    *reinterpret_cast<uint2*>(row + kcol + d) =
+                        make_uint2(pack2(dk[dt][4 * g] * scale, dk[dt][4 * g + 1] * scale),
+                                   pack2(dk[dt][4 * g + 2] * scale, dk[dt][4 * g + 3] * scale));
+                if constexpr (WV)
+                    *reinterpret_cast<uint2*>(row + vcol + d) =
                     make_uint2(pack2(dv[dt][4 * g], dv[dt][4 * g + 1]), pack2(dv[dt][4 * g + 2], dv[dt][4 * g + 3]));
             }
     }
@@ -1169,11 +1189,16 @@ hipError_t attn_bwd(const AttnBwdArgs& a, hipStream_t s) {
         if (a.hd == 128) {
             attn_dsum_k<128><<<nb, 256, 0, s>>>(a);
             attn_dq2_k<128><<<gq, 256, 0, s>>>(a, n_qt);
-            attn_dkdv2_k<128><<<gk, 256, 0, s>>>(a, n_kt);
+            if (MT_ATTN_SPLIT) {
+                attn_dkdv2_k<128, 1><<<gk, 256, 0, s>>>(a, n_kt);
+                attn_dkdv2_k<128, 2><<<gk, 256, 0, s>>>(a, n_kt);
+            } else {
+                attn_dkdv2_k<128, 0><<<gk, 256, 0, s>>>(a, n_kt);
+            }
         } else {
             attn_dsum_k<64><<<nb, 256, 0, s>>>(a);
             attn_dq2_k<64><<<gq, 256, 0, s>>>(a, n_qt);
-            attn_dkdv2_k<64><<<gk, 256, 0, s>>>(a, n_kt);
+            attn_dkdv2_k<64, 0><<<gk, 256, 0, s>>>(a, n_kt);
         }
         return hipGetLastError();
     }
