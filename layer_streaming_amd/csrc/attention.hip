@@ -29,9 +29,6 @@ namespace {
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr int BKV = 64;  // keys (or queries) per staged tile
-#ifndef MT_ATTN_AGPR
-#define MT_ATTN_AGPR 1
-#endif
 #ifndef MT_ATTN_SPLIT
 #define MT_ATTN_SPLIT 0  // 1: dK and dV of the direct-load backward in two launches
 #endif
@@ -688,12 +685,6 @@ __global__ __launch_bounds__(256, MODE == 2 ? 2 : 1) void attn_dkdv2_k(AttnBwdAr
     constexpr bool WK = MODE != 2, WV = MODE != 1;  // dK, dV wanted
     constexpr int NS = HD / 16, ND = HD / 32, NCH = HD / 8;
     constexpr int TILE = BKV * NCH, NI = TILE / 256;
-#if MT_ATTN_AGPR
-    {  // an accumulation-register operand: lets the compiler keep MFMA accumulators there
-        float z = 0.f;
-        asm volatile("; acc" : "+a"(z));
-    }
-#endif
     __shared__ uint4 Qh[2][TILE];
     __shared__ uint4 Qb[WK ? 2 : 1][WK ? TILE : 1];
     __shared__ uint4 Ds[2][TILE];
