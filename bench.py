@@ -167,6 +167,50 @@ def traffic_probe(torch, mt, cfg):
     log("traffic probe done")
 
 
+def attention_probe(torch, mt, cfg, S):
+    """The attention kernels alone at one sequence of length S with the
+    workload's heads: forward and backward three times each on seeded
+    synthetic q, k (fp16, with the bf16 copy the recompute writes), v, dO
+    (bf16); HIP-event times and TFLOP/s (causal: 4 Hq hd S(S+1)/2 for the
+    forward, 2.5 times that for the backward)."""
+    Hq, Hkv, hd = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    ld, nq, nr = (Hq + 2 * Hkv) * hd, Hq * hd, (Hq + Hkv) * hd
+    g = torch.Generator(device="cpu").manual_seed(0)
+    qkv = torch.randn(S, ld, generator=g).to(torch.float16).cuda().view(torch.int16)
+    qkb = torch.randn(S, nr, generator=g).to(torch.bfloat16).cuda().view(torch.int16)
+    do = torch.randn(S, nq, generator=g).to(torch.bfloat16).cuda().view(torch.int16)
+    o = torch.zeros(S, nq, dtype=torch.int16, device="cuda")
+    lse = torch.zeros(Hq * S, device="cuda")
+    dsum = torch.zeros_like(lse)
+    dqkv = torch.zeros(S, ld, dtype=torch.int16, device="cuda")
+    st = torch.cuda.current_stream()
+    s = st.cuda_stream
+
+    def fwd():
+        mt.check(mt.lib.mt_k_attn_fwd(qkv.data_ptr(), ld, o.data_ptr(), nq, lse.data_ptr(), 1, S, Hq, Hkv, hd, s),
+                 "attn_fwd")
+
+    def bwd():
+        mt.check(mt.lib.mt_k_attn_bwd(qkv.data_ptr(), ld, o.data_ptr(), do.data_ptr(), nq, lse.data_ptr(),
+                                      dsum.data_ptr(), dqkv.data_ptr(), ld, 1, S, Hq, Hkv, hd, qkb.data_ptr(), nr, s),
+                 "attn_bwd")
+    fl = 4.0 * Hq * hd * S * (S + 1) / 2
+    out = {}
+    for name, fn, f in (("fwd", fwd, fl), ("bwd", bwd, 2.5 * fl)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(3):
+            fn()
+        e1.record(st)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 3
+        out[name] = {"ms": round(ms, 3), "tflops": round(f / (ms / 1e3) / 1e12, 1)}
+        log(f"attention {name} S={S}: {ms:.2f} ms, {f / ms / 1e9:.0f} TFLOP/s")
+    print(json.dumps({"attention_probe": {"S": S, "heads": [Hq, Hkv, hd], **out}}), flush=True)
+
+
 def ablations(torch, mt, shape, cfg, args, tokens, labels, base_value):
     """The cheap ablations: the same workload with one weight slot (no
     prefetch), one gradient slab, and W and G sharing combined slots."""
@@ -286,6 +330,8 @@ def main():
                          "decoder layer, so every slot is layer-sized; 0: the head as one unit")
     ap.add_argument("--own-streams", action="store_true",
                     help="let the library create its three streams instead of passing torch's")
+    ap.add_argument("--attn-probe", type=int, default=0, metavar="S",
+                    help="only time the attention kernels at one sequence of length S with the workload's heads")
     ap.add_argument("--micro", type=int, default=1,
                     help="micro-batches of batch x seq per optimizer step (gradient accumulation on the host)")
     ap.add_argument("--cross-step", type=int, default=1,
@@ -304,6 +350,9 @@ def main():
     cfg = SHAPES[args.config]
     if args.traffic_probe:
         traffic_probe(torch, mt, cfg)
+        return
+    if args.attn_probe:
+        attention_probe(torch, mt, cfg, args.attn_probe)
         return
     B, S = cfg["batch"], cfg["seq"]
     T = B * S
