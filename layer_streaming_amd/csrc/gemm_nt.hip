@@ -20,8 +20,15 @@
 //    last step of a tile runs its MFMAs after the barrier, behind the first
 //    reads of the next tile;
 //  * the MFMA takes the B fragment as its first operand, so a lane's
-//    accumulator holds 4 consecutive output columns of one row and the
-//    epilogue stores 8 or 16 bytes per lane.
+//    accumulator holds 4 consecutive output columns of one row;
+//  * the epilogue passes the accumulators through LDS so that every store
+//    instruction writes whole row segments (8 or 16 bytes per lane);
+//  * large problems (at least one 256 x 256 tile per CU) take a second form
+//    of the main loop with 64-deep k-tiles in two stages (gemm_nt64_k below):
+//    whole 128-byte rows per load request and half the barriers.  Measured
+//    on MI355X at the 7B gate|up shape (8192 x 37888 x 3584, random bf16):
+//    1215 TFLOP/s against 1111 for the 32-deep form with the LDS epilogue
+//    and 1076 with stores straight from the accumulators.
 #include "kcommon.h"
 #include "kernels.h"
 
@@ -30,16 +37,34 @@ namespace {
 
 // Build-time variants; the defaults are the faster ones as measured on
 // MI355X with random bf16 operands (gate|up 8192 x 37888 x 3584): raised
-// priority over the MFMA groups 1090 TFLOP/s vs 1028 without; non-temporal
-// C stores 741; 4 x 2 waves instead of 2 x 4 within 2% of the default.
+// priority over the MFMA groups 1215 TFLOP/s vs 1143 without (1090 vs 1028
+// in the 32-deep form); non-temporal C stores 741 (32-deep, direct stores);
+// 4 x 2 waves instead of 2 x 4, all loads of a tile with one k-step, tile
+// groups 4 or 16 deep: within 1-2% of the default.  Four waves of 128 x 128
+// (one per SIMD) lose 4-6%.
 #ifndef MT_NT_PRIO
 #define MT_NT_PRIO 1      // 1: raise the wave's issue priority over its MFMA groups
 #endif
 #ifndef MT_NT_NTSTORE
 #define MT_NT_NTSTORE 0   // 1: non-temporal epilogue stores (C does not stay in L2)
 #endif
+#ifndef MT_NT_STAGED
+#define MT_NT_STAGED 1    // 1: the epilogue goes through LDS so that stores cover whole row segments
+#endif
+#ifndef MT_NT_K64
+#define MT_NT_K64 1       // 1: 64-deep k-tiles in two stages for the large-tile shape
+#endif
+#ifndef MT_NT_L1
+#define MT_NT_L1 -1       // 64-deep form: loads of a tile issued one k-step later (-1: half)
+#endif
+#ifndef MT_NT_GROUP
+#define MT_NT_GROUP 8     // 64-deep form: tiles grouped this deep along M
+#endif
+#ifndef MT_NT_NW
+#define MT_NT_NW 8        // waves of the 256 x 256 block
+#endif
 #ifndef MT_NT_WM
-#define MT_NT_WM 2        // waves along M of the 256 x 256 block (8 waves)
+#define MT_NT_WM 2        // of which along M
 #endif
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -226,6 +251,51 @@ __device__ __forceinline__ void store4(const GemmArgs& p, int row, int col, cons
     }
 }
 
+// Epilogue through LDS.  Stored straight from the accumulators, one store
+// instruction would cover 32 rows with 16 bytes each, i.e. 32 separate
+// memory requests, and with every block finishing at about the same time the
+// requests, not the bytes, bound the epilogue.  Instead each wave passes its
+// accumulators through CAP bytes of LDS of its own (st), in P passes of FM/P
+// row blocks, as fp32 rows of TN values (16-byte chunks XOR-swizzled with
+// the row's low 4 bits, which makes both the column-wise writes and the
+// row-wise reads conflict-free), and reads them back so that a store
+// instruction covers whole row segments of TN values.  The caller's last
+// barrier came after every wave's last LDS read and after every load into
+// LDS had landed, so the region is free.  row0/col0: the wave's first output.
+template <int FM, int FN, int TM, int TN, int CAP, int EPI>
+__device__ __forceinline__ void staged_store(const GemmArgs& p, const f32x16_t (&acc)[FM][FN], float4* st, int lane,
+                                             int row0, int col0) {
+    constexpr int P = (TM * TN * 4 + CAP - 1) / CAP;   // passes
+    constexpr int FMP = FM / P, RP = FMP * 32, CPR = TN / 4;
+    static_assert(FM % P == 0 && RP * CPR * 16 <= CAP && CPR >= 16 && 64 % CPR == 0, "staging layout");
+    static_for<0, P>([&](auto pass_) {
+        constexpr int pass = decltype(pass_)::value;
+#pragma unroll
+        for (int ii = 0; ii < FMP; ++ii) {
+            const int r = ii * 32 + (lane & 31);
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x16_t& a = acc[pass * FMP + ii][j];
+                    const int c = j * 8 + 2 * q + (lane >> 5);
+                    st[r * CPR + (c ^ (r & 15))] = make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+                }
+        }
+#pragma unroll
+        for (int it = 0; it < RP * CPR / 64; ++it) {
+            const int e = it * 64 + lane;
+            const int r = e / CPR, c = e % CPR;
+            const float4 w = st[r * CPR + (c ^ (r & 15))];
+            const int row = row0 + pass * RP + r, col = col0 + c * 4;
+            if (row < p.M && col < p.N) {
+                const float v[4] = {w.x, w.y, w.z, w.w};
+                store4<EPI>(p, row, col, v);
+            }
+        }
+    });
+}
+
 template <int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_k(GemmArgs p, int tiles_m, int tiles_n) {
     constexpr int NW = WM * WN;
@@ -351,6 +421,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_k(GemmArgs p, int tiles_
 
     // acc[i][j] element r of lane l: row m0 + wm*TM + 32i + l%32, column
     // n0 + wn*TN + 32j + 8*(r/4) + 4*(l/32) + r%4.
+#if MT_NT_STAGED
+    {
+        static_assert(BM == BN && NW <= 8, "one stage array per wave");
+        uint4* const arr = wave == 0 ? As0 : wave == 1 ? As1 : wave == 2 ? As2 : wave == 3 ? As3
+                         : wave == 4 ? Bs0 : wave == 5 ? Bs1 : wave == 6 ? Bs2 : Bs3;
+        staged_store<FM, FN, TM, TN, BM * 64, EPI>(p, acc, reinterpret_cast<float4*>(arr), lane, m0 + wm * TM,
+                                                    n0 + wn * TN);
+    }
+#else
     const int ml = lane & 31, nq = (lane >> 5) * 4;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -366,21 +445,248 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_k(GemmArgs p, int tiles_
                 store4<EPI>(p, row, col, v);
             }
     }
+#endif
 }
 
-template <int BM, int BN, int WM, int WN>
+
+// ---------------------------------------------------------------------------
+// The same product with 64-deep k-tiles in two LDS stages.  A tile row is then
+// 128 bytes, one whole cache line, so a load instruction makes 8 line-sized
+// requests instead of 16 half-line ones, and the block synchronises once per
+// 64 k instead of once per 32.  With two stages the loads of tile t+2 go into
+// the stage of tile t as soon as the barrier at the end of tile t has passed
+// (half with the last k-step of tile t, half with the first of tile t+1), so
+// they have a whole tile of MFMA work to arrive in, as many cycles as the
+// four 32-deep stages give.
+constexpr int BK64 = 64;
+
+// Physical chunk (of eight) of logical chunk c in a 128-byte LDS row r: a
+// 128-bit read of 16 consecutive rows touches each of the 16 positions of a
+// 256-byte bank line once when rows of one parity take distinct chunks.
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+
+// Loads of one operand's ROWS x 64 tile: instruction i of wave w covers tile
+// rows 8*(i*NW + w) .. +7 (64 lanes x 16 bytes = 8 rows of 128 bytes).
+template <int ROWS, int NW>
+struct DirectLoader64 {
+    static constexpr int NI = ROWS / (8 * NW);
+    static_assert(NI >= 1 && ROWS % (8 * NW) == 0, "tile rows must cover the waves");
+    uint32_t off[NI];
+    int kk[NI];
+
+    __device__ __forceinline__ void init(int lane, int wave, int64_t ld) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int r = (i * NW + wave) * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ swz8(r);
+            off[i] = uint32_t((int64_t(r) * ld + c * 8) * 2);
+            kk[i] = c * 8;
+        }
+    }
+    __device__ __forceinline__ void issue_one(int i, i32x4_t rs, uint4* stage, int wave, int k0, int K) const {
+        const uint32_t base = uint32_t(reinterpret_cast<uintptr_t>((lds_ptr_t)stage));
+        uint32_t v = off[i] + uint32_t(k0) * 2u;
+        if (k0 + kk[i] >= K) v = OOB;
+        dma16(rs, __builtin_amdgcn_readfirstlane(base + uint32_t(i * NW + wave) * 1024u), v);
+    }
+    __device__ __forceinline__ void issue(i32x4_t rs, uint4* stage, int wave, int k0, int K) const {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) issue_one(i, rs, stage, wave, k0, K);
+    }
+};
+
+template <int FM, int FN, int TM, int TN>
+__device__ __forceinline__ void read_frags64(const uint4* __restrict__ a_l, const uint4* __restrict__ b_l, int ks,
+                                             int wm, int wn, int lane, uint4 (&fa)[FM], uint4 (&fb)[FN]) {
+    const int kc = ks * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int r = wm * TM + i * 32 + (lane & 31);
+        fa[i] = a_l[r * 8 + (kc ^ swz8(r))];
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int r = wn * TN + j * 32 + (lane & 31);
+        fb[j] = b_l[r * 8 + (kc ^ swz8(r))];
+    }
+}
+
+template <int BM, int BN, int WM, int WN, int EPI>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_nt64_k(GemmArgs p, int tiles_m, int tiles_n) {
+    constexpr int NW = WM * WN;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr bool F16 = EPI == EPI_F32_F16IN;
+    __shared__ uint4 As0[BM * 8], As1[BM * 8];
+    __shared__ uint4 Bs0[BN * 8], Bs1[BN * 8];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+
+    // tile order: as in gemm_nt_k
+    const int total = tiles_m * tiles_n;
+    int pid = blockIdx.x;
+    if ((total & 7) == 0) pid = (pid & 7) * (total >> 3) + (pid >> 3);
+    constexpr int GROUP = MT_NT_GROUP;
+    const int per_group = GROUP * tiles_n;
+    const int g = pid / per_group;
+    const int first_m = g * GROUP;
+    const int gsz = min(tiles_m - first_m, GROUP);
+    const int tm = first_m + (pid % per_group) % gsz;
+    const int tn = (pid % per_group) / gsz;
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int rows_a = min(BM, p.M - m0), rows_b = min(BN, p.N - n0);
+    const auto ra = make_rsrc(static_cast<const uint16_t*>(p.A) + int64_t(m0) * p.lda,
+                              uint32_t((int64_t(rows_a - 1) * p.lda + p.K) * 2));
+    const auto rb = make_rsrc(static_cast<const uint16_t*>(p.B) + int64_t(n0) * p.ldb,
+                              uint32_t((int64_t(rows_b - 1) * p.ldb + p.K) * 2));
+    DirectLoader64<BM, NW> la;
+    DirectLoader64<BN, NW> lb;
+    la.init(lane, wave, p.lda);
+    lb.init(lane, wave, p.ldb);
+    constexpr int NIA = DirectLoader64<BM, NW>::NI;
+    constexpr int NIT = NIA + DirectLoader64<BN, NW>::NI;  // loads per wave per tile
+    // loads of a tile issued with the last k-step of the tile two earlier
+    // (NIT - L1) and with the first k-step of the tile before it (L1)
+    constexpr int L1 = MT_NT_L1 < 0 ? NIT / 2 : MT_NT_L1;
+    static_assert(L1 >= 0 && L1 < NIT && (FM * FN) % (NIT - L1) == 0 && (L1 == 0 || (FM * FN) % L1 == 0),
+                  "load interleave");
+
+    f32x16_t acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int nk = (p.K + BK64 - 1) / BK64;
+    uint4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+
+#define RD(SA, SB, KS, FA, FB) read_frags64<FM, FN, TM, TN>(SA, SB, KS, wm, wn, lane, FA, FB)
+#define MM(FA, FB) mma_frags<FM, FN, F16>(FA, FB, acc)
+#define PRIO(x) if (MT_NT_PRIO) __builtin_amdgcn_s_setprio(x)
+#define LOAD_ONE(g, XA, XB, T)                                                           \
+    if constexpr ((g) < NIA) la.issue_one((g), ra, XA, wave, (T) * BK64, p.K);           \
+    else lb.issue_one((g) - NIA, rb, XB, wave, (T) * BK64, p.K)
+// One k-step's MFMAs with loads G0 .. G0+NL-1 of tile T2, spread evenly.
+#define MM_LOADS(FA, FB, G0, NL, XA, XB, T2, do_load)                                    \
+    static_for<0, NL>([&](auto g_) {                                                     \
+        constexpr int g = decltype(g_)::value;                                           \
+        constexpr int mg = FM * FN / (NL);                                               \
+        if (do_load) { LOAD_ONE((G0) + g, XA, XB, T2); }                                 \
+        mma_part<FM, FN, F16, g * mg, mg>(FA, FB, acc);                                  \
+        __builtin_amdgcn_sched_barrier(0);                                               \
+    })
+// Tile T in stage (SA, SB), the other stage (NA, NB) receiving tile T+1.
+// Step 0 multiplies (fragments read before) while step 1 is read, and
+// carries the second half of tile T+1's loads; steps 1 and 2 likewise; then
+// the block waits for tile T+1 (the only loads in flight), reads its step 0
+// and multiplies step 3 of tile T with the first half of tile T+2's loads,
+// which go into this tile's stage, free since the barrier.
+#define TILE(T, SA, SB, NA, NB)                                                          \
+    if ((T) < nk) {                                                                      \
+        const bool ld1 = (T) >= 1 && (T) + 1 < nk;                                       \
+        const bool ld2 = (T) + 2 < nk;                                                   \
+        RD(SA, SB, 1, fa1, fb1);                                                         \
+        __builtin_amdgcn_sched_barrier(0);                                               \
+        PRIO(1);                                                                         \
+        if constexpr (L1 > 0) { MM_LOADS(fa0, fb0, NIT - L1, L1, NA, NB, (T) + 1, ld1); }  \
+        else { MM(fa0, fb0); }                                                           \
+        PRIO(0);                                                                         \
+        RD(SA, SB, 2, fa0, fb0);                                                         \
+        __builtin_amdgcn_sched_barrier(0);                                               \
+        PRIO(1);                                                                         \
+        MM(fa1, fb1);                                                                    \
+        PRIO(0);                                                                         \
+        __builtin_amdgcn_sched_barrier(0);                                               \
+        RD(SA, SB, 3, fa1, fb1);                                                         \
+        __builtin_amdgcn_sched_barrier(0);                                               \
+        PRIO(1);                                                                         \
+        MM(fa0, fb0);                                                                    \
+        PRIO(0);                                                                         \
+        wait_vmem<0>();                                                                  \
+        barrier_lds();                                                                   \
+        if ((T) + 1 < nk) { RD(NA, NB, 0, fa0, fb0); }                                   \
+        __builtin_amdgcn_sched_barrier(0);                                               \
+        PRIO(1);                                                                         \
+        MM_LOADS(fa1, fb1, 0, NIT - L1, SA, SB, (T) + 2, ld2);                           \
+        PRIO(0);                                                                         \
+    }
+
+    la.issue(ra, As0, wave, 0, p.K);
+    lb.issue(rb, Bs0, wave, 0, p.K);
+    if (nk > 1) {
+        la.issue(ra, As1, wave, BK64, p.K);
+        lb.issue(rb, Bs1, wave, BK64, p.K);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmem<NIT>();
+    } else {
+        wait_vmem<0>();
+    }
+    barrier_lds();
+    RD(As0, Bs0, 0, fa0, fb0);
+    for (int t = 0; t < nk; t += 2) {
+        TILE(t, As0, Bs0, As1, Bs1)
+        TILE(t + 1, As1, Bs1, As0, Bs0)
+    }
+#undef TILE
+#undef MM_LOADS
+#undef LOAD_ONE
+#undef PRIO
+#undef MM
+#undef RD
+
+    {
+        static_assert(BM == BN && NW % 4 == 0 && NW <= 8, "stage arrays split among the waves");
+        constexpr int PER = NW / 4;                  // waves per stage array
+        constexpr int CAP = BM * 128 / PER;          // bytes per wave
+        const int q = wave / PER;
+        uint4* const arr = q == 0 ? As0 : q == 1 ? As1 : q == 2 ? Bs0 : Bs1;
+        staged_store<FM, FN, TM, TN, CAP, EPI>(p, acc, reinterpret_cast<float4*>(arr) + (wave % PER) * (CAP / 16),
+                                               lane, m0 + wm * TM, n0 + wn * TN);
+    }
+}
+
+template <int BM, int BN, int WM, int WN, bool K64>
 hipError_t launch(GemmEpi epi, const GemmArgs& a, hipStream_t s) {
     const int tm = (a.M + BM - 1) / BM, tn = (a.N + BN - 1) / BN;
     const dim3 grid(tm * tn), block(WM * WN * 64);
     switch (epi) {
-        case EPI_BF16: gemm_nt_k<BM, BN, WM, WN, EPI_BF16><<<grid, block, 0, s>>>(a, tm, tn); break;
-        case EPI_BF16_RESID: gemm_nt_k<BM, BN, WM, WN, EPI_BF16_RESID><<<grid, block, 0, s>>>(a, tm, tn); break;
-        case EPI_F32: gemm_nt_k<BM, BN, WM, WN, EPI_F32><<<grid, block, 0, s>>>(a, tm, tn); break;
-        case EPI_F32_ACC: gemm_nt_k<BM, BN, WM, WN, EPI_F32_ACC><<<grid, block, 0, s>>>(a, tm, tn); break;
-        case EPI_BF16_ACCF32: gemm_nt_k<BM, BN, WM, WN, EPI_BF16_ACCF32><<<grid, block, 0, s>>>(a, tm, tn); break;
-        case EPI_F32_RESID: gemm_nt_k<BM, BN, WM, WN, EPI_F32_RESID><<<grid, block, 0, s>>>(a, tm, tn); break;
-        case EPI_BF16_RESID32: gemm_nt_k<BM, BN, WM, WN, EPI_BF16_RESID32><<<grid, block, 0, s>>>(a, tm, tn); break;
-        case EPI_F32_F16IN: gemm_nt_k<BM, BN, WM, WN, EPI_F32_F16IN><<<grid, block, 0, s>>>(a, tm, tn); break;
+        case EPI_BF16:
+            if constexpr (K64) gemm_nt64_k<BM, BN, WM, WN, EPI_BF16><<<grid, block, 0, s>>>(a, tm, tn);
+            else gemm_nt_k<BM, BN, WM, WN, EPI_BF16><<<grid, block, 0, s>>>(a, tm, tn);
+            break;
+        case EPI_BF16_RESID:
+            if constexpr (K64) gemm_nt64_k<BM, BN, WM, WN, EPI_BF16_RESID><<<grid, block, 0, s>>>(a, tm, tn);
+            else gemm_nt_k<BM, BN, WM, WN, EPI_BF16_RESID><<<grid, block, 0, s>>>(a, tm, tn);
+            break;
+        case EPI_F32:
+            if constexpr (K64) gemm_nt64_k<BM, BN, WM, WN, EPI_F32><<<grid, block, 0, s>>>(a, tm, tn);
+            else gemm_nt_k<BM, BN, WM, WN, EPI_F32><<<grid, block, 0, s>>>(a, tm, tn);
+            break;
+        case EPI_F32_ACC:
+            if constexpr (K64) gemm_nt64_k<BM, BN, WM, WN, EPI_F32_ACC><<<grid, block, 0, s>>>(a, tm, tn);
+            else gemm_nt_k<BM, BN, WM, WN, EPI_F32_ACC><<<grid, block, 0, s>>>(a, tm, tn);
+            break;
+        case EPI_BF16_ACCF32:
+            if constexpr (K64) gemm_nt64_k<BM, BN, WM, WN, EPI_BF16_ACCF32><<<grid, block, 0, s>>>(a, tm, tn);
+            else gemm_nt_k<BM, BN, WM, WN, EPI_BF16_ACCF32><<<grid, block, 0, s>>>(a, tm, tn);
+            break;
+        case EPI_F32_RESID:
+            if constexpr (K64) gemm_nt64_k<BM, BN, WM, WN, EPI_F32_RESID><<<grid, block, 0, s>>>(a, tm, tn);
+            else gemm_nt_k<BM, BN, WM, WN, EPI_F32_RESID><<<grid, block, 0, s>>>(a, tm, tn);
+            break;
+        case EPI_BF16_RESID32:
+            if constexpr (K64) gemm_nt64_k<BM, BN, WM, WN, EPI_BF16_RESID32><<<grid, block, 0, s>>>(a, tm, tn);
+            else gemm_nt_k<BM, BN, WM, WN, EPI_BF16_RESID32><<<grid, block, 0, s>>>(a, tm, tn);
+            break;
+        case EPI_F32_F16IN:
+            if constexpr (K64) gemm_nt64_k<BM, BN, WM, WN, EPI_F32_F16IN><<<grid, block, 0, s>>>(a, tm, tn);
+            else gemm_nt_k<BM, BN, WM, WN, EPI_F32_F16IN><<<grid, block, 0, s>>>(a, tm, tn);
+            break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -399,8 +705,8 @@ hipError_t gemm_nt_direct(GemmEpi epi, const GemmArgs& a, hipStream_t s) {
     if (epi == EPI_BF16_ACCF32 && ((a.ldacc & 3) || !al16(a.Cacc))) return hipErrorNotSupported;
     if (a.lda > (int64_t(1) << 21) || a.ldb > (int64_t(1) << 21)) return hipErrorNotSupported;
     const int64_t big_tiles = int64_t((a.M + 255) / 256) * ((a.N + 255) / 256);
-    if (big_tiles >= 256) return launch<256, 256, MT_NT_WM, 8 / MT_NT_WM>(epi, a, s);
-    return launch<128, 128, 2, 2>(epi, a, s);
+    if (big_tiles >= 256) return launch<256, 256, MT_NT_WM, MT_NT_NW / MT_NT_WM, MT_NT_K64 != 0>(epi, a, s);
+    return launch<128, 128, 2, 2, false>(epi, a, s);
 }
 
 }  // namespace mt
