@@ -58,8 +58,8 @@ SHAPES = {
 # profiles/gemm_gateup_traffic_7b.md.  Valid only for the kernel sources it was
 # taken on (sha256 over the files in order): reported as null once they change.
 TRAFFIC = {"sources": ["layer_streaming_amd/csrc/gemm_nt.hip", "layer_streaming_amd/csrc/kcommon.h"],
-           "sha256": "e25e77bfba310585be5eb6190e19d1949c491add75f4ef6171b641b1e0b75f33",
-           "fetch_bytes": 3317797202, "write_bytes": 638521504}
+           "sha256": "433141231075b6e89187de92500c5bb42783643c64e8aa9fc7d9279b88967bea",
+           "fetch_bytes": 3317838231, "write_bytes": 620756992}
 
 
 def traffic_bytes(config):
@@ -417,6 +417,10 @@ def main():
     fl0 = gemm_flops(cfg, T)
     recompute = cfg["n_layers"] * (fl0["gemm_qkv"] + fl0["gemm_o"] + fl0["gemm_gateup"] +
                                    2 * 2 * T * cfg["n_heads"] * cfg["head_dim"] * (S + 1) / 2)
+    # a vocabulary-chunked head (head_vocab_chunk != 0) computes the logits
+    # twice: its backward recomputes each chunk's logits
+    logit_passes = 2 if args.head_vocab_chunk != 0 else 1
+    recompute += (logit_passes - 1) * head_gemm_flops(cfg, T)
     out["hw_tflops_per_s"] = round((mf + nm * recompute) / (ms_per_step / 1e3) / 1e12, 2)
     hb_step = host_bytes_per_step(cfg, T, nm)
     out["host_memory"] = {"bytes_per_step": int(hb_step), "achieved_GBps": round(hb_step / (ms_per_step / 1e3) / 1e9, 1),
@@ -462,7 +466,8 @@ def main():
         hf = head_gemm_flops(cfg, T)
         for k in ("head_logits", "head_dx", "head_dw"):
             if k in sites and sites[k][0] > 0:
-                out["gemm_tflops"][k] = round(hf * nm * len(stats) / (sites[k][0] / 1e3) / 1e12, 1)
+                passes = logit_passes if k == "head_logits" else 1
+                out["gemm_tflops"][k] = round(hf * passes * nm * len(stats) / (sites[k][0] / 1e3) / 1e12, 1)
         hb = hbm_bytes(cfg, T)
         out["hbm_kernels_GBps"] = {k: round(hb[k] * sites[k][1] / (sites[k][0] / 1e3) / 1e9, 1)
                                    for k in hb if k in sites and sites[k][0] > 0}
