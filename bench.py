@@ -118,21 +118,23 @@ def hbm_bytes(cfg, T):
     }
 
 
-def host_bytes_per_step(cfg, T, n_micro=1):
-    """Host DRAM bytes one synchronous step moves.  Per micro-batch: the pack
-    (read W, streaming write to staging) and the DMA read of staging for the
-    forward and the backward visit of every streamed unit, the DMA write of
-    every streamed unit's gradient, the checkpoint ring out and back in, and
-    the embedding rows.  Per optimizer step and parameter: Adam's 30 B with
-    one micro-batch; with n > 1 the first stores the slab into G (4 B), each
-    middle one adds into G (6 B), the last adds and runs Adam (34 B)."""
+def host_bytes_per_step(cfg, T, n_micro=1, pinned=False):
+    """Host DRAM bytes one step moves.  Per micro-batch: for the forward and
+    the backward visit of every streamed unit, the DMA read of its weights,
+    preceded, unless the W regions are pinned (pin_weights), by the pack (read
+    W, streaming write to staging); the DMA write of every streamed unit's
+    gradient, the checkpoint ring out and back in, and the embedding rows.
+    Per optimizer step and parameter: Adam's 30 B with one micro-batch; with
+    n > 1 the first stores the slab into G (4 B), each middle one adds into G
+    (6 B), the last adds and runs Adam (34 B)."""
     L, d, F, V = cfg["n_layers"], cfg["d_model"], cfg["ffn_dim"], cfg["vocab"]
     hq, hkv, hd = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]
     p_layer = d * hq * hd + 2 * d * hkv * hd + hq * hd * d + 3 * d * F + 2 * d
     streamed = L * p_layer + V * d + d
     p_embed = V * d
     per_param = 30 if n_micro == 1 else 4 + 6 * (n_micro - 2) + 34
-    per_micro = 2 * (4 + 2) * streamed + 2 * streamed + 2 * L * T * d * 2 + 2 * T * d * 2
+    visit = 2 if pinned else 4 + 2
+    per_micro = 2 * visit * streamed + 2 * streamed + 2 * L * T * d * 2 + 2 * T * d * 2
     return per_param * (streamed + p_embed) + n_micro * per_micro
 
 
@@ -422,7 +424,7 @@ def main():
     logit_passes = 2 if args.head_vocab_chunk != 0 else 1
     recompute += (logit_passes - 1) * head_gemm_flops(cfg, T)
     out["hw_tflops_per_s"] = round((mf + nm * recompute) / (ms_per_step / 1e3) / 1e12, 2)
-    hb_step = host_bytes_per_step(cfg, T, nm)
+    hb_step = host_bytes_per_step(cfg, T, nm, pinned=bool(args.pin_weights))
     out["host_memory"] = {"bytes_per_step": int(hb_step), "achieved_GBps": round(hb_step / (ms_per_step / 1e3) / 1e9, 1),
                           "adam_alone_GBps": host_adam_probe(mt)}
 
