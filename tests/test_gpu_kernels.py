@@ -99,6 +99,98 @@ def test_gemm_epilogues():
     assert_close(host_f32(dC3), 2 * ref + R, "C bf16 = acc + R f32")
 
 
+# The NT kernel's 64-deep form runs when a grid has at least 256 tiles of
+# 256 x 256.  These shapes reach it with ragged rows and columns and with k
+# ending inside a tile (k-tile counts 1, 2, 3, 4, 16 and 42).
+GEMM_BIG = [(4104, 4040, 200), (4000, 4100, 1000), (4352, 3848, 72), (4100, 4104, 8), (4096, 4096, 136),
+            (4104, 4096, 2632)]
+
+
+def _elementwise_check(got, ref, A, B, name, K):
+    """Every output element within the bound of its own dot product:
+    half a bf16 ulp of the result plus fp32 accumulation of K exact products,
+    |err| <= 2^-8 |ref| + 4 K 2^-24 ||a_i|| ||b_j|| (Cauchy-Schwarz on the sum
+    of |a_ik b_jk|).  A lost or misplaced 8-deep k-chunk, row or column moves
+    most of the elements it touches well past it."""
+    na = np.linalg.norm(A.astype(np.float64), axis=1)
+    nb = np.linalg.norm(B.astype(np.float64), axis=1)
+    bound = 2.0 ** -8 * np.abs(ref) + 4.0 * K * 2.0 ** -24 * np.outer(na, nb) + 1e-30
+    err = np.abs(np.asarray(got, np.float64) - ref)
+    bad = err > bound
+    assert not bad.any(), (f"{name}: {int(bad.sum())} elements outside the bound, first at "
+                           f"{tuple(int(x) for x in np.argwhere(bad)[0])}")
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_BIG)
+def test_gemm_nt_large_tile_form(M, N, K):
+    log(f"gemm NT large-tile form M={M} N={N} K={K}")
+    A = synth.bf16_exact_normal(RNG, (M, K))
+    B = synth.bf16_exact_normal(RNG, (N, K))
+    ref = A.astype(np.float64) @ B.astype(np.float64).T
+    dA, dB = dev_bits(A), dev_bits(B)
+    dC = dev_zeros_bits((M, N))
+    mt.check(mt.lib.mt_k_gemm(0, 0, dA.data_ptr(), K, dB.data_ptr(), K, dC.data_ptr(), N, None, 0, None, 0,
+                              M, N, K, _stream()), "gemm")
+    _sync()
+    got = host_f32(dC)
+    assert_close(got, ref, "C")
+    _elementwise_check(got, ref, A, B, "C", K)
+
+
+def test_gemm_nt_large_tile_epilogues():
+    """Every epilogue of the 64-deep form on one ragged shape (partial last
+    k-tile, partial row and column tiles), with leading dimensions wider than
+    the operands."""
+    M, N, K = 4104, 4040, 200
+    lda, ldb, ldc = K + 24, K + 8, N + 12
+    log(f"gemm NT large-tile epilogues M={M} N={N} K={K}")
+    A = synth.bf16_exact_normal(RNG, (M, lda))
+    B = synth.bf16_exact_normal(RNG, (N, ldb))
+    R = synth.bf16_exact_normal(RNG, (M, ldc))
+    ref = A[:, :K].astype(np.float64) @ B[:, :K].astype(np.float64).T
+    dA, dB, dR = dev_bits(A), dev_bits(B), dev_bits(R)
+    s = _stream()
+    Rv = R[:, :N].astype(np.float64)
+
+    def run(epi, C, Rp=None, ldr=0, acc=None):
+        mt.check(mt.lib.mt_k_gemm(0, epi, dA.data_ptr(), lda, dB.data_ptr(), ldb, C.data_ptr(), ldc,
+                                  Rp, ldr, acc, ldc if acc else 0, M, N, K, s), f"gemm epi {epi}")
+        _sync()
+
+    dC = dev_zeros_bits((M, ldc))
+    run(1, dC, dR.data_ptr(), ldc)
+    got = host_f32(dC)[:, :N]
+    assert_close(got, ref + Rv, "C+R")
+    _elementwise_check(got, ref + Rv, A[:, :K], B[:, :K], "C+R", K)
+    assert np.all(host_f32(dC)[:, N:] == 0), "C+R: columns past N written"
+    c32 = torch.zeros((M, ldc), dtype=torch.float32, device="cuda")
+    run(2, c32)
+    got32 = c32.cpu().numpy()[:, :N]
+    assert_close(got32, ref, "C f32", tol=1e-5)
+    _elementwise_check(got32, ref, A[:, :K], B[:, :K], "C f32", K)
+    run(3, c32)
+    assert_close(c32.cpu().numpy()[:, :N], 2 * ref, "C f32 += ", tol=1e-5)
+    dC2 = dev_zeros_bits((M, ldc))
+    run(4, dC2, acc=c32.data_ptr())
+    assert_close(host_f32(dC2)[:, :N], 3 * ref, "C bf16 from f32 partial")
+    h32 = torch.zeros((M, ldc), dtype=torch.float32, device="cuda")
+    run(5, h32, dR.data_ptr(), ldc)
+    assert_close(h32.cpu().numpy()[:, :N], ref + Rv, "C f32 = acc + R bf16", tol=1e-5)
+    dC3 = dev_zeros_bits((M, ldc))
+    run(6, dC3, h32.data_ptr(), ldc)
+    assert_close(host_f32(dC3)[:, :N], 2 * ref + Rv, "C bf16 = acc + R f32")
+    # fp16 operands
+    A16 = RNG.standard_normal((M, lda)).astype(np.float16)
+    B16 = (0.02 * RNG.standard_normal((N, ldb))).astype(np.float16)
+    dA16, dB16 = dev_f16(A16), dev_f16(B16)
+    c16 = torch.zeros((M, ldc), dtype=torch.float32, device="cuda")
+    mt.check(mt.lib.mt_k_gemm(0, 7, dA16.data_ptr(), lda, dB16.data_ptr(), ldb, c16.data_ptr(), ldc, None, 0,
+                              None, 0, M, N, K, s), "gemm f16")
+    _sync()
+    ref16 = A16[:, :K].astype(np.float64) @ B16[:, :K].astype(np.float64).T
+    assert_close(c16.cpu().numpy()[:, :N], ref16, "C f16 operands", tol=1e-5)
+
+
 def test_gemm_rejects_misaligned_shapes():
     A = dev_zeros_bits((16, 16))
     r = mt.lib.mt_k_gemm(0, 0, A.data_ptr(), 12, A.data_ptr(), 16, A.data_ptr(), 16, None, 0, None, 0,
