@@ -675,6 +675,17 @@ __global__ __launch_bounds__(256) void attn_dq2_k(AttnBwdArgs a, int n_qt) {
     }
 }
 
+// Compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. N-1.
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for_from(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for_from<I + 1, N>(f);
+    }
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for_n(F&& f) { static_for_from<0, N>(f); }
+
 // dK, dV: block = 4 waves x 32 keys of one (b, kv head); query tiles of 64
 // over the group's heads, staged as fp16 Q rows (scores), bf16 Q (read
 // transposed for dK) and bf16 dO (rows for dP, transposed for dV).  MODE 0
@@ -768,16 +779,33 @@ __global__ __launch_bounds__(256, MODE == 2 ? 2 : 1) void attn_dkdv2_k(AttnBwdAr
             
             f32x16_t st[2], dp[2];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) { st[t][r] = 0.f; dp[t][r] = 0.f; }
+            // S^T and dP^T over the head dimension in k-steps of 16: the
+            // fragments of step s+1 are read while step s multiplies (left to
+            // itself the compiler waits for each fragment right before its
+            // MFMA), and the four accumulations of a step are independent.
+            uint4 fq[2][2], fd[2][2];
+            auto rd = [&](int s, uint4(&q)[2], uint4(&d)[2]) {
 #pragma unroll
-                for (int s = 0; s < NS; ++s) {
-                    st[t] = MFMA32H(as_f16x8(tile_row<HD>(Qh[cur], 32 * t + c, 2 * s + hh)), kf[s], st[t]);
-                    if constexpr (WK)
-                        dp[t] = MFMA32(as_bf16x8(tile_row<HD>(Ds[cur], 32 * t + c, 2 * s + hh)), vf[s], dp[t]);
+                for (int t = 0; t < 2; ++t) {
+                    q[t] = tile_row<HD>(Qh[cur], 32 * t + c, 2 * s + hh);
+                    if constexpr (WK) d[t] = tile_row<HD>(Ds[cur], 32 * t + c, 2 * s + hh);
                 }
-            }
+            };
+            rd(0, fq[0], fd[0]);
+            static_for_n<NS>([&](auto s_) {
+                constexpr int s = decltype(s_)::value;
+                if constexpr (s + 1 < NS) rd(s + 1, fq[(s + 1) & 1], fd[(s + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    st[t] = MFMA32H(as_f16x8(fq[s & 1][t]), kf[s], st[t]);
+                    if constexpr (WK) dp[t] = MFMA32(as_bf16x8(fd[s & 1][t]), vf[s], dp[t]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
             bf16x8_t pb[2][2], dsb[2][2];
             const bool full = kw + 31 <= q0 && q0 + BKV <= S && kw + 32 <= S;
 #pragma unroll
