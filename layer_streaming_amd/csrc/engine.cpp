@@ -358,7 +358,6 @@ struct Ctx {
     std::deque<Job> jobs;
     std::vector<int64_t> adam_gen;  // updates applied per unit
     double adam_wait_ms = 0.0;
-    int64_t bwd_complete = 0;  // last step whose backward has handed over every gradient
     std::vector<int> free_slabs;
     bool stop = false;
     int jobs_pending = 0;
@@ -712,18 +711,23 @@ void Ctx::slab_worker() {
             std::unique_lock<std::mutex> lk(q_mu);
             q_cv.wait(lk, [&] { return stop || !jobs.empty(); });
             if (jobs.empty()) return;
-            // While the backward runs: arrival order, which frees the slabs
-            // in the order the backward needs them.  With cross_step, once a
-            // step's backward is over its remaining updates go lowest rank
-            // first: the next forward needs the input embedding, then the
-            // layers in order, then the head.
+            // With cross_step the updates go lowest rank first, in the order
+            // the next forward needs the units: the input embedding, the
+            // layers in order, then the head.  The backward hands gradients
+            // over from the head down, so while it runs the worker takes the
+            // newest arrival and the backlog it cannot keep up with piles up
+            // at the top of the model, which the next forward reaches last
+            // (in arrival order the backlog would be the bottom layers, and
+            // the next forward would wait for it from its first layer on).
+            // The number of pending jobs, and so of slabs held, does not
+            // depend on the order.  Equal ranks (one unit's micro-batch jobs,
+            // the head's chunks) keep arrival order.  Without cross_step
+            // every update completes inside the step: arrival order.
             auto rank = [&](const Job& x) { return x.unit == lay.embed() ? -1 : x.unit; };
             auto it = jobs.begin();
-            if (opt.cross_step && jobs.front().step_id <= bwd_complete)
-                it = std::min_element(jobs.begin(), jobs.end(), [&](const Job& x, const Job& y) {
-                    return (x.step_id <= bwd_complete ? rank(x) : INT32_MAX) <
-                           (y.step_id <= bwd_complete ? rank(y) : INT32_MAX);
-                });
+            if (opt.cross_step)
+                it = std::min_element(jobs.begin(), jobs.end(),
+                                      [&](const Job& x, const Job& y) { return rank(x) < rank(y); });
             j = *it;
             jobs.erase(it);
         }
@@ -1517,10 +1521,6 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
         {
             const int wo = wait_offload(off_submitted - 1);  // every gradient copy issued
             if (wo != MT_OK) return wo;
-        }
-        if (mb + 1 == n_micro) {
-            std::lock_guard<std::mutex> lk(q_mu);
-            bwd_complete = step + 1;
         }
         ph.bwd = next_tev();
         HIPC(hipEventRecord(ph.bwd, st_c));
