@@ -554,6 +554,17 @@ __device__ __forceinline__ bf16x8_t tile_colT(const uint4* t, int dt, int tt, in
     return as_bf16x8(make_uint4(r[0].x, r[0].y, r[1].x, r[1].y));
 }
 
+// Compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. N-1.
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for_from(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for_from<I + 1, N>(f);
+    }
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for_n(F&& f) { static_for_from<0, N>(f); }
+
 // dQ: block = 4 waves x 32 queries of one (b, h); key tiles of 64 staged as
 // fp16 K rows (scores), bf16 K (read transposed for dQ) and bf16 V rows.
 template <int HD>
@@ -622,15 +633,30 @@ __global__ __launch_bounds__(256) void attn_dq2_k(AttnBwdArgs a, int n_qt) {
         if (k0 <= qw + 31) {
             f32x16_t st[2], dp[2];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) { st[t][r] = 0.f; dp[t][r] = 0.f; }
+            // k-step s+1's fragments are read while step s multiplies
+            uint4 fk[2][2], fv[2][2];
+            auto rd = [&](int s, uint4(&k)[2], uint4(&v)[2]) {
 #pragma unroll
-                for (int s = 0; s < NS; ++s) {
-                    st[t] = MFMA32H(as_f16x8(tile_row<HD>(Kh[cur], 32 * t + c, 2 * s + hh)), qf[s], st[t]);
-                    dp[t] = MFMA32(as_bf16x8(tile_row<HD>(Vs[cur], 32 * t + c, 2 * s + hh)), dof[s], dp[t]);
+                for (int t = 0; t < 2; ++t) {
+                    k[t] = tile_row<HD>(Kh[cur], 32 * t + c, 2 * s + hh);
+                    v[t] = tile_row<HD>(Vs[cur], 32 * t + c, 2 * s + hh);
                 }
-            }
+            };
+            rd(0, fk[0], fv[0]);
+            static_for_n<NS>([&](auto s_) {
+                constexpr int s = decltype(s_)::value;
+                if constexpr (s + 1 < NS) rd(s + 1, fk[(s + 1) & 1], fv[(s + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    st[t] = MFMA32H(as_f16x8(fk[s & 1][t]), qf[s], st[t]);
+                    dp[t] = MFMA32(as_bf16x8(fv[s & 1][t]), dof[s], dp[t]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
             bf16x8_t dsb[2][2];
             const bool full = k0 + BKV - 1 <= qw && k0 + BKV <= S;
 #pragma unroll
@@ -674,17 +700,6 @@ __global__ __launch_bounds__(256) void attn_dq2_k(AttnBwdArgs a, int n_qt) {
             }
     }
 }
-
-// Compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. N-1.
-template <int I, int N, class F>
-__device__ __forceinline__ void static_for_from(F&& f) {
-    if constexpr (I < N) {
-        f(std::integral_constant<int, I>{});
-        static_for_from<I + 1, N>(f);
-    }
-}
-template <int N, class F>
-__device__ __forceinline__ void static_for_n(F&& f) { static_for_from<0, N>(f); }
 
 // dK, dV: block = 4 waves x 32 keys of one (b, kv head); query tiles of 64
 // over the group's heads, staged as fp16 Q rows (scores), bf16 Q (read
