@@ -23,7 +23,7 @@
 //    accumulator holds 4 consecutive output columns of one row;
 //  * the epilogue passes the accumulators through LDS so that every store
 //    instruction writes whole row segments (8 or 16 bytes per lane);
-//  * large problems (at least one 256 x 256 tile per CU) take a second form
+//  * large problems (from about half a 256 x 256 tile per CU) take a second form
 //    of the main loop with 64-deep k-tiles in two stages (gemm_nt64_k below):
 //    whole 128-byte rows per load request and half the barriers.  Measured
 //    on MI355X at the 7B gate|up shape (8192 x 37888 x 3584, random bf16):
@@ -53,6 +53,14 @@ namespace {
 #endif
 #ifndef MT_NT_K64
 #define MT_NT_K64 1       // 1: 64-deep k-tiles in two stages for the large-tile shape
+#endif
+#ifndef MT_NT_BIG_MIN
+// Fewest 256 x 256 tiles for the large-tile form.  Measured (K = 8192, bf16,
+// TFLOP/s, 64-deep 256 x 256 against 32-deep 128 x 128): 64 tiles 467/748,
+// 100 698/685 (540/658 at K = 2048), 121 828/648, 144 988/637, 196 1177/723,
+// 252 1320/754: a grid that leaves some CUs idle still wins from about half
+// the CUs up.
+#define MT_NT_BIG_MIN 120
 #endif
 #ifndef MT_NT_L1
 #define MT_NT_L1 -1       // 64-deep form: loads of a tile issued one k-step later (-1: half)
@@ -705,7 +713,7 @@ hipError_t gemm_nt_direct(GemmEpi epi, const GemmArgs& a, hipStream_t s) {
     if (epi == EPI_BF16_ACCF32 && ((a.ldacc & 3) || !al16(a.Cacc))) return hipErrorNotSupported;
     if (a.lda > (int64_t(1) << 21) || a.ldb > (int64_t(1) << 21)) return hipErrorNotSupported;
     const int64_t big_tiles = int64_t((a.M + 255) / 256) * ((a.N + 255) / 256);
-    if (big_tiles >= 256) return launch<256, 256, MT_NT_WM, MT_NT_NW / MT_NT_WM, MT_NT_K64 != 0>(epi, a, s);
+    if (big_tiles >= MT_NT_BIG_MIN) return launch<256, 256, MT_NT_WM, MT_NT_NW / MT_NT_WM, MT_NT_K64 != 0>(epi, a, s);
     return launch<128, 128, 2, 2, false>(epi, a, s);
 }
 
