@@ -182,9 +182,12 @@ void plan_workspace(const Layout& lay, const mt_options& o, Carver& cv, Workspac
     {
         const uint64_t T8 = uint64_t((T + 7) & ~int64_t(7));  // token rows padded for the dW products
         const uint64_t ta = uint64_t(std::max({d, 2 * F, nqkv})) * T8;
+        // the chunked head's dX transposes one E_out chunk (d x its rows)
+        uint64_t head_t = 0;
+        for (const HeadChunk& c : head_chunks(lay, o)) head_t = std::max<uint64_t>(head_t, uint64_t(d) * c.rows);
         const uint64_t tb = std::max({uint64_t(F) * std::max<uint64_t>(T8, uint64_t(2 * d)),
                                       uint64_t(std::max(nq, nqkv)) * std::max<uint64_t>(T8, uint64_t(d)),
-                                      uint64_t(d) * T8});
+                                      uint64_t(d) * T8, head_t});
         ws.tA = cv.take<uint16_t>(ta * 2);
         ws.tB = cv.take<uint16_t>(tb * 2);
     }
@@ -1118,9 +1121,12 @@ hipError_t Ctx::head_chunk_bwd(const HeadChunk& ch, bool first, bool last, const
                                 inv_tokens, s);
         }));
         HIPR(site(S_HEAD_DX, [&] {
-            GemmArgs a{ws.dlogits, ch.rows, E, d, ws.dnf_acc + int64_t(r0) * d, d, nullptr, 0, nullptr, 0,
+            // dX = dlogits E as the NT product on E^T, transposed once per
+            // vocabulary chunk (the workspace holds d x the largest chunk)
+            if (c == 0) HIPR(transpose16(E, d, ws.tB, ch.rows, ch.rows, d, s));
+            GemmArgs a{ws.dlogits, ch.rows, ws.tB, ch.rows, ws.dnf_acc + int64_t(r0) * d, d, nullptr, 0, nullptr, 0,
                        rows, d, ch.rows};
-            return gemm(GEMM_NN, first ? EPI_F32 : EPI_F32_ACC, a, s);
+            return gemm(GEMM_NT, first ? EPI_F32 : EPI_F32_ACC, a, s);
         }));
         HIPR(site(S_HEAD_DW, [&] {
             GemmArgs a{ws.dlogits, ch.rows, ws.nf + int64_t(r0) * d, d, nullptr, d, nullptr, 0, nullptr, 0,
