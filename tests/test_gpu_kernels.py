@@ -101,10 +101,11 @@ def test_gemm_epilogues():
 
 # The NT kernel's 64-deep form runs when a grid has at least 120 tiles of
 # 256 x 256.  These shapes reach it with ragged rows and columns and with k
-# ending inside a tile (k-tile counts 1, 2, 3, 4, 16 and 42), and with a grid
-# smaller than the CU count (3080 x 3000: 156 tiles).
+# ending inside a tile (k-tile counts 1, 2, 3, 4, 16 and 42), with a grid
+# smaller than the CU count (3080 x 3000: 156 tiles) and with several rounds
+# of tiles (6152 x 5384: 550 tiles, 8200 x 8200: 1089).
 GEMM_BIG = [(4104, 4040, 200), (4000, 4100, 1000), (4352, 3848, 72), (4100, 4104, 8), (4096, 4096, 136),
-            (4104, 4096, 2632), (3080, 3000, 200)]
+            (4104, 4096, 2632), (3080, 3000, 200), (6152, 5384, 200), (8200, 8200, 72)]
 
 
 def _elementwise_check(got, ref, A, B, name, K):
