@@ -22,8 +22,11 @@ __device__ __forceinline__ void load8(const float* __restrict__ row, int c, floa
     f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
 
-// One wave per row, four rows per 256-thread block.
-template <class TX>
+// One wave per row, four rows per 256-thread block.  The row stays in
+// registers (CPL 8-element chunks per lane) between the sum of squares and
+// the scaling, so it is read from memory once; all of a lane's loads are
+// issued before the first is used.
+template <class TX, int CPL>
 __global__ __launch_bounds__(256) void rmsnorm_fwd_k(const TX* __restrict__ x,
                                                      const uint4* __restrict__ gamma,
                                                      uint4* __restrict__ n, uint4* __restrict__ n16,
@@ -33,25 +36,34 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_k(const TX* __restrict__ x,
     if (row >= T) return;
     const int nv = d >> 3;
     const TX* xr = x + int64_t(row) * d;
-    float ss = 0.f;
-    for (int c = lane; c < nv; c += 64) {
-        float f[8];
-        load8(xr, c, f);
+    float f[CPL][8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) ss += f[k] * f[k];
+    for (int k = 0; k < CPL; ++k) {
+        const int c = lane + 64 * k;
+        if (c < nv) load8(xr, c, f[k]);
     }
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k)
+        if (lane + 64 * k < nv) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += f[k][e] * f[k][e];
+        }
     ss = wave_sum(ss);
     const float r = 1.0f / sqrtf(ss / float(d) + eps);
     uint4* nr = n + int64_t(row) * nv;
     uint4* nh = n16 ? n16 + int64_t(row) * nv : nullptr;
-    for (int c = lane; c < nv; c += 64) {
-        float f[8], g[8];
-        load8(xr, c, f);
-        unpack8(gamma[c], g);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) f[k] = (f[k] * r) * g[k];
-        nr[c] = pack8(f);
-        if (nh) nh[c] = pack8h(f);
+    for (int k = 0; k < CPL; ++k) {
+        const int c = lane + 64 * k;
+        if (c < nv) {
+            float g[8];
+            unpack8(gamma[c], g);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[k][e] = (f[k][e] * r) * g[e];
+            nr[c] = pack8(f[k]);
+            if (nh) nh[c] = pack8h(f[k]);
+        }
     }
     if (lane == 0) rstd[row] = r;
 }
@@ -508,11 +520,23 @@ hipError_t rmsnorm_fwd(const void* x, bool x_f32, const uint16_t* gamma, uint16_
     const uint4* g = reinterpret_cast<const uint4*>(gamma);
     uint4* nv = reinterpret_cast<uint4*>(n);
     uint4* nh = reinterpret_cast<uint4*>(n_f16);
-    if (x_f32)
-        rmsnorm_fwd_k<float><<<blocks(T, 4), 256, 0, s>>>(static_cast<const float*>(x), g, nv, nh, rstd, T, d, eps);
-    else
-        rmsnorm_fwd_k<uint16_t><<<blocks(T, 4), 256, 0, s>>>(static_cast<const uint16_t*>(x), g, nv, nh, rstd, T,
-                                                              d, eps);
+    // chunks of 8 per lane: d / 512 rounded up to a power of two (d <= 8192)
+    const int need = (d / 8 + 63) / 64;
+    auto run = [&](auto cpl_) {
+        constexpr int CPL = decltype(cpl_)::value;
+        if (x_f32)
+            rmsnorm_fwd_k<float, CPL><<<blocks(T, 4), 256, 0, s>>>(static_cast<const float*>(x), g, nv, nh, rstd, T, d,
+                                                                   eps);
+        else
+            rmsnorm_fwd_k<uint16_t, CPL><<<blocks(T, 4), 256, 0, s>>>(static_cast<const uint16_t*>(x), g, nv, nh, rstd,
+                                                                      T, d, eps);
+    };
+    if (need <= 1) run(std::integral_constant<int, 1>{});
+    else if (need <= 2) run(std::integral_constant<int, 2>{});
+    else if (need <= 4) run(std::integral_constant<int, 4>{});
+    else if (need <= 8) run(std::integral_constant<int, 8>{});
+    else if (need <= 16) run(std::integral_constant<int, 16>{});
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
