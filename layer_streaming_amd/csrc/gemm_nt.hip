@@ -62,6 +62,9 @@ namespace {
 // the CUs up.
 #define MT_NT_BIG_MIN 120
 #endif
+#ifndef MT_NT_ST8
+#define MT_NT_ST8 1       // 1: bf16 epilogues store 8 columns (16 bytes) per lane
+#endif
 #ifndef MT_NT_L1
 #define MT_NT_L1 -1       // 64-deep form: loads of a tile issued one k-step later (-1: half)
 #endif
@@ -290,15 +293,38 @@ __device__ __forceinline__ void staged_store(const GemmArgs& p, const f32x16_t (
                     st[r * CPR + (c ^ (r & 15))] = make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
                 }
         }
+        if constexpr (EPI == EPI_BF16 && MT_NT_ST8) {
+            // bf16 out, no epilogue operand: 8 columns (16 bytes) per lane
 #pragma unroll
-        for (int it = 0; it < RP * CPR / 64; ++it) {
-            const int e = it * 64 + lane;
-            const int r = e / CPR, c = e % CPR;
-            const float4 w = st[r * CPR + (c ^ (r & 15))];
-            const int row = row0 + pass * RP + r, col = col0 + c * 4;
-            if (row < p.M && col < p.N) {
-                const float v[4] = {w.x, w.y, w.z, w.w};
-                store4<EPI>(p, row, col, v);
+            for (int it = 0; it < RP * CPR / 128; ++it) {
+                const int e = it * 64 + lane;
+                const int r = e / (CPR / 2), c = 2 * (e % (CPR / 2));
+                const float4 w0 = st[r * CPR + (c ^ (r & 15))];
+                const float4 w1 = st[r * CPR + ((c + 1) ^ (r & 15))];
+                const int row = row0 + pass * RP + r, col = col0 + c * 4;
+                if (row < p.M && col < p.N) {
+                    if (col + 8 <= p.N && (p.ldc & 7) == 0) {
+                        const uint4 v = make_uint4(pack2(w0.x, w0.y), pack2(w0.z, w0.w), pack2(w1.x, w1.y),
+                                                   pack2(w1.z, w1.w));
+                        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.C) + int64_t(row) * p.ldc + col) = v;
+                    } else {
+                        const float v0[4] = {w0.x, w0.y, w0.z, w0.w}, v1[4] = {w1.x, w1.y, w1.z, w1.w};
+                        store4<EPI>(p, row, col, v0);
+                        if (col + 4 < p.N) store4<EPI>(p, row, col + 4, v1);
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int it = 0; it < RP * CPR / 64; ++it) {
+                const int e = it * 64 + lane;
+                const int r = e / CPR, c = e % CPR;
+                const float4 w = st[r * CPR + (c ^ (r & 15))];
+                const int row = row0 + pass * RP + r, col = col0 + c * 4;
+                if (row < p.M && col < p.N) {
+                    const float v[4] = {w.x, w.y, w.z, w.w};
+                    store4<EPI>(p, row, col, v);
+                }
             }
         }
     });
