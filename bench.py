@@ -58,8 +58,8 @@ SHAPES = {
 # profiles/gemm_gateup_traffic_7b.md.  Valid only for the kernel sources it was
 # taken on (sha256 over the files in order): reported as null once they change.
 TRAFFIC = {"sources": ["layer_streaming_amd/csrc/gemm_nt.hip", "layer_streaming_amd/csrc/kcommon.h"],
-           "sha256": "c98b57b34579e146438b5afb13ff762b9f37f65cdb60672560d4baca098813cc",
-           "fetch_bytes": 3317856083, "write_bytes": 620756992}
+           "sha256": "1bef37c1b74e5bcd98f513ee2fa5ed6d9676e909c36ba6313ae60c4bbcb5648f",
+           "fetch_bytes": 3317871570, "write_bytes": 620756992}
 
 
 def traffic_bytes(config):
