@@ -139,6 +139,28 @@ def test_gemm_nt_large_tile_form(M, N, K):
     _elementwise_check(got, ref, A, B, "C", K)
 
 
+@pytest.mark.parametrize("ldc", [4044, 4048])
+def test_gemm_nt_large_tile_partial_column_chunk(ldc):
+    """bf16 output whose last 8-column chunk is cut by N (N = 4044), with a
+    leading dimension that does (4048) and does not (4044) allow 16-byte
+    stores; columns from N to ldc stay untouched."""
+    M, N, K = 4104, 4044, 136
+    log(f"gemm NT large-tile partial chunk M={M} N={N} K={K} ldc={ldc}")
+    A = synth.bf16_exact_normal(RNG, (M, K))
+    B = synth.bf16_exact_normal(RNG, (N, K))
+    ref = A.astype(np.float64) @ B.astype(np.float64).T
+    dA, dB = dev_bits(A), dev_bits(B)
+    dC = dev_zeros_bits((M, ldc))
+    mt.check(mt.lib.mt_k_gemm(0, 0, dA.data_ptr(), K, dB.data_ptr(), K, dC.data_ptr(), ldc, None, 0, None, 0,
+                              M, N, K, _stream()), "gemm")
+    _sync()
+    full = host_f32(dC)
+    got = full[:, :N]
+    assert_close(got, ref, "C")
+    _elementwise_check(got, ref, A, B, "C", K)
+    assert np.all(full[:, N:] == 0), "columns past N written"
+
+
 def test_gemm_nt_large_tile_epilogues():
     """Every epilogue of the 64-deep form on one ragged shape (partial last
     k-tile, partial row and column tiles), with leading dimensions wider than
