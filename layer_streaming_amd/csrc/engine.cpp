@@ -348,7 +348,9 @@ struct Ctx {
     // Modes: a one-micro-batch step copies the slab into G and runs Adam;
     // with micro-batches the first stores the slab into G, the middle ones
     // accumulate into G, the last accumulates and runs Adam.
-    enum { JOB_ADAM, JOB_STORE, JOB_ACCUM, JOB_ACCUM_ADAM };
+    // JOB_ADAM_ROWS / JOB_ADAM_EXCEPT: the input embedding's update split
+    // by rows (the rows the next batch gathers, then all the others).
+    enum { JOB_ADAM, JOB_STORE, JOB_ACCUM, JOB_ACCUM_ADAM, JOB_ADAM_ROWS, JOB_ADAM_EXCEPT };
     struct Job {
         int unit, slab;
         int64_t elems;
@@ -357,6 +359,7 @@ struct Ctx {
         int mode;
         int64_t off = 0;    // first tile element (a head chunk starts inside the tile)
         bool last = true;   // completes the unit's update of this step
+        std::shared_ptr<const std::vector<int32_t>> rows;  // JOB_ADAM_ROWS / _EXCEPT
     };
     std::deque<Job> jobs;
     std::vector<int64_t> adam_gen;  // updates applied per unit
@@ -368,6 +371,14 @@ struct Ctx {
     std::string worker_error;
     double adam_ms_acc = 0.0, pack_ms = 0.0;
     AdamStep cur_adam{};
+    // With cross_step the input embedding's update is held back until the
+    // next step's tokens are known (or until anything else needs the store):
+    // then the rows that step gathers are updated first, the others after.
+    bool emb_deferred = false;
+    AdamStep emb_adam{};
+    int64_t emb_step_id = 0;
+    int64_t emb_rows_issued = 0, emb_rows_done = 0;  // JOB_ADAM_ROWS jobs
+    bool emb_split = false;  // this step's gathers follow a split update
     // schedule state
     std::vector<int> slot_unit;
     int slot_ptr = 0, staging_ptr = 0;
@@ -726,7 +737,9 @@ void Ctx::slab_worker() {
             // depend on the order.  Equal ranks (one unit's micro-batch jobs,
             // the head's chunks) keep arrival order.  Without cross_step
             // every update completes inside the step: arrival order.
-            auto rank = [&](const Job& x) { return x.unit == lay.embed() ? -1 : x.unit; };
+            auto rank = [&](const Job& x) {
+                return x.mode == JOB_ADAM_ROWS ? -2 : x.unit == lay.embed() ? -1 : x.unit;
+            };
             auto it = jobs.begin();
             if (opt.cross_step)
                 it = std::min_element(jobs.begin(), jobs.end(),
@@ -752,8 +765,36 @@ void Ctx::slab_worker() {
             tp.m += j.off;
             tp.v += j.off;
             const uint16_t* src = j.slab >= 0 ? reinterpret_cast<const uint16_t*>(slabs[j.slab]) : tp.g;
+            const int64_t d = lay.sh.d_model;
             switch (j.mode) {
                 case JOB_ADAM: adam_unit(*adam_pool, tp, src, j.elems, j.a); break;
+                case JOB_ADAM_ROWS:
+                case JOB_ADAM_EXCEPT: {
+                    // one row of the embedding tile at a time
+                    auto row_adam = [&](int64_t r) {
+                        TilePtrs q = tp;
+                        q.w += r * d;
+                        q.g += r * d;
+                        q.master += r * d;
+                        q.m += r * d;
+                        q.v += r * d;
+                        adam_range(q, q.g, 0, d, j.a);
+                    };
+                    const std::vector<int32_t>& rows = *j.rows;
+                    if (j.mode == JOB_ADAM_ROWS) {
+                        adam_pool->parallel_for(int64_t(rows.size()), 16, [&](int64_t b, int64_t e) {
+                            for (int64_t i = b; i < e; ++i) row_adam(rows[size_t(i)]);
+                        });
+                    } else {
+                        std::vector<char> skip(size_t(j.elems / d), 0);
+                        for (int32_t r : rows) skip[size_t(r)] = 1;
+                        adam_pool->parallel_for(j.elems / d, 16, [&](int64_t b, int64_t e) {
+                            for (int64_t r = b; r < e; ++r)
+                                if (!skip[size_t(r)]) row_adam(r);
+                        });
+                    }
+                    break;
+                }
                 case JOB_STORE: parallel_copy(*adam_pool, tp.g, src, j.elems * 2); break;
                 case JOB_ACCUM: accum_unit(*adam_pool, tp.g, src, j.elems); break;
                 default:
@@ -772,7 +813,9 @@ void Ctx::slab_worker() {
                 worker_error = err;
             }
             if (j.slab >= 0) free_slabs.push_back(j.slab);
-            if (j.last && (j.mode == JOB_ADAM || j.mode == JOB_ACCUM_ADAM)) ++adam_gen[j.unit];
+            if (j.last && (j.mode == JOB_ADAM || j.mode == JOB_ACCUM_ADAM || j.mode == JOB_ADAM_EXCEPT))
+                ++adam_gen[j.unit];
+            if (j.mode == JOB_ADAM_ROWS) ++emb_rows_done;
             --jobs_pending;
         }
         free_cv.notify_all();
@@ -886,6 +929,12 @@ int Ctx::wait_adam(int unit) {
 
 int Ctx::drain_jobs() {
     std::unique_lock<std::mutex> lk(q_mu);
+    if (emb_deferred) {  // the whole update of the input embedding, unsplit
+        jobs.push_back({lay.embed(), -1, lay.units[lay.embed()].elems, emb_adam, emb_step_id, JOB_ADAM});
+        ++jobs_pending;
+        emb_deferred = false;
+        q_cv.notify_one();
+    }
     free_cv.wait(lk, [&] { return jobs_pending == 0; });
     if (worker_status != MT_OK) {
         failed = true;
@@ -1378,9 +1427,48 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
         {
             const int le = ensure_loaded(lay.embed());
             if (le != MT_OK) return le;
-            // The previous step's update of E_in (queued with cross_step) first.
-            const int we = wait_adam(lay.embed());
-            if (we != MT_OK) return we;
+            // The previous step's update of E_in first.  Held back with
+            // cross_step: the rows this step gathers (over all its
+            // micro-batches) are updated now, the others are queued behind
+            // them (they are needed by the next step's gather, or by the end
+            // of this step's backward, which overwrites G).
+            if (mb == 0) emb_split = false;
+            if (mb == 0) {
+                std::unique_lock<std::mutex> lk(q_mu);
+                if (emb_deferred) {
+                    auto rows = std::make_shared<std::vector<int32_t>>();
+                    std::vector<char> seen(size_t(V), 0);
+                    for (int64_t t = 0; t < int64_t(n_micro) * T; ++t)
+                        if (!seen[size_t(tokens[t])]) {
+                            seen[size_t(tokens[t])] = 1;
+                            rows->push_back(tokens[t]);
+                        }
+                    const int64_t ne = lay.units[lay.embed()].elems;
+                    Job a{lay.embed(), -1, ne, emb_adam, emb_step_id, JOB_ADAM_ROWS, 0, false, rows};
+                    Job b{lay.embed(), -1, ne, emb_adam, emb_step_id, JOB_ADAM_EXCEPT, 0, true, rows};
+                    jobs.push_back(a);
+                    jobs.push_back(b);
+                    jobs_pending += 2;
+                    ++emb_rows_issued;
+                    emb_deferred = false;
+                    emb_split = true;
+                    q_cv.notify_all();
+                    const auto t0 = Clock::now();
+                    free_cv.wait(lk, [&] { return emb_rows_done >= emb_rows_issued || worker_status != MT_OK; });
+                    adam_wait_ms += ms_since(t0);
+                    if (worker_status != MT_OK) {
+                        failed = true;
+                        set_error(worker_error);
+                        const int st = worker_status;
+                        worker_status = MT_OK;
+                        return st;
+                    }
+                }
+            }
+            if (!emb_split) {  // (after a split, every micro-batch's rows are updated)
+                const int we = wait_adam(lay.embed());
+                if (we != MT_OK) return we;
+            }
             const TilePtrs e = tile_ptrs(store, lay, lay.embed(), wblock);
             pack_pool->parallel_for(T, 64, [&](int64_t b, int64_t en) {
                 for (int64_t t = b; t < en; ++t)
@@ -1540,6 +1628,10 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
         HIPC(hsync(loss_done));
         loss_sum += double(*loss_pin);
         t_bwd = ms_since(t_start);
+        if (mb == 0) {  // the previous step's update of E_in reads G: it must be over
+            const int we = wait_adam(lay.embed());
+            if (we != MT_OK) return we;
+        }
         const TilePtrs e = tile_ptrs(store, lay, lay.embed(), wblock);
         if (mb == 0) {
             // Clear last step's rows; rows not listed are zero.
@@ -1587,7 +1679,14 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
         failed = true;
         MT_FAIL(MT_E_INTERNAL, "injected slab-worker fault at unit %d", lay.embed());
     }
-    enqueue_job(lay.embed(), -1, JOB_ADAM);
+    if (opt.cross_step) {
+        std::lock_guard<std::mutex> lk(q_mu);
+        emb_deferred = true;
+        emb_adam = cur_adam;
+        emb_step_id = step + 1;
+    } else {
+        enqueue_job(lay.embed(), -1, JOB_ADAM);
+    }
     // Synchronous step: every update lands before returning.  cross_step:
     // they run on; report a worker error that has already happened.
     int jr = MT_OK;
