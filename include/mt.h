@@ -94,9 +94,11 @@ typedef struct mt_options {
     int32_t cross_step;          /* 1: mt_train_step returns once the loss is known and every
                                     unit's Adam is queued; Adam runs on, lowest unit first, and the
                                     next step streams a unit only after its update has landed
-                                    (the next forward overlaps the Adam tail).  Same results as 0.
-                                    mt_sync, and every entry that reads or writes the store, wait
-                                    for the queued updates first.  0 (default): synchronous step */
+                                    (the next forward overlaps the Adam tail).  The input
+                                    embedding's update waits for the next step's tokens, whose
+                                    rows it updates first.  Same results as 0.  mt_sync, and every
+                                    entry that reads or writes the store, wait for the queued
+                                    updates first.  0 (default): synchronous step */
     int32_t ckpt_interval;       /* k >= 1: the forward keeps every k-th layer input (layers 0, k,
                                     2k, ...); the backward restores a block's first input, re-runs
                                     the forward of the block's first k-1 layers to rebuild the
