@@ -5,7 +5,11 @@ of 128, SwiGLU ffn 18944, vocab 152064, untied embeddings), batch 8 x seq
 1024 of seeded uniform token ids, weights N(0, 0.02^2) in bf16 from seed 1234,
 host store of 16 bytes per parameter.  One step = streamed forward of every
 layer, the fused LM head, recompute + backward of every layer with gradient
-offload, and the host Adam over all 7.6B parameters (synchronous).
+offload, and the host Adam over all 7.6B parameters.  Defaults: cross-step
+pipelining (the next forward overlaps this step's host Adam; the timed region
+ends with a sync, so every step's update is timed), the weight regions in one
+page-locked block, layer-sized LM-head chunks, two weight slots, 16 gradient
+slabs.
 
 Prints ONE JSON line on stdout (progress goes to stderr):
   value            whole-step training tokens/s (inputs resident on the host
@@ -315,7 +319,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--host-threads", type=int, default=0)
     ap.add_argument("--slots", type=int, default=2)
-    ap.add_argument("--slabs", type=int, default=12)
+    # 16 gradient slabs: with the pages' 12 the host Adam (slower than the
+    # backward on this host) holds every slab near the end of the backward and
+    # the gradient copies stall (measured 9.72K against 10.28K tokens/s,
+    # alternating runs on one box); --slabs 12 runs the pages' pool
+    ap.add_argument("--slabs", type=int, default=16)
     ap.add_argument("--slot-mode", type=int, default=0)
     ap.add_argument("--resident", type=int, default=0)
     ap.add_argument("--pin-store", type=int, default=0)
