@@ -30,6 +30,7 @@
 // which is idle in forward, and copied back with the weights in backward.
 #include "engine.h"
 
+#include <algorithm>
 #include <chrono>
 #include <cstdlib>
 #include <cstring>
@@ -365,6 +366,7 @@ struct Ctx {
     std::vector<int64_t> adam_gen;  // updates applied per unit
     double adam_wait_ms = 0.0;
     std::vector<int> free_slabs;
+    std::vector<char> slab_landed;  // the slab's copy is known complete (set by the offload thread)
     bool stop = false;
     int jobs_pending = 0;
     int worker_status = MT_OK;
@@ -619,6 +621,7 @@ int Ctx::init(const mt_shape& sh, const mt_options& o, void* arena_, uint64_t by
         if (!p) MT_FAIL(MT_E_NOMEM, "cannot allocate pinned gradient slab %d", k);
         slabs.push_back(p);
         free_slabs.push_back(k);
+        slab_landed.push_back(0);
     }
     const uint64_t T = uint64_t(opt.max_batch) * opt.max_seq;
     const uint64_t td = al4k(T * sh.d_model * 2);
@@ -740,10 +743,26 @@ void Ctx::slab_worker() {
             auto rank = [&](const Job& x) {
                 return x.mode == JOB_ADAM_ROWS ? -2 : x.unit == lay.embed() ? -1 : x.unit;
             };
+            // Only the newest job's slab can still be in flight (a slab's
+            // copy is submitted after the previous one completed), so a
+            // lowest-rank pick would often wait for it while an older job's
+            // gradients sit ready: take the lowest rank among the jobs the
+            // offload thread has seen land, and wait only when there is none.  The earliest job of
+            // the chosen rank goes first, so equal ranks keep arrival order.
             auto it = jobs.begin();
-            if (opt.cross_step)
-                it = std::min_element(jobs.begin(), jobs.end(),
-                                      [&](const Job& x, const Job& y) { return rank(x) < rank(y); });
+            if (opt.cross_step) {
+                // (no event query here: under the queue lock it was seen to
+                // stall for as long as the copy the offload thread waits on)
+                auto landed = [&](const Job& x) { return x.slab < 0 || slab_landed[size_t(x.slab)] != 0; };
+                auto best = jobs.end();
+                for (auto k = jobs.begin(); k != jobs.end(); ++k)
+                    if ((best == jobs.end() || rank(*k) < rank(*best)) && landed(*k)) best = k;
+                if (best == jobs.end())
+                    best = std::min_element(jobs.begin(), jobs.end(),
+                                            [&](const Job& x, const Job& y) { return rank(x) < rank(y); });
+                it = std::find_if(jobs.begin(), jobs.end(), [&](const Job& x) { return rank(x) == rank(*best); });
+                host_rec("host_pick", it->unit, int(jobs.size()) * 100 + int(landed(*it)), Clock::now());
+            }
             j = *it;
             jobs.erase(it);
         }
@@ -838,6 +857,10 @@ void Ctx::offload_worker() {
         // One gradient copy in flight at a time (the previous slab's copy
         // cannot have been re-recorded: only this thread acquires slabs).
         if (off_prev_slab >= 0) e = hsync(slab_done[off_prev_slab]);
+        if (e == hipSuccess && off_prev_slab >= 0 && off_prev_slab != k) {
+            std::lock_guard<std::mutex> lk(q_mu);
+            slab_landed[size_t(off_prev_slab)] = 1;
+        }
         off_prev_slab = k;
         hipEvent_t a = nullptr, b = nullptr;
         if (e == hipSuccess) e = hipStreamWaitEvent(st_g, bwd_done[r.ga].e, 0);
@@ -870,6 +893,14 @@ void Ctx::offload_worker() {
             ++off_issued;
         }
         off_cv.notify_all();
+        // The next copy waits for this one anyway: wait here, so the slab
+        // worker learns that the gradients landed also when no further
+        // request follows (the backward's last unit).  An error is left to
+        // the worker's own wait on the slab.
+        if (e == hipSuccess && hsync(slab_done[k]) == hipSuccess) {
+            std::lock_guard<std::mutex> lk(q_mu);
+            slab_landed[size_t(k)] = 1;
+        }
     }
 }
 
@@ -895,6 +926,7 @@ int Ctx::acquire_slab() {
         auto it = std::min_element(free_slabs.begin(), free_slabs.end());
         k = *it;
         free_slabs.erase(it);
+        slab_landed[size_t(k)] = 0;
     }
     host_rec("host_slab_wait", -1, k, t0);
     return k;
