@@ -312,7 +312,7 @@ def cpu_baseline(ctx, cfg, mt):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=10)  # ~8 s timed: the closing sync drains one step's host Adam once
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="7b", choices=sorted(SHAPES))
     ap.add_argument("--no-profile", action="store_true", help="skip per-kernel HIP event timing")
