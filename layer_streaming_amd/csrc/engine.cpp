@@ -367,6 +367,7 @@ struct Ctx {
     double adam_wait_ms = 0.0;
     std::vector<int> free_slabs;
     std::vector<char> slab_landed;  // the slab's copy is known complete (set by the offload thread)
+    bool emb_urgent = false;        // a thread waits for the input embedding's update
     bool stop = false;
     int jobs_pending = 0;
     int worker_status = MT_OK;
@@ -740,8 +741,13 @@ void Ctx::slab_worker() {
             // depend on the order.  Equal ranks (one unit's micro-batch jobs,
             // the head's chunks) keep arrival order.  Without cross_step
             // every update completes inside the step: arrival order.
+            // The part of a split embedding update that the next gather does
+            // not read goes last (it fills the worker's idle time before the
+            // head's gradients land), until a thread has to wait for it.
             auto rank = [&](const Job& x) {
-                return x.mode == JOB_ADAM_ROWS ? -2 : x.unit == lay.embed() ? -1 : x.unit;
+                if (x.mode == JOB_ADAM_ROWS) return -2;
+                if (x.mode == JOB_ADAM_EXCEPT) return emb_urgent ? -1 : lay.embed() + 1;
+                return x.unit == lay.embed() ? -1 : x.unit;
             };
             // Only the newest job's slab can still be in flight (a slab's
             // copy is submitted after the previous one completed), so a
@@ -765,6 +771,7 @@ void Ctx::slab_worker() {
             }
             j = *it;
             jobs.erase(it);
+            if (j.mode == JOB_ADAM_EXCEPT) emb_urgent = false;
         }
         int status = MT_OK;
         std::string err;
@@ -947,6 +954,7 @@ void Ctx::enqueue_job(int unit, int slab, int mode, int64_t off, int64_t elems, 
 int Ctx::wait_adam(int unit) {
     std::unique_lock<std::mutex> lk(q_mu);
     const auto t0 = Clock::now();
+    if (unit == lay.embed() && adam_gen[unit] < step) emb_urgent = true;
     free_cv.wait(lk, [&] { return adam_gen[unit] >= step || worker_status != MT_OK; });
     adam_wait_ms += ms_since(t0);
     if (worker_status != MT_OK) {
