@@ -187,7 +187,11 @@ int mt_init(const mt_shape* shape, const mt_options* opt, void* gpu_arena, uint6
  * context is created, every step appends its intervals (compute visits with
  * their kind and unit, H2D and D2H copies with their bytes; device-clock ms
  * from the step's first event) to <path> as CSV lines
- * step,kind,visit,unit,start_ms,end_ms,bytes. */
+ * step,kind,visit,unit,start_ms,end_ms,bytes.  Host-side spans follow with
+ * the kind host_job (one update job; visit = mode*100 + slab), host_pick (the
+ * worker's choice; visit = jobs queued*100 + whether its gradients had
+ * landed), host_slab_wait, host_staging_wait and host_pack, on the host
+ * clock from the step's start. */
 int mt_train_step(mt_ctx* ctx, const int32_t* tokens, const int32_t* labels, int32_t batch,
                   int32_t seq, float* loss_out, mt_stats* stats_out);
 
