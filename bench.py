@@ -49,11 +49,16 @@ SHAPES = {
                  batch=1, seq=131072,
                  workload="long-context step: 8 layers of the 7B-shaped layer, batch 1 x seq 131072, causal, "
                           "layer-streamed with host Adam"),
-    "70b_x4": dict(n_layers=4, d_model=8192, n_heads=64, n_kv_heads=8, head_dim=128, ffn_dim=28672, vocab=128256,
-                   batch=4, seq=2048,
-                   workload="70B-layer-shaped decoder, 4 layers, d_model 8192, 64q/8kv heads x 128, ffn 28672, "
-                            "vocab 128256, batch 4 x seq 2048, layer-streamed train step with host Adam"),
+    "14b": dict(n_layers=48, d_model=5120, n_heads=40, n_kv_heads=8, head_dim=128, ffn_dim=13824, vocab=152064,
+                batch=4, seq=2048,
+                workload="14B-shaped decoder, 48 layers, d_model 5120, 40q/8kv heads x 128, ffn 13824, "
+                         "vocab 152064, batch 4 x seq 2048, layer-streamed train step with host Adam"),
+    "70b": dict(n_layers=4, d_model=8192, n_heads=64, n_kv_heads=8, head_dim=128, ffn_dim=28672, vocab=128256,
+                batch=4, seq=2048,
+                workload="70B-layer-shaped decoder, {L} layers, d_model 8192, 64q/8kv heads x 128, ffn 28672, "
+                         "vocab 128256, batch 4 x seq 2048, layer-streamed train step with host Adam"),
 }
+SHAPES["70b_x4"] = SHAPES["70b"]
 
 
 # HBM bytes per launch of the dominant kernel (the gate|up GEMM at the 7B
@@ -116,9 +121,11 @@ def hbm_bytes(cfg, T):
     return {
         "rms1_fwd": T * d * 2 + 2 * T * d * 2 + T * 4,     # x in; n (bf16) and n (fp16) out; rstd
         "rms2_fwd": T * d * 4 + T * d * 2 + T * 4,         # fp32 h1 in; n2 out; rstd
-        "rope_fwd": T * nqkv * 4 + T * nqkv * 2,           # fp32 projection in; q, k fp16 and v bf16 out
+        "rope_fwd": T * nqkv * 4 + T * nqkv * 2,           # fp32 projection in; q, k, v fp16 out
         "swiglu_fwd": T * 2 * F * 2 + T * F * 2,           # gate|up in; m out
         "swiglu_bwd": T * F * 2 + T * 2 * F * 2 + T * 2 * F * 2,  # dm, gate|up in; dgate|dup out
+        "rms1_bwd": 4 * T * d * 2 + T * 4,                # dn, x, residual in; dx out; rstd
+        "rms2_bwd": T * d * 2 + T * d * 4 + 2 * T * d * 2 + T * 4,  # dn, fp32 h1, residual in; dh1 out
     }
 
 
@@ -152,6 +159,49 @@ def model_flops_per_step(cfg, T, S):
     return 6 * p_lin * L * T + 6 * T * d * V + 3 * attn_fwd * L
 
 
+def pages_flops_per_step(cfg, T, S):
+    """The pages' throughput convention, for comparability only: 6 N T over
+    all N parameters (embeddings included) plus 12 L Hq hd S T for the
+    attention scores and values (non-causal, forward and backward)."""
+    L, d, F, V = cfg["n_layers"], cfg["d_model"], cfg["ffn_dim"], cfg["vocab"]
+    hq, hkv, hd = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    n_total = L * (d * hq * hd + 2 * d * hkv * hd + hq * hd * d + 3 * d * F + 2 * d) + 2 * V * d + d
+    return 6 * n_total * T + 12 * L * hq * hd * S * T
+
+
+def host_mem_available():
+    """MemAvailable of /proc/meminfo in bytes (None when unreadable)."""
+    try:
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemAvailable:"):
+                    return int(line.split()[1]) * 1024
+    except OSError:
+        pass
+    return None
+
+
+def host_info():
+    """CPU model, sockets, cores, threads and NUMA layout (lscpu), and the
+    CPUs this process may run on."""
+    import subprocess
+    info = {"cpus_usable": len(os.sched_getaffinity(0))}
+    try:
+        r = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10)
+        keys = {"Model name": "model", "Socket(s)": "sockets", "Core(s) per socket": "cores_per_socket",
+                "Thread(s) per core": "threads_per_core", "NUMA node(s)": "numa_nodes", "CPU(s)": "cpus"}
+        for line in r.stdout.splitlines():
+            k, _, v = line.partition(":")
+            k, v = k.strip(), v.strip()
+            if k in keys:
+                info[keys[k]] = int(v) if v.isdigit() else v
+            elif k.startswith("NUMA node") and k.endswith("CPU(s)"):
+                info.setdefault("numa_cpus", {})[k.split()[1]] = v
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return info
+
+
 def traffic_probe(torch, mt, cfg):
     """The dominant GEMM (gate|up, NT, bf16, random operands) three times,
     then a 1 GiB fill and three 1 GiB device copies as the counters'
@@ -176,29 +226,30 @@ def traffic_probe(torch, mt, cfg):
 def attention_probe(torch, mt, cfg, S):
     """The attention kernels alone at one sequence of length S with the
     workload's heads: forward and backward three times each on seeded
-    synthetic q, k (fp16, with the bf16 copy the recompute writes), v, dO
-    (bf16); HIP-event times and TFLOP/s (causal: 4 Hq hd S(S+1)/2 for the
+    synthetic q, k, v (fp16) and dO (bf16); HIP-event times and TFLOP/s
+    (causal: 4 Hq hd S(S+1)/2 for the
     forward, 2.5 times that for the backward)."""
     Hq, Hkv, hd = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]
-    ld, nq, nr = (Hq + 2 * Hkv) * hd, Hq * hd, (Hq + Hkv) * hd
+    ld, nq = (Hq + 2 * Hkv) * hd, Hq * hd
     g = torch.Generator(device="cpu").manual_seed(0)
     qkv = torch.randn(S, ld, generator=g).to(torch.float16).cuda().view(torch.int16)
-    qkb = torch.randn(S, nr, generator=g).to(torch.bfloat16).cuda().view(torch.int16)
     do = torch.randn(S, nq, generator=g).to(torch.bfloat16).cuda().view(torch.int16)
     o = torch.zeros(S, nq, dtype=torch.int16, device="cuda")
     lse = torch.zeros(Hq * S, device="cuda")
-    dsum = torch.zeros_like(lse)
+    work = torch.zeros(int(mt.lib.mt_k_attn_bwd_work_bytes(1, S, Hq, hd)), dtype=torch.uint8, device="cuda")
     dqkv = torch.zeros(S, ld, dtype=torch.int16, device="cuda")
+    dqk32 = torch.zeros(S, ld, dtype=torch.float32, device="cuda")
     st = torch.cuda.current_stream()
     s = st.cuda_stream
 
     def fwd():
-        mt.check(mt.lib.mt_k_attn_fwd(qkv.data_ptr(), ld, o.data_ptr(), nq, lse.data_ptr(), 1, S, Hq, Hkv, hd, s),
+        mt.check(mt.lib.mt_k_attn_fwd(qkv.data_ptr(), ld, o.data_ptr(), nq, lse.data_ptr(), 1, S, Hq, Hkv, hd, None, s),
                  "attn_fwd")
 
-    def bwd():
+    def bwd():  # as the step runs it: dQ, dK in fp32
         mt.check(mt.lib.mt_k_attn_bwd(qkv.data_ptr(), ld, o.data_ptr(), do.data_ptr(), nq, lse.data_ptr(),
-                                      dsum.data_ptr(), dqkv.data_ptr(), ld, 1, S, Hq, Hkv, hd, qkb.data_ptr(), nr, s),
+                                      work.data_ptr(), dqkv.data_ptr(), ld, 1, S, Hq, Hkv, hd, dqk32.data_ptr(), ld,
+                                      None, s),
                  "attn_bwd")
     fl = 4.0 * Hq * hd * S * (S + 1) / 2
     out = {}
@@ -225,11 +276,13 @@ def ablations(torch, mt, shape, cfg, args, tokens, labels, base_value):
     res = {}
     for name, kw in (("one_weight_slot", dict(n_weight_slots=1)), ("one_grad_slab", dict(n_grad_slabs=1)),
                      ("combined_slots", dict(slot_mode=1))):
-        opt = mt.default_options(max_batch=B, max_seq=S, host_threads=args.host_threads, seed=synth.SEED_WEIGHTS,
-                                 cross_step=args.cross_step, pin_weights=args.pin_weights, **kw)
+        base = dict(host_threads=args.host_threads, seed=synth.SEED_WEIGHTS, cross_step=args.cross_step,
+                    pin_weights=args.pin_weights, head_vocab_chunk=args.head_vocab_chunk, n_grad_slabs=args.slabs)
+        base.update(kw)
+        opt = mt.default_options(max_batch=B, max_seq=S, **base)
         arena_bytes, _, _ = mt.workspace_bytes(shape, opt)
         arena = torch.empty(arena_bytes, dtype=torch.uint8, device="cuda")
-        ctx = mt.Context(shape, opt, arena.data_ptr(), arena_bytes)
+        ctx = mt.Context(shape, opt, arena.data_ptr(), arena_bytes, [st.cuda_stream for st in bench_streams(torch)])
         ctx.train_step(tokens, labels)
         ctx.sync()
         torch.cuda.synchronize()
@@ -303,10 +356,126 @@ def cpu_baseline(ctx, cfg, mt):
     T = cfg["batch"] * cfg["seq"]
     t_step = (L * t_layer + t_head) * (T / Ts) + t_adam
     cores = len(os.sched_getaffinity(0))
-    return {"value": T / t_step, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": T / t_step, "unit": "tokens/s", "cores": cores, "kind": "oracle", "host": host_info(),
             "sample": f"float64 numpy oracle: one decoder layer (fwd, recompute, bwd) and the LM head at 1x{Ss} "
                       f"tokens, Adam over a 16M-element slice; step extrapolated as L*layer + head scaled to "
                       f"{T} tokens + Adam over all parameters ({t_step:.1f} s per step)"}
+
+
+def step_batches(cfg, n_micro, k):
+    """Seeded token ids of timed or warm-up step k: a fresh batch every step
+    (the attention forward's rescaling depends on the data)."""
+    from layer_streaming_amd import synth
+    B, S = cfg["batch"], cfg["seq"]
+    tl = [synth.tokens_labels(synth.SEED_TOKENS + 1000 * k + j, B, S, cfg["vocab"]) for j in range(n_micro)]
+    if n_micro == 1:
+        return tl[0]
+    return np.stack([t for t, _ in tl]), np.stack([lb for _, lb in tl])
+
+
+_STREAMS = []
+
+
+def bench_streams(torch):
+    """The three streams (compute, weight H2D, gradient D2H) every context of
+    this process runs on, created once: the runtime maps streams onto a few
+    hardware queues in creation order, and two of the three sharing a queue
+    would serialize compute and copies (seen as an overlap ratio near zero on
+    the second context of a process that created fresh streams for it)."""
+    if not _STREAMS:
+        _STREAMS.extend(torch.cuda.Stream() for _ in range(3))
+    return _STREAMS
+
+
+def run_workload(torch, mt, cfg, args, opt_kw, steps, warmup, keep=False):
+    """One context on the workload: init, warm-up steps, timed steps (fresh
+    tokens each), closing sync inside the timed region.  Refuses, before
+    allocating anything, when the host store and pinned memory would not fit
+    the host's available memory.  Returns (result dict, ctx, arena); the
+    context is closed unless keep."""
+    from layer_streaming_amd import synth
+    B, S = cfg["batch"], cfg["seq"]
+    T = B * S
+    nm = args.micro
+    shape = mt.make_shape(cfg["n_layers"], cfg["d_model"], cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"],
+                          cfg["ffn_dim"], cfg["vocab"])
+    opt = mt.default_options(max_batch=B, max_seq=S, seed=synth.SEED_WEIGHTS, **opt_kw)
+    arena_bytes, pinned_bytes, store_bytes = mt.workspace_bytes(shape, opt)
+    # resident host bytes: the store (its W regions stay untouched when they
+    # live in the pinned block), the pinned memory, the fp32 embedding
+    # scatter accumulator, 8 GB for the process itself
+    w_bytes = 2 * (store_bytes // 16)
+    need = store_bytes - (w_bytes if opt_kw.get("pin_weights") else 0) + pinned_bytes + \
+        4 * cfg["vocab"] * cfg["d_model"] + (8 << 30)
+    avail = host_mem_available()
+    log(f"[{cfg['n_layers']} layers] arena {arena_bytes / 1e9:.2f} GB, pinned {pinned_bytes / 1e9:.2f} GB, "
+        f"store {store_bytes / 1e9:.2f} GB; host needs ~{need / 1e9:.1f} GB, available "
+        f"{avail / 1e9 if avail else float('nan'):.1f} GB")
+    if avail is not None and need > avail:
+        return {"refused": "host memory", "need_bytes": int(need), "available_bytes": int(avail)}, None, None
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    arena = torch.empty(arena_bytes, dtype=torch.uint8, device="cuda")
+    streams = bench_streams(torch)
+    t0 = time.time()
+    ctx = mt.Context(shape, opt, arena.data_ptr(), arena_bytes,
+                     (None, None, None) if args.own_streams else [s.cuda_stream for s in streams])
+    torch.cuda.synchronize()
+    mem_delta = int(free0 - torch.cuda.mem_get_info()[0])
+    log(f"init (host store + seeded weights) {time.time() - t0:.1f} s; device memory taken {mem_delta / 1e9:.3f} GB")
+
+    def one_step(k):
+        t, lb = step_batches(cfg, nm, k)
+        return ctx.train_step(t, lb) if nm == 1 else ctx.train_step_accum(t, lb)
+
+    for i in range(warmup):
+        loss, st = one_step(i)
+        log(f"warmup {i}: loss {loss:.4f} step {st.step_ms:.0f} ms")
+    ctx.sync()  # queued host updates (cross_step) land before the clock starts
+    torch.cuda.synchronize()
+    stats = []
+    t0 = time.perf_counter()
+    for i in range(steps):
+        loss, st = one_step(warmup + i)
+        stats.append(mt.stats_dict(st))
+        log(f"step {i}: loss {loss:.4f} step {st.step_ms:.0f} ms (fwd {st.fwd_ms:.0f} head {st.head_ms:.0f} "
+            f"bwd {st.bwd_ms:.0f} adam tail {st.adam_tail_ms:.0f}; adam busy {st.adam_ms:.0f}, "
+            f"pack {st.pack_ms:.0f}; waited for adam {st.adam_wait_ms:.0f}; overlap {st.overlap_ratio:.2f})")
+    ctx.sync()  # every step's host Adam is inside the timed region
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    res = {"value": nm * T * steps / elapsed, "ms_per_step": elapsed * 1e3 / steps, "stats": stats,
+           "mem_delta": mem_delta, "loss": float(loss), "opt": dict(opt_kw)}
+    if not keep:
+        ctx.close()
+        ctx = None
+        del arena
+        arena = None
+        torch.cuda.empty_cache()
+    return res, ctx, arena
+
+
+def pcie_block(stats):
+    """Transfer and overlap figures (device clock, averaged over timed steps)."""
+    def mean(k, i=None):
+        return float(np.mean([s[k] if i is None else s[k][i] for s in stats]))
+    h2d_b, h2d_ms, d2h_b, d2h_ms = mean("h2d_bytes"), mean("h2d_busy_ms"), mean("d2h_bytes"), mean("d2h_busy_ms")
+    phases = ("fwd", "head", "bwd")
+    x_ms, ov_ms = mean("copy_union_ms"), mean("overlap_ms")
+    return {"h2d_GBps": round(h2d_b / (h2d_ms / 1e3) / 1e9, 2) if h2d_ms else None,
+            "d2h_GBps": round(d2h_b / (d2h_ms / 1e3) / 1e9, 2) if d2h_ms else None,
+            "h2d_GB_per_step": round(h2d_b / 1e9, 3), "d2h_GB_per_step": round(d2h_b / 1e9, 3),
+            "peak_GBps": PCIE_GEN5_X16_GBS,
+            "h2d_frac_of_peak_while_busy": round(h2d_b / (h2d_ms / 1e3) / 1e9 / PCIE_GEN5_X16_GBS, 3) if h2d_ms else None,
+            "h2d_busy_frac_of_step": round(mean("pcie_busy_frac"), 3),
+            "overlap_ratio": round(mean("overlap_ratio"), 3),
+            "transfer_hidden_frac": round(ov_ms / x_ms, 3) if x_ms else None,
+            "compute_union_ms": round(mean("compute_union_ms"), 1), "copy_union_ms": round(x_ms, 1),
+            "overlap_by_phase": {ph: round(mean("overlap_phase", i), 3) for i, ph in enumerate(phases)},
+            "exposed_transfer_ms_by_phase": {ph: round(mean("exposed_transfer_ms", i), 1)
+                                             for i, ph in enumerate(phases)},
+            "switch_gap_ms_median_by_phase": {ph: round(mean("switch_gap_ms", i), 3) for i, ph in enumerate(phases)},
+            "device_idle_ms_by_phase": {ph: round(mean("device_idle_ms", i), 1) for i, ph in enumerate(phases)}}
 
 
 def main():
@@ -315,8 +484,15 @@ def main():
     ap.add_argument("--steps", type=int, default=10)  # ~8 s timed: the closing sync drains one step's host Adam once
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="7b", choices=sorted(SHAPES))
+    ap.add_argument("--layers", type=int, default=0, help="override the workload's depth")
+    ap.add_argument("--depths", default="",
+                    help="comma-separated depths: run the workload at each depth in a fresh context, one after "
+                         "the other, and report tokens/s and the device memory taken per depth (70b: 4,8)")
     ap.add_argument("--no-profile", action="store_true", help="skip per-kernel HIP event timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-pages-config", action="store_true",
+                    help="skip the second timed run on the pages' pinned footprint (pageable W packed into two "
+                         "pinned staging buffers, 12 gradient slabs)")
     ap.add_argument("--host-threads", type=int, default=0)
     ap.add_argument("--slots", type=int, default=2)
     # 16 gradient slabs: with the pages' 12 the host Adam (slower than the
@@ -356,64 +532,42 @@ def main():
         sys.exit(2)
 
     import torch
-    from layer_streaming_amd import mt, synth
-    cfg = SHAPES[args.config]
+    from layer_streaming_amd import mt
+    cfg = dict(SHAPES[args.config])
+    if args.layers:
+        cfg["n_layers"] = args.layers
+    cfg["workload"] = cfg["workload"].format(L=cfg["n_layers"])
     if args.traffic_probe:
         traffic_probe(torch, mt, cfg)
         return
     if args.attn_probe:
         attention_probe(torch, mt, cfg, args.attn_probe)
         return
+    torch.cuda.init()
+    opt_kw = dict(profile_kernels=0 if args.no_profile else 1, host_threads=args.host_threads,
+                  n_weight_slots=args.slots, n_grad_slabs=args.slabs, slot_mode=args.slot_mode,
+                  resident=args.resident, pin_store=args.pin_store, cross_step=args.cross_step,
+                  pin_weights=args.pin_weights, head_vocab_chunk=args.head_vocab_chunk)
+    if args.depths:
+        depth_sweep(torch, mt, cfg, args, opt_kw)
+        return
     B, S = cfg["batch"], cfg["seq"]
     T = B * S
-    shape = mt.make_shape(cfg["n_layers"], cfg["d_model"], cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"],
-                          cfg["ffn_dim"], cfg["vocab"])
-    opt = mt.default_options(max_batch=B, max_seq=S, profile_kernels=0 if args.no_profile else 1,
-                             host_threads=args.host_threads, n_weight_slots=args.slots, n_grad_slabs=args.slabs,
-                             slot_mode=args.slot_mode, resident=args.resident, pin_store=args.pin_store,
-                             cross_step=args.cross_step, pin_weights=args.pin_weights,
-                             head_vocab_chunk=args.head_vocab_chunk, seed=synth.SEED_WEIGHTS)
-    arena_bytes, pinned_bytes, store_bytes = mt.workspace_bytes(shape, opt)
-    log(f"arena {arena_bytes / 1e9:.2f} GB, pinned {pinned_bytes / 1e9:.2f} GB, store {store_bytes / 1e9:.2f} GB")
-    torch.cuda.init()
-    free0, _ = torch.cuda.mem_get_info()
-    arena = torch.empty(arena_bytes, dtype=torch.uint8, device="cuda")
-    streams = [torch.cuda.Stream() for _ in range(3)]
-    t0 = time.time()
-    ctx = mt.Context(shape, opt, arena.data_ptr(), arena_bytes,
-                     (None, None, None) if args.own_streams else [s.cuda_stream for s in streams])
-    log(f"init (host store + seeded weights) {time.time() - t0:.1f} s")
-    tokens, labels = synth.tokens_labels(synth.SEED_TOKENS, B, S, cfg["vocab"])
     nm = args.micro
-    if nm > 1:
-        tl = [synth.tokens_labels(synth.SEED_TOKENS + j, B, S, cfg["vocab"]) for j in range(nm)]
-        mtok, mlab = np.stack([t for t, _ in tl]), np.stack([lb for _, lb in tl])
-
-    def one_step():
-        return ctx.train_step(tokens, labels) if nm == 1 else ctx.train_step_accum(mtok, mlab)
-
-    for i in range(args.warmup):
-        loss, st = one_step()
-        log(f"warmup {i}: loss {loss:.4f} step {st.step_ms:.0f} ms")
-    ctx.sync()  # queued host updates (cross_step) land before the clock starts
-    torch.cuda.synchronize()
-    stats = []
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        loss, st = one_step()
-        stats.append(mt.stats_dict(st))
-        log(f"step {i}: loss {loss:.4f} step {st.step_ms:.0f} ms (fwd {st.fwd_ms:.0f} head {st.head_ms:.0f} "
-            f"bwd {st.bwd_ms:.0f} adam tail {st.adam_tail_ms:.0f}; adam busy {st.adam_ms:.0f}, "
-            f"pack {st.pack_ms:.0f}; waited for adam {st.adam_wait_ms:.0f}; overlap {st.overlap_ratio:.2f})")
-    ctx.sync()  # every step's host Adam is inside the timed region
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / args.steps
-    value = nm * T * args.steps / elapsed
+    res, ctx, arena = run_workload(torch, mt, cfg, args, opt_kw, args.steps, args.warmup, keep=True)
+    if ctx is None:
+        print(json.dumps({"metric": METRIC, "value": None, "refused": res}), flush=True)
+        sys.exit(3)
+    stats, value, ms_per_step = res["stats"], res["value"], res["ms_per_step"]
+    sat = int(sum(s["fp16_saturated"] for s in stats))
 
     out = {"metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 2), "higher_is_better": True,
-           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "precision": {"storage": "bf16 weights, gradients and activations; fp32 master, m, v; fp32 accumulation",
+                         "attention": "fp16 operands (n1, Wqkv, q, k, v, P, o, Wo) and fp16 MFMA in the forward, "
+                                      "range-guarded", "fp16_saturated_in_timed_steps": sat},
+           "data": "synthetic: seeded uniform token ids, a fresh batch every step",
            "config": {"workload": cfg["workload"], "global_batch": nm * B, "micro_batches": nm, "seq_len": S,
                       "layers": cfg["n_layers"],
                       "parallelism": "single GPU, layer-streamed", "weight_slots": args.slots,
@@ -422,6 +576,7 @@ def main():
                       "head_vocab_chunk": args.head_vocab_chunk}}
     mf = nm * model_flops_per_step(cfg, T, S)
     out["model_tflops_per_s"] = round(mf / (ms_per_step / 1e3) / 1e12, 2)
+    out["pages_convention_tflops_per_s"] = round(nm * pages_flops_per_step(cfg, T, S) / (ms_per_step / 1e3) / 1e12, 2)
     # hardware FLOPs add the recomputed forward of every layer (the down GEMM
     # is not recomputed: backward needs its input, not its output)
     fl0 = gemm_flops(cfg, T)
@@ -435,28 +590,12 @@ def main():
     hb_step = host_bytes_per_step(cfg, T, nm, pinned=bool(args.pin_weights))
     out["host_memory"] = {"bytes_per_step": int(hb_step), "achieved_GBps": round(hb_step / (ms_per_step / 1e3) / 1e9, 1),
                           "adam_alone_GBps": host_adam_probe(mt)}
-
-    # Transfer and overlap figures (device clock, averaged over timed steps).
-    h2d_b = np.mean([s["h2d_bytes"] for s in stats])
-    h2d_ms = np.mean([s["h2d_busy_ms"] for s in stats])
-    d2h_b = np.mean([s["d2h_bytes"] for s in stats])
-    d2h_ms = np.mean([s["d2h_busy_ms"] for s in stats])
-    out["pcie"] = {"h2d_GBps": round(h2d_b / (h2d_ms / 1e3) / 1e9, 2) if h2d_ms else None,
-                   "d2h_GBps": round(d2h_b / (d2h_ms / 1e3) / 1e9, 2) if d2h_ms else None,
-                   "h2d_GB_per_step": round(h2d_b / 1e9, 3), "d2h_GB_per_step": round(d2h_b / 1e9, 3),
-                   "peak_GBps": PCIE_GEN5_X16_GBS,
-                   "h2d_busy_frac_of_step": round(float(np.mean([s["pcie_busy_frac"] for s in stats])), 3),
-                   "overlap_ratio": round(float(np.mean([s["overlap_ratio"] for s in stats])), 3),
-                   "overlap_by_phase": {ph: round(float(np.mean([s["overlap_phase"][i] for s in stats])), 3)
-                                        for i, ph in enumerate(("fwd", "head", "bwd"))},
-                   "exposed_transfer_ms_by_phase": {ph: round(float(np.mean([s["exposed_transfer_ms"][i]
-                                                                             for s in stats])), 1)
-                                                    for i, ph in enumerate(("fwd", "head", "bwd"))}}
+    out["pcie"] = pcie_block(stats)
     out["phases_ms"] = {k: round(float(np.mean([s[k] for s in stats])), 1)
                         for k in ("fwd_ms", "head_ms", "bwd_ms", "adam_tail_ms", "compute_busy_ms",
                                   "adam_ms", "adam_wait_ms", "pack_ms")}
     out["memory"] = {"gpu_arena_bytes": int(stats[0]["gpu_arena_bytes"]),
-                     "gpu_mem_used_delta_bytes": int(free0 - torch.cuda.mem_get_info()[0]),
+                     "gpu_mem_used_delta_bytes": res["mem_delta"],
                      "pinned_bytes": int(stats[0]["pinned_bytes"]),
                      "host_store_bytes": int(stats[0]["host_store_bytes"])}
     if not args.no_profile:
@@ -494,9 +633,63 @@ def main():
         out["cpu_baseline"] = cpu_baseline(ctx, cfg, mt)
     ctx.close()
     del arena
+    torch.cuda.empty_cache()
+    if not args.no_pages_config and args.pin_weights and nm == 1:
+        # The pages' pinned footprint: pageable W packed into two pinned
+        # staging buffers sized to the largest streamed block, 12 slabs.
+        pk = dict(opt_kw, pin_weights=0, n_grad_slabs=12)
+        ps = max(2, min(args.steps, 5))
+        log(f"pages configuration: pin_weights=0, 12 slabs, {ps} timed steps")
+        pres, _, _ = run_workload(torch, mt, cfg, args, pk, ps, 1)
+        if "refused" in pres:
+            out["pages_config"] = pres
+        else:
+            pst = pres["stats"]
+            out["pages_config"] = {
+                "value": round(pres["value"], 2), "unit": "tokens/s", "steps": ps,
+                "ms_per_step": round(pres["ms_per_step"], 2), "pin_weights": 0, "grad_slabs": 12,
+                "pinned_bytes": int(pst[0]["pinned_bytes"]), "gpu_arena_bytes": int(pst[0]["gpu_arena_bytes"]),
+                "phases_ms": {k: round(float(np.mean([s[k] for s in pst])), 1)
+                              for k in ("fwd_ms", "head_ms", "bwd_ms", "adam_ms", "adam_wait_ms", "pack_ms")},
+                "pcie": pcie_block(pst)}
     if args.ablations:
-        out["ablations"] = ablations(torch, mt, shape, cfg, args, tokens, labels, T / (ms_per_step / 1e3))
+        out["ablations"] = ablations(torch, mt, mt.make_shape(
+            cfg["n_layers"], cfg["d_model"], cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["ffn_dim"],
+            cfg["vocab"]), cfg, args, *step_batches(cfg, 1, 0), T / (ms_per_step / 1e3))
     print(json.dumps(out), flush=True)
+
+
+def depth_sweep(torch, mt, cfg, args, opt_kw):
+    """The workload at several depths, each in a fresh context one after the
+    other: tokens/s, layer-tokens/s (tokens/s times depth: constant when the
+    step time grows linearly with depth), and the device memory each context
+    took (the arena does not depend on the depth)."""
+    depths = [int(x) for x in args.depths.split(",") if x]
+    # One untimed step of a one-layer context first: the runtime's one-time
+    # device allocations (code objects, the library's static buffers) then
+    # fall outside every measured context.
+    run_workload(torch, mt, dict(cfg, n_layers=1), args, dict(opt_kw, profile_kernels=0), 1, 0)
+    rows = []
+    for L in depths:
+        c = dict(cfg, n_layers=L)
+        res, _, _ = run_workload(torch, mt, c, args, opt_kw, args.steps, args.warmup)
+        if "refused" in res:
+            rows.append({"layers": L, **res})
+            continue
+        st = res["stats"]
+        rows.append({"layers": L, "tokens_per_s": round(res["value"], 1),
+                     "layer_tokens_per_s": round(res["value"] * L, 1), "ms_per_step": round(res["ms_per_step"], 1),
+                     "gpu_arena_bytes": int(st[0]["gpu_arena_bytes"]), "gpu_mem_used_delta_bytes": res["mem_delta"],
+                     "pinned_bytes": int(st[0]["pinned_bytes"]), "host_store_bytes": int(st[0]["host_store_bytes"]),
+                     "pcie": pcie_block(st)})
+        log(f"depth {L}: {res['value']:.0f} tokens/s, device memory taken {res['mem_delta'] / 1e9:.3f} GB")
+    ok = [r for r in rows if "refused" not in r]
+    print(json.dumps({"metric": METRIC, "depth_sweep": rows, "workload": cfg["workload"].replace(
+        f"{cfg['n_layers']} layers", "L layers"), "steps": args.steps, "warmup": args.warmup,
+        "gpu_arena_constant_across_depths": len({r["gpu_arena_bytes"] for r in ok}) == 1 if ok else None,
+        "gpu_mem_used_delta_spread_bytes": (max(r["gpu_mem_used_delta_bytes"] for r in ok) -
+                                            min(r["gpu_mem_used_delta_bytes"] for r in ok)) if ok else None}),
+        flush=True)
 
 
 if __name__ == "__main__":

@@ -145,6 +145,17 @@ typedef struct mt_stats {
     int32_t n_sites;                       /* kernel sites timed (profile_kernels) */
     double site_ms[MT_MAX_SITES];          /* summed device time per site */
     uint64_t site_launches[MT_MAX_SITES];  /* launches per site */
+    uint64_t fp16_saturated;  /* fp16 range guard: values of the attention operands (n1, Wqkv, Wo, q, k,
+                                 v, o) whose magnitude exceeded the fp16 range in this step and were
+                                 saturated to +-65504 (0 in a healthy run) */
+    double compute_union_ms;  /* |C|: union of compute-stream visit spans (device clock) */
+    double copy_union_ms;     /* |X|: union of H2D and D2H copy spans */
+    double overlap_ms;        /* |C ∩ X|; |C ∩ X| / |X| is the share of transfer time hidden under compute */
+    double switch_gap_ms[3];  /* median gap between the end of one compute visit and the start of the
+                                 next, per phase (forward, head, backward): the double-buffer switch
+                                 latency, including any wait for the next unit's weights ([Hotdry]
+                                 monitoring section: switch latency) */
+    double device_idle_ms[3]; /* per phase: time with neither a compute visit nor a copy running */
 } mt_stats;
 
 typedef struct mt_tensor_info {
@@ -224,7 +235,10 @@ int mt_sync(mt_ctx* ctx);
  * buffers x_dev, y_dev (BF16 [batch*seq x d_model] row-major).  Streams the
  * layer's current weights in through the same pack, copy, weights-ready and
  * bind path as a step, runs the forward kernels and synchronises the compute
- * stream. */
+ * stream.  This is one visit of the stateless block template: the layer's
+ * streamed weights bound to a template that holds no parameters of its own
+ * ([Lilting] "Stateless Layer Templates"; [Peter] stateless template
+ * section; [Review] 3-2 item 5). */
 int mt_layer_fwd(mt_ctx* ctx, int32_t layer, const void* x_dev, void* y_dev, int32_t batch,
                  int32_t seq);
 
@@ -232,12 +246,19 @@ int mt_layer_fwd(mt_ctx* ctx, int32_t layer, const void* x_dev, void* y_dev, int
  * layer input, dy_dev the gradient of its output; writes dx_dev (BF16
  * [batch*seq x d_model]) and grad_tile_dev (BF16, the unit's W-region
  * layout of mt_tensor_desc, caller-owned device memory).  No Adam runs and
- * the store is not touched. */
+ * the store is not touched.  The backward visit of one layer: its forward
+ * recomputed from the stored input, then differentiated ([Review] 3-2 item 2
+ * "Streaming forward and block-wise backward"; [Argon] "Block-Wise
+ * Recomputation"), with the gradients in the tile layout they are streamed
+ * out in ([Hotdry] pinned gradient slabs). */
 int mt_layer_bwd(mt_ctx* ctx, int32_t layer, const void* x_dev, const void* dy_dev, void* dx_dev,
                  void* grad_tile_dev, int32_t batch, int32_t seq);
 
 /* Describe tensor idx of unit (offsets in elements inside the unit's W
- * region).  Pure host function.  Errors: MT_E_INVAL. */
+ * region).  Pure host function.  Errors: MT_E_INVAL.  The layout is the
+ * layer-contiguous tile: one unit's tensors back to back in one flat region,
+ * so a unit streams as a single copy ([Review] 3-2 item 4 "Layer-contiguous
+ * tiling and pinned slabs"; [Hotdry] host memory layout section). */
 int mt_tensor_desc(const mt_shape* shape, int32_t unit, int32_t idx, mt_tensor_info* out);
 
 /* Number of tensors in a unit (9, 2 or 1), or a negative error. */
@@ -250,7 +271,12 @@ uint64_t mt_unit_elems(const mt_shape* shape, int32_t unit);
 /* Copy one tensor between the host store and caller host memory.  `which`
  * is MT_W/MT_G (BF16, 2 bytes per element) or MT_MASTER/MT_M/MT_V (FP32);
  * bytes must equal rows*cols*element size.  mt_set_tensor(MT_W) also
- * refreshes nothing else: set MT_MASTER too to keep them consistent. */
+ * refreshes nothing else: set MT_MASTER too to keep them consistent.  The
+ * store is the host master copy of all persistent state, BF16 W and G with
+ * the FP32 master, m and v ([Review] 3-2 item 1; [Lilting] 16-byte per
+ * parameter table).  Both wait for queued host updates first.  Errors:
+ * MT_E_INVAL (unit, tensor, which or bytes out of range, NULL pointers), or
+ * a host worker's or a lazy restore's error. */
 int mt_get_tensor(mt_ctx* ctx, int32_t unit, int32_t idx, int32_t which, void* host_dst,
                   uint64_t bytes);
 int mt_set_tensor(mt_ctx* ctx, int32_t unit, int32_t idx, int32_t which, const void* host_src,

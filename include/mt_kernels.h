@@ -29,19 +29,26 @@ extern "C" {
  * epi 0: C bf16 = acc; 1: C bf16 = acc + R (bf16, ldr); 2: C f32 = acc;
  * 3: C f32 += acc; 4: C bf16 = acc + Cacc (f32, ldacc); 5: C f32 = acc + R
  * (bf16); 6: C bf16 = acc + R (f32); 7: A and B are fp16 (not bf16), C f32 =
- * acc, layout 0 only. */
+ * acc, layout 0 only; 8: A and B fp16, C f32 = acc + R (bf16), layout 0 only. */
 int mt_k_gemm(int32_t layout, int32_t epi, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
               int64_t ldc, const void* R, int64_t ldr, const void* Cacc, int64_t ldacc, int32_t M, int32_t N,
               int32_t K, void* stream);
+
+/* fp16 range guard.  Every entry that writes fp16 values (the attention
+ * operands) saturates a value whose magnitude rounds beyond the fp16 range
+ * (|x| >= 65520, or not finite) to +-65504 (a NaN stays a NaN) and, when
+ * fp16_ovf is not NULL, adds the number of such values to the uint32 device
+ * counter fp16_ovf points at (the caller zeroes it). */
 
 /* RMSNorm: n = gamma * x / sqrt(mean(x^2) + eps) per row of x [T x d]
  * (x bf16, or f32 when x_f32 != 0); rstd [T] f32 = 1/sqrt(mean(x^2) + eps).
  * n_f16 (may be NULL) receives n rounded to fp16 instead of bf16. */
 int mt_k_rmsnorm_fwd(const void* x, int32_t x_f32, const void* gamma, void* n, void* n_f16, void* rstd, int32_t T,
-                     int32_t d, float eps, void* stream);
+                     int32_t d, float eps, void* fp16_ovf, void* stream);
 /* dx = resid + rstd * (g - nh * mean(g * nh)), g = dn*gamma, nh = x*rstd
  * (resid may be NULL); dgamma [d] bf16 = sum_t dn * nh, summed in a fixed
- * order through `scratch` (f32, mt_k_rmsnorm_bwd_scratch_elems). */
+ * order through `scratch` (f32, mt_k_rmsnorm_bwd_scratch_elems(T, d) =
+ * min(ceil(T / 4), 512) * d floats).  d <= 8192. */
 int64_t mt_k_rmsnorm_bwd_scratch_elems(int32_t T, int32_t d);
 int mt_k_rmsnorm_bwd(const void* dn, const void* x, int32_t x_f32, const void* gamma, const void* rstd,
                      const void* resid, void* dx, void* dgamma, void* scratch, int32_t T, int32_t d, void* stream);
@@ -53,16 +60,16 @@ int mt_k_rmsnorm_bwd(const void* dn, const void* x, int32_t x_f32, const void* g
 int mt_k_rope(void* qkv, int64_t ld, void* table, int32_t T, int32_t S, int32_t n_rot_heads, int32_t hd,
               float base, int32_t dir, void* stream);
 /* Forward rotary embedding on the f32 QKV projection in [T x ldin] (n_heads
- * heads of hd): the first n_rot_heads heads (q and k) are rotated in f32 and
- * written as fp16, the others (v) as bf16, to out [T x ldout]; out_bf16 (may
- * be NULL) [T x ld_bf16] also gets the rotated heads in bf16 (the attention
+ * heads of hd): the first n_rot_heads heads (q and k) are rotated in f32, and
+ * every head is written as fp16 to out [T x ldout]; out_bf16 (may be NULL)
+ * [T x ld_bf16, ld_bf16 >= n_heads*hd] also gets them in bf16 (the attention
  * backward's gradient products take them in that form).  Same angles and
  * table as mt_k_rope. */
 int mt_k_qkv_rope_cvt(const void* in, int64_t ldin, void* out, int64_t ldout, void* out_bf16, int64_t ld_bf16,
                       void* table, int32_t T, int32_t S, int32_t n_rot_heads, int32_t n_heads, int32_t hd, float base,
-                      void* stream);
+                      void* fp16_ovf, void* stream);
 /* y[i] = fp16(x[i]) for bf16 x, n a multiple of 8. */
-int mt_k_bf16_to_f16(const void* x, void* y, int64_t n, void* stream);
+int mt_k_bf16_to_f16(const void* x, void* y, int64_t n, void* fp16_ovf, void* stream);
 
 /* SwiGLU on gu [T x 2F] = [gate | up]: m [T x F] = silu(gate) * up;
  * backward dgu = [dm * up * silu'(gate) | dm * silu(gate)]. */
@@ -72,19 +79,28 @@ int mt_k_swiglu_bwd(const void* dm, const void* gu, void* dgu, int32_t T, int32_
 /* Causal GQA attention on qkv [B*S x ld] (q heads at column 0, k heads at
  * Hq*hd, v heads at (Hq+Hkv)*hd; query head h reads KV head h/(Hq/Hkv)),
  * scale 1/sqrt(hd): o [B*S x ldo], lse [B x Hq x S] f32 (natural log).
- * q and k are fp16, v, o, dout and dqkv bf16.
+ * q, k, v and o are fp16 (o range-guarded); dout and dqkv bf16.
  * hd in {64, 128}. */
 int mt_k_attn_fwd(const void* qkv, int64_t ld, void* o, int64_t ldo, void* lse, int32_t B, int32_t S, int32_t Hq,
-                  int32_t Hkv, int32_t hd, void* stream);
-/* Backward: dqkv [B*S x ldd] gets dQ, dK, dV in the qkv column layout (the
- * K and V gradients summed over each KV group, in a fixed order); dsum is
- * f32 scratch [B x Hq x S].  qk_bf16 (may be NULL): bf16 copy of the rotated
- * q and k heads [B*S x ld_bf16] (k after the Hq query heads), which lets the
- * kernels load every tile straight into LDS; NULL: they round the fp16 q and
- * k to bf16 themselves. */
+                  int32_t Hkv, int32_t hd, void* fp16_ovf, void* stream);
+/* Backward: dqkv [B*S x ldd] gets dV, and dQ and dK too unless dqk32 is
+ * given, in the qkv column layout (the K and V gradients summed over each KV
+ * group, in a fixed order), bf16.  dqk32 (may be NULL): dQ and dK in fp32
+ * [B*S x ld32, ld32 >= (Hq+Hkv)*hd] instead (query heads, then key heads).
+ * The products run on fp16: dO (bf16) is multiplied by the power of two 2^k
+ * that keeps every |dP|, |D| and |dS| below 2^15 given max|dO| and max|v|
+ * (range-guarded into fp16_ovf, may be NULL), the results are scaled back by
+ * 2^-k.  work: device scratch of mt_k_attn_bwd_work_bytes(B, S, Hq, hd)
+ * bytes, 256-byte aligned (D, the scaled dO, the two maxima). */
+int64_t mt_k_attn_bwd_work_bytes(int32_t B, int32_t S, int32_t Hq, int32_t hd);
 int mt_k_attn_bwd(const void* qkv, int64_t ld, const void* o, const void* dout, int64_t ldo, const void* lse,
-                  void* dsum, void* dqkv, int64_t ldd, int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t hd,
-                  const void* qk_bf16, int64_t ld_bf16, void* stream);
+                  void* work, void* dqkv, int64_t ldd, int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t hd,
+                  void* dqk32, int64_t ld32, void* fp16_ovf, void* stream);
+/* Rotary embedding of the first n_rot_heads heads of fp32 in [T x ldin]
+ * (same angles and table as mt_k_rope; dir -1 rotates by -theta, the
+ * backward), written as bf16 to out [T x ldout] with one rounding. */
+int mt_k_rope_f32_bf16(const void* in, int64_t ldin, void* out, int64_t ldout, void* table, int32_t T, int32_t S,
+                       int32_t n_rot_heads, int32_t hd, float base, int32_t dir, void* stream);
 
 /* Cross-entropy of logits [Tc x V] f32 against int32 labels [Tc]:
  * loss_rows [Tc] = logsumexp - logit[label]; dlogits [Tc x V] bf16 =
@@ -94,9 +110,11 @@ int mt_k_ce(const void* logits, const void* labels, void* loss_rows, void* dlogi
 int mt_k_mean(const void* x, void* out, int32_t n, void* stream);
 int mt_k_f32_to_bf16(const void* x, void* y, int64_t n, void* stream);
 /* Transpose of an R x C matrix of 16-bit elements: dst[c*ldd + r] = src[r*lds + c]
- * (the backward products take both operands reduction-contiguous).  Errors:
- * MT_E_INVAL for negative sizes, lds < C or ldd < R. */
-int mt_k_transpose16(const void* src, int64_t lds, void* dst, int64_t ldd, int32_t R, int32_t C, void* stream);
+ * (the backward products take both operands reduction-contiguous); with
+ * f16_to_bf16 != 0 src holds fp16 and dst gets each value rounded to bf16.
+ * Errors: MT_E_INVAL for negative sizes, lds < C or ldd < R. */
+int mt_k_transpose16(const void* src, int64_t lds, void* dst, int64_t ldd, int32_t R, int32_t C, int32_t f16_to_bf16,
+                     void* stream);
 
 /* Host (CPU) entries, no GPU needed. */
 /* The production host Adam over n elements of caller arrays: G <- gsrc,

@@ -71,15 +71,15 @@ static int kst(hipError_t e, const char* what) {
 int mt_k_gemm(int32_t layout, int32_t epi, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
               int64_t ldc, const void* R, int64_t ldr, const void* Cacc, int64_t ldacc, int32_t M, int32_t N,
               int32_t K, void* stream) {
-    if (layout < 0 || layout > 2 || epi < 0 || epi > 7) MT_FAIL(MT_E_INVAL, "bad layout or epilogue");
+    if (layout < 0 || layout > 2 || epi < 0 || epi > 8) MT_FAIL(MT_E_INVAL, "bad layout or epilogue");
     mt::GemmArgs a{A, lda, B, ldb, C, ldc, R, ldr, static_cast<const float*>(Cacc), ldacc, M, N, K};
     return kst(mt::gemm(mt::GemmLayout(layout), mt::GemmEpi(epi), a, S_(stream)), "gemm");
 }
 
 int mt_k_rmsnorm_fwd(const void* x, int32_t x_f32, const void* gamma, void* n, void* n_f16, void* rstd, int32_t T,
-                     int32_t d, float eps, void* stream) {
+                     int32_t d, float eps, void* fp16_ovf, void* stream) {
     return kst(mt::rmsnorm_fwd(x, x_f32 != 0, U16(gamma), U16(n), n_f16 ? U16(n_f16) : nullptr, F32(rstd), T, d, eps,
-                               S_(stream)),
+                               S_(stream), static_cast<uint32_t*>(fp16_ovf)),
                "rmsnorm_fwd");
 }
 
@@ -102,16 +102,17 @@ int mt_k_rope(void* qkv, int64_t ld, void* table, int32_t T, int32_t S, int32_t 
 
 int mt_k_qkv_rope_cvt(const void* in, int64_t ldin, void* out, int64_t ldout, void* out_bf16, int64_t ld_bf16,
                       void* table, int32_t T, int32_t S, int32_t n_rot_heads, int32_t n_heads, int32_t hd, float base,
-                      void* stream) {
+                      void* fp16_ovf, void* stream) {
     hipError_t e = mt::rope_table(static_cast<float2*>(table), S, hd, base, S_(stream));
     if (e != hipSuccess) return kst(e, "rope_table");
     return kst(mt::qkv_rope_cvt(F32(in), ldin, U16(out), ldout, static_cast<uint16_t*>(out_bf16), ld_bf16,
-                                static_cast<float2*>(table), T, S, n_rot_heads, n_heads, hd, S_(stream)),
+                                static_cast<float2*>(table), T, S, n_rot_heads, n_heads, hd, S_(stream),
+                                static_cast<uint32_t*>(fp16_ovf)),
                "qkv_rope_cvt");
 }
 
-int mt_k_bf16_to_f16(const void* x, void* y, int64_t n, void* stream) {
-    return kst(mt::bf16_to_f16(U16(x), U16(y), n, S_(stream)), "bf16_to_f16");
+int mt_k_bf16_to_f16(const void* x, void* y, int64_t n, void* fp16_ovf, void* stream) {
+    return kst(mt::bf16_to_f16(U16(x), U16(y), n, S_(stream), static_cast<uint32_t*>(fp16_ovf)), "bf16_to_f16");
 }
 
 int mt_k_swiglu_fwd(const void* gu, void* m, int32_t T, int32_t F, void* stream) {
@@ -123,17 +124,33 @@ int mt_k_swiglu_bwd(const void* dm, const void* gu, void* dgu, int32_t T, int32_
 }
 
 int mt_k_attn_fwd(const void* qkv, int64_t ld, void* o, int64_t ldo, void* lse, int32_t B, int32_t S, int32_t Hq,
-                  int32_t Hkv, int32_t hd, void* stream) {
-    mt::AttnArgs a{U16(qkv), ld, U16(o), ldo, F32(lse), B, S, Hq, Hkv, hd};
+                  int32_t Hkv, int32_t hd, void* fp16_ovf, void* stream) {
+    mt::AttnArgs a{U16(qkv), ld, U16(o), ldo, F32(lse), B, S, Hq, Hkv, hd, static_cast<uint32_t*>(fp16_ovf)};
     return kst(mt::attn_fwd(a, S_(stream)), "attn_fwd");
 }
 
+int64_t mt_k_attn_bwd_work_bytes(int32_t B, int32_t S, int32_t Hq, int32_t hd) {
+    if (B <= 0 || S <= 0 || Hq <= 0 || hd <= 0) return 0;
+    return mt::attn_bwd_work_bytes(B, S, Hq, hd);
+}
+
 int mt_k_attn_bwd(const void* qkv, int64_t ld, const void* o, const void* dout, int64_t ldo, const void* lse,
-                  void* dsum, void* dqkv, int64_t ldd, int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t hd,
-                  const void* qk_bf16, int64_t ld_bf16, void* stream) {
-    mt::AttnBwdArgs a{U16(qkv), ld, U16(o), U16(dout), ldo, F32(lse), F32(dsum), U16(dqkv), ldd, B, S, Hq, Hkv, hd,
-                      static_cast<const uint16_t*>(qk_bf16), ld_bf16};
+                  void* work, void* dqkv, int64_t ldd, int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t hd,
+                  void* dqk32, int64_t ld32, void* fp16_ovf, void* stream) {
+    if (!work || (reinterpret_cast<uintptr_t>(work) & 255)) MT_FAIL(MT_E_INVAL, "attn_bwd: work must be 256-byte aligned");
+    mt::AttnBwdArgs a{U16(qkv), ld, U16(o), U16(dout), ldo, F32(lse), nullptr, nullptr, nullptr, U16(dqkv), ldd,
+                      B, S, Hq, Hkv, hd, F32(dqk32), ld32, static_cast<uint32_t*>(fp16_ovf)};
+    if (B > 0 && S > 0 && Hq > 0 && (hd == 64 || hd == 128)) mt::attn_bwd_carve(work, B, S, Hq, hd, a);
     return kst(mt::attn_bwd(a, S_(stream)), "attn_bwd");
+}
+
+int mt_k_rope_f32_bf16(const void* in, int64_t ldin, void* out, int64_t ldout, void* table, int32_t T, int32_t S,
+                       int32_t n_rot_heads, int32_t hd, float base, int32_t dir, void* stream) {
+    hipError_t e = mt::rope_table(static_cast<float2*>(table), S, hd, base, S_(stream));
+    if (e != hipSuccess) return kst(e, "rope_table");
+    return kst(mt::rope_f32_to_bf16(F32(in), ldin, U16(out), ldout, static_cast<float2*>(table), T, S, n_rot_heads,
+                                    hd, dir, S_(stream)),
+               "rope_f32_to_bf16");
 }
 
 int mt_k_ce(const void* logits, const void* labels, void* loss_rows, void* dlogits, int32_t Tc, int32_t V,
@@ -147,8 +164,9 @@ int mt_k_mean(const void* x, void* out, int32_t n, void* stream) {
     return kst(mt::mean_reduce(F32(x), F32(out), n, S_(stream)), "mean_reduce");
 }
 
-int mt_k_transpose16(const void* src, int64_t lds, void* dst, int64_t ldd, int32_t R, int32_t C, void* stream) {
-    return kst(mt::transpose16(U16(src), lds, U16(dst), ldd, R, C, S_(stream)), "transpose16");
+int mt_k_transpose16(const void* src, int64_t lds, void* dst, int64_t ldd, int32_t R, int32_t C, int32_t f16_to_bf16,
+                     void* stream) {
+    return kst(mt::transpose16(U16(src), lds, U16(dst), ldd, R, C, S_(stream), f16_to_bf16 != 0), "transpose16");
 }
 
 int mt_k_f32_to_bf16(const void* x, void* y, int64_t n, void* stream) {

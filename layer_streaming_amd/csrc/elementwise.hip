@@ -30,7 +30,8 @@ template <class TX, int CPL>
 __global__ __launch_bounds__(256) void rmsnorm_fwd_k(const TX* __restrict__ x,
                                                      const uint4* __restrict__ gamma,
                                                      uint4* __restrict__ n, uint4* __restrict__ n16,
-                                                     float* __restrict__ rstd, int T, int d, float eps) {
+                                                     float* __restrict__ rstd, int T, int d, float eps,
+                                                     uint32_t* __restrict__ ovf) {
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= T) return;
@@ -53,6 +54,7 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_k(const TX* __restrict__ x,
     const float r = 1.0f / sqrtf(ss / float(d) + eps);
     uint4* nr = n + int64_t(row) * nv;
     uint4* nh = n16 ? n16 + int64_t(row) * nv : nullptr;
+    uint32_t nov = 0;
 #pragma unroll
     for (int k = 0; k < CPL; ++k) {
         const int c = lane + 64 * k;
@@ -62,16 +64,39 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_k(const TX* __restrict__ x,
 #pragma unroll
             for (int e = 0; e < 8; ++e) f[k][e] = (f[k][e] * r) * g[e];
             nr[c] = pack8(f[k]);
-            if (nh) nh[c] = pack8h(f[k]);
+            if (nh) nh[c] = pack8h_sat(f[k], nov);
         }
     }
+    count_ovf(ovf, nov);
     if (lane == 0) rstd[row] = r;
 }
 
-// Backward: each wave takes RPW consecutive rows; each lane accumulates the
-// gamma gradient of its columns in registers and writes one partial row per
-// wave; dgamma_reduce sums the partial rows in order.
-constexpr int RPW = 8;
+// Backward.  Block b (four waves) takes the rows [T b / nb, T (b+1) / nb),
+// its waves interleaved (wave w: rows r0 + w, r0 + w + 4, ...).  A wave keeps
+// one row's dn, x and residual chunks in registers (every load issued before
+// the first use), forms the row's dot product with a wave reduction, writes
+// dx and accumulates the gain gradient of its lane's columns in fp32
+// registers; gamma sits in LDS.  The block's four waves then add their sums
+// in LDS in wave order into one partial row per block, and dgamma_reduce sums
+// the blocks' rows in block order: the order is fixed, so results are
+// bit-reproducible.  At most RMS_BWD_MAX_BLOCKS blocks (several per CU, so
+// that the loads of one wave overlap the arithmetic of others), and at most
+// 4M partial floats.
+constexpr int RMS_BWD_MAX_BLOCKS = 512;
+
+__device__ __forceinline__ void load_raw(const uint16_t* __restrict__ row, int c, uint4 (&v)[2]) {
+    v[0] = reinterpret_cast<const uint4*>(row)[c];
+}
+__device__ __forceinline__ void load_raw(const float* __restrict__ row, int c, uint4 (&v)[2]) {
+    v[0] = reinterpret_cast<const uint4*>(row)[2 * c];
+    v[1] = reinterpret_cast<const uint4*>(row)[2 * c + 1];
+}
+__device__ __forceinline__ void unpack_raw(const uint4 (&v)[2], float* f, uint16_t) { unpack8(v[0], f); }
+__device__ __forceinline__ void unpack_raw(const uint4 (&v)[2], float* f, float) {
+    const float4 a = __builtin_bit_cast(float4, v[0]), b = __builtin_bit_cast(float4, v[1]);
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
 
 template <int NCL, class TX>
 __global__ __launch_bounds__(256) void rmsnorm_bwd_k(const uint4* __restrict__ dn,
@@ -81,72 +106,108 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_k(const uint4* __restrict__ d
                                                      const uint4* __restrict__ resid,
                                                      uint4* __restrict__ dx,
                                                      float* __restrict__ partial, int T, int d) {
-    const int wave_id = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
+    __shared__ uint4 gs[64 * NCL];     // gamma
+    __shared__ float red[512 * NCL];   // the block's gain-gradient row
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nv = d >> 3;
+    for (int c = threadIdx.x; c < nv; c += 256) gs[c] = gamma[c];
+    __syncthreads();
+    const int nb = gridDim.x;
+    const int r0 = int(int64_t(T) * blockIdx.x / nb), r1 = int(int64_t(T) * (blockIdx.x + 1) / nb);
     float dg[NCL][8];
 #pragma unroll
     for (int j = 0; j < NCL; ++j)
 #pragma unroll
         for (int k = 0; k < 8; ++k) dg[j][k] = 0.f;
-    float gm[NCL][8];
-#pragma unroll
-    for (int j = 0; j < NCL; ++j) {
-        int c = lane + 64 * j;
-        if (c < nv) unpack8(gamma[c], gm[j]);
-    }
-    const int row0 = wave_id * RPW;
-    for (int rr = 0; rr < RPW; ++rr) {
-        const int row = row0 + rr;
-        if (row >= T) break;
+    for (int row = r0 + wave; row < r1; row += 4) {
         const float r = rstd[row];
         const uint4* dnr = dn + int64_t(row) * nv;
         const TX* xr = x + int64_t(row) * d;
-        float g[NCL][8], nh[NCL][8];
+        const uint4* rr_ = resid ? resid + int64_t(row) * nv : nullptr;
+        // the residual's loads go out with the others unless the row is wide
+        constexpr bool EARLY_Q = NCL <= 4;
+        uint4 a[NCL], q[NCL], xv[NCL][2];
+#pragma unroll
+        for (int j = 0; j < NCL; ++j) {
+            const int c = lane + 64 * j;
+            if (c < nv) {
+                a[j] = dnr[c];
+                load_raw(xr, c, xv[j]);
+                if (EARLY_Q && rr_) q[j] = rr_[c];
+            }
+        }
         float dot = 0.f;
 #pragma unroll
         for (int j = 0; j < NCL; ++j) {
-            int c = lane + 64 * j;
+            const int c = lane + 64 * j;
             if (c < nv) {
-                float a[8], b[8];
-                unpack8(dnr[c], a);
-                load8(xr, c, b);
+                float av[8], xf[8], g8[8];
+                unpack8(a[j], av);
+                unpack_raw(xv[j], xf, TX());
+                unpack8(gs[c], g8);
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
-                    nh[j][k] = b[k] * r;
-                    g[j][k] = a[k] * gm[j][k];
-                    dg[j][k] += a[k] * nh[j][k];
-                    dot += g[j][k] * nh[j][k];
+                    const float nh = xf[k] * r;
+                    dot += (av[k] * g8[k]) * nh;
+                    dg[j][k] += av[k] * nh;
                 }
             }
         }
         dot = wave_sum(dot) / float(d);
-        uint4* dxr = dx + int64_t(row) * nv;
-        const uint4* rr_ = resid ? resid + int64_t(row) * nv : nullptr;
+        // Keep only the packed row in registers across the reduction: the
+        // unpacked values are formed again below (a few bit operations)
+        // instead of being held, which would double the registers per row.
+        auto opaque = [](uint4& v) { asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w)); };
 #pragma unroll
         for (int j = 0; j < NCL; ++j) {
-            int c = lane + 64 * j;
+            opaque(a[j]);
+            opaque(xv[j][0]);
+            if constexpr (sizeof(TX) == 4) opaque(xv[j][1]);
+        }
+        if (!EARLY_Q && rr_) {
+#pragma unroll
+            for (int j = 0; j < NCL; ++j) {
+                const int c = lane + 64 * j;
+                if (c < nv) q[j] = rr_[c];
+            }
+        }
+        uint4* dxr = dx + int64_t(row) * nv;
+#pragma unroll
+        for (int j = 0; j < NCL; ++j) {
+            const int c = lane + 64 * j;
             if (c < nv) {
-                float o[8], q[8];
-                if (rr_) unpack8(rr_[c], q);
+                float av[8], xf[8], g8[8], o[8], qv[8];
+                unpack8(a[j], av);
+                unpack_raw(xv[j], xf, TX());
+                unpack8(gs[c], g8);
+                if (rr_) unpack8(q[j], qv);
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
-                    o[k] = r * (g[j][k] - nh[j][k] * dot);
-                    if (rr_) o[k] += q[k];
+                    const float nh = xf[k] * r;
+                    o[k] = r * ((av[k] * g8[k]) - nh * dot);
+                    if (rr_) o[k] += qv[k];
                 }
                 dxr[c] = pack8(o);
             }
         }
     }
-    float* pr = partial + int64_t(wave_id) * d;
+    // the waves' gain gradients, added in wave order
+#pragma unroll 1
+    for (int w = 0; w < 4; ++w) {
+        if (wave == w) {
 #pragma unroll
-    for (int j = 0; j < NCL; ++j) {
-        int c = lane + 64 * j;
-        if (c < nv) {
+            for (int j = 0; j < NCL; ++j) {
+                const int c = lane + 64 * j;
+                if (c < nv) {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) pr[c * 8 + k] = dg[j][k];
+                    for (int k = 0; k < 8; ++k) red[c * 8 + k] = (w == 0 ? 0.f : red[c * 8 + k]) + dg[j][k];
+                }
+            }
         }
+        __syncthreads();
     }
+    float* pr = partial + int64_t(blockIdx.x) * d;
+    for (int i = threadIdx.x; i < d; i += 256) pr[i] = red[i];
 }
 
 // 64 columns per block, 16 waves: wave w sums partial rows w, w+16, ... of
@@ -210,15 +271,61 @@ __global__ void rope_apply_k(uint16_t* __restrict__ qkv, int64_t ld, const float
     *phi = pack8(oh);
 }
 
+// Rotation of the fp32 input's first nrot heads, one thread per 8 pairs
+// (e..e+7, e+half..e+half+7) of one head, written as bf16.
+__global__ void rope_f32_bf16_k(const float* __restrict__ in, int64_t ldin, uint16_t* __restrict__ out,
+                                int64_t ldout, const float2* __restrict__ tab, int T, int S, int nrot, int hd,
+                                int dir) {
+    const int half = hd >> 1, per_head = half >> 3;
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= int64_t(T) * nrot * per_head) return;
+    const int e8 = int(i % per_head);
+    const int64_t th = i / per_head;
+    const int h = int(th % nrot);
+    const int t = int(th / nrot);
+    const int s = t % S;
+    const float* src = in + int64_t(t) * ldin + int64_t(h) * hd + e8 * 8;
+    float lo[8], hi[8], ol[8], oh[8];
+    *reinterpret_cast<float4*>(lo) = reinterpret_cast<const float4*>(src)[0];
+    *reinterpret_cast<float4*>(lo + 4) = reinterpret_cast<const float4*>(src)[1];
+    *reinterpret_cast<float4*>(hi) = reinterpret_cast<const float4*>(src + half)[0];
+    *reinterpret_cast<float4*>(hi + 4) = reinterpret_cast<const float4*>(src + half)[1];
+    const float2* tr = tab + int64_t(s) * half + e8 * 8;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const float2 cs = tr[k];
+        const float sn = dir > 0 ? cs.y : -cs.y;
+        ol[k] = lo[k] * cs.x - hi[k] * sn;
+        oh[k] = hi[k] * cs.x + lo[k] * sn;
+    }
+    uint16_t* dst = out + int64_t(t) * ldout + int64_t(h) * hd + e8 * 8;
+    *reinterpret_cast<uint4*>(dst) = pack8(ol);
+    *reinterpret_cast<uint4*>(dst + half) = pack8(oh);
+}
+
+// Eight fp16 in a uint4 rounded to eight bf16 (RNE).
+__device__ __forceinline__ uint4 h8_to_bf8(const uint4& v) {
+    auto c = [](uint32_t w) {
+        return uint32_t(f2bf(h2f(uint16_t(w & 0xFFFFu)))) | (uint32_t(f2bf(h2f(uint16_t(w >> 16)))) << 16);
+    };
+    return make_uint4(c(v.x), c(v.y), c(v.z), c(v.w));
+}
+
 // Rotary embedding on the fp32 output of the QKV projection, written as the
-// 2-byte operands of attention: rotated q and k heads in fp16, v in bf16.
+// fp16 operands of attention (q and k rotated, v as it is), each value
+// saturated and counted by the fp16 range guard.  outb (optional) receives
+// the same fp16 values rounded to bf16, for the gradient products of the
+// attention backward (bf16 MFMA): the operands the kernels that stage
+// through registers would form themselves.
 __global__ void qkv_rope_cvt_k(const float* __restrict__ in, int64_t ldin, uint16_t* __restrict__ out,
                                int64_t ldout, uint16_t* __restrict__ outb, int64_t ldb,
-                               const float2* __restrict__ tab, int T, int S, int nrot, int nall, int hd) {
+                               const float2* __restrict__ tab, int T, int S, int nrot, int nall, int hd,
+                               uint32_t* __restrict__ ovf) {
     const int half = hd >> 1, per_head = half >> 3;
     const int64_t n_rot_items = int64_t(T) * nrot * per_head;
     const int64_t n_v_items = int64_t(T) * (nall - nrot) * (hd >> 3);
     const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    uint32_t nov = 0;
     if (i < n_rot_items) {
         const int e8 = int(i % per_head);
         const int64_t th = i / per_head;
@@ -241,32 +348,40 @@ __global__ void qkv_rope_cvt_k(const float* __restrict__ in, int64_t ldin, uint1
             oh[k] = hi[k] * cs.x + lo[k] * cs.y;
         }
         uint16_t* dst = out + int64_t(t) * ldout + int64_t(h) * hd + e8 * 8;
-        *reinterpret_cast<uint4*>(dst) = pack8h(ol);
-        *reinterpret_cast<uint4*>(dst + half) = pack8h(oh);
-        if (outb) {  // bf16 copy of the rotated q / k for the gradient products
+        const uint4 hl = pack8h_sat(ol, nov), hh = pack8h_sat(oh, nov);
+        *reinterpret_cast<uint4*>(dst) = hl;
+        *reinterpret_cast<uint4*>(dst + half) = hh;
+        if (outb) {
             uint16_t* db = outb + int64_t(t) * ldb + int64_t(h) * hd + e8 * 8;
-            *reinterpret_cast<uint4*>(db) = pack8(ol);
-            *reinterpret_cast<uint4*>(db + half) = pack8(oh);
+            *reinterpret_cast<uint4*>(db) = h8_to_bf8(hl);
+            *reinterpret_cast<uint4*>(db + half) = h8_to_bf8(hh);
         }
     } else if (i < n_rot_items + n_v_items) {
         const int64_t j = i - n_rot_items;
         const int vw = (nall - nrot) * hd;
         const int c8 = int(j % (vw >> 3));
         const int t = int(j / (vw >> 3));
-        const float* src = in + int64_t(t) * ldin + int64_t(nrot) * hd + c8 * 8;
+        const int64_t col = int64_t(nrot) * hd + c8 * 8;
+        const float* src = in + int64_t(t) * ldin + col;
         float f[8];
         *reinterpret_cast<float4*>(f) = reinterpret_cast<const float4*>(src)[0];
         *reinterpret_cast<float4*>(f + 4) = reinterpret_cast<const float4*>(src)[1];
-        *reinterpret_cast<uint4*>(out + int64_t(t) * ldout + int64_t(nrot) * hd + c8 * 8) = pack8(f);
+        const uint4 h8 = pack8h_sat(f, nov);
+        *reinterpret_cast<uint4*>(out + int64_t(t) * ldout + col) = h8;
+        if (outb) *reinterpret_cast<uint4*>(outb + int64_t(t) * ldb + col) = h8_to_bf8(h8);
     }
+    count_ovf(ovf, nov);
 }
 
-__global__ void bf16_to_f16_k(const uint4* __restrict__ in, uint4* __restrict__ out, int64_t n8) {
+__global__ void bf16_to_f16_k(const uint4* __restrict__ in, uint4* __restrict__ out, int64_t n8,
+                              uint32_t* __restrict__ ovf) {
     const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i >= n8) return;
     float f[8];
     unpack8(in[i], f);
-    out[i] = pack8h(f);
+    uint32_t nov = 0;
+    out[i] = pack8h_sat(f, nov);
+    count_ovf(ovf, nov);
 }
 
 // -------------------------------------------------------------- SwiGLU ----
@@ -464,14 +579,17 @@ __device__ __forceinline__ uint32_t h16of(const uint4& v, int e) {
     return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
 }
 
-// dst[c][r] = src[r][c] for bf16 (any 16-bit) matrices.  One wave per
+// dst[c][r] = src[r][c] for bf16 (any 16-bit) matrices; with F16_TO_BF16 the
+// source holds fp16 and every element is rounded to bf16 on the way (RNE).  One wave per
 // 64 x 64 tile; lane (tx, ty) = (lane % 8, lane / 8) moves the 8 x 8 block at
 // rows 8 ty.., columns 8 tx..: eight 16-byte row loads, a transpose in
 // registers, eight 16-byte row stores.  Eight lanes cover 128 contiguous
 // bytes of a source row on load and of a destination row on store.  VEC: rows
 // of both matrices start 16-byte aligned; blocks that cross the matrix edge,
 // and every block when !VEC, go element by element.
-template <bool VEC>
+__device__ __forceinline__ uint32_t h2bf(uint32_t h) { return f2bf(h2f(uint16_t(h))); }
+
+template <bool VEC, bool F16_TO_BF16>
 __global__ __launch_bounds__(256) void transpose16_k(const uint16_t* __restrict__ src, int64_t lds,
                                                      uint16_t* __restrict__ dst, int64_t ldd, int R, int C,
                                                      int tiles_c, int64_t n_tiles) {
@@ -490,7 +608,8 @@ __global__ __launch_bounds__(256) void transpose16_k(const uint16_t* __restrict_
             uint32_t w[4];
 #pragma unroll
             for (int i = 0; i < 8; i += 2) {
-                const uint32_t a = h16of(in[i], j), b = h16of(in[i + 1], j);
+                uint32_t a = h16of(in[i], j), b = h16of(in[i + 1], j);
+                if constexpr (F16_TO_BF16) { a = h2bf(a); b = h2bf(b); }
                 w[i >> 1] = a | (b << 16);
             }
             *reinterpret_cast<uint4*>(dst + int64_t(c + j) * ldd + r) = make_uint4(w[0], w[1], w[2], w[3]);
@@ -499,7 +618,10 @@ __global__ __launch_bounds__(256) void transpose16_k(const uint16_t* __restrict_
     }
     const int nr = min(8, R - r), nc = min(8, C - c);
     for (int i = 0; i < nr; ++i)
-        for (int j = 0; j < nc; ++j) dst[int64_t(c + j) * ldd + r + i] = src[int64_t(r + i) * lds + c + j];
+        for (int j = 0; j < nc; ++j) {
+            const uint16_t v = src[int64_t(r + i) * lds + c + j];
+            dst[int64_t(c + j) * ldd + r + i] = F16_TO_BF16 ? uint16_t(h2bf(v)) : v;
+        }
 }
 
 __global__ void fill_zero_k(uint4* __restrict__ p, int64_t n16) {
@@ -513,7 +635,7 @@ inline unsigned blocks(int64_t n, int b) { return unsigned((n + b - 1) / b); }
 }  // namespace
 
 hipError_t rmsnorm_fwd(const void* x, bool x_f32, const uint16_t* gamma, uint16_t* n, uint16_t* n_f16,
-                       float* rstd, int T, int d, float eps, hipStream_t s) {
+                       float* rstd, int T, int d, float eps, hipStream_t s, uint32_t* ovf) {
     if (T < 0 || d <= 0 || (d & 7) || !al16(x) || !al16(gamma) || !al16(n) || (n_f16 && !al16(n_f16)))
         return hipErrorInvalidValue;
     if (T == 0) return hipSuccess;
@@ -526,10 +648,10 @@ hipError_t rmsnorm_fwd(const void* x, bool x_f32, const uint16_t* gamma, uint16_
         constexpr int CPL = decltype(cpl_)::value;
         if (x_f32)
             rmsnorm_fwd_k<float, CPL><<<blocks(T, 4), 256, 0, s>>>(static_cast<const float*>(x), g, nv, nh, rstd, T, d,
-                                                                   eps);
+                                                                   eps, ovf);
         else
             rmsnorm_fwd_k<uint16_t, CPL><<<blocks(T, 4), 256, 0, s>>>(static_cast<const uint16_t*>(x), g, nv, nh, rstd,
-                                                                      T, d, eps);
+                                                                      T, d, eps, ovf);
     };
     if (need <= 1) run(std::integral_constant<int, 1>{});
     else if (need <= 2) run(std::integral_constant<int, 2>{});
@@ -540,41 +662,62 @@ hipError_t rmsnorm_fwd(const void* x, bool x_f32, const uint16_t* gamma, uint16_
     return hipGetLastError();
 }
 
+hipError_t rope_f32_to_bf16(const float* in, int64_t ldin, uint16_t* out, int64_t ldout, const float2* tab, int T,
+                            int S, int n_rot_heads, int hd, int dir, hipStream_t s) {
+    if (T < 0 || S <= 0 || n_rot_heads < 0 || (hd & 15) || (ldin & 3) || (ldout & 7) ||
+        ldin < int64_t(n_rot_heads) * hd || ldout < int64_t(n_rot_heads) * hd || !al16(in) || !al16(out) || !tab)
+        return hipErrorInvalidValue;
+    const int64_t n = int64_t(T) * n_rot_heads * (hd / 16);
+    if (n == 0) return hipSuccess;
+    rope_f32_bf16_k<<<blocks(n, 256), 256, 0, s>>>(in, ldin, out, ldout, tab, T, S, n_rot_heads, hd, dir);
+    return hipGetLastError();
+}
+
 hipError_t qkv_rope_cvt(const float* in, int64_t ldin, uint16_t* out, int64_t ldout, uint16_t* outb, int64_t ldb,
-                        const float2* tab, int T, int S, int n_rot_heads, int n_heads, int hd, hipStream_t s) {
+                        const float2* tab, int T, int S, int n_rot_heads, int n_heads, int hd, hipStream_t s,
+                        uint32_t* ovf) {
     if (T < 0 || S <= 0 || n_rot_heads < 0 || n_heads < n_rot_heads || (hd & 15) || (ldin & 3) || (ldout & 7) ||
         ldin < int64_t(n_heads) * hd || ldout < int64_t(n_heads) * hd || !al16(in) || !al16(out))
         return hipErrorInvalidValue;
-    if (outb && ((ldb & 7) || ldb < int64_t(n_rot_heads) * hd || !al16(outb))) return hipErrorInvalidValue;
+    if (outb && ((ldb & 7) || ldb < int64_t(n_heads) * hd || !al16(outb))) return hipErrorInvalidValue;
     if (T == 0) return hipSuccess;
     const int64_t n = int64_t(T) * n_rot_heads * (hd / 16) + int64_t(T) * (n_heads - n_rot_heads) * (hd / 8);
     qkv_rope_cvt_k<<<blocks(n, 256), 256, 0, s>>>(in, ldin, out, ldout, outb, ldb, tab, T, S, n_rot_heads, n_heads,
-                                                   hd);
+                                                   hd, ovf);
     return hipGetLastError();
 }
 
-hipError_t bf16_to_f16(const uint16_t* in, uint16_t* out, int64_t n, hipStream_t s) {
+hipError_t bf16_to_f16(const uint16_t* in, uint16_t* out, int64_t n, hipStream_t s, uint32_t* ovf) {
     if (n < 0 || (n & 7) || !al16(in) || !al16(out)) return hipErrorInvalidValue;
     if (n == 0) return hipSuccess;
     bf16_to_f16_k<<<blocks(n / 8, 256), 256, 0, s>>>(reinterpret_cast<const uint4*>(in),
-                                                     reinterpret_cast<uint4*>(out), n / 8);
+                                                     reinterpret_cast<uint4*>(out), n / 8, ovf);
     return hipGetLastError();
 }
 
-int64_t rmsnorm_bwd_partial_elems(int T, int d) {
-    const int64_t waves = (int64_t(T) + RPW - 1) / RPW;
-    return ((waves + 3) / 4) * 4 * int64_t(d);
-}
+static int rmsnorm_bwd_blocks(int T) { return std::max(1, std::min(T / 4 + (T % 4 != 0), RMS_BWD_MAX_BLOCKS)); }
+
+int64_t rmsnorm_bwd_partial_elems(int T, int d) { return T <= 0 ? 0 : int64_t(rmsnorm_bwd_blocks(T)) * d; }
 
 template <class TX>
 static void rmsnorm_bwd_launch(int ncl, unsigned nb, const uint4* dn, const TX* x, const uint4* g,
                                const float* rstd, const uint4* resid, uint4* dx, float* partial, int T, int d,
                                hipStream_t s) {
-    if (ncl <= 1) rmsnorm_bwd_k<1, TX><<<nb, 256, 0, s>>>(dn, x, g, rstd, resid, dx, partial, T, d);
-    else if (ncl <= 2) rmsnorm_bwd_k<2, TX><<<nb, 256, 0, s>>>(dn, x, g, rstd, resid, dx, partial, T, d);
-    else if (ncl <= 4) rmsnorm_bwd_k<4, TX><<<nb, 256, 0, s>>>(dn, x, g, rstd, resid, dx, partial, T, d);
-    else if (ncl <= 8) rmsnorm_bwd_k<8, TX><<<nb, 256, 0, s>>>(dn, x, g, rstd, resid, dx, partial, T, d);
-    else rmsnorm_bwd_k<16, TX><<<nb, 256, 0, s>>>(dn, x, g, rstd, resid, dx, partial, T, d);
+    // chunks of 8 columns per lane: the exact count up to 8 (d <= 4096), else 16
+    auto go = [&](auto n_) {
+        rmsnorm_bwd_k<decltype(n_)::value, TX><<<nb, 256, 0, s>>>(dn, x, g, rstd, resid, dx, partial, T, d);
+    };
+    switch (ncl) {
+        case 1: go(std::integral_constant<int, 1>{}); break;
+        case 2: go(std::integral_constant<int, 2>{}); break;
+        case 3: go(std::integral_constant<int, 3>{}); break;
+        case 4: go(std::integral_constant<int, 4>{}); break;
+        case 5: go(std::integral_constant<int, 5>{}); break;
+        case 6: go(std::integral_constant<int, 6>{}); break;
+        case 7: go(std::integral_constant<int, 7>{}); break;
+        case 8: go(std::integral_constant<int, 8>{}); break;
+        default: go(std::integral_constant<int, 16>{});
+    }
 }
 
 hipError_t rmsnorm_bwd(const uint16_t* dn, const void* x, bool x_f32, const uint16_t* gamma,
@@ -583,8 +726,7 @@ hipError_t rmsnorm_bwd(const uint16_t* dn, const void* x, bool x_f32, const uint
     if (T <= 0 || d <= 0 || (d & 7) || d > 8192) return hipErrorInvalidValue;
     if (!al16(dn) || !al16(x) || !al16(gamma) || !al16(dx) || (resid && !al16(resid)))
         return hipErrorInvalidValue;
-    const int64_t waves = (int64_t(T) + RPW - 1) / RPW;
-    const unsigned nb = unsigned((waves + 3) / 4);
+    const unsigned nb = unsigned(rmsnorm_bwd_blocks(T));
     const int ncl = ((d >> 3) + 63) / 64;
     auto U = [](const uint16_t* p) { return reinterpret_cast<const uint4*>(p); };
     uint4* dxv = reinterpret_cast<uint4*>(dx);
@@ -597,7 +739,7 @@ hipError_t rmsnorm_bwd(const uint16_t* dn, const void* x, bool x_f32, const uint
                                      partial, T, d, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dgamma_reduce_k<<<(d + 63) / 64, 1024, 0, s>>>(partial, int(nb) * 4, d, dgamma);
+    dgamma_reduce_k<<<(d + 63) / 64, 1024, 0, s>>>(partial, int(nb), d, dgamma);
     return hipGetLastError();
 }
 
@@ -681,7 +823,8 @@ hipError_t ce_chunk_bwd(const float* logits, const int32_t* labels, const float*
     return hipGetLastError();
 }
 
-hipError_t transpose16(const uint16_t* src, int64_t lds, uint16_t* dst, int64_t ldd, int R, int C, hipStream_t s) {
+hipError_t transpose16(const uint16_t* src, int64_t lds, uint16_t* dst, int64_t ldd, int R, int C, hipStream_t s,
+                       bool f16_to_bf16) {
     if (R < 0 || C < 0 || !src || !dst || lds < C || ldd < R) return hipErrorInvalidValue;
     if (R == 0 || C == 0) return hipSuccess;
     const int tiles_c = (C + 63) / 64;
@@ -689,10 +832,14 @@ hipError_t transpose16(const uint16_t* src, int64_t lds, uint16_t* dst, int64_t 
     const int64_t nb = (n_tiles + 3) / 4;
     if (nb > INT32_MAX) return hipErrorInvalidValue;
     const bool vec = (lds % 8) == 0 && (ldd % 8) == 0 && al16(src) && al16(dst);
-    if (vec)
-        transpose16_k<true><<<unsigned(nb), 256, 0, s>>>(src, lds, dst, ldd, R, C, tiles_c, n_tiles);
-    else
-        transpose16_k<false><<<unsigned(nb), 256, 0, s>>>(src, lds, dst, ldd, R, C, tiles_c, n_tiles);
+    auto go = [&](auto vec_, auto cvt_) {
+        transpose16_k<decltype(vec_)::value, decltype(cvt_)::value>
+            <<<unsigned(nb), 256, 0, s>>>(src, lds, dst, ldd, R, C, tiles_c, n_tiles);
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    if (vec) f16_to_bf16 ? go(T_{}, T_{}) : go(T_{}, F_{});
+    else f16_to_bf16 ? go(F_{}, T_{}) : go(F_{}, F_{});
     return hipGetLastError();
 }
 

@@ -168,7 +168,7 @@ void plan_workspace(const Layout& lay, const mt_options& o, Carver& cv, Workspac
     ws.h1 = cv.take<float>(td * 2);
     ws.n2 = cv.take<uint16_t>(td);
     ws.qkv = cv.take<uint16_t>(uint64_t(T) * nqkv * 2);
-    ws.qkb = cv.take<uint16_t>(uint64_t(T) * (sh.n_heads + sh.n_kv_heads) * sh.head_dim * 2);
+    ws.do16 = cv.take<uint16_t>(uint64_t(T) * nq * 2);
     ws.dqkv = cv.take<uint16_t>(uint64_t(T) * nqkv * 2);
     ws.o = cv.take<uint16_t>(uint64_t(T) * nq * 2);
     ws.dout = cv.take<uint16_t>(uint64_t(T) * nq * 2);
@@ -221,6 +221,8 @@ void plan_workspace(const Layout& lay, const mt_options& o, Carver& cv, Workspac
     ws.deout_acc = tc < T ? cv.take<float>(uint64_t(vc) * d * 4) : nullptr;
     ws.loss_rows = cv.take<float>(uint64_t(T) * 4);
     ws.loss = cv.take<float>(256);
+    ws.ovf = cv.take<uint32_t>(256);
+    ws.amax = cv.take<uint32_t>(256);
 }
 
 ArenaPlan plan_arena(const Layout& lay, const mt_options& o, uint8_t* base, Workspace* ws) {
@@ -510,7 +512,7 @@ struct Ctx {
     hipError_t gemm_nn_t(const uint16_t* A, int64_t lda, const uint16_t* Bm, int64_t ldb, uint16_t* C, int64_t ldc,
                          int M, int N, int K);
     hipError_t gemm_tn_t(const uint16_t* A, int64_t lda, const uint16_t* Bm, int64_t ldb, uint16_t* C, int64_t ldc,
-                         int M, int N, int K);
+                         int M, int N, int K, bool b_f16 = false);
     hipError_t ensure_rope(int S);
     int pick_slot(int unit, bool* need_stream);
     // Stream W of `unit` (elements [e0, e0 + n), n < 0: all) into `slot`; the
@@ -1063,29 +1065,34 @@ hipError_t Ctx::fwd_layer(const LayerView& w, const uint16_t* x, uint16_t* y, in
     const int nq = sh.n_heads * sh.head_dim;
     const int nqkv = (sh.n_heads + 2 * sh.n_kv_heads) * sh.head_dim;
     hipStream_t s = st_c;
-    // Logit path in fp16: n1 and Wqkv go to the QKV product as fp16 (a bf16
+    // Attention in fp16: n1 and Wqkv go to the QKV product as fp16 (a bf16
     // value in fp16's normal range converts exactly; smaller ones keep an
     // absolute error under 2^-25), the projection comes back in fp32, RoPE
-    // rotates it in fp32 and q, k are stored as fp16, v as bf16.
-    HIPR(site(S_RMS1_FWD, [&] { return rmsnorm_fwd(x, false, w.g1, ws.n1, ws.n1h, ws.rstd1, T, d, sh.rms_eps, s); }));
+    // rotates q and k in fp32 and q, k, v are stored as fp16; the attention
+    // products run on the fp16 MFMA and o is fp16, and so are the operands of
+    // the O product (Wo converted like Wqkv).  Every fp16 value is range
+    // guarded (saturated and counted in ws.ovf).
+    HIPR(site(S_RMS1_FWD, [&] {
+        return rmsnorm_fwd(x, false, w.g1, ws.n1, ws.n1h, ws.rstd1, T, d, sh.rms_eps, s, ws.ovf);
+    }));
     HIPR(site(S_GEMM_QKV, [&] {
-        HIPR(bf16_to_f16(w.wqkv, ws.w16, int64_t(nqkv) * d, s));
+        HIPR(bf16_to_f16(w.wqkv, ws.w16, int64_t(nqkv) * d, s, ws.ovf));
         GemmArgs a{ws.n1h, d, ws.w16, d, ws.qkv32, nqkv, nullptr, 0, nullptr, 0, T, nqkv, d};
         return gemm(GEMM_NT, EPI_F32_F16IN, a, s);
     }));
     HIPR(site(S_ROPE_FWD, [&] {
-        // The recompute (no y) feeds the backward: it also keeps q, k in bf16.
-        const int64_t nr = int64_t(sh.n_heads + sh.n_kv_heads) * sh.head_dim;
-        return qkv_rope_cvt(ws.qkv32, nqkv, ws.qkv, nqkv, need_y ? nullptr : ws.qkb, nr, ws.rope_tab, T, S,
-                            sh.n_heads + sh.n_kv_heads, sh.n_heads + 2 * sh.n_kv_heads, sh.head_dim, s);
+        return qkv_rope_cvt(ws.qkv32, nqkv, ws.qkv, nqkv, nullptr, 0, ws.rope_tab, T, S, sh.n_heads + sh.n_kv_heads,
+                            sh.n_heads + 2 * sh.n_kv_heads, sh.head_dim, s, ws.ovf);
     }));
     HIPR(site(S_ATTN_FWD, [&] {
-        AttnArgs a{ws.qkv, nqkv, ws.o, nq, ws.lse, B, S, sh.n_heads, sh.n_kv_heads, sh.head_dim};
+        AttnArgs a{ws.qkv, nqkv, ws.o, nq, ws.lse, B, S, sh.n_heads, sh.n_kv_heads, sh.head_dim, ws.ovf};
         return attn_fwd(a, s);
     }));
     HIPR(site(S_GEMM_O, [&] {
-        GemmArgs a{ws.o, nq, w.wo, nq, ws.h1, d, x, d, nullptr, 0, T, d, nq};
-        return gemm(GEMM_NT, EPI_F32_RESID, a, s);
+        // ws.w16 is free again: the QKV product before it on this stream read it
+        HIPR(bf16_to_f16(w.wo, ws.w16, int64_t(d) * nq, s, ws.ovf));
+        GemmArgs a{ws.o, nq, ws.w16, nq, ws.h1, d, x, d, nullptr, 0, T, d, nq};
+        return gemm(GEMM_NT, EPI_F32_F16IN_RESID, a, s);
     }));
     HIPR(site(S_RMS2_FWD, [&] { return rmsnorm_fwd(ws.h1, true, w.g2, ws.n2, nullptr, ws.rstd2, T, d, sh.rms_eps, s); }));
     HIPR(site(S_GEMM_GATEUP, [&] {
@@ -1126,15 +1133,20 @@ hipError_t Ctx::bwd_layer(const LayerView& w, const LayerView& g, const uint16_t
     }));
     // attention
     HIPR(site(S_GEMM_O_DX, [&] { return gemm_nn_t(ws.dh1, d, w.wo, nq, ws.dout, nq, T, nq, d); }));
-    HIPR(site(S_GEMM_O_DW, [&] { return gemm_tn_t(ws.dh1, d, ws.o, nq, g.wo, nq, d, nq, T); }));
+    // o is fp16: its transpose rounds it to bf16 for the bf16 product
+    HIPR(site(S_GEMM_O_DW, [&] { return gemm_tn_t(ws.dh1, d, ws.o, nq, g.wo, nq, d, nq, T, true); }));
+    // The attention backward on the fp16 operands of the recomputed forward:
+    // dV into dqkv, dQ and dK in fp32 into the projection buffer (free since
+    // the recompute's rotation read it), then rotated back by -theta and
+    // rounded to bf16 once.
     HIPR(site(S_ATTN_BWD, [&] {
-        AttnBwdArgs a{ws.qkv, nqkv, ws.o, ws.dout, nq, ws.lse, ws.dsum, ws.dqkv, nqkv,
-                      B, S, sh.n_heads, sh.n_kv_heads, sh.head_dim,
-                      ws.qkb, int64_t(sh.n_heads + sh.n_kv_heads) * sh.head_dim};
+        AttnBwdArgs a{ws.qkv, nqkv, ws.o, ws.dout, nq, ws.lse, ws.dsum, ws.do16, ws.amax, ws.dqkv, nqkv,
+                      B, S, sh.n_heads, sh.n_kv_heads, sh.head_dim, ws.qkv32, nqkv, ws.ovf};
         return attn_bwd(a, s);
     }));
     HIPR(site(S_ROPE_BWD, [&] {
-        return rope_apply(ws.dqkv, nqkv, ws.rope_tab, T, S, sh.n_heads + sh.n_kv_heads, sh.head_dim, -1, s);
+        return rope_f32_to_bf16(ws.qkv32, nqkv, ws.dqkv, nqkv, ws.rope_tab, T, S, sh.n_heads + sh.n_kv_heads,
+                                sh.head_dim, -1, s);
     }));
     HIPR(site(S_GEMM_QKV_DX, [&] { return gemm_nn_t(ws.dqkv, nqkv, w.wqkv, d, ws.dn, d, T, d, nqkv); }));
     HIPR(site(S_GEMM_QKV_DW, [&] { return gemm_tn_t(ws.dqkv, nqkv, ws.n1, d, g.wqkv, d, nqkv, d, T); }));
@@ -1248,16 +1260,16 @@ hipError_t Ctx::gemm_nn_t(const uint16_t* A, int64_t lda, const uint16_t* Bm, in
 
 // C[M x N] = A^T B with A stored [K x M] and B [K x N]: both transposed, then
 // NT.  K (the tokens) is padded to a multiple of 8 with zero columns, which
-// add nothing.
+// add nothing.  b_f16: B holds fp16, rounded to bf16 by its transpose.
 hipError_t Ctx::gemm_tn_t(const uint16_t* A, int64_t lda, const uint16_t* Bm, int64_t ldb, uint16_t* C, int64_t ldc,
-                          int M, int N, int K) {
+                          int M, int N, int K, bool b_f16) {
     const int Kp = (K + 7) & ~7;
     if (Kp != K) {
         HIPR(fill_zero(ws.tA, int64_t(M) * Kp * 2, st_c));
         HIPR(fill_zero(ws.tB, int64_t(N) * Kp * 2, st_c));
     }
     HIPR(transpose16(A, lda, ws.tA, Kp, K, M, st_c));
-    HIPR(transpose16(Bm, ldb, ws.tB, Kp, K, N, st_c));
+    HIPR(transpose16(Bm, ldb, ws.tB, Kp, K, N, st_c, b_f16));
     GemmArgs a{ws.tA, Kp, ws.tB, Kp, C, ldc, nullptr, 0, nullptr, 0, M, N, Kp};
     return gemm(GEMM_NT, EPI_BF16, a, st_c);
 }
@@ -1401,6 +1413,7 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
     // power of two).
     const float inv_tokens = 1.0f / float(int64_t(n_micro) * T);
     HIPC(hipEventRecord(t_base, st_c));
+    HIPC(fill_zero(ws.ovf, 256, st_c));  // fp16 range guard counter of this step
     HIPC(ensure_rope(S));
     if (opt.resident) {
         // The comparison run: every unit's weights copied up once, no streaming.
@@ -1741,6 +1754,8 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
             worker_status = MT_OK;
         }
     }
+    uint32_t* ovf_pin = reinterpret_cast<uint32_t*>(loss_pin) + 1;
+    HIPC(hipMemcpyAsync(ovf_pin, ws.ovf, 4, hipMemcpyDeviceToHost, st_c));
     HIPC(hsync(loss_done));
     HIPC(hipStreamSynchronize(st_c));
     HIPC(hipStreamSynchronize(st_w));
@@ -1849,6 +1864,9 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
         const double inter = intersect(Cm, Xm);
         const double lc = len(Cm), lx = len(Xm);
         stats->overlap_ratio = std::min(lc, lx) > 0 ? inter / std::min(lc, lx) : 0.0;
+        stats->compute_union_ms = lc;
+        stats->copy_union_ms = lx;
+        stats->overlap_ms = inter;
         stats->pcie_busy_frac = t_total > 0 ? len(Hm) / t_total : 0.0;
         // The same per phase (forward, head, backward), and the transfer time
         // no compute hides, |X \ C|.
@@ -1868,12 +1886,47 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
             stats->overlap_phase[p] = std::min(lcp[p], lxp[p]) > 0 ? ip[p] / std::min(lcp[p], lxp[p]) : 0.0;
             stats->exposed_transfer_ms[p] = lxp[p] - ip[p];
         }
+        // Switch gaps (end of a compute visit to the start of the next, by
+        // the phase the next visit starts in) and device idle time (neither
+        // compute nor copies) per phase.
+        {
+            std::vector<std::pair<double, double>> cv;
+            for (auto& iv : intervals)
+                if (iv.kind == 0) cv.push_back({el(t_base, iv.a), el(t_base, iv.b)});
+            std::sort(cv.begin(), cv.end());
+            std::vector<double> gaps[3];
+            double idle[3] = {};
+            for (const Phases& ph : phases) {
+                const double edges[4] = {el(t_base, ph.start), el(t_base, ph.fwd), el(t_base, ph.head),
+                                         el(t_base, ph.bwd)};
+                for (size_t i = 1; i < cv.size(); ++i) {
+                    const double st = cv[i].first;
+                    for (int p = 0; p < 3; ++p)
+                        if (st > edges[p] && st <= edges[p + 1]) gaps[p].push_back(std::max(0.0, st - cv[i - 1].second));
+                }
+                for (int p = 0; p < 3; ++p) {
+                    std::vector<std::pair<double, double>> both = clip(Cm, edges[p], edges[p + 1]);
+                    const auto xp = clip(Xm, edges[p], edges[p + 1]);
+                    both.insert(both.end(), xp.begin(), xp.end());
+                    idle[p] += (edges[p + 1] - edges[p]) - len(merge(both));
+                }
+            }
+            for (int p = 0; p < 3; ++p) {
+                auto& g = gaps[p];
+                if (!g.empty()) {
+                    std::nth_element(g.begin(), g.begin() + g.size() / 2, g.end());
+                    stats->switch_gap_ms[p] = g[g.size() / 2];
+                }
+                stats->device_idle_ms[p] = std::max(0.0, idle[p]);
+            }
+        }
         stats->pack_ms = pack_ms;
         {
             std::lock_guard<std::mutex> lk(q_mu);
             stats->adam_ms = adam_ms_acc;
             stats->adam_wait_ms = adam_wait_ms;
         }
+        stats->fp16_saturated = *ovf_pin;
         stats->gpu_arena_bytes = plan.total;
         stats->pinned_bytes = pplan.total;
         stats->host_store_bytes = uint64_t(lay.store_bytes);

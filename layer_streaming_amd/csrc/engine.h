@@ -45,7 +45,7 @@ struct Workspace {
     std::vector<uint16_t*> xc;
     uint16_t* ckpt_dev = nullptr;  // [L+1][maxT x d] when checkpoints stay on the GPU
     uint16_t *n1, *qkv, *o, *n2, *gu, *m;
-    uint16_t* qkb;  // bf16 copy of the rotated q and k (recompute), for the attention backward
+    uint16_t* do16;  // attention backward: dO scaled by 2^k, fp16
     float* h1;  // residual stream inside a layer, kept in fp32
     // logit path: fp16 copies of n1 and Wqkv, fp32 QKV projection before RoPE
     uint16_t *n1h, *w16;
@@ -64,6 +64,8 @@ struct Workspace {
     // head streamed in E_out row chunks: fp32 dnf accumulated over the
     // chunks, running max / sum of exp / label logit / LSE per token
     float *dnf_acc = nullptr, *ce_m = nullptr, *ce_l = nullptr, *ce_z = nullptr, *ce_lse = nullptr;
+    uint32_t* ovf = nullptr;  // fp16 range guard: values saturated in this step
+    uint32_t* amax = nullptr;  // attention backward: max|dO|, max|v| (256 bytes)
     uint64_t bytes = 0;
 };
 

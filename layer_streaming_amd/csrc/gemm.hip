@@ -191,7 +191,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs p, int tile
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
-                    if constexpr (EPI == EPI_F32_F16IN)
+                    if constexpr (EPI == EPI_F32_F16IN || EPI == EPI_F32_F16IN_RESID)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(af[i]), as_f16x8(bfr[j]),
                                                                            acc[i][j], 0, 0, 0);
                     else
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs p, int tile
                 } else if constexpr (EPI == EPI_F32_ACC) {
                     float* c = static_cast<float*>(p.C) + int64_t(row) * p.ldc + col;
                     *c = *c + v;
-                } else if constexpr (EPI == EPI_F32_RESID) {
+                } else if constexpr (EPI == EPI_F32_RESID || EPI == EPI_F32_F16IN_RESID) {
                     v += bf2f(static_cast<const uint16_t*>(p.R)[int64_t(row) * p.ldr + col]);
                     static_cast<float*>(p.C)[int64_t(row) * p.ldc + col] = v;
                 } else if constexpr (EPI == EPI_BF16_RESID32) {
@@ -271,6 +271,12 @@ hipError_t launch_epi(GemmEpi epi, const GemmArgs& a, hipStream_t s) {
                 break;
             }
             return hipErrorInvalidValue;
+        case EPI_F32_F16IN_RESID:
+            if constexpr (AK && BKM) {
+                gemm_kernel<BM, BN, WM, WN, AK, BKM, EPI_F32_F16IN_RESID><<<grid, block, 0, s>>>(a, tm, tn);
+                break;
+            }
+            return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -304,11 +310,12 @@ hipError_t gemm(GemmLayout lay, GemmEpi epi, const GemmArgs& a, hipStream_t s) {
     if (ak ? a.lda < a.K : a.lda < a.M) return hipErrorInvalidValue;
     if (bk ? a.ldb < a.K : a.ldb < a.N) return hipErrorInvalidValue;
     if (a.ldc < a.N) return hipErrorInvalidValue;
-    if ((epi == EPI_BF16_RESID || epi == EPI_F32_RESID || epi == EPI_BF16_RESID32) && (!a.R || a.ldr < a.N))
+    if ((epi == EPI_BF16_RESID || epi == EPI_F32_RESID || epi == EPI_BF16_RESID32 || epi == EPI_F32_F16IN_RESID) &&
+        (!a.R || a.ldr < a.N))
         return hipErrorInvalidValue;
     if (epi == EPI_BF16_ACCF32 && (!a.Cacc || a.ldacc < a.N)) return hipErrorInvalidValue;
-    if (epi == EPI_F32_F16IN && lay != GEMM_NT) return hipErrorInvalidValue;
-    if (int(epi) < 0 || int(epi) > int(EPI_F32_F16IN)) return hipErrorInvalidValue;
+    if ((epi == EPI_F32_F16IN || epi == EPI_F32_F16IN_RESID) && lay != GEMM_NT) return hipErrorInvalidValue;
+    if (int(epi) < 0 || int(epi) > int(EPI_F32_F16IN_RESID)) return hipErrorInvalidValue;
     if (lay == GEMM_NT) {
         const hipError_t e = gemm_nt_direct(epi, a, s);
         if (e != hipErrorNotSupported) return e;

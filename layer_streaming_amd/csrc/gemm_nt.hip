@@ -223,7 +223,7 @@ __device__ __forceinline__ void store4(const GemmArgs& p, int row, int col, cons
     const int64_t ci = int64_t(row) * p.ldc + col;
     if (col + 4 <= p.N) {
         float w[4] = {v[0], v[1], v[2], v[3]};
-        if constexpr (EPI == EPI_BF16_RESID || EPI == EPI_F32_RESID) {
+        if constexpr (EPI == EPI_BF16_RESID || EPI == EPI_F32_RESID || EPI == EPI_F32_F16IN_RESID) {
             const uint2 r = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.R) + int64_t(row) * p.ldr + col);
             w[0] += bflo(r.x); w[1] += bfhi(r.x); w[2] += bflo(r.y); w[3] += bfhi(r.y);
         } else if constexpr (EPI == EPI_BF16_RESID32) {
@@ -236,7 +236,8 @@ __device__ __forceinline__ void store4(const GemmArgs& p, int row, int col, cons
             const float4 r = *reinterpret_cast<const float4*>(static_cast<const float*>(p.C) + ci);
             w[0] += r.x; w[1] += r.y; w[2] += r.z; w[3] += r.w;
         }
-        if constexpr (EPI == EPI_F32 || EPI == EPI_F32_F16IN || EPI == EPI_F32_ACC || EPI == EPI_F32_RESID)
+        if constexpr (EPI == EPI_F32 || EPI == EPI_F32_F16IN || EPI == EPI_F32_ACC || EPI == EPI_F32_RESID ||
+                      EPI == EPI_F32_F16IN_RESID)
             st_f4(static_cast<float*>(p.C) + ci, w);
         else
             st_b4(static_cast<uint16_t*>(p.C) + ci, w);
@@ -247,7 +248,7 @@ __device__ __forceinline__ void store4(const GemmArgs& p, int row, int col, cons
         const int c = col + e;
         if (c >= p.N) break;
         float w = v[e];
-        if constexpr (EPI == EPI_BF16_RESID || EPI == EPI_F32_RESID)
+        if constexpr (EPI == EPI_BF16_RESID || EPI == EPI_F32_RESID || EPI == EPI_F32_F16IN_RESID)
             w += bf2f(static_cast<const uint16_t*>(p.R)[int64_t(row) * p.ldr + c]);
         else if constexpr (EPI == EPI_BF16_RESID32)
             w += static_cast<const float*>(p.R)[int64_t(row) * p.ldr + c];
@@ -255,7 +256,8 @@ __device__ __forceinline__ void store4(const GemmArgs& p, int row, int col, cons
             w += p.Cacc[int64_t(row) * p.ldacc + c];
         else if constexpr (EPI == EPI_F32_ACC)
             w += static_cast<const float*>(p.C)[ci + e];
-        if constexpr (EPI == EPI_F32 || EPI == EPI_F32_F16IN || EPI == EPI_F32_ACC || EPI == EPI_F32_RESID)
+        if constexpr (EPI == EPI_F32 || EPI == EPI_F32_F16IN || EPI == EPI_F32_ACC || EPI == EPI_F32_RESID ||
+                      EPI == EPI_F32_F16IN_RESID)
             static_cast<float*>(p.C)[ci + e] = w;
         else
             static_cast<uint16_t*>(p.C)[ci + e] = f2bf(w);
@@ -335,7 +337,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_k(GemmArgs p, int tiles_
     constexpr int NW = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
-    constexpr bool F16 = EPI == EPI_F32_F16IN;
+    constexpr bool F16 = EPI == EPI_F32_F16IN || EPI == EPI_F32_F16IN_RESID;
     // four stages, one array each, so that the compiler can tell the LDS
     // reads of one stage from the loads in flight into another
     __shared__ uint4 As0[BM * 4], As1[BM * 4], As2[BM * 4], As3[BM * 4];
@@ -550,7 +552,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt64_k(GemmArgs p, int tile
     constexpr int NW = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
-    constexpr bool F16 = EPI == EPI_F32_F16IN;
+    constexpr bool F16 = EPI == EPI_F32_F16IN || EPI == EPI_F32_F16IN_RESID;
     __shared__ uint4 As0[BM * 8], As1[BM * 8];
     __shared__ uint4 Bs0[BN * 8], Bs1[BN * 8];
 
@@ -721,6 +723,10 @@ hipError_t launch(GemmEpi epi, const GemmArgs& a, hipStream_t s) {
             if constexpr (K64) gemm_nt64_k<BM, BN, WM, WN, EPI_F32_F16IN><<<grid, block, 0, s>>>(a, tm, tn);
             else gemm_nt_k<BM, BN, WM, WN, EPI_F32_F16IN><<<grid, block, 0, s>>>(a, tm, tn);
             break;
+        case EPI_F32_F16IN_RESID:
+            if constexpr (K64) gemm_nt64_k<BM, BN, WM, WN, EPI_F32_F16IN_RESID><<<grid, block, 0, s>>>(a, tm, tn);
+            else gemm_nt_k<BM, BN, WM, WN, EPI_F32_F16IN_RESID><<<grid, block, 0, s>>>(a, tm, tn);
+            break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -733,7 +739,8 @@ inline bool al16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) =
 hipError_t gemm_nt_direct(GemmEpi epi, const GemmArgs& a, hipStream_t s) {
     // Preconditions beyond gemm()'s checks: 4-column epilogue vectors stay
     // aligned, and a block's rows x ld fit the 31-bit buffer offsets.
-    const bool resid = epi == EPI_BF16_RESID || epi == EPI_F32_RESID || epi == EPI_BF16_RESID32;
+    const bool resid = epi == EPI_BF16_RESID || epi == EPI_F32_RESID || epi == EPI_BF16_RESID32 ||
+                       epi == EPI_F32_F16IN_RESID;
     if ((a.ldc & 3) || !al16(a.C)) return hipErrorNotSupported;
     if (resid && ((a.ldr & 3) || !al16(a.R))) return hipErrorNotSupported;
     if (epi == EPI_BF16_ACCF32 && ((a.ldacc & 3) || !al16(a.Cacc))) return hipErrorNotSupported;

@@ -63,3 +63,28 @@ __device__ __forceinline__ uint4 pack8h(const float* f) {
     auto p = [](float a, float b) { return uint32_t(f2h(a)) | (uint32_t(f2h(b)) << 16); };
     return make_uint4(p(f[0], f[1]), p(f[2], f[3]), p(f[4], f[5]), p(f[6], f[7]));
 }
+
+// Range guard of the fp16 operands.  A value whose magnitude rounds beyond
+// the largest finite fp16 (|x| >= 65520, or not finite) is counted in n and
+// saturated to +-65504 (a NaN stays a NaN); every other value converts with
+// round to nearest even.  Values below fp16's normal range (2^-14) become
+// subnormals with an absolute error of at most 2^-25.
+__device__ __forceinline__ uint16_t f2h_sat(float f, uint32_t& n) {
+    if (!(fabsf(f) < 65520.f)) {
+        ++n;
+        if (f == f) f = copysignf(65504.f, f);
+    }
+    return f2h(f);
+}
+__device__ __forceinline__ uint32_t pack2h_sat(float a, float b, uint32_t& n) {
+    return uint32_t(f2h_sat(a, n)) | (uint32_t(f2h_sat(b, n)) << 16);
+}
+__device__ __forceinline__ uint4 pack8h_sat(const float* f, uint32_t& n) {
+    return make_uint4(pack2h_sat(f[0], f[1], n), pack2h_sat(f[2], f[3], n), pack2h_sat(f[4], f[5], n),
+                      pack2h_sat(f[6], f[7], n));
+}
+// Add a lane's overflow count to the caller's counter (only lanes that saw
+// one: the common case issues no atomic at all).
+__device__ __forceinline__ void count_ovf(uint32_t* ovf, uint32_t n) {
+    if (ovf && n) atomicAdd(ovf, n);
+}

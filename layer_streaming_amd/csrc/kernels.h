@@ -24,6 +24,7 @@ enum GemmEpi {
     EPI_F32_RESID = 5,   // C(f32)  = acc + R(bf16)
     EPI_BF16_RESID32 = 6,// C(bf16) = acc + R(f32)
     EPI_F32_F16IN = 7,   // operands fp16 (not bf16), C(f32) = acc; NT layout only
+    EPI_F32_F16IN_RESID = 8,  // operands fp16, C(f32) = acc + R(bf16); NT layout only
 };
 struct GemmArgs {
     const void* A; int64_t lda;
@@ -42,8 +43,10 @@ hipError_t gemm_nt_direct(GemmEpi epi, const GemmArgs& a, hipStream_t s);
 // ------------------------------------------------------------- RMSNorm ----
 // n = gamma * x * rstd, rstd = 1/sqrt(mean(x^2)+eps); x bf16 or fp32 (x_f32),
 // n and gamma bf16; n_f16 (may be null) receives the same values in fp16.
+// ovf (may be null): counter of fp16 values out of range (saturated to
+// +-65504), the range guard of every fp16 operand the kernels write.
 hipError_t rmsnorm_fwd(const void* x, bool x_f32, const uint16_t* gamma, uint16_t* n, uint16_t* n_f16,
-                       float* rstd, int T, int d, float eps, hipStream_t s);
+                       float* rstd, int T, int d, float eps, hipStream_t s, uint32_t* ovf = nullptr);
 // dx = resid + rstd*(g - nh*mean(g*nh)), g = dn*gamma, nh = x*rstd (resid may be null);
 // dgamma = sum_t dn*nh written as bf16 (two-stage, fixed order).  `partial` is
 // fp32 scratch of rmsnorm_bwd_partial_elems(T, d) elements.
@@ -59,13 +62,20 @@ hipError_t rope_table(float2* tab, int S, int hd, float base, hipStream_t s);
 // position s = t % S; dir = +1 forward, -1 backward (rotation by -theta).
 hipError_t rope_apply(uint16_t* qkv, int64_t ld, const float2* tab, int T, int S, int n_rot_heads,
                       int hd, int dir, hipStream_t s);
+// The same rotation of the first n_rot_heads heads of fp32 in [T x ldin],
+// written as bf16 to out [T x ldout] (one rounding): the attention backward's
+// dQ, dK rotated back by -theta (dir = -1).
+hipError_t rope_f32_to_bf16(const float* in, int64_t ldin, uint16_t* out, int64_t ldout, const float2* tab, int T,
+                            int S, int n_rot_heads, int hd, int dir, hipStream_t s);
 // From the fp32 QKV projection in [T x ldin] (n_heads heads of hd): rotate the
-// first n_rot_heads (q and k) and write them as fp16, the rest (v) as bf16,
-// into out [T x ldout] (the attention operand buffer).
+// first n_rot_heads (q and k), and write every head as fp16 (saturated and
+// counted in ovf) into out [T x ldout] (the attention operand buffer); outb
+// (may be null) [T x ldb, ldb >= n_heads*hd] gets the same heads in bf16.
 hipError_t qkv_rope_cvt(const float* in, int64_t ldin, uint16_t* out, int64_t ldout, uint16_t* outb, int64_t ldb,
-                        const float2* tab, int T, int S, int n_rot_heads, int n_heads, int hd, hipStream_t s);
-// Elementwise bf16 -> fp16 (n a multiple of 8).
-hipError_t bf16_to_f16(const uint16_t* in, uint16_t* out, int64_t n, hipStream_t s);
+                        const float2* tab, int T, int S, int n_rot_heads, int n_heads, int hd, hipStream_t s,
+                        uint32_t* ovf = nullptr);
+// Elementwise bf16 -> fp16 (n a multiple of 8), saturated and counted in ovf.
+hipError_t bf16_to_f16(const uint16_t* in, uint16_t* out, int64_t n, hipStream_t s, uint32_t* ovf = nullptr);
 
 // -------------------------------------------------------------- SwiGLU ----
 // gu [T x 2F] = [gate | up] -> m [T x F] = silu(gate) * up.
@@ -75,27 +85,35 @@ hipError_t swiglu_bwd(const uint16_t* dm, const uint16_t* gu, uint16_t* dgu, int
                       hipStream_t s);
 
 // ----------------------------------------------------------- Attention ----
-// qkv [B*S x ld]: q heads at column 0, k heads at Hq*hd, v heads at (Hq+Hkv)*hd;
-// q and k are fp16 (the logit path), v bf16.  o, dout and dqkv are bf16.
+// qkv [B*S x ld]: q heads at column 0, k heads at Hq*hd, v heads at (Hq+Hkv)*hd,
+// all fp16; the forward's products (scores and P.V) run on the fp16 MFMA and
+// o is written as fp16.  dout and dqkv are bf16.
 struct AttnArgs {
     const uint16_t* qkv; int64_t ld;
-    uint16_t* o; int64_t ldo;   // [B*S x Hq*hd]
+    uint16_t* o; int64_t ldo;   // [B*S x Hq*hd] fp16
     float* lse;                 // [B x Hq x S], natural-log sum-exp of scaled scores
     int B, S, Hq, Hkv, hd;
+    uint32_t* ovf = nullptr;    // fp16 range guard: o values saturated to +-65504
 };
 hipError_t attn_fwd(const AttnArgs& a, hipStream_t s);
 struct AttnBwdArgs {
-    const uint16_t* qkv; int64_t ld;
-    const uint16_t* o; const uint16_t* dout; int64_t ldo;
+    const uint16_t* qkv; int64_t ld;  // fp16 q, k, v as the forward used them
+    const uint16_t* o; const uint16_t* dout; int64_t ldo;  // o fp16, dout bf16
     const float* lse;
-    float* dsum;                // scratch [B x Hq x S]: rowsum(dO * O)
-    uint16_t* dqkv; int64_t ldd; // output, same column layout as qkv
+    float* dsum;           // scratch [B x Hq x S]: rowsum(dO * O) 2^k
+    uint16_t* do16;        // scratch [B*S x Hq*hd] fp16: dO 2^k
+    uint32_t* amax;        // scratch, 256 bytes: max|dO| and max|v| that fix 2^k
+    uint16_t* dqkv; int64_t ldd;  // output in qkv's column layout: dV bf16, and dQ, dK bf16 unless dqk32
     int B, S, Hq, Hkv, hd;
-    // Optional bf16 copy of the rotated q and k, [B*S x (Hq+Hkv)*hd] (k after
-    // the Hq query heads), for the gradient products; null: the kernels round
-    // the fp16 q and k to bf16 themselves (staging through registers).
-    const uint16_t* qkb = nullptr; int64_t ldb = 0;
+    // Optional: dQ and dK in fp32 [B*S x ld32] (the Hq query heads, then the
+    // Hkv key heads), for a rotation that rounds them to bf16 once.
+    float* dqk32 = nullptr; int64_t ld32 = 0;
+    uint32_t* ovf = nullptr;  // fp16 range guard of the scaled dO
 };
+// Scratch bytes of attn_bwd (dsum, do16, amax) and their carving from one
+// 256-byte-aligned block.
+int64_t attn_bwd_work_bytes(int B, int S, int Hq, int hd);
+void attn_bwd_carve(void* work, int B, int S, int Hq, int hd, AttnBwdArgs& a);
 hipError_t attn_bwd(const AttnBwdArgs& a, hipStream_t s);
 
 // ------------------------------------------------------- Cross-entropy ----
@@ -119,7 +137,9 @@ hipError_t ce_chunk_bwd(const float* logits, const int32_t* labels, const float*
 // --------------------------------------------------------------- misc -----
 hipError_t f32_to_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t s);
 hipError_t fill_zero(void* p, int64_t bytes, hipStream_t s);
-// dst[c * ldd + r] = src[r * lds + c] for an R x C matrix of 16-bit elements.
-hipError_t transpose16(const uint16_t* src, int64_t lds, uint16_t* dst, int64_t ldd, int R, int C, hipStream_t s);
+// dst[c * ldd + r] = src[r * lds + c] for an R x C matrix of 16-bit elements;
+// f16_to_bf16: the source is fp16 and the destination gets it rounded to bf16.
+hipError_t transpose16(const uint16_t* src, int64_t lds, uint16_t* dst, int64_t ldd, int R, int C, hipStream_t s,
+                       bool f16_to_bf16 = false);
 
 }  // namespace mt

@@ -50,7 +50,10 @@ class mt_stats(C.Structure):
                 ("exposed_transfer_ms", C.c_double * 3),
                 ("h2d_bytes", C.c_uint64), ("d2h_bytes", C.c_uint64), ("gpu_arena_bytes", C.c_uint64),
                 ("pinned_bytes", C.c_uint64), ("host_store_bytes", C.c_uint64), ("n_sites", C.c_int32),
-                ("site_ms", C.c_double * MT_MAX_SITES), ("site_launches", C.c_uint64 * MT_MAX_SITES)]
+                ("site_ms", C.c_double * MT_MAX_SITES), ("site_launches", C.c_uint64 * MT_MAX_SITES),
+                ("fp16_saturated", C.c_uint64), ("compute_union_ms", C.c_double),
+                ("copy_union_ms", C.c_double), ("overlap_ms", C.c_double), ("switch_gap_ms", C.c_double * 3),
+                ("device_idle_ms", C.c_double * 3)]
 
 
 class mt_tensor_info(C.Structure):
@@ -88,7 +91,7 @@ _SIGS = {
     # test entries
     "mt_k_gemm": (C.c_int, [C.c_int32, C.c_int32, _P, C.c_int64, _P, C.c_int64, _P, C.c_int64, _P, C.c_int64,
                             _P, C.c_int64, C.c_int32, C.c_int32, C.c_int32, _P]),
-    "mt_k_rmsnorm_fwd": (C.c_int, [_P, C.c_int32, _P, _P, _P, _P, C.c_int32, C.c_int32, C.c_float, _P]),
+    "mt_k_rmsnorm_fwd": (C.c_int, [_P, C.c_int32, _P, _P, _P, _P, C.c_int32, C.c_int32, C.c_float, _P, _P]),
     "mt_k_rmsnorm_bwd_scratch_elems": (C.c_int64, [C.c_int32, C.c_int32]),
     "mt_k_rmsnorm_bwd": (C.c_int, [_P, _P, C.c_int32, _P, _P, _P, _P, _P, _P, C.c_int32, C.c_int32, _P]),
     "mt_k_rope": (C.c_int, [_P, C.c_int64, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_float, C.c_int32,
@@ -96,16 +99,19 @@ _SIGS = {
     "mt_k_swiglu_fwd": (C.c_int, [_P, _P, C.c_int32, C.c_int32, _P]),
     "mt_k_swiglu_bwd": (C.c_int, [_P, _P, _P, C.c_int32, C.c_int32, _P]),
     "mt_k_attn_fwd": (C.c_int, [_P, C.c_int64, _P, C.c_int64, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
-                                C.c_int32, _P]),
+                                C.c_int32, _P, _P]),
+    "mt_k_attn_bwd_work_bytes": (C.c_int64, [C.c_int32, C.c_int32, C.c_int32, C.c_int32]),
     "mt_k_attn_bwd": (C.c_int, [_P, C.c_int64, _P, _P, C.c_int64, _P, _P, _P, C.c_int64, C.c_int32, C.c_int32,
-                                C.c_int32, C.c_int32, C.c_int32, _P, C.c_int64, _P]),
+                                C.c_int32, C.c_int32, C.c_int32, _P, C.c_int64, _P, _P]),
+    "mt_k_rope_f32_bf16": (C.c_int, [_P, C.c_int64, _P, C.c_int64, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                     C.c_float, C.c_int32, _P]),
     "mt_k_ce": (C.c_int, [_P, _P, _P, _P, C.c_int32, C.c_int32, C.c_float, _P]),
     "mt_k_mean": (C.c_int, [_P, _P, C.c_int32, _P]),
     "mt_k_f32_to_bf16": (C.c_int, [_P, _P, C.c_int64, _P]),
-    "mt_k_transpose16": (C.c_int, [_P, C.c_int64, _P, C.c_int64, C.c_int32, C.c_int32, _P]),
+    "mt_k_transpose16": (C.c_int, [_P, C.c_int64, _P, C.c_int64, C.c_int32, C.c_int32, C.c_int32, _P]),
     "mt_k_qkv_rope_cvt": (C.c_int, [_P, C.c_int64, _P, C.c_int64, _P, C.c_int64, _P, C.c_int32, C.c_int32,
-                                    C.c_int32, C.c_int32, C.c_int32, C.c_float, _P]),
-    "mt_k_bf16_to_f16": (C.c_int, [_P, _P, C.c_int64, _P]),
+                                    C.c_int32, C.c_int32, C.c_int32, C.c_float, _P, _P]),
+    "mt_k_bf16_to_f16": (C.c_int, [_P, _P, C.c_int64, _P, _P]),
     "mt_host_adam": (C.c_int, [_P, _P, _P, _P, _P, _P, C.c_int64, C.c_int64, C.c_float, C.c_float, C.c_float,
                                C.c_float, C.c_int32]),
     "mt_host_accum": (C.c_int, [_P, _P, C.c_int64, C.c_int32]),
@@ -269,10 +275,10 @@ class Context:
 
 def stats_dict(st):
     names = site_names()
-    d = {k: getattr(st, k) for k, _ in mt_stats._fields_
-         if k not in ("site_ms", "site_launches", "overlap_phase", "exposed_transfer_ms")}
-    d["overlap_phase"] = list(st.overlap_phase)
-    d["exposed_transfer_ms"] = list(st.exposed_transfer_ms)
+    arrays = ("overlap_phase", "exposed_transfer_ms", "switch_gap_ms", "device_idle_ms")
+    d = {k: getattr(st, k) for k, _ in mt_stats._fields_ if k not in ("site_ms", "site_launches") + arrays}
+    for k in arrays:
+        d[k] = list(getattr(st, k))
     d["sites"] = {names[i]: {"ms": st.site_ms[i], "launches": st.site_launches[i]}
                   for i in range(min(st.n_sites, len(names)))}
     return d

@@ -76,14 +76,17 @@ def assert_close(got, ref, name, tol=TOL):
 
 
 def attn_inputs(rng, T, Hq, Hkv, hd, qk_std=1.0):
-    """qkv [T x (Hq+2Hkv)hd] as the attention kernels take it: q and k as fp16
-    (normal, std qk_std), v as bf16 (standard normal).  Returns the values
-    (float32) and the device bit patterns (int16)."""
+    """qkv [T x (Hq+2Hkv)hd] as the attention kernels take it: q and k
+    (normal, std qk_std) and v (standard normal) as fp16.  Returns the values
+    (float32), the device fp16 bit patterns (int16), and the device bf16 copy
+    of the same values that the backward's gradient products take (int16)."""
     import torch
-    from layer_streaming_amd import synth
+    from oracle.bf16 import bf16_bits
     nr = (Hq + Hkv) * hd
     qk = (qk_std * rng.standard_normal((T, nr))).astype(np.float16)
-    v = synth.bf16_exact_normal(rng, (T, Hkv * hd))
-    bits = np.concatenate([qk.view(np.uint16), (v.view(np.uint32) >> 16).astype(np.uint16)], axis=1)
-    vals = np.concatenate([qk.astype(np.float32), v], axis=1)
-    return vals, torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
+    v = rng.standard_normal((T, Hkv * hd)).astype(np.float16)
+    h = np.concatenate([qk, v], axis=1)
+    vals = h.astype(np.float32)
+    dev = torch.from_numpy(np.ascontiguousarray(h).view(np.int16)).cuda()
+    devb = torch.from_numpy(np.ascontiguousarray(bf16_bits(vals)).view(np.int16)).cuda()
+    return vals, dev, devb

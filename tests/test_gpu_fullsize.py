@@ -17,7 +17,7 @@ import pytest
 from layer_streaming_amd import synth
 from oracle import block, step as ostep
 from oracle.bf16 import bf16_bits
-from tests.gpu_util import assert_close, attn_inputs, dev_bits, dev_zeros_bits, host_f32, log, widen
+from tests.gpu_util import assert_close, attn_inputs, dev_bits, dev_zeros_bits, host_f16, host_f32, log, widen
 
 pytestmark = pytest.mark.gpu
 
@@ -80,21 +80,20 @@ def test_attention_long_context_sampled():
     log(f"attention B={B} S={S} Hq={Hq} Hkv={Hkv} hd={hd}")
     ld, nq = (Hq + 2 * Hkv) * hd, Hq * hd
     rng = np.random.default_rng(77)
-    qkv, d_qkv = attn_inputs(rng, S, Hq, Hkv, hd)
+    qkv, d_qkv, _ = attn_inputs(rng, S, Hq, Hkv, hd)
     dout = synth.bf16_exact_normal(rng, (S, nq))
     d_do = dev_bits(dout)
     d_o = dev_zeros_bits((S, nq))
     lse = torch.zeros(Hq * S, dtype=torch.float32, device="cuda")
-    dsum = torch.zeros(Hq * S, dtype=torch.float32, device="cuda")
+    work = torch.zeros(int(mt.lib.mt_k_attn_bwd_work_bytes(B, S, Hq, hd)), dtype=torch.uint8, device="cuda")
     d_dqkv = dev_zeros_bits((S, ld))
     s = torch.cuda.current_stream().cuda_stream
-    mt.check(mt.lib.mt_k_attn_fwd(d_qkv.data_ptr(), ld, d_o.data_ptr(), nq, lse.data_ptr(), B, S, Hq, Hkv, hd, s))
-    nr = (Hq + Hkv) * hd  # the bf16 copy of q, k the engine's recompute writes
-    d_qkb = dev_bits(widen(bf16_bits(qkv[:, :nr])))
+    mt.check(mt.lib.mt_k_attn_fwd(d_qkv.data_ptr(), ld, d_o.data_ptr(), nq, lse.data_ptr(), B, S, Hq, Hkv, hd,
+                                  None, s))
     mt.check(mt.lib.mt_k_attn_bwd(d_qkv.data_ptr(), ld, d_o.data_ptr(), d_do.data_ptr(), nq, lse.data_ptr(),
-                                  dsum.data_ptr(), d_dqkv.data_ptr(), ld, B, S, Hq, Hkv, hd, d_qkb.data_ptr(), nr, s))
+                                  work.data_ptr(), d_dqkv.data_ptr(), ld, B, S, Hq, Hkv, hd, None, 0, None, s))
     torch.cuda.synchronize()
-    o_g = host_f32(d_o).reshape(S, Hq, hd)
+    o_g = host_f16(d_o).reshape(S, Hq, hd)
     g_g = host_f32(d_dqkv).reshape(S, Hq + 2 * Hkv, hd)
     lse_g = lse.cpu().numpy().reshape(Hq, S)
     assert np.all(np.isfinite(o_g)) and np.all(np.isfinite(g_g)) and np.all(np.isfinite(lse_g))

@@ -213,6 +213,12 @@ def test_gemm_nt_large_tile_epilogues():
     _sync()
     ref16 = A16[:, :K].astype(np.float64) @ B16[:, :K].astype(np.float64).T
     assert_close(c16.cpu().numpy()[:, :N], ref16, "C f16 operands", tol=1e-5)
+    # fp16 operands with the bf16 residual (the O product of the attention)
+    c16r = torch.zeros((M, ldc), dtype=torch.float32, device="cuda")
+    mt.check(mt.lib.mt_k_gemm(0, 8, dA16.data_ptr(), lda, dB16.data_ptr(), ldb, c16r.data_ptr(), ldc, dR.data_ptr(),
+                              ldc, None, 0, M, N, K, s), "gemm f16 + resid")
+    _sync()
+    assert_close(c16r.cpu().numpy()[:, :N], ref16 + Rv, "C f16 operands + R", tol=1e-5)
 
 
 def test_gemm_rejects_misaligned_shapes():
@@ -238,6 +244,17 @@ def test_gemm_f16_operands(M, N, K):
     r = mt.lib.mt_k_gemm(1, 7, dA.data_ptr(), K, dB.data_ptr(), N, dC.data_ptr(), N, None, 0, None, 0,
                          M, N, K, _stream())
     assert r == mt.MT_E_INVAL
+    # epilogue 8: the same with a bf16 residual (ragged N exercises the
+    # element-wise tail of the residual read)
+    R = synth.bf16_exact_normal(RNG, (M, N))
+    dR = dev_bits(R)
+    dC8 = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+    mt.check(mt.lib.mt_k_gemm(0, 8, dA.data_ptr(), K, dB.data_ptr(), K, dC8.data_ptr(), N, dR.data_ptr(), N,
+                              None, 0, M, N, K, _stream()), "gemm f16 + resid")
+    _sync()
+    assert_close(dC8.cpu().numpy(), ref + R, "C + R", tol=1e-5)
+    assert mt.lib.mt_k_gemm(0, 8, dA.data_ptr(), K, dB.data_ptr(), K, dC8.data_ptr(), N, None, 0, None, 0,
+                            M, N, K, _stream()) == mt.MT_E_INVAL  # no residual
 
 
 # --------------------------------------------------------------- RMSNorm --
@@ -259,8 +276,9 @@ def test_rmsnorm_fwd_bwd(T, d, x_f32):
     rstd = torch.zeros(T, dtype=torch.float32, device="cuda")
     dgam, ddn, dres = dev_bits(g), dev_bits(dn), dev_bits(res)
     s = _stream()
+    ovf = torch.zeros(4, dtype=torch.int32, device="cuda")
     mt.check(mt.lib.mt_k_rmsnorm_fwd(dx_.data_ptr(), x_f32, dgam.data_ptr(), n_.data_ptr(), nh_.data_ptr(),
-                                     rstd.data_ptr(), T, d, eps, s))
+                                     rstd.data_ptr(), T, d, eps, ovf.data_ptr(), s))
     scratch = torch.zeros(int(mt.lib.mt_k_rmsnorm_bwd_scratch_elems(T, d)), dtype=torch.float32, device="cuda")
     ddx = dev_zeros_bits((T, d))
     mt.check(mt.lib.mt_k_rmsnorm_bwd(ddn.data_ptr(), dx_.data_ptr(), x_f32, dgam.data_ptr(), rstd.data_ptr(),
@@ -270,6 +288,7 @@ def test_rmsnorm_fwd_bwd(T, d, x_f32):
     n_ref, r_ref = block.rmsnorm_fwd(xd, g.astype(np.float64), eps)
     assert_close(host_f32(n_), n_ref, "n")
     assert_close(host_f16(nh_), n_ref, "n (fp16)", tol=1e-3)
+    assert ovf[0].item() == 0
     assert_close(rstd.cpu().numpy(), r_ref, "rstd", tol=1e-5)
     dx_ref, dg_ref = block.rmsnorm_bwd(dn.astype(np.float64), xd, g.astype(np.float64), r_ref)
     assert_close(host_f32(ddx), dx_ref + res, "dx")
@@ -316,9 +335,9 @@ def test_rope_long_positions():
 
 @pytest.mark.parametrize("hd,S", [(64, 100), (128, 100), (128, 131072)])
 def test_qkv_rope_cvt(hd, S):
-    """Forward RoPE on the f32 projection: q, k rotated and stored fp16 (and
-    bf16 in a second buffer), v rounded to bf16 (bit-exact against
-    round-to-nearest-even)."""
+    """Forward RoPE on the f32 projection: q, k rotated, every head stored as
+    fp16 (v bit-exact against round-to-nearest-even) and, in a second buffer,
+    as bf16 (v bit-exact)."""
     hq, hkv = (4, 2) if S < 1000 else (1, 1)
     B = 2 if S < 1000 else 1
     log(f"qkv_rope_cvt hd={hd} S={S}")
@@ -328,24 +347,100 @@ def test_qkv_rope_cvt(hd, S):
     dx = torch.from_numpy(x).cuda()
     out = dev_zeros_bits((T, ld))
     nr = (hq + hkv) * hd
-    outb = dev_zeros_bits((T, nr))
+    outb = dev_zeros_bits((T, ld))
     tab = torch.zeros(S * hd, dtype=torch.float32, device="cuda")
-    mt.check(mt.lib.mt_k_qkv_rope_cvt(dx.data_ptr(), ld, out.data_ptr(), ld, outb.data_ptr(), nr, tab.data_ptr(), T,
-                                      S, hq + hkv, hq + 2 * hkv, hd, 10000.0, _stream()))
+    ovf = torch.zeros(4, dtype=torch.int32, device="cuda")
+    mt.check(mt.lib.mt_k_qkv_rope_cvt(dx.data_ptr(), ld, out.data_ptr(), ld, outb.data_ptr(), ld, tab.data_ptr(), T,
+                                      S, hq + hkv, hq + 2 * hkv, hd, 10000.0, ovf.data_ptr(), _stream()))
     _sync()
     got_qk = host_f16(out)[:, :nr]
     rot = x[:, :nr].astype(np.float64).reshape(B, S, hq + hkv, hd)
     ref = block.rope_fwd(rot, 10000.0).reshape(T, nr)
     assert_close(got_qk, ref, "q, k (fp16)", tol=1e-3)
-    assert_close(host_f32(outb), ref, "q, k (bf16)", tol=5e-3)
     got_v = out.cpu().numpy().view(np.uint16)[:, nr:]
-    np.testing.assert_array_equal(got_v, bf16_bits(x[:, nr:]))
+    np.testing.assert_array_equal(got_v, x[:, nr:].astype(np.float16).view(np.uint16))
+    # the bf16 copy is the bf16 rounding of the fp16 values, bit for bit
+    np.testing.assert_array_equal(outb.cpu().numpy().view(np.uint16), bf16_bits(host_f16(out)))
+    assert ovf[0].item() == 0
     # without the bf16 copy: same fp16 output
     out2 = dev_zeros_bits((T, ld))
     mt.check(mt.lib.mt_k_qkv_rope_cvt(dx.data_ptr(), ld, out2.data_ptr(), ld, None, 0, tab.data_ptr(), T, S,
-                                      hq + hkv, hq + 2 * hkv, hd, 10000.0, _stream()))
+                                      hq + hkv, hq + 2 * hkv, hd, 10000.0, None, _stream()))
     _sync()
     assert torch.equal(out, out2)
+    # a bf16 copy narrower than every head is refused
+    assert mt.lib.mt_k_qkv_rope_cvt(dx.data_ptr(), ld, out2.data_ptr(), ld, outb.data_ptr(), nr, tab.data_ptr(), T,
+                                    S, hq + hkv, hq + 2 * hkv, hd, 10000.0, None, _stream()) == mt.MT_E_INVAL
+
+
+# ------------------------------------------------------ fp16 range guard --
+def _f16_sat_ref(x):
+    """The guard's definition: |x| < 65520 rounds to nearest even (numpy's
+    float16 cast), anything else saturates to +-65504 and counts; NaN stays
+    NaN and counts."""
+    x = np.asarray(x, np.float32)
+    over = ~(np.abs(x) < 65520.0)
+    y = np.where(over & ~np.isnan(x), np.copysign(np.float32(65504.0), x), x).astype(np.float16)
+    return y, int(over.sum())
+
+
+def test_fp16_range_guard_conversion():
+    """bf16 -> fp16 of the weights of the fp16 products: values near and past
+    the fp16 maximum, infinities, NaN, fp16 subnormals and values below them,
+    against the guard's definition bit for bit, with the exact count."""
+    edge = np.array([65504.0, -65504.0, 65280.0, 65536.0, -65536.0, 1e5, -3e38, np.inf, -np.inf, np.nan,
+                     2.0 ** -14, 2.0 ** -15, 3 * 2.0 ** -24, 2.0 ** -25, 2.0 ** -26, -(2.0 ** -20), 0.0, -0.0,
+                     1.0, 0.02], np.float32)
+    x = np.concatenate([edge, synth.bf16_exact_normal(RNG, (4076,), std=3e4)])
+    x = widen(bf16_bits(x))  # exactly bf16
+    ref, n_over = _f16_sat_ref(x)
+    dx = torch.from_numpy(bf16_bits(x).view(np.int16)).cuda()
+    dy = dev_zeros_bits(x.shape)
+    ovf = torch.zeros(4, dtype=torch.int32, device="cuda")
+    mt.check(mt.lib.mt_k_bf16_to_f16(dx.data_ptr(), dy.data_ptr(), x.size, ovf.data_ptr(), _stream()))
+    _sync()
+    got = dy.cpu().numpy().view(np.uint16)
+    nan = np.isnan(x)
+    assert np.array_equal(got[~nan], ref.view(np.uint16)[~nan])
+    assert np.all(np.isnan(got[nan].view(np.float16)))
+    assert ovf[0].item() == n_over and n_over > 5
+
+
+def test_fp16_range_guard_norm_and_rope():
+    """The fp16 copy of the norm output and the RoPE conversion saturate and
+    count too: a gain of 2^20 drives n past the fp16 range."""
+    T, d = 40, 256
+    x = synth.bf16_exact_normal(RNG, (T, d))
+    g = np.full(d, 2.0 ** 20, np.float32)
+    dx_, dg = dev_bits(x), dev_bits(g)
+    n_, nh_ = dev_zeros_bits((T, d)), dev_zeros_bits((T, d))
+    rstd = torch.zeros(T, dtype=torch.float32, device="cuda")
+    ovf = torch.zeros(4, dtype=torch.int32, device="cuda")
+    mt.check(mt.lib.mt_k_rmsnorm_fwd(dx_.data_ptr(), 0, dg.data_ptr(), n_.data_ptr(), nh_.data_ptr(),
+                                     rstd.data_ptr(), T, d, 1e-6, ovf.data_ptr(), _stream()))
+    _sync()
+    n_ref, _ = block.rmsnorm_fwd(x.astype(np.float64), g.astype(np.float64), 1e-6)
+    got = nh_.cpu().numpy().view(np.float16).astype(np.float64)
+    over = np.abs(n_ref) >= 65600.0  # clear of the boundary, where fp32 and fp64 may round apart
+    assert np.all(got[over] == np.copysign(65504.0, n_ref[over]))
+    assert np.all(np.isfinite(got))
+    cnt = int(np.sum(np.abs(n_ref) >= 65520.0))
+    assert abs(ovf[0].item() - cnt) <= 2 and cnt > T * d // 2
+    # RoPE conversion of an out-of-range projection
+    hd, S = 64, T
+    ld = 3 * hd
+    xp = (RNG.standard_normal((T, ld)) * 1e5).astype(np.float32)
+    dxp = torch.from_numpy(xp).cuda()
+    out = dev_zeros_bits((T, ld))
+    tab = torch.zeros(S * hd, dtype=torch.float32, device="cuda")
+    ovf.zero_()
+    mt.check(mt.lib.mt_k_qkv_rope_cvt(dxp.data_ptr(), ld, out.data_ptr(), ld, None, 0, tab.data_ptr(), T, S, 2, 3,
+                                      hd, 10000.0, ovf.data_ptr(), _stream()))
+    _sync()
+    h = out.cpu().numpy().view(np.float16)
+    assert np.all(np.isfinite(h)) and np.max(np.abs(h)) == 65504.0
+    _, cnt_v = _f16_sat_ref(xp[:, 2 * hd:])
+    assert ovf[0].item() >= cnt_v > 0
 
 
 # ---------------------------------------------------------------- SwiGLU --
@@ -373,12 +468,11 @@ ATTN_CASES = [(2, 200, 4, 2, 64), (1, 300, 7, 1, 128), (2, 128, 4, 4, 128), (1, 
 
 
 @pytest.mark.parametrize("B,S,Hq,Hkv,hd", ATTN_CASES)
-@pytest.mark.parametrize("qkb", [True, False], ids=["direct", "staged"])
-def test_attention_fwd_bwd(B, S, Hq, Hkv, hd, qkb):
-    """Forward, then backward in both forms: tiles loaded straight into LDS
-    with the bf16 copy of q and k, or staged through registers rounding the
-    fp16 q and k."""
-    _attention_case(B, S, Hq, Hkv, hd, 1.0, qkb)
+@pytest.mark.parametrize("f32_out", [False, True], ids=["bf16-dqk", "f32-dqk"])
+def test_attention_fwd_bwd(B, S, Hq, Hkv, hd, f32_out):
+    """Forward and backward (fp16 products, scaled dO) against the float64
+    oracle; dQ and dK written as bf16 into the qkv layout, or as fp32."""
+    _attention_case(B, S, Hq, Hkv, hd, 1.0, f32_out)
 
 
 def test_attention_sharp_logits():
@@ -387,39 +481,76 @@ def test_attention_sharp_logits():
     _attention_case(1, 700, 8, 2, 128, 2.0, True)
 
 
-def _attention_case(B, S, Hq, Hkv, hd, qk_std, with_qkb):
-    log(f"attention B={B} S={S} Hq={Hq} Hkv={Hkv} hd={hd} qk_std={qk_std} qkb={with_qkb}")
+@pytest.mark.parametrize("do_std", [1e-9, 1e-4, 3e2])
+def test_attention_bwd_scale_follows_gradient_size(do_std):
+    """The backward's power-of-two scale follows max|dO|: gradients many
+    orders of magnitude below fp16's normal range (the loss scale of a long
+    sequence) and well above 1 give the same relative accuracy."""
+    _attention_case(2, 130, 4, 2, 128, 1.0, True, do_std=do_std)
+
+
+def _attention_case(B, S, Hq, Hkv, hd, qk_std, f32_out, do_std=1.0):
+    log(f"attention B={B} S={S} Hq={Hq} Hkv={Hkv} hd={hd} qk_std={qk_std} f32_out={f32_out} do_std={do_std}")
     T = B * S
     ld = (Hq + 2 * Hkv) * hd
-    nq = Hq * hd
-    qkv, d_qkv = attn_inputs(RNG, T, Hq, Hkv, hd, qk_std)
-    dout = synth.bf16_exact_normal(RNG, (T, nq))
+    nq, nr = Hq * hd, (Hq + Hkv) * hd
+    qkv, d_qkv, _ = attn_inputs(RNG, T, Hq, Hkv, hd, qk_std)
+    dout = synth.bf16_exact_normal(RNG, (T, nq), std=do_std)
     d_do = dev_bits(dout)
     d_o = dev_zeros_bits((T, nq))
     lse = torch.zeros(B * Hq * S, dtype=torch.float32, device="cuda")
-    dsum = torch.zeros(B * Hq * S, dtype=torch.float32, device="cuda")
+    work = torch.zeros(int(mt.lib.mt_k_attn_bwd_work_bytes(B, S, Hq, hd)), dtype=torch.uint8, device="cuda")
     d_dqkv = dev_zeros_bits((T, ld))
+    dqk32 = torch.zeros((T, nr), dtype=torch.float32, device="cuda") if f32_out else None
+    ovf = torch.zeros(4, dtype=torch.int32, device="cuda")
     s = _stream()
-    mt.check(mt.lib.mt_k_attn_fwd(d_qkv.data_ptr(), ld, d_o.data_ptr(), nq, lse.data_ptr(), B, S, Hq, Hkv, hd, s))
-    nr = (Hq + Hkv) * hd
-    d_qkb = dev_bits(widen(bf16_bits(qkv[:, :nr]))) if with_qkb else None
+    mt.check(mt.lib.mt_k_attn_fwd(d_qkv.data_ptr(), ld, d_o.data_ptr(), nq, lse.data_ptr(), B, S, Hq, Hkv, hd,
+                                  ovf.data_ptr(), s))
     mt.check(mt.lib.mt_k_attn_bwd(d_qkv.data_ptr(), ld, d_o.data_ptr(), d_do.data_ptr(), nq, lse.data_ptr(),
-                                  dsum.data_ptr(), d_dqkv.data_ptr(), ld, B, S, Hq, Hkv, hd,
-                                  d_qkb.data_ptr() if with_qkb else None, nr if with_qkb else 0, s))
+                                  work.data_ptr(), d_dqkv.data_ptr(), ld, B, S, Hq, Hkv, hd,
+                                  dqk32.data_ptr() if f32_out else None, nr if f32_out else 0, ovf.data_ptr(), s))
     _sync()
+    assert ovf[0].item() == 0
     x = qkv.astype(np.float64).reshape(B, S, Hq + 2 * Hkv, hd)
     q, k, v = x[:, :, :Hq], x[:, :, Hq:Hq + Hkv], x[:, :, Hq + Hkv:]
     o_ref = block.attention_fwd(q, k, v)
-    o_gpu = host_f32(d_o)
-    assert_close(o_gpu, o_ref.reshape(T, nq), "o")
+    o_gpu = host_f16(d_o)
+    assert_close(o_gpu, o_ref.reshape(T, nq), "o (fp16)", tol=2e-3)
     lse_ref = block.attention_lse(q, k)   # [B, Hq, S]
     assert_close(lse.cpu().numpy().reshape(B, Hq, S), lse_ref, "lse", tol=1e-4)
-    # Backward from the GPU's own (bf16) O, as the kernel sees it.
     dq, dk, dv = block.attention_bwd(dout.astype(np.float64).reshape(B, S, Hq, hd), q, k, v)
     g = host_f32(d_dqkv).reshape(B, S, Hq + 2 * Hkv, hd)
-    assert_close(g[:, :, :Hq], dq, "dq")
-    assert_close(g[:, :, Hq:Hq + Hkv], dk, "dk")
-    assert_close(g[:, :, Hq + Hkv:], dv, "dv")
+    gqk = dqk32.cpu().numpy().reshape(B, S, Hq + Hkv, hd).astype(np.float64) if f32_out else g
+    if S == 1:
+        # one key: P = 1 and D = dP, so dS = 0 and dQ, dK vanish up to the
+        # fp32 summation order of dP (MFMA) against D (a loop)
+        bound = 1e-5 * do_std
+        assert np.max(np.abs(gqk[:, :, :Hq + Hkv])) <= bound, np.max(np.abs(gqk[:, :, :Hq + Hkv]))
+    assert_close(gqk[:, :, :Hq], dq, "dq", tol=5e-3)
+    assert_close(gqk[:, :, Hq:Hq + Hkv], dk, "dk", tol=5e-3)
+    assert_close(g[:, :, Hq + Hkv:], dv, "dv", tol=5e-3)
+    if f32_out:  # dQ, dK only in the fp32 buffer
+        assert np.all(g[:, :, :Hq + Hkv] == 0)
+
+
+@pytest.mark.parametrize("hd", [64, 128])
+def test_rope_f32_to_bf16_backward(hd):
+    """The rotation by -theta of fp32 gradients, rounded to bf16 once."""
+    B, S, h = 2, 100, 3
+    log(f"rope f32 -> bf16 hd={hd}")
+    T, ld = B * S, h * hd + 8
+    x = RNG.standard_normal((T, ld)).astype(np.float32)
+    dx = torch.from_numpy(x).cuda()
+    out = dev_zeros_bits((T, h * hd))
+    tab = torch.zeros(S * hd, dtype=torch.float32, device="cuda")
+    mt.check(mt.lib.mt_k_rope_f32_bf16(dx.data_ptr(), ld, out.data_ptr(), h * hd, tab.data_ptr(), T, S, h, hd,
+                                       10000.0, -1, _stream()))
+    _sync()
+    ref = block.rope_bwd(x[:, :h * hd].astype(np.float64).reshape(B, S, h, hd), 10000.0).reshape(T, h * hd)
+    got = host_f32(out)
+    assert_close(got, ref, "rope bwd (bf16 out)", tol=3e-3)
+    # one rounding: every element within half a bf16 ulp of the fp32 rotation (plus fp32 slack)
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6)
 
 
 # --------------------------------------------------------- Cross-entropy --
@@ -483,9 +614,24 @@ def test_transpose16_bit_exact(R, C, pad_s, pad_d):
     src = rng.integers(0, 1 << 16, size=(R, lds), dtype=np.uint16)
     dsrc = torch.from_numpy(src.view(np.int16)).cuda()
     ddst = torch.full((C, ldd), 0x1234, dtype=torch.int16, device="cuda")
-    mt.check(mt.lib.mt_k_transpose16(dsrc.data_ptr(), lds, ddst.data_ptr(), ldd, R, C, _stream()))
+    mt.check(mt.lib.mt_k_transpose16(dsrc.data_ptr(), lds, ddst.data_ptr(), ldd, R, C, 0, _stream()))
     _sync()
     got = ddst.cpu().numpy().view(np.uint16)
     assert np.array_equal(got[:, :R], src[:, :C].T)
     assert np.all(got[:, R:] == 0x1234)
-    assert mt.lib.mt_k_transpose16(dsrc.data_ptr(), lds, ddst.data_ptr(), R - 1, R, C, _stream()) == mt.MT_E_INVAL
+    assert mt.lib.mt_k_transpose16(dsrc.data_ptr(), lds, ddst.data_ptr(), R - 1, R, C, 0, _stream()) == mt.MT_E_INVAL
+
+
+@pytest.mark.parametrize("R,C", [(130, 77), (1000, 520)])
+def test_transpose16_fp16_to_bf16(R, C):
+    """The transpose that hands the fp16 attention output to the bf16 dW
+    product: each element rounded to bf16 (RNE), bit for bit."""
+    log(f"transpose16 fp16->bf16 {R}x{C}")
+    rng = np.random.default_rng(R + C)
+    src = (rng.standard_normal((R, C)) * 10.0 ** rng.uniform(-6, 4, (R, C))).astype(np.float16)
+    dsrc = torch.from_numpy(src.view(np.int16)).cuda()
+    ddst = dev_zeros_bits((C, R))
+    mt.check(mt.lib.mt_k_transpose16(dsrc.data_ptr(), C, ddst.data_ptr(), R, R, C, 1, _stream()))
+    _sync()
+    got = ddst.cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, bf16_bits(src.astype(np.float32)).T)

@@ -92,31 +92,30 @@ def test_layer_fwd_bwd_parity(kw, B, S):
 
 
 # ------------------------------------------------------------ full step --
-# Gradients are compared per streamed unit (a layer's, the head's and the
+# Gradients are compared per tensor (every gradient of every unit, the input
+# embedding's included) and per streamed unit (a layer's, the head's and the
 # embedding's whole BF16 gradient tile, the granularity gradients leave the
-# GPU in) on every workload, and per tensor on all but the GQA B3 x S40
-# shape, all at normwise relative error <= 1e-2.  There the attention query
-# projection's gradient of layer 1 sits at the floor of the remaining bf16
-# roundings (1.000e-2 measured), so that shape is bounded per unit and its
-# per-tensor errors are logged.
-def _cmp_units(ctx, kw, g_ref, per_tensor):
+# GPU in), all at normwise relative error <= 1e-2.
+def _cmp_units(ctx, kw, g_ref):
     L = kw["n_layers"]
     units = [(i, ostep.LAYER_TENSORS, g_ref["layers"][i], f"L{i}") for i in range(L)]
     units += [(L, ostep.HEAD_TENSORS, g_ref["head"], "head"), (L + 1, ("e_in",), {"e_in": g_ref["e_in"]}, "emb")]
+    worst = (0.0, "")
     for u, names, ref, tag in units:
         got_all, ref_all = [], []
         for j, n in enumerate(names):
             got = widen(ctx.get_tensor(u, j, mt.MT_G))
-            # per tensor: asserted where per_tensor, else reported
-            assert_close(got, ref[n], f"{tag}.d{n}", tol=TOL if per_tensor else np.inf)
+            e = assert_close(got, ref[n], f"{tag}.d{n}")
+            worst = max(worst, (e, f"{tag}.d{n}"))
             got_all.append(got.reshape(-1))
             ref_all.append(np.asarray(ref[n]).reshape(-1))
         assert_close(np.concatenate(got_all), np.concatenate(ref_all), f"{tag} gradient tile")
+    log(f"  worst gradient tensor: {worst[1]} {worst[0]:.3e}")
+    return worst[0]
 
 
-@pytest.mark.parametrize("kw,B,S,per_tensor", [(CFG1, 2, 128, True), (GQA, 3, 40, False),
-                                               (HD128, 2, 100, True), (HD128, 1, 1, True)])
-def test_train_step_parity(kw, B, S, per_tensor):
+@pytest.mark.parametrize("kw,B,S", [(CFG1, 2, 128), (GQA, 3, 40), (HD128, 2, 100), (HD128, 1, 1)])
+def test_train_step_parity(kw, B, S):
     log(f"train step {kw} B={B} S={S}")
     ctx = make_ctx(kw, B, S)
     sh = oracle_shape(kw)
@@ -127,7 +126,7 @@ def test_train_step_parity(kw, B, S, per_tensor):
     log(f"  loss gpu {loss:.6f}  step {st.step_ms:.1f} ms")
     loss_ref, g_ref = ostep.grads_monolithic(params, tokens, labels, sh)
     assert abs(loss - loss_ref) / abs(loss_ref) <= 1e-2, (loss, loss_ref)
-    _cmp_units(ctx, kw, g_ref, per_tensor)
+    _cmp_units(ctx, kw, g_ref)
     # The host Adam consumed exactly the gradients the store now holds.
     for (u, j), m0 in masters0:
         g = widen(ctx.get_tensor(u, j, mt.MT_G))
@@ -156,8 +155,98 @@ def test_multi_chunk_head_parity():
     assert abs(loss - loss_ref) / abs(loss_ref) <= 1e-2
     L = kw["n_layers"]
     assert_close(widen(ctx.get_tensor(L, 1, mt.MT_G)), g_ref["head"]["e_out"], "head.de_out")
-    _cmp_units(ctx, kw, g_ref, per_tensor=True)
+    _cmp_units(ctx, kw, g_ref)
     ctx.close()
+
+
+# ------------------------------------------- the benchmarked option set --
+# The options the benchmark runs with: cross-step pipelining, the weight
+# regions in one page-locked block, the LM head in layer-sized E_out chunks,
+# 16 gradient slabs, per-kernel timing, every host thread.  Three layers and
+# a vocabulary of 8192 give three head chunks; three steps with distinct
+# tokens run the split update of the input embedding twice.
+BENCH_OPTS = dict(cross_step=1, pin_weights=1, head_vocab_chunk=-1, n_grad_slabs=16, profile_kernels=1,
+                  host_threads=0)
+BENCHLIKE = dict(n_layers=3, d_model=256, n_heads=4, n_kv_heads=2, head_dim=64, ffn_dim=688, vocab=8192)
+
+
+def _oracle_store(ctx, kw):
+    """The context's whole state in the oracle's store layout (float32 W
+    values, master, m, v per tensor)."""
+    L = kw["n_layers"]
+
+    def unit(u, names):
+        return {n: {"w": widen(ctx.get_tensor(u, j, mt.MT_W)), "master": ctx.get_tensor(u, j, mt.MT_MASTER).copy(),
+                    "m": ctx.get_tensor(u, j, mt.MT_M).copy(), "v": ctx.get_tensor(u, j, mt.MT_V).copy()}
+                for j, n in enumerate(names)}
+    return {"layers": [unit(i, ostep.LAYER_TENSORS) for i in range(L)], "head": unit(L, ostep.HEAD_TENSORS),
+            "e_in": unit(L + 1, ("e_in",))}
+
+
+def _units(kw):
+    L = kw["n_layers"]
+    return ([(i, ostep.LAYER_TENSORS, lambda t, i=i: t["layers"][i], f"L{i}") for i in range(L)] +
+            [(L, ostep.HEAD_TENSORS, lambda t: t["head"], "head"), (L + 1, ("e_in",), lambda t: t["e_in"], "emb")])
+
+
+def test_bench_option_set_three_steps_against_oracle():
+    """Three steps with the benchmark's options, nothing read between them,
+    against three steps of the oracle's streamed training (its gradients
+    rounded to BF16, its Adam at t = 1, 2, 3) from the same initial state:
+    the loss of every step, the last step's gradients, and the Adam moments
+    m and sqrt(v) (sqrt(v) has the gradient's units) per tensor within 1e-2."""
+    kw, B, S = BENCHLIKE, 2, 64
+    log(f"bench option set, 3 steps, vs the oracle's 3-step training {kw}")
+    ctx = make_ctx(kw, B, S, **BENCH_OPTS)
+    store = _oracle_store(ctx, kw)
+    batches = [synth.tokens_labels(700 + k, B, S, kw["vocab"]) for k in range(3)]
+    losses = [ctx.train_step(t, lb)[0] for t, lb in batches]
+    ctx.sync()
+    assert ctx.step_count() == 3
+    sh = oracle_shape(kw)
+    for k, (t, lb) in enumerate(batches):
+        loss_ref, g_ref = ostep.train_step(store, t, lb, sh, k + 1)
+        log(f"  step {k + 1}: loss gpu {losses[k]:.6f} oracle {loss_ref:.6f}")
+        assert abs(losses[k] - loss_ref) <= 1e-2 * abs(loss_ref)
+    worst = 0.0
+    for u, names, pick, tag in _units(kw):
+        for j, n in enumerate(names):
+            ref = pick(store)[n]
+            worst = max(worst, assert_close(widen(ctx.get_tensor(u, j, mt.MT_G)), pick(g_ref)[n], f"{tag}.d{n}"))
+            assert_close(ctx.get_tensor(u, j, mt.MT_M), ref["m"], f"{tag}.m({n})")
+            assert_close(np.sqrt(ctx.get_tensor(u, j, mt.MT_V).astype(np.float64)),
+                         np.sqrt(ref["v"].astype(np.float64)), f"{tag}.sqrt_v({n})")
+    log(f"  worst step-3 gradient tensor {worst:.3e}")
+    ctx.close()
+
+
+def _run_steps(kw, B, S, n, **opts):
+    ctx = make_ctx(kw, B, S, **opts)
+    losses = []
+    for k in range(n):
+        tokens, labels = synth.tokens_labels(700 + k, B, S, kw["vocab"])
+        losses.append(ctx.train_step(tokens, labels)[0])
+    state = [(key, which, a) for which in (mt.MT_W, mt.MT_G, mt.MT_MASTER, mt.MT_M, mt.MT_V)
+             for key, a in read_all(ctx, kw, which)]
+    ctx.close()
+    return losses, state
+
+
+@pytest.mark.parametrize("opts", [BENCH_OPTS, dict(BENCH_OPTS, pin_weights=0, n_grad_slabs=12)],
+                         ids=["bench", "pages-pinned-footprint"])
+def test_bench_option_set_bit_identical_to_synchronous_path(opts):
+    """The benchmark's option set (and the pages' pinned footprint: two
+    staging buffers and 12 slabs) against the plain synchronous streamed
+    path with the same chunked head, over three steps: losses and the whole
+    store (W, G, master, m, v) bit for bit."""
+    kw, B, S = BENCHLIKE, 2, 64
+    log(f"bench option set vs synchronous path: {opts}")
+    base_losses, base_state = _run_steps(kw, B, S, 3, head_vocab_chunk=-1)
+    losses, state = _run_steps(kw, B, S, 3, **opts)
+    assert [np.float32(x).tobytes() for x in losses] == [np.float32(x).tobytes() for x in base_losses]
+    for (k1, w1, a1), (k2, w2, a2) in zip(base_state, state):
+        assert k1 == k2 and w1 == w2
+        assert np.array_equal(a1.view(np.uint8), a2.view(np.uint8)), (k1, w1)
 
 
 # ------------------------------------------------------- bit identity ----
@@ -221,6 +310,23 @@ def test_checkpoint_interval_bit_identical(deep_baseline_run, opts):
         assert np.array_equal(a1.view(np.uint8), a2.view(np.uint8)), (k1, w1)
 
 
+@pytest.mark.parametrize("k", [2, 3])
+def test_checkpoint_interval_step_parity(k):
+    """Block-wise recomputation against the oracle: 5 layers in blocks of k
+    (the block's first input kept, the others rebuilt in the backward), the
+    loss and every gradient tensor within 1e-2 of the plain definition."""
+    kw, B, S = DEEP, 2, 64
+    log(f"checkpoint interval {k} vs the oracle")
+    ctx = make_ctx(kw, B, S, ckpt_interval=k)
+    tokens, labels = synth.tokens_labels(23, B, S, kw["vocab"])
+    params = read_params(ctx, kw)
+    loss, _ = ctx.train_step(tokens, labels)
+    loss_ref, g_ref = ostep.grads_monolithic(params, tokens, labels, oracle_shape(kw))
+    assert abs(loss - loss_ref) / abs(loss_ref) <= 1e-2, (loss, loss_ref)
+    _cmp_units(ctx, kw, g_ref)
+    ctx.close()
+
+
 # ------------------------------------------- vocabulary-chunked head ----
 BIGV = dict(n_layers=2, d_model=256, n_heads=4, n_kv_heads=2, head_dim=64, ffn_dim=688, vocab=8192)
 
@@ -242,7 +348,7 @@ def test_vocab_chunked_head_step_parity(kw, B, S, opts):
     loss, _ = ctx.train_step(tokens, labels)
     loss_ref, g_ref = ostep.grads_monolithic(params, tokens, labels, oracle_shape(kw))
     assert abs(loss - loss_ref) / abs(loss_ref) <= 1e-2, (loss, loss_ref)
-    _cmp_units(ctx, kw, g_ref, per_tensor=True)
+    _cmp_units(ctx, kw, g_ref)
     L = kw["n_layers"]
     for (u, j), m0 in masters0:
         if u != L:
@@ -320,7 +426,7 @@ def test_accumulated_step_parity():
     log(f"  loss gpu {loss:.6f}  step {st.step_ms:.1f} ms")
     loss_ref, g_ref = ostep.grads_accumulated(params, tokens, labels, oracle_shape(kw))
     assert abs(loss - loss_ref) / abs(loss_ref) <= 1e-2, (loss, loss_ref)
-    _cmp_units(ctx, kw, g_ref, per_tensor=True)
+    _cmp_units(ctx, kw, g_ref)
     for (u, j), m0 in masters0:
         g = widen(ctx.get_tensor(u, j, mt.MT_G))
         z = np.zeros_like(m0)
