@@ -53,6 +53,23 @@ int64_t mt_k_rmsnorm_bwd_scratch_elems(int32_t T, int32_t d);
 int mt_k_rmsnorm_bwd(const void* dn, const void* x, int32_t x_f32, const void* gamma, const void* rstd,
                      const void* resid, void* dx, void* dgamma, void* scratch, int32_t T, int32_t d, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * mt_k_rmsnorm_bwd with its gain-gradient partials in a library-owned static
+ * device buffer of MT_NOALLOC_SCRATCH_BYTES (16 MiB on every GPU the library
+ * runs on, held until the process ends) instead of a caller scratch buffer.
+ * Same arguments otherwise, same results bit for bit.  The call allocates
+ * nothing; the buffer's device address is looked up once per device, on
+ * the first call with that device current.  MT_E_INVAL, before any device
+ * work, when the partials, mt_k_rmsnorm_bwd_scratch_elems(T, d) floats (at
+ * most 512 * d), exceed the buffer's 4194304: every width the kernel
+ * supports (d <= 8192) fits, for any T.  Every partial is written before it
+ * is read, so the buffer needs no clearing.  Every call on one GPU shares the buffer: calls that overlap on
+ * one GPU (concurrent streams or threads) race. */
+#define MT_NOALLOC_SCRATCH_BYTES (16u << 20)
+int mt_k_rmsnorm_bwd_noalloc(const void* dn, const void* x, int32_t x_f32, const void* gamma, const void* rstd,
+                             const void* resid, void* dx, void* dgamma, int32_t T, int32_t d, void* stream);
+
 /* Rotary embedding, rotate-half pairs (e, e+hd/2), angle s*base^(-2e/hd)
  * with s = t % S, in place on the first n_rot_heads heads of each row of
  * qkv [T x ld]; dir +1 forward, -1 backward.  table: device scratch of

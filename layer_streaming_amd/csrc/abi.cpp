@@ -92,6 +92,17 @@ int mt_k_rmsnorm_bwd(const void* dn, const void* x, int32_t x_f32, const void* g
                "rmsnorm_bwd");
 }
 
+int mt_k_rmsnorm_bwd_noalloc(const void* dn, const void* x, int32_t x_f32, const void* gamma, const void* rstd,
+                             const void* resid, void* dx, void* dgamma, int32_t T, int32_t d, void* stream) {
+    if (T > 0 && d > 0 && mt::rmsnorm_bwd_partial_elems(T, d) > mt::RMSNORM_NOALLOC_FLOATS)
+        MT_FAIL(MT_E_INVAL, "rmsnorm_bwd_noalloc: T = %d x d = %d needs %lld partial floats, more than the %lld of "
+                "the static buffer", T, d, (long long)mt::rmsnorm_bwd_partial_elems(T, d),
+                (long long)mt::RMSNORM_NOALLOC_FLOATS);
+    return kst(mt::rmsnorm_bwd_noalloc(U16(dn), x, x_f32 != 0, U16(gamma), F32(rstd), resid ? U16(resid) : nullptr,
+                                       U16(dx), U16(dgamma), T, d, S_(stream)),
+               "rmsnorm_bwd_noalloc");
+}
+
 int mt_k_rope(void* qkv, int64_t ld, void* table, int32_t T, int32_t S, int32_t n_rot_heads, int32_t hd,
               float base, int32_t dir, void* stream) {
     hipError_t e = mt::rope_table(static_cast<float2*>(table), S, hd, base, S_(stream));

@@ -3,6 +3,8 @@
 // cross-entropy, and small conversions.  All read and write bf16 in 16-byte
 // vectors (8 elements per lane), keep statistics in fp32 and reduce in a
 // fixed order, so every result is bit-reproducible run to run.
+#include <mutex>
+
 #include "kcommon.h"
 #include "kernels.h"
 
@@ -741,6 +743,45 @@ hipError_t rmsnorm_bwd(const uint16_t* dn, const void* x, bool x_f32, const uint
     if (e != hipSuccess) return e;
     dgamma_reduce_k<<<(d + 63) / 64, 1024, 0, s>>>(partial, int(nb), d, dgamma);
     return hipGetLastError();
+}
+
+// ------------------------------------------ allocation-free entry ----
+// The gain-gradient partials of rmsnorm_bwd in a file-scope device array:
+// one copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the
+// symbol): the device address comes from hipGetSymbolAddress, looked up once
+// per device with that device current.
+static __device__ __align__(256) float scratch[RMSNORM_NOALLOC_FLOATS];
+
+namespace {
+std::mutex noalloc_mu;
+float* noalloc_ptr[64] = {};
+}  // namespace
+
+hipError_t rmsnorm_bwd_noalloc(const uint16_t* dn, const void* x, bool x_f32, const uint16_t* gamma,
+                               const float* rstd, const uint16_t* resid, uint16_t* dx, uint16_t* dgamma, int T, int d,
+                               hipStream_t s) {
+    if (T <= 0 || d <= 0 || (d & 7) || d > 8192) return hipErrorInvalidValue;
+    if (rmsnorm_bwd_partial_elems(T, d) > RMSNORM_NOALLOC_FLOATS) return hipErrorInvalidValue;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    float* ptr;
+    {
+        std::lock_guard<std::mutex> lk(noalloc_mu);
+        if (!noalloc_ptr[dev]) {
+            void* p = nullptr;
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            noalloc_ptr[dev] = static_cast<float*>(p);
+        }
+        ptr = noalloc_ptr[dev];
+    }
+    // Every partial row is written by rmsnorm_bwd_k before dgamma_reduce_k
+    // reads it, so the buffer needs no clearing between calls.
+    return rmsnorm_bwd(dn, x, x_f32, gamma, rstd, resid, dx, dgamma, ptr, T, d, s);
 }
 
 hipError_t rope_table(float2* tab, int S, int hd, float base, hipStream_t s) {

@@ -54,6 +54,14 @@ hipError_t rmsnorm_bwd(const uint16_t* dn, const void* x, bool x_f32, const uint
                        const float* rstd, const uint16_t* resid, uint16_t* dx, uint16_t* dgamma,
                        float* partial, int T, int d, hipStream_t s);
 int64_t rmsnorm_bwd_partial_elems(int T, int d);
+// rmsnorm_bwd with its partials in a static per-GPU device array of
+// RMSNORM_NOALLOC_FLOATS floats instead of a caller buffer (no allocation);
+// hipErrorInvalidValue when rmsnorm_bwd_partial_elems(T, d) exceeds it.
+// Calls that overlap on one GPU race on the array.
+constexpr int64_t RMSNORM_NOALLOC_FLOATS = int64_t(4) << 20;  // 16 MiB
+hipError_t rmsnorm_bwd_noalloc(const uint16_t* dn, const void* x, bool x_f32, const uint16_t* gamma,
+                               const float* rstd, const uint16_t* resid, uint16_t* dx, uint16_t* dgamma, int T, int d,
+                               hipStream_t s);
 
 // ---------------------------------------------------------------- RoPE ----
 // Table of cos/sin [S x hd/2] (float2), angle s*base^(-2e/hd) in double.

@@ -94,6 +94,7 @@ _SIGS = {
     "mt_k_rmsnorm_fwd": (C.c_int, [_P, C.c_int32, _P, _P, _P, _P, C.c_int32, C.c_int32, C.c_float, _P, _P]),
     "mt_k_rmsnorm_bwd_scratch_elems": (C.c_int64, [C.c_int32, C.c_int32]),
     "mt_k_rmsnorm_bwd": (C.c_int, [_P, _P, C.c_int32, _P, _P, _P, _P, _P, _P, C.c_int32, C.c_int32, _P]),
+    "mt_k_rmsnorm_bwd_noalloc": (C.c_int, [_P, _P, C.c_int32, _P, _P, _P, _P, _P, C.c_int32, C.c_int32, _P]),
     "mt_k_rope": (C.c_int, [_P, C.c_int64, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_float, C.c_int32,
                             _P]),
     "mt_k_swiglu_fwd": (C.c_int, [_P, _P, C.c_int32, C.c_int32, _P]),
