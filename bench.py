@@ -67,8 +67,8 @@ SHAPES["70b_x4"] = SHAPES["70b"]
 # profiles/gemm_gateup_traffic_7b.md.  Valid only for the kernel sources it was
 # taken on (sha256 over the files in order): reported as null once they change.
 TRAFFIC = {"sources": ["layer_streaming_amd/csrc/gemm_nt.hip", "layer_streaming_amd/csrc/kcommon.h"],
-           "sha256": "1bef37c1b74e5bcd98f513ee2fa5ed6d9676e909c36ba6313ae60c4bbcb5648f",
-           "fetch_bytes": 3317871570, "write_bytes": 620756992}
+           "sha256": "7335c133c6005fe4a6986c7c795709213a6682bf8d7fdf0a82d06c4a40f09c81",
+           "fetch_bytes": 3317900506, "write_bytes": 620756992}
 
 
 def traffic_bytes(config):
@@ -223,35 +223,36 @@ def traffic_probe(torch, mt, cfg):
     log("traffic probe done")
 
 
-def attention_probe(torch, mt, cfg, S):
-    """The attention kernels alone at one sequence of length S with the
+def attention_probe(torch, mt, cfg, S, B=1):
+    """The attention kernels alone at B sequences of length S with the
     workload's heads: forward and backward three times each on seeded
     synthetic q, k, v (fp16) and dO (bf16); HIP-event times and TFLOP/s
-    (causal: 4 Hq hd S(S+1)/2 for the
+    (causal: 4 B Hq hd S(S+1)/2 for the
     forward, 2.5 times that for the backward)."""
     Hq, Hkv, hd = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]
     ld, nq = (Hq + 2 * Hkv) * hd, Hq * hd
+    T = B * S
     g = torch.Generator(device="cpu").manual_seed(0)
-    qkv = torch.randn(S, ld, generator=g).to(torch.float16).cuda().view(torch.int16)
-    do = torch.randn(S, nq, generator=g).to(torch.bfloat16).cuda().view(torch.int16)
-    o = torch.zeros(S, nq, dtype=torch.int16, device="cuda")
-    lse = torch.zeros(Hq * S, device="cuda")
-    work = torch.zeros(int(mt.lib.mt_k_attn_bwd_work_bytes(1, S, Hq, hd)), dtype=torch.uint8, device="cuda")
-    dqkv = torch.zeros(S, ld, dtype=torch.int16, device="cuda")
-    dqk32 = torch.zeros(S, ld, dtype=torch.float32, device="cuda")
+    qkv = torch.randn(T, ld, generator=g).to(torch.float16).cuda().view(torch.int16)
+    do = torch.randn(T, nq, generator=g).to(torch.bfloat16).cuda().view(torch.int16)
+    o = torch.zeros(T, nq, dtype=torch.int16, device="cuda")
+    lse = torch.zeros(Hq * T, device="cuda")
+    work = torch.zeros(int(mt.lib.mt_k_attn_bwd_work_bytes(B, S, Hq, Hkv, hd)), dtype=torch.uint8, device="cuda")
+    dqkv = torch.zeros(T, ld, dtype=torch.int16, device="cuda")
+    dqk32 = torch.zeros(T, ld, dtype=torch.float32, device="cuda")
     st = torch.cuda.current_stream()
     s = st.cuda_stream
 
     def fwd():
-        mt.check(mt.lib.mt_k_attn_fwd(qkv.data_ptr(), ld, o.data_ptr(), nq, lse.data_ptr(), 1, S, Hq, Hkv, hd, None, s),
+        mt.check(mt.lib.mt_k_attn_fwd(qkv.data_ptr(), ld, o.data_ptr(), nq, lse.data_ptr(), B, S, Hq, Hkv, hd, None, s),
                  "attn_fwd")
 
     def bwd():  # as the step runs it: dQ, dK in fp32
         mt.check(mt.lib.mt_k_attn_bwd(qkv.data_ptr(), ld, o.data_ptr(), do.data_ptr(), nq, lse.data_ptr(),
-                                      work.data_ptr(), dqkv.data_ptr(), ld, 1, S, Hq, Hkv, hd, dqk32.data_ptr(), ld,
-                                      None, s),
+                                      work.data_ptr(), dqkv.data_ptr(), ld, B, S, Hq, Hkv, hd, dqk32.data_ptr(), ld,
+                                      0, None, s),
                  "attn_bwd")
-    fl = 4.0 * Hq * hd * S * (S + 1) / 2
+    fl = 4.0 * B * Hq * hd * S * (S + 1) / 2
     out = {}
     for name, fn, f in (("fwd", fwd, fl), ("bwd", bwd, 2.5 * fl)):
         fn()
@@ -264,8 +265,8 @@ def attention_probe(torch, mt, cfg, S):
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / 3
         out[name] = {"ms": round(ms, 3), "tflops": round(f / (ms / 1e3) / 1e12, 1)}
-        log(f"attention {name} S={S}: {ms:.2f} ms, {f / ms / 1e9:.0f} TFLOP/s")
-    print(json.dumps({"attention_probe": {"S": S, "heads": [Hq, Hkv, hd], **out}}), flush=True)
+        log(f"attention {name} B={B} S={S}: {ms:.2f} ms, {f / ms / 1e9:.0f} TFLOP/s")
+    print(json.dumps({"attention_probe": {"B": B, "S": S, "heads": [Hq, Hkv, hd], **out}}), flush=True)
 
 
 def ablations(torch, mt, shape, cfg, args, tokens, labels, base_value):
@@ -475,7 +476,18 @@ def pcie_block(stats):
             "exposed_transfer_ms_by_phase": {ph: round(mean("exposed_transfer_ms", i), 1)
                                              for i, ph in enumerate(phases)},
             "switch_gap_ms_median_by_phase": {ph: round(mean("switch_gap_ms", i), 3) for i, ph in enumerate(phases)},
-            "device_idle_ms_by_phase": {ph: round(mean("device_idle_ms", i), 1) for i, ph in enumerate(phases)}}
+            "device_idle_ms_by_phase": {ph: round(mean("device_idle_ms", i), 1) for i, ph in enumerate(phases)},
+            # link idle before each weight-stream copy by what it waited for: its slot (the earliest any
+            # schedule over the same slots could issue it), the host (the weights' update or pack), other
+            # copies (checkpoint restores, labels, inputs)
+            "h2d_link_idle_ms_by_phase": {ph: {c: round(mean("h2d_idle_ms", 3 * i + j), 1)
+                                               for j, c in enumerate(("slot", "host", "other"))}
+                                          for i, ph in enumerate(phases)},
+            # visits whose inputs were ready before the previous visit ended: start minus that end
+            "switch_latency_ready_visits_ms": {"median": round(mean("ready_switch_ms", 0), 4),
+                                               "p90": round(mean("ready_switch_ms", 1), 4),
+                                               "ready_visits": round(mean("ready_switches"), 1),
+                                               "visits": round(mean("switches"), 1)}}
 
 
 def main():
@@ -517,7 +529,8 @@ def main():
     ap.add_argument("--own-streams", action="store_true",
                     help="let the library create its three streams instead of passing torch's")
     ap.add_argument("--attn-probe", type=int, default=0, metavar="S",
-                    help="only time the attention kernels at one sequence of length S with the workload's heads")
+                    help="only time the attention kernels at sequences of length S with the workload's heads")
+    ap.add_argument("--attn-batch", type=int, default=1, metavar="B", help="sequences in the attention probe")
     ap.add_argument("--micro", type=int, default=1,
                     help="micro-batches of batch x seq per optimizer step (gradient accumulation on the host)")
     ap.add_argument("--cross-step", type=int, default=1,
@@ -541,7 +554,7 @@ def main():
         traffic_probe(torch, mt, cfg)
         return
     if args.attn_probe:
-        attention_probe(torch, mt, cfg, args.attn_probe)
+        attention_probe(torch, mt, cfg, args.attn_probe, args.attn_batch)
         return
     torch.cuda.init()
     opt_kw = dict(profile_kernels=0 if args.no_profile else 1, host_threads=args.host_threads,

@@ -156,6 +156,20 @@ typedef struct mt_stats {
                                  latency, including any wait for the next unit's weights ([Hotdry]
                                  monitoring section: switch latency) */
     double device_idle_ms[3]; /* per phase: time with neither a compute visit nor a copy running */
+    /* Prefetch timing ([Peter] technical details, memory prefetch strategy):
+     * the time the host-to-device link idles before a copy on the weight
+     * stream, per phase and by what the copy waited for: [p][0] its slot
+     * (the earliest any schedule over the same slots could issue it),
+     * [p][1] the host (the update of its weights, or the pack), [p][2]
+     * copies that are not weights (checkpoint restores, labels, inputs). */
+    double h2d_idle_ms[3][3];
+    /* Switch latency of the double buffer ([Hotdry] monitoring section):
+     * start of a compute visit minus the end of the one before, over the
+     * visits whose weights (and, writing gradients, whose gradient area)
+     * were ready before the previous visit ended: median and 90th
+     * percentile; ready_switches of switches visits were ready. */
+    double ready_switch_ms[2];
+    int32_t ready_switches, switches;
 } mt_stats;
 
 typedef struct mt_tensor_info {

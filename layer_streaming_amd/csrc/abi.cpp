@@ -140,18 +140,26 @@ int mt_k_attn_fwd(const void* qkv, int64_t ld, void* o, int64_t ldo, void* lse, 
     return kst(mt::attn_fwd(a, S_(stream)), "attn_fwd");
 }
 
-int64_t mt_k_attn_bwd_work_bytes(int32_t B, int32_t S, int32_t Hq, int32_t hd) {
-    if (B <= 0 || S <= 0 || Hq <= 0 || hd <= 0) return 0;
-    return mt::attn_bwd_work_bytes(B, S, Hq, hd);
+int64_t mt_k_attn_bwd_work_bytes(int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t hd) {
+    if (B <= 0 || S <= 0 || Hq <= 0 || Hkv <= 0 || hd <= 0 || Hq % Hkv) return 0;
+    return mt::attn_bwd_work_bytes(B, S, Hq, Hkv, hd);
+}
+
+int32_t mt_k_attn_dkdv_splits(int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t hd, int32_t head_splits) {
+    if (B <= 0 || S <= 0 || Hq <= 0 || Hkv <= 0 || hd <= 0 || Hq % Hkv || head_splits < 0) return 0;
+    return mt::attn_dkdv_splits(B, S, Hq, Hkv, hd, mt::attn_bwd_part_elems(B, S, Hq, Hkv, hd), head_splits);
 }
 
 int mt_k_attn_bwd(const void* qkv, int64_t ld, const void* o, const void* dout, int64_t ldo, const void* lse,
                   void* work, void* dqkv, int64_t ldd, int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t hd,
-                  void* dqk32, int64_t ld32, void* fp16_ovf, void* stream) {
+                  void* dqk32, int64_t ld32, int32_t head_splits, void* fp16_ovf, void* stream) {
     if (!work || (reinterpret_cast<uintptr_t>(work) & 255)) MT_FAIL(MT_E_INVAL, "attn_bwd: work must be 256-byte aligned");
+    if (head_splits < 0) MT_FAIL(MT_E_INVAL, "attn_bwd: head_splits must be >= 0");
     mt::AttnBwdArgs a{U16(qkv), ld, U16(o), U16(dout), ldo, F32(lse), nullptr, nullptr, nullptr, U16(dqkv), ldd,
                       B, S, Hq, Hkv, hd, F32(dqk32), ld32, static_cast<uint32_t*>(fp16_ovf)};
-    if (B > 0 && S > 0 && Hq > 0 && (hd == 64 || hd == 128)) mt::attn_bwd_carve(work, B, S, Hq, hd, a);
+    a.splits = head_splits;
+    if (B > 0 && S > 0 && Hq > 0 && Hkv > 0 && Hq % Hkv == 0 && (hd == 64 || hd == 128))
+        mt::attn_bwd_carve(work, B, S, Hq, Hkv, hd, a);
     return kst(mt::attn_bwd(a, S_(stream)), "attn_bwd");
 }
 

@@ -333,64 +333,87 @@ __device__ __forceinline__ float grad_scale(const uint32_t* amax, int hd) {
 }
 
 // max |dO| over [T x Hq*hd] (row stride ldo) and max |v| over the value
-// heads of qkv; one atomic max per wave into amax[0], amax[1] (zeroed first).
+// heads of qkv into amax[0], amax[1] (zeroed first): the first nb_do blocks
+// stride over dO, the rest over v, four 16-byte loads in flight per lane; one
+// atomic max per block.  Indices are 32-bit (the host checks T*Hq*hd/8 <
+// 2^31).
 template <int HD>
 __global__ __launch_bounds__(256) void attn_amax_k(AttnBwdArgs a, int nb_do) {
-    const int64_t T = int64_t(a.B) * a.S;
+    __shared__ float red[4];
+    const uint32_t T = uint32_t(int64_t(a.B) * a.S);
     const bool is_do = int(blockIdx.x) < nb_do;
-    const int bi = is_do ? int(blockIdx.x) : int(blockIdx.x) - nb_do;
-    const int nb = is_do ? nb_do : int(gridDim.x) - nb_do;
-    const int per_row = (is_do ? a.Hq : a.Hkv) * HD / 8;  // 16-byte chunks per row
-    const int64_t n = T * per_row;
-    float mx = 0.f;
-    for (int64_t i = int64_t(bi) * 256 + threadIdx.x; i < n; i += int64_t(nb) * 256) {
-        const int64_t t = i / per_row;
-        const int cc = int(i % per_row);
+    const uint32_t bi = is_do ? blockIdx.x : blockIdx.x - nb_do;
+    const uint32_t nb = is_do ? uint32_t(nb_do) : gridDim.x - nb_do;
+    const uint32_t per_row = uint32_t(is_do ? a.Hq : a.Hkv) * (HD / 8);  // 16-byte chunks per row
+    const uint32_t n = T * per_row, stride = nb * 256;
+    const uint16_t* vcol = a.qkv + int64_t(a.Hq + a.Hkv) * HD;
+    auto chunk = [&](uint32_t i) {
+        const uint32_t t = i / per_row, cc = i - t * per_row;
+        return is_do ? reinterpret_cast<const uint4*>(a.dout + int64_t(t) * a.ldo)[cc]
+                     : reinterpret_cast<const uint4*>(vcol + int64_t(t) * a.ld)[cc];
+    };
+    auto fold = [&](const uint4& v, float& mx) {
         float f[8];
-        if (is_do) {
-            unpack8(reinterpret_cast<const uint4*>(a.dout + t * a.ldo)[cc], f);
-        } else {
-            const uint16_t* vrow = a.qkv + t * a.ld + int64_t(a.Hq + a.Hkv) * HD;
-            unpack8h(reinterpret_cast<const uint4*>(vrow)[cc], f);
-        }
+        if (is_do) unpack8(v, f);
+        else unpack8h(v, f);
 #pragma unroll
         for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(f[e]));
+    };
+    float mx = 0.f;
+    uint32_t i = bi * 256 + threadIdx.x;
+    for (; n > 3 * stride && i < n - 3 * stride; i += 4 * stride) {
+        const uint4 v0 = chunk(i), v1 = chunk(i + stride), v2 = chunk(i + 2 * stride), v3 = chunk(i + 3 * stride);
+        fold(v0, mx);
+        fold(v1, mx);
+        fold(v2, mx);
+        fold(v3, mx);
     }
+    for (; i < n; i += stride) fold(chunk(i), mx);
     mx = wave_max(mx);
-    if ((threadIdx.x & 63) == 0) atomicMax(a.amax + (is_do ? 0 : 1), __float_as_uint(mx));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        atomicMax(a.amax + (is_do ? 0 : 1), __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
 }
 
-// One thread per (token, query head): D 2^k = rowsum(dO * O) 2^k (O fp16) into
-// dsum, and dO 2^k in fp16 into do16 (range-guarded; the scale keeps it
-// below 2^14).
+// D 2^k = rowsum(dO * O) 2^k (O fp16) into dsum, and dO 2^k in fp16 into
+// do16 (range-guarded; the scale keeps it below 2^14).  One lane per 16-byte
+// chunk of a (token, query head) row: the HD/8 lanes of a row are adjacent,
+// so a wave instruction covers whole rows, and the row's dot product is
+// reduced across them in a fixed order.
 template <int HD>
 __global__ __launch_bounds__(256) void attn_prep_k(AttnBwdArgs a) {
-    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    const int64_t T = int64_t(a.B) * a.S;
-    if (i >= T * a.Hq) return;
+    constexpr int L = HD / 8;  // lanes per row
+    const uint32_t i = blockIdx.x * 256 + threadIdx.x;
+    const uint32_t nrow = uint32_t(int64_t(a.B) * a.S) * uint32_t(a.Hq);
+    const uint32_t r = i / L;
+    const int j = int(i % L);
     const float s2k = grad_scale(a.amax, HD);
-    const int h = int(i % a.Hq);
-    const int64_t t = i / a.Hq;
-    const uint4* o = reinterpret_cast<const uint4*>(a.o + t * a.ldo + h * HD);
-    const uint4* g = reinterpret_cast<const uint4*>(a.dout + t * a.ldo + h * HD);
-    uint4* g16 = reinterpret_cast<uint4*>(a.do16 + t * (int64_t(a.Hq) * HD) + h * HD);
     float s = 0.f;
-    uint32_t nov = 0;
-#pragma unroll 4
-    for (int j = 0; j < HD / 8; ++j) {
+    uint32_t nov = 0, t = 0;
+    int h = 0;
+    if (r < nrow) {
+        t = r / uint32_t(a.Hq);
+        h = int(r - t * uint32_t(a.Hq));
+        const uint4 ov = reinterpret_cast<const uint4*>(a.o + int64_t(t) * a.ldo + h * HD)[j];
+        const uint4 gv = reinterpret_cast<const uint4*>(a.dout + int64_t(t) * a.ldo + h * HD)[j];
         float x[8], y[8];
-        unpack8h(o[j], x);
-        unpack8(g[j], y);
+        unpack8h(ov, x);
+        unpack8(gv, y);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             s += x[k] * y[k];
             y[k] *= s2k;
         }
-        g16[j] = pack8h_sat(y, nov);
+        reinterpret_cast<uint4*>(a.do16 + int64_t(t) * (int64_t(a.Hq) * HD) + h * HD)[j] = pack8h_sat(y, nov);
+    }
+#pragma unroll
+    for (int o = L / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+    if (r < nrow && j == 0) {
+        const uint32_t b = t / uint32_t(a.S), sq = t - b * uint32_t(a.S);
+        a.dsum[(int64_t(b) * a.Hq + h) * a.S + sq] = s * s2k;
     }
     count_ovf(a.ovf, nov);
-    const int b = int(t / a.S), sq = int(t % a.S);
-    a.dsum[(int64_t(b) * a.Hq + h) * a.S + sq] = s * s2k;
 }
 
 // Write four consecutive gradient columns of one row: fp32 into the fp32
@@ -533,71 +556,89 @@ __global__ __launch_bounds__(256, 2) void attn_dq_k(AttnBwdArgs a, int n_qt) {
     }
 }
 
-// dK, dV: block = 4 waves x 32 keys of one (b, kv head); query tiles of 64
-// over the group's heads, staged as fp16 Q (rows for the scores, read
-// transposed for dK) and the scaled fp16 dO (rows for dP, transposed for dV).
+// dK, dV: block = 8 waves over 128 keys of one (b, kv head), looping over
+// 64-query tiles of the group's query heads (or, split ns ways, of the
+// split's share of them), head by head, each from the block's diagonal to
+// the end of the sequence.  The work of a key tile shrinks with its
+// position (causal), so blocks go out heaviest first when kt_slow (key tile
+// the slowest index), else key tiles of one (b, kv head) in a row.  With
+// ns > 1 each block writes its fp32 partial sums, which attn_dkdv_reduce_k
+// adds in split order.  Waves w and w+4 (one SIMD) share keys
+// k0 + 32 w ..+31 and split each tile's work: the score wave (w < 4) holds K
+// for its keys, forms S = Q K^T and P, hands P (fp32) to its partner through
+// LDS and accumulates dV += P^T dO; the gradient wave holds V, forms
+// dP = dO V^T and, after a barrier, dS = P (dP - D) and dK += dS^T Q.  Each
+// wave keeps one accumulator set, so the kernel fits 256 registers (two
+// waves per SIMD) and one wave's exponentials and conversions run beside the
+// other's products.  The score waves stage the Q tiles, the gradient waves
+// the dO tiles.
 template <int HD>
-__global__ __launch_bounds__(256, 1) void attn_dkdv_k(AttnBwdArgs a, int n_kt) {
+__global__ __launch_bounds__(512, 1) void attn_dkdv_k(AttnBwdArgs a, int n_kt, int ns, int kt_slow) {
     constexpr int NS = HD / 16, ND = HD / 32, NCH = HD / 8;
     constexpr int TILE = BKV * NCH, NI = TILE / 256;
     __shared__ uint4 Qs[2][TILE];
     __shared__ uint4 Ds[2][TILE];
     __shared__ __align__(16) float Ls[2][BKV];
     __shared__ __align__(16) float Dd[2][BKV];
+    __shared__ float4 Px[4][8][64];  // per key group: lane l's 32 probabilities as 8 float4
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int pw = wave & 3;
+    const bool sw = wave < 4;
     const int hh = lane >> 5, c = lane & 31;
-    const int kt = int(blockIdx.x % n_kt);
-    const int bk = int(blockIdx.x / n_kt);
+    int kt, bk;
+    const int split = int(blockIdx.x % unsigned(ns));
+    {
+        const int r = int(blockIdx.x / unsigned(ns)), nbk = a.B * a.Hkv;
+        kt = kt_slow ? r / nbk : r % n_kt;
+        bk = kt_slow ? r % nbk : r / n_kt;
+    }
     const int hk = bk % a.Hkv, b = bk / a.Hkv;
     const int G = a.Hq / a.Hkv;
+    const int h_lo = hk * G + split * G / ns, ng = hk * G + (split + 1) * G / ns - h_lo;
     const int S = a.S;
-    const int k0 = kt * 128, kw = k0 + wave * 32, key = kw + c;
+    const int k0 = kt * 128, kw = k0 + pw * 32, key = kw + c;
     const int64_t ldg = int64_t(a.Hq) * HD;  // do16 row stride
     const uint16_t* base = a.qkv + int64_t(b) * S * a.ld;
     const uint16_t* gbase = a.do16 + int64_t(b) * S * ldg;
     const int kcol = (a.Hq + hk) * HD, vcol = (a.Hq + a.Hkv + hk) * HD;
     const float s2k = grad_scale(a.amax, HD);
 
-    f16x8_t kf[NS], vf[NS];
+    // K (score wave) or V (gradient wave) of the wave's keys: the B operand
+    f16x8_t kv[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-        uint4 v = make_uint4(0, 0, 0, 0), w = v;
-        if (key < S) {
-            v = *reinterpret_cast<const uint4*>(base + int64_t(key) * a.ld + kcol + (2 * s + hh) * 8);
-            w = *reinterpret_cast<const uint4*>(base + int64_t(key) * a.ld + vcol + (2 * s + hh) * 8);
-        }
-        kf[s] = as_f16x8(v);
-        vf[s] = as_f16x8(w);
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (key < S) v = *reinterpret_cast<const uint4*>(base + int64_t(key) * a.ld + (sw ? kcol : vcol) + (2 * s + hh) * 8);
+        kv[s] = as_f16x8(v);
     }
 
-    uint32_t offq[NI], offd[NI];
-    tile_offsets<HD>(offq, wave, lane, a.ld);
-    tile_offsets<HD>(offd, wave, lane, ldg);
+    uint32_t off[NI];
+    tile_offsets<HD>(off, pw, lane, sw ? a.ld : ldg);
     float lreg = 0.f, dreg = 0.f;
     auto issue = [&](int hq, int q0, int buf) {
-        tile_issue<HD>(base + int64_t(q0) * a.ld + hq * HD, a.ld, S - q0, offq, lds_addr(&Qs[buf][0]), wave);
-        tile_issue<HD>(gbase + int64_t(q0) * ldg + hq * HD, ldg, S - q0, offd, lds_addr(&Ds[buf][0]), wave);
+        if (sw) tile_issue<HD>(base + int64_t(q0) * a.ld + hq * HD, a.ld, S - q0, off, lds_addr(&Qs[buf][0]), pw);
+        else tile_issue<HD>(gbase + int64_t(q0) * ldg + hq * HD, ldg, S - q0, off, lds_addr(&Ds[buf][0]), pw);
         if (tid < BKV) {
-            const int64_t off = (int64_t(b) * a.Hq + hq) * S;
+            const int64_t o = (int64_t(b) * a.Hq + hq) * S;
             const int qq = q0 + tid;
-            lreg = qq < S ? a.lse[off + qq] * LOG2E : 0.f;
-            dreg = qq < S ? a.dsum[off + qq] : 0.f;
+            lreg = qq < S ? a.lse[o + qq] * LOG2E : 0.f;
+            dreg = qq < S ? a.dsum[o + qq] : 0.f;
         }
     };
 
-    f32x16_t dk[ND], dv[ND];
+    f32x16_t acc[ND];  // dV (score wave) or dK (gradient wave), transposed: rows = head dim, lane = key
 #pragma unroll
     for (int i = 0; i < ND; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) { dk[i][r] = 0.f; dv[i][r] = 0.f; }
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
     const float sc = LOG2E * rsqrtf(float(HD));
 
     const int qb0 = k0 / BKV;
     const int nqb = (S + BKV - 1) / BKV - qb0;  // per head
-    const int total = nqb * G;
+    const int total = nqb * ng;
     if (total > 0) {
-        issue(hk * G, qb0 * BKV, 0);
+        issue(h_lo, qb0 * BKV, 0);
         if (tid < BKV) {
             Ls[0][tid] = lreg;
             Dd[0][tid] = dreg;
@@ -607,51 +648,43 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_k(AttnBwdArgs a, int n_kt) {
     for (int it = 0; it < total; ++it) {
         const int cur = it & 1;
         const int q0 = (qb0 + it % nqb) * BKV;
-        if (it + 1 < total) issue(hk * G + (it + 1) / nqb, (qb0 + (it + 1) % nqb) * BKV, cur ^ 1);
-        {  // every wave computes; a tile wholly before its keys is masked to zero
-            f32x16_t st[2], dp[2];
+        if (it + 1 < total) issue(h_lo + (it + 1) / nqb, (qb0 + (it + 1) % nqb) * BKV, cur ^ 1);
+        // some query of the tile at or after one of the wave's keys
+        const bool live = kw <= q0 + BKV - 1;
+        const bool full = kw + 31 <= q0 && q0 + BKV <= S && kw + 32 <= S;
+        const uint4* At = sw ? Qs[cur] : Ds[cur];
+        f32x16_t st[2];  // S (score wave) or dP (gradient wave): rows = queries, lane = key
+        if (live) {
+            // fragments read PA - 1 k-steps ahead of their products
+            constexpr int PA = 3;
+            uint4 fa[PA][2];
+            auto rd = [&](int s, uint4(&f)[2]) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) { st[t][r] = 0.f; dp[t][r] = 0.f; }
-            // S^T and dP^T over the head dimension in k-steps of 16: the
-            // fragments of step s+1 are read while step s multiplies (left to
-            // itself the compiler waits for each fragment right before its
-            // MFMA), and the four accumulations of a step are independent.
-            uint4 fq[2][2], fd[2][2];
-            auto rd = [&](int s, uint4(&qv)[2], uint4(&dvv)[2]) {
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    qv[t] = tile_row<HD>(Qs[cur], 32 * t + c, 2 * s + hh);
-                    dvv[t] = tile_row<HD>(Ds[cur], 32 * t + c, 2 * s + hh);
-                }
+                for (int t = 0; t < 2; ++t) f[t] = tile_row<HD>(At, 32 * t + c, 2 * s + hh);
             };
-            rd(0, fq[0], fd[0]);
+            static_for_n<PA - 1>([&](auto s_) { rd(decltype(s_)::value, fa[decltype(s_)::value]); });
             static_for_n<NS>([&](auto s_) {
                 constexpr int s = decltype(s_)::value;
-                if constexpr (s + 1 < NS) rd(s + 1, fq[(s + 1) & 1], fd[(s + 1) & 1]);
+                if constexpr (s + PA - 1 < NS) rd(s + PA - 1, fa[(s + PA - 1) % PA]);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    st[t] = MFMA32H(as_f16x8(fq[s & 1][t]), kf[s], st[t]);
-                    dp[t] = MFMA32H(as_f16x8(fd[s & 1][t]), vf[s], dp[t]);
-                }
+                for (int t = 0; t < 2; ++t)
+                    st[t] = MFMA32H(as_f16x8(fa[s % PA][t]), kv[s], s == 0 ? f32x16_t{} : st[t]);
                 __builtin_amdgcn_sched_barrier(0);
             });
-            f16x8_t pb[2][2], dsb[2][2];
-            const bool full = kw + 31 <= q0 && q0 + BKV <= S && kw + 32 <= S;
+        }
+        f16x8_t op[2][2];  // P (score wave) or dS (gradient wave) as the fp16 B operand
+        if (sw && live) {
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
-                    float tp[8], td[8];
+                    float tp[8];
 #pragma unroll
                     for (int g4 = 0; g4 < 2; ++g4) {
-                        // four consecutive queries' statistics in one 16-byte read each
                         const int qb = 32 * t + 8 * (2 * s2 + g4) + 4 * hh;
-                        float lv[4], dv4[4];
+                        float lv[4];
                         *reinterpret_cast<float4*>(lv) = *reinterpret_cast<const float4*>(&Ls[cur][qb]);
-                        *reinterpret_cast<float4*>(dv4) = *reinterpret_cast<const float4*>(&Dd[cur][qb]);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int j = 4 * g4 + e, r = 8 * s2 + j;
@@ -661,21 +694,65 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_k(AttnBwdArgs a, int n_kt) {
                                 if (key > qq || qq >= S || key >= S) p = 0.f;
                             }
                             tp[j] = p;
-                            td[j] = p * (dp[t][r] - dv4[e]);
                         }
+                        Px[pw][4 * t + 2 * s2 + g4][lane] = make_float4(tp[4 * g4], tp[4 * g4 + 1], tp[4 * g4 + 2],
+                                                                        tp[4 * g4 + 3]);
                     }
-                    pb[t][s2] = pack_h8(tp);
-                    dsb[t][s2] = pack_h8(td);
+                    op[t][s2] = pack_h8(tp);
                 }
-#pragma unroll
-            for (int dt = 0; dt < ND; ++dt)
+        }
+        // The first fragments of the dV (dK) products do not depend on P:
+        // read them now, so they land while the exponentials run.
+        const uint4* Bt = sw ? Ds[cur] : Qs[cur];
+        constexpr int PB = 4;
+        f16x8_t fb[PB];
+        if (live)
+            static_for_n<PB - 1>([&](auto j_) {
+                constexpr int j = decltype(j_)::value;
+                fb[j] = tile_colT<HD>(Bt, j % ND, j / ND / 2, (j / ND) % 2, lane);
+            });
+        // P is in LDS (the next tile's loads stay in flight)
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (live) {
+            if (!sw) {
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
                     for (int s2 = 0; s2 < 2; ++s2) {
-                        dv[dt] = MFMA32H(tile_colT<HD>(Ds[cur], dt, t, s2, lane), pb[t][s2], dv[dt]);
-                        dk[dt] = MFMA32H(tile_colT<HD>(Qs[cur], dt, t, s2, lane), dsb[t][s2], dk[dt]);
+                        float td[8];
+#pragma unroll
+                        for (int g4 = 0; g4 < 2; ++g4) {
+                            const int qb = 32 * t + 8 * (2 * s2 + g4) + 4 * hh;
+                            float dv4[4];
+                            *reinterpret_cast<float4*>(dv4) = *reinterpret_cast<const float4*>(&Dd[cur][qb]);
+                            const float4 pv = Px[pw][4 * t + 2 * s2 + g4][lane];
+                            const float pp[4] = {pv.x, pv.y, pv.z, pv.w};
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const int j = 4 * g4 + e;
+                                td[j] = pp[e] * (st[t][8 * s2 + j] - dv4[e]);
+                            }
+                        }
+                        op[t][s2] = pack_h8(td);
                     }
+            }
+            // dV (or dK) over the tile's 64 queries: the four accumulators
+            // take turns, and each transposed fragment is read PB - 1
+            // products ahead of its MFMA.
+            static_for_n<4 * ND>([&](auto i_) {
+                constexpr int i = decltype(i_)::value;
+                constexpr int dt = i % ND, t = i / ND / 2, s2 = (i / ND) % 2;
+                if constexpr (i + PB - 1 < 4 * ND) {
+                    constexpr int j = i + PB - 1;
+                    fb[j % PB] = tile_colT<HD>(Bt, j % ND, j / ND / 2, (j / ND) % 2, lane);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                acc[dt] = MFMA32H(fb[i % PB], op[t][s2], acc[dt]);
+                __builtin_amdgcn_sched_barrier(0);
+            });
         }
         if (it + 1 < total && tid < BKV) {
             Ls[cur ^ 1][tid] = lreg;
@@ -684,21 +761,65 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_k(AttnBwdArgs a, int n_kt) {
         barrier_tile();
     }
     if (key < S) {
-        const float inv = 1.0f / s2k, scale = rsqrtf(float(HD)) * inv;
+        const float inv = 1.0f / s2k, scale = sw ? inv : rsqrtf(float(HD)) * inv;
         const int64_t row = int64_t(b) * S + key;
-        float* r32 = a.dqk32 ? a.dqk32 + row * a.ld32 + (a.Hq + hk) * HD : nullptr;
-        uint16_t* rk = a.dqkv + row * a.ldd + kcol;
-        uint16_t* rv = a.dqkv + row * a.ldd + vcol;
+        if (ns > 1) {
+            const int64_t T = int64_t(a.B) * S, w = int64_t(a.Hkv) * HD;
+            float* prow = a.dpart + (int64_t(split) * T + row) * (2 * w) + hk * HD + (sw ? w : 0);
 #pragma unroll
-        for (int dt = 0; dt < ND; ++dt)
+            for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d = 32 * dt + 8 * g + 4 * hh;
-                store_grad4(r32, rk, d, dk[dt][4 * g] * scale, dk[dt][4 * g + 1] * scale, dk[dt][4 * g + 2] * scale,
-                            dk[dt][4 * g + 3] * scale);
-                *reinterpret_cast<uint2*>(rv + d) = make_uint2(pack2(dv[dt][4 * g] * inv, dv[dt][4 * g + 1] * inv),
-                                                               pack2(dv[dt][4 * g + 2] * inv, dv[dt][4 * g + 3] * inv));
-            }
+                for (int g = 0; g < 4; ++g)
+                    *reinterpret_cast<float4*>(prow + 32 * dt + 8 * g + 4 * hh) =
+                        make_float4(acc[dt][4 * g] * scale, acc[dt][4 * g + 1] * scale, acc[dt][4 * g + 2] * scale,
+                                    acc[dt][4 * g + 3] * scale);
+        } else if (sw) {
+            uint16_t* rv = a.dqkv + row * a.ldd + vcol;
+#pragma unroll
+            for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *reinterpret_cast<uint2*>(rv + 32 * dt + 8 * g + 4 * hh) =
+                        make_uint2(pack2(acc[dt][4 * g] * scale, acc[dt][4 * g + 1] * scale),
+                                   pack2(acc[dt][4 * g + 2] * scale, acc[dt][4 * g + 3] * scale));
+        } else {
+            float* r32 = a.dqk32 ? a.dqk32 + row * a.ld32 + (a.Hq + hk) * HD : nullptr;
+            uint16_t* rk = a.dqkv + row * a.ldd + kcol;
+#pragma unroll
+            for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    store_grad4(r32, rk, 32 * dt + 8 * g + 4 * hh, acc[dt][4 * g] * scale,
+                                acc[dt][4 * g + 1] * scale, acc[dt][4 * g + 2] * scale, acc[dt][4 * g + 3] * scale);
+        }
+    }
+}
+
+// Sum of the ns partials of the split dK/dV pass, in split order: dK into
+// the fp32 buffer (or bf16 dqkv), dV into dqkv in bf16.  One lane per four
+// columns of a row's [dK | dV] partial.
+__global__ __launch_bounds__(256) void attn_dkdv_reduce_k(AttnBwdArgs a, int ns) {
+    const int64_t T = int64_t(a.B) * a.S;
+    const int w = a.Hkv * a.hd, q4 = w / 2;  // columns of one half; float4s per row
+    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= T * q4) return;
+    const int64_t row = i / q4;
+    const int j = int(i - row * q4) * 4;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int p = 0; p < ns; ++p) {
+        const float4 v = *reinterpret_cast<const float4*>(a.dpart + (int64_t(p) * T + row) * (2 * int64_t(w)) + j);
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+    }
+    if (j < w) {
+        const int col = a.Hq * a.hd + j;
+        if (a.dqk32) *reinterpret_cast<float4*>(a.dqk32 + row * a.ld32 + col) = acc;
+        else *reinterpret_cast<uint2*>(a.dqkv + row * a.ldd + col) = make_uint2(pack2(acc.x, acc.y), pack2(acc.z, acc.w));
+    } else {
+        const int col = (a.Hq + a.Hkv) * a.hd + (j - w);
+        *reinterpret_cast<uint2*>(a.dqkv + row * a.ldd + col) = make_uint2(pack2(acc.x, acc.y), pack2(acc.z, acc.w));
     }
 }
 
@@ -723,19 +844,41 @@ hipError_t attn_fwd(const AttnArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-int64_t attn_bwd_work_bytes(int B, int S, int Hq, int hd) {
-    auto al = [](int64_t x) { return (x + 255) & ~int64_t(255); };
-    const int64_t T = int64_t(B) * S;
-    return al(T * Hq * 4) + al(T * Hq * hd * 2) + 256;
+int attn_dkdv_splits(int B, int S, int Hq, int Hkv, int hd, int64_t part_elems, int req) {
+    if (B <= 0 || S <= 0 || Hkv <= 0 || Hq % Hkv) return 1;
+    const int G = Hq / Hkv;
+    const int64_t blocks = int64_t(B) * Hkv * ((S + 127) / 128);
+    int ns = req > 0 ? std::min(req, G) : blocks >= 512 ? 1 : int(std::min<int64_t>(G, (512 + blocks - 1) / blocks));
+    const int64_t per = int64_t(B) * S * 2 * Hkv * hd;
+    while (ns > 1 && ns * per > part_elems) --ns;
+    return std::max(ns, 1);
 }
 
-void attn_bwd_carve(void* work, int B, int S, int Hq, int hd, AttnBwdArgs& a) {
-    auto al = [](int64_t x) { return (x + 255) & ~int64_t(255); };
+int64_t attn_bwd_part_elems(int B, int S, int Hq, int Hkv, int hd) {
+    const int ns = attn_dkdv_splits(B, S, Hq, Hkv, hd, INT64_MAX, 0);
+    return ns > 1 ? int64_t(ns) * B * S * 2 * Hkv * hd : 0;
+}
+
+namespace {
+int64_t al256(int64_t x) { return (x + 255) & ~int64_t(255); }
+}  // namespace
+
+int64_t attn_bwd_work_bytes(int B, int S, int Hq, int Hkv, int hd) {
+    const int64_t T = int64_t(B) * S;
+    return al256(T * Hq * 4) + al256(T * Hq * hd * 2) + 256 + al256(attn_bwd_part_elems(B, S, Hq, Hkv, hd) * 4);
+}
+
+void attn_bwd_carve(void* work, int B, int S, int Hq, int Hkv, int hd, AttnBwdArgs& a) {
     const int64_t T = int64_t(B) * S;
     uint8_t* p = static_cast<uint8_t*>(work);
     a.dsum = reinterpret_cast<float*>(p);
-    a.do16 = reinterpret_cast<uint16_t*>(p + al(T * Hq * 4));
-    a.amax = reinterpret_cast<uint32_t*>(p + al(T * Hq * 4) + al(T * Hq * hd * 2));
+    p += al256(T * Hq * 4);
+    a.do16 = reinterpret_cast<uint16_t*>(p);
+    p += al256(T * Hq * hd * 2);
+    a.amax = reinterpret_cast<uint32_t*>(p);
+    p += 256;
+    a.dpart_elems = attn_bwd_part_elems(B, S, Hq, Hkv, hd);
+    a.dpart = a.dpart_elems ? reinterpret_cast<float*>(p) : nullptr;
 }
 
 hipError_t attn_bwd(const AttnBwdArgs& a, hipStream_t s) {
@@ -744,14 +887,20 @@ hipError_t attn_bwd(const AttnBwdArgs& a, hipStream_t s) {
     if (!a.dsum || !a.do16 || !a.amax || !a.dqkv) return hipErrorInvalidValue;
     if (a.dqk32 && (a.ld32 < int64_t(a.Hq + a.Hkv) * a.hd || (a.ld32 & 3))) return hipErrorInvalidValue;
     const int64_t T = int64_t(a.B) * a.S;
+    // the maxima and prep kernels index 16-byte chunks with 32 bits (with
+    // room for a grid stride past the end)
+    if (T * a.Hq * (a.hd / 8) >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    const int ns = attn_dkdv_splits(a.B, a.S, a.Hq, a.Hkv, a.hd, a.dpart ? a.dpart_elems : 0, a.splits);
     const int n_qt = (a.S + 127) / 128;
     const int n_kt = (a.S + 127) / 128;
+    const int64_t nk = int64_t(n_kt) * a.B * a.Hkv * ns;
+    const int kt_slow = nk <= 2048;
     const dim3 gq(unsigned(int64_t(n_qt) * a.B * a.Hq));
-    const dim3 gk(unsigned(int64_t(n_kt) * a.B * a.Hkv));
-    const unsigned np = unsigned((T * a.Hq + 255) / 256);
+    const dim3 gk(static_cast<unsigned>(nk));
+    const unsigned np = unsigned((T * a.Hq * (a.hd / 8) + 255) / 256);
     // maxima: enough blocks to cover the chip, each striding over its part
     const int nb_do = int(std::min<int64_t>(1024, (T * a.Hq * a.hd / 8 + 255) / 256));
-    const int nb_v = int(std::min<int64_t>(256, (T * a.Hkv * a.hd / 8 + 255) / 256));
+    const int nb_v = int(std::min<int64_t>(128, (T * a.Hkv * a.hd / 8 + 255) / 256));
     hipError_t e = fill_zero(a.amax, 256, s);
     if (e != hipSuccess) return e;
     auto run = [&](auto hd_) {
@@ -759,10 +908,14 @@ hipError_t attn_bwd(const AttnBwdArgs& a, hipStream_t s) {
         attn_amax_k<HD><<<nb_do + nb_v, 256, 0, s>>>(a, nb_do);
         attn_prep_k<HD><<<np, 256, 0, s>>>(a);
         attn_dq_k<HD><<<gq, 256, 0, s>>>(a, n_qt);
-        attn_dkdv_k<HD><<<gk, 256, 0, s>>>(a, n_kt);
+        attn_dkdv_k<HD><<<gk, 512, 0, s>>>(a, n_kt, ns, kt_slow);
     };
     if (a.hd == 128) run(std::integral_constant<int, 128>{});
     else run(std::integral_constant<int, 64>{});
+    if (ns > 1) {
+        const int64_t n4 = T * (a.Hkv * a.hd / 2);
+        attn_dkdv_reduce_k<<<unsigned((n4 + 255) / 256), 256, 0, s>>>(a, ns);
+    }
     return hipGetLastError();
 }
 

@@ -31,6 +31,7 @@
 #include "engine.h"
 
 #include <algorithm>
+#include <array>
 #include <chrono>
 #include <cstdlib>
 #include <cstring>
@@ -190,6 +191,7 @@ void plan_workspace(const Layout& lay, const mt_options& o, Carver& cv, Workspac
                                       uint64_t(std::max(nq, nqkv)) * std::max<uint64_t>(T8, uint64_t(d)),
                                       uint64_t(d) * T8, head_t});
         ws.tA = cv.take<uint16_t>(ta * 2);
+        ws.tA_bytes = ta * 2;
         ws.tB = cv.take<uint16_t>(tb * 2);
     }
     ws.rstd1 = cv.take<float>(uint64_t(T) * 4);
@@ -440,6 +442,9 @@ struct Ctx {
         int kind;  // 0 compute, 1 h2d, 2 d2h
         uint64_t bytes;
         int visit = -1, unit = -1;  // compute: the visit kind and unit
+        int slot = -1;              // compute and weight copies: the weight slot
+        int64_t seq = -1;           // gradient copies: the offload request; compute: the one it waited for
+        int last_h2d = -1;          // compute: index of the last weight-stream copy it waited for
     };
     std::vector<Interval> intervals;
     std::vector<Interval> off_intervals;  // gradient copies, filled by the offload thread
@@ -473,14 +478,19 @@ struct Ctx {
         }
         return tev[tev_next++];
     }
-    hipError_t h2d(void* dst, const void* src, uint64_t bytes, hipStream_t s) {
+    hipError_t h2d(void* dst, const void* src, uint64_t bytes, hipStream_t s, int slot = -1) {
         hipEvent_t a = timing ? next_tev() : nullptr, b = timing ? next_tev() : nullptr;
         if (a) hipEventRecord(a, s);
         hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, s);
         if (b) hipEventRecord(b, s);
-        if (a && b) intervals.push_back({a, b, 1, bytes});
+        if (a && b) {
+            intervals.push_back({a, b, 1, bytes});
+            intervals.back().slot = slot;
+            last_h2d = int(intervals.size()) - 1;
+        }
         return e;
     }
+    int last_h2d = -1;  // index in intervals of the latest weight-stream copy
     hipError_t d2h(void* dst, const void* src, uint64_t bytes, hipStream_t s) {
         hipEvent_t a = timing ? next_tev() : nullptr, b = timing ? next_tev() : nullptr;
         if (a) hipEventRecord(a, s);
@@ -894,7 +904,10 @@ void Ctx::offload_worker() {
         }
         {
             std::lock_guard<std::mutex> lk(off_mu);
-            if (a && b && e == hipSuccess) off_intervals.push_back({a, b, 2, r.bytes, -1, k});
+            if (a && b && e == hipSuccess) {
+                off_intervals.push_back({a, b, 2, r.bytes, -1, k});
+                off_intervals.back().seq = off_issued;
+            }
             if (e != hipSuccess && off_status == MT_OK) {
                 off_status = MT_E_HIP;
                 off_error = strfmt("HIP error '%s' offloading the gradient of unit %d", hipGetErrorString(e), r.unit);
@@ -1141,7 +1154,8 @@ hipError_t Ctx::bwd_layer(const LayerView& w, const LayerView& g, const uint16_t
     // rounded to bf16 once.
     HIPR(site(S_ATTN_BWD, [&] {
         AttnBwdArgs a{ws.qkv, nqkv, ws.o, ws.dout, nq, ws.lse, ws.dsum, ws.do16, ws.amax, ws.dqkv, nqkv,
-                      B, S, sh.n_heads, sh.n_kv_heads, sh.head_dim, ws.qkv32, nqkv, ws.ovf};
+                      B, S, sh.n_heads, sh.n_kv_heads, sh.head_dim, ws.qkv32, nqkv, ws.ovf,
+                      reinterpret_cast<float*>(ws.tA), int64_t(ws.tA_bytes / 4), 0};
         return attn_bwd(a, s);
     }));
     HIPR(site(S_ROPE_BWD, [&] {
@@ -1345,7 +1359,7 @@ int Ctx::stream_unit(int unit, int slot, int id, int64_t e0, int64_t n) {
     if (wo != MT_OK) return wo;
     HIPC(wait(st_w, slot_free[slot]));
     if (store_pinned || wblock) {
-        HIPC(h2d(arena + plan.wslot[slot], src, bytes, st_w));
+        HIPC(h2d(arena + plan.wslot[slot], src, bytes, st_w, slot));
     } else {
         const int p = staging_ptr;
         staging_ptr ^= 1;
@@ -1356,7 +1370,7 @@ int Ctx::stream_unit(int unit, int slot, int id, int64_t e0, int64_t n) {
         parallel_copy(*pack_pool, staging[p], src, int64_t(bytes));
         pack_ms += ms_since(t0);
         host_rec("host_pack", unit, p, t0);
-        HIPC(h2d(arena + plan.wslot[slot], staging[p], bytes, st_w));
+        HIPC(h2d(arena + plan.wslot[slot], staging[p], bytes, st_w, slot));
         HIPC(rec(staging_free[p], st_w));
     }
     slot_unit[slot] = id < 0 ? unit : id;
@@ -1391,6 +1405,7 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
     slot_ptr = 0;
     tev_next = 0;
     intervals.clear();
+    last_h2d = -1;
     site_recs.clear();
     {
         // The offload thread is idle between steps: every request was issued.
@@ -1567,16 +1582,26 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
             Ev& wr = wready[slot];
             HIPC(rec(wr, st_w));
             HIPC(wait(st_c, wr));
+            const int vis_h2d = last_h2d;  // the compute waits for every weight-stream copy issued so far
             // Head and backward write a gradient area: wait until its last
             // offload is done (Buffer-Free) before the visit's clock starts.
             int ga = 0;
+            int64_t vis_seq = -1;
             if (kind == V_HEAD || kind == V_BWD || kind == V_HBWD) {
                 ga = combined ? slot : gnext;
                 if (!combined) gnext ^= 1;
+                vis_seq = ga_last_req[ga];
                 const int wo = wait_offload(ga_last_req[ga]);
                 if (wo != MT_OK) return wo;
                 HIPC(wait(st_c, buf_free[ga]));
             }
+            auto visit_rec = [&](hipEvent_t a, hipEvent_t b) {
+                Interval iv{a, b, 0, 0, kind, unit};
+                iv.slot = opt.resident ? -1 : slot;
+                iv.seq = vis_seq;
+                iv.last_h2d = vis_h2d;
+                intervals.push_back(iv);
+            };
             hipEvent_t va = next_tev(), vz = next_tev();
             HIPC(hipEventRecord(va, st_c));
             if (kind == V_FWD) {
@@ -1586,7 +1611,7 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
                 if (opt.ckpt_on_host) HIPC(wait(st_c, ckpt_done[(unit + 1) & 1]));
                 HIPC(fwd_layer(bind_layer(lay, wbase), x, y, B, S, true));
                 HIPC(hipEventRecord(vz, st_c));
-                intervals.push_back({va, vz, 0, 0, kind, unit});
+                visit_rec(va, vz);
                 HIPC(rec(slot_free[slot], st_c));
                 if (opt.ckpt_on_host) {
                     // Checkpoint the layer input on the gradient stream (idle in forward).
@@ -1612,7 +1637,7 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
                     HIPC(rec(loss_done, st_c));
                 }
                 HIPC(hipEventRecord(vz, st_c));
-                intervals.push_back({va, vz, 0, 0, kind, unit});
+                visit_rec(va, vz);
                 HIPC(rec(slot_free[slot], st_c));
                 continue;
             }
@@ -1620,7 +1645,7 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
                 // Rebuild the next layer's input inside the block's bank.
                 HIPC(fwd_layer(bind_layer(lay, wbase), xb[vs.pos], xb[vs.pos + 1], B, S, true));
                 HIPC(hipEventRecord(vz, st_c));
-                intervals.push_back({va, vz, 0, 0, kind, unit});
+                visit_rec(va, vz);
                 HIPC(rec(slot_free[slot], st_c));
                 continue;
             }
@@ -1644,7 +1669,7 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
                 if (opt.ckpt_on_host && vs.pos == 0) HIPC(rec(xc_free[bank], st_c));
             }
             HIPC(hipEventRecord(vz, st_c));
-            intervals.push_back({va, vz, 0, 0, kind, unit});
+            visit_rec(va, vz);
             if (!combined) HIPC(rec(slot_free[slot], st_c));
             HIPC(rec(bwd_done[ga], st_c));
             // Gradient offload: Backward-Done -> free slab -> Buffer-Free.
@@ -1918,6 +1943,71 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
                     stats->switch_gap_ms[p] = g[g.size() / 2];
                 }
                 stats->device_idle_ms[p] = std::max(0.0, idle[p]);
+            }
+        }
+        // Why the link idled before each weight-stream copy, and the switch
+        // latency of the visits that had nothing to wait for.
+        {
+            const double eps = 0.02;  // ms: events on one stream back to back
+            std::vector<std::pair<double, double>> tm(intervals.size());
+            for (size_t i = 0; i < intervals.size(); ++i) tm[i] = {el(t_base, intervals[i].a), el(t_base, intervals[i].b)};
+            std::vector<std::array<double, 4>> pe;
+            for (const Phases& ph : phases)
+                pe.push_back({el(t_base, ph.start), el(t_base, ph.fwd), el(t_base, ph.head), el(t_base, ph.bwd)});
+            auto phase_of = [&](double t) {
+                for (const auto& e : pe)
+                    for (int p = 0; p < 3; ++p)
+                        if (t >= e[p] && t <= e[p + 1]) return p;
+                return -1;
+            };
+            bool have_prev = false;
+            double prev_end = 0.0;  // end of the previous weight-stream copy
+            for (size_t i = 0; i < intervals.size(); ++i) {
+                const Interval& iv = intervals[i];
+                if (iv.kind != 1) continue;
+                const double s0 = tm[i].first, gap = s0 - prev_end;
+                const bool counted = have_prev && gap > eps;
+                prev_end = have_prev ? std::max(prev_end, tm[i].second) : tm[i].second;
+                have_prev = true;
+                const int p = phase_of(s0);
+                if (!counted || p < 0) continue;
+                int cause = 2;
+                if (iv.slot >= 0) {
+                    // the end of the last compute visit on this slot before the copy
+                    double f = -1.0;
+                    for (size_t j = 0; j < intervals.size(); ++j)
+                        if (intervals[j].kind == 0 && intervals[j].slot == iv.slot && tm[j].second <= s0 + eps)
+                            f = std::max(f, tm[j].second);
+                    cause = f >= 0.0 && s0 - f <= eps ? 0 : 1;
+                }
+                stats->h2d_idle_ms[p][cause] += gap;
+            }
+            std::vector<size_t> cvis;
+            for (size_t i = 0; i < intervals.size(); ++i)
+                if (intervals[i].kind == 0) cvis.push_back(i);
+            std::sort(cvis.begin(), cvis.end(), [&](size_t x, size_t y) { return tm[x].first < tm[y].first; });
+            std::vector<double> rs;
+            for (size_t k = 1; k < cvis.size(); ++k) {
+                const size_t i = cvis[k], j = cvis[k - 1];
+                ++stats->switches;
+                const Interval& iv = intervals[i];
+                double ready = iv.last_h2d >= 0 ? tm[size_t(iv.last_h2d)].second : 0.0;
+                if (iv.seq >= 0) {
+                    bool found = false;
+                    for (size_t m = 0; m < intervals.size(); ++m)
+                        if (intervals[m].kind == 2 && intervals[m].seq == iv.seq) {
+                            ready = std::max(ready, tm[m].second);
+                            found = true;
+                        }
+                    if (!found) continue;
+                }
+                if (ready <= tm[j].second + eps) rs.push_back(std::max(0.0, tm[i].first - tm[j].second));
+            }
+            stats->ready_switches = int32_t(rs.size());
+            if (!rs.empty()) {
+                std::sort(rs.begin(), rs.end());
+                stats->ready_switch_ms[0] = rs[rs.size() / 2];
+                stats->ready_switch_ms[1] = rs[std::min(rs.size() - 1, size_t(0.9 * double(rs.size())))];
             }
         }
         stats->pack_ms = pack_ms;

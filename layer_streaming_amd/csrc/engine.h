@@ -54,6 +54,7 @@ struct Workspace {
     uint16_t *dy[2], *dm, *dgu, *dn, *dh1, *dout, *dqkv;
     // reduction-contiguous copies of the backward products' operands
     uint16_t *tA, *tB;
+    uint64_t tA_bytes = 0;  // also the dK/dV split partials of the attention backward (tA is idle then)
     float *dsum, *partial;
     float2* rope_tab;
     int32_t* labels;

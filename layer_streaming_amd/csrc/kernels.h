@@ -117,11 +117,23 @@ struct AttnBwdArgs {
     // Hkv key heads), for a rotation that rounds them to bf16 once.
     float* dqk32 = nullptr; int64_t ld32 = 0;
     uint32_t* ovf = nullptr;  // fp16 range guard of the scaled dO
+    // fp32 scratch for the partial sums of a dK/dV pass split over the query
+    // heads of each KV group (short sequences: too few key tiles to fill the
+    // chip).  splits: 0 = automatic, n = at most n; either way reduced to
+    // what dpart_elems holds.
+    float* dpart = nullptr; int64_t dpart_elems = 0;
+    int splits = 0;
 };
-// Scratch bytes of attn_bwd (dsum, do16, amax) and their carving from one
-// 256-byte-aligned block.
-int64_t attn_bwd_work_bytes(int B, int S, int Hq, int hd);
-void attn_bwd_carve(void* work, int B, int S, int Hq, int hd, AttnBwdArgs& a);
+// Query-head splits the dK/dV pass takes for a shape: automatic (req 0:
+// enough blocks for two per CU, at most Hq/Hkv) or at most req, reduced to
+// fit part_elems floats (ns * B*S * 2*Hkv*hd).
+int attn_dkdv_splits(int B, int S, int Hq, int Hkv, int hd, int64_t part_elems, int req);
+// Floats of partials the automatic split needs (0 without a split).
+int64_t attn_bwd_part_elems(int B, int S, int Hq, int Hkv, int hd);
+// Scratch bytes of attn_bwd (dsum, do16, amax, and the partials of the
+// automatic split) and their carving from one 256-byte-aligned block.
+int64_t attn_bwd_work_bytes(int B, int S, int Hq, int Hkv, int hd);
+void attn_bwd_carve(void* work, int B, int S, int Hq, int Hkv, int hd, AttnBwdArgs& a);
 hipError_t attn_bwd(const AttnBwdArgs& a, hipStream_t s);
 
 // ------------------------------------------------------- Cross-entropy ----

@@ -53,7 +53,8 @@ class mt_stats(C.Structure):
                 ("site_ms", C.c_double * MT_MAX_SITES), ("site_launches", C.c_uint64 * MT_MAX_SITES),
                 ("fp16_saturated", C.c_uint64), ("compute_union_ms", C.c_double),
                 ("copy_union_ms", C.c_double), ("overlap_ms", C.c_double), ("switch_gap_ms", C.c_double * 3),
-                ("device_idle_ms", C.c_double * 3)]
+                ("device_idle_ms", C.c_double * 3), ("h2d_idle_ms", C.c_double * 9),
+                ("ready_switch_ms", C.c_double * 2), ("ready_switches", C.c_int32), ("switches", C.c_int32)]
 
 
 class mt_tensor_info(C.Structure):
@@ -101,9 +102,10 @@ _SIGS = {
     "mt_k_swiglu_bwd": (C.c_int, [_P, _P, _P, C.c_int32, C.c_int32, _P]),
     "mt_k_attn_fwd": (C.c_int, [_P, C.c_int64, _P, C.c_int64, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                 C.c_int32, _P, _P]),
-    "mt_k_attn_bwd_work_bytes": (C.c_int64, [C.c_int32, C.c_int32, C.c_int32, C.c_int32]),
+    "mt_k_attn_bwd_work_bytes": (C.c_int64, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32]),
+    "mt_k_attn_dkdv_splits": (C.c_int32, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32]),
     "mt_k_attn_bwd": (C.c_int, [_P, C.c_int64, _P, _P, C.c_int64, _P, _P, _P, C.c_int64, C.c_int32, C.c_int32,
-                                C.c_int32, C.c_int32, C.c_int32, _P, C.c_int64, _P, _P]),
+                                C.c_int32, C.c_int32, C.c_int32, _P, C.c_int64, C.c_int32, _P, _P]),
     "mt_k_rope_f32_bf16": (C.c_int, [_P, C.c_int64, _P, C.c_int64, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                      C.c_float, C.c_int32, _P]),
     "mt_k_ce": (C.c_int, [_P, _P, _P, _P, C.c_int32, C.c_int32, C.c_float, _P]),
@@ -276,7 +278,8 @@ class Context:
 
 def stats_dict(st):
     names = site_names()
-    arrays = ("overlap_phase", "exposed_transfer_ms", "switch_gap_ms", "device_idle_ms")
+    arrays = ("overlap_phase", "exposed_transfer_ms", "switch_gap_ms", "device_idle_ms", "h2d_idle_ms",
+              "ready_switch_ms")
     d = {k: getattr(st, k) for k, _ in mt_stats._fields_ if k not in ("site_ms", "site_launches") + arrays}
     for k in arrays:
         d[k] = list(getattr(st, k))

@@ -85,13 +85,13 @@ def test_attention_long_context_sampled():
     d_do = dev_bits(dout)
     d_o = dev_zeros_bits((S, nq))
     lse = torch.zeros(Hq * S, dtype=torch.float32, device="cuda")
-    work = torch.zeros(int(mt.lib.mt_k_attn_bwd_work_bytes(B, S, Hq, hd)), dtype=torch.uint8, device="cuda")
+    work = torch.zeros(int(mt.lib.mt_k_attn_bwd_work_bytes(B, S, Hq, Hkv, hd)), dtype=torch.uint8, device="cuda")
     d_dqkv = dev_zeros_bits((S, ld))
     s = torch.cuda.current_stream().cuda_stream
     mt.check(mt.lib.mt_k_attn_fwd(d_qkv.data_ptr(), ld, d_o.data_ptr(), nq, lse.data_ptr(), B, S, Hq, Hkv, hd,
                                   None, s))
     mt.check(mt.lib.mt_k_attn_bwd(d_qkv.data_ptr(), ld, d_o.data_ptr(), d_do.data_ptr(), nq, lse.data_ptr(),
-                                  work.data_ptr(), d_dqkv.data_ptr(), ld, B, S, Hq, Hkv, hd, None, 0, None, s))
+                                  work.data_ptr(), d_dqkv.data_ptr(), ld, B, S, Hq, Hkv, hd, None, 0, 0, None, s))
     torch.cuda.synchronize()
     o_g = host_f16(d_o).reshape(S, Hq, hd)
     g_g = host_f32(d_dqkv).reshape(S, Hq + 2 * Hkv, hd)

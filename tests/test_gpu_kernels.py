@@ -489,8 +489,33 @@ def test_attention_bwd_scale_follows_gradient_size(do_std):
     _attention_case(2, 130, 4, 2, 128, 1.0, True, do_std=do_std)
 
 
-def _attention_case(B, S, Hq, Hkv, hd, qk_std, f32_out, do_std=1.0):
-    log(f"attention B={B} S={S} Hq={Hq} Hkv={Hkv} hd={hd} qk_std={qk_std} f32_out={f32_out} do_std={do_std}")
+@pytest.mark.parametrize("B,S,Hq,Hkv,hd,splits,taken", [(1, 300, 7, 1, 128, 1, 1), (1, 300, 7, 1, 128, 3, 3),
+                                                         (1, 1024, 28, 4, 128, 1, 1), (2, 200, 4, 2, 64, 1, 1),
+                                                         (1, 1024, 28, 4, 128, 0, 7), (2, 200, 4, 2, 64, 0, 2)])
+def test_attention_dkdv_head_split(B, S, Hq, Hkv, hd, splits, taken):
+    """The dK/dV pass with each KV group's query heads split over several
+    blocks (fp32 partials added in split order; 3 of 7 heads is uneven) and
+    without a split: both against the oracle."""
+    assert mt.lib.mt_k_attn_dkdv_splits(B, S, Hq, Hkv, hd, splits) == taken
+    _attention_case(B, S, Hq, Hkv, hd, 1.0, True, splits=splits)
+
+
+def test_attention_dkdv_split_count_rule():
+    """Automatic splits: none once there are 512 key-tile blocks, else enough
+    for 512, at most Hq/Hkv; an explicit count is capped by the group."""
+    sp = mt.lib.mt_k_attn_dkdv_splits
+    assert sp(8, 1024, 28, 4, 128, 0) == 2          # 256 key-tile blocks
+    assert sp(4, 2048, 64, 8, 128, 0) == 1          # 512
+    assert sp(1, 131072, 28, 4, 128, 0) == 1
+    assert sp(1, 100, 7, 1, 128, 0) == 7
+    assert sp(1, 100, 7, 1, 128, 9) == 7
+    assert sp(1, 100, 4, 4, 128, 0) == 1            # one query head per group
+    assert sp(1, 100, 6, 4, 128, 0) == 0            # not a grouping
+
+
+def _attention_case(B, S, Hq, Hkv, hd, qk_std, f32_out, do_std=1.0, splits=0):
+    log(f"attention B={B} S={S} Hq={Hq} Hkv={Hkv} hd={hd} qk_std={qk_std} f32_out={f32_out} do_std={do_std} "
+        f"splits={splits}")
     T = B * S
     ld = (Hq + 2 * Hkv) * hd
     nq, nr = Hq * hd, (Hq + Hkv) * hd
@@ -499,7 +524,7 @@ def _attention_case(B, S, Hq, Hkv, hd, qk_std, f32_out, do_std=1.0):
     d_do = dev_bits(dout)
     d_o = dev_zeros_bits((T, nq))
     lse = torch.zeros(B * Hq * S, dtype=torch.float32, device="cuda")
-    work = torch.zeros(int(mt.lib.mt_k_attn_bwd_work_bytes(B, S, Hq, hd)), dtype=torch.uint8, device="cuda")
+    work = torch.zeros(int(mt.lib.mt_k_attn_bwd_work_bytes(B, S, Hq, Hkv, hd)), dtype=torch.uint8, device="cuda")
     d_dqkv = dev_zeros_bits((T, ld))
     dqk32 = torch.zeros((T, nr), dtype=torch.float32, device="cuda") if f32_out else None
     ovf = torch.zeros(4, dtype=torch.int32, device="cuda")
@@ -508,7 +533,8 @@ def _attention_case(B, S, Hq, Hkv, hd, qk_std, f32_out, do_std=1.0):
                                   ovf.data_ptr(), s))
     mt.check(mt.lib.mt_k_attn_bwd(d_qkv.data_ptr(), ld, d_o.data_ptr(), d_do.data_ptr(), nq, lse.data_ptr(),
                                   work.data_ptr(), d_dqkv.data_ptr(), ld, B, S, Hq, Hkv, hd,
-                                  dqk32.data_ptr() if f32_out else None, nr if f32_out else 0, ovf.data_ptr(), s))
+                                  dqk32.data_ptr() if f32_out else None, nr if f32_out else 0, splits,
+                                  ovf.data_ptr(), s))
     _sync()
     assert ovf[0].item() == 0
     x = qkv.astype(np.float64).reshape(B, S, Hq + 2 * Hkv, hd)
