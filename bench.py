@@ -323,7 +323,10 @@ def cpu_baseline(ctx, cfg, mt):
     one decoder layer (forward, recompute, backward) and the LM head at
     B=1 x S=1024 tokens of the workload's shapes, and Adam over a 16M-element
     slice; extrapolate to the full step (L layers, head, Adam over all
-    parameters) in the metric's unit."""
+    parameters) in the metric's unit.  For sequences longer than 4096 the
+    layer's attention terms grow with S^2: the layer is timed at S = 1024 and
+    2048 and t(S) = a S + b S^2 is fitted through the two points and
+    evaluated at the workload's length."""
     from oracle import step as ostep
     from layer_streaming_amd import synth
     sh = ostep.Shape(cfg["n_layers"], cfg["d_model"], cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"],
@@ -332,35 +335,50 @@ def cpu_baseline(ctx, cfg, mt):
     w = {n: widen(ctx.get_tensor(0, j, mt.MT_W)) for j, n in enumerate(ostep.LAYER_TENSORS)}
     L = cfg["n_layers"]
     hw = {n: widen(ctx.get_tensor(L, j, mt.MT_W)) for j, n in enumerate(ostep.HEAD_TENSORS)}
-    Bs, Ss = 1, min(1024, cfg["seq"])
-    Ts = Bs * Ss
     rng = np.random.default_rng(0)
-    x = rng.standard_normal((Ts, sh.d_model)) * 0.02
-    dy = rng.standard_normal((Ts, sh.d_model)) * 1e-4
-    _, labels = synth.tokens_labels(synth.SEED_TOKENS, Bs, Ss, sh.vocab)
-    t0 = time.perf_counter()
-    ostep.layer_fwd(x, w, sh, Bs, Ss)                     # forward
-    _, c = ostep.layer_fwd(x, w, sh, Bs, Ss)              # recompute
-    ostep.layer_bwd(dy, c, w, sh, Bs, Ss)                 # backward
-    t_layer = time.perf_counter() - t0
-    log(f"cpu oracle: layer fwd+recompute+bwd at T={Ts}: {t_layer:.2f} s")
+
+    def time_layer(Ss):
+        x = rng.standard_normal((Ss, sh.d_model)) * 0.02
+        dy = rng.standard_normal((Ss, sh.d_model)) * 1e-4
+        t0 = time.perf_counter()
+        ostep.layer_fwd(x, w, sh, 1, Ss)                     # forward
+        _, c = ostep.layer_fwd(x, w, sh, 1, Ss)              # recompute
+        ostep.layer_bwd(dy, c, w, sh, 1, Ss)                 # backward
+        t = time.perf_counter() - t0
+        log(f"cpu oracle: layer fwd+recompute+bwd at 1x{Ss}: {t:.2f} s")
+        return t
+
+    B, S = cfg["batch"], cfg["seq"]
+    T = B * S
+    Sh = min(1024, S)
+    if S > 4096:
+        (S1, t1), (S2, t2) = [(s_, time_layer(s_)) for s_ in (1024, 2048)]
+        b = (t2 / S2 - t1 / S1) / (S2 - S1)
+        a = t1 / S1 - b * S1
+        t_layers = L * B * (a * S + b * S * S)
+        how = (f"one decoder layer (fwd, recompute, bwd) at 1x1024 and 1x2048 tokens, fitted as a*S + b*S^2 "
+               f"(a = {a:.3e} s, b = {b:.3e} s) and evaluated at S = {S}; the LM head at 1x{Sh} tokens scaled to "
+               f"{T}")
+    else:
+        t_layers = L * time_layer(Sh) * (T / Sh)
+        how = f"one decoder layer (fwd, recompute, bwd) and the LM head at 1x{Sh} tokens, scaled to {T} tokens"
+    x = rng.standard_normal((Sh, sh.d_model)) * 0.02
+    _, labels = synth.tokens_labels(synth.SEED_TOKENS, 1, Sh, sh.vocab)
     t0 = time.perf_counter()
     ostep.head_fwd_bwd(x, hw, labels.reshape(-1), sh)
     t_head = time.perf_counter() - t0
-    log(f"cpu oracle: head fwd+bwd at T={Ts}: {t_head:.2f} s")
+    log(f"cpu oracle: head fwd+bwd at T={Sh}: {t_head:.2f} s")
     n = 1 << 24
     st = [rng.standard_normal(n).astype(np.float32) for _ in range(4)]
     t0 = time.perf_counter()
     ostep.adam_update(st[0], st[1], np.abs(st[2]), st[3], 1, 1e-4, 0.9, 0.999, 1e-8)
     t_adam = (time.perf_counter() - t0) * sh.n_params() / n
     log(f"cpu oracle: Adam over {sh.n_params() / 1e9:.2f}B params (from a {n} sample): {t_adam:.2f} s")
-    T = cfg["batch"] * cfg["seq"]
-    t_step = (L * t_layer + t_head) * (T / Ts) + t_adam
+    t_step = t_layers + t_head * (T / Sh) + t_adam
     cores = len(os.sched_getaffinity(0))
     return {"value": T / t_step, "unit": "tokens/s", "cores": cores, "kind": "oracle", "host": host_info(),
-            "sample": f"float64 numpy oracle: one decoder layer (fwd, recompute, bwd) and the LM head at 1x{Ss} "
-                      f"tokens, Adam over a 16M-element slice; step extrapolated as L*layer + head scaled to "
-                      f"{T} tokens + Adam over all parameters ({t_step:.1f} s per step)"}
+            "sample": f"float64 numpy oracle: {how}; Adam over a 16M-element slice scaled to all parameters; "
+                      f"step extrapolated as L layers + head + Adam ({t_step:.1f} s per step)"}
 
 
 def step_batches(cfg, n_micro, k):

@@ -76,7 +76,24 @@ __device__ __forceinline__ void dma16(i32x4_t rs, uint32_t lds_addr, uint32_t vo
                  : "s"(lds_addr), "v"(voff), "s"(rs)
                  : "memory");
 }
+// 4 bytes per lane into LDS at lds_addr + 4 * lane (as dma16).
+__device__ __forceinline__ void dma4(i32x4_t rs, uint32_t lds_addr, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_addr), "v"(voff), "s"(rs)
+                 : "memory");
+}
 __device__ __forceinline__ void wait_vmem0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N of this wave's vector-memory operations are in flight
+// (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    else static_assert(N < 0, "unsupported count");
+}
 // Block barrier after this wave's loads landed (vmcnt) and its LDS reads
 // completed (lgkmcnt through the builtin, so the compiler knows).
 __device__ __forceinline__ void barrier_tile() {
@@ -559,32 +576,36 @@ __global__ __launch_bounds__(256, 2) void attn_dq_k(AttnBwdArgs a, int n_qt) {
 // dK, dV: block = 8 waves over 128 keys of one (b, kv head), looping over
 // 64-query tiles of the group's query heads (or, split ns ways, of the
 // split's share of them), head by head, each from the block's diagonal to
-// the end of the sequence.  The work of a key tile shrinks with its
-// position (causal), so blocks go out heaviest first when kt_slow (key tile
-// the slowest index), else key tiles of one (b, kv head) in a row.  With
-// ns > 1 each block writes its fp32 partial sums, which attn_dkdv_reduce_k
-// adds in split order.  Waves w and w+4 (one SIMD) share keys
-// k0 + 32 w ..+31 and split each tile's work: the score wave (w < 4) holds K
-// for its keys, forms S = Q K^T and P, hands P (fp32) to its partner through
-// LDS and accumulates dV += P^T dO; the gradient wave holds V, forms
-// dP = dO V^T and, after a barrier, dS = P (dP - D) and dK += dS^T Q.  Each
-// wave keeps one accumulator set, so the kernel fits 256 registers (two
-// waves per SIMD) and one wave's exponentials and conversions run beside the
-// other's products.  The score waves stage the Q tiles, the gradient waves
-// the dO tiles.
+// the end of the sequence.  The work of a key tile shrinks with its position
+// (causal), so blocks go out heaviest first when kt_slow (key tile the
+// slowest index), else key tiles of one (b, kv head) in a row.  With ns > 1
+// each block writes its fp32 partial sums, which attn_dkdv_reduce_k adds in
+// split order.
+//
+// Waves w and w+4 (one SIMD) share keys k0 + 32 w ..+31 and work as a
+// two-stage pipeline over half tiles of 32 queries.  The front wave (w < 4)
+// holds K and V of its keys, forms S = Q K^T and dP = dO V^T for half h,
+// then P and dS = P (dP - D) in fp32, and hands both over through LDS in the
+// fp16 form the products take.  The back wave accumulates dV += P^T dO and
+// dK += dS^T Q for half h - 1 meanwhile, so one barrier per half tile
+// separates the stages and each SIMD always has one wave's products beside
+// the other's exponentials.  Q and dO tiles sit in three LDS buffers: a tile
+// is used by the front wave in two phases and by the back wave one phase
+// later, and its successor's loads are issued three phases before it is
+// needed; the log-sum-exp and D rows come in with the same direct loads.
 template <int HD>
 __global__ __launch_bounds__(512, 1) void attn_dkdv_k(AttnBwdArgs a, int n_kt, int ns, int kt_slow) {
     constexpr int NS = HD / 16, ND = HD / 32, NCH = HD / 8;
     constexpr int TILE = BKV * NCH, NI = TILE / 256;
-    __shared__ uint4 Qs[2][TILE];
-    __shared__ uint4 Ds[2][TILE];
-    __shared__ __align__(16) float Ls[2][BKV];
-    __shared__ __align__(16) float Dd[2][BKV];
-    __shared__ float4 Px[4][8][64];  // per key group: lane l's 32 probabilities as 8 float4
+    __shared__ uint4 Qs[3][TILE];
+    __shared__ uint4 Ds[3][TILE];
+    __shared__ __align__(16) float Ls[3][BKV];
+    __shared__ __align__(16) float Dd[3][BKV];
+    __shared__ uint4 Xh[2][4][4][64];  // per half tile and key group: P (s2 = 0, 1) and dS (s2 = 0, 1) per lane
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int pw = wave & 3;
-    const bool sw = wave < 4;
+    const bool front = wave < 4;
     const int hh = lane >> 5, c = lane & 31;
     int kt, bk;
     const int split = int(blockIdx.x % unsigned(ns));
@@ -604,193 +625,191 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_k(AttnBwdArgs a, int n_kt, i
     const int kcol = (a.Hq + hk) * HD, vcol = (a.Hq + a.Hkv + hk) * HD;
     const float s2k = grad_scale(a.amax, HD);
 
-    // K (score wave) or V (gradient wave) of the wave's keys: the B operand
-    f16x8_t kv[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (key < S) v = *reinterpret_cast<const uint4*>(base + int64_t(key) * a.ld + (sw ? kcol : vcol) + (2 * s + hh) * 8);
-        kv[s] = as_f16x8(v);
-    }
+    const int qb0 = k0 / BKV;
+    const int nqb = (S + BKV - 1) / BKV - qb0;  // query tiles per head
+    const int tt = nqb * ng;                     // tiles: head h_lo + j / nqb, query tile qb0 + j % nqb
 
     uint32_t off[NI];
-    tile_offsets<HD>(off, pw, lane, sw ? a.ld : ldg);
-    float lreg = 0.f, dreg = 0.f;
-    auto issue = [&](int hq, int q0, int buf) {
-        if (sw) tile_issue<HD>(base + int64_t(q0) * a.ld + hq * HD, a.ld, S - q0, off, lds_addr(&Qs[buf][0]), pw);
+    tile_offsets<HD>(off, pw, lane, front ? a.ld : ldg);
+    int last_issued = -1;
+    auto issue_tile = [&](int j) {  // tile j into buffer j % 3
+        const int hq = h_lo + j / nqb, q0 = (qb0 + j % nqb) * BKV, buf = j % 3;
+        if (front) tile_issue<HD>(base + int64_t(q0) * a.ld + hq * HD, a.ld, S - q0, off, lds_addr(&Qs[buf][0]), pw);
         else tile_issue<HD>(gbase + int64_t(q0) * ldg + hq * HD, ldg, S - q0, off, lds_addr(&Ds[buf][0]), pw);
-        if (tid < BKV) {
-            const int64_t o = (int64_t(b) * a.Hq + hq) * S;
-            const int qq = q0 + tid;
-            lreg = qq < S ? a.lse[o + qq] * LOG2E : 0.f;
-            dreg = qq < S ? a.dsum[o + qq] : 0.f;
+        if (wave == 0) {
+            const int64_t o = (int64_t(b) * a.Hq + hq) * S + q0;
+            const uint32_t ext = uint32_t(min(BKV, S - q0)) * 4u;
+            dma4(make_rsrc(a.lse + o, ext), __builtin_amdgcn_readfirstlane(lds_addr(&Ls[buf][0])), uint32_t(lane) * 4u);
+            dma4(make_rsrc(a.dsum + o, ext), __builtin_amdgcn_readfirstlane(lds_addr(&Dd[buf][0])), uint32_t(lane) * 4u);
         }
+        last_issued = j;
     };
-
-    f32x16_t acc[ND];  // dV (score wave) or dK (gradient wave), transposed: rows = head dim, lane = key
-#pragma unroll
-    for (int i = 0; i < ND; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
-    const float sc = LOG2E * rsqrtf(float(HD));
-
-    const int qb0 = k0 / BKV;
-    const int nqb = (S + BKV - 1) / BKV - qb0;  // per head
-    const int total = nqb * ng;
-    if (total > 0) {
-        issue(h_lo, qb0 * BKV, 0);
-        if (tid < BKV) {
-            Ls[0][tid] = lreg;
-            Dd[0][tid] = dreg;
+    // End of a phase: this wave's LDS traffic done, and every tile up to
+    // `need` landed (only a newer tile's loads may still be in flight).
+    auto phase_end = [&](int need) {
+        if (last_issued > need) {
+            if (wave == 0) wait_vmem<NI + 2>();
+            else wait_vmem<NI>();
+        } else {
+            wait_vmem<0>();
         }
-    }
-    barrier_tile();
-    for (int it = 0; it < total; ++it) {
-        const int cur = it & 1;
-        const int q0 = (qb0 + it % nqb) * BKV;
-        if (it + 1 < total) issue(h_lo + (it + 1) / nqb, (qb0 + (it + 1) % nqb) * BKV, cur ^ 1);
-        // some query of the tile at or after one of the wave's keys
-        const bool live = kw <= q0 + BKV - 1;
-        const bool full = kw + 31 <= q0 && q0 + BKV <= S && kw + 32 <= S;
-        const uint4* At = sw ? Qs[cur] : Ds[cur];
-        f32x16_t st[2];  // S (score wave) or dP (gradient wave): rows = queries, lane = key
-        if (live) {
-            // fragments read PA - 1 k-steps ahead of their products
-            constexpr int PA = 3;
-            uint4 fa[PA][2];
-            auto rd = [&](int s, uint4(&f)[2]) {
-#pragma unroll
-                for (int t = 0; t < 2; ++t) f[t] = tile_row<HD>(At, 32 * t + c, 2 * s + hh);
-            };
-            static_for_n<PA - 1>([&](auto s_) { rd(decltype(s_)::value, fa[decltype(s_)::value]); });
-            static_for_n<NS>([&](auto s_) {
-                constexpr int s = decltype(s_)::value;
-                if constexpr (s + PA - 1 < NS) rd(s + PA - 1, fa[(s + PA - 1) % PA]);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    st[t] = MFMA32H(as_f16x8(fa[s % PA][t]), kv[s], s == 0 ? f32x16_t{} : st[t]);
-                __builtin_amdgcn_sched_barrier(0);
-            });
-        }
-        f16x8_t op[2][2];  // P (score wave) or dS (gradient wave) as the fp16 B operand
-        if (sw && live) {
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    float tp[8];
-#pragma unroll
-                    for (int g4 = 0; g4 < 2; ++g4) {
-                        const int qb = 32 * t + 8 * (2 * s2 + g4) + 4 * hh;
-                        float lv[4];
-                        *reinterpret_cast<float4*>(lv) = *reinterpret_cast<const float4*>(&Ls[cur][qb]);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int j = 4 * g4 + e, r = 8 * s2 + j;
-                            float p = ex2(fmaf(st[t][r], sc, -lv[e]));
-                            if (!full) {
-                                const int qq = q0 + qb + e;
-                                if (key > qq || qq >= S || key >= S) p = 0.f;
-                            }
-                            tp[j] = p;
-                        }
-                        Px[pw][4 * t + 2 * s2 + g4][lane] = make_float4(tp[4 * g4], tp[4 * g4 + 1], tp[4 * g4 + 2],
-                                                                        tp[4 * g4 + 3]);
-                    }
-                    op[t][s2] = pack_h8(tp);
-                }
-        }
-        // The first fragments of the dV (dK) products do not depend on P:
-        // read them now, so they land while the exponentials run.
-        const uint4* Bt = sw ? Ds[cur] : Qs[cur];
-        constexpr int PB = 4;
-        f16x8_t fb[PB];
-        if (live)
-            static_for_n<PB - 1>([&](auto j_) {
-                constexpr int j = decltype(j_)::value;
-                fb[j] = tile_colT<HD>(Bt, j % ND, j / ND / 2, (j / ND) % 2, lane);
-            });
-        // P is in LDS (the next tile's loads stay in flight)
         __builtin_amdgcn_s_waitcnt(0xC07F);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (live) {
-            if (!sw) {
+    };
+    // Phase p: the front wave works on half tile p, the back wave on p - 1;
+    // the tile two ahead of the front wave's is issued on odd phases.  Both
+    // loops below run the same phases and barriers.
+    auto next_tile = [&](int p) {
+        if ((p & 1) && (p + 3) / 2 < tt) issue_tile((p + 3) / 2);
+    };
+
+    issue_tile(0);
+    if (tt > 1) issue_tile(1);
+    phase_end(0);
+    if (front) {
+        // K and V of the wave's keys: the B operands of S and dP.
+        f16x8_t kf[NS], vf[NS];
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2) {
-                        float td[8];
-#pragma unroll
-                        for (int g4 = 0; g4 < 2; ++g4) {
-                            const int qb = 32 * t + 8 * (2 * s2 + g4) + 4 * hh;
-                            float dv4[4];
-                            *reinterpret_cast<float4*>(dv4) = *reinterpret_cast<const float4*>(&Dd[cur][qb]);
-                            const float4 pv = Px[pw][4 * t + 2 * s2 + g4][lane];
-                            const float pp[4] = {pv.x, pv.y, pv.z, pv.w};
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const int j = 4 * g4 + e;
-                                td[j] = pp[e] * (st[t][8 * s2 + j] - dv4[e]);
-                            }
-                        }
-                        op[t][s2] = pack_h8(td);
-                    }
+        for (int s = 0; s < NS; ++s) {
+            uint4 u = make_uint4(0, 0, 0, 0), v = u;
+            if (key < S) {
+                u = *reinterpret_cast<const uint4*>(base + int64_t(key) * a.ld + kcol + (2 * s + hh) * 8);
+                v = *reinterpret_cast<const uint4*>(base + int64_t(key) * a.ld + vcol + (2 * s + hh) * 8);
             }
-            // dV (or dK) over the tile's 64 queries: the four accumulators
-            // take turns, and each transposed fragment is read PB - 1
-            // products ahead of its MFMA.
-            static_for_n<4 * ND>([&](auto i_) {
-                constexpr int i = decltype(i_)::value;
-                constexpr int dt = i % ND, t = i / ND / 2, s2 = (i / ND) % 2;
-                if constexpr (i + PB - 1 < 4 * ND) {
-                    constexpr int j = i + PB - 1;
-                    fb[j % PB] = tile_colT<HD>(Bt, j % ND, j / ND / 2, (j / ND) % 2, lane);
+            kf[s] = as_f16x8(u);
+            vf[s] = as_f16x8(v);
+        }
+        const float sc = LOG2E * rsqrtf(float(HD));
+        for (int p = 0; p <= 2 * tt; ++p) {
+            next_tile(p);
+            const int h = p;
+            const int j = h >> 1, t = h & 1, buf = j % 3;
+            const int q0 = (qb0 + j % nqb) * BKV, qh = q0 + 32 * t;
+            // some query of the half at or after one of the pair's keys
+            if (h < 2 * tt && kw <= qh + 31) {
+                uint4* X = &Xh[h & 1][pw][0][0];
+                f32x16_t st, dp;
+                constexpr int PA = 3;
+                uint4 fa[PA][2];
+                auto rd = [&](int s, uint4(&f)[2]) {
+                    f[0] = tile_row<HD>(Qs[buf], 32 * t + c, 2 * s + hh);
+                    f[1] = tile_row<HD>(Ds[buf], 32 * t + c, 2 * s + hh);
+                };
+                static_for_n<PA - 1>([&](auto s_) { rd(decltype(s_)::value, fa[decltype(s_)::value]); });
+                static_for_n<NS>([&](auto s_) {
+                    constexpr int s = decltype(s_)::value;
+                    if constexpr (s + PA - 1 < NS) rd(s + PA - 1, fa[(s + PA - 1) % PA]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    st = MFMA32H(as_f16x8(fa[s % PA][0]), kf[s], s == 0 ? f32x16_t{} : st);
+                    dp = MFMA32H(as_f16x8(fa[s % PA][1]), vf[s], s == 0 ? f32x16_t{} : dp);
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+                const bool full = kw + 31 <= qh && qh + 32 <= S && kw + 32 <= S;
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    float tp[8], td[8];
+#pragma unroll
+                    for (int g4 = 0; g4 < 2; ++g4) {
+                        const int qb = 32 * t + 8 * (2 * s2 + g4) + 4 * hh;  // query within the tile
+                        float lv[4], dv4[4];
+                        *reinterpret_cast<float4*>(lv) = *reinterpret_cast<const float4*>(&Ls[buf][qb]);
+                        *reinterpret_cast<float4*>(dv4) = *reinterpret_cast<const float4*>(&Dd[buf][qb]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int jj = 4 * g4 + e, r = 8 * s2 + jj;
+                            float pr = ex2(fmaf(st[r], sc, -lv[e] * LOG2E));
+                            if (!full) {
+                                const int qq = q0 + qb + e;
+                                if (key > qq || qq >= S || key >= S) pr = 0.f;
+                            }
+                            tp[jj] = pr;
+                            td[jj] = pr * (dp[r] - dv4[e]);
+                        }
+                    }
+                    X[s2 * 64 + lane] = __builtin_bit_cast(uint4, pack_h8(tp));
+                    X[(2 + s2) * 64 + lane] = __builtin_bit_cast(uint4, pack_h8(td));
                 }
-                __builtin_amdgcn_sched_barrier(0);
-                acc[dt] = MFMA32H(fb[i % PB], op[t][s2], acc[dt]);
-                __builtin_amdgcn_sched_barrier(0);
-            });
+            }
+            phase_end((p + 1) >> 1);
         }
-        if (it + 1 < total && tid < BKV) {
-            Ls[cur ^ 1][tid] = lreg;
-            Dd[cur ^ 1][tid] = dreg;
+        return;
+    }
+    f32x16_t acc_v[ND], acc_k[ND];  // dV and dK, transposed (rows = head dim, lane = key)
+#pragma unroll
+    for (int i = 0; i < ND; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            acc_v[i][r] = 0.f;
+            acc_k[i][r] = 0.f;
         }
-        barrier_tile();
+    for (int p = 0; p <= 2 * tt; ++p) {
+        next_tile(p);
+        const int h = p - 1;
+        if (h >= 0) {
+            const int j = h >> 1, t = h & 1, buf = j % 3;
+            const int qh = (qb0 + j % nqb) * BKV + 32 * t;
+            if (kw <= qh + 31) {
+                const uint4* X = &Xh[h & 1][pw][0][0];
+                f16x8_t op[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) op[i] = as_f16x8(X[i * 64 + lane]);
+                // dV += P^T dO and dK += dS^T Q over the half's 32 queries: the
+                // accumulators take turns; fragments read PB - 1 products ahead.
+                constexpr int NP = 4 * ND, PB = 4;
+                auto frag = [&](int i) {
+                    const int dt = (i >> 1) % ND, s2 = (i >> 1) / ND, k = i & 1;
+                    return tile_colT<HD>(k ? Qs[buf] : Ds[buf], dt, t, s2, lane);
+                };
+                f16x8_t fb[PB];
+                static_for_n<PB - 1>([&](auto i_) { fb[decltype(i_)::value] = frag(decltype(i_)::value); });
+                static_for_n<NP>([&](auto i_) {
+                    constexpr int i = decltype(i_)::value;
+                    constexpr int dt = (i >> 1) % ND, s2 = (i >> 1) / ND, k = i & 1;
+                    if constexpr (i + PB - 1 < NP) fb[(i + PB - 1) % PB] = frag(i + PB - 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (k) acc_k[dt] = MFMA32H(fb[i % PB], op[2 + s2], acc_k[dt]);
+                    else acc_v[dt] = MFMA32H(fb[i % PB], op[s2], acc_v[dt]);
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            }
+        }
+        phase_end((p + 1) >> 1);
     }
     if (key < S) {
-        const float inv = 1.0f / s2k, scale = sw ? inv : rsqrtf(float(HD)) * inv;
+        const float inv = 1.0f / s2k, scale = rsqrtf(float(HD)) * inv;
         const int64_t row = int64_t(b) * S + key;
         if (ns > 1) {
             const int64_t T = int64_t(a.B) * S, w = int64_t(a.Hkv) * HD;
-            float* prow = a.dpart + (int64_t(split) * T + row) * (2 * w) + hk * HD + (sw ? w : 0);
+            float* prow = a.dpart + (int64_t(split) * T + row) * (2 * w) + hk * HD;
 #pragma unroll
             for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    *reinterpret_cast<float4*>(prow + 32 * dt + 8 * g + 4 * hh) =
-                        make_float4(acc[dt][4 * g] * scale, acc[dt][4 * g + 1] * scale, acc[dt][4 * g + 2] * scale,
-                                    acc[dt][4 * g + 3] * scale);
-        } else if (sw) {
+                for (int g = 0; g < 4; ++g) {
+                    const int d = 32 * dt + 8 * g + 4 * hh;
+                    *reinterpret_cast<float4*>(prow + d) =
+                        make_float4(acc_k[dt][4 * g] * scale, acc_k[dt][4 * g + 1] * scale,
+                                    acc_k[dt][4 * g + 2] * scale, acc_k[dt][4 * g + 3] * scale);
+                    *reinterpret_cast<float4*>(prow + w + d) =
+                        make_float4(acc_v[dt][4 * g] * inv, acc_v[dt][4 * g + 1] * inv, acc_v[dt][4 * g + 2] * inv,
+                                    acc_v[dt][4 * g + 3] * inv);
+                }
+        } else {
+            float* r32 = a.dqk32 ? a.dqk32 + row * a.ld32 + (a.Hq + hk) * HD : nullptr;
+            uint16_t* rk = a.dqkv + row * a.ldd + kcol;
             uint16_t* rv = a.dqkv + row * a.ldd + vcol;
 #pragma unroll
             for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    *reinterpret_cast<uint2*>(rv + 32 * dt + 8 * g + 4 * hh) =
-                        make_uint2(pack2(acc[dt][4 * g] * scale, acc[dt][4 * g + 1] * scale),
-                                   pack2(acc[dt][4 * g + 2] * scale, acc[dt][4 * g + 3] * scale));
-        } else {
-            float* r32 = a.dqk32 ? a.dqk32 + row * a.ld32 + (a.Hq + hk) * HD : nullptr;
-            uint16_t* rk = a.dqkv + row * a.ldd + kcol;
-#pragma unroll
-            for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    store_grad4(r32, rk, 32 * dt + 8 * g + 4 * hh, acc[dt][4 * g] * scale,
-                                acc[dt][4 * g + 1] * scale, acc[dt][4 * g + 2] * scale, acc[dt][4 * g + 3] * scale);
+                for (int g = 0; g < 4; ++g) {
+                    const int d = 32 * dt + 8 * g + 4 * hh;
+                    store_grad4(r32, rk, d, acc_k[dt][4 * g] * scale, acc_k[dt][4 * g + 1] * scale,
+                                acc_k[dt][4 * g + 2] * scale, acc_k[dt][4 * g + 3] * scale);
+                    *reinterpret_cast<uint2*>(rv + d) =
+                        make_uint2(pack2(acc_v[dt][4 * g] * inv, acc_v[dt][4 * g + 1] * inv),
+                                   pack2(acc_v[dt][4 * g + 2] * inv, acc_v[dt][4 * g + 3] * inv));
+                }
         }
     }
 }
