@@ -318,6 +318,51 @@ def host_adam_probe(mt, n=256 << 20):
     return round(30 * n / best / 1e9, 1)
 
 
+def host_probe(mt):
+    """The host's DRAM against the host Adam: the library's Adam alone at 8,
+    12 and 16 threads (30 B/param), and a parallel copy and a parallel read
+    of 8 GB at 8 and 16 threads, as one JSON line."""
+    import ctypes
+    from concurrent.futures import ThreadPoolExecutor
+    out = {"cpus": len(os.sched_getaffinity(0)), "adam_GBps": {}, "copy_GBps": {}, "read_GBps": {}}
+    n = 512 << 20
+    w, g = np.zeros(n, np.uint16), np.zeros(n, np.uint16)
+    gs = np.full(n, 0x3A83, np.uint16)
+    ms, m, v = np.ones(n, np.float32), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    for th in (8, 12, 16):
+        best = 1e9
+        for _ in range(3):
+            t0 = time.perf_counter()
+            mt.check(mt.lib.mt_host_adam(w.ctypes.data, g.ctypes.data, ms.ctypes.data, m.ctypes.data,
+                                         v.ctypes.data, gs.ctypes.data, n, 1, 1e-4, 0.9, 0.999, 1e-8, th),
+                     "mt_host_adam")
+            best = min(best, time.perf_counter() - t0)
+        out["adam_GBps"][th] = round(30 * n / best / 1e9, 1)
+        log(f"host Adam, {th} threads: {out['adam_GBps'][th]} GB/s")
+    del w, g, gs, ms, m, v
+    nb = 8 << 30
+    src, dst = np.ones(nb, np.uint8), np.zeros(nb, np.uint8)
+    for th in (8, 16):
+        ch = nb // th
+
+        def cp(i):
+            ctypes.memmove(dst.ctypes.data + i * ch, src.ctypes.data + i * ch, ch)
+
+        def rd(i):
+            return int(src[i * ch:(i + 1) * ch].view(np.uint64).sum())
+        with ThreadPoolExecutor(th) as ex:
+            list(ex.map(cp, range(th)))
+            for name, fn, mult in (("copy_GBps", cp, 2), ("read_GBps", rd, 1)):
+                best = 1e9
+                for _ in range(3):
+                    t0 = time.perf_counter()
+                    list(ex.map(fn, range(th)))
+                    best = min(best, time.perf_counter() - t0)
+                out[name][th] = round(mult * nb / best / 1e9, 1)
+        log(f"copy (read + write) and read, {th} threads: {out['copy_GBps'][th]}, {out['read_GBps'][th]} GB/s")
+    print(json.dumps({"host_probe": out}), flush=True)
+
+
 def cpu_baseline(ctx, cfg, mt):
     """Time the oracle (float64 numpy, all host cores) on a bounded sample:
     one decoder layer (forward, recompute, backward) and the LM head at
@@ -549,6 +594,8 @@ def main():
     ap.add_argument("--attn-probe", type=int, default=0, metavar="S",
                     help="only time the attention kernels at sequences of length S with the workload's heads")
     ap.add_argument("--attn-batch", type=int, default=1, metavar="B", help="sequences in the attention probe")
+    ap.add_argument("--host-probe", action="store_true",
+                    help="only measure host DRAM: the host Adam alone at 8/12/16 threads, a parallel copy and read")
     ap.add_argument("--micro", type=int, default=1,
                     help="micro-batches of batch x seq per optimizer step (gradient accumulation on the host)")
     ap.add_argument("--cross-step", type=int, default=1,
@@ -568,6 +615,9 @@ def main():
     if args.layers:
         cfg["n_layers"] = args.layers
     cfg["workload"] = cfg["workload"].format(L=cfg["n_layers"])
+    if args.host_probe:
+        host_probe(mt)
+        return
     if args.traffic_probe:
         traffic_probe(torch, mt, cfg)
         return
