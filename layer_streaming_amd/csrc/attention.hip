@@ -184,7 +184,7 @@ __device__ __forceinline__ void static_for_n(F&& f) { static_for_from<0, N>(f); 
 // register set lets two blocks share a CU, so one wave's softmax runs while
 // the other's products do.
 template <int HD>
-__global__ __launch_bounds__(256, 2) void attn_fwd_k(AttnArgs a, int n_qt) {
+__global__ __launch_bounds__(256, 2) void attn_fwd_k(AttnArgs a, int n_qt, int qt_slow) {
     constexpr int NS = HD / 16, ND = HD / 32, NCH = HD / 8;
     constexpr int TILE = BKV * NCH;  // 16-byte chunks per tile
     constexpr int NI = TILE / 256;   // wave instructions per tile and operand
@@ -194,8 +194,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_k(AttnArgs a, int n_qt) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hh = lane >> 5, c = lane & 31;
-    const int qt = n_qt - 1 - int(blockIdx.x % n_qt);
-    const int bh = int(blockIdx.x / n_qt);
+    // Query tile heaviest first: across all (b, h) when qt_slow (up to 256
+    // tiles per head: the last blocks out are the lightest), else within each
+    // (b, h) (longer sequences: the blocks in flight share one head's K and V
+    // in L2; measured at S = 131072 the global order was 5% slower).
+    const int nbh = a.B * a.Hq;
+    const int qt = n_qt - 1 - (qt_slow ? int(blockIdx.x / unsigned(nbh)) : int(blockIdx.x % unsigned(n_qt)));
+    const int bh = qt_slow ? int(blockIdx.x % unsigned(nbh)) : int(blockIdx.x / unsigned(n_qt));
     const int h = bh % a.Hq, b = bh / a.Hq;
     const int hk = h / (a.Hq / a.Hkv);
     const int S = a.S;
@@ -445,7 +450,7 @@ __device__ __forceinline__ void store_grad4(float* f32row, uint16_t* b16row, int
 // fp16 K (rows for the scores, read transposed for dQ) and fp16 V (rows for
 // dP).
 template <int HD>
-__global__ __launch_bounds__(256, 2) void attn_dq_k(AttnBwdArgs a, int n_qt) {
+__global__ __launch_bounds__(256, 2) void attn_dq_k(AttnBwdArgs a, int n_qt, int qt_slow) {
     constexpr int NS = HD / 16, ND = HD / 32, NCH = HD / 8;
     constexpr int TILE = BKV * NCH, NI = TILE / 256;
     __shared__ uint4 Ks[2][TILE];
@@ -453,8 +458,13 @@ __global__ __launch_bounds__(256, 2) void attn_dq_k(AttnBwdArgs a, int n_qt) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hh = lane >> 5, c = lane & 31;
-    const int qt = n_qt - 1 - int(blockIdx.x % n_qt);
-    const int bh = int(blockIdx.x / n_qt);
+    // Query tile heaviest first: across all (b, h) when qt_slow (up to 256
+    // tiles per head: the last blocks out are the lightest), else within each
+    // (b, h) (longer sequences: the blocks in flight share one head's K and V
+    // in L2; measured at S = 131072 the global order was 5% slower).
+    const int nbh = a.B * a.Hq;
+    const int qt = n_qt - 1 - (qt_slow ? int(blockIdx.x / unsigned(nbh)) : int(blockIdx.x % unsigned(n_qt)));
+    const int bh = qt_slow ? int(blockIdx.x % unsigned(nbh)) : int(blockIdx.x / unsigned(n_qt));
     const int h = bh % a.Hq, b = bh / a.Hq;
     const int hk = h / (a.Hq / a.Hkv);
     const int S = a.S;
@@ -858,8 +868,9 @@ hipError_t attn_fwd(const AttnArgs& a, hipStream_t s) {
     if (!attn_shape_ok(a.B, a.S, a.Hq, a.Hkv, a.hd, a.ld, a.ldo)) return hipErrorInvalidValue;
     const int n_qt = (a.S + 127) / 128;
     const dim3 grid(unsigned(int64_t(n_qt) * a.B * a.Hq));
-    if (a.hd == 128) attn_fwd_k<128><<<grid, 256, 0, s>>>(a, n_qt);
-    else attn_fwd_k<64><<<grid, 256, 0, s>>>(a, n_qt);
+    const int qt_slow = n_qt <= 256;
+    if (a.hd == 128) attn_fwd_k<128><<<grid, 256, 0, s>>>(a, n_qt, qt_slow);
+    else attn_fwd_k<64><<<grid, 256, 0, s>>>(a, n_qt, qt_slow);
     return hipGetLastError();
 }
 
@@ -926,7 +937,7 @@ hipError_t attn_bwd(const AttnBwdArgs& a, hipStream_t s) {
         constexpr int HD = decltype(hd_)::value;
         attn_amax_k<HD><<<nb_do + nb_v, 256, 0, s>>>(a, nb_do);
         attn_prep_k<HD><<<np, 256, 0, s>>>(a);
-        attn_dq_k<HD><<<gq, 256, 0, s>>>(a, n_qt);
+        attn_dq_k<HD><<<gq, 256, 0, s>>>(a, n_qt, n_qt <= 256);
         attn_dkdv_k<HD><<<gk, 512, 0, s>>>(a, n_kt, ns, kt_slow);
     };
     if (a.hd == 128) run(std::integral_constant<int, 128>{});
