@@ -500,19 +500,6 @@ def test_attention_dkdv_head_split(B, S, Hq, Hkv, hd, splits, taken):
     _attention_case(B, S, Hq, Hkv, hd, 1.0, True, splits=splits)
 
 
-def test_attention_dkdv_split_count_rule():
-    """Automatic splits: none once there are 512 key-tile blocks, else enough
-    for 512, at most Hq/Hkv; an explicit count is capped by the group."""
-    sp = mt.lib.mt_k_attn_dkdv_splits
-    assert sp(8, 1024, 28, 4, 128, 0) == 2          # 256 key-tile blocks
-    assert sp(4, 2048, 64, 8, 128, 0) == 1          # 512
-    assert sp(1, 131072, 28, 4, 128, 0) == 1
-    assert sp(1, 100, 7, 1, 128, 0) == 7
-    assert sp(1, 100, 7, 1, 128, 9) == 7
-    assert sp(1, 100, 4, 4, 128, 0) == 1            # one query head per group
-    assert sp(1, 100, 6, 4, 128, 0) == 0            # not a grouping
-
-
 def _attention_case(B, S, Hq, Hkv, hd, qk_std, f32_out, do_std=1.0, splits=0):
     log(f"attention B={B} S={S} Hq={Hq} Hkv={Hkv} hd={hd} qk_std={qk_std} f32_out={f32_out} do_std={do_std} "
         f"splits={splits}")

@@ -292,3 +292,29 @@ def test_init_is_deterministic_across_thread_counts_and_statistically_normal():
             # normal, not uniform: kurtosis ~ 3
             k = np.mean((x - x.mean()) ** 4) / x.var() ** 2
             assert abs(k - 3.0) < 0.15
+
+
+def test_attention_dkdv_split_count_rule():
+    """Automatic splits: none once there are 512 key-tile blocks, else enough
+    for 512, at most Hq/Hkv; an explicit count is capped by the group."""
+    sp = mt.lib.mt_k_attn_dkdv_splits
+    assert sp(8, 1024, 28, 4, 128, 0) == 2          # 256 key-tile blocks
+    assert sp(4, 2048, 64, 8, 128, 0) == 1          # 512
+    assert sp(1, 131072, 28, 4, 128, 0) == 1
+    assert sp(1, 100, 7, 1, 128, 0) == 7
+    assert sp(1, 100, 7, 1, 128, 9) == 7
+    assert sp(1, 100, 4, 4, 128, 0) == 1            # one query head per group
+    assert sp(1, 100, 6, 4, 128, 0) == 0            # not a grouping
+
+
+def test_attention_backward_work_covers_the_automatic_split():
+    """The attention backward's scratch holds D, the scaled dO, the maxima and,
+    when the dK/dV pass splits, the fp32 partials of every split."""
+    al = lambda x: (x + 255) // 256 * 256
+    for B, S, Hq, Hkv, hd in [(8, 1024, 28, 4, 128), (1, 131072, 28, 4, 128), (1, 300, 7, 1, 64)]:
+        T = B * S
+        ns = mt.lib.mt_k_attn_dkdv_splits(B, S, Hq, Hkv, hd, 0)
+        part = ns * T * 2 * Hkv * hd if ns > 1 else 0
+        want = al(T * Hq * 4) + al(T * Hq * hd * 2) + 256 + al(part * 4)
+        assert mt.lib.mt_k_attn_bwd_work_bytes(B, S, Hq, Hkv, hd) == want
+    assert mt.lib.mt_k_attn_bwd_work_bytes(1, 100, 6, 4, 128) == 0   # not a grouping
