@@ -318,6 +318,29 @@ def host_adam_probe(mt, n=256 << 20):
     return round(30 * n / best / 1e9, 1)
 
 
+def pcie_probe(torch, nbytes=512 << 20):
+    """Pinned host <-> device copy rates on their own (best of 5, HIP events
+    on a side stream): the yardstick for the step's H2D and D2H rates."""
+    h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    d = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    st = torch.cuda.Stream()
+    out = {}
+    for name, fn in (("h2d", lambda: d.copy_(h, non_blocking=True)), ("d2h", lambda: h.copy_(d, non_blocking=True))):
+        best = 1e9
+        with torch.cuda.stream(st):
+            fn()
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(st)
+                fn()
+                e1.record(st)
+                e1.synchronize()
+                best = min(best, e0.elapsed_time(e1))
+        out[name] = round(nbytes / (best / 1e3) / 1e9, 1)
+    del h, d
+    return out
+
+
 def host_probe(mt):
     """The host's DRAM against the host Adam: the library's Adam alone at 8,
     12 and 16 threads (30 B/param), and a parallel copy and a parallel read
@@ -395,6 +418,28 @@ def cpu_baseline(ctx, cfg, mt):
 
     B, S = cfg["batch"], cfg["seq"]
     T = B * S
+    cores = len(os.sched_getaffinity(0))
+    if sh.n_params() < 100_000_000:
+        # a small model: the oracle's whole streamed step (gradients, BF16
+        # rounding, Adam over every tensor) on the workload's batch, median of 3
+        def unit(u, names):
+            return {n: {"w": widen(ctx.get_tensor(u, j, mt.MT_W)).astype(np.float32),
+                        "master": ctx.get_tensor(u, j, mt.MT_MASTER).copy(),
+                        "m": ctx.get_tensor(u, j, mt.MT_M).copy(), "v": ctx.get_tensor(u, j, mt.MT_V).copy()}
+                    for j, n in enumerate(names)}
+        store = {"layers": [unit(i, ostep.LAYER_TENSORS) for i in range(L)], "head": unit(L, ostep.HEAD_TENSORS),
+                 "e_in": unit(L + 1, ("e_in",))}
+        tokens, labels = synth.tokens_labels(synth.SEED_TOKENS, B, S, sh.vocab)
+        ts = []
+        for k in range(3):
+            t0 = time.perf_counter()
+            ostep.train_step(store, tokens, labels, sh, k + 1)
+            ts.append(time.perf_counter() - t0)
+        t_step = sorted(ts)[1]
+        log(f"cpu oracle: full step at {B}x{S}: {t_step:.3f} s (median of 3)")
+        return {"value": T / t_step, "unit": "tokens/s", "cores": cores, "kind": "oracle", "host": host_info(),
+                "sample": f"float64 numpy oracle: the whole streamed step at {B}x{S} (gradients, BF16 rounding, "
+                          f"Adam over every tensor), measured, median of 3 ({t_step:.3f} s per step)"}
     Sh = min(1024, S)
     if S > 4096:
         (S1, t1), (S2, t2) = [(s_, time_layer(s_)) for s_ in (1024, 2048)]
@@ -420,7 +465,6 @@ def cpu_baseline(ctx, cfg, mt):
     t_adam = (time.perf_counter() - t0) * sh.n_params() / n
     log(f"cpu oracle: Adam over {sh.n_params() / 1e9:.2f}B params (from a {n} sample): {t_adam:.2f} s")
     t_step = t_layers + t_head * (T / Sh) + t_adam
-    cores = len(os.sched_getaffinity(0))
     return {"value": T / t_step, "unit": "tokens/s", "cores": cores, "kind": "oracle", "host": host_info(),
             "sample": f"float64 numpy oracle: {how}; Adam over a 16M-element slice scaled to all parameters; "
                       f"step extrapolated as L layers + head + Adam ({t_step:.1f} s per step)"}
@@ -672,6 +716,10 @@ def main():
     out["host_memory"] = {"bytes_per_step": int(hb_step), "achieved_GBps": round(hb_step / (ms_per_step / 1e3) / 1e9, 1),
                           "adam_alone_GBps": host_adam_probe(mt)}
     out["pcie"] = pcie_block(stats)
+    probe = pcie_probe(torch)
+    out["pcie"]["probe_GBps"] = probe
+    if out["pcie"]["h2d_GBps"]:
+        out["pcie"]["h2d_frac_of_probe_while_busy"] = round(out["pcie"]["h2d_GBps"] / probe["h2d"], 3)
     out["phases_ms"] = {k: round(float(np.mean([s[k] for s in stats])), 1)
                         for k in ("fwd_ms", "head_ms", "bwd_ms", "adam_tail_ms", "compute_busy_ms",
                                   "adam_ms", "adam_wait_ms", "pack_ms")}
@@ -701,6 +749,15 @@ def main():
         hb = hbm_bytes(cfg, T)
         out["hbm_kernels_GBps"] = {k: round(hb[k] * sites[k][1] / (sites[k][0] / 1e3) / 1e9, 1)
                                    for k in hb if k in sites and sites[k][0] > 0}
+        if sites.get("head_ce", [0.0])[0] > 0:
+            # fp32 logits read by the forward (logsumexp) pass, read again and bf16 dlogits written by the
+            # backward pass of the chunked head; read once and dlogits written by the single-unit head
+            ce_b = T * cfg["vocab"] * (10 if args.head_vocab_chunk != 0 else 6) * nm * len(stats)
+            out["hbm_kernels_GBps"]["head_ce"] = round(ce_b / (sites["head_ce"][0] / 1e3) / 1e9, 1)
+        af = 4.0 * cfg["batch"] * cfg["n_heads"] * cfg["head_dim"] * cfg["seq"] * (cfg["seq"] + 1) / 2
+        out["attention_tflops"] = {k: round(f * sites[k][1] / (sites[k][0] / 1e3) / 1e12, 1)
+                                   for k, f in (("attn_fwd", af), ("attn_bwd", 2.5 * af))
+                                   if k in sites and sites[k][0] > 0}
         dom = "gemm_gateup"
         ms, n = sites[dom]
         avg_ms = ms / n
