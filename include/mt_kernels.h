@@ -112,8 +112,8 @@ int mt_k_attn_fwd(const void* qkv, int64_t ld, void* o, int64_t ldo, void* lse, 
  * enough blocks for two per CU; n: at most n; never more than Hq/Hkv or than
  * the work buffer's partials hold) and adds their fp32 partial sums in split
  * order.  work: device scratch of mt_k_attn_bwd_work_bytes(B, S, Hq, Hkv, hd)
- * bytes, 256-byte aligned (D, the scaled dO, the two maxima, the partials of
- * the automatic split); B*S*Hq*hd/8 < 2^31.  mt_k_attn_dkdv_splits: the
+ * bytes, 256-byte aligned (D and the base-2 log-sum-exp, the scaled dO, the
+ * two maxima, the partials of the automatic split); B*S*Hq*hd/8 < 2^31.  mt_k_attn_dkdv_splits: the
  * split count mt_k_attn_bwd takes with such a buffer (0 on a bad shape). */
 int64_t mt_k_attn_bwd_work_bytes(int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t hd);
 int32_t mt_k_attn_dkdv_splits(int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t hd, int32_t head_splits);

@@ -46,9 +46,14 @@ constexpr int BKV = 64;  // keys (or queries) per staged tile
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Pack eight fp32 values (probabilities, or scaled dS bounded by 2^15) into an
-// fp16 MFMA operand.
+// fp16 MFMA operand, round to nearest even: pairs through gfx950's
+// v_cvt_pk_f16_f32 (one instruction per two values).
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ f16x8_t pack_h8(const float* v) {
-    auto p = [](float a, float b) { return uint32_t(f2h(a)) | (uint32_t(f2h(b)) << 16); };
+    auto p = [](float a, float b) {
+        const f32x2_t f = {a, b};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
+    };
     return as_f16x8(make_uint4(p(v[0], v[1]), p(v[2], v[3]), p(v[4], v[5]), p(v[6], v[7])));
 }
 
@@ -398,7 +403,8 @@ __global__ __launch_bounds__(256) void attn_amax_k(AttnBwdArgs a, int nb_do) {
         atomicMax(a.amax + (is_do ? 0 : 1), __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
 }
 
-// D 2^k = rowsum(dO * O) 2^k (O fp16) into dsum, and dO 2^k in fp16 into
+// D 2^k = rowsum(dO * O) 2^k (O fp16) into dsum, the log-sum-exp in base 2
+// (lse log2 e) into its second half for the dK/dV kernel, and dO 2^k in fp16 into
 // do16 (range-guarded; the scale keeps it below 2^14).  One lane per 16-byte
 // chunk of a (token, query head) row: the HD/8 lanes of a row are adjacent,
 // so a wave instruction covers whole rows, and the row's dot product is
@@ -433,7 +439,9 @@ __global__ __launch_bounds__(256) void attn_prep_k(AttnBwdArgs a) {
     for (int o = L / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
     if (r < nrow && j == 0) {
         const uint32_t b = t / uint32_t(a.S), sq = t - b * uint32_t(a.S);
-        a.dsum[(int64_t(b) * a.Hq + h) * a.S + sq] = s * s2k;
+        const int64_t idx = (int64_t(b) * a.Hq + h) * a.S + sq;
+        a.dsum[idx] = s * s2k;
+        a.dsum[int64_t(nrow) + idx] = a.lse[idx] * LOG2E;
     }
     count_ovf(a.ovf, nov);
 }
@@ -649,7 +657,8 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_k(AttnBwdArgs a, int n_kt, i
         if (wave == 0) {
             const int64_t o = (int64_t(b) * a.Hq + hq) * S + q0;
             const uint32_t ext = uint32_t(min(BKV, S - q0)) * 4u;
-            dma4(make_rsrc(a.lse + o, ext), __builtin_amdgcn_readfirstlane(lds_addr(&Ls[buf][0])), uint32_t(lane) * 4u);
+            const float* lse2 = a.dsum + int64_t(a.B) * a.S * a.Hq;  // base-2 log-sum-exp, written by prep
+            dma4(make_rsrc(lse2 + o, ext), __builtin_amdgcn_readfirstlane(lds_addr(&Ls[buf][0])), uint32_t(lane) * 4u);
             dma4(make_rsrc(a.dsum + o, ext), __builtin_amdgcn_readfirstlane(lds_addr(&Dd[buf][0])), uint32_t(lane) * 4u);
         }
         last_issued = j;
@@ -729,7 +738,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_k(AttnBwdArgs a, int n_kt, i
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int jj = 4 * g4 + e, r = 8 * s2 + jj;
-                            float pr = ex2(fmaf(st[r], sc, -lv[e] * LOG2E));
+                            float pr = ex2(fmaf(st[r], sc, -lv[e]));
                             if (!full) {
                                 const int qq = q0 + qb + e;
                                 if (key > qq || qq >= S || key >= S) pr = 0.f;
@@ -895,14 +904,14 @@ int64_t al256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
 int64_t attn_bwd_work_bytes(int B, int S, int Hq, int Hkv, int hd) {
     const int64_t T = int64_t(B) * S;
-    return al256(T * Hq * 4) + al256(T * Hq * hd * 2) + 256 + al256(attn_bwd_part_elems(B, S, Hq, Hkv, hd) * 4);
+    return al256(2 * T * Hq * 4) + al256(T * Hq * hd * 2) + 256 + al256(attn_bwd_part_elems(B, S, Hq, Hkv, hd) * 4);
 }
 
 void attn_bwd_carve(void* work, int B, int S, int Hq, int Hkv, int hd, AttnBwdArgs& a) {
     const int64_t T = int64_t(B) * S;
     uint8_t* p = static_cast<uint8_t*>(work);
     a.dsum = reinterpret_cast<float*>(p);
-    p += al256(T * Hq * 4);
+    p += al256(2 * T * Hq * 4);
     a.do16 = reinterpret_cast<uint16_t*>(p);
     p += al256(T * Hq * hd * 2);
     a.amax = reinterpret_cast<uint32_t*>(p);

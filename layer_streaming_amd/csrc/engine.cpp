@@ -197,7 +197,7 @@ void plan_workspace(const Layout& lay, const mt_options& o, Carver& cv, Workspac
     ws.rstd1 = cv.take<float>(uint64_t(T) * 4);
     ws.rstd2 = cv.take<float>(uint64_t(T) * 4);
     ws.lse = cv.take<float>(uint64_t(T) * sh.n_heads * 4);
-    ws.dsum = cv.take<float>(uint64_t(T) * sh.n_heads * 4);
+    ws.dsum = cv.take<float>(uint64_t(T) * sh.n_heads * 4 * 2);
     ws.partial = cv.take<float>(uint64_t(rmsnorm_bwd_partial_elems(int(T), int(d))) * 4);
     ws.rope_tab = cv.take<float2>(uint64_t(o.max_seq) * (sh.head_dim / 2) * 8);
     ws.labels = cv.take<int32_t>(uint64_t(T) * 4);

@@ -308,13 +308,14 @@ def test_attention_dkdv_split_count_rule():
 
 
 def test_attention_backward_work_covers_the_automatic_split():
-    """The attention backward's scratch holds D, the scaled dO, the maxima and,
+    """The attention backward's scratch holds D and the base-2 log-sum-exp,
+    the scaled dO, the maxima and,
     when the dK/dV pass splits, the fp32 partials of every split."""
     al = lambda x: (x + 255) // 256 * 256
     for B, S, Hq, Hkv, hd in [(8, 1024, 28, 4, 128), (1, 131072, 28, 4, 128), (1, 300, 7, 1, 64)]:
         T = B * S
         ns = mt.lib.mt_k_attn_dkdv_splits(B, S, Hq, Hkv, hd, 0)
         part = ns * T * 2 * Hkv * hd if ns > 1 else 0
-        want = al(T * Hq * 4) + al(T * Hq * hd * 2) + 256 + al(part * 4)
+        want = al(2 * T * Hq * 4) + al(T * Hq * hd * 2) + 256 + al(part * 4)
         assert mt.lib.mt_k_attn_bwd_work_bytes(B, S, Hq, Hkv, hd) == want
     assert mt.lib.mt_k_attn_bwd_work_bytes(1, 100, 6, 4, 128) == 0   # not a grouping
