@@ -403,8 +403,9 @@ __global__ __launch_bounds__(256) void attn_amax_k(AttnBwdArgs a, int nb_do) {
         atomicMax(a.amax + (is_do ? 0 : 1), __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
 }
 
-// D 2^k = rowsum(dO * O) 2^k (O fp16) into dsum, the log-sum-exp in base 2
-// (lse log2 e) into its second half for the dK/dV kernel, and dO 2^k in fp16 into
+// -D 2^k = -rowsum(dO * O) 2^k (O fp16) into dsum (negated: the dK/dV kernel
+// starts its dP accumulation from it, so the MFMA forms dP - D), the
+// log-sum-exp in base 2 (lse log2 e) into its second half, and dO 2^k in fp16 into
 // do16 (range-guarded; the scale keeps it below 2^14).  One lane per 16-byte
 // chunk of a (token, query head) row: the HD/8 lanes of a row are adjacent,
 // so a wave instruction covers whole rows, and the row's dot product is
@@ -440,7 +441,7 @@ __global__ __launch_bounds__(256) void attn_prep_k(AttnBwdArgs a) {
     if (r < nrow && j == 0) {
         const uint32_t b = t / uint32_t(a.S), sq = t - b * uint32_t(a.S);
         const int64_t idx = (int64_t(b) * a.Hq + h) * a.S + sq;
-        a.dsum[idx] = s * s2k;
+        a.dsum[idx] = -(s * s2k);
         a.dsum[int64_t(nrow) + idx] = a.lse[idx] * LOG2E;
     }
     count_ovf(a.ovf, nov);
@@ -497,7 +498,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_k(AttnBwdArgs a, int n_qt, int
     }
     const int64_t st_off = (int64_t(b) * a.Hq + h) * S;
     const float lse2 = q < S ? a.lse[st_off + q] * LOG2E : 0.f;
-    const float dq_d = q < S ? a.dsum[st_off + q] : 0.f;
+    const float dq_nd = q < S ? a.dsum[st_off + q] : 0.f;  // -D 2^k
 
     uint32_t off[NI];
     tile_offsets<HD>(off, wave, lane, a.ld);
@@ -563,7 +564,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_k(AttnBwdArgs a, int n_qt, int
                             const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
                             if (key > q || key >= S) p = 0.f;
                         }
-                        tmp[j] = p * (dp[t][r] - dq_d);
+                        tmp[j] = p * (dp[t][r] + dq_nd);
                     }
                     dsb[t][s2] = pack_h8(tmp);
                 }
@@ -717,12 +718,23 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_k(AttnBwdArgs a, int n_kt, i
                     f[1] = tile_row<HD>(Ds[buf], 32 * t + c, 2 * s + hh);
                 };
                 static_for_n<PA - 1>([&](auto s_) { rd(decltype(s_)::value, fa[decltype(s_)::value]); });
+                // dP starts from -D of each element's query, so the products
+                // leave dP - D (element r: query 8 (r/4) + 4 hh + r%4 of the half)
+                f32x16_t dinit;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const float4 nd = *reinterpret_cast<const float4*>(&Dd[buf][32 * t + 8 * g + 4 * hh]);
+                    dinit[4 * g] = nd.x;
+                    dinit[4 * g + 1] = nd.y;
+                    dinit[4 * g + 2] = nd.z;
+                    dinit[4 * g + 3] = nd.w;
+                }
                 static_for_n<NS>([&](auto s_) {
                     constexpr int s = decltype(s_)::value;
                     if constexpr (s + PA - 1 < NS) rd(s + PA - 1, fa[(s + PA - 1) % PA]);
                     __builtin_amdgcn_sched_barrier(0);
                     st = MFMA32H(as_f16x8(fa[s % PA][0]), kf[s], s == 0 ? f32x16_t{} : st);
-                    dp = MFMA32H(as_f16x8(fa[s % PA][1]), vf[s], s == 0 ? f32x16_t{} : dp);
+                    dp = MFMA32H(as_f16x8(fa[s % PA][1]), vf[s], s == 0 ? dinit : dp);
                     __builtin_amdgcn_sched_barrier(0);
                 });
                 const bool full = kw + 31 <= qh && qh + 32 <= S && kw + 32 <= S;
@@ -732,9 +744,8 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_k(AttnBwdArgs a, int n_kt, i
 #pragma unroll
                     for (int g4 = 0; g4 < 2; ++g4) {
                         const int qb = 32 * t + 8 * (2 * s2 + g4) + 4 * hh;  // query within the tile
-                        float lv[4], dv4[4];
+                        float lv[4];
                         *reinterpret_cast<float4*>(lv) = *reinterpret_cast<const float4*>(&Ls[buf][qb]);
-                        *reinterpret_cast<float4*>(dv4) = *reinterpret_cast<const float4*>(&Dd[buf][qb]);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int jj = 4 * g4 + e, r = 8 * s2 + jj;
@@ -744,7 +755,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_k(AttnBwdArgs a, int n_kt, i
                                 if (key > qq || qq >= S || key >= S) pr = 0.f;
                             }
                             tp[jj] = pr;
-                            td[jj] = pr * (dp[r] - dv4[e]);
+                            td[jj] = pr * dp[r];  // dp holds dP - D
                         }
                     }
                     X[s2 * 64 + lane] = __builtin_bit_cast(uint4, pack_h8(tp));

@@ -108,7 +108,7 @@ struct AttnBwdArgs {
     const uint16_t* qkv; int64_t ld;  // fp16 q, k, v as the forward used them
     const uint16_t* o; const uint16_t* dout; int64_t ldo;  // o fp16, dout bf16
     const float* lse;
-    float* dsum;           // scratch [2 x B x Hq x S]: rowsum(dO * O) 2^k, then lse log2(e)
+    float* dsum;           // scratch [2 x B x Hq x S]: -rowsum(dO * O) 2^k, then lse log2(e)
     uint16_t* do16;        // scratch [B*S x Hq*hd] fp16: dO 2^k
     uint32_t* amax;        // scratch, 256 bytes: max|dO| and max|v| that fix 2^k
     uint16_t* dqkv; int64_t ldd;  // output in qkv's column layout: dV bf16, and dQ, dK bf16 unless dqk32
