@@ -118,6 +118,12 @@ typedef struct mt_options {
                                     staging buffers sized to the largest layer).  0 (default): the
                                     head is one unit; -1: rows per chunk chosen so a chunk fits the
                                     largest decoder layer's slot; k > 0 (a multiple of 8): k rows */
+    int32_t poison_released;     /* debug, 1: fill every weight slot with bf16 NaN when its last
+                                    compute visit releases it (the slot is then re-streamed even
+                                    where it still held the unit), and every gradient area once
+                                    its copy to a slab is done; a late reader of a released
+                                    buffer then turns the step's results to NaN.  Needs
+                                    slot_mode 0 and resident 0.  Same results as 0 */
     uint64_t slot_bytes_override;      /* 0: largest unit's weight bytes */
     uint64_t workspace_bytes_override; /* 0: computed from max_batch*max_seq */
     float lr, beta1, beta2, adam_eps;  /* 1e-4, 0.9, 0.999, 1e-8 */

@@ -631,6 +631,11 @@ __global__ void fill_zero_k(uint4* __restrict__ p, int64_t n16) {
     if (i < n16) p[i] = make_uint4(0, 0, 0, 0);
 }
 
+__global__ void fill_u32_k(uint4* __restrict__ p, int64_t n16, uint32_t v) {
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += int64_t(gridDim.x) * blockDim.x)
+        p[i] = make_uint4(v, v, v, v);
+}
+
 inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 inline unsigned blocks(int64_t n, int b) { return unsigned((n + b - 1) / b); }
 
@@ -881,6 +886,15 @@ hipError_t transpose16(const uint16_t* src, int64_t lds, uint16_t* dst, int64_t 
     using F_ = std::false_type;
     if (vec) f16_to_bf16 ? go(T_{}, T_{}) : go(T_{}, F_{});
     else f16_to_bf16 ? go(F_{}, T_{}) : go(F_{}, F_{});
+    return hipGetLastError();
+}
+
+hipError_t fill_u32(void* p, int64_t bytes, uint32_t pattern, hipStream_t s) {
+    if (bytes < 0 || (bytes & 15) || !al16(p)) return hipErrorInvalidValue;
+    if (bytes == 0) return hipSuccess;
+    const int64_t n16 = bytes / 16;
+    fill_u32_k<<<unsigned(std::min<int64_t>(4096, (n16 + 255) / 256)), 256, 0, s>>>(reinterpret_cast<uint4*>(p), n16,
+                                                                                   pattern);
     return hipGetLastError();
 }
 

@@ -301,6 +301,9 @@ int validate_options(const mt_options* o) {
     if (o->pin_weights && o->pin_store) MT_FAIL(MT_E_INVAL, "pin_weights and pin_store exclude each other");
     if (o->head_vocab_chunk < -1 || (o->head_vocab_chunk > 0 && (o->head_vocab_chunk & 7)))
         MT_FAIL(MT_E_INVAL, "head_vocab_chunk must be -1, 0 or a positive multiple of 8");
+    if (o->poison_released < 0 || o->poison_released > 1) MT_FAIL(MT_E_INVAL, "poison_released must be 0 or 1");
+    if (o->poison_released && (o->slot_mode != 0 || o->resident))
+        MT_FAIL(MT_E_INVAL, "poison_released needs slot_mode 0 and resident 0");
     if (!(o->lr >= 0.f) || !(o->beta1 >= 0.f && o->beta1 < 1.f) || !(o->beta2 >= 0.f && o->beta2 < 1.f) ||
         !(o->adam_eps > 0.f))
         MT_FAIL(MT_E_INVAL, "bad Adam hyper-parameters");
@@ -891,6 +894,10 @@ void Ctx::offload_worker() {
         if (e == hipSuccess) e = hipMemcpyAsync(slabs[k], r.gbase, r.bytes, hipMemcpyDeviceToHost, st_g);
         if (e == hipSuccess && b) e = hipEventRecord(b, st_g);
         if (e == hipSuccess) e = rec(slab_done[k], st_g);
+        // poison_released: the gradient area holds NaN from here until the
+        // next visit that writes it
+        if (e == hipSuccess && opt.poison_released && !(r.bytes & 15))
+            e = fill_u32(r.gbase, int64_t(r.bytes), 0x7FC07FC0u, st_g);
         if (e == hipSuccess) e = rec(buf_free[r.ga], st_g);
         if (e == hipSuccess && r.slot >= 0) e = rec(slot_free[r.slot], st_g);
         // The job is queued before the request counts as issued, so a
@@ -1547,6 +1554,17 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
         HIPC(h2d(x_first, x0_pin, td, st_w));
         HIPC(rec(emb_ready, st_w));
 
+        // A compute visit is done with its weight slot: release it (with
+        // poison_released, filled with NaN first and forgotten, so any later
+        // reader that was not re-streamed reads NaN).
+        auto release_slot = [&](int s_) -> hipError_t {
+            if (opt.poison_released) {
+                const hipError_t e = fill_u32(arena + plan.wslot[s_], int64_t(plan.slot_bytes), 0x7FC07FC0u, st_c);
+                if (e != hipSuccess) return e;
+                slot_unit[s_] = -1;
+            }
+            return rec(slot_free[s_], st_c);
+        };
         int gnext = 0, nbwd = 0, restored = -1;
         for (const Visit& vs : sched) {
             const int kind = vs.kind, unit = vs.unit;
@@ -1612,7 +1630,7 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
                 HIPC(fwd_layer(bind_layer(lay, wbase), x, y, B, S, true));
                 HIPC(hipEventRecord(vz, st_c));
                 visit_rec(va, vz);
-                HIPC(rec(slot_free[slot], st_c));
+                HIPC(release_slot(slot));
                 if (opt.ckpt_on_host) {
                     // Checkpoint the layer input on the gradient stream (idle in forward).
                     if (unit % K == 0) {
@@ -1638,7 +1656,7 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
                 }
                 HIPC(hipEventRecord(vz, st_c));
                 visit_rec(va, vz);
-                HIPC(rec(slot_free[slot], st_c));
+                HIPC(release_slot(slot));
                 continue;
             }
             if (kind == V_REFWD) {
@@ -1646,7 +1664,7 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
                 HIPC(fwd_layer(bind_layer(lay, wbase), xb[vs.pos], xb[vs.pos + 1], B, S, true));
                 HIPC(hipEventRecord(vz, st_c));
                 visit_rec(va, vz);
-                HIPC(rec(slot_free[slot], st_c));
+                HIPC(release_slot(slot));
                 continue;
             }
             // Head or backward: gradients go to a gradient area, then to a slab.
@@ -1670,7 +1688,7 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
             }
             HIPC(hipEventRecord(vz, st_c));
             visit_rec(va, vz);
-            if (!combined) HIPC(rec(slot_free[slot], st_c));
+            if (!combined) HIPC(release_slot(slot));
             HIPC(rec(bwd_done[ga], st_c));
             // Gradient offload: Backward-Done -> free slab -> Buffer-Free.
             {
@@ -2110,6 +2128,7 @@ int mt_default_options(mt_options* o) {
     o->ckpt_interval = 1;
     o->pin_weights = 0;
     o->head_vocab_chunk = 0;
+    o->poison_released = 0;
     o->lr = 1e-4f;
     o->beta1 = 0.9f;
     o->beta2 = 0.999f;

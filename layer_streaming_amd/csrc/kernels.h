@@ -157,6 +157,8 @@ hipError_t ce_chunk_bwd(const float* logits, const int32_t* labels, const float*
 // --------------------------------------------------------------- misc -----
 hipError_t f32_to_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t s);
 hipError_t fill_zero(void* p, int64_t bytes, hipStream_t s);
+// Every 32-bit word of [p, p + bytes) set to `pattern` (bytes a multiple of 16).
+hipError_t fill_u32(void* p, int64_t bytes, uint32_t pattern, hipStream_t s);
 // dst[c * ldd + r] = src[r * lds + c] for an R x C matrix of 16-bit elements;
 // f16_to_bf16: the source is fp16 and the destination gets it rounded to bf16.
 hipError_t transpose16(const uint16_t* src, int64_t lds, uint16_t* dst, int64_t ldd, int R, int C, hipStream_t s,

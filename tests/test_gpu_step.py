@@ -220,12 +220,15 @@ def test_bench_option_set_three_steps_against_oracle():
     ctx.close()
 
 
-def _run_steps(kw, B, S, n, **opts):
+def _run_steps(kw, B, S, n, stats_out=None, **opts):
     ctx = make_ctx(kw, B, S, **opts)
     losses = []
     for k in range(n):
         tokens, labels = synth.tokens_labels(700 + k, B, S, kw["vocab"])
-        losses.append(ctx.train_step(tokens, labels)[0])
+        loss, st = ctx.train_step(tokens, labels)
+        losses.append(loss)
+        if stats_out is not None:
+            stats_out.append(st)
     state = [(key, which, a) for which in (mt.MT_W, mt.MT_G, mt.MT_MASTER, mt.MT_M, mt.MT_V)
              for key, a in read_all(ctx, kw, which)]
     ctx.close()
@@ -411,6 +414,32 @@ def test_vocab_chunked_head_with_micro_batches():
 def _micro_batches(kw, n, B, S, seed0):
     tl = [synth.tokens_labels(seed0 + j, B, S, kw["vocab"]) for j in range(n)]
     return np.stack([t for t, _ in tl]), np.stack([lb for _, lb in tl])
+
+
+@pytest.mark.parametrize("opts", [dict(), dict(head_vocab_chunk=256, ckpt_interval=2, cross_step=1, n_grad_slabs=3),
+                                  dict(pin_weights=1, n_weight_slots=3, head_vocab_chunk=-1)],
+                         ids=["default", "chunked-head,interval2,cross-step", "pinned,3slots"])
+def test_poisoned_released_buffers_change_nothing(opts):
+    """Race check of the streaming protocol: with poison_released every
+    weight slot is filled with NaN when its last visit releases it, and every
+    gradient area once its copy to a slab is done.  Three steps must give
+    bit-identical losses and state to the same run without poisoning: no
+    kernel reads a released slot or gradient area, and every visit writes
+    its whole gradient area."""
+    log(f"poisoned release vs plain: {opts}")
+    st0, st1 = [], []
+    base_losses, base_state = _run_steps(DEEP, 2, 48, 3, stats_out=st0, **opts)
+    losses, state = _run_steps(DEEP, 2, 48, 3, stats_out=st1, poison_released=1, **opts)
+    assert all(np.isfinite(losses))
+    # the poison is live: a released slot is never reused, so a unit whose
+    # slot the next visit could have reused is streamed again
+    h0, h1 = st0[-1].h2d_bytes, st1[-1].h2d_bytes
+    log(f"  h2d bytes per step: plain {h0}, poisoned {h1}")
+    assert h1 > h0
+    assert [np.float32(x).tobytes() for x in losses] == [np.float32(x).tobytes() for x in base_losses]
+    for (k1, w1, a1), (k2, w2, a2) in zip(base_state, state):
+        assert k1 == k2 and w1 == w2
+        assert np.array_equal(a1.view(np.uint8), a2.view(np.uint8)), (k1, w1)
 
 
 def test_accumulated_step_parity():

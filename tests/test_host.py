@@ -126,7 +126,7 @@ def test_bad_shapes_rejected(field, value):
 @pytest.mark.parametrize("field,value", [("n_weight_slots", 0), ("n_weight_slots", 5), ("n_grad_slabs", 0),
                                          ("slot_mode", 2), ("max_batch", 0), ("beta1", 1.0), ("ckpt_interval", 0),
                                          ("cross_step", 2), ("pin_weights", 2), ("head_vocab_chunk", -2),
-                                         ("head_vocab_chunk", 12)])
+                                         ("head_vocab_chunk", 12), ("poison_released", 2)])
 def test_bad_options_rejected(field, value):
     o = mt.default_options()
     setattr(o, field, value)
@@ -135,7 +135,8 @@ def test_bad_options_rejected(field, value):
 
 
 def test_option_conflicts_rejected():
-    for kw in (dict(ckpt_interval=2, ckpt_on_host=0), dict(pin_weights=1, pin_store=1)):
+    for kw in (dict(ckpt_interval=2, ckpt_on_host=0), dict(pin_weights=1, pin_store=1),
+               dict(poison_released=1, slot_mode=1), dict(poison_released=1, resident=1)):
         o = mt.default_options(**kw)
         a, p, h = C.c_uint64(), C.c_uint64(), C.c_uint64()
         assert mt.lib.mt_workspace_bytes(C.byref(CFG1), C.byref(o), C.byref(a), C.byref(p), C.byref(h)) == mt.MT_E_INVAL
