@@ -132,6 +132,11 @@ void ThreadPool::worker_loop() {
             cv_.wait(lk, [&] { return stop_ || gen_ != seen; });
             if (stop_) return;
             seen = gen_;
+            // Woken after every chunk of this job was claimed: the submitter may
+            // already have returned and be writing the next job's fields (and
+            // resetting the chunk counter) without waiting for this thread, so
+            // it must not touch them; it waits for the next generation instead.
+            if (next_.load() >= nchunks_) continue;
             ++active_;
         }
         run_chunks();

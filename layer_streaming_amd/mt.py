@@ -3,8 +3,8 @@
 Argument marshalling only: every step of the training path runs in the
 library.  PyTorch is used by callers for device memory and streams; this
 module passes raw pointers (``tensor.data_ptr()``, ``stream.cuda_stream``).
-Importing it loads ``libmt.so`` from this package directory and raises if
-the library is missing, so a missing build fails loudly instead of falling
+Importing it loads ``libmt.so`` from this package directory (or the build
+that ``MT_LIBRARY`` names) and raises if the library is missing, so a missing build fails loudly instead of falling
 back to anything else.
 """
 import ctypes as C
@@ -12,7 +12,9 @@ import os
 
 import numpy as np
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmt.so")
+# MT_LIBRARY names another build of the same sources (the host-sanitizer copy);
+# by default the library built in this directory is loaded.
+_LIB_PATH = os.environ.get("MT_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmt.so")
 if not os.path.exists(_LIB_PATH):
     raise ImportError(f"{_LIB_PATH} is not built; run `python -m layer_streaming_amd.build`")
 lib = C.CDLL(_LIB_PATH)

@@ -295,6 +295,17 @@ def test_init_is_deterministic_across_thread_counts_and_statistically_normal():
             assert abs(k - 3.0) < 0.15
 
 
+def test_thread_pool_back_to_back_jobs_match_one_thread():
+    """The init runs one pool job per tensor, back to back on one pool, so
+    workers woken for one job can arrive while the next is being set up.  Many
+    such calls with 8 threads give the one-thread tile every time (and, under
+    the ThreadSanitizer build, no report)."""
+    ref, _ = _init_tile(CFG1, 1, 99, 1)
+    for _ in range(40):
+        b, _ = _init_tile(CFG1, 1, 99, 8)
+        assert np.array_equal(b, ref)
+
+
 def test_attention_dkdv_split_count_rule():
     """Automatic splits: none once there are 512 key-tile blocks, else enough
     for 512, at most Hq/Hkv; an explicit count is capped by the group."""
