@@ -129,13 +129,15 @@ def hbm_bytes(cfg, T):
     }
 
 
-def host_bytes_per_step(cfg, T, n_micro=1, pinned=False):
+def host_bytes_per_step(cfg, T, n_micro=1, pinned=False, keep_grads=True):
     """Host DRAM bytes one step moves.  Per micro-batch: for the forward and
     the backward visit of every streamed unit, the DMA read of its weights,
     preceded, unless the W regions are pinned (pin_weights), by the pack (read
     W, streaming write to staging); the DMA write of every streamed unit's
     gradient, the checkpoint ring out and back in, and the embedding rows.
-    Per optimizer step and parameter: Adam's 30 B with one micro-batch; with
+    Per optimizer step and parameter: Adam's 30 B with one micro-batch (read
+    the slab, master, m, v; write master, m, v, W and the copy into G), 28 B
+    when the store does not keep gradients (keep_grads = 0: no G copy); with
     n > 1 the first stores the slab into G (4 B), each middle one adds into G
     (6 B), the last adds and runs Adam (34 B)."""
     L, d, F, V = cfg["n_layers"], cfg["d_model"], cfg["ffn_dim"], cfg["vocab"]
@@ -143,7 +145,7 @@ def host_bytes_per_step(cfg, T, n_micro=1, pinned=False):
     p_layer = d * hq * hd + 2 * d * hkv * hd + hq * hd * d + 3 * d * F + 2 * d
     streamed = L * p_layer + V * d + d
     p_embed = V * d
-    per_param = 30 if n_micro == 1 else 4 + 6 * (n_micro - 2) + 34
+    per_param = (30 if keep_grads else 28) if n_micro == 1 else 4 + 6 * (n_micro - 2) + 34
     visit = 2 if pinned else 4 + 2
     per_micro = 2 * visit * streamed + 2 * streamed + 2 * L * T * d * 2 + 2 * T * d * 2
     return per_param * (streamed + p_embed) + n_micro * per_micro
@@ -642,6 +644,10 @@ def main():
                     help="only measure host DRAM: the host Adam alone at 8/12/16 threads, a parallel copy and read")
     ap.add_argument("--micro", type=int, default=1,
                     help="micro-batches of batch x seq per optimizer step (gradient accumulation on the host)")
+    ap.add_argument("--keep-grads", type=int, default=0,
+                    help="0 (default): with one micro-batch Adam reads each gradient slab without copying it into "
+                         "the store's G (2 B/param less host traffic; same weights and optimizer state); 1: the "
+                         "slab is copied into G as the pages' unpack step does")
     ap.add_argument("--cross-step", type=int, default=1,
                     help="1 (default): the next step's forward overlaps this step's Adam tail (same results); "
                          "0: every step synchronous")
@@ -672,7 +678,8 @@ def main():
     opt_kw = dict(profile_kernels=0 if args.no_profile else 1, host_threads=args.host_threads,
                   n_weight_slots=args.slots, n_grad_slabs=args.slabs, slot_mode=args.slot_mode,
                   resident=args.resident, pin_store=args.pin_store, cross_step=args.cross_step,
-                  pin_weights=args.pin_weights, head_vocab_chunk=args.head_vocab_chunk)
+                  pin_weights=args.pin_weights, head_vocab_chunk=args.head_vocab_chunk,
+                  keep_grads=args.keep_grads)
     if args.depths:
         depth_sweep(torch, mt, cfg, args, opt_kw)
         return
@@ -698,7 +705,7 @@ def main():
                       "parallelism": "single GPU, layer-streamed", "weight_slots": args.slots,
                       "grad_slabs": args.slabs, "slot_mode": args.slot_mode, "resident": args.resident,
                       "cross_step": args.cross_step, "pin_weights": args.pin_weights,
-                      "head_vocab_chunk": args.head_vocab_chunk}}
+                      "head_vocab_chunk": args.head_vocab_chunk, "keep_grads": args.keep_grads}}
     mf = nm * model_flops_per_step(cfg, T, S)
     out["model_tflops_per_s"] = round(mf / (ms_per_step / 1e3) / 1e12, 2)
     out["pages_convention_tflops_per_s"] = round(nm * pages_flops_per_step(cfg, T, S) / (ms_per_step / 1e3) / 1e12, 2)
@@ -712,7 +719,7 @@ def main():
     logit_passes = 2 if args.head_vocab_chunk != 0 else 1
     recompute += (logit_passes - 1) * head_gemm_flops(cfg, T)
     out["hw_tflops_per_s"] = round((mf + nm * recompute) / (ms_per_step / 1e3) / 1e12, 2)
-    hb_step = host_bytes_per_step(cfg, T, nm, pinned=bool(args.pin_weights))
+    hb_step = host_bytes_per_step(cfg, T, nm, pinned=bool(args.pin_weights), keep_grads=bool(args.keep_grads))
     out["host_memory"] = {"bytes_per_step": int(hb_step), "achieved_GBps": round(hb_step / (ms_per_step / 1e3) / 1e9, 1),
                           "adam_alone_GBps": host_adam_probe(mt)}
     out["pcie"] = pcie_block(stats)
@@ -774,10 +781,11 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_pages_config and args.pin_weights and nm == 1:
         # The pages' pinned footprint: pageable W packed into two pinned
-        # staging buffers sized to the largest streamed block, 12 slabs.
-        pk = dict(opt_kw, pin_weights=0, n_grad_slabs=12)
+        # staging buffers sized to the largest streamed block, 12 slabs, and
+        # every gradient slab unpacked into the store's G before Adam.
+        pk = dict(opt_kw, pin_weights=0, n_grad_slabs=12, keep_grads=1)
         ps = max(2, min(args.steps, 5))
-        log(f"pages configuration: pin_weights=0, 12 slabs, {ps} timed steps")
+        log(f"pages configuration: pin_weights=0, 12 slabs, keep_grads=1, {ps} timed steps")
         pres, _, _ = run_workload(torch, mt, cfg, args, pk, ps, 1)
         if "refused" in pres:
             out["pages_config"] = pres
@@ -785,7 +793,7 @@ def main():
             pst = pres["stats"]
             out["pages_config"] = {
                 "value": round(pres["value"], 2), "unit": "tokens/s", "steps": ps,
-                "ms_per_step": round(pres["ms_per_step"], 2), "pin_weights": 0, "grad_slabs": 12,
+                "ms_per_step": round(pres["ms_per_step"], 2), "pin_weights": 0, "grad_slabs": 12, "keep_grads": 1,
                 "pinned_bytes": int(pst[0]["pinned_bytes"]), "gpu_arena_bytes": int(pst[0]["gpu_arena_bytes"]),
                 "phases_ms": {k: round(float(np.mean([s[k] for s in pst])), 1)
                               for k in ("fwd_ms", "head_ms", "bwd_ms", "adam_ms", "adam_wait_ms", "pack_ms")},

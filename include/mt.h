@@ -124,6 +124,13 @@ typedef struct mt_options {
                                     its copy to a slab is done; a late reader of a released
                                     buffer then turns the step's results to NaN.  Needs
                                     slot_mode 0 and resident 0.  Same results as 0 */
+    int32_t keep_grads;          /* 1 (default): the store's G region receives every unit's BF16
+                                    gradient (the slab is unpacked into G, then Adam reads it:
+                                    [Hotdry] the CPU thread that unpacks slabs and runs Adam).
+                                    0: with one micro-batch per step Adam reads the slab itself
+                                    and G is not written (2 B/param less host-DRAM traffic per
+                                    step); G still accumulates micro-batches, and
+                                    mt_get_tensor(MT_G) is refused.  Same W, master, m, v */
     uint64_t slot_bytes_override;      /* 0: largest unit's weight bytes */
     uint64_t workspace_bytes_override; /* 0: computed from max_batch*max_seq */
     float lr, beta1, beta2, adam_eps;  /* 1e-4, 0.9, 0.999, 1e-8 */
@@ -295,7 +302,8 @@ uint64_t mt_unit_elems(const mt_shape* shape, int32_t unit);
  * store is the host master copy of all persistent state, BF16 W and G with
  * the FP32 master, m and v ([Review] 3-2 item 1; [Lilting] 16-byte per
  * parameter table).  Both wait for queued host updates first.  Errors:
- * MT_E_INVAL (unit, tensor, which or bytes out of range, NULL pointers), or
+ * MT_E_INVAL (unit, tensor, which or bytes out of range, NULL pointers),
+ * MT_E_STATE for mt_get_tensor(MT_G) on a context with keep_grads = 0, or
  * a host worker's or a lazy restore's error. */
 int mt_get_tensor(mt_ctx* ctx, int32_t unit, int32_t idx, int32_t which, void* host_dst,
                   uint64_t bytes);

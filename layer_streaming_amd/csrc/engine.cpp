@@ -304,6 +304,7 @@ int validate_options(const mt_options* o) {
     if (o->poison_released < 0 || o->poison_released > 1) MT_FAIL(MT_E_INVAL, "poison_released must be 0 or 1");
     if (o->poison_released && (o->slot_mode != 0 || o->resident))
         MT_FAIL(MT_E_INVAL, "poison_released needs slot_mode 0 and resident 0");
+    if (o->keep_grads != 0 && o->keep_grads != 1) MT_FAIL(MT_E_INVAL, "keep_grads must be 0 or 1");
     if (!(o->lr >= 0.f) || !(o->beta1 >= 0.f && o->beta1 < 1.f) || !(o->beta2 >= 0.f && o->beta2 < 1.f) ||
         !(o->adam_eps > 0.f))
         MT_FAIL(MT_E_INVAL, "bad Adam hyper-parameters");
@@ -808,7 +809,12 @@ void Ctx::slab_worker() {
             const uint16_t* src = j.slab >= 0 ? reinterpret_cast<const uint16_t*>(slabs[j.slab]) : tp.g;
             const int64_t d = lay.sh.d_model;
             switch (j.mode) {
-                case JOB_ADAM: adam_unit(*adam_pool, tp, src, j.elems, j.a); break;
+                case JOB_ADAM:
+                    // keep_grads = 0: the update reads the slab and leaves G
+                    // alone (the copy into G is skipped when the two coincide)
+                    if (!opt.keep_grads) tp.g = const_cast<uint16_t*>(src);
+                    adam_unit(*adam_pool, tp, src, j.elems, j.a);
+                    break;
                 case JOB_ADAM_ROWS:
                 case JOB_ADAM_EXCEPT: {
                     // one row of the embedding tile at a time
@@ -2129,6 +2135,7 @@ int mt_default_options(mt_options* o) {
     o->pin_weights = 0;
     o->head_vocab_chunk = 0;
     o->poison_released = 0;
+    o->keep_grads = 1;
     o->lr = 1e-4f;
     o->beta1 = 0.9f;
     o->beta2 = 0.999f;
@@ -2258,6 +2265,8 @@ int mt_get_tensor(mt_ctx* c, int32_t unit, int32_t idx, int32_t which, void* dst
     const mt::TensorDesc& t = u.t[idx];
     const uint64_t n = uint64_t(t.rows * t.cols), es = which <= MT_G ? 2 : 4;
     if (bytes != n * es) MT_FAIL(MT_E_INVAL, "bytes %llu != %llu", (unsigned long long)bytes, (unsigned long long)(n * es));
+    if (which == MT_G && !c->impl.opt.keep_grads)
+        MT_FAIL(MT_E_STATE, "gradients are not kept in the store (keep_grads = 0)");
     const int ds = c->impl.drain_jobs();  // updates still queued by a cross-step train step
     if (ds != MT_OK) return ds;
     const int ls = c->impl.ensure_loaded(unit);  // a shard still pending after a lazy restore

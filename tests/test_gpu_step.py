@@ -162,11 +162,12 @@ def test_multi_chunk_head_parity():
 # ------------------------------------------- the benchmarked option set --
 # The options the benchmark runs with: cross-step pipelining, the weight
 # regions in one page-locked block, the LM head in layer-sized E_out chunks,
-# 16 gradient slabs, per-kernel timing, every host thread.  Three layers and
-# a vocabulary of 8192 give three head chunks; three steps with distinct
-# tokens run the split update of the input embedding twice.
+# 16 gradient slabs, per-kernel timing, every host thread, Adam reading the
+# slabs without a copy into the store's G.  Three layers and a vocabulary of
+# 8192 give three head chunks; three steps with distinct tokens run the split
+# update of the input embedding twice.
 BENCH_OPTS = dict(cross_step=1, pin_weights=1, head_vocab_chunk=-1, n_grad_slabs=16, profile_kernels=1,
-                  host_threads=0)
+                  host_threads=0, keep_grads=0)
 BENCHLIKE = dict(n_layers=3, d_model=256, n_heads=4, n_kv_heads=2, head_dim=64, ffn_dim=688, vocab=8192)
 
 
@@ -189,15 +190,20 @@ def _units(kw):
             [(L, ostep.HEAD_TENSORS, lambda t: t["head"], "head"), (L + 1, ("e_in",), lambda t: t["e_in"], "emb")])
 
 
-def test_bench_option_set_three_steps_against_oracle():
+@pytest.mark.parametrize("opts", [BENCH_OPTS, dict(BENCH_OPTS, keep_grads=1)], ids=["bench", "bench,keep-grads"])
+def test_bench_option_set_three_steps_against_oracle(opts):
     """Three steps with the benchmark's options, nothing read between them,
     against three steps of the oracle's streamed training (its gradients
     rounded to BF16, its Adam at t = 1, 2, 3) from the same initial state:
-    the loss of every step, the last step's gradients, and the Adam moments
-    m and sqrt(v) (sqrt(v) has the gradient's units) per tensor within 1e-2."""
+    the loss of every step, the Adam moments m and sqrt(v) (sqrt(v) has the
+    gradient's units) per tensor within 1e-2, and, where the store keeps
+    them, the last step's gradients.  Without them m still carries the last
+    gradient at weight 0.1 against 0.081 and 0.09 for the two before, so a
+    wrong last gradient shows in m."""
     kw, B, S = BENCHLIKE, 2, 64
-    log(f"bench option set, 3 steps, vs the oracle's 3-step training {kw}")
-    ctx = make_ctx(kw, B, S, **BENCH_OPTS)
+    keep = opts.get("keep_grads", 1) == 1
+    log(f"bench option set, 3 steps, vs the oracle's 3-step training {kw} {opts}")
+    ctx = make_ctx(kw, B, S, **opts)
     store = _oracle_store(ctx, kw)
     batches = [synth.tokens_labels(700 + k, B, S, kw["vocab"]) for k in range(3)]
     losses = [ctx.train_step(t, lb)[0] for t, lb in batches]
@@ -212,15 +218,20 @@ def test_bench_option_set_three_steps_against_oracle():
     for u, names, pick, tag in _units(kw):
         for j, n in enumerate(names):
             ref = pick(store)[n]
-            worst = max(worst, assert_close(widen(ctx.get_tensor(u, j, mt.MT_G)), pick(g_ref)[n], f"{tag}.d{n}"))
+            if keep:
+                worst = max(worst, assert_close(widen(ctx.get_tensor(u, j, mt.MT_G)), pick(g_ref)[n], f"{tag}.d{n}"))
             assert_close(ctx.get_tensor(u, j, mt.MT_M), ref["m"], f"{tag}.m({n})")
             assert_close(np.sqrt(ctx.get_tensor(u, j, mt.MT_V).astype(np.float64)),
                          np.sqrt(ref["v"].astype(np.float64)), f"{tag}.sqrt_v({n})")
-    log(f"  worst step-3 gradient tensor {worst:.3e}")
+    if keep:
+        log(f"  worst step-3 gradient tensor {worst:.3e}")
+    else:
+        with pytest.raises(mt.MTError, match="not kept"):
+            ctx.get_tensor(0, 0, mt.MT_G)
     ctx.close()
 
 
-def _run_steps(kw, B, S, n, stats_out=None, **opts):
+def _run_steps(kw, B, S, n, stats_out=None, with_g=True, **opts):
     ctx = make_ctx(kw, B, S, **opts)
     losses = []
     for k in range(n):
@@ -229,23 +240,26 @@ def _run_steps(kw, B, S, n, stats_out=None, **opts):
         losses.append(loss)
         if stats_out is not None:
             stats_out.append(st)
-    state = [(key, which, a) for which in (mt.MT_W, mt.MT_G, mt.MT_MASTER, mt.MT_M, mt.MT_V)
-             for key, a in read_all(ctx, kw, which)]
+    # with_g=False: compared without G (a store that does not keep gradients)
+    whiches = (mt.MT_W, mt.MT_G, mt.MT_MASTER, mt.MT_M, mt.MT_V) if with_g else \
+        (mt.MT_W, mt.MT_MASTER, mt.MT_M, mt.MT_V)
+    state = [(key, which, a) for which in whiches for key, a in read_all(ctx, kw, which)]
     ctx.close()
     return losses, state
 
 
-@pytest.mark.parametrize("opts", [BENCH_OPTS, dict(BENCH_OPTS, pin_weights=0, n_grad_slabs=12)],
+@pytest.mark.parametrize("opts", [BENCH_OPTS, dict(BENCH_OPTS, pin_weights=0, n_grad_slabs=12, keep_grads=1)],
                          ids=["bench", "pages-pinned-footprint"])
 def test_bench_option_set_bit_identical_to_synchronous_path(opts):
     """The benchmark's option set (and the pages' pinned footprint: two
     staging buffers and 12 slabs) against the plain synchronous streamed
     path with the same chunked head, over three steps: losses and the whole
-    store (W, G, master, m, v) bit for bit."""
+    store (W, master, m, v, and G where the option set keeps it) bit for bit."""
     kw, B, S = BENCHLIKE, 2, 64
     log(f"bench option set vs synchronous path: {opts}")
-    base_losses, base_state = _run_steps(kw, B, S, 3, head_vocab_chunk=-1)
-    losses, state = _run_steps(kw, B, S, 3, **opts)
+    with_g = opts.get("keep_grads", 1) == 1
+    base_losses, base_state = _run_steps(kw, B, S, 3, with_g=with_g, head_vocab_chunk=-1)
+    losses, state = _run_steps(kw, B, S, 3, with_g=with_g, **opts)
     assert [np.float32(x).tobytes() for x in losses] == [np.float32(x).tobytes() for x in base_losses]
     for (k1, w1, a1), (k2, w2, a2) in zip(base_state, state):
         assert k1 == k2 and w1 == w2

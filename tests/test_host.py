@@ -126,7 +126,8 @@ def test_bad_shapes_rejected(field, value):
 @pytest.mark.parametrize("field,value", [("n_weight_slots", 0), ("n_weight_slots", 5), ("n_grad_slabs", 0),
                                          ("slot_mode", 2), ("max_batch", 0), ("beta1", 1.0), ("ckpt_interval", 0),
                                          ("cross_step", 2), ("pin_weights", 2), ("head_vocab_chunk", -2),
-                                         ("head_vocab_chunk", 12), ("poison_released", 2)])
+                                         ("head_vocab_chunk", 12), ("poison_released", 2),
+                                         ("keep_grads", 2), ("keep_grads", -1)])
 def test_bad_options_rejected(field, value):
     o = mt.default_options()
     setattr(o, field, value)
