@@ -1277,19 +1277,32 @@ hipError_t Ctx::head_chunk_bwd(const HeadChunk& ch, bool first, bool last, const
     return hipSuccess;
 }
 
-// C[M x N] = A[M x K] B[K x N] (B row-major): B transposed into tB, then NT.
+// C[M x N] = A[M x K] B[K x N] (B row-major): straight from the k-major B
+// where the direct kernel takes the grid, else B transposed into tB, then NT.
 hipError_t Ctx::gemm_nn_t(const uint16_t* A, int64_t lda, const uint16_t* Bm, int64_t ldb, uint16_t* C, int64_t ldc,
                           int M, int N, int K) {
+    {
+        GemmArgs a{A, lda, Bm, ldb, C, ldc, nullptr, 0, nullptr, 0, M, N, K};
+        const hipError_t e = gemm_direct_checked(GEMM_NN, EPI_BF16, a, st_c);
+        if (e != hipErrorNotSupported) return e;
+    }
     HIPR(transpose16(Bm, ldb, ws.tB, K, K, N, st_c));
     GemmArgs a{A, lda, ws.tB, K, C, ldc, nullptr, 0, nullptr, 0, M, N, K};
     return gemm(GEMM_NT, EPI_BF16, a, st_c);
 }
 
-// C[M x N] = A^T B with A stored [K x M] and B [K x N]: both transposed, then
-// NT.  K (the tokens) is padded to a multiple of 8 with zero columns, which
-// add nothing.  b_f16: B holds fp16, rounded to bf16 by its transpose.
+// C[M x N] = A^T B with A stored [K x M] and B [K x N]: straight from the
+// k-major operands where the direct kernel takes the grid, else both
+// transposed, then NT; K (the tokens) is then padded to a multiple of 8 with
+// zero columns, which add nothing.  b_f16: B holds fp16, rounded to bf16 by
+// its transpose (always the transposed form).
 hipError_t Ctx::gemm_tn_t(const uint16_t* A, int64_t lda, const uint16_t* Bm, int64_t ldb, uint16_t* C, int64_t ldc,
                           int M, int N, int K, bool b_f16) {
+    if (!b_f16) {
+        GemmArgs a{A, lda, Bm, ldb, C, ldc, nullptr, 0, nullptr, 0, M, N, K};
+        const hipError_t e = gemm_direct_checked(GEMM_TN, EPI_BF16, a, st_c);
+        if (e != hipErrorNotSupported) return e;
+    }
     const int Kp = (K + 7) & ~7;
     if (Kp != K) {
         HIPR(fill_zero(ws.tA, int64_t(M) * Kp * 2, st_c));

@@ -297,7 +297,7 @@ hipError_t launch_layout(GemmEpi epi, const GemmArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t gemm(GemmLayout lay, GemmEpi epi, const GemmArgs& a, hipStream_t s) {
+static hipError_t gemm_check(GemmLayout lay, GemmEpi epi, const GemmArgs& a) {
     if (a.M <= 0 || a.N <= 0 || a.K <= 0) return hipErrorInvalidValue;
     if (!a.A || !a.B || !a.C) return hipErrorInvalidValue;
     // 16-byte vector loads: the contiguous dimension and every leading
@@ -316,8 +316,19 @@ hipError_t gemm(GemmLayout lay, GemmEpi epi, const GemmArgs& a, hipStream_t s) {
     if (epi == EPI_BF16_ACCF32 && (!a.Cacc || a.ldacc < a.N)) return hipErrorInvalidValue;
     if ((epi == EPI_F32_F16IN || epi == EPI_F32_F16IN_RESID) && lay != GEMM_NT) return hipErrorInvalidValue;
     if (int(epi) < 0 || int(epi) > int(EPI_F32_F16IN_RESID)) return hipErrorInvalidValue;
-    if (lay == GEMM_NT) {
-        const hipError_t e = gemm_nt_direct(epi, a, s);
+    return hipSuccess;
+}
+
+hipError_t gemm_direct_checked(GemmLayout lay, GemmEpi epi, const GemmArgs& a, hipStream_t s) {
+    const hipError_t c = gemm_check(lay, epi, a);
+    return c != hipSuccess ? c : gemm_direct(lay, epi, a, s);
+}
+
+hipError_t gemm(GemmLayout lay, GemmEpi epi, const GemmArgs& a, hipStream_t s) {
+    const hipError_t c = gemm_check(lay, epi, a);
+    if (c != hipSuccess) return c;
+    {
+        const hipError_t e = gemm_direct(lay, epi, a, s);
         if (e != hipErrorNotSupported) return e;
     }
     switch (lay) {

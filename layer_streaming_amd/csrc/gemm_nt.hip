@@ -29,6 +29,8 @@
 //    on MI355X at the 7B gate|up shape (8192 x 37888 x 3584, random bf16):
 //    1215 TFLOP/s against 1111 for the 32-deep form with the LDS epilogue
 //    and 1076 with stores straight from the accumulators.
+#include <type_traits>
+
 #include "kcommon.h"
 #include "kernels.h"
 
@@ -76,6 +78,9 @@ namespace {
 #endif
 #ifndef MT_NT_WM
 #define MT_NT_WM 2        // of which along M
+#endif
+#ifndef MT_GEMM_KMAJOR
+#define MT_GEMM_KMAJOR 1  // 1: NN and TN products read k-major operands straight (256 x 256 grids)
 #endif
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -531,23 +536,100 @@ struct DirectLoader64 {
     }
 };
 
-template <int FM, int FN, int TM, int TN>
+// An operand stored k-major ([K x rows], the layouts NN and TN take for B,
+// and TN for A) is tiled the other way round: LDS row k holds the tile's
+// COLS output rows at that k (COLS * 2 bytes, one whole global row segment
+// per load request), and a fragment's 8 k of one output row are read
+// across rows with ds_read_b64_tr_b16.  Physical chunk of logical chunk c in
+// tile row k: c ^ 4 (k & 3), so the four rows one such read spans land in
+// four distinct 64-byte bank groups.
+__device__ __forceinline__ int swzT(int k) { return (k & 3) << 2; }
+
+// Loads of one k-major operand's 64 x COLS tile: instruction i of wave w
+// fills LDS chunks (i*NW + w)*64 + lane, RPI whole tile rows.
+template <int COLS, int NW>
+struct DirectLoader64T {
+    static constexpr int CPR = COLS / 8;                 // 16-byte chunks per tile row
+    static constexpr int RPI = 64 / CPR;                 // tile rows per wave instruction
+    static constexpr int NI = 64 / (RPI * NW);
+    static_assert(CPR * RPI == 64 && NI >= 1 && RPI * NW * NI == 64, "tile rows must cover the waves");
+    uint32_t off[NI];
+    int kr[NI];   // the lane's tile row (k within the tile)
+    uint32_t ld2;
+
+    __device__ __forceinline__ void init(int lane, int wave, int64_t ld) {
+        ld2 = uint32_t(ld * 2);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int pos = (i * NW + wave) * 64 + lane;
+            const int r = pos / CPR;
+            const int c = (pos % CPR) ^ swzT(r);
+            off[i] = uint32_t((int64_t(r) * ld + c * 8) * 2);
+            kr[i] = r;
+        }
+    }
+    __device__ __forceinline__ void issue_one(int i, i32x4_t rs, uint4* stage, int wave, int k0, int K) const {
+        const uint32_t base = uint32_t(reinterpret_cast<uintptr_t>((lds_ptr_t)stage));
+        uint32_t v = off[i] + uint32_t(k0) * ld2;
+        if (k0 + kr[i] >= K) v = OOB;
+        dma16(rs, __builtin_amdgcn_readfirstlane(base + uint32_t(i * NW + wave) * 1024u), v);
+    }
+    __device__ __forceinline__ void issue(i32x4_t rs, uint4* stage, int wave, int k0, int K) const {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) issue_one(i, rs, stage, wave, k0, K);
+    }
+};
+
+// Fragment of k-step ks for output rows col0 .. col0+31 of a k-major tile:
+// lane l gets row col0 + l%32 at k = 16 ks + 8 (l/32) + 0..7, the layout a
+// 128-bit read of a k-contiguous tile gives.  Each ds_read_b64_tr_b16 reads
+// four tile rows (k) x 16 columns per 16 lanes, every lane addressing one
+// 8-byte piece, and hands lane i column i of them.
+template <int COLS>
+__device__ __forceinline__ uint4 frag_kmajor(const uint4* t, int ks, int col0, int lane) {
+    const int j = lane & 15, g16 = (lane >> 4) & 1, hh = lane >> 5;
+    const int col = col0 + 16 * g16 + 4 * (j & 3);
+    const char* base = reinterpret_cast<const char*>(t);
+    uint2 r[2];
+#pragma unroll
+    for (int e2 = 0; e2 < 2; ++e2) {
+        const int k = 16 * ks + 8 * hh + 4 * e2 + (j >> 2);
+        const int off = k * (COLS * 2) + (((col >> 3) ^ swzT(k)) * 16) + (col & 7) * 2;
+        typedef short i16x4_t __attribute__((ext_vector_type(4)));
+        const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(lds_ptr_t)(base + off));
+        r[e2] = __builtin_bit_cast(uint2, v);
+    }
+    return make_uint4(r[0].x, r[0].y, r[1].x, r[1].y);
+}
+
+template <int FM, int FN, int TM, int TN, bool TA = false, bool TB = false, int BM = 0, int BN = 0>
 __device__ __forceinline__ void read_frags64(const uint4* __restrict__ a_l, const uint4* __restrict__ b_l, int ks,
                                              int wm, int wn, int lane, uint4 (&fa)[FM], uint4 (&fb)[FN]) {
     const int kc = ks * 2 + (lane >> 5);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-        const int r = wm * TM + i * 32 + (lane & 31);
-        fa[i] = a_l[r * 8 + (kc ^ swz8(r))];
+        if constexpr (TA) {
+            fa[i] = frag_kmajor<BM>(a_l, ks, wm * TM + i * 32, lane);
+        } else {
+            const int r = wm * TM + i * 32 + (lane & 31);
+            fa[i] = a_l[r * 8 + (kc ^ swz8(r))];
+        }
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-        const int r = wn * TN + j * 32 + (lane & 31);
-        fb[j] = b_l[r * 8 + (kc ^ swz8(r))];
+        if constexpr (TB) {
+            fb[j] = frag_kmajor<BN>(b_l, ks, wn * TN + j * 32, lane);
+        } else {
+            const int r = wn * TN + j * 32 + (lane & 31);
+            fb[j] = b_l[r * 8 + (kc ^ swz8(r))];
+        }
     }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
+// TA / TB: A / B stored k-major (A [K x M], B [K x N]); the other layouts
+// of C = op(A) op(B) then run on the same main loop with no transposed copy.
+template <int BM, int BN, int WM, int WN, int EPI, bool TA = false, bool TB = false>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_nt64_k(GemmArgs p, int tiles_m, int tiles_n) {
     constexpr int NW = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
@@ -574,16 +656,27 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt64_k(GemmArgs p, int tile
     const int m0 = tm * BM, n0 = tn * BN;
 
     const int rows_a = min(BM, p.M - m0), rows_b = min(BN, p.N - n0);
-    const auto ra = make_rsrc(static_cast<const uint16_t*>(p.A) + int64_t(m0) * p.lda,
-                              uint32_t((int64_t(rows_a - 1) * p.lda + p.K) * 2));
-    const auto rb = make_rsrc(static_cast<const uint16_t*>(p.B) + int64_t(n0) * p.ldb,
-                              uint32_t((int64_t(rows_b - 1) * p.ldb + p.K) * 2));
-    DirectLoader64<BM, NW> la;
-    DirectLoader64<BN, NW> lb;
+    // The resources end at the block's last element: past it (rows beyond M
+    // or N of a k-contiguous operand, k beyond K of a k-major one) reads give
+    // zero.  A k-major operand's columns past M or N inside the extent read
+    // neighbouring elements, which reach only accumulator rows or columns
+    // that are never stored.
+    const auto ra = TA ? make_rsrc(static_cast<const uint16_t*>(p.A) + m0,
+                                   uint32_t((int64_t(p.K - 1) * p.lda + rows_a) * 2))
+                       : make_rsrc(static_cast<const uint16_t*>(p.A) + int64_t(m0) * p.lda,
+                                   uint32_t((int64_t(rows_a - 1) * p.lda + p.K) * 2));
+    const auto rb = TB ? make_rsrc(static_cast<const uint16_t*>(p.B) + n0,
+                                   uint32_t((int64_t(p.K - 1) * p.ldb + rows_b) * 2))
+                       : make_rsrc(static_cast<const uint16_t*>(p.B) + int64_t(n0) * p.ldb,
+                                   uint32_t((int64_t(rows_b - 1) * p.ldb + p.K) * 2));
+    using LA = std::conditional_t<TA, DirectLoader64T<BM, NW>, DirectLoader64<BM, NW>>;
+    using LB = std::conditional_t<TB, DirectLoader64T<BN, NW>, DirectLoader64<BN, NW>>;
+    LA la;
+    LB lb;
     la.init(lane, wave, p.lda);
     lb.init(lane, wave, p.ldb);
-    constexpr int NIA = DirectLoader64<BM, NW>::NI;
-    constexpr int NIT = NIA + DirectLoader64<BN, NW>::NI;  // loads per wave per tile
+    constexpr int NIA = LA::NI;
+    constexpr int NIT = NIA + LB::NI;  // loads per wave per tile
     // loads of a tile issued with the last k-step of the tile two earlier
     // (NIT - L1) and with the first k-step of the tile before it (L1)
     constexpr int L1 = MT_NT_L1 < 0 ? NIT / 2 : MT_NT_L1;
@@ -601,7 +694,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt64_k(GemmArgs p, int tile
     const int nk = (p.K + BK64 - 1) / BK64;
     uint4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
 
-#define RD(SA, SB, KS, FA, FB) read_frags64<FM, FN, TM, TN>(SA, SB, KS, wm, wn, lane, FA, FB)
+#define RD(SA, SB, KS, FA, FB) read_frags64<FM, FN, TM, TN, TA, TB, BM, BN>(SA, SB, KS, wm, wn, lane, FA, FB)
 #define MM(FA, FB) mma_frags<FM, FN, F16>(FA, FB, acc)
 #define PRIO(x) if (MT_NT_PRIO) __builtin_amdgcn_s_setprio(x)
 #define LOAD_ONE(g, XA, XB, T)                                                           \
@@ -732,22 +825,50 @@ hipError_t launch(GemmEpi epi, const GemmArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// The k-major forms (NN: B k-major; TN: both), 256 x 256 tiles only, with
+// the epilogues the backward products and the head use.
+template <bool TA, bool TB>
+hipError_t launch_kmajor(GemmEpi epi, const GemmArgs& a, hipStream_t s) {
+    constexpr int WM = MT_NT_WM, WN = MT_NT_NW / MT_NT_WM;
+    const int tm = (a.M + 255) / 256, tn = (a.N + 255) / 256;
+    const dim3 grid(tm * tn), block(WM * WN * 64);
+    switch (epi) {
+        case EPI_BF16: gemm_nt64_k<256, 256, WM, WN, EPI_BF16, TA, TB><<<grid, block, 0, s>>>(a, tm, tn); break;
+        case EPI_F32: gemm_nt64_k<256, 256, WM, WN, EPI_F32, TA, TB><<<grid, block, 0, s>>>(a, tm, tn); break;
+        case EPI_F32_ACC: gemm_nt64_k<256, 256, WM, WN, EPI_F32_ACC, TA, TB><<<grid, block, 0, s>>>(a, tm, tn); break;
+        case EPI_BF16_ACCF32:
+            gemm_nt64_k<256, 256, WM, WN, EPI_BF16_ACCF32, TA, TB><<<grid, block, 0, s>>>(a, tm, tn);
+            break;
+        default: return hipErrorNotSupported;
+    }
+    return hipGetLastError();
+}
+
 inline bool al16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; }
 
 }  // namespace
 
-hipError_t gemm_nt_direct(GemmEpi epi, const GemmArgs& a, hipStream_t s) {
+hipError_t gemm_direct(GemmLayout lay, GemmEpi epi, const GemmArgs& a, hipStream_t s) {
     // Preconditions beyond gemm()'s checks: 4-column epilogue vectors stay
-    // aligned, and a block's rows x ld fit the 31-bit buffer offsets.
+    // aligned, and a block's extent fits the 31-bit buffer offsets (a
+    // k-contiguous operand: 256 rows x ld; a k-major one: K rows x ld).
     const bool resid = epi == EPI_BF16_RESID || epi == EPI_F32_RESID || epi == EPI_BF16_RESID32 ||
                        epi == EPI_F32_F16IN_RESID;
     if ((a.ldc & 3) || !al16(a.C)) return hipErrorNotSupported;
     if (resid && ((a.ldr & 3) || !al16(a.R))) return hipErrorNotSupported;
     if (epi == EPI_BF16_ACCF32 && ((a.ldacc & 3) || !al16(a.Cacc))) return hipErrorNotSupported;
-    if (a.lda > (int64_t(1) << 21) || a.ldb > (int64_t(1) << 21)) return hipErrorNotSupported;
+    const bool ta = lay == GEMM_TN, tb = lay != GEMM_NT;
+    constexpr int64_t lim = (int64_t(1) << 30) - 256;  // elements below 2^31 bytes
+    if (ta ? int64_t(a.K) * a.lda > lim : a.lda > (int64_t(1) << 21)) return hipErrorNotSupported;
+    if (tb ? int64_t(a.K) * a.ldb > lim : a.ldb > (int64_t(1) << 21)) return hipErrorNotSupported;
     const int64_t big_tiles = int64_t((a.M + 255) / 256) * ((a.N + 255) / 256);
-    if (big_tiles >= MT_NT_BIG_MIN) return launch<256, 256, MT_NT_WM, MT_NT_NW / MT_NT_WM, MT_NT_K64 != 0>(epi, a, s);
-    return launch<128, 128, 2, 2, false>(epi, a, s);
+    if (lay == GEMM_NT) {
+        if (big_tiles >= MT_NT_BIG_MIN)
+            return launch<256, 256, MT_NT_WM, MT_NT_NW / MT_NT_WM, MT_NT_K64 != 0>(epi, a, s);
+        return launch<128, 128, 2, 2, false>(epi, a, s);
+    }
+    if (!MT_GEMM_KMAJOR || !MT_NT_K64 || big_tiles < MT_NT_BIG_MIN) return hipErrorNotSupported;
+    return ta ? launch_kmajor<true, true>(epi, a, s) : launch_kmajor<false, true>(epi, a, s);
 }
 
 }  // namespace mt

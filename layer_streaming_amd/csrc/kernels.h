@@ -35,10 +35,16 @@ struct GemmArgs {
     int M, N, K;
 };
 hipError_t gemm(GemmLayout lay, GemmEpi epi, const GemmArgs& a, hipStream_t s);
-// The NT path with direct global->LDS tile loads (called by gemm() after its
-// checks); hipErrorNotSupported when its alignment or size preconditions
-// fail, and gemm() then uses the generic kernel.
-hipError_t gemm_nt_direct(GemmEpi epi, const GemmArgs& a, hipStream_t s);
+// The path with direct global->LDS tile loads (called by gemm() after its
+// checks): every NT product, and NN / TN products on grids of at least
+// 120 tiles of 256 x 256 with the epilogues EPI_BF16, EPI_F32, EPI_F32_ACC
+// and EPI_BF16_ACCF32 (their k-major operands read transposed from LDS).
+// hipErrorNotSupported when a precondition fails; gemm() then uses the
+// generic kernel, and the backward products transpose and take the NT form.
+hipError_t gemm_direct(GemmLayout lay, GemmEpi epi, const GemmArgs& a, hipStream_t s);
+// gemm()'s argument checks, then gemm_direct: hipErrorInvalidValue for bad
+// arguments, hipErrorNotSupported when only the generic kernel could run it.
+hipError_t gemm_direct_checked(GemmLayout lay, GemmEpi epi, const GemmArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------- RMSNorm ----
 // n = gamma * x * rstd, rstd = 1/sqrt(mean(x^2)+eps); x bf16 or fp32 (x_f32),

@@ -139,6 +139,62 @@ def test_gemm_nt_large_tile_form(M, N, K):
     _elementwise_check(got, ref, A, B, "C", K)
 
 
+# NN and TN grids of at least 120 tiles of 256 x 256 read their k-major
+# operands straight (transposed fragments from LDS): ragged M, N and K,
+# leading dimensions wider than the operands, the backward products' shapes.
+KMAJOR_CASES = [(1, 4104, 4040, 200, 24, 8), (2, 4104, 4040, 997, 16, 8), (1, 2056, 7176, 520, 0, 0),
+                (2, 3584, 4608, 1000, 0, 0), (2, 4608, 3584, 136, 8, 16)]
+
+
+@pytest.mark.parametrize("layout,M,N,K,pa,pb", KMAJOR_CASES)
+def test_gemm_kmajor_large_tile_form(layout, M, N, K, pa, pb):
+    log(f"gemm k-major large-tile form layout={layout} M={M} N={N} K={K} pads {pa},{pb}")
+    a_cols = K if layout == 1 else M
+    A = synth.bf16_exact_normal(RNG, (M, K + pa) if layout == 1 else (K, M + pa))
+    B = synth.bf16_exact_normal(RNG, (K, N + pb))
+    opA = A[:, :K] if layout == 1 else A[:, :M].T
+    opB = B[:, :N]
+    ref = opA.astype(np.float64) @ opB.astype(np.float64)
+    dA, dB = dev_bits(A), dev_bits(B)
+    dC = dev_zeros_bits((M, N + 4))
+    mt.check(mt.lib.mt_k_gemm(layout, 0, dA.data_ptr(), a_cols + pa, dB.data_ptr(), N + pb, dC.data_ptr(), N + 4,
+                              None, 0, None, 0, M, N, K, _stream()), "gemm")
+    _sync()
+    full = host_f32(dC)
+    got = full[:, :N]
+    assert_close(got, ref, "C")
+    _elementwise_check(got, ref, np.ascontiguousarray(opA), np.ascontiguousarray(opB.T), "C", K)
+    assert np.all(full[:, N:] == 0), "columns past N written"
+
+
+def test_gemm_kmajor_head_epilogues():
+    """The TN epilogues the vocabulary-chunked head's dW runs on the k-major
+    form: fp32 out, fp32 accumulate, bf16 from an fp32 partial."""
+    M, N, K = 4104, 3584, 300
+    log(f"gemm TN k-major epilogues M={M} N={N} K={K}")
+    A = synth.bf16_exact_normal(RNG, (K, M))
+    B = synth.bf16_exact_normal(RNG, (K, N))
+    ref = A.T.astype(np.float64) @ B.astype(np.float64)
+    dA, dB = dev_bits(A), dev_bits(B)
+    s = _stream()
+    c32 = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+
+    def run(epi, C, acc=None):
+        mt.check(mt.lib.mt_k_gemm(2, epi, dA.data_ptr(), M, dB.data_ptr(), N, C.data_ptr(), N, None, 0, acc,
+                                  N if acc else 0, M, N, K, s), f"gemm epi {epi}")
+        _sync()
+
+    run(2, c32)
+    got32 = c32.cpu().numpy()
+    assert_close(got32, ref, "C f32", tol=1e-5)
+    _elementwise_check(got32, ref, np.ascontiguousarray(A.T), np.ascontiguousarray(B.T), "C f32", K)
+    run(3, c32)
+    assert_close(c32.cpu().numpy(), 2 * ref, "C f32 += ", tol=1e-5)
+    dC = dev_zeros_bits((M, N))
+    run(4, dC, acc=c32.data_ptr())
+    assert_close(host_f32(dC), 3 * ref, "C bf16 from f32 partial")
+
+
 @pytest.mark.parametrize("ldc", [4044, 4048])
 def test_gemm_nt_large_tile_partial_column_chunk(ldc):
     """bf16 output whose last 8-column chunk is cut by N (N = 4044), with a
