@@ -1238,6 +1238,7 @@ hipError_t Ctx::head_chunk_bwd(const HeadChunk& ch, bool first, bool last, const
     uint16_t* gE = g + eoff;
     const int tc = int(std::min<int64_t>(ws.head_chunk, T));
     const int nch = (T + tc - 1) / tc;
+    bool tB_holds_chunk = false;  // E^T of this vocabulary chunk in the workspace
     for (int c = 0; c < nch; ++c) {
         const int r0 = c * tc, rows = std::min(tc, T - r0);
         HIPR(site(S_HEAD_LOGITS, [&] {
@@ -1249,12 +1250,22 @@ hipError_t Ctx::head_chunk_bwd(const HeadChunk& ch, bool first, bool last, const
                                 inv_tokens, s);
         }));
         HIPR(site(S_HEAD_DX, [&] {
-            // dX = dlogits E as the NT product on E^T, transposed once per
+            // dX = dlogits E, E read k-major where the direct kernel takes
+            // the grid; else the NT product on E^T, transposed once per
             // vocabulary chunk (the workspace holds d x the largest chunk)
-            if (c == 0) HIPR(transpose16(E, d, ws.tB, ch.rows, ch.rows, d, s));
-            GemmArgs a{ws.dlogits, ch.rows, ws.tB, ch.rows, ws.dnf_acc + int64_t(r0) * d, d, nullptr, 0, nullptr, 0,
-                       rows, d, ch.rows};
-            return gemm(GEMM_NT, first ? EPI_F32 : EPI_F32_ACC, a, s);
+            const GemmEpi epi = first ? EPI_F32 : EPI_F32_ACC;
+            float* dx = ws.dnf_acc + int64_t(r0) * d;
+            {
+                GemmArgs a{ws.dlogits, ch.rows, E, d, dx, d, nullptr, 0, nullptr, 0, rows, d, ch.rows};
+                const hipError_t e = gemm_direct_checked(GEMM_NN, epi, a, s);
+                if (e != hipErrorNotSupported) return e;
+            }
+            if (!tB_holds_chunk) {
+                HIPR(transpose16(E, d, ws.tB, ch.rows, ch.rows, d, s));
+                tB_holds_chunk = true;
+            }
+            GemmArgs a{ws.dlogits, ch.rows, ws.tB, ch.rows, dx, d, nullptr, 0, nullptr, 0, rows, d, ch.rows};
+            return gemm(GEMM_NT, epi, a, s);
         }));
         HIPR(site(S_HEAD_DW, [&] {
             GemmArgs a{ws.dlogits, ch.rows, ws.nf + int64_t(r0) * d, d, nullptr, d, nullptr, 0, nullptr, 0,
@@ -1294,12 +1305,13 @@ hipError_t Ctx::gemm_nn_t(const uint16_t* A, int64_t lda, const uint16_t* Bm, in
 // C[M x N] = A^T B with A stored [K x M] and B [K x N]: straight from the
 // k-major operands where the direct kernel takes the grid, else both
 // transposed, then NT; K (the tokens) is then padded to a multiple of 8 with
-// zero columns, which add nothing.  b_f16: B holds fp16, rounded to bf16 by
-// its transpose (always the transposed form).
+// zero columns, which add nothing.  b_f16: B holds fp16, rounded to bf16 as
+// its fragments are read, or by its transpose.
 hipError_t Ctx::gemm_tn_t(const uint16_t* A, int64_t lda, const uint16_t* Bm, int64_t ldb, uint16_t* C, int64_t ldc,
                           int M, int N, int K, bool b_f16) {
-    if (!b_f16) {
+    {
         GemmArgs a{A, lda, Bm, ldb, C, ldc, nullptr, 0, nullptr, 0, M, N, K};
+        a.b_f16 = b_f16;
         const hipError_t e = gemm_direct_checked(GEMM_TN, EPI_BF16, a, st_c);
         if (e != hipErrorNotSupported) return e;
     }

@@ -316,6 +316,7 @@ static hipError_t gemm_check(GemmLayout lay, GemmEpi epi, const GemmArgs& a) {
     if (epi == EPI_BF16_ACCF32 && (!a.Cacc || a.ldacc < a.N)) return hipErrorInvalidValue;
     if ((epi == EPI_F32_F16IN || epi == EPI_F32_F16IN_RESID) && lay != GEMM_NT) return hipErrorInvalidValue;
     if (int(epi) < 0 || int(epi) > int(EPI_F32_F16IN_RESID)) return hipErrorInvalidValue;
+    if (a.b_f16 && (lay != GEMM_TN || epi != EPI_BF16)) return hipErrorInvalidValue;
     return hipSuccess;
 }
 
@@ -331,6 +332,7 @@ hipError_t gemm(GemmLayout lay, GemmEpi epi, const GemmArgs& a, hipStream_t s) {
         const hipError_t e = gemm_direct(lay, epi, a, s);
         if (e != hipErrorNotSupported) return e;
     }
+    if (a.b_f16) return hipErrorNotSupported;  // only the direct form converts B
     switch (lay) {
         case GEMM_NT: return launch_layout<true, true>(epi, a, s);
         case GEMM_NN: return launch_layout<true, false>(epi, a, s);

@@ -603,7 +603,14 @@ __device__ __forceinline__ uint4 frag_kmajor(const uint4* t, int ks, int col0, i
     return make_uint4(r[0].x, r[0].y, r[1].x, r[1].y);
 }
 
-template <int FM, int FN, int TM, int TN, bool TA = false, bool TB = false, int BM = 0, int BN = 0>
+// fp16 fragment rounded to bf16 (exact widening, then round to nearest even).
+__device__ __forceinline__ uint4 f16_frag_to_bf16(const uint4& v) {
+    typedef float f32x8_t __attribute__((ext_vector_type(8)));
+    const f32x8_t f = __builtin_convertvector(as_f16x8(v), f32x8_t);
+    return __builtin_bit_cast(uint4, __builtin_convertvector(f, bf16x8_t));
+}
+
+template <int FM, int FN, int TM, int TN, bool TA = false, bool TB = false, int BM = 0, int BN = 0, bool BH = false>
 __device__ __forceinline__ void read_frags64(const uint4* __restrict__ a_l, const uint4* __restrict__ b_l, int ks,
                                              int wm, int wn, int lane, uint4 (&fa)[FM], uint4 (&fb)[FN]) {
     const int kc = ks * 2 + (lane >> 5);
@@ -620,6 +627,7 @@ __device__ __forceinline__ void read_frags64(const uint4* __restrict__ a_l, cons
     for (int j = 0; j < FN; ++j) {
         if constexpr (TB) {
             fb[j] = frag_kmajor<BN>(b_l, ks, wn * TN + j * 32, lane);
+            if constexpr (BH) fb[j] = f16_frag_to_bf16(fb[j]);
         } else {
             const int r = wn * TN + j * 32 + (lane & 31);
             fb[j] = b_l[r * 8 + (kc ^ swz8(r))];
@@ -629,7 +637,8 @@ __device__ __forceinline__ void read_frags64(const uint4* __restrict__ a_l, cons
 
 // TA / TB: A / B stored k-major (A [K x M], B [K x N]); the other layouts
 // of C = op(A) op(B) then run on the same main loop with no transposed copy.
-template <int BM, int BN, int WM, int WN, int EPI, bool TA = false, bool TB = false>
+// BH: B holds fp16 values, rounded to bf16 as each fragment is read.
+template <int BM, int BN, int WM, int WN, int EPI, bool TA = false, bool TB = false, bool BH = false>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_nt64_k(GemmArgs p, int tiles_m, int tiles_n) {
     constexpr int NW = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
@@ -694,7 +703,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt64_k(GemmArgs p, int tile
     const int nk = (p.K + BK64 - 1) / BK64;
     uint4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
 
-#define RD(SA, SB, KS, FA, FB) read_frags64<FM, FN, TM, TN, TA, TB, BM, BN>(SA, SB, KS, wm, wn, lane, FA, FB)
+#define RD(SA, SB, KS, FA, FB) read_frags64<FM, FN, TM, TN, TA, TB, BM, BN, BH>(SA, SB, KS, wm, wn, lane, FA, FB)
 #define MM(FA, FB) mma_frags<FM, FN, F16>(FA, FB, acc)
 #define PRIO(x) if (MT_NT_PRIO) __builtin_amdgcn_s_setprio(x)
 #define LOAD_ONE(g, XA, XB, T)                                                           \
@@ -832,6 +841,14 @@ hipError_t launch_kmajor(GemmEpi epi, const GemmArgs& a, hipStream_t s) {
     constexpr int WM = MT_NT_WM, WN = MT_NT_NW / MT_NT_WM;
     const int tm = (a.M + 255) / 256, tn = (a.N + 255) / 256;
     const dim3 grid(tm * tn), block(WM * WN * 64);
+    if (a.b_f16) {
+        if constexpr (TA && TB) {
+            if (epi != EPI_BF16) return hipErrorNotSupported;
+            gemm_nt64_k<256, 256, WM, WN, EPI_BF16, true, true, true><<<grid, block, 0, s>>>(a, tm, tn);
+            return hipGetLastError();
+        }
+        return hipErrorNotSupported;
+    }
     switch (epi) {
         case EPI_BF16: gemm_nt64_k<256, 256, WM, WN, EPI_BF16, TA, TB><<<grid, block, 0, s>>>(a, tm, tn); break;
         case EPI_F32: gemm_nt64_k<256, 256, WM, WN, EPI_F32, TA, TB><<<grid, block, 0, s>>>(a, tm, tn); break;
@@ -858,6 +875,7 @@ hipError_t gemm_direct(GemmLayout lay, GemmEpi epi, const GemmArgs& a, hipStream
     if (resid && ((a.ldr & 3) || !al16(a.R))) return hipErrorNotSupported;
     if (epi == EPI_BF16_ACCF32 && ((a.ldacc & 3) || !al16(a.Cacc))) return hipErrorNotSupported;
     const bool ta = lay == GEMM_TN, tb = lay != GEMM_NT;
+    if (a.b_f16 && !(ta && epi == EPI_BF16)) return hipErrorNotSupported;
     constexpr int64_t lim = (int64_t(1) << 30) - 256;  // elements below 2^31 bytes
     if (ta ? int64_t(a.K) * a.lda > lim : a.lda > (int64_t(1) << 21)) return hipErrorNotSupported;
     if (tb ? int64_t(a.K) * a.ldb > lim : a.ldb > (int64_t(1) << 21)) return hipErrorNotSupported;

@@ -33,12 +33,14 @@ struct GemmArgs {
     const void* R; int64_t ldr;       // residual (EPI_*RESID*)
     const float* Cacc; int64_t ldacc; // fp32 partial sum, EPI_BF16_ACCF32
     int M, N, K;
+    bool b_f16 = false;               // B holds fp16, rounded to bf16 as it is read (TN, EPI_BF16, direct form only)
 };
 hipError_t gemm(GemmLayout lay, GemmEpi epi, const GemmArgs& a, hipStream_t s);
 // The path with direct global->LDS tile loads (called by gemm() after its
 // checks): every NT product, and NN / TN products on grids of at least
 // 120 tiles of 256 x 256 with the epilogues EPI_BF16, EPI_F32, EPI_F32_ACC
-// and EPI_BF16_ACCF32 (their k-major operands read transposed from LDS).
+// and EPI_BF16_ACCF32 (their k-major operands read transposed from LDS), and
+// TN with an fp16 B (b_f16) and EPI_BF16.
 // hipErrorNotSupported when a precondition fails; gemm() then uses the
 // generic kernel, and the backward products transpose and take the NT form.
 hipError_t gemm_direct(GemmLayout lay, GemmEpi epi, const GemmArgs& a, hipStream_t s);
