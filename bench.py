@@ -67,8 +67,8 @@ SHAPES["70b_x4"] = SHAPES["70b"]
 # profiles/gemm_gateup_traffic_7b.md.  Valid only for the kernel sources it was
 # taken on (sha256 over the files in order): reported as null once they change.
 TRAFFIC = {"sources": ["layer_streaming_amd/csrc/gemm_nt.hip", "layer_streaming_amd/csrc/kcommon.h"],
-           "sha256": "7335c133c6005fe4a6986c7c795709213a6682bf8d7fdf0a82d06c4a40f09c81",
-           "fetch_bytes": 3317900506, "write_bytes": 620756992}
+           "sha256": "886b271e3c1bbd04a8443fe1984e97586272442d8dc9f4d6ee884d379e49acb3",
+           "fetch_bytes": 3317853709, "write_bytes": 620756992}
 
 
 def traffic_bytes(config):
