@@ -644,6 +644,10 @@ def main():
                     help="only measure host DRAM: the host Adam alone at 8/12/16 threads, a parallel copy and read")
     ap.add_argument("--micro", type=int, default=1,
                     help="micro-batches of batch x seq per optimizer step (gradient accumulation on the host)")
+    ap.add_argument("--ckpt-attn", type=int, default=-1,
+                    help="1: checkpoint each layer's attention output and log-sum-exp with its input, so the "
+                         "backward's recompute skips the attention forward (same results); 0: recompute it; "
+                         "-1 (default): 1 for sequences of 8192 and longer, where that forward dominates")
     ap.add_argument("--keep-grads", type=int, default=0,
                     help="0 (default): with one micro-batch Adam reads each gradient slab without copying it into "
                          "the store's G (2 B/param less host traffic; same weights and optimizer state); 1: the "
@@ -675,11 +679,12 @@ def main():
         attention_probe(torch, mt, cfg, args.attn_probe, args.attn_batch)
         return
     torch.cuda.init()
+    ckpt_attn = args.ckpt_attn if args.ckpt_attn >= 0 else int(cfg["seq"] >= 8192)
     opt_kw = dict(profile_kernels=0 if args.no_profile else 1, host_threads=args.host_threads,
                   n_weight_slots=args.slots, n_grad_slabs=args.slabs, slot_mode=args.slot_mode,
                   resident=args.resident, pin_store=args.pin_store, cross_step=args.cross_step,
                   pin_weights=args.pin_weights, head_vocab_chunk=args.head_vocab_chunk,
-                  keep_grads=args.keep_grads)
+                  keep_grads=args.keep_grads, ckpt_attn=ckpt_attn)
     if args.depths:
         depth_sweep(torch, mt, cfg, args, opt_kw)
         return
@@ -705,21 +710,25 @@ def main():
                       "parallelism": "single GPU, layer-streamed", "weight_slots": args.slots,
                       "grad_slabs": args.slabs, "slot_mode": args.slot_mode, "resident": args.resident,
                       "cross_step": args.cross_step, "pin_weights": args.pin_weights,
-                      "head_vocab_chunk": args.head_vocab_chunk, "keep_grads": args.keep_grads}}
+                      "head_vocab_chunk": args.head_vocab_chunk, "keep_grads": args.keep_grads,
+                      "ckpt_attn": ckpt_attn}}
     mf = nm * model_flops_per_step(cfg, T, S)
     out["model_tflops_per_s"] = round(mf / (ms_per_step / 1e3) / 1e12, 2)
     out["pages_convention_tflops_per_s"] = round(nm * pages_flops_per_step(cfg, T, S) / (ms_per_step / 1e3) / 1e12, 2)
     # hardware FLOPs add the recomputed forward of every layer (the down GEMM
-    # is not recomputed: backward needs its input, not its output)
+    # is not recomputed: backward needs its input, not its output; nor is the
+    # attention forward when its output is checkpointed)
     fl0 = gemm_flops(cfg, T)
     recompute = cfg["n_layers"] * (fl0["gemm_qkv"] + fl0["gemm_o"] + fl0["gemm_gateup"] +
-                                   2 * 2 * T * cfg["n_heads"] * cfg["head_dim"] * (S + 1) / 2)
+                                   (0 if ckpt_attn else 2 * 2 * T * cfg["n_heads"] * cfg["head_dim"] * (S + 1) / 2))
     # a vocabulary-chunked head (head_vocab_chunk != 0) computes the logits
     # twice: its backward recomputes each chunk's logits
     logit_passes = 2 if args.head_vocab_chunk != 0 else 1
     recompute += (logit_passes - 1) * head_gemm_flops(cfg, T)
     out["hw_tflops_per_s"] = round((mf + nm * recompute) / (ms_per_step / 1e3) / 1e12, 2)
     hb_step = host_bytes_per_step(cfg, T, nm, pinned=bool(args.pin_weights), keep_grads=bool(args.keep_grads))
+    if ckpt_attn:  # the attention checkpoint ring, written in forward and read in backward
+        hb_step += nm * 2 * cfg["n_layers"] * T * cfg["n_heads"] * (2 * cfg["head_dim"] + 4)
     out["host_memory"] = {"bytes_per_step": int(hb_step), "achieved_GBps": round(hb_step / (ms_per_step / 1e3) / 1e9, 1),
                           "adam_alone_GBps": host_adam_probe(mt)}
     out["pcie"] = pcie_block(stats)

@@ -131,6 +131,14 @@ typedef struct mt_options {
                                     and G is not written (2 B/param less host-DRAM traffic per
                                     step); G still accumulates micro-batches, and
                                     mt_get_tensor(MT_G) is refused.  Same W, master, m, v */
+    int32_t ckpt_attn;           /* 1: the forward also checkpoints every layer's attention output
+                                    (fp16) and log-sum-exp (fp32) to a second pinned host ring,
+                                    and the backward's recompute restores them instead of running
+                                    the attention forward again: long sequences, where that
+                                    forward dominates the recompute, trade T*Hq*hd*2 + T*Hq*4
+                                    bytes per layer each way over PCIe for it.  Needs
+                                    ckpt_on_host = 1 and ckpt_interval = 1.  Same results as 0
+                                    (default) */
     uint64_t slot_bytes_override;      /* 0: largest unit's weight bytes */
     uint64_t workspace_bytes_override; /* 0: computed from max_batch*max_seq */
     float lr, beta1, beta2, adam_eps;  /* 1e-4, 0.9, 0.999, 1e-8 */

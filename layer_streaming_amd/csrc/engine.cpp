@@ -139,6 +139,12 @@ int64_t stream_elems_max(const Layout& lay, const mt_options& o) {
     return m;
 }
 
+// One layer's checkpointed attention: the fp16 output, then the fp32 log-sum-exp.
+uint64_t attn_ckpt_o_bytes(const mt_shape& sh, uint64_t T) { return al4k(T * sh.n_heads * sh.head_dim * 2); }
+uint64_t attn_ckpt_bytes(const mt_shape& sh, uint64_t T) {
+    return attn_ckpt_o_bytes(sh, T) + al4k(T * sh.n_heads * 4);
+}
+
 // Checkpoint interval, capped at the depth, and the host ring entries it needs.
 int ckpt_k(const mt_options& o, const mt_shape& sh) { return std::max(1, std::min(o.ckpt_interval, sh.n_layers)); }
 int ckpt_slots(const mt_options& o, const mt_shape& sh) {
@@ -197,6 +203,12 @@ void plan_workspace(const Layout& lay, const mt_options& o, Carver& cv, Workspac
     ws.rstd1 = cv.take<float>(uint64_t(T) * 4);
     ws.rstd2 = cv.take<float>(uint64_t(T) * 4);
     ws.lse = cv.take<float>(uint64_t(T) * sh.n_heads * 4);
+    ws.oa[0] = ws.oa[1] = ws.o;
+    ws.lsea[0] = ws.lsea[1] = ws.lse;
+    if (o.ckpt_attn) {
+        ws.oa[1] = cv.take<uint16_t>(uint64_t(T) * nq * 2);
+        ws.lsea[1] = cv.take<float>(uint64_t(T) * sh.n_heads * 4);
+    }
     ws.dsum = cv.take<float>(uint64_t(T) * sh.n_heads * 4 * 2);
     ws.partial = cv.take<float>(uint64_t(rmsnorm_bwd_partial_elems(int(T), int(d))) * 4);
     ws.rope_tab = cv.take<float2>(uint64_t(o.max_seq) * (sh.head_dim / 2) * 8);
@@ -281,6 +293,7 @@ PinnedPlan plan_pinned(const Layout& lay, const mt_options& o, uint64_t slot_byt
     p.weights = o.pin_weights ? uint64_t(lay.w_bytes) : 0;
     p.slab = uint64_t(o.n_grad_slabs) * slot_bytes;
     p.ckpt = o.ckpt_on_host ? al4k(T * lay.sh.d_model * 2) * ckpt_slots(o, lay.sh) : 0;
+    if (o.ckpt_attn) p.ckpt += attn_ckpt_bytes(lay.sh, T) * uint64_t(lay.sh.n_layers);
     p.io = 2 * al4k(T * lay.sh.d_model * 2) + al4k(T * 4) + 4096;
     p.total = p.staging + p.slab + p.ckpt + p.io + p.weights;
     return p;
@@ -305,6 +318,9 @@ int validate_options(const mt_options* o) {
     if (o->poison_released && (o->slot_mode != 0 || o->resident))
         MT_FAIL(MT_E_INVAL, "poison_released needs slot_mode 0 and resident 0");
     if (o->keep_grads != 0 && o->keep_grads != 1) MT_FAIL(MT_E_INVAL, "keep_grads must be 0 or 1");
+    if (o->ckpt_attn != 0 && o->ckpt_attn != 1) MT_FAIL(MT_E_INVAL, "ckpt_attn must be 0 or 1");
+    if (o->ckpt_attn && (!o->ckpt_on_host || o->ckpt_interval != 1))
+        MT_FAIL(MT_E_INVAL, "ckpt_attn needs ckpt_on_host = 1 and ckpt_interval = 1");
     if (!(o->lr >= 0.f) || !(o->beta1 >= 0.f && o->beta1 < 1.f) || !(o->beta2 >= 0.f && o->beta2 < 1.f) ||
         !(o->adam_eps > 0.f))
         MT_FAIL(MT_E_INVAL, "bad Adam hyper-parameters");
@@ -329,6 +345,7 @@ struct Ctx {
     uint8_t* staging[2] = {};
     std::vector<uint8_t*> slabs;
     uint8_t* ckpt_host = nullptr;
+    uint8_t* attn_host = nullptr;  // ckpt_attn: per layer, o (fp16) then lse (fp32)
     uint16_t *x0_pin = nullptr, *dx0_pin = nullptr;
     int32_t* lab_pin = nullptr;
     float* loss_pin = nullptr;
@@ -342,6 +359,7 @@ struct Ctx {
     hipStream_t st_c = nullptr, st_w = nullptr, st_g = nullptr;
     bool own[3] = {false, false, false};
     std::vector<Ev> wready, slot_free, bwd_done, buf_free, slab_done;
+    Ev attn_ck_done[2], attn_buf_free[2];  // ckpt_attn: a buffer's D2H done / its last backward reader done
     Ev staging_free[2], xc_free[2], ckpt_done[2], xready, emb_ready, fwd_ckpt_all, dx0_done, loss_done,
         res_ready;
     std::vector<hipEvent_t> tev;  // timing events
@@ -514,9 +532,13 @@ struct Ctx {
         site_recs.push_back({id, a, b});
         return e;
     }
-    hipError_t fwd_layer(const LayerView& w, const uint16_t* x, uint16_t* y, int B, int S, bool need_y);
+    // ob: which attention output / log-sum-exp pair (ws.oa, ws.lsea) the
+    // layer uses; attn_restored: that pair already holds the checkpointed
+    // attention of this layer, so the recompute skips the attention forward.
+    hipError_t fwd_layer(const LayerView& w, const uint16_t* x, uint16_t* y, int B, int S, bool need_y, int ob = 0,
+                         bool attn_restored = false);
     hipError_t bwd_layer(const LayerView& w, const LayerView& g, const uint16_t* x, const uint16_t* dy,
-                         uint16_t* dx, int B, int S);
+                         uint16_t* dx, int B, int S, int ob = 0, bool attn_restored = false);
     hipError_t head(const HeadView& w, const HeadView& g, const uint16_t* xL, uint16_t* dy, int B, int S,
                     float inv_tokens);
     hipError_t head_chunk_fwd(const HeadChunk& ch, bool first, bool last, const void* wbase, const uint16_t* xL,
@@ -646,6 +668,10 @@ int Ctx::init(const mt_shape& sh, const mt_options& o, void* arena_, uint64_t by
         ckpt_host = pinned_alloc(this, td * uint64_t(ckpt_slots(opt, sh)));
         if (!ckpt_host) MT_FAIL(MT_E_NOMEM, "cannot allocate the pinned checkpoint ring");
     }
+    if (opt.ckpt_attn) {
+        attn_host = pinned_alloc(this, attn_ckpt_bytes(sh, T) * uint64_t(sh.n_layers));
+        if (!attn_host) MT_FAIL(MT_E_NOMEM, "cannot allocate the pinned attention checkpoint ring");
+    }
     x0_pin = reinterpret_cast<uint16_t*>(pinned_alloc(this, td));
     dx0_pin = reinterpret_cast<uint16_t*>(pinned_alloc(this, td));
     lab_pin = reinterpret_cast<int32_t*>(pinned_alloc(this, al4k(T * 4)));
@@ -671,7 +697,8 @@ int Ctx::init(const mt_shape& sh, const mt_options& o, void* arena_, uint64_t by
     for (auto* v : {&wready, &slot_free, &bwd_done, &buf_free, &slab_done})
         for (auto& e : *v) HIPC(mk(e));
     for (Ev* e : {&staging_free[0], &staging_free[1], &xc_free[0], &xc_free[1], &ckpt_done[0], &ckpt_done[1],
-                  &xready, &emb_ready, &fwd_ckpt_all, &dx0_done, &loss_done, &res_ready})
+                  &xready, &emb_ready, &fwd_ckpt_all, &dx0_done, &loss_done, &res_ready, &attn_ck_done[0],
+                  &attn_ck_done[1], &attn_buf_free[0], &attn_buf_free[1]})
         HIPC(mk(*e));
     HIPC(hipEventCreate(&t_base));
     for (int i = 0; i < 1024; ++i) {
@@ -721,7 +748,8 @@ Ctx::~Ctx() {
         for (auto& e : *v)
             if (e.e) hipEventDestroy(e.e);
     for (Ev* e : {&staging_free[0], &staging_free[1], &xc_free[0], &xc_free[1], &ckpt_done[0], &ckpt_done[1],
-                  &xready, &emb_ready, &fwd_ckpt_all, &dx0_done, &loss_done, &res_ready})
+                  &xready, &emb_ready, &fwd_ckpt_all, &dx0_done, &loss_done, &res_ready, &attn_ck_done[0],
+                  &attn_ck_done[1], &attn_buf_free[0], &attn_buf_free[1]})
         if (e->e) hipEventDestroy(e->e);
     for (auto e : tev) hipEventDestroy(e);
     if (t_base) hipEventDestroy(t_base);
@@ -1085,7 +1113,8 @@ hipError_t Ctx::ensure_rope(int S) {
 // Forward of one decoder layer on the compute stream.  With need_y false
 // (the recompute before backward) the last GEMM is skipped: backward needs
 // the intermediates, not the output.
-hipError_t Ctx::fwd_layer(const LayerView& w, const uint16_t* x, uint16_t* y, int B, int S, bool need_y) {
+hipError_t Ctx::fwd_layer(const LayerView& w, const uint16_t* x, uint16_t* y, int B, int S, bool need_y, int ob,
+                          bool attn_restored) {
     const mt_shape& sh = lay.sh;
     const int T = B * S, d = sh.d_model, F = sh.ffn_dim;
     const int nq = sh.n_heads * sh.head_dim;
@@ -1110,14 +1139,16 @@ hipError_t Ctx::fwd_layer(const LayerView& w, const uint16_t* x, uint16_t* y, in
         return qkv_rope_cvt(ws.qkv32, nqkv, ws.qkv, nqkv, nullptr, 0, ws.rope_tab, T, S, sh.n_heads + sh.n_kv_heads,
                             sh.n_heads + 2 * sh.n_kv_heads, sh.head_dim, s, ws.ovf);
     }));
-    HIPR(site(S_ATTN_FWD, [&] {
-        AttnArgs a{ws.qkv, nqkv, ws.o, nq, ws.lse, B, S, sh.n_heads, sh.n_kv_heads, sh.head_dim, ws.ovf};
-        return attn_fwd(a, s);
-    }));
+    if (!attn_restored) {
+        HIPR(site(S_ATTN_FWD, [&] {
+            AttnArgs a{ws.qkv, nqkv, ws.oa[ob], nq, ws.lsea[ob], B, S, sh.n_heads, sh.n_kv_heads, sh.head_dim, ws.ovf};
+            return attn_fwd(a, s);
+        }));
+    }
     HIPR(site(S_GEMM_O, [&] {
         // ws.w16 is free again: the QKV product before it on this stream read it
         HIPR(bf16_to_f16(w.wo, ws.w16, int64_t(d) * nq, s, ws.ovf));
-        GemmArgs a{ws.o, nq, ws.w16, nq, ws.h1, d, x, d, nullptr, 0, T, d, nq};
+        GemmArgs a{ws.oa[ob], nq, ws.w16, nq, ws.h1, d, x, d, nullptr, 0, T, d, nq};
         return gemm(GEMM_NT, EPI_F32_F16IN_RESID, a, s);
     }));
     HIPR(site(S_RMS2_FWD, [&] { return rmsnorm_fwd(ws.h1, true, w.g2, ws.n2, nullptr, ws.rstd2, T, d, sh.rms_eps, s); }));
@@ -1138,8 +1169,8 @@ hipError_t Ctx::fwd_layer(const LayerView& w, const uint16_t* x, uint16_t* y, in
 // Recompute, then backward of one decoder layer; writes dx and the layer's
 // BF16 gradients into the views g.
 hipError_t Ctx::bwd_layer(const LayerView& w, const LayerView& g, const uint16_t* x, const uint16_t* dy,
-                          uint16_t* dx, int B, int S) {
-    HIPR(fwd_layer(w, x, nullptr, B, S, false));
+                          uint16_t* dx, int B, int S, int ob, bool attn_restored) {
+    HIPR(fwd_layer(w, x, nullptr, B, S, false, ob, attn_restored));
     const mt_shape& sh = lay.sh;
     const int T = B * S, d = sh.d_model, F = sh.ffn_dim;
     const int nq = sh.n_heads * sh.head_dim;
@@ -1159,14 +1190,14 @@ hipError_t Ctx::bwd_layer(const LayerView& w, const LayerView& g, const uint16_t
     }));
     // attention
     HIPR(site(S_GEMM_O_DX, [&] { return gemm_nn_t(ws.dh1, d, w.wo, nq, ws.dout, nq, T, nq, d); }));
-    // o is fp16: its transpose rounds it to bf16 for the bf16 product
-    HIPR(site(S_GEMM_O_DW, [&] { return gemm_tn_t(ws.dh1, d, ws.o, nq, g.wo, nq, d, nq, T, true); }));
+    // o is fp16: rounded to bf16 for the bf16 product
+    HIPR(site(S_GEMM_O_DW, [&] { return gemm_tn_t(ws.dh1, d, ws.oa[ob], nq, g.wo, nq, d, nq, T, true); }));
     // The attention backward on the fp16 operands of the recomputed forward:
     // dV into dqkv, dQ and dK in fp32 into the projection buffer (free since
     // the recompute's rotation read it), then rotated back by -theta and
     // rounded to bf16 once.
     HIPR(site(S_ATTN_BWD, [&] {
-        AttnBwdArgs a{ws.qkv, nqkv, ws.o, ws.dout, nq, ws.lse, ws.dsum, ws.do16, ws.amax, ws.dqkv, nqkv,
+        AttnBwdArgs a{ws.qkv, nqkv, ws.oa[ob], ws.dout, nq, ws.lsea[ob], ws.dsum, ws.do16, ws.amax, ws.dqkv, nqkv,
                       B, S, sh.n_heads, sh.n_kv_heads, sh.head_dim, ws.qkv32, nqkv, ws.ovf,
                       reinterpret_cast<float*>(ws.tA), int64_t(ws.tA_bytes / 4), 0};
         return attn_bwd(a, s);
@@ -1461,6 +1492,11 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
     timing = true;
     const uint64_t td = uint64_t(T) * d * 2;
     const uint64_t td_al = al4k(uint64_t(ws.maxT) * d * 2);
+    // ckpt_attn ring: per layer at the workspace's token count, o then lse
+    const uint64_t ab_al = attn_ckpt_bytes(lay.sh, uint64_t(ws.maxT));
+    const uint64_t ao_al = attn_ckpt_o_bytes(lay.sh, uint64_t(ws.maxT));
+    const uint64_t ao_bytes = uint64_t(B) * S * lay.sh.n_heads * lay.sh.head_dim * 2;
+    const uint64_t al_bytes = uint64_t(B) * S * lay.sh.n_heads * 4;
     // Each micro-batch's loss gradient is that of the mean over all n*B*S
     // tokens: 1/(n T) (a power-of-two multiple of 1/T's rounding when n is a
     // power of two).
@@ -1628,6 +1664,17 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
                 HIPC(wait(st_w, xc_free[bank]));
                 HIPC(h2d(xb[0], ckpt_host + uint64_t(unit / K) * td_al, td, st_w));
             }
+            // ckpt_attn: the layer's attention output and log-sum-exp come
+            // back into the pair the backward visit two back has finished with
+            // (the weights-ready event below covers these copies too)
+            const int ob_b = opt.ckpt_attn && kind == V_BWD ? (nbwd & 1) : 0;
+            if (opt.ckpt_attn && kind == V_BWD) {
+                const uint8_t* h = attn_host + uint64_t(unit) * ab_al;
+                HIPC(wait(st_w, fwd_ckpt_all));
+                HIPC(wait(st_w, attn_buf_free[ob_b]));
+                HIPC(h2d(ws.oa[ob_b], h, ao_bytes, st_w));
+                HIPC(h2d(ws.lsea[ob_b], h + ao_al, al_bytes, st_w));
+            }
             Ev& wr = wready[slot];
             HIPC(rec(wr, st_w));
             HIPC(wait(st_c, wr));
@@ -1658,7 +1705,11 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
                 uint16_t* y =
                     opt.ckpt_on_host ? ws.x[(unit + 1) & 1] : ws.ckpt_dev + uint64_t(unit + 1) * ws.maxT * d;
                 if (opt.ckpt_on_host) HIPC(wait(st_c, ckpt_done[(unit + 1) & 1]));
-                HIPC(fwd_layer(bind_layer(lay, wbase), x, y, B, S, true));
+                // ckpt_attn: layers alternate attention buffers; this one's
+                // previous contents (two layers back) must be on the host
+                const int ob = opt.ckpt_attn ? (unit & 1) : 0;
+                if (opt.ckpt_attn) HIPC(wait(st_c, attn_ck_done[ob]));
+                HIPC(fwd_layer(bind_layer(lay, wbase), x, y, B, S, true, ob));
                 HIPC(hipEventRecord(vz, st_c));
                 visit_rec(va, vz);
                 HIPC(release_slot(slot));
@@ -1670,6 +1721,14 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
                         HIPC(rec(ckpt_done[unit & 1], st_g));
                     }
                     HIPC(rec(xready, st_c));
+                    if (opt.ckpt_attn) {
+                        // ... and the layer's attention output and log-sum-exp
+                        uint8_t* h = attn_host + uint64_t(unit) * ab_al;
+                        HIPC(wait(st_g, xready));
+                        HIPC(d2h(h, ws.oa[ob], ao_bytes, st_g));
+                        HIPC(d2h(h + ao_al, ws.lsea[ob], al_bytes, st_g));
+                        HIPC(rec(attn_ck_done[ob], st_g));
+                    }
                     if (unit == L - 1) HIPC(rec(fwd_ckpt_all, st_g));
                 }
                 if (unit == L - 1) {
@@ -1712,7 +1771,8 @@ int Ctx::train_step(const int32_t* tokens, const int32_t* labels, int n_micro, i
             } else {
                 const uint16_t* x = opt.ckpt_on_host ? xb[vs.pos] : ws.ckpt_dev + uint64_t(unit) * ws.maxT * d;
                 HIPC(bwd_layer(bind_layer(lay, wbase), bind_layer(lay, gbase), x, ws.dy[nbwd & 1],
-                               ws.dy[(nbwd + 1) & 1], B, S));
+                               ws.dy[(nbwd + 1) & 1], B, S, ob_b, opt.ckpt_attn != 0));
+                if (opt.ckpt_attn) HIPC(rec(attn_buf_free[ob_b], st_c));
                 ++nbwd;
                 // The block's bank is free once its first layer's backward ran.
                 if (opt.ckpt_on_host && vs.pos == 0) HIPC(rec(xc_free[bank], st_c));
@@ -2161,6 +2221,7 @@ int mt_default_options(mt_options* o) {
     o->head_vocab_chunk = 0;
     o->poison_released = 0;
     o->keep_grads = 1;
+    o->ckpt_attn = 0;
     o->lr = 1e-4f;
     o->beta1 = 0.9f;
     o->beta2 = 0.999f;

@@ -45,6 +45,11 @@ struct Workspace {
     std::vector<uint16_t*> xc;
     uint16_t* ckpt_dev = nullptr;  // [L+1][maxT x d] when checkpoints stay on the GPU
     uint16_t *n1, *qkv, *o, *n2, *gu, *m;
+    // attention output and log-sum-exp buffers: [0] = o, lse; [1] a second
+    // pair with checkpointed attention (alternate layers, so a layer's
+    // checkpoint copy or restore overlaps the neighbouring layer's visit)
+    uint16_t* oa[2] = {};
+    float* lsea[2] = {};
     uint16_t* do16;  // attention backward: dO scaled by 2^k, fp16
     float* h1;  // residual stream inside a layer, kept in fp32
     // logit path: fp16 copies of n1 and Wqkv, fp32 QKV projection before RoPE

@@ -38,7 +38,7 @@ class mt_options(C.Structure):
                 ("profile_kernels", C.c_int32), ("pin_store", C.c_int32), ("cross_step", C.c_int32),
                 ("ckpt_interval", C.c_int32),
                 ("pin_weights", C.c_int32), ("head_vocab_chunk", C.c_int32), ("poison_released", C.c_int32),
-                ("keep_grads", C.c_int32),
+                ("keep_grads", C.c_int32), ("ckpt_attn", C.c_int32),
                 ("slot_bytes_override", C.c_uint64), ("workspace_bytes_override", C.c_uint64),
                 ("lr", C.c_float), ("beta1", C.c_float), ("beta2", C.c_float), ("adam_eps", C.c_float),
                 ("init_std", C.c_float), ("seed", C.c_uint64)]

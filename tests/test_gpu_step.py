@@ -270,7 +270,8 @@ def test_bench_option_set_bit_identical_to_synchronous_path(opts):
 VARIANTS = [dict(resident=1), dict(n_weight_slots=1), dict(n_weight_slots=3), dict(n_grad_slabs=1),
             dict(slot_mode=1), dict(ckpt_on_host=0), dict(host_threads=3), dict(pin_store=1),
             dict(cross_step=1), dict(cross_step=1, n_grad_slabs=1), dict(cross_step=1, resident=1),
-            dict(pin_weights=1), dict(pin_weights=1, cross_step=1)]
+            dict(pin_weights=1), dict(pin_weights=1, cross_step=1), dict(ckpt_attn=1),
+            dict(ckpt_attn=1, cross_step=1, pin_weights=1), dict(ckpt_attn=1, resident=1, n_grad_slabs=1)]
 
 
 def _run_two_steps(kw, B, S, **opts):
@@ -311,13 +312,16 @@ def deep_baseline_run():
 
 @pytest.mark.parametrize("opts", [dict(ckpt_interval=2), dict(ckpt_interval=3), dict(ckpt_interval=5),
                                   dict(ckpt_interval=7), dict(ckpt_interval=2, n_weight_slots=1),
-                                  dict(ckpt_interval=3, cross_step=1)],
+                                  dict(ckpt_interval=3, cross_step=1), dict(ckpt_attn=1),
+                                  dict(ckpt_attn=1, n_weight_slots=1, slot_mode=1)],
                          ids=lambda o: ",".join(f"{k}={v}" for k, v in o.items()))
 def test_checkpoint_interval_bit_identical(deep_baseline_run, opts):
     """Block-wise recomputation (every k-th layer input kept, the block's
     other inputs rebuilt by re-running its forward) changes where the inputs
     come from, not their values: 5 layers in blocks of 2, 3, 5 and 7 (capped
-    at the depth) give the per-layer-checkpoint results bit for bit."""
+    at the depth) give the per-layer-checkpoint results bit for bit; so does
+    checkpointing each layer's attention output and log-sum-exp as well, so
+    that the recompute skips the attention forward."""
     log(f"checkpoint interval vs every layer: {opts}")
     base_losses, base_state = deep_baseline_run
     losses, state = _run_two_steps(DEEP, 2, 64, **opts)
@@ -431,8 +435,9 @@ def _micro_batches(kw, n, B, S, seed0):
 
 
 @pytest.mark.parametrize("opts", [dict(), dict(head_vocab_chunk=256, ckpt_interval=2, cross_step=1, n_grad_slabs=3),
+                                  dict(ckpt_attn=1, cross_step=1),
                                   dict(pin_weights=1, n_weight_slots=3, head_vocab_chunk=-1)],
-                         ids=["default", "chunked-head,interval2,cross-step", "pinned,3slots"])
+                         ids=["default", "chunked-head,interval2,cross-step", "attn-ckpt,cross-step", "pinned,3slots"])
 def test_poisoned_released_buffers_change_nothing(opts):
     """Race check of the streaming protocol: with poison_released every
     weight slot is filled with NaN when its last visit releases it, and every
@@ -541,7 +546,7 @@ def accum_baseline_run():
 
 @pytest.mark.parametrize("opts", [dict(cross_step=1), dict(n_grad_slabs=1), dict(n_weight_slots=1),
                                   dict(ckpt_interval=2), dict(resident=1), dict(slot_mode=1),
-                                  dict(cross_step=1, n_grad_slabs=1, ckpt_interval=3)],
+                                  dict(cross_step=1, n_grad_slabs=1, ckpt_interval=3), dict(ckpt_attn=1)],
                          ids=lambda o: ",".join(f"{k}={v}" for k, v in o.items()))
 def test_accumulated_steps_bit_identical_across_streaming_options(accum_baseline_run, opts):
     log(f"accumulated steps vs default streaming: {opts}")

@@ -127,7 +127,7 @@ def test_bad_shapes_rejected(field, value):
                                          ("slot_mode", 2), ("max_batch", 0), ("beta1", 1.0), ("ckpt_interval", 0),
                                          ("cross_step", 2), ("pin_weights", 2), ("head_vocab_chunk", -2),
                                          ("head_vocab_chunk", 12), ("poison_released", 2),
-                                         ("keep_grads", 2), ("keep_grads", -1)])
+                                         ("keep_grads", 2), ("keep_grads", -1), ("ckpt_attn", 2)])
 def test_bad_options_rejected(field, value):
     o = mt.default_options()
     setattr(o, field, value)
@@ -137,10 +137,29 @@ def test_bad_options_rejected(field, value):
 
 def test_option_conflicts_rejected():
     for kw in (dict(ckpt_interval=2, ckpt_on_host=0), dict(pin_weights=1, pin_store=1),
-               dict(poison_released=1, slot_mode=1), dict(poison_released=1, resident=1)):
+               dict(poison_released=1, slot_mode=1), dict(poison_released=1, resident=1),
+               dict(ckpt_attn=1, ckpt_on_host=0), dict(ckpt_attn=1, ckpt_interval=2)):
         o = mt.default_options(**kw)
         a, p, h = C.c_uint64(), C.c_uint64(), C.c_uint64()
         assert mt.lib.mt_workspace_bytes(C.byref(CFG1), C.byref(o), C.byref(a), C.byref(p), C.byref(h)) == mt.MT_E_INVAL
+
+
+def test_attention_checkpoint_ring_sizes():
+    """ckpt_attn adds a second attention buffer pair to the arena (T x Hq*hd
+    fp16 and B*S*Hq fp32) and a pinned ring of one such pair per layer; the
+    host store does not change."""
+    def sizes(**kw):
+        o = mt.default_options(max_batch=2, max_seq=64, **kw)
+        a, p, h = C.c_uint64(), C.c_uint64(), C.c_uint64()
+        assert mt.lib.mt_workspace_bytes(C.byref(CFG1), C.byref(o), C.byref(a), C.byref(p), C.byref(h)) == 0
+        return a.value, p.value, h.value
+    a0, p0, h0 = sizes()
+    a1, p1, h1 = sizes(ckpt_attn=1)
+    T, nq, Hq, L = 128, 4 * 64, 4, 2
+    al4k = lambda x: (x + 4095) // 4096 * 4096
+    assert h1 == h0
+    assert p1 - p0 == L * (al4k(T * nq * 2) + al4k(T * Hq * 4))
+    assert T * nq * 2 + T * Hq * 4 <= a1 - a0 <= T * nq * 2 + T * Hq * 4 + 1024
 
 
 def test_vocab_chunked_head_sizes_slots_to_the_decoder_layer():
