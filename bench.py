@@ -225,7 +225,7 @@ def traffic_probe(torch, mt, cfg):
     log("traffic probe done")
 
 
-def attention_probe(torch, mt, cfg, S, B=1):
+def attention_probe(torch, mt, cfg, S, B=1, dq_form=0):
     """The attention kernels alone at B sequences of length S with the
     workload's heads: forward and backward three times each on seeded
     synthetic q, k, v (fp16) and dO (bf16); HIP-event times and TFLOP/s
@@ -252,7 +252,7 @@ def attention_probe(torch, mt, cfg, S, B=1):
     def bwd():  # as the step runs it: dQ, dK in fp32
         mt.check(mt.lib.mt_k_attn_bwd(qkv.data_ptr(), ld, o.data_ptr(), do.data_ptr(), nq, lse.data_ptr(),
                                       work.data_ptr(), dqkv.data_ptr(), ld, B, S, Hq, Hkv, hd, dqk32.data_ptr(), ld,
-                                      0, None, s),
+                                      0, dq_form, None, s),
                  "attn_bwd")
     fl = 4.0 * B * Hq * hd * S * (S + 1) / 2
     out = {}
@@ -640,6 +640,8 @@ def main():
     ap.add_argument("--attn-probe", type=int, default=0, metavar="S",
                     help="only time the attention kernels at sequences of length S with the workload's heads")
     ap.add_argument("--attn-batch", type=int, default=1, metavar="B", help="sequences in the attention probe")
+    ap.add_argument("--attn-dq-form", type=int, default=0, choices=(0, 1, 2),
+                    help="attention probe's dQ: 0 as the step takes it, 1 recomputed, 2 from the stored dS")
     ap.add_argument("--host-probe", action="store_true",
                     help="only measure host DRAM: the host Adam alone at 8/12/16 threads, a parallel copy and read")
     ap.add_argument("--micro", type=int, default=1,
@@ -676,7 +678,7 @@ def main():
         traffic_probe(torch, mt, cfg)
         return
     if args.attn_probe:
-        attention_probe(torch, mt, cfg, args.attn_probe, args.attn_batch)
+        attention_probe(torch, mt, cfg, args.attn_probe, args.attn_batch, args.attn_dq_form)
         return
     torch.cuda.init()
     ckpt_attn = args.ckpt_attn if args.ckpt_attn >= 0 else int(cfg["seq"] >= 8192)

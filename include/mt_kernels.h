@@ -111,15 +111,22 @@ int mt_k_attn_fwd(const void* qkv, int64_t ld, void* o, int64_t ldo, void* lse, 
  * group's query heads over head_splits blocks per key tile (0: automatic,
  * enough blocks for two per CU; n: at most n; never more than Hq/Hkv or than
  * the work buffer's partials hold) and adds their fp32 partial sums in split
- * order.  work: device scratch of mt_k_attn_bwd_work_bytes(B, S, Hq, Hkv, hd)
- * bytes, 256-byte aligned (D and the base-2 log-sum-exp, the scaled dO, the
- * two maxima, the partials of the automatic split); B*S*Hq*hd/8 < 2^31.  mt_k_attn_dkdv_splits: the
- * split count mt_k_attn_bwd takes with such a buffer (0 on a bad shape). */
+ * order.  dQ either recomputes the scores and dP per query tile, or, for
+ * sequences up to 1024 with at most 1 GiB of it, is formed as dS K from the
+ * dS (2^k-scaled fp16) the dK/dV pass stores in the work buffer: dq_form 0
+ * takes the stored form where the shape allows, 1 always recomputes, 2
+ * requires the stored form (MT_E_INVAL where the shape does not allow it).
+ * work: device scratch of mt_k_attn_bwd_work_bytes(B, S, Hq, Hkv, hd) bytes,
+ * 256-byte aligned (D and the base-2 log-sum-exp, the scaled dO, the two
+ * maxima, the partials of the automatic split, the stored dS where the shape
+ * takes it: B*Hq*Sp*Sp*2 bytes, Sp = S rounded up to 128);
+ * B*S*Hq*hd/8 < 2^31.  mt_k_attn_dkdv_splits: the split count mt_k_attn_bwd
+ * takes with such a buffer (0 on a bad shape). */
 int64_t mt_k_attn_bwd_work_bytes(int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t hd);
 int32_t mt_k_attn_dkdv_splits(int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t hd, int32_t head_splits);
 int mt_k_attn_bwd(const void* qkv, int64_t ld, const void* o, const void* dout, int64_t ldo, const void* lse,
                   void* work, void* dqkv, int64_t ldd, int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t hd,
-                  void* dqk32, int64_t ld32, int32_t head_splits, void* fp16_ovf, void* stream);
+                  void* dqk32, int64_t ld32, int32_t head_splits, int32_t dq_form, void* fp16_ovf, void* stream);
 /* Rotary embedding of the first n_rot_heads heads of fp32 in [T x ldin]
  * (same angles and table as mt_k_rope; dir -1 rotates by -theta, the
  * backward), written as bf16 to out [T x ldout] with one rounding. */

@@ -152,14 +152,17 @@ int32_t mt_k_attn_dkdv_splits(int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int
 
 int mt_k_attn_bwd(const void* qkv, int64_t ld, const void* o, const void* dout, int64_t ldo, const void* lse,
                   void* work, void* dqkv, int64_t ldd, int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t hd,
-                  void* dqk32, int64_t ld32, int32_t head_splits, void* fp16_ovf, void* stream) {
+                  void* dqk32, int64_t ld32, int32_t head_splits, int32_t dq_form, void* fp16_ovf, void* stream) {
     if (!work || (reinterpret_cast<uintptr_t>(work) & 255)) MT_FAIL(MT_E_INVAL, "attn_bwd: work must be 256-byte aligned");
     if (head_splits < 0) MT_FAIL(MT_E_INVAL, "attn_bwd: head_splits must be >= 0");
+    if (dq_form < 0 || dq_form > 2) MT_FAIL(MT_E_INVAL, "attn_bwd: dq_form must be 0, 1 or 2");
+    if (dq_form == 2 && mt::attn_ds_bytes(B, S, Hq) == 0)
+        MT_FAIL(MT_E_INVAL, "attn_bwd: this shape does not take the stored-dS form of dQ");
     mt::AttnBwdArgs a{U16(qkv), ld, U16(o), U16(dout), ldo, F32(lse), nullptr, nullptr, nullptr, U16(dqkv), ldd,
                       B, S, Hq, Hkv, hd, F32(dqk32), ld32, static_cast<uint32_t*>(fp16_ovf)};
     a.splits = head_splits;
     if (B > 0 && S > 0 && Hq > 0 && Hkv > 0 && Hq % Hkv == 0 && (hd == 64 || hd == 128))
-        mt::attn_bwd_carve(work, B, S, Hq, Hkv, hd, a);
+        mt::attn_bwd_carve(work, B, S, Hq, Hkv, hd, a, dq_form != 1);
     return kst(mt::attn_bwd(a, S_(stream)), "attn_bwd");
 }
 

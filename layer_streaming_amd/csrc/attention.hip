@@ -592,6 +592,85 @@ __global__ __launch_bounds__(256, 2) void attn_dq_k(AttnBwdArgs a, int n_qt, int
     }
 }
 
+// dQ = dS K from the dS the dK/dV pass stored (stored-dS form, short
+// sequences): block = 4 waves x 32 queries of one (b, h), key tiles of 64.
+// Each tile stages K and the matching 64 rows (keys) x 128 columns (the
+// block's queries) of dS with the same swizzled layout, and both operands
+// are read transposed, dS with lane = query, so the contraction runs over
+// the same key permutation in both.  Key blocks of 32 above the wave's
+// queries were never written and are skipped; rows past the sequence read
+// as zero, and query columns past it only reach rows that are not stored.
+template <int HD>
+__global__ __launch_bounds__(256, 2) void attn_dq_ds_k(AttnBwdArgs a, int n_qt, int qt_slow) {
+    constexpr int ND = HD / 32, NCH = HD / 8;
+    constexpr int TILE = BKV * NCH, NI = TILE / 256;
+    constexpr int STILE = BKV * 16, SNI = STILE / 256;  // dS tile: 64 keys x 128 queries
+    __shared__ uint4 Ks[2][TILE];
+    __shared__ uint4 Ss[2][STILE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hh = lane >> 5, c = lane & 31;
+    const int nbh = a.B * a.Hq;
+    const int qt = n_qt - 1 - (qt_slow ? int(blockIdx.x / unsigned(nbh)) : int(blockIdx.x % unsigned(n_qt)));
+    const int bh = qt_slow ? int(blockIdx.x % unsigned(nbh)) : int(blockIdx.x / unsigned(n_qt));
+    const int h = bh % a.Hq, b = bh / a.Hq;
+    const int hk = h / (a.Hq / a.Hkv);
+    const int S = a.S;
+    const int q0 = qt * 128, qw = q0 + wave * 32, q = qw + c;
+    const uint16_t* kbase = a.qkv + int64_t(b) * S * a.ld + (a.Hq + hk) * HD;
+    const uint16_t* dsbase = a.ds + (int64_t(b) * a.Hq + h) * a.ds_ld * a.ds_ld + q0;
+    const float s2k = grad_scale(a.amax, HD);
+
+    uint32_t koff[NI], soff[SNI];
+    tile_offsets<HD>(koff, wave, lane, a.ld);
+    tile_offsets<128>(soff, wave, lane, a.ds_ld);
+    auto issue = [&](int k0, int buf) {
+        tile_issue<HD>(kbase + int64_t(k0) * a.ld, a.ld, S - k0, koff, lds_addr(&Ks[buf][0]), wave);
+        tile_issue<128>(dsbase + int64_t(k0) * a.ds_ld, a.ds_ld, S - k0, soff, lds_addr(&Ss[buf][0]), wave);
+    };
+
+    f32x16_t acc[ND];
+#pragma unroll
+    for (int i = 0; i < ND; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+
+    const int k_end = min(S, q0 + 128);
+    const int nkb = (k_end + BKV - 1) / BKV;
+    issue(0, 0);
+    barrier_tile();
+    for (int kb = 0; kb < nkb; ++kb) {
+        const int cur = kb & 1;
+        const int k0 = kb * BKV;
+        if (kb + 1 < nkb) issue(k0 + BKV, cur ^ 1);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            if (k0 + 32 * t <= qw + 31) {
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const f16x8_t dsf = tile_colT<128>(Ss[cur], wave, t, s2, lane);
+#pragma unroll
+                    for (int dt = 0; dt < ND; ++dt)
+                        acc[dt] = MFMA32H(tile_colT<HD>(Ks[cur], dt, t, s2, lane), dsf, acc[dt]);
+                }
+            }
+        }
+        barrier_tile();
+    }
+    if (q < S) {
+        const float scale = rsqrtf(float(HD)) / s2k;
+        const int64_t row = int64_t(b) * S + q;
+        float* r32 = a.dqk32 ? a.dqk32 + row * a.ld32 + h * HD : nullptr;
+        uint16_t* r16 = a.dqkv + row * a.ldd + h * HD;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                store_grad4(r32, r16, 32 * dt + 8 * g + 4 * hh, acc[dt][4 * g] * scale, acc[dt][4 * g + 1] * scale,
+                            acc[dt][4 * g + 2] * scale, acc[dt][4 * g + 3] * scale);
+    }
+}
+
 // dK, dV: block = 8 waves over 128 keys of one (b, kv head), looping over
 // 64-query tiles of the group's query heads (or, split ns ways, of the
 // split's share of them), head by head, each from the block's diagonal to
@@ -702,7 +781,21 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_k(AttnBwdArgs a, int n_kt, i
             vf[s] = as_f16x8(v);
         }
         const float sc = LOG2E * rsqrtf(float(HD));
+        // stored-dS form: the previous phase's dS goes out at the start of
+        // the next one, before its tile loads, so the end-of-phase wait
+        // (loads land in order) finds those stores long acknowledged
+        uint4 ds_prev[2];
+        uint16_t* ds_row = nullptr;  // this lane's key row of the previous phase's block, at its first query
         for (int p = 0; p <= 2 * tt; ++p) {
+            if (ds_row) {
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const int qo = 16 * s2 + 4 * hh;
+                    *reinterpret_cast<uint2*>(ds_row + qo) = make_uint2(ds_prev[s2].x, ds_prev[s2].y);
+                    *reinterpret_cast<uint2*>(ds_row + qo + 8) = make_uint2(ds_prev[s2].z, ds_prev[s2].w);
+                }
+                ds_row = nullptr;
+            }
             next_tile(p);
             const int h = p;
             const int j = h >> 1, t = h & 1, buf = j % 3;
@@ -759,7 +852,13 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_k(AttnBwdArgs a, int n_kt, i
                         }
                     }
                     X[s2 * 64 + lane] = __builtin_bit_cast(uint4, pack_h8(tp));
-                    X[(2 + s2) * 64 + lane] = __builtin_bit_cast(uint4, pack_h8(td));
+                    const uint4 dsv = __builtin_bit_cast(uint4, pack_h8(td));
+                    X[(2 + s2) * 64 + lane] = dsv;
+                    ds_prev[s2] = dsv;
+                }
+                if (a.ds && key < S) {
+                    const int hq = h_lo + j / nqb;
+                    ds_row = a.ds + ((int64_t(b) * a.Hq + hq) * a.ds_ld + key) * a.ds_ld + qh;
                 }
             }
             phase_end((p + 1) >> 1);
@@ -913,12 +1012,24 @@ namespace {
 int64_t al256(int64_t x) { return (x + 255) & ~int64_t(255); }
 }  // namespace
 
-int64_t attn_bwd_work_bytes(int B, int S, int Hq, int Hkv, int hd) {
-    const int64_t T = int64_t(B) * S;
-    return al256(2 * T * Hq * 4) + al256(T * Hq * hd * 2) + 256 + al256(attn_bwd_part_elems(B, S, Hq, Hkv, hd) * 4);
+// The stored form trades two of dQ's three products for writing and reading
+// dS (4 bytes per score): measured at B8 x S1024 (28 / 4 heads) it takes the
+// backward from 0.493 to 0.456 ms, at B4 x S2048 (40 / 8) from 1.092 to 1.075
+// ms, where dQ already runs its products well; so only up to S = 1024.
+int64_t attn_ds_bytes(int B, int S, int Hq) {
+    if (B <= 0 || S <= 0 || Hq <= 0 || S > 1024) return 0;
+    const int64_t sp = (int64_t(S) + 127) / 128 * 128;
+    const int64_t bytes = int64_t(B) * Hq * sp * sp * 2;
+    return bytes <= (int64_t(1) << 30) ? bytes : 0;
 }
 
-void attn_bwd_carve(void* work, int B, int S, int Hq, int Hkv, int hd, AttnBwdArgs& a) {
+int64_t attn_bwd_work_bytes(int B, int S, int Hq, int Hkv, int hd) {
+    const int64_t T = int64_t(B) * S;
+    return al256(2 * T * Hq * 4) + al256(T * Hq * hd * 2) + 256 + al256(attn_bwd_part_elems(B, S, Hq, Hkv, hd) * 4) +
+           al256(attn_ds_bytes(B, S, Hq));
+}
+
+void attn_bwd_carve(void* work, int B, int S, int Hq, int Hkv, int hd, AttnBwdArgs& a, bool with_ds) {
     const int64_t T = int64_t(B) * S;
     uint8_t* p = static_cast<uint8_t*>(work);
     a.dsum = reinterpret_cast<float*>(p);
@@ -929,6 +1040,10 @@ void attn_bwd_carve(void* work, int B, int S, int Hq, int Hkv, int hd, AttnBwdAr
     p += 256;
     a.dpart_elems = attn_bwd_part_elems(B, S, Hq, Hkv, hd);
     a.dpart = a.dpart_elems ? reinterpret_cast<float*>(p) : nullptr;
+    p += al256(a.dpart_elems * 4);
+    const int64_t dsb = with_ds ? attn_ds_bytes(B, S, Hq) : 0;
+    a.ds = dsb ? reinterpret_cast<uint16_t*>(p) : nullptr;
+    a.ds_ld = dsb ? (int64_t(S) + 127) / 128 * 128 : 0;
 }
 
 hipError_t attn_bwd(const AttnBwdArgs& a, hipStream_t s) {
@@ -953,12 +1068,16 @@ hipError_t attn_bwd(const AttnBwdArgs& a, hipStream_t s) {
     const int nb_v = int(std::min<int64_t>(128, (T * a.Hkv * a.hd / 8 + 255) / 256));
     hipError_t e = fill_zero(a.amax, 256, s);
     if (e != hipSuccess) return e;
+    // stored-dS form: dS must cover every key row and 128-query block
+    const bool use_ds = a.ds != nullptr;
+    if (use_ds && (a.ds_ld < (int64_t(a.S) + 127) / 128 * 128 || (a.ds_ld & 127))) return hipErrorInvalidValue;
     auto run = [&](auto hd_) {
         constexpr int HD = decltype(hd_)::value;
         attn_amax_k<HD><<<nb_do + nb_v, 256, 0, s>>>(a, nb_do);
         attn_prep_k<HD><<<np, 256, 0, s>>>(a);
-        attn_dq_k<HD><<<gq, 256, 0, s>>>(a, n_qt, n_qt <= 256);
+        if (!use_ds) attn_dq_k<HD><<<gq, 256, 0, s>>>(a, n_qt, n_qt <= 256);
         attn_dkdv_k<HD><<<gk, 512, 0, s>>>(a, n_kt, ns, kt_slow);
+        if (use_ds) attn_dq_ds_k<HD><<<gq, 256, 0, s>>>(a, n_qt, n_qt <= 256);
     };
     if (a.hd == 128) run(std::integral_constant<int, 128>{});
     else run(std::integral_constant<int, 64>{});

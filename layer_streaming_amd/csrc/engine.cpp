@@ -196,8 +196,15 @@ void plan_workspace(const Layout& lay, const mt_options& o, Carver& cv, Workspac
         const uint64_t tb = std::max({uint64_t(F) * std::max<uint64_t>(T8, uint64_t(2 * d)),
                                       uint64_t(std::max(nq, nqkv)) * std::max<uint64_t>(T8, uint64_t(d)),
                                       uint64_t(d) * T8, head_t});
-        ws.tA = cv.take<uint16_t>(ta * 2);
-        ws.tA_bytes = ta * 2;
+        // tA also holds the attention backward's dK/dV split partials and
+        // its stored dS (it is idle then)
+        // (at the largest batch x seq; smaller steps split more or recompute dQ
+        // when their partials and dS do not fit)
+        const uint64_t attn_b = uint64_t((attn_bwd_part_elems(o.max_batch, o.max_seq, sh.n_heads, sh.n_kv_heads,
+                                                               sh.head_dim) * 4 + 255) & ~int64_t(255)) +
+                                uint64_t(attn_ds_bytes(o.max_batch, o.max_seq, sh.n_heads));
+        ws.tA_bytes = std::max<uint64_t>(ta * 2, attn_b);
+        ws.tA = cv.take<uint16_t>(ws.tA_bytes);
         ws.tB = cv.take<uint16_t>(tb * 2);
     }
     ws.rstd1 = cv.take<float>(uint64_t(T) * 4);
@@ -1197,9 +1204,19 @@ hipError_t Ctx::bwd_layer(const LayerView& w, const LayerView& g, const uint16_t
     // the recompute's rotation read it), then rotated back by -theta and
     // rounded to bf16 once.
     HIPR(site(S_ATTN_BWD, [&] {
+        const int64_t part = std::min<int64_t>(attn_bwd_part_elems(B, S, sh.n_heads, sh.n_kv_heads, sh.head_dim),
+                                               int64_t(ws.tA_bytes / 4));
         AttnBwdArgs a{ws.qkv, nqkv, ws.oa[ob], ws.dout, nq, ws.lsea[ob], ws.dsum, ws.do16, ws.amax, ws.dqkv, nqkv,
                       B, S, sh.n_heads, sh.n_kv_heads, sh.head_dim, ws.qkv32, nqkv, ws.ovf,
-                      reinterpret_cast<float*>(ws.tA), int64_t(ws.tA_bytes / 4), 0};
+                      reinterpret_cast<float*>(ws.tA), part, 0};
+        // the stored-dS form of dQ where the shape takes it (the region after
+        // the partials; the workspace was sized for the largest batch x seq)
+        const int64_t dsb = attn_ds_bytes(B, S, sh.n_heads);
+        const uint64_t ds_off = uint64_t((part * 4 + 255) & ~int64_t(255));
+        if (dsb > 0 && ds_off + uint64_t(dsb) <= ws.tA_bytes) {
+            a.ds = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(ws.tA) + ds_off);
+            a.ds_ld = (int64_t(S) + 127) / 128 * 128;
+        }
         return attn_bwd(a, s);
     }));
     HIPR(site(S_ROPE_BWD, [&] {

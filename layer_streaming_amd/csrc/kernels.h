@@ -131,6 +131,13 @@ struct AttnBwdArgs {
     // what dpart_elems holds.
     float* dpart = nullptr; int64_t dpart_elems = 0;
     int splits = 0;
+    // Optional: the stored-dS form of dQ (short sequences).  The dK/dV pass
+    // writes dS 2^k in fp16 into ds ([B*Hq] x [ds_ld keys] x [ds_ld queries],
+    // ds_ld = S rounded up to 128; only the blocks on or below the diagonal),
+    // and dQ = dS K is formed from it afterwards instead of recomputing the
+    // scores and dP.  nullptr: dQ recomputes them.
+    uint16_t* ds = nullptr;
+    int64_t ds_ld = 0;
 };
 // Query-head splits the dK/dV pass takes for a shape: automatic (req 0:
 // enough blocks for two per CU, at most Hq/Hkv) or at most req, reduced to
@@ -138,10 +145,15 @@ struct AttnBwdArgs {
 int attn_dkdv_splits(int B, int S, int Hq, int Hkv, int hd, int64_t part_elems, int req);
 // Floats of partials the automatic split needs (0 without a split).
 int64_t attn_bwd_part_elems(int B, int S, int Hq, int Hkv, int hd);
-// Scratch bytes of attn_bwd (dsum, do16, amax, and the partials of the
-// automatic split) and their carving from one 256-byte-aligned block.
+// Bytes of the stored dS a shape takes the stored-dS form of dQ with (S up
+// to 1024 and at most 1 GiB of dS), else 0.
+int64_t attn_ds_bytes(int B, int S, int Hq);
+// Scratch bytes of attn_bwd (dsum, do16, amax, the partials of the
+// automatic split and the stored dS where the shape takes it) and their
+// carving from one 256-byte-aligned block; with_ds = false leaves the dS
+// region unused (dQ recomputes).
 int64_t attn_bwd_work_bytes(int B, int S, int Hq, int Hkv, int hd);
-void attn_bwd_carve(void* work, int B, int S, int Hq, int Hkv, int hd, AttnBwdArgs& a);
+void attn_bwd_carve(void* work, int B, int S, int Hq, int Hkv, int hd, AttnBwdArgs& a, bool with_ds = true);
 hipError_t attn_bwd(const AttnBwdArgs& a, hipStream_t s);
 
 // ------------------------------------------------------- Cross-entropy ----

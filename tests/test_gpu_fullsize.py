@@ -91,7 +91,7 @@ def test_attention_long_context_sampled():
     mt.check(mt.lib.mt_k_attn_fwd(d_qkv.data_ptr(), ld, d_o.data_ptr(), nq, lse.data_ptr(), B, S, Hq, Hkv, hd,
                                   None, s))
     mt.check(mt.lib.mt_k_attn_bwd(d_qkv.data_ptr(), ld, d_o.data_ptr(), d_do.data_ptr(), nq, lse.data_ptr(),
-                                  work.data_ptr(), d_dqkv.data_ptr(), ld, B, S, Hq, Hkv, hd, None, 0, 0, None, s))
+                                  work.data_ptr(), d_dqkv.data_ptr(), ld, B, S, Hq, Hkv, hd, None, 0, 0, 0, None, s))
     torch.cuda.synchronize()
     o_g = host_f16(d_o).reshape(S, Hq, hd)
     g_g = host_f32(d_dqkv).reshape(S, Hq + 2 * Hkv, hd)

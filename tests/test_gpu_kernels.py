@@ -525,16 +525,20 @@ ATTN_CASES = [(2, 200, 4, 2, 64), (1, 300, 7, 1, 128), (2, 128, 4, 4, 128), (1, 
 
 @pytest.mark.parametrize("B,S,Hq,Hkv,hd", ATTN_CASES)
 @pytest.mark.parametrize("f32_out", [False, True], ids=["bf16-dqk", "f32-dqk"])
-def test_attention_fwd_bwd(B, S, Hq, Hkv, hd, f32_out):
+@pytest.mark.parametrize("dq_form", [1, 2], ids=["dq-recomputed", "dq-stored-ds"])
+def test_attention_fwd_bwd(B, S, Hq, Hkv, hd, f32_out, dq_form):
     """Forward and backward (fp16 products, scaled dO) against the float64
-    oracle; dQ and dK written as bf16 into the qkv layout, or as fp32."""
-    _attention_case(B, S, Hq, Hkv, hd, 1.0, f32_out)
+    oracle; dQ and dK written as bf16 into the qkv layout, or as fp32; dQ
+    recomputing the scores and dP, or formed from the dS the dK/dV pass
+    stored."""
+    _attention_case(B, S, Hq, Hkv, hd, 1.0, f32_out, dq_form=dq_form)
 
 
-def test_attention_sharp_logits():
+@pytest.mark.parametrize("dq_form", [1, 2], ids=["dq-recomputed", "dq-stored-ds"])
+def test_attention_sharp_logits(dq_form):
     """q, k with std 2 (logits of std 4): a peaked softmax, where the logit
     path's rounding matters most."""
-    _attention_case(1, 700, 8, 2, 128, 2.0, True)
+    _attention_case(1, 700, 8, 2, 128, 2.0, True, dq_form=dq_form)
 
 
 @pytest.mark.parametrize("do_std", [1e-9, 1e-4, 3e2])
@@ -556,9 +560,9 @@ def test_attention_dkdv_head_split(B, S, Hq, Hkv, hd, splits, taken):
     _attention_case(B, S, Hq, Hkv, hd, 1.0, True, splits=splits)
 
 
-def _attention_case(B, S, Hq, Hkv, hd, qk_std, f32_out, do_std=1.0, splits=0):
+def _attention_case(B, S, Hq, Hkv, hd, qk_std, f32_out, do_std=1.0, splits=0, dq_form=0):
     log(f"attention B={B} S={S} Hq={Hq} Hkv={Hkv} hd={hd} qk_std={qk_std} f32_out={f32_out} do_std={do_std} "
-        f"splits={splits}")
+        f"splits={splits} dq_form={dq_form}")
     T = B * S
     ld = (Hq + 2 * Hkv) * hd
     nq, nr = Hq * hd, (Hq + Hkv) * hd
@@ -576,7 +580,7 @@ def _attention_case(B, S, Hq, Hkv, hd, qk_std, f32_out, do_std=1.0, splits=0):
                                   ovf.data_ptr(), s))
     mt.check(mt.lib.mt_k_attn_bwd(d_qkv.data_ptr(), ld, d_o.data_ptr(), d_do.data_ptr(), nq, lse.data_ptr(),
                                   work.data_ptr(), d_dqkv.data_ptr(), ld, B, S, Hq, Hkv, hd,
-                                  dqk32.data_ptr() if f32_out else None, nr if f32_out else 0, splits,
+                                  dqk32.data_ptr() if f32_out else None, nr if f32_out else 0, splits, dq_form,
                                   ovf.data_ptr(), s))
     _sync()
     assert ovf[0].item() == 0
