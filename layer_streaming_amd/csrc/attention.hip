@@ -594,12 +594,14 @@ __global__ __launch_bounds__(256, 2) void attn_dq_k(AttnBwdArgs a, int n_qt, int
 
 // dQ = dS K from the dS the dK/dV pass stored (stored-dS form, short
 // sequences): block = 4 waves x 32 queries of one (b, h), key tiles of 64.
-// Each tile stages K and the matching 64 rows (keys) x 128 columns (the
-// block's queries) of dS with the same swizzled layout, and both operands
-// are read transposed, dS with lane = query, so the contraction runs over
-// the same key permutation in both.  Key blocks of 32 above the wave's
-// queries were never written and are skipped; rows past the sequence read
-// as zero, and query columns past it only reach rows that are not stored.
+// Each tile stages K and the matching 64 keys x 128 queries of dS (eight
+// stored 32 x 32 blocks) with the same swizzled row layout, and both
+// operands are read transposed, dS with lane = query position, so the
+// contraction runs over the same key permutation in both; lane c's output
+// row is the query its position holds in the stored order.  Key blocks of
+// 32 above the wave's queries were never written and are skipped; keys past
+// the sequence read as zero, and query columns past it only reach rows that
+// are not stored.
 template <int HD>
 __global__ __launch_bounds__(256, 2) void attn_dq_ds_k(AttnBwdArgs a, int n_qt, int qt_slow) {
     constexpr int ND = HD / 32, NCH = HD / 8;
@@ -618,15 +620,31 @@ __global__ __launch_bounds__(256, 2) void attn_dq_ds_k(AttnBwdArgs a, int n_qt, 
     const int S = a.S;
     const int q0 = qt * 128, qw = q0 + wave * 32, q = qw + c;
     const uint16_t* kbase = a.qkv + int64_t(b) * S * a.ld + (a.Hq + hk) * HD;
-    const uint16_t* dsbase = a.ds + (int64_t(b) * a.Hq + h) * a.ds_ld * a.ds_ld + q0;
+    const int nb = int(a.ds_ld / 32);
+    const uint16_t* dsbase = a.ds + (int64_t(b) * a.Hq + h) * nb * nb * 1024 + (q0 / 32) * 1024;
     const float s2k = grad_scale(a.amax, HD);
 
     uint32_t koff[NI], soff[SNI];
+    int srow[SNI];
     tile_offsets<HD>(koff, wave, lane, a.ld);
-    tile_offsets<128>(soff, wave, lane, a.ds_ld);
+    // the dS tile's LDS slot (row r, chunk) takes logical chunk lc of row r:
+    // key block r / 32, query block lc / 4, row r % 32, 16 bytes at 16 (lc % 4)
+#pragma unroll
+    for (int i = 0; i < SNI; ++i) {
+        const int pos = (4 * i + wave) * 64 + lane;
+        const int r = pos / 16;
+        const int lc = (pos % 16) ^ aswz<128>(r);
+        soff[i] = uint32_t((((r / 32) * nb + lc / 4) * 1024 + (r % 32) * 32 + (lc % 4) * 8) * 2);
+        srow[i] = r;
+    }
     auto issue = [&](int k0, int buf) {
         tile_issue<HD>(kbase + int64_t(k0) * a.ld, a.ld, S - k0, koff, lds_addr(&Ks[buf][0]), wave);
-        tile_issue<128>(dsbase + int64_t(k0) * a.ds_ld, a.ds_ld, S - k0, soff, lds_addr(&Ss[buf][0]), wave);
+        const i32x4_t rs = make_rsrc(dsbase + int64_t(k0 / 32) * nb * 1024, uint32_t((int64_t(nb + 3) * 1024 + 1024) * 2));
+        const uint32_t lds = lds_addr(&Ss[buf][0]);
+#pragma unroll
+        for (int i = 0; i < SNI; ++i)
+            dma16(rs, __builtin_amdgcn_readfirstlane(lds + uint32_t((4 * i + wave) * 1024)),
+                  k0 + srow[i] < S ? soff[i] : 0x80000000u);
     };
 
     f32x16_t acc[ND];
@@ -657,9 +675,11 @@ __global__ __launch_bounds__(256, 2) void attn_dq_ds_k(AttnBwdArgs a, int n_qt, 
         }
         barrier_tile();
     }
-    if (q < S) {
+    // query of position c in the stored order: 8 (c / 4 % 4) + 4 (c / 16) + c % 4
+    const int qs = qw + 8 * ((c >> 2) & 3) + 4 * (c >> 4) + (c & 3);
+    if (qs < S) {
         const float scale = rsqrtf(float(HD)) / s2k;
-        const int64_t row = int64_t(b) * S + q;
+        const int64_t row = int64_t(b) * S + qs;
         float* r32 = a.dqk32 ? a.dqk32 + row * a.ld32 + h * HD : nullptr;
         uint16_t* r16 = a.dqkv + row * a.ldd + h * HD;
 #pragma unroll
@@ -783,17 +803,17 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_k(AttnBwdArgs a, int n_kt, i
         const float sc = LOG2E * rsqrtf(float(HD));
         // stored-dS form: the previous phase's dS goes out at the start of
         // the next one, before its tile loads, so the end-of-phase wait
-        // (loads land in order) finds those stores long acknowledged
+        // (loads land in order) finds those stores long acknowledged.  A
+        // 32-key x 32-query block is 2 KB: key row c holds the 32 queries in
+        // the order 0-3, 8-11, 16-19, 24-27, 4-7, 12-15, 20-23, 28-31, which
+        // puts each lane's two fp16 octets (s2 = 0, 1) side by side at byte
+        // 32 hh + 16 s2: every store instruction fills whole row segments
         uint4 ds_prev[2];
         uint16_t* ds_row = nullptr;  // this lane's key row of the previous phase's block, at its first query
         for (int p = 0; p <= 2 * tt; ++p) {
             if (ds_row) {
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    const int qo = 16 * s2 + 4 * hh;
-                    *reinterpret_cast<uint2*>(ds_row + qo) = make_uint2(ds_prev[s2].x, ds_prev[s2].y);
-                    *reinterpret_cast<uint2*>(ds_row + qo + 8) = make_uint2(ds_prev[s2].z, ds_prev[s2].w);
-                }
+                *reinterpret_cast<uint4*>(ds_row) = ds_prev[0];
+                *reinterpret_cast<uint4*>(ds_row + 8) = ds_prev[1];
                 ds_row = nullptr;
             }
             next_tile(p);
@@ -857,8 +877,8 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_k(AttnBwdArgs a, int n_kt, i
                     ds_prev[s2] = dsv;
                 }
                 if (a.ds && key < S) {
-                    const int hq = h_lo + j / nqb;
-                    ds_row = a.ds + ((int64_t(b) * a.Hq + hq) * a.ds_ld + key) * a.ds_ld + qh;
+                    const int hq = h_lo + j / nqb, nb = int(a.ds_ld / 32);
+                    ds_row = a.ds + (((int64_t(b) * a.Hq + hq) * nb + kw / 32) * nb + qh / 32) * 1024 + c * 32 + 16 * hh;
                 }
             }
             phase_end((p + 1) >> 1);

@@ -132,10 +132,11 @@ struct AttnBwdArgs {
     float* dpart = nullptr; int64_t dpart_elems = 0;
     int splits = 0;
     // Optional: the stored-dS form of dQ (short sequences).  The dK/dV pass
-    // writes dS 2^k in fp16 into ds ([B*Hq] x [ds_ld keys] x [ds_ld queries],
-    // ds_ld = S rounded up to 128; only the blocks on or below the diagonal),
-    // and dQ = dS K is formed from it afterwards instead of recomputing the
-    // scores and dP.  nullptr: dQ recomputes them.
+    // writes dS 2^k in fp16 into ds: per (b, h) ds_ld/32 x ds_ld/32 blocks of
+    // 32 keys x 32 queries (2 KB, key-major, queries in a fixed permuted
+    // order; ds_ld = S rounded up to 128; only the blocks on or below the
+    // diagonal), and dQ = dS K is formed from it afterwards instead of
+    // recomputing the scores and dP.  nullptr: dQ recomputes them.
     uint16_t* ds = nullptr;
     int64_t ds_ld = 0;
 };
