@@ -721,7 +721,8 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_k(AttnBwdArgs a, int n_kt, i
     __shared__ __align__(16) float Dd[3][BKV];
     __shared__ uint4 Xh[2][4][4][64];  // per half tile and key group: P (s2 = 0, 1) and dS (s2 = 0, 1) per lane
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the wave index as a scalar, so that every per-wave test below is a branch
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int pw = wave & 3;
     const bool front = wave < 4;
     const int hh = lane >> 5, c = lane & 31;
@@ -860,17 +861,19 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_k(AttnBwdArgs a, int n_kt, i
                         float lv[4];
                         *reinterpret_cast<float4*>(lv) = *reinterpret_cast<const float4*>(&Ls[buf][qb]);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int jj = 4 * g4 + e, r = 8 * s2 + jj;
-                            float pr = ex2(fmaf(st[r], sc, -lv[e]));
-                            if (!full) {
-                                const int qq = q0 + qb + e;
-                                if (key > qq || qq >= S || key >= S) pr = 0.f;
-                            }
-                            tp[jj] = pr;
-                            td[jj] = pr * dp[r];  // dp holds dP - D
+                        for (int e = 0; e < 4; ++e) tp[4 * g4 + e] = ex2(fmaf(st[8 * s2 + 4 * g4 + e], sc, -lv[e]));
+                    }
+                    // causal and sequence-end masks only on the wave's tiles that
+                    // cross the diagonal or the end (a uniform branch)
+                    if (__builtin_expect(!full, 0)) {
+#pragma unroll
+                        for (int jj = 0; jj < 8; ++jj) {
+                            const int qq = q0 + 32 * t + 8 * (2 * s2 + (jj >> 2)) + 4 * hh + (jj & 3);
+                            if (key > qq || qq >= S || key >= S) tp[jj] = 0.f;
                         }
                     }
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj) td[jj] = tp[jj] * dp[8 * s2 + jj];  // dp holds dP - D
                     X[s2 * 64 + lane] = __builtin_bit_cast(uint4, pack_h8(tp));
                     const uint4 dsv = __builtin_bit_cast(uint4, pack_h8(td));
                     X[(2 + s2) * 64 + lane] = dsv;
