@@ -465,7 +465,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_k(AttnBwdArgs a, int n_qt, int
     __shared__ uint4 Ks[2][TILE];
     __shared__ uint4 Vs[2][TILE];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hh = lane >> 5, c = lane & 31;
     // Query tile heaviest first: across all (b, h) when qt_slow (up to 256
     // tiles per head: the last blocks out are the lightest), else within each
@@ -557,15 +557,17 @@ __global__ __launch_bounds__(256, 2) void attn_dq_k(AttnBwdArgs a, int n_qt, int
                 for (int s2 = 0; s2 < 2; ++s2) {
                     float tmp[8];
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const int r = 8 * s2 + j;
-                        float p = ex2(fmaf(st[t][r], sc, -lse2));
-                        if (!full) {
+                    for (int j = 0; j < 8; ++j) tmp[j] = ex2(fmaf(st[t][8 * s2 + j], sc, -lse2));
+                    if (__builtin_expect(!full, 0)) {  // a uniform branch: only tiles crossing the diagonal or the end
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            const int r = 8 * s2 + j;
                             const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
-                            if (key > q || key >= S) p = 0.f;
+                            if (key > q || key >= S) tmp[j] = 0.f;
                         }
-                        tmp[j] = p * (dp[t][r] + dq_nd);
                     }
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) tmp[j] *= dp[t][8 * s2 + j] + dq_nd;
                     dsb[t][s2] = pack_h8(tmp);
                 }
 #pragma unroll
@@ -610,7 +612,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_ds_k(AttnBwdArgs a, int n_qt, 
     __shared__ uint4 Ks[2][TILE];
     __shared__ uint4 Ss[2][STILE];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hh = lane >> 5, c = lane & 31;
     const int nbh = a.B * a.Hq;
     const int qt = n_qt - 1 - (qt_slow ? int(blockIdx.x / unsigned(nbh)) : int(blockIdx.x % unsigned(n_qt)));
