@@ -522,6 +522,11 @@ __global__ __launch_bounds__(256, 2) void attn_dq_k(AttnBwdArgs a, int n_qt, int
         const int cur = kb & 1;
         const int k0 = kb * BKV;
         if (kb + 1 < nkb) issue(k0 + BKV, cur ^ 1);
+        // dS of the tile, zero where the whole tile lies above the wave's
+        // queries; the dQ products then run unconditionally, which lets the
+        // accumulators stay in place across iterations (a conditional update
+        // made the compiler copy all 64 of them in and out every tile)
+        f16x8_t dsb[2][2];
         if (k0 <= qw + 31) {
             f32x16_t st[2], dp[2];
 #pragma unroll
@@ -549,7 +554,6 @@ __global__ __launch_bounds__(256, 2) void attn_dq_k(AttnBwdArgs a, int n_qt, int
                 }
                 __builtin_amdgcn_sched_barrier(0);
             });
-            f16x8_t dsb[2][2];
             const bool full = k0 + BKV - 1 <= qw && k0 + BKV <= S;
 #pragma unroll
             for (int t = 0; t < 2; ++t)
@@ -570,14 +574,19 @@ __global__ __launch_bounds__(256, 2) void attn_dq_k(AttnBwdArgs a, int n_qt, int
                     for (int j = 0; j < 8; ++j) tmp[j] *= dp[t][8 * s2 + j] + dq_nd;
                     dsb[t][s2] = pack_h8(tmp);
                 }
+        } else {
 #pragma unroll
-            for (int dt = 0; dt < ND; ++dt)
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2)
-                        acc[dt] = MFMA32H(tile_colT<HD>(Ks[cur], dt, t, s2, lane), dsb[t][s2], acc[dt]);
+                for (int s2 = 0; s2 < 2; ++s2) dsb[t][s2] = f16x8_t{};
         }
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+                    acc[dt] = MFMA32H(tile_colT<HD>(Ks[cur], dt, t, s2, lane), dsb[t][s2], acc[dt]);
         barrier_tile();
     }
     if (q < S) {
