@@ -118,7 +118,8 @@ int mt_k_attn_fwd(const void* qkv, int64_t ld, void* o, int64_t ldo, void* lse, 
  * requires the stored form (MT_E_INVAL where the shape does not allow it).
  * work: device scratch of mt_k_attn_bwd_work_bytes(B, S, Hq, Hkv, hd) bytes,
  * 256-byte aligned (D and the base-2 log-sum-exp, the scaled dO, the two
- * maxima, the partials of the automatic split, the stored dS where the shape
+ * maxima as 8 KB of partial maxima, the partials of the automatic split, the
+ * stored dS where the shape
  * takes it: B*Hq*Sp*Sp*2 bytes, Sp = S rounded up to 128);
  * B*S*Hq*hd/8 < 2^31.  mt_k_attn_dkdv_splits: the split count mt_k_attn_bwd
  * takes with such a buffer (0 on a bad shape). */

@@ -346,10 +346,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_k(AttnArgs a, int n_qt, int q
 // 2^k for the fp16 backward: the largest power of two with
 // max|dO| 2^k max|v| hd <= 2^14 (so |dP| = |dO . v| and |D| = |dO . o| stay
 // <= 2^14, o being a convex combination of v, and |dS| = P |dP - D| <= 2^15)
-// and max|dO| 2^k <= 2^14; 1 when dO is zero.  amax holds the two maxima as
-// float bit patterns (non-negative floats order like their bits).
+// and max|dO| 2^k <= 2^14; 1 when dO is zero.  amax holds each maximum as
+// AMAX_W partial maxima, one per 256-byte line (dO's in lines 0.., v's in
+// lines AMAX_W..), as float bit patterns (non-negative floats order like
+// their bits): the blocks of attn_amax_k spread their atomics over them, as
+// atomics on one word, or on words of one line, serialise (about 11 ns each
+// measured: 20 us for 1152 blocks).  The reads here are uniform, so they are
+// scalar loads.
+constexpr int AMAX_W = 16, AMAX_LINE = 64;  // partial maxima per quantity; words per line
+static_assert(2 * AMAX_W * AMAX_LINE * 4 == ATTN_AMAX_BYTES, "maxima scratch size");
 __device__ __forceinline__ float grad_scale(const uint32_t* amax, int hd) {
-    const float a = __uint_as_float(amax[0]), v = __uint_as_float(amax[1]);
+    uint32_t ab = 0, vb = 0;
+#pragma unroll
+    for (int i = 0; i < AMAX_W; ++i) {
+        ab = max(ab, amax[i * AMAX_LINE]);
+        vb = max(vb, amax[(AMAX_W + i) * AMAX_LINE]);
+    }
+    const float a = __uint_as_float(ab), v = __uint_as_float(vb);
     if (!(a > 0.f)) return 1.f;
     float lim = 16384.f / a;
     if (v > 0.f) lim = fminf(lim, 16384.f / (a * v * float(hd)));
@@ -360,10 +373,10 @@ __device__ __forceinline__ float grad_scale(const uint32_t* amax, int hd) {
 }
 
 // max |dO| over [T x Hq*hd] (row stride ldo) and max |v| over the value
-// heads of qkv into amax[0], amax[1] (zeroed first): the first nb_do blocks
-// stride over dO, the rest over v, four 16-byte loads in flight per lane; one
-// atomic max per block.  Indices are 32-bit (the host checks T*Hq*hd/8 <
-// 2^31).
+// heads of qkv into the partial maxima of amax (zeroed first): the first
+// nb_do blocks stride over dO, the rest over v, four 16-byte loads in flight
+// per lane; one atomic max per block, block i into partial i % AMAX_W of
+// its maximum.  Indices are 32-bit (the host checks T*Hq*hd/8 < 2^31).
 template <int HD>
 __global__ __launch_bounds__(256) void attn_amax_k(AttnBwdArgs a, int nb_do) {
     __shared__ float red[4];
@@ -400,7 +413,8 @@ __global__ __launch_bounds__(256) void attn_amax_k(AttnBwdArgs a, int nb_do) {
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
     __syncthreads();
     if (threadIdx.x == 0)
-        atomicMax(a.amax + (is_do ? 0 : 1), __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
+        atomicMax(a.amax + ((is_do ? 0 : AMAX_W) + bi % AMAX_W) * AMAX_LINE,
+                  __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
 }
 
 // -D 2^k = -rowsum(dO * O) 2^k (O fp16) into dsum (negated: the dK/dV kernel
@@ -409,23 +423,27 @@ __global__ __launch_bounds__(256) void attn_amax_k(AttnBwdArgs a, int nb_do) {
 // do16 (range-guarded; the scale keeps it below 2^14).  One lane per 16-byte
 // chunk of a (token, query head) row: the HD/8 lanes of a row are adjacent,
 // so a wave instruction covers whole rows, and the row's dot product is
-// reduced across them in a fixed order.
+// reduced across them in a fixed order.  Rows go in the [B x Hq x S] order of
+// dsum and lse, so a wave's sixteen rows of those are one 64-byte piece (in
+// token order, their 4-byte entries lay S apart and each took a memory
+// transaction of its own).
 template <int HD>
 __global__ __launch_bounds__(256) void attn_prep_k(AttnBwdArgs a) {
     constexpr int L = HD / 8;  // lanes per row
     const uint32_t i = blockIdx.x * 256 + threadIdx.x;
     const uint32_t nrow = uint32_t(int64_t(a.B) * a.S) * uint32_t(a.Hq);
-    const uint32_t r = i / L;
+    const uint32_t r = i / L;  // (b, h, sq) with sq fastest: the index into dsum and lse
     const int j = int(i % L);
     const float s2k = grad_scale(a.amax, HD);
     float s = 0.f;
-    uint32_t nov = 0, t = 0;
-    int h = 0;
+    uint32_t nov = 0;
     if (r < nrow) {
-        t = r / uint32_t(a.Hq);
-        h = int(r - t * uint32_t(a.Hq));
-        const uint4 ov = reinterpret_cast<const uint4*>(a.o + int64_t(t) * a.ldo + h * HD)[j];
-        const uint4 gv = reinterpret_cast<const uint4*>(a.dout + int64_t(t) * a.ldo + h * HD)[j];
+        const uint32_t bh = r / uint32_t(a.S), sq = r - bh * uint32_t(a.S);
+        const uint32_t b = bh / uint32_t(a.Hq);
+        const int h = int(bh - b * uint32_t(a.Hq));
+        const int64_t t = int64_t(b) * a.S + sq;
+        const uint4 ov = reinterpret_cast<const uint4*>(a.o + t * a.ldo + h * HD)[j];
+        const uint4 gv = reinterpret_cast<const uint4*>(a.dout + t * a.ldo + h * HD)[j];
         float x[8], y[8];
         unpack8h(ov, x);
         unpack8(gv, y);
@@ -434,15 +452,13 @@ __global__ __launch_bounds__(256) void attn_prep_k(AttnBwdArgs a) {
             s += x[k] * y[k];
             y[k] *= s2k;
         }
-        reinterpret_cast<uint4*>(a.do16 + int64_t(t) * (int64_t(a.Hq) * HD) + h * HD)[j] = pack8h_sat(y, nov);
+        reinterpret_cast<uint4*>(a.do16 + t * (int64_t(a.Hq) * HD) + h * HD)[j] = pack8h_sat(y, nov);
     }
 #pragma unroll
     for (int o = L / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
     if (r < nrow && j == 0) {
-        const uint32_t b = t / uint32_t(a.S), sq = t - b * uint32_t(a.S);
-        const int64_t idx = (int64_t(b) * a.Hq + h) * a.S + sq;
-        a.dsum[idx] = -(s * s2k);
-        a.dsum[int64_t(nrow) + idx] = a.lse[idx] * LOG2E;
+        a.dsum[r] = -(s * s2k);
+        a.dsum[int64_t(nrow) + r] = a.lse[r] * LOG2E;
     }
     count_ovf(a.ovf, nov);
 }
@@ -979,29 +995,43 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_k(AttnBwdArgs a, int n_kt, i
 
 // Sum of the ns partials of the split dK/dV pass, in split order: dK into
 // the fp32 buffer (or bf16 dqkv), dV into dqkv in bf16.  One lane per four
-// columns of a row's [dK | dV] partial.
+// columns of a row's [dK | dV] partial, all of its partials loaded before the
+// first is added.  Indices are 32-bit: a pass splits only with fewer than 512
+// key-tile blocks, so T*Hkv < 2^16 and T*Hkv*hd/2 < 2^22 (a 64-bit division
+// here had cost more than the loads).
 __global__ __launch_bounds__(256) void attn_dkdv_reduce_k(AttnBwdArgs a, int ns) {
-    const int64_t T = int64_t(a.B) * a.S;
-    const int w = a.Hkv * a.hd, q4 = w / 2;  // columns of one half; float4s per row
-    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    constexpr int NP = 8;  // partials loaded at once
+    const uint32_t T = uint32_t(a.B) * uint32_t(a.S);
+    const uint32_t w = uint32_t(a.Hkv * a.hd), q4 = w / 2;  // columns of one half; float4s per row
+    const uint32_t i = blockIdx.x * 256u + threadIdx.x;
     if (i >= T * q4) return;
-    const int64_t row = i / q4;
-    const int j = int(i - row * q4) * 4;
+    const uint32_t row = i / q4;
+    const uint32_t j = (i - row * q4) * 4;
+    const float* src = a.dpart + int64_t(row) * (2 * w) + j;
+    const int64_t pstride = int64_t(T) * (2 * w);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int p = 0; p < ns; ++p) {
-        const float4 v = *reinterpret_cast<const float4*>(a.dpart + (int64_t(p) * T + row) * (2 * int64_t(w)) + j);
-        acc.x += v.x;
-        acc.y += v.y;
-        acc.z += v.z;
-        acc.w += v.w;
+    for (int p0 = 0; p0 < ns; p0 += NP) {
+        float4 v[NP];
+#pragma unroll
+        for (int u = 0; u < NP; ++u)
+            if (p0 + u < ns) v[u] = *reinterpret_cast<const float4*>(src + (p0 + u) * pstride);
+#pragma unroll
+        for (int u = 0; u < NP; ++u)
+            if (p0 + u < ns) {
+                acc.x += v[u].x;
+                acc.y += v[u].y;
+                acc.z += v[u].z;
+                acc.w += v[u].w;
+            }
     }
+    const int64_t orow = int64_t(row);
     if (j < w) {
-        const int col = a.Hq * a.hd + j;
-        if (a.dqk32) *reinterpret_cast<float4*>(a.dqk32 + row * a.ld32 + col) = acc;
-        else *reinterpret_cast<uint2*>(a.dqkv + row * a.ldd + col) = make_uint2(pack2(acc.x, acc.y), pack2(acc.z, acc.w));
+        const int col = a.Hq * a.hd + int(j);
+        if (a.dqk32) *reinterpret_cast<float4*>(a.dqk32 + orow * a.ld32 + col) = acc;
+        else *reinterpret_cast<uint2*>(a.dqkv + orow * a.ldd + col) = make_uint2(pack2(acc.x, acc.y), pack2(acc.z, acc.w));
     } else {
-        const int col = (a.Hq + a.Hkv) * a.hd + (j - w);
-        *reinterpret_cast<uint2*>(a.dqkv + row * a.ldd + col) = make_uint2(pack2(acc.x, acc.y), pack2(acc.z, acc.w));
+        const int col = (a.Hq + a.Hkv) * a.hd + int(j - w);
+        *reinterpret_cast<uint2*>(a.dqkv + orow * a.ldd + col) = make_uint2(pack2(acc.x, acc.y), pack2(acc.z, acc.w));
     }
 }
 
@@ -1059,7 +1089,8 @@ int64_t attn_ds_bytes(int B, int S, int Hq) {
 
 int64_t attn_bwd_work_bytes(int B, int S, int Hq, int Hkv, int hd) {
     const int64_t T = int64_t(B) * S;
-    return al256(2 * T * Hq * 4) + al256(T * Hq * hd * 2) + 256 + al256(attn_bwd_part_elems(B, S, Hq, Hkv, hd) * 4) +
+    return al256(2 * T * Hq * 4) + al256(T * Hq * hd * 2) + ATTN_AMAX_BYTES +
+           al256(attn_bwd_part_elems(B, S, Hq, Hkv, hd) * 4) +
            al256(attn_ds_bytes(B, S, Hq));
 }
 
@@ -1071,7 +1102,7 @@ void attn_bwd_carve(void* work, int B, int S, int Hq, int Hkv, int hd, AttnBwdAr
     a.do16 = reinterpret_cast<uint16_t*>(p);
     p += al256(T * Hq * hd * 2);
     a.amax = reinterpret_cast<uint32_t*>(p);
-    p += 256;
+    p += ATTN_AMAX_BYTES;
     a.dpart_elems = attn_bwd_part_elems(B, S, Hq, Hkv, hd);
     a.dpart = a.dpart_elems ? reinterpret_cast<float*>(p) : nullptr;
     p += al256(a.dpart_elems * 4);
@@ -1090,6 +1121,8 @@ hipError_t attn_bwd(const AttnBwdArgs& a, hipStream_t s) {
     // room for a grid stride past the end)
     if (T * a.Hq * (a.hd / 8) >= (int64_t(1) << 31)) return hipErrorInvalidValue;
     const int ns = attn_dkdv_splits(a.B, a.S, a.Hq, a.Hkv, a.hd, a.dpart ? a.dpart_elems : 0, a.splits);
+    // the split reduction indexes with 32 bits (never reached: splits stop at 512 key-tile blocks)
+    if (ns > 1 && T * (a.Hkv * a.hd / 2) >= (int64_t(1) << 31)) return hipErrorInvalidValue;
     const int n_qt = (a.S + 127) / 128;
     const int n_kt = (a.S + 127) / 128;
     const int64_t nk = int64_t(n_kt) * a.B * a.Hkv * ns;
@@ -1100,7 +1133,7 @@ hipError_t attn_bwd(const AttnBwdArgs& a, hipStream_t s) {
     // maxima: enough blocks to cover the chip, each striding over its part
     const int nb_do = int(std::min<int64_t>(1024, (T * a.Hq * a.hd / 8 + 255) / 256));
     const int nb_v = int(std::min<int64_t>(128, (T * a.Hkv * a.hd / 8 + 255) / 256));
-    hipError_t e = fill_zero(a.amax, 256, s);
+    hipError_t e = fill_zero(a.amax, ATTN_AMAX_BYTES, s);
     if (e != hipSuccess) return e;
     // stored-dS form: dS must cover every key row and 128-query block
     const bool use_ds = a.ds != nullptr;

@@ -243,7 +243,7 @@ void plan_workspace(const Layout& lay, const mt_options& o, Carver& cv, Workspac
     ws.loss_rows = cv.take<float>(uint64_t(T) * 4);
     ws.loss = cv.take<float>(256);
     ws.ovf = cv.take<uint32_t>(256);
-    ws.amax = cv.take<uint32_t>(256);
+    ws.amax = cv.take<uint32_t>(ATTN_AMAX_BYTES);
 }
 
 ArenaPlan plan_arena(const Layout& lay, const mt_options& o, uint8_t* base, Workspace* ws) {

@@ -71,7 +71,7 @@ struct Workspace {
     // chunks, running max / sum of exp / label logit / LSE per token
     float *dnf_acc = nullptr, *ce_m = nullptr, *ce_l = nullptr, *ce_z = nullptr, *ce_lse = nullptr;
     uint32_t* ovf = nullptr;  // fp16 range guard: values saturated in this step
-    uint32_t* amax = nullptr;  // attention backward: max|dO|, max|v| (256 bytes)
+    uint32_t* amax = nullptr;  // attention backward: partial maxima of |dO|, |v| (ATTN_AMAX_BYTES)
     uint64_t bytes = 0;
 };
 

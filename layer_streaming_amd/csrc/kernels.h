@@ -112,13 +112,16 @@ struct AttnArgs {
     uint32_t* ovf = nullptr;    // fp16 range guard: o values saturated to +-65504
 };
 hipError_t attn_fwd(const AttnArgs& a, hipStream_t s);
+// Bytes of the attention backward's maxima scratch: 16 partial maxima of
+// |dO| and 16 of |v|, each in its own 256-byte line.
+constexpr int64_t ATTN_AMAX_BYTES = 8192;
 struct AttnBwdArgs {
     const uint16_t* qkv; int64_t ld;  // fp16 q, k, v as the forward used them
     const uint16_t* o; const uint16_t* dout; int64_t ldo;  // o fp16, dout bf16
     const float* lse;
     float* dsum;           // scratch [2 x B x Hq x S]: -rowsum(dO * O) 2^k, then lse log2(e)
     uint16_t* do16;        // scratch [B*S x Hq*hd] fp16: dO 2^k
-    uint32_t* amax;        // scratch, 256 bytes: max|dO| and max|v| that fix 2^k
+    uint32_t* amax;        // scratch, ATTN_AMAX_BYTES: partial maxima of |dO| and |v| that fix 2^k
     uint16_t* dqkv; int64_t ldd;  // output in qkv's column layout: dV bf16, and dQ, dK bf16 unless dqk32
     int B, S, Hq, Hkv, hd;
     // Optional: dQ and dK in fp32 [B*S x ld32] (the Hq query heads, then the

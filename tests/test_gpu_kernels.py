@@ -551,16 +551,20 @@ def test_attention_bwd_scale_follows_gradient_size(do_std):
 
 @pytest.mark.parametrize("B,S,Hq,Hkv,hd,splits,taken", [(1, 300, 7, 1, 128, 1, 1), (1, 300, 7, 1, 128, 3, 3),
                                                          (1, 1024, 28, 4, 128, 1, 1), (2, 200, 4, 2, 64, 1, 1),
-                                                         (1, 1024, 28, 4, 128, 0, 7), (2, 200, 4, 2, 64, 0, 2)])
+                                                         (1, 1024, 28, 4, 128, 0, 7), (2, 200, 4, 2, 64, 0, 2),
+                                                         (2, 256, 260, 130, 64, 2, 1)])
 def test_attention_dkdv_head_split(B, S, Hq, Hkv, hd, splits, taken):
     """The dK/dV pass with each KV group's query heads split over several
     blocks (fp32 partials added in split order; 3 of 7 heads is uneven) and
-    without a split: both against the oracle."""
+    without a split: both against the oracle.  The backward runs twice on
+    the same inputs and must repeat bit for bit.  A pass with 512 key-tile
+    blocks or more has no partials in its scratch, so a requested split is
+    not taken (the last case, 520 blocks)."""
     assert mt.lib.mt_k_attn_dkdv_splits(B, S, Hq, Hkv, hd, splits) == taken
-    _attention_case(B, S, Hq, Hkv, hd, 1.0, True, splits=splits)
+    _attention_case(B, S, Hq, Hkv, hd, 1.0, True, splits=splits, repeat=True)
 
 
-def _attention_case(B, S, Hq, Hkv, hd, qk_std, f32_out, do_std=1.0, splits=0, dq_form=0):
+def _attention_case(B, S, Hq, Hkv, hd, qk_std, f32_out, do_std=1.0, splits=0, dq_form=0, repeat=False):
     log(f"attention B={B} S={S} Hq={Hq} Hkv={Hkv} hd={hd} qk_std={qk_std} f32_out={f32_out} do_std={do_std} "
         f"splits={splits} dq_form={dq_form}")
     T = B * S
@@ -584,6 +588,17 @@ def _attention_case(B, S, Hq, Hkv, hd, qk_std, f32_out, do_std=1.0, splits=0, dq
                                   ovf.data_ptr(), s))
     _sync()
     assert ovf[0].item() == 0
+    if repeat:
+        d_dqkv2 = dev_zeros_bits((T, ld))
+        dqk32_2 = torch.zeros((T, nr), dtype=torch.float32, device="cuda") if f32_out else None
+        mt.check(mt.lib.mt_k_attn_bwd(d_qkv.data_ptr(), ld, d_o.data_ptr(), d_do.data_ptr(), nq, lse.data_ptr(),
+                                      work.data_ptr(), d_dqkv2.data_ptr(), ld, B, S, Hq, Hkv, hd,
+                                      dqk32_2.data_ptr() if f32_out else None, nr if f32_out else 0, splits,
+                                      dq_form, ovf.data_ptr(), s))
+        _sync()
+        assert torch.equal(d_dqkv2, d_dqkv)
+        if f32_out:
+            assert torch.equal(dqk32_2.view(torch.int32), dqk32.view(torch.int32))
     x = qkv.astype(np.float64).reshape(B, S, Hq + 2 * Hkv, hd)
     q, k, v = x[:, :, :Hq], x[:, :, Hq:Hq + Hkv], x[:, :, Hq + Hkv:]
     o_ref = block.attention_fwd(q, k, v)

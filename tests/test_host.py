@@ -341,7 +341,8 @@ def test_attention_dkdv_split_count_rule():
 
 def test_attention_backward_work_covers_the_automatic_split():
     """The attention backward's scratch holds D and the base-2 log-sum-exp,
-    the scaled dO, the maxima, when the dK/dV pass splits the fp32 partials
+    the scaled dO, the partial maxima (32 lines of 256 bytes), when the
+    dK/dV pass splits the fp32 partials
     of every split, and for sequences up to 1024 whose dS fits 1 GiB the
     stored dS (B*Hq*Sp^2 fp16, Sp = S rounded up to 128)."""
     al = lambda x: (x + 255) // 256 * 256
@@ -354,6 +355,6 @@ def test_attention_backward_work_covers_the_automatic_split():
         part = ns * T * 2 * Hkv * hd if ns > 1 else 0
         sp = (S + 127) // 128 * 128
         ds = B * Hq * sp * sp * 2 if has_ds else 0
-        want = al(2 * T * Hq * 4) + al(T * Hq * hd * 2) + 256 + al(part * 4) + al(ds)
+        want = al(2 * T * Hq * 4) + al(T * Hq * hd * 2) + 8192 + al(part * 4) + al(ds)
         assert mt.lib.mt_k_attn_bwd_work_bytes(B, S, Hq, Hkv, hd) == want, (B, S, Hq)
     assert mt.lib.mt_k_attn_bwd_work_bytes(1, 100, 6, 4, 128) == 0   # not a grouping
