@@ -34,6 +34,25 @@ int mt_k_gemm(int32_t layout, int32_t epi, const void* A, int64_t lda, const voi
               int64_t ldc, const void* R, int64_t ldr, const void* Cacc, int64_t ldacc, int32_t M, int32_t N,
               int32_t K, void* stream);
 
+/* mt_k_gemm with scratch for the K-split of the last partial round of
+ * 256 x 256 tiles (the form the library's own products take): when the
+ * product runs on 256 x 256 tiles and the tiles do not fill whole rounds of
+ * the 256 CUs, the tiles of the last, partial round may be cut into `splits`
+ * ranges of K, each a block of its own, whose fp32 partials (256 KB per block,
+ * in `ws`) a second kernel adds in split order before the epilogue.
+ * splits = 0: the library's choice (mt_k_gemm_split_plan); 1: no split;
+ * n > 1: n ranges (tests), MT_E_INVAL if ws_bytes cannot hold them.  ws must
+ * be 16-byte aligned and overlap no operand; ws = NULL is mt_k_gemm. */
+int mt_k_gemm_split(int32_t layout, int32_t epi, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                    int64_t ldc, const void* R, int64_t ldr, const void* Cacc, int64_t ldacc, int32_t M, int32_t N,
+                    int32_t K, void* ws, int64_t ws_bytes, int32_t splits, void* stream);
+/* The split the library takes for an M x N x K product on 256 x 256 tiles
+ * with ws_bytes of scratch (host only, no GPU): writes the number of tiles
+ * that run whole, the number of K ranges of each later tile (1: no split)
+ * and the 64-deep k-steps per range. */
+int mt_k_gemm_split_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int32_t* n_full, int32_t* splits,
+                         int32_t* ksteps);
+
 /* fp16 range guard.  Every entry that writes fp16 values (the attention
  * operands) saturates a value whose magnitude rounds beyond the fp16 range
  * (|x| >= 65520, or not finite) to +-65504 (a NaN stays a NaN) and, when

@@ -76,6 +76,30 @@ int mt_k_gemm(int32_t layout, int32_t epi, const void* A, int64_t lda, const voi
     return kst(mt::gemm(mt::GemmLayout(layout), mt::GemmEpi(epi), a, S_(stream)), "gemm");
 }
 
+int mt_k_gemm_split(int32_t layout, int32_t epi, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                    int64_t ldc, const void* R, int64_t ldr, const void* Cacc, int64_t ldacc, int32_t M, int32_t N,
+                    int32_t K, void* ws, int64_t ws_bytes, int32_t splits, void* stream) {
+    if (layout < 0 || layout > 2 || epi < 0 || epi > 8) MT_FAIL(MT_E_INVAL, "bad layout or epilogue");
+    if (splits < 0 || splits > 64 || ws_bytes < 0) MT_FAIL(MT_E_INVAL, "bad split count or scratch size");
+    if (ws && (reinterpret_cast<uintptr_t>(ws) & 15)) MT_FAIL(MT_E_INVAL, "scratch not 16-byte aligned");
+    mt::GemmArgs a{A, lda, B, ldb, C, ldc, R, ldr, static_cast<const float*>(Cacc), ldacc, M, N, K};
+    a.ws = static_cast<float*>(ws);
+    a.ws_bytes = ws ? uint64_t(ws_bytes) : 0;
+    a.force_splits = splits;
+    return kst(mt::gemm(mt::GemmLayout(layout), mt::GemmEpi(epi), a, S_(stream)), "gemm_split");
+}
+
+int mt_k_gemm_split_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int32_t* n_full, int32_t* splits,
+                         int32_t* ksteps) {
+    if (M <= 0 || N <= 0 || K <= 0 || ws_bytes < 0 || !n_full || !splits || !ksteps)
+        MT_FAIL(MT_E_INVAL, "bad split plan arguments");
+    const mt::GemmSplit sp = mt::gemm_split_plan(M, N, K, uint64_t(ws_bytes));
+    *n_full = sp.n_full;
+    *splits = sp.splits;
+    *ksteps = sp.kper;
+    return MT_OK;
+}
+
 int mt_k_rmsnorm_fwd(const void* x, int32_t x_f32, const void* gamma, void* n, void* n_f16, void* rstd, int32_t T,
                      int32_t d, float eps, void* fp16_ovf, void* stream) {
     return kst(mt::rmsnorm_fwd(x, x_f32 != 0, U16(gamma), U16(n), n_f16 ? U16(n_f16) : nullptr, F32(rstd), T, d, eps,

@@ -246,6 +246,14 @@ void plan_workspace(const Layout& lay, const mt_options& o, Carver& cv, Workspac
     ws.amax = cv.take<uint32_t>(ATTN_AMAX_BYTES);
 }
 
+// A direct-form product's tail-split scratch: tA, which no transpose holds
+// while such a product runs (the fallbacks that transpose into tA get none).
+GemmArgs split_ws(GemmArgs a, const Workspace& ws) {
+    a.ws = reinterpret_cast<float*>(ws.tA);
+    a.ws_bytes = ws.tA_bytes;
+    return a;
+}
+
 ArenaPlan plan_arena(const Layout& lay, const mt_options& o, uint8_t* base, Workspace* ws) {
     ArenaPlan p;
     p.slot_bytes = o.slot_bytes_override ? al4k(o.slot_bytes_override)
@@ -1140,7 +1148,7 @@ hipError_t Ctx::fwd_layer(const LayerView& w, const uint16_t* x, uint16_t* y, in
     HIPR(site(S_GEMM_QKV, [&] {
         HIPR(bf16_to_f16(w.wqkv, ws.w16, int64_t(nqkv) * d, s, ws.ovf));
         GemmArgs a{ws.n1h, d, ws.w16, d, ws.qkv32, nqkv, nullptr, 0, nullptr, 0, T, nqkv, d};
-        return gemm(GEMM_NT, EPI_F32_F16IN, a, s);
+        return gemm(GEMM_NT, EPI_F32_F16IN, split_ws(a, ws), s);
     }));
     HIPR(site(S_ROPE_FWD, [&] {
         return qkv_rope_cvt(ws.qkv32, nqkv, ws.qkv, nqkv, nullptr, 0, ws.rope_tab, T, S, sh.n_heads + sh.n_kv_heads,
@@ -1156,18 +1164,18 @@ hipError_t Ctx::fwd_layer(const LayerView& w, const uint16_t* x, uint16_t* y, in
         // ws.w16 is free again: the QKV product before it on this stream read it
         HIPR(bf16_to_f16(w.wo, ws.w16, int64_t(d) * nq, s, ws.ovf));
         GemmArgs a{ws.oa[ob], nq, ws.w16, nq, ws.h1, d, x, d, nullptr, 0, T, d, nq};
-        return gemm(GEMM_NT, EPI_F32_F16IN_RESID, a, s);
+        return gemm(GEMM_NT, EPI_F32_F16IN_RESID, split_ws(a, ws), s);
     }));
     HIPR(site(S_RMS2_FWD, [&] { return rmsnorm_fwd(ws.h1, true, w.g2, ws.n2, nullptr, ws.rstd2, T, d, sh.rms_eps, s); }));
     HIPR(site(S_GEMM_GATEUP, [&] {
         GemmArgs a{ws.n2, d, w.wgu, d, ws.gu, 2 * F, nullptr, 0, nullptr, 0, T, 2 * F, d};
-        return gemm(GEMM_NT, EPI_BF16, a, s);
+        return gemm(GEMM_NT, EPI_BF16, split_ws(a, ws), s);
     }));
     HIPR(site(S_SWIGLU_FWD, [&] { return swiglu_fwd(ws.gu, ws.m, T, F, s); }));
     if (need_y) {
         HIPR(site(S_GEMM_DOWN, [&] {
             GemmArgs a{ws.m, F, w.wd, F, y, d, ws.h1, d, nullptr, 0, T, d, F};
-            return gemm(GEMM_NT, EPI_BF16_RESID32, a, s);
+            return gemm(GEMM_NT, EPI_BF16_RESID32, split_ws(a, ws), s);
         }));
     }
     return hipSuccess;
@@ -1253,7 +1261,7 @@ hipError_t Ctx::head_chunk_fwd(const HeadChunk& ch, bool first, bool last, const
         const int rows = std::min(tc, T - r0);
         HIPR(site(S_HEAD_LOGITS, [&] {
             GemmArgs a{ws.nf + int64_t(r0) * d, d, E, d, ws.logits, ch.rows, nullptr, 0, nullptr, 0, rows, ch.rows, d};
-            return gemm(GEMM_NT, EPI_F32, a, s);
+            return gemm(GEMM_NT, EPI_F32, split_ws(a, ws), s);
         }));
         HIPR(site(S_HEAD_CE, [&] {
             return ce_chunk_fwd(ws.logits, ws.labels + r0, rows, ch.rows, ch.row0, first, ws.ce_m + r0,
@@ -1291,7 +1299,7 @@ hipError_t Ctx::head_chunk_bwd(const HeadChunk& ch, bool first, bool last, const
         const int r0 = c * tc, rows = std::min(tc, T - r0);
         HIPR(site(S_HEAD_LOGITS, [&] {
             GemmArgs a{ws.nf + int64_t(r0) * d, d, E, d, ws.logits, ch.rows, nullptr, 0, nullptr, 0, rows, ch.rows, d};
-            return gemm(GEMM_NT, EPI_F32, a, s);
+            return gemm(GEMM_NT, EPI_F32, split_ws(a, ws), s);
         }));
         HIPR(site(S_HEAD_CE, [&] {
             return ce_chunk_bwd(ws.logits, ws.labels + r0, ws.ce_lse + r0, rows, ch.rows, ch.row0, ws.dlogits,
@@ -1305,7 +1313,7 @@ hipError_t Ctx::head_chunk_bwd(const HeadChunk& ch, bool first, bool last, const
             float* dx = ws.dnf_acc + int64_t(r0) * d;
             {
                 GemmArgs a{ws.dlogits, ch.rows, E, d, dx, d, nullptr, 0, nullptr, 0, rows, d, ch.rows};
-                const hipError_t e = gemm_direct_checked(GEMM_NN, epi, a, s);
+                const hipError_t e = gemm_direct_checked(GEMM_NN, epi, split_ws(a, ws), s);
                 if (e != hipErrorNotSupported) return e;
             }
             if (!tB_holds_chunk) {
@@ -1323,7 +1331,7 @@ hipError_t Ctx::head_chunk_bwd(const HeadChunk& ch, bool first, bool last, const
             else if (c == 0) { a.C = ws.deout_acc; epi = EPI_F32; }
             else if (c + 1 < nch) { a.C = ws.deout_acc; epi = EPI_F32_ACC; }
             else { a.C = gE; a.Cacc = ws.deout_acc; a.ldacc = d; epi = EPI_BF16_ACCF32; }
-            return gemm(GEMM_TN, epi, a, s);
+            return gemm(GEMM_TN, epi, split_ws(a, ws), s);
         }));
     }
     if (last) {
@@ -1342,7 +1350,7 @@ hipError_t Ctx::gemm_nn_t(const uint16_t* A, int64_t lda, const uint16_t* Bm, in
                           int M, int N, int K) {
     {
         GemmArgs a{A, lda, Bm, ldb, C, ldc, nullptr, 0, nullptr, 0, M, N, K};
-        const hipError_t e = gemm_direct_checked(GEMM_NN, EPI_BF16, a, st_c);
+        const hipError_t e = gemm_direct_checked(GEMM_NN, EPI_BF16, split_ws(a, ws), st_c);
         if (e != hipErrorNotSupported) return e;
     }
     HIPR(transpose16(Bm, ldb, ws.tB, K, K, N, st_c));
@@ -1360,7 +1368,7 @@ hipError_t Ctx::gemm_tn_t(const uint16_t* A, int64_t lda, const uint16_t* Bm, in
     {
         GemmArgs a{A, lda, Bm, ldb, C, ldc, nullptr, 0, nullptr, 0, M, N, K};
         a.b_f16 = b_f16;
-        const hipError_t e = gemm_direct_checked(GEMM_TN, EPI_BF16, a, st_c);
+        const hipError_t e = gemm_direct_checked(GEMM_TN, EPI_BF16, split_ws(a, ws), st_c);
         if (e != hipErrorNotSupported) return e;
     }
     const int Kp = (K + 7) & ~7;
@@ -1388,14 +1396,14 @@ hipError_t Ctx::head(const HeadView& w, const HeadView& g, const uint16_t* xL, u
         const int r0 = c * tc, rows = std::min(tc, T - r0);
         HIPR(site(S_HEAD_LOGITS, [&] {
             GemmArgs a{ws.nf + int64_t(r0) * d, d, w.eout, d, ws.logits, V, nullptr, 0, nullptr, 0, rows, V, d};
-            return gemm(GEMM_NT, EPI_F32, a, s);
+            return gemm(GEMM_NT, EPI_F32, split_ws(a, ws), s);
         }));
         HIPR(site(S_HEAD_CE, [&] {
             return ce_fwd_bwd(ws.logits, ws.labels + r0, ws.loss_rows + r0, ws.dlogits, rows, V, inv_tokens, s);
         }));
         HIPR(site(S_HEAD_DX, [&] {
             GemmArgs a{ws.dlogits, V, w.eout, d, ws.dnf + int64_t(r0) * d, d, nullptr, 0, nullptr, 0, rows, d, V};
-            return gemm(GEMM_NN, EPI_BF16, a, s);
+            return gemm(GEMM_NN, EPI_BF16, split_ws(a, ws), s);
         }));
         HIPR(site(S_HEAD_DW, [&] {
             GemmArgs a{ws.dlogits, V, ws.nf + int64_t(r0) * d, d, nullptr, d, nullptr, 0, nullptr, 0, V, d, rows};
@@ -1404,7 +1412,7 @@ hipError_t Ctx::head(const HeadView& w, const HeadView& g, const uint16_t* xL, u
             else if (c == 0) { a.C = ws.deout_acc; epi = EPI_F32; }
             else if (c + 1 < nch) { a.C = ws.deout_acc; epi = EPI_F32_ACC; }
             else { a.C = g.eout; a.Cacc = ws.deout_acc; a.ldacc = d; epi = EPI_BF16_ACCF32; }
-            return gemm(GEMM_TN, epi, a, s);
+            return gemm(GEMM_TN, epi, split_ws(a, ws), s);
         }));
     }
     HIPR(site(S_HEAD_RMS_BWD, [&] {

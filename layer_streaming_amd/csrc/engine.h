@@ -60,6 +60,7 @@ struct Workspace {
     // reduction-contiguous copies of the backward products' operands
     uint16_t *tA, *tB;
     uint64_t tA_bytes = 0;  // also the dK/dV split partials of the attention backward (tA is idle then)
+                            // and the fp32 partial tiles of split direct-form GEMMs (idle then too)
     float *dsum, *partial;
     float2* rope_tab;
     int32_t* labels;

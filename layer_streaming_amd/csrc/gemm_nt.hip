@@ -501,6 +501,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_k(GemmArgs p, int tiles_
 // four 32-deep stages give.
 constexpr int BK64 = 64;
 
+// Tile (tm, tn) of position pid in the order of gemm_nt_k: tiles grouped
+// MT_NT_GROUP deep along M, N-major within a group.
+__device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
+    constexpr int GROUP = MT_NT_GROUP;
+    const int per_group = GROUP * tiles_n;
+    const int g = pid / per_group;
+    const int first_m = g * GROUP;
+    const int gsz = min(tiles_m - first_m, GROUP);
+    tm = first_m + (pid % per_group) % gsz;
+    tn = (pid % per_group) / gsz;
+}
+
 // Physical chunk (of eight) of logical chunk c in a 128-byte LDS row r: a
 // 128-bit read of 16 consecutive rows touches each of the 16 positions of a
 // 256-byte bank line once when rows of one parity take distinct chunks.
@@ -639,7 +651,7 @@ __device__ __forceinline__ void read_frags64(const uint4* __restrict__ a_l, cons
 // of C = op(A) op(B) then run on the same main loop with no transposed copy.
 // BH: B holds fp16 values, rounded to bf16 as each fragment is read.
 template <int BM, int BN, int WM, int WN, int EPI, bool TA = false, bool TB = false, bool BH = false>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_nt64_k(GemmArgs p, int tiles_m, int tiles_n) {
+__global__ __launch_bounds__(WM * WN * 64) void gemm_nt64_k(GemmArgs p, int tiles_m, int tiles_n, GemmSplit sp) {
     constexpr int NW = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
@@ -651,17 +663,21 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt64_k(GemmArgs p, int tile
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
 
-    // tile order: as in gemm_nt_k
-    const int total = tiles_m * tiles_n;
-    int pid = blockIdx.x;
-    if ((total & 7) == 0) pid = (pid & 7) * (total >> 3) + (pid >> 3);
-    constexpr int GROUP = MT_NT_GROUP;
-    const int per_group = GROUP * tiles_n;
-    const int g = pid / per_group;
-    const int first_m = g * GROUP;
-    const int gsz = min(tiles_m - first_m, GROUP);
-    const int tm = first_m + (pid % per_group) % gsz;
-    const int tn = (pid % per_group) / gsz;
+    // Blocks below sp.n_full take whole tiles in the order of gemm_nt_k; each
+    // later block takes k-steps [kb, kb + nkl) of tile n_full + slot / splits
+    // and leaves its fp32 partial in scratch slot `slot`.
+    const int nk = (p.K + BK64 - 1) / BK64;
+    int pid = blockIdx.x, kb = 0, nkl = nk, slot = -1;
+    if (pid < sp.n_full) {
+        if ((sp.n_full & 7) == 0) pid = (pid & 7) * (sp.n_full >> 3) + (pid >> 3);
+    } else {
+        slot = pid - sp.n_full;
+        pid = sp.n_full + slot / sp.splits;
+        kb = (slot % sp.splits) * sp.kper;
+        nkl = min(nk - kb, sp.kper);
+    }
+    int tm, tn;
+    tile_coords(pid, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
     const int rows_a = min(BM, p.M - m0), rows_b = min(BN, p.N - n0);
@@ -700,15 +716,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt64_k(GemmArgs p, int tile
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    const int nk = (p.K + BK64 - 1) / BK64;
     uint4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
 
 #define RD(SA, SB, KS, FA, FB) read_frags64<FM, FN, TM, TN, TA, TB, BM, BN, BH>(SA, SB, KS, wm, wn, lane, FA, FB)
 #define MM(FA, FB) mma_frags<FM, FN, F16>(FA, FB, acc)
 #define PRIO(x) if (MT_NT_PRIO) __builtin_amdgcn_s_setprio(x)
 #define LOAD_ONE(g, XA, XB, T)                                                           \
-    if constexpr ((g) < NIA) la.issue_one((g), ra, XA, wave, (T) * BK64, p.K);           \
-    else lb.issue_one((g) - NIA, rb, XB, wave, (T) * BK64, p.K)
+    if constexpr ((g) < NIA) la.issue_one((g), ra, XA, wave, (kb + (T)) * BK64, p.K);    \
+    else lb.issue_one((g) - NIA, rb, XB, wave, (kb + (T)) * BK64, p.K)
 // One k-step's MFMAs with loads G0 .. G0+NL-1 of tile T2, spread evenly.
 #define MM_LOADS(FA, FB, G0, NL, XA, XB, T2, do_load)                                    \
     static_for<0, NL>([&](auto g_) {                                                     \
@@ -725,9 +740,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt64_k(GemmArgs p, int tile
 // and multiplies step 3 of tile T with the first half of tile T+2's loads,
 // which go into this tile's stage, free since the barrier.
 #define TILE(T, SA, SB, NA, NB)                                                          \
-    if ((T) < nk) {                                                                      \
-        const bool ld1 = (T) >= 1 && (T) + 1 < nk;                                       \
-        const bool ld2 = (T) + 2 < nk;                                                   \
+    if ((T) < nkl) {                                                                     \
+        const bool ld1 = (T) >= 1 && (T) + 1 < nkl;                                      \
+        const bool ld2 = (T) + 2 < nkl;                                                  \
         RD(SA, SB, 1, fa1, fb1);                                                         \
         __builtin_amdgcn_sched_barrier(0);                                               \
         PRIO(1);                                                                         \
@@ -747,18 +762,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt64_k(GemmArgs p, int tile
         PRIO(0);                                                                         \
         wait_vmem<0>();                                                                  \
         barrier_lds();                                                                   \
-        if ((T) + 1 < nk) { RD(NA, NB, 0, fa0, fb0); }                                   \
+        if ((T) + 1 < nkl) { RD(NA, NB, 0, fa0, fb0); }                                  \
         __builtin_amdgcn_sched_barrier(0);                                               \
         PRIO(1);                                                                         \
         MM_LOADS(fa1, fb1, 0, NIT - L1, SA, SB, (T) + 2, ld2);                           \
         PRIO(0);                                                                         \
     }
 
-    la.issue(ra, As0, wave, 0, p.K);
-    lb.issue(rb, Bs0, wave, 0, p.K);
-    if (nk > 1) {
-        la.issue(ra, As1, wave, BK64, p.K);
-        lb.issue(rb, Bs1, wave, BK64, p.K);
+    la.issue(ra, As0, wave, kb * BK64, p.K);
+    lb.issue(rb, Bs0, wave, kb * BK64, p.K);
+    if (nkl > 1) {
+        la.issue(ra, As1, wave, (kb + 1) * BK64, p.K);
+        lb.issue(rb, Bs1, wave, (kb + 1) * BK64, p.K);
         __builtin_amdgcn_sched_barrier(0);
         wait_vmem<NIT>();
     } else {
@@ -766,7 +781,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt64_k(GemmArgs p, int tile
     }
     barrier_lds();
     RD(As0, Bs0, 0, fa0, fb0);
-    for (int t = 0; t < nk; t += 2) {
+    for (int t = 0; t < nkl; t += 2) {
         TILE(t, As0, Bs0, As1, Bs1)
         TILE(t + 1, As1, Bs1, As0, Bs0)
     }
@@ -783,55 +798,145 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt64_k(GemmArgs p, int tile
         constexpr int CAP = BM * 128 / PER;          // bytes per wave
         const int q = wave / PER;
         uint4* const arr = q == 0 ? As0 : q == 1 ? As1 : q == 2 ? Bs0 : Bs1;
-        staged_store<FM, FN, TM, TN, CAP, EPI>(p, acc, reinterpret_cast<float4*>(arr) + (wave % PER) * (CAP / 16),
-                                               lane, m0 + wm * TM, n0 + wn * TN);
+        float4* const st = reinterpret_cast<float4*>(arr) + (wave % PER) * (CAP / 16);
+        if (slot >= 0) {
+            // partial tile: fp32 rows of BN values in scratch slot `slot`
+            GemmArgs q2 = p;
+            q2.C = p.ws + int64_t(slot) * (BM * BN);
+            q2.ldc = BN;
+            q2.M = BM;
+            q2.N = BN;
+            staged_store<FM, FN, TM, TN, CAP, EPI_F32>(q2, acc, st, lane, wm * TM, wn * TN);
+        } else {
+            staged_store<FM, FN, TM, TN, CAP, EPI>(p, acc, st, lane, m0 + wm * TM, n0 + wn * TN);
+        }
     }
+}
+
+// Tail tiles of a split product: output tile n_full + blockIdx.x / 64 is the
+// sum of its `splits` fp32 partials in split order (k-ranges ascending), then
+// the product's epilogue.  Thread: 4 consecutive columns of one row.
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_split_fixup_k(GemmArgs p, int tiles_m, int tiles_n, GemmSplit sp) {
+    const int t = blockIdx.x >> 6;
+    const int e = (blockIdx.x & 63) * 256 + threadIdx.x;
+    const int r = e >> 6, c = (e & 63) * 4;
+    int tm, tn;
+    tile_coords(sp.n_full + t, tiles_m, tiles_n, tm, tn);
+    const int row = tm * 256 + r, col = tn * 256 + c;
+    if (row >= p.M || col >= p.N) return;
+    const float* w = p.ws + int64_t(t) * sp.splits * 65536 + r * 256 + c;
+    float4 a = *reinterpret_cast<const float4*>(w);
+    for (int i = 1; i < sp.splits; ++i) {
+        const float4 b = *reinterpret_cast<const float4*>(w + int64_t(i) * 65536);
+        a.x += b.x;
+        a.y += b.y;
+        a.z += b.z;
+        a.w += b.w;
+    }
+    const float v[4] = {a.x, a.y, a.z, a.w};
+    store4<EPI>(p, row, col, v);
+}
+
+// The split a direct-form launch on 256 x 256 tiles takes (see gemm_split_plan).
+hipError_t split_for(const GemmArgs& a, int tm, int tn, GemmSplit& sp) {
+    const int total = tm * tn, nk = (a.K + 63) / 64;
+    sp = GemmSplit{total, 1, nk};
+    if (!a.ws) return hipSuccess;
+    if (a.force_splits <= 0) {
+        sp = gemm_split_plan(a.M, a.N, a.K, a.ws_bytes);
+        return hipSuccess;
+    }
+    if (a.force_splits == 1) return hipSuccess;
+    const int n_full = (total / 256) * 256;
+    if (n_full == total) return hipSuccess;
+    const int kper = (nk + a.force_splits - 1) / a.force_splits;
+    const int splits = (nk + kper - 1) / kper;   // every split non-empty
+    if (splits <= 1) return hipSuccess;
+    if (uint64_t(total - n_full) * splits * 65536u * 4u > a.ws_bytes) return hipErrorInvalidValue;
+    sp = GemmSplit{n_full, splits, kper};
+    return hipSuccess;
+}
+
+template <int EPI>
+void launch_fixup_e(const GemmArgs& a, int tm, int tn, const GemmSplit& sp, hipStream_t s) {
+    const int tail = tm * tn - sp.n_full;
+    gemm_split_fixup_k<EPI><<<dim3(tail * 64), dim3(256), 0, s>>>(a, tm, tn, sp);
+}
+
+hipError_t launch_fixup(GemmEpi epi, const GemmArgs& a, int tm, int tn, const GemmSplit& sp, hipStream_t s) {
+    switch (epi) {
+        case EPI_BF16: launch_fixup_e<EPI_BF16>(a, tm, tn, sp, s); break;
+        case EPI_BF16_RESID: launch_fixup_e<EPI_BF16_RESID>(a, tm, tn, sp, s); break;
+        case EPI_F32: launch_fixup_e<EPI_F32>(a, tm, tn, sp, s); break;
+        case EPI_F32_ACC: launch_fixup_e<EPI_F32_ACC>(a, tm, tn, sp, s); break;
+        case EPI_BF16_ACCF32: launch_fixup_e<EPI_BF16_ACCF32>(a, tm, tn, sp, s); break;
+        case EPI_F32_RESID: launch_fixup_e<EPI_F32_RESID>(a, tm, tn, sp, s); break;
+        case EPI_BF16_RESID32: launch_fixup_e<EPI_BF16_RESID32>(a, tm, tn, sp, s); break;
+        case EPI_F32_F16IN: launch_fixup_e<EPI_F32_F16IN>(a, tm, tn, sp, s); break;
+        case EPI_F32_F16IN_RESID: launch_fixup_e<EPI_F32_F16IN_RESID>(a, tm, tn, sp, s); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// Grid of a split launch: whole tiles, then `splits` blocks per tail tile.
+inline dim3 split_grid(int tm, int tn, const GemmSplit& sp) {
+    return dim3(sp.n_full + (tm * tn - sp.n_full) * sp.splits);
 }
 
 template <int BM, int BN, int WM, int WN, bool K64>
 hipError_t launch(GemmEpi epi, const GemmArgs& a, hipStream_t s) {
     const int tm = (a.M + BM - 1) / BM, tn = (a.N + BN - 1) / BN;
-    const dim3 grid(tm * tn), block(WM * WN * 64);
+    const dim3 block(WM * WN * 64);
+    GemmSplit sp{tm * tn, 1, (a.K + 63) / 64};
+    if constexpr (K64 && BM == 256 && BN == 256) {
+        const hipError_t e = split_for(a, tm, tn, sp);
+        if (e != hipSuccess) return e;
+    }
+    const dim3 grid = K64 ? split_grid(tm, tn, sp) : dim3(tm * tn);
     switch (epi) {
         case EPI_BF16:
-            if constexpr (K64) gemm_nt64_k<BM, BN, WM, WN, EPI_BF16><<<grid, block, 0, s>>>(a, tm, tn);
+            if constexpr (K64) gemm_nt64_k<BM, BN, WM, WN, EPI_BF16><<<grid, block, 0, s>>>(a, tm, tn, sp);
             else gemm_nt_k<BM, BN, WM, WN, EPI_BF16><<<grid, block, 0, s>>>(a, tm, tn);
             break;
         case EPI_BF16_RESID:
-            if constexpr (K64) gemm_nt64_k<BM, BN, WM, WN, EPI_BF16_RESID><<<grid, block, 0, s>>>(a, tm, tn);
+            if constexpr (K64) gemm_nt64_k<BM, BN, WM, WN, EPI_BF16_RESID><<<grid, block, 0, s>>>(a, tm, tn, sp);
             else gemm_nt_k<BM, BN, WM, WN, EPI_BF16_RESID><<<grid, block, 0, s>>>(a, tm, tn);
             break;
         case EPI_F32:
-            if constexpr (K64) gemm_nt64_k<BM, BN, WM, WN, EPI_F32><<<grid, block, 0, s>>>(a, tm, tn);
+            if constexpr (K64) gemm_nt64_k<BM, BN, WM, WN, EPI_F32><<<grid, block, 0, s>>>(a, tm, tn, sp);
             else gemm_nt_k<BM, BN, WM, WN, EPI_F32><<<grid, block, 0, s>>>(a, tm, tn);
             break;
         case EPI_F32_ACC:
-            if constexpr (K64) gemm_nt64_k<BM, BN, WM, WN, EPI_F32_ACC><<<grid, block, 0, s>>>(a, tm, tn);
+            if constexpr (K64) gemm_nt64_k<BM, BN, WM, WN, EPI_F32_ACC><<<grid, block, 0, s>>>(a, tm, tn, sp);
             else gemm_nt_k<BM, BN, WM, WN, EPI_F32_ACC><<<grid, block, 0, s>>>(a, tm, tn);
             break;
         case EPI_BF16_ACCF32:
-            if constexpr (K64) gemm_nt64_k<BM, BN, WM, WN, EPI_BF16_ACCF32><<<grid, block, 0, s>>>(a, tm, tn);
+            if constexpr (K64) gemm_nt64_k<BM, BN, WM, WN, EPI_BF16_ACCF32><<<grid, block, 0, s>>>(a, tm, tn, sp);
             else gemm_nt_k<BM, BN, WM, WN, EPI_BF16_ACCF32><<<grid, block, 0, s>>>(a, tm, tn);
             break;
         case EPI_F32_RESID:
-            if constexpr (K64) gemm_nt64_k<BM, BN, WM, WN, EPI_F32_RESID><<<grid, block, 0, s>>>(a, tm, tn);
+            if constexpr (K64) gemm_nt64_k<BM, BN, WM, WN, EPI_F32_RESID><<<grid, block, 0, s>>>(a, tm, tn, sp);
             else gemm_nt_k<BM, BN, WM, WN, EPI_F32_RESID><<<grid, block, 0, s>>>(a, tm, tn);
             break;
         case EPI_BF16_RESID32:
-            if constexpr (K64) gemm_nt64_k<BM, BN, WM, WN, EPI_BF16_RESID32><<<grid, block, 0, s>>>(a, tm, tn);
+            if constexpr (K64) gemm_nt64_k<BM, BN, WM, WN, EPI_BF16_RESID32><<<grid, block, 0, s>>>(a, tm, tn, sp);
             else gemm_nt_k<BM, BN, WM, WN, EPI_BF16_RESID32><<<grid, block, 0, s>>>(a, tm, tn);
             break;
         case EPI_F32_F16IN:
-            if constexpr (K64) gemm_nt64_k<BM, BN, WM, WN, EPI_F32_F16IN><<<grid, block, 0, s>>>(a, tm, tn);
+            if constexpr (K64) gemm_nt64_k<BM, BN, WM, WN, EPI_F32_F16IN><<<grid, block, 0, s>>>(a, tm, tn, sp);
             else gemm_nt_k<BM, BN, WM, WN, EPI_F32_F16IN><<<grid, block, 0, s>>>(a, tm, tn);
             break;
         case EPI_F32_F16IN_RESID:
-            if constexpr (K64) gemm_nt64_k<BM, BN, WM, WN, EPI_F32_F16IN_RESID><<<grid, block, 0, s>>>(a, tm, tn);
+            if constexpr (K64) gemm_nt64_k<BM, BN, WM, WN, EPI_F32_F16IN_RESID><<<grid, block, 0, s>>>(a, tm, tn, sp);
             else gemm_nt_k<BM, BN, WM, WN, EPI_F32_F16IN_RESID><<<grid, block, 0, s>>>(a, tm, tn);
             break;
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || sp.splits <= 1) return e;
+    return launch_fixup(epi, a, tm, tn, sp, s);
 }
 
 // The k-major forms (NN: B k-major; TN: both), 256 x 256 tiles only, with
@@ -840,25 +945,34 @@ template <bool TA, bool TB>
 hipError_t launch_kmajor(GemmEpi epi, const GemmArgs& a, hipStream_t s) {
     constexpr int WM = MT_NT_WM, WN = MT_NT_NW / MT_NT_WM;
     const int tm = (a.M + 255) / 256, tn = (a.N + 255) / 256;
-    const dim3 grid(tm * tn), block(WM * WN * 64);
-    if (a.b_f16) {
-        if constexpr (TA && TB) {
-            if (epi != EPI_BF16) return hipErrorNotSupported;
-            gemm_nt64_k<256, 256, WM, WN, EPI_BF16, true, true, true><<<grid, block, 0, s>>>(a, tm, tn);
-            return hipGetLastError();
-        }
+    const dim3 block(WM * WN * 64);
+    if (a.b_f16 && !(TA && TB && epi == EPI_BF16)) return hipErrorNotSupported;
+    if (epi != EPI_BF16 && epi != EPI_F32 && epi != EPI_F32_ACC && epi != EPI_BF16_ACCF32)
         return hipErrorNotSupported;
+    GemmSplit sp;
+    {
+        const hipError_t e = split_for(a, tm, tn, sp);
+        if (e != hipSuccess) return e;
     }
-    switch (epi) {
-        case EPI_BF16: gemm_nt64_k<256, 256, WM, WN, EPI_BF16, TA, TB><<<grid, block, 0, s>>>(a, tm, tn); break;
-        case EPI_F32: gemm_nt64_k<256, 256, WM, WN, EPI_F32, TA, TB><<<grid, block, 0, s>>>(a, tm, tn); break;
-        case EPI_F32_ACC: gemm_nt64_k<256, 256, WM, WN, EPI_F32_ACC, TA, TB><<<grid, block, 0, s>>>(a, tm, tn); break;
-        case EPI_BF16_ACCF32:
-            gemm_nt64_k<256, 256, WM, WN, EPI_BF16_ACCF32, TA, TB><<<grid, block, 0, s>>>(a, tm, tn);
-            break;
-        default: return hipErrorNotSupported;
+    const dim3 grid = split_grid(tm, tn, sp);
+    if (a.b_f16) {
+        if constexpr (TA && TB)
+            gemm_nt64_k<256, 256, WM, WN, EPI_BF16, true, true, true><<<grid, block, 0, s>>>(a, tm, tn, sp);
+    } else {
+        switch (epi) {
+            case EPI_BF16: gemm_nt64_k<256, 256, WM, WN, EPI_BF16, TA, TB><<<grid, block, 0, s>>>(a, tm, tn, sp); break;
+            case EPI_F32: gemm_nt64_k<256, 256, WM, WN, EPI_F32, TA, TB><<<grid, block, 0, s>>>(a, tm, tn, sp); break;
+            case EPI_F32_ACC:
+                gemm_nt64_k<256, 256, WM, WN, EPI_F32_ACC, TA, TB><<<grid, block, 0, s>>>(a, tm, tn, sp);
+                break;
+            default:
+                gemm_nt64_k<256, 256, WM, WN, EPI_BF16_ACCF32, TA, TB><<<grid, block, 0, s>>>(a, tm, tn, sp);
+                break;
+        }
     }
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || sp.splits <= 1) return e;
+    return launch_fixup(epi, a, tm, tn, sp, s);
 }
 
 inline bool al16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; }
@@ -887,6 +1001,41 @@ hipError_t gemm_direct(GemmLayout lay, GemmEpi epi, const GemmArgs& a, hipStream
     }
     if (!MT_GEMM_KMAJOR || !MT_NT_K64 || big_tiles < MT_NT_BIG_MIN) return hipErrorNotSupported;
     return ta ? launch_kmajor<true, true>(epi, a, s) : launch_kmajor<false, true>(epi, a, s);
+}
+
+// Cost model of the tail split, in units of one 64-deep k-step of a 256 x 256
+// tile on a busy CU (~1.8 us at the clock the chip holds under dense MFMA
+// load).  The first full rounds of tiles run whole; the last, partial round
+// of r < 256 tiles leaves CUs idle for as long as one tile takes.  Cut into s
+// k-ranges, its r * s blocks run in ceil(r * s / 256) rounds of ceil(nk / s)
+// steps, each block also storing its 256 KB fp32 partial (~3 steps); a second
+// kernel then reads the partials back and writes the output (~4 TB/s, plus
+// ~6 steps of launch).  The split with the lowest predicted time is taken if
+// it saves at least 5%; ties go to fewer splits (less scratch traffic).
+GemmSplit gemm_split_plan(int64_t M, int64_t N, int64_t K, uint64_t ws_bytes) {
+    const int64_t tm = (M + 255) / 256, tn = (N + 255) / 256, total = tm * tn;
+    const int64_t nk = (K + 63) / 64;
+    GemmSplit best{int(total), 1, int(nk)};
+    const int64_t r = total % 256, n_full = total - r, R = n_full / 256;
+    if (r == 0 || total >= (int64_t(1) << 30)) return best;
+    constexpr double TAU_S = 1.8e-6, FIX_BPS = 4.0e12, FIX_LAUNCH = 6.0, STORE = 3.0;
+    const double base = double((total + 255) / 256) * double(nk);
+    double best_t = 0.95 * base;
+    for (int64_t s = 2; s <= 16; ++s) {
+        const int64_t kper = (nk + s - 1) / s;
+        const int64_t se = (nk + kper - 1) / kper;
+        if (kper < 4 || se != s) continue;
+        const int64_t units = r * s;
+        if (uint64_t(units) * 65536u * 4u > ws_bytes) continue;
+        const double fix_bytes = double(units) * 262144.0 + double(r) * 262144.0;
+        const double t = double(R) * double(nk) + double((units + 255) / 256) * (double(kper) + STORE) +
+                         fix_bytes / FIX_BPS / TAU_S + FIX_LAUNCH;
+        if (t < best_t) {
+            best_t = t;
+            best = GemmSplit{int(n_full), int(s), int(kper)};
+        }
+    }
+    return best;
 }
 
 }  // namespace mt

@@ -34,7 +34,22 @@ struct GemmArgs {
     const float* Cacc; int64_t ldacc; // fp32 partial sum, EPI_BF16_ACCF32
     int M, N, K;
     bool b_f16 = false;               // B holds fp16, rounded to bf16 as it is read (TN, EPI_BF16, direct form only)
+    // Device scratch for the K-split of the last partial round of 256 x 256
+    // tiles (fp32 partial tiles, 256 KB each); null: no split.  Used only by
+    // the direct form; must not overlap A, B, C, R or Cacc.
+    float* ws = nullptr;
+    uint64_t ws_bytes = 0;
+    int force_splits = 0;             // > 0: split the tail this many ways (tests); 0: gemm_split_plan decides
 };
+// How a direct-form product on 256 x 256 tiles is cut: the first n_full tiles
+// run whole; each later tile runs as `splits` blocks over consecutive ranges
+// of kper 64-deep k-steps, whose fp32 partials a second kernel adds in split
+// order before the epilogue (deterministic for a given shape).
+struct GemmSplit { int n_full; int splits; int kper; };
+// The split the direct form takes for an M x N x K product given ws_bytes of
+// scratch: splits = 1 unless cutting the last partial round of tiles is
+// predicted to save at least 5% (cost model in gemm_nt.hip).
+GemmSplit gemm_split_plan(int64_t M, int64_t N, int64_t K, uint64_t ws_bytes);
 hipError_t gemm(GemmLayout lay, GemmEpi epi, const GemmArgs& a, hipStream_t s);
 // The path with direct global->LDS tile loads (called by gemm() after its
 // checks): every NT product, and NN / TN products on grids of at least

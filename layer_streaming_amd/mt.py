@@ -95,6 +95,9 @@ _SIGS = {
     # test entries
     "mt_k_gemm": (C.c_int, [C.c_int32, C.c_int32, _P, C.c_int64, _P, C.c_int64, _P, C.c_int64, _P, C.c_int64,
                             _P, C.c_int64, C.c_int32, C.c_int32, C.c_int32, _P]),
+    "mt_k_gemm_split": (C.c_int, [C.c_int32, C.c_int32, _P, C.c_int64, _P, C.c_int64, _P, C.c_int64, _P, C.c_int64,
+                                  _P, C.c_int64, C.c_int32, C.c_int32, C.c_int32, _P, C.c_int64, C.c_int32, _P]),
+    "mt_k_gemm_split_plan": (C.c_int, [C.c_int64, C.c_int64, C.c_int64, C.c_int64, _P, _P, _P]),
     "mt_k_rmsnorm_fwd": (C.c_int, [_P, C.c_int32, _P, _P, _P, _P, C.c_int32, C.c_int32, C.c_float, _P, _P]),
     "mt_k_rmsnorm_bwd_scratch_elems": (C.c_int64, [C.c_int32, C.c_int32]),
     "mt_k_rmsnorm_bwd": (C.c_int, [_P, _P, C.c_int32, _P, _P, _P, _P, _P, _P, C.c_int32, C.c_int32, _P]),

@@ -313,6 +313,136 @@ def test_gemm_f16_operands(M, N, K):
                             M, N, K, _stream()) == mt.MT_E_INVAL  # no residual
 
 
+# The tail split: the tiles of the last, partial round of 256 x 256 tiles run
+# as several blocks over consecutive K ranges whose fp32 partials a second
+# kernel adds in split order before the epilogue.  Forced split counts, on
+# grids with whole rounds before the tail (306 and 272 tiles: 256 whole) and
+# without (156 tiles: every tile split), ragged M, N and K (a last k-range
+# shorter than the others), every layout.  Checked element by element against
+# the float64 product, bit for bit against itself (deterministic), and bit for
+# bit against the unsplit product outside the tail tiles.
+def _tile_coords(pid, tiles_m, tiles_n, group=8):
+    per_group = group * tiles_n
+    first_m = (pid // per_group) * group
+    gsz = min(tiles_m - first_m, group)
+    return first_m + (pid % per_group) % gsz, (pid % per_group) // gsz
+
+
+def _tail_mask(M, N, n_full):
+    tm, tn = (M + 255) // 256, (N + 255) // 256
+    mask = np.zeros((M, N), bool)
+    for pid in range(n_full, tm * tn):
+        i, j = _tile_coords(pid, tm, tn)
+        mask[i * 256:(i + 1) * 256, j * 256:(j + 1) * 256] = True
+    return mask
+
+
+SPLIT_CASES = [(0, 4104, 4360, 520, 3), (0, 3080, 3000, 1000, 2), (1, 4104, 4360, 1000, 5), (2, 4104, 4040, 997, 4),
+               (2, 3584, 3584, 1032, 7), (1, 4104, 4360, 200, 16)]
+
+
+@pytest.mark.parametrize("layout,M,N,K,splits", SPLIT_CASES)
+def test_gemm_tail_split(layout, M, N, K, splits):
+    log(f"gemm tail split layout={layout} M={M} N={N} K={K} splits={splits}")
+    a_shape = (M, K) if layout in (0, 1) else (K, M)
+    b_shape = (N, K) if layout == 0 else (K, N)
+    A = synth.bf16_exact_normal(RNG, a_shape)
+    B = synth.bf16_exact_normal(RNG, b_shape)
+    opA = A if layout in (0, 1) else A.T
+    opB = B.T if layout == 0 else B
+    ref = opA.astype(np.float64) @ opB.astype(np.float64)
+    dA, dB = dev_bits(A), dev_bits(B)
+    tiles = ((M + 255) // 256) * ((N + 255) // 256)
+    n_full = (tiles // 256) * 256
+    nk = (K + 63) // 64
+    kper = -(-nk // splits)
+    eff = -(-nk // kper)
+    ws = torch.empty((tiles - n_full) * eff * 65536, dtype=torch.float32, device="cuda")
+
+    def run(sp):
+        dC = dev_zeros_bits((M, N))
+        mt.check(mt.lib.mt_k_gemm_split(layout, 0, dA.data_ptr(), a_shape[1], dB.data_ptr(), b_shape[1],
+                                        dC.data_ptr(), N, None, 0, None, 0, M, N, K, ws.data_ptr(),
+                                        ws.numel() * 4, sp, _stream()), "gemm_split")
+        _sync()
+        return dC.cpu().numpy()
+
+    got = run(splits)
+    again = run(splits)
+    plain = run(1)
+    gotf = widen(got.view(np.uint16))
+    assert_close(gotf, ref, "C split")
+    _elementwise_check(gotf, ref, np.ascontiguousarray(opA), np.ascontiguousarray(opB.T), "C split", K)
+    assert np.array_equal(got, again), "split product not deterministic"
+    outside = ~_tail_mask(M, N, n_full)
+    assert np.array_equal(got[outside], plain[outside]), "whole tiles changed by the split"
+    assert not np.array_equal(got, plain), "split not taken"
+
+
+def test_gemm_tail_split_epilogues():
+    """The fixup kernel's epilogues: fp32 out and accumulate, bf16 from an fp32
+    partial, the residual forms of the forward products, fp16 operands."""
+    M, N, K = 4104, 4040, 600
+    ldc = N + 12
+    log(f"gemm tail split epilogues M={M} N={N} K={K}")
+    A = synth.bf16_exact_normal(RNG, (M, K))
+    B = synth.bf16_exact_normal(RNG, (N, K))
+    R = synth.bf16_exact_normal(RNG, (M, ldc))
+    ref = A.astype(np.float64) @ B.astype(np.float64).T
+    Rv = R[:, :N].astype(np.float64)
+    dA, dB, dR = dev_bits(A), dev_bits(B), dev_bits(R)
+    ws = torch.empty(16 * 3 * 65536, dtype=torch.float32, device="cuda")
+    s = _stream()
+
+    def run(epi, C, Rp=None, ldr=0, acc=None, a=dA, b=dB):
+        mt.check(mt.lib.mt_k_gemm_split(0, epi, a.data_ptr(), K, b.data_ptr(), K, C.data_ptr(), ldc, Rp, ldr, acc,
+                                        ldc if acc else 0, M, N, K, ws.data_ptr(), ws.numel() * 4, 3, s),
+                 f"gemm split epi {epi}")
+        _sync()
+
+    dC = dev_zeros_bits((M, ldc))
+    run(1, dC, dR.data_ptr(), ldc)
+    assert_close(host_f32(dC)[:, :N], ref + Rv, "C+R")
+    assert np.all(host_f32(dC)[:, N:] == 0), "columns past N written"
+    c32 = torch.zeros((M, ldc), dtype=torch.float32, device="cuda")
+    run(2, c32)
+    got32 = c32.cpu().numpy()[:, :N]
+    assert_close(got32, ref, "C f32", tol=1e-5)
+    _elementwise_check(got32, ref, A, B, "C f32", K)
+    run(3, c32)
+    assert_close(c32.cpu().numpy()[:, :N], 2 * ref, "C f32 += ", tol=1e-5)
+    dC2 = dev_zeros_bits((M, ldc))
+    run(4, dC2, acc=c32.data_ptr())
+    assert_close(host_f32(dC2)[:, :N], 3 * ref, "C bf16 from f32 partial")
+    h32 = torch.zeros((M, ldc), dtype=torch.float32, device="cuda")
+    run(5, h32, dR.data_ptr(), ldc)
+    assert_close(h32.cpu().numpy()[:, :N], ref + Rv, "C f32 = acc + R bf16", tol=1e-5)
+    dC3 = dev_zeros_bits((M, ldc))
+    run(6, dC3, h32.data_ptr(), ldc)
+    assert_close(host_f32(dC3)[:, :N], 2 * ref + Rv, "C bf16 = acc + R f32")
+    A16 = RNG.standard_normal((M, K)).astype(np.float16)
+    B16 = (0.02 * RNG.standard_normal((N, K))).astype(np.float16)
+    dA16, dB16 = dev_f16(A16), dev_f16(B16)
+    ref16 = A16.astype(np.float64) @ B16.astype(np.float64).T
+    c16 = torch.zeros((M, ldc), dtype=torch.float32, device="cuda")
+    run(7, c16, a=dA16, b=dB16)
+    assert_close(c16.cpu().numpy()[:, :N], ref16, "C f16 operands", tol=1e-5)
+    c16r = torch.zeros((M, ldc), dtype=torch.float32, device="cuda")
+    run(8, c16r, dR.data_ptr(), ldc, a=dA16, b=dB16)
+    assert_close(c16r.cpu().numpy()[:, :N], ref16 + Rv, "C f16 operands + R", tol=1e-5)
+
+
+def test_gemm_tail_split_refuses_small_scratch():
+    M, N, K = 3080, 3000, 1000
+    dA = dev_zeros_bits((M, K))
+    dB = dev_zeros_bits((N, K))
+    dC = dev_zeros_bits((M, N))
+    ws = torch.empty(65536, dtype=torch.float32, device="cuda")
+    rc = mt.lib.mt_k_gemm_split(0, 0, dA.data_ptr(), K, dB.data_ptr(), K, dC.data_ptr(), N, None, 0, None, 0,
+                                M, N, K, ws.data_ptr(), ws.numel() * 4, 2, _stream())
+    assert rc == mt.MT_E_INVAL
+
+
 # --------------------------------------------------------------- RMSNorm --
 @pytest.mark.parametrize("T,d,x_f32", [(37, 256, 0), (130, 3584, 0), (9, 8192, 0), (1, 64, 0), (130, 3584, 1),
                                        (21, 256, 1)])

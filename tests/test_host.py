@@ -358,3 +358,38 @@ def test_attention_backward_work_covers_the_automatic_split():
         want = al(2 * T * Hq * 4) + al(T * Hq * hd * 2) + 8192 + al(part * 4) + al(ds)
         assert mt.lib.mt_k_attn_bwd_work_bytes(B, S, Hq, Hkv, hd) == want, (B, S, Hq)
     assert mt.lib.mt_k_attn_bwd_work_bytes(1, 100, 6, 4, 128) == 0   # not a grouping
+
+
+def _split_plan(M, N, K, ws):
+    nf, sp, kp = C.c_int32(), C.c_int32(), C.c_int32()
+    assert mt.lib.mt_k_gemm_split_plan(M, N, K, ws, C.byref(nf), C.byref(sp), C.byref(kp)) == mt.MT_OK
+    return nf.value, sp.value, kp.value
+
+
+def test_gemm_tail_split_plan():
+    """The tail split the direct-form GEMM takes: only a partial last round of
+    256 x 256 tiles is cut, every K range is non-empty, the partials fit the
+    scratch, and at the 7B layer shapes (T = 8192) the long-K products with a
+    partial round split while the gate|up forward product (18.5 rounds of short
+    K) and grids of whole rounds do not."""
+    T, d, F, nqkv = 8192, 3584, 18944, 4608
+    ws = 620 << 20
+    shapes = {"qkv": (T, nqkv, d), "o": (T, d, d), "gateup": (T, 2 * F, d), "down": (T, d, F),
+              "down_dx": (T, F, d), "down_dw": (d, F, T), "gateup_dx": (T, d, 2 * F), "gateup_dw": (2 * F, d, T),
+              "o_dw": (d, d, T), "qkv_dw": (nqkv, d, T), "whole_rounds": (8192, 8192, 8192)}
+    plans = {k: _split_plan(*v, ws) for k, v in shapes.items()}
+    for name, (M, N, K) in shapes.items():
+        n_full, splits, kper = plans[name]
+        tiles = -(-M // 256) * -(-N // 256)
+        nk = -(-K // 64)
+        if splits == 1:
+            assert n_full == tiles and kper == nk, name
+            continue
+        assert n_full == tiles - tiles % 256 and tiles % 256, name
+        assert (splits - 1) * kper < nk <= splits * kper, name
+        assert (tiles - n_full) * splits * 256 * 1024 <= ws, name
+    assert plans["gateup"][1] == 1 and plans["whole_rounds"][1] == 1 and plans["o_dw"][1] == 1
+    assert plans["gateup_dx"][1] > 1 and plans["gateup_dw"][1] > 1 and plans["down_dw"][1] > 1
+    # no scratch, no split; scratch too small for any split, no split
+    assert _split_plan(T, d, 2 * F, 0)[1] == 1
+    assert _split_plan(T, d, 2 * F, 1 << 20)[1] == 1
