@@ -242,6 +242,8 @@ def attention_probe(torch, mt, cfg, S, B=1, dq_form=0):
     work = torch.zeros(int(mt.lib.mt_k_attn_bwd_work_bytes(B, S, Hq, Hkv, hd)), dtype=torch.uint8, device="cuda")
     dqkv = torch.zeros(T, ld, dtype=torch.int16, device="cuda")
     dqk32 = torch.zeros(T, ld, dtype=torch.float32, device="cuda")
+    tab = torch.zeros(S * hd, dtype=torch.float32, device="cuda")
+    base = [10000.0]   # the first call computes the RoPE table, later ones reuse it
     st = torch.cuda.current_stream()
     s = st.cuda_stream
 
@@ -249,11 +251,12 @@ def attention_probe(torch, mt, cfg, S, B=1, dq_form=0):
         mt.check(mt.lib.mt_k_attn_fwd(qkv.data_ptr(), ld, o.data_ptr(), nq, lse.data_ptr(), B, S, Hq, Hkv, hd, None, s),
                  "attn_fwd")
 
-    def bwd():  # as the step runs it: dQ, dK in fp32
-        mt.check(mt.lib.mt_k_attn_bwd(qkv.data_ptr(), ld, o.data_ptr(), do.data_ptr(), nq, lse.data_ptr(),
-                                      work.data_ptr(), dqkv.data_ptr(), ld, B, S, Hq, Hkv, hd, dqk32.data_ptr(), ld,
-                                      0, dq_form, None, s),
+    def bwd():  # as the step runs it: dQ rotated back in the dQ kernel (bf16), dK in fp32
+        mt.check(mt.lib.mt_k_attn_bwd_rope(qkv.data_ptr(), ld, o.data_ptr(), do.data_ptr(), nq, lse.data_ptr(),
+                                           work.data_ptr(), dqkv.data_ptr(), ld, B, S, Hq, Hkv, hd, dqk32.data_ptr(),
+                                           ld, 0, dq_form, None, tab.data_ptr(), base[0], s),
                  "attn_bwd")
+        base[0] = 0.0
     fl = 4.0 * B * Hq * hd * S * (S + 1) / 2
     out = {}
     for name, fn, f in (("fwd", fwd, fl), ("bwd", bwd, 2.5 * fl)):

@@ -147,6 +147,18 @@ int32_t mt_k_attn_dkdv_splits(int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int
 int mt_k_attn_bwd(const void* qkv, int64_t ld, const void* o, const void* dout, int64_t ldo, const void* lse,
                   void* work, void* dqkv, int64_t ldd, int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t hd,
                   void* dqk32, int64_t ld32, int32_t head_splits, int32_t dq_form, void* fp16_ovf, void* stream);
+/* mt_k_attn_bwd with the RoPE backward folded in (the form the step runs):
+ * dQ and dK are rotated by -theta where they are finished (the dQ kernel,
+ * the dK/dV kernel or its split reduction) and go to dqkv's query and key
+ * columns in bf16, rounded once after the rotation; dV as before; dqk32 is
+ * not written (may be NULL).  The rotation uses mt_k_rope's angles
+ * (positions restart every S tokens), its table ([S x hd/2] float2) computed
+ * into `table` for base > 0, or taken as a previous call left it for
+ * base = 0. */
+int mt_k_attn_bwd_rope(const void* qkv, int64_t ld, const void* o, const void* dout, int64_t ldo, const void* lse,
+                       void* work, void* dqkv, int64_t ldd, int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t hd,
+                       void* dqk32, int64_t ld32, int32_t head_splits, int32_t dq_form, void* fp16_ovf, void* table,
+                       float base, void* stream);
 /* Rotary embedding of the first n_rot_heads heads of fp32 in [T x ldin]
  * (same angles and table as mt_k_rope; dir -1 rotates by -theta, the
  * backward), written as bf16 to out [T x ldout] with one rounding. */

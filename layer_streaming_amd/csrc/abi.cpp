@@ -190,6 +190,31 @@ int mt_k_attn_bwd(const void* qkv, int64_t ld, const void* o, const void* dout, 
     return kst(mt::attn_bwd(a, S_(stream)), "attn_bwd");
 }
 
+int mt_k_attn_bwd_rope(const void* qkv, int64_t ld, const void* o, const void* dout, int64_t ldo, const void* lse,
+                       void* work, void* dqkv, int64_t ldd, int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t hd,
+                       void* dqk32, int64_t ld32, int32_t head_splits, int32_t dq_form, void* fp16_ovf, void* table,
+                       float base, void* stream) {
+    if (!table || (reinterpret_cast<uintptr_t>(table) & 15)) MT_FAIL(MT_E_INVAL, "attn_bwd_rope: bad table");
+    if (!work || (reinterpret_cast<uintptr_t>(work) & 255)) MT_FAIL(MT_E_INVAL, "attn_bwd: work must be 256-byte aligned");
+    if (head_splits < 0) MT_FAIL(MT_E_INVAL, "attn_bwd: head_splits must be >= 0");
+    if (dq_form < 0 || dq_form > 2) MT_FAIL(MT_E_INVAL, "attn_bwd: dq_form must be 0, 1 or 2");
+    if (dq_form == 2 && mt::attn_ds_bytes(B, S, Hq) == 0)
+        MT_FAIL(MT_E_INVAL, "attn_bwd: this shape does not take the stored-dS form of dQ");
+    if (B <= 0 || S <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || (hd != 64 && hd != 128))
+        MT_FAIL(MT_E_INVAL, "attn_bwd_rope: bad shape");
+    if (base < 0.f) MT_FAIL(MT_E_INVAL, "attn_bwd_rope: base must be > 0, or 0 for a table computed before");
+    if (base > 0.f) {
+        const hipError_t e = mt::rope_table(static_cast<float2*>(table), S, hd, base, S_(stream));
+        if (e != hipSuccess) return kst(e, "rope_table");
+    }
+    mt::AttnBwdArgs a{U16(qkv), ld, U16(o), U16(dout), ldo, F32(lse), nullptr, nullptr, nullptr, U16(dqkv), ldd,
+                      B, S, Hq, Hkv, hd, F32(dqk32), ld32, static_cast<uint32_t*>(fp16_ovf)};
+    a.splits = head_splits;
+    a.rope_tab = static_cast<const float2*>(table);
+    mt::attn_bwd_carve(work, B, S, Hq, Hkv, hd, a, dq_form != 1);
+    return kst(mt::attn_bwd(a, S_(stream)), "attn_bwd_rope");
+}
+
 int mt_k_rope_f32_bf16(const void* in, int64_t ldin, void* out, int64_t ldout, void* table, int32_t T, int32_t S,
                        int32_t n_rot_heads, int32_t hd, float base, int32_t dir, void* stream) {
     hipError_t e = mt::rope_table(static_cast<float2*>(table), S, hd, base, S_(stream));

@@ -354,6 +354,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_k(AttnArgs a, int n_qt, int q
 // measured: 20 us for 1152 blocks).  The reads here are uniform, so they are
 // scalar loads.
 constexpr int AMAX_W = 16, AMAX_LINE = 64;  // partial maxima per quantity; words per line
+constexpr int AMAX_U = 8;                    // 16-byte loads in flight per lane of the maxima kernel
 static_assert(2 * AMAX_W * AMAX_LINE * 4 == ATTN_AMAX_BYTES, "maxima scratch size");
 __device__ __forceinline__ float grad_scale(const uint32_t* amax, int hd) {
     uint32_t ab = 0, vb = 0;
@@ -374,9 +375,10 @@ __device__ __forceinline__ float grad_scale(const uint32_t* amax, int hd) {
 
 // max |dO| over [T x Hq*hd] (row stride ldo) and max |v| over the value
 // heads of qkv into the partial maxima of amax (zeroed first): the first
-// nb_do blocks stride over dO, the rest over v, four 16-byte loads in flight
-// per lane; one atomic max per block, block i into partial i % AMAX_W of
-// its maximum.  Indices are 32-bit (the host checks T*Hq*hd/8 < 2^31).
+// nb_do blocks stride over dO, the rest over v, AMAX_U 16-byte loads in
+// flight per lane (all issued before the first is used); one atomic max per
+// block, block i into partial i % AMAX_W of its maximum.  Indices are 32-bit
+// (the host checks T*Hq*hd/8 < 2^31).
 template <int HD>
 __global__ __launch_bounds__(256) void attn_amax_k(AttnBwdArgs a, int nb_do) {
     __shared__ float red[4];
@@ -400,15 +402,16 @@ __global__ __launch_bounds__(256) void attn_amax_k(AttnBwdArgs a, int nb_do) {
         for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(f[e]));
     };
     float mx = 0.f;
-    uint32_t i = bi * 256 + threadIdx.x;
-    for (; n > 3 * stride && i < n - 3 * stride; i += 4 * stride) {
-        const uint4 v0 = chunk(i), v1 = chunk(i + stride), v2 = chunk(i + 2 * stride), v3 = chunk(i + 3 * stride);
-        fold(v0, mx);
-        fold(v1, mx);
-        fold(v2, mx);
-        fold(v3, mx);
+    for (uint32_t i0 = bi * 256 + threadIdx.x; i0 < n; i0 += AMAX_U * stride) {
+        uint4 v[AMAX_U];
+#pragma unroll
+        for (int u = 0; u < AMAX_U; ++u) {
+            const uint32_t i = i0 + u * stride;
+            v[u] = i < n ? chunk(i) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < AMAX_U; ++u) fold(v[u], mx);
     }
-    for (; i < n; i += stride) fold(chunk(i), mx);
     mx = wave_max(mx);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
     __syncthreads();
@@ -469,6 +472,77 @@ __device__ __forceinline__ void store_grad4(float* f32row, uint16_t* b16row, int
                                             float x3) {
     if (f32row) *reinterpret_cast<float4*>(f32row + d) = make_float4(x0, x1, x2, x3);
     else *reinterpret_cast<uint2*>(b16row + d) = make_uint2(pack2(x0, x1), pack2(x2, x3));
+}
+
+// The (cos, sin) pairs a lane's dQ columns rotate with at sequence position
+// pos: pairs e = 32 dt + 8 g + 4 hh + 0..3 for dt < ND/2, two float4 (four
+// pairs) per (dt, g).  Zero without a table.
+template <int HD>
+__device__ __forceinline__ void load_rope_row(const AttnBwdArgs& a, int pos, int hh, float4 (&cs)[HD / 8]) {
+    constexpr int ND = HD / 32;
+    if (!a.rope_tab) {
+#pragma unroll
+        for (int i = 0; i < HD / 8; ++i) cs[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        return;
+    }
+    const float4* tr = reinterpret_cast<const float4*>(a.rope_tab + int64_t(pos) * (HD / 2));
+#pragma unroll
+    for (int dt = 0; dt < ND / 2; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int e = 32 * dt + 8 * g + 4 * hh;
+            cs[2 * (4 * dt + g)] = tr[e / 2];
+            cs[2 * (4 * dt + g) + 1] = tr[e / 2 + 1];
+        }
+}
+
+// One row's gradient as a lane of the dQ and dK/dV kernels holds it
+// (columns 32 dt + 8 g + 4 hh + 0..3, acc scaled by `scale`), rotated by
+// -theta with the pairs load_rope_row gave (e and e + HD/2 sit in the same
+// lane, blocks dt and dt + ND/2) and rounded to bf16 once into r16.  The
+// rotation is the transpose of the forward's: lo' = lo cos + hi sin,
+// hi' = hi cos - lo sin.
+template <int HD>
+__device__ __forceinline__ void store_rot_bf16(uint16_t* r16, const f32x16_t (&acc)[HD / 32], float scale, int hh,
+                                               const float4 (&cs)[HD / 8]) {
+    constexpr int ND = HD / 32;
+#pragma unroll
+    for (int dt = 0; dt < ND / 2; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int e = 32 * dt + 8 * g + 4 * hh;
+            const float4 c0 = cs[2 * (4 * dt + g)], c1 = cs[2 * (4 * dt + g) + 1];
+            const float cv[4] = {c0.x, c0.z, c1.x, c1.z}, sv[4] = {c0.y, c0.w, c1.y, c1.w};
+            float ol[4], oh[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float lo = acc[dt][4 * g + j] * scale, hi = acc[dt + ND / 2][4 * g + j] * scale;
+                ol[j] = lo * cv[j] + hi * sv[j];
+                oh[j] = hi * cv[j] - lo * sv[j];
+            }
+            *reinterpret_cast<uint2*>(r16 + e) = make_uint2(pack2(ol[0], ol[1]), pack2(ol[2], ol[3]));
+            *reinterpret_cast<uint2*>(r16 + e + HD / 2) = make_uint2(pack2(oh[0], oh[1]), pack2(oh[2], oh[3]));
+        }
+}
+
+// dQ of one query row: rotated and rounded once with a.rope_tab, else
+// stored as store_grad4 does (fp32 into dqk32 when set, else bf16).
+template <int HD>
+__device__ __forceinline__ void store_dq_row(const AttnBwdArgs& a, const f32x16_t (&acc)[HD / 32], float scale,
+                                             int64_t row, int h, int hh, const float4 (&cs)[HD / 8]) {
+    constexpr int ND = HD / 32;
+    uint16_t* r16 = a.dqkv + row * a.ldd + h * HD;
+    if (a.rope_tab) {
+        store_rot_bf16<HD>(r16, acc, scale, hh, cs);
+        return;
+    }
+    float* r32 = a.dqk32 ? a.dqk32 + row * a.ld32 + h * HD : nullptr;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            store_grad4(r32, r16, 32 * dt + 8 * g + 4 * hh, acc[dt][4 * g] * scale, acc[dt][4 * g + 1] * scale,
+                        acc[dt][4 * g + 2] * scale, acc[dt][4 * g + 3] * scale);
 }
 
 // dQ: block = 4 waves x 32 queries of one (b, h); key tiles of 64 staged as
@@ -606,16 +680,9 @@ __global__ __launch_bounds__(256, 2) void attn_dq_k(AttnBwdArgs a, int n_qt, int
         barrier_tile();
     }
     if (q < S) {
-        const float scale = rsqrtf(float(HD)) / s2k;
-        const int64_t row = int64_t(b) * S + q;
-        float* r32 = a.dqk32 ? a.dqk32 + row * a.ld32 + h * HD : nullptr;
-        uint16_t* r16 = a.dqkv + row * a.ldd + h * HD;
-#pragma unroll
-        for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                store_grad4(r32, r16, 32 * dt + 8 * g + 4 * hh, acc[dt][4 * g] * scale, acc[dt][4 * g + 1] * scale,
-                            acc[dt][4 * g + 2] * scale, acc[dt][4 * g + 3] * scale);
+        float4 cs[HD / 8];   // loaded here: this kernel has no registers to spare over its loop
+        load_rope_row<HD>(a, q, hh, cs);
+        store_dq_row<HD>(a, acc, rsqrtf(float(HD)) / s2k, int64_t(b) * S + q, h, hh, cs);
     }
 }
 
@@ -650,6 +717,11 @@ __global__ __launch_bounds__(256, 2) void attn_dq_ds_k(AttnBwdArgs a, int n_qt, 
     const int nb = int(a.ds_ld / 32);
     const uint16_t* dsbase = a.ds + (int64_t(b) * a.Hq + h) * nb * nb * 1024 + (q0 / 32) * 1024;
     const float s2k = grad_scale(a.amax, HD);
+    // the rotation's (cos, sin) pairs of the lane's output row (query of
+    // position c in the stored order), loaded now so they arrive during the loop
+    const int qs = qw + 8 * ((c >> 2) & 3) + 4 * (c >> 4) + (c & 3);
+    float4 cs[HD / 8];
+    load_rope_row<HD>(a, min(qs, S - 1), hh, cs);
 
     uint32_t koff[NI], soff[SNI];
     int srow[SNI];
@@ -702,20 +774,8 @@ __global__ __launch_bounds__(256, 2) void attn_dq_ds_k(AttnBwdArgs a, int n_qt, 
         }
         barrier_tile();
     }
-    // query of position c in the stored order: 8 (c / 4 % 4) + 4 (c / 16) + c % 4
-    const int qs = qw + 8 * ((c >> 2) & 3) + 4 * (c >> 4) + (c & 3);
-    if (qs < S) {
-        const float scale = rsqrtf(float(HD)) / s2k;
-        const int64_t row = int64_t(b) * S + qs;
-        float* r32 = a.dqk32 ? a.dqk32 + row * a.ld32 + h * HD : nullptr;
-        uint16_t* r16 = a.dqkv + row * a.ldd + h * HD;
-#pragma unroll
-        for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                store_grad4(r32, r16, 32 * dt + 8 * g + 4 * hh, acc[dt][4 * g] * scale, acc[dt][4 * g + 1] * scale,
-                            acc[dt][4 * g + 2] * scale, acc[dt][4 * g + 3] * scale);
-    }
+    // qs: the query of position c in the stored order, 8 (c / 4 % 4) + 4 (c / 16) + c % 4
+    if (qs < S) store_dq_row<HD>(a, acc, rsqrtf(float(HD)) / s2k, int64_t(b) * S + qs, h, hh, cs);
 }
 
 // dK, dV: block = 8 waves over 128 keys of one (b, kv head), looping over
@@ -975,16 +1035,27 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_k(AttnBwdArgs a, int n_kt, i
                                     acc_v[dt][4 * g + 3] * inv);
                 }
         } else {
-            float* r32 = a.dqk32 ? a.dqk32 + row * a.ld32 + (a.Hq + hk) * HD : nullptr;
             uint16_t* rk = a.dqkv + row * a.ldd + kcol;
             uint16_t* rv = a.dqkv + row * a.ldd + vcol;
+            if (a.rope_tab) {
+                float4 cs[HD / 8];
+                load_rope_row<HD>(a, key, hh, cs);
+                store_rot_bf16<HD>(rk, acc_k, scale, hh, cs);
+            } else {
+                float* r32 = a.dqk32 ? a.dqk32 + row * a.ld32 + (a.Hq + hk) * HD : nullptr;
+#pragma unroll
+                for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        store_grad4(r32, rk, 32 * dt + 8 * g + 4 * hh, acc_k[dt][4 * g] * scale,
+                                    acc_k[dt][4 * g + 1] * scale, acc_k[dt][4 * g + 2] * scale,
+                                    acc_k[dt][4 * g + 3] * scale);
+            }
 #pragma unroll
             for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int d = 32 * dt + 8 * g + 4 * hh;
-                    store_grad4(r32, rk, d, acc_k[dt][4 * g] * scale, acc_k[dt][4 * g + 1] * scale,
-                                acc_k[dt][4 * g + 2] * scale, acc_k[dt][4 * g + 3] * scale);
                     *reinterpret_cast<uint2*>(rv + d) =
                         make_uint2(pack2(acc_v[dt][4 * g] * inv, acc_v[dt][4 * g + 1] * inv),
                                    pack2(acc_v[dt][4 * g + 2] * inv, acc_v[dt][4 * g + 3] * inv));
@@ -1032,6 +1103,49 @@ __global__ __launch_bounds__(256) void attn_dkdv_reduce_k(AttnBwdArgs a, int ns)
     } else {
         const int col = (a.Hq + a.Hkv) * a.hd + int(j - w);
         *reinterpret_cast<uint2*>(a.dqkv + orow * a.ldd + col) = make_uint2(pack2(acc.x, acc.y), pack2(acc.z, acc.w));
+    }
+}
+
+// The same sum with dK rotated by -theta and rounded to bf16 once (a.rope_tab
+// set): one lane per four columns e..e+3 and their partners e+hd/2.. of one
+// head's dK or dV in one row, the first Hkv*hd/8 lanes of a row on dK, the
+// rest on dV.  Rotation as in store_rot_bf16.
+__global__ __launch_bounds__(256) void attn_dkdv_reduce_rot_k(AttnBwdArgs a, int ns) {
+    const uint32_t T = uint32_t(a.B) * uint32_t(a.S);
+    const uint32_t hd = uint32_t(a.hd), half = hd / 2, w = uint32_t(a.Hkv) * hd;
+    const uint32_t per_row = w / 4, gph = hd / 8;  // lanes per row; 4-column groups per head half
+    const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+    if (i >= T * per_row) return;
+    const uint32_t row = i / per_row, t = i - row * per_row;
+    const bool is_k = t < per_row / 2;
+    const uint32_t u = is_k ? t : t - per_row / 2;
+    const uint32_t hk = u / gph, e = (u - hk * gph) * 4;
+    const uint32_t c0 = hk * hd + e;  // column of the pair's first half within dK (or dV)
+    const float* src = a.dpart + int64_t(row) * (2 * w) + (is_k ? 0 : w) + c0;
+    const int64_t pstride = int64_t(T) * (2 * w);
+    float lo[4] = {0.f, 0.f, 0.f, 0.f}, hi[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < ns; ++p) {
+        const float4 x = *reinterpret_cast<const float4*>(src + p * pstride);
+        const float4 y = *reinterpret_cast<const float4*>(src + p * pstride + half);
+        lo[0] += x.x; lo[1] += x.y; lo[2] += x.z; lo[3] += x.w;
+        hi[0] += y.x; hi[1] += y.y; hi[2] += y.z; hi[3] += y.w;
+    }
+    uint16_t* dst = a.dqkv + int64_t(row) * a.ldd + (is_k ? a.Hq : a.Hq + a.Hkv) * a.hd + c0;
+    if (is_k) {
+        const float4* tr = reinterpret_cast<const float4*>(a.rope_tab + int64_t(row % uint32_t(a.S)) * half + e);
+        const float4 q0 = tr[0], q1 = tr[1];
+        const float cv[4] = {q0.x, q0.z, q1.x, q1.z}, sv[4] = {q0.y, q0.w, q1.y, q1.w};
+        float ol[4], oh[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            ol[j] = lo[j] * cv[j] + hi[j] * sv[j];
+            oh[j] = hi[j] * cv[j] - lo[j] * sv[j];
+        }
+        *reinterpret_cast<uint2*>(dst) = make_uint2(pack2(ol[0], ol[1]), pack2(ol[2], ol[3]));
+        *reinterpret_cast<uint2*>(dst + half) = make_uint2(pack2(oh[0], oh[1]), pack2(oh[2], oh[3]));
+    } else {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(pack2(lo[0], lo[1]), pack2(lo[2], lo[3]));
+        *reinterpret_cast<uint2*>(dst + half) = make_uint2(pack2(hi[0], hi[1]), pack2(hi[2], hi[3]));
     }
 }
 
@@ -1130,9 +1244,11 @@ hipError_t attn_bwd(const AttnBwdArgs& a, hipStream_t s) {
     const dim3 gq(unsigned(int64_t(n_qt) * a.B * a.Hq));
     const dim3 gk(static_cast<unsigned>(nk));
     const unsigned np = unsigned((T * a.Hq * (a.hd / 8) + 255) / 256);
-    // maxima: enough blocks to cover the chip, each striding over its part
-    const int nb_do = int(std::min<int64_t>(1024, (T * a.Hq * a.hd / 8 + 255) / 256));
-    const int nb_v = int(std::min<int64_t>(128, (T * a.Hkv * a.hd / 8 + 255) / 256));
+    // maxima: one pass of AMAX_U loads per lane where 2048 blocks (eight per
+    // CU) cover the tensors, else 2048 blocks striding over their parts
+    const int64_t ck_do = T * a.Hq * a.hd / 8, ck_v = T * a.Hkv * a.hd / 8, per_block = 256 * AMAX_U;
+    const int nb_v = int(std::min<int64_t>(256, (ck_v + per_block - 1) / per_block));
+    const int nb_do = int(std::min<int64_t>(2048 - nb_v, (ck_do + per_block - 1) / per_block));
     hipError_t e = fill_zero(a.amax, ATTN_AMAX_BYTES, s);
     if (e != hipSuccess) return e;
     // stored-dS form: dS must cover every key row and 128-query block
@@ -1150,7 +1266,8 @@ hipError_t attn_bwd(const AttnBwdArgs& a, hipStream_t s) {
     else run(std::integral_constant<int, 64>{});
     if (ns > 1) {
         const int64_t n4 = T * (a.Hkv * a.hd / 2);
-        attn_dkdv_reduce_k<<<unsigned((n4 + 255) / 256), 256, 0, s>>>(a, ns);
+        if (a.rope_tab) attn_dkdv_reduce_rot_k<<<unsigned((n4 / 2 + 255) / 256), 256, 0, s>>>(a, ns);
+        else attn_dkdv_reduce_k<<<unsigned((n4 + 255) / 256), 256, 0, s>>>(a, ns);
     }
     return hipGetLastError();
 }

@@ -1208,15 +1208,15 @@ hipError_t Ctx::bwd_layer(const LayerView& w, const LayerView& g, const uint16_t
     // o is fp16: rounded to bf16 for the bf16 product
     HIPR(site(S_GEMM_O_DW, [&] { return gemm_tn_t(ws.dh1, d, ws.oa[ob], nq, g.wo, nq, d, nq, T, true); }));
     // The attention backward on the fp16 operands of the recomputed forward:
-    // dV into dqkv, dQ and dK in fp32 into the projection buffer (free since
-    // the recompute's rotation read it), then rotated back by -theta and
-    // rounded to bf16 once.
+    // dV, and dQ and dK rotated back by -theta where they are finished,
+    // rounded to bf16 once into dqkv.
     HIPR(site(S_ATTN_BWD, [&] {
         const int64_t part = std::min<int64_t>(attn_bwd_part_elems(B, S, sh.n_heads, sh.n_kv_heads, sh.head_dim),
                                                int64_t(ws.tA_bytes / 4));
         AttnBwdArgs a{ws.qkv, nqkv, ws.oa[ob], ws.dout, nq, ws.lsea[ob], ws.dsum, ws.do16, ws.amax, ws.dqkv, nqkv,
-                      B, S, sh.n_heads, sh.n_kv_heads, sh.head_dim, ws.qkv32, nqkv, ws.ovf,
+                      B, S, sh.n_heads, sh.n_kv_heads, sh.head_dim, nullptr, 0, ws.ovf,
                       reinterpret_cast<float*>(ws.tA), part, 0};
+        a.rope_tab = ws.rope_tab;
         // the stored-dS form of dQ where the shape takes it (the region after
         // the partials; the workspace was sized for the largest batch x seq)
         const int64_t dsb = attn_ds_bytes(B, S, sh.n_heads);
@@ -1226,10 +1226,6 @@ hipError_t Ctx::bwd_layer(const LayerView& w, const LayerView& g, const uint16_t
             a.ds_ld = (int64_t(S) + 127) / 128 * 128;
         }
         return attn_bwd(a, s);
-    }));
-    HIPR(site(S_ROPE_BWD, [&] {
-        return rope_f32_to_bf16(ws.qkv32, nqkv, ws.dqkv, nqkv, ws.rope_tab, T, S, sh.n_heads + sh.n_kv_heads,
-                                sh.head_dim, -1, s);
     }));
     HIPR(site(S_GEMM_QKV_DX, [&] { return gemm_nn_t(ws.dqkv, nqkv, w.wqkv, d, ws.dn, d, T, d, nqkv); }));
     HIPR(site(S_GEMM_QKV_DW, [&] { return gemm_tn_t(ws.dqkv, nqkv, ws.n1, d, g.wqkv, d, nqkv, d, T); }));

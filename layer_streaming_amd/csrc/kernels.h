@@ -157,6 +157,11 @@ struct AttnBwdArgs {
     // recomputing the scores and dP.  nullptr: dQ recomputes them.
     uint16_t* ds = nullptr;
     int64_t ds_ld = 0;
+    // Optional: the RoPE table (cos, sin) [S x hd/2].  Set, dQ and dK are
+    // rotated by -theta where they are finished (the dQ kernel, the dK/dV
+    // kernel or the split reduction) and written to dqkv in bf16, rounded
+    // once; dqk32 is not used.
+    const float2* rope_tab = nullptr;
 };
 // Query-head splits the dK/dV pass takes for a shape: automatic (req 0:
 // enough blocks for two per CU, at most Hq/Hkv) or at most req, reduced to

@@ -751,6 +751,64 @@ def _attention_case(B, S, Hq, Hkv, hd, qk_std, f32_out, do_std=1.0, splits=0, dq
         assert np.all(g[:, :, :Hq + Hkv] == 0)
 
 
+@pytest.mark.parametrize("B,S,Hq,Hkv,hd,dq_form,splits", [(2, 300, 8, 2, 128, 1, 1), (2, 300, 8, 2, 128, 2, 3),
+                                                          (1, 1024, 28, 4, 128, 2, 0), (3, 77, 4, 2, 64, 1, 2),
+                                                          (3, 77, 4, 2, 64, 2, 1)])
+def test_attention_bwd_rope_fused(B, S, Hq, Hkv, hd, dq_form, splits):
+    """The RoPE backward folded into the attention backward (the step's form):
+    dQ and dK rotated by -theta where they are finished (dQ kernel; dK/dV
+    kernel, or the reduction of a head-split pass) and rounded to bf16 once.
+    Against the oracle's attention backward followed by its RoPE backward, and
+    against the unfused path (fp32 dQ, dK, then the rotation kernel) to within
+    one bf16 rounding; dV unchanged bit for bit."""
+    log(f"attention bwd with RoPE bwd B={B} S={S} Hq={Hq} Hkv={Hkv} hd={hd} dq_form={dq_form} splits={splits}")
+    T = B * S
+    ld = (Hq + 2 * Hkv) * hd
+    nq, nr = Hq * hd, (Hq + Hkv) * hd
+    qkv, d_qkv, _ = attn_inputs(RNG, T, Hq, Hkv, hd, 1.0)
+    dout = synth.bf16_exact_normal(RNG, (T, nq))
+    d_do = dev_bits(dout)
+    d_o = dev_zeros_bits((T, nq))
+    lse = torch.zeros(B * Hq * S, dtype=torch.float32, device="cuda")
+    work = torch.zeros(int(mt.lib.mt_k_attn_bwd_work_bytes(B, S, Hq, Hkv, hd)), dtype=torch.uint8, device="cuda")
+    ovf = torch.zeros(4, dtype=torch.int32, device="cuda")
+    tab = torch.zeros(S * hd, dtype=torch.float32, device="cuda")
+    s = _stream()
+    mt.check(mt.lib.mt_k_attn_fwd(d_qkv.data_ptr(), ld, d_o.data_ptr(), nq, lse.data_ptr(), B, S, Hq, Hkv, hd,
+                                  ovf.data_ptr(), s))
+    # unfused: fp32 dQ and dK, then both rotated by the rotation kernel
+    g32 = torch.zeros((T, nr), dtype=torch.float32, device="cuda")
+    g_un = dev_zeros_bits((T, ld))
+    mt.check(mt.lib.mt_k_attn_bwd(d_qkv.data_ptr(), ld, d_o.data_ptr(), d_do.data_ptr(), nq, lse.data_ptr(),
+                                  work.data_ptr(), g_un.data_ptr(), ld, B, S, Hq, Hkv, hd, g32.data_ptr(), nr, splits,
+                                  dq_form, ovf.data_ptr(), s))
+    rot_un = dev_zeros_bits((T, nr))
+    mt.check(mt.lib.mt_k_rope_f32_bf16(g32.data_ptr(), nr, rot_un.data_ptr(), nr, tab.data_ptr(), T, S, Hq + Hkv, hd,
+                                       10000.0, -1, s))
+    # fused
+    g_fu = dev_zeros_bits((T, ld))
+    mt.check(mt.lib.mt_k_attn_bwd_rope(d_qkv.data_ptr(), ld, d_o.data_ptr(), d_do.data_ptr(), nq, lse.data_ptr(),
+                                       work.data_ptr(), g_fu.data_ptr(), ld, B, S, Hq, Hkv, hd, None, 0, splits,
+                                       dq_form, ovf.data_ptr(), tab.data_ptr(), 10000.0, s))
+    _sync()
+    assert ovf[0].item() == 0
+    gf = g_fu.cpu().numpy()
+    assert np.array_equal(gf[:, nr:], g_un.cpu().numpy()[:, nr:]), "dV changed"
+    got = widen(gf[:, :nr].view(np.uint16))
+    unf = widen(rot_un.cpu().numpy().view(np.uint16))
+    # within one bf16 rounding of each other: the same fp32 rotation up to the
+    # contraction of its products into FMAs (a few fp32 ulps of the row's
+    # largest terms), then rounded once
+    row_max = np.max(np.abs(unf), axis=1, keepdims=True)
+    assert np.all(np.abs(got - unf) <= np.maximum(np.abs(unf), np.abs(got)) * 2.0 ** -7 + row_max * 2.0 ** -20)
+    log(f"  fused vs unfused: {np.mean(got != unf):.2e} of dQ, dK elements differ")
+    x = qkv.astype(np.float64).reshape(B, S, Hq + 2 * Hkv, hd)
+    q, k, v = x[:, :, :Hq], x[:, :, Hq:Hq + Hkv], x[:, :, Hq + Hkv:]
+    dq, dk, _ = block.attention_bwd(dout.astype(np.float64).reshape(B, S, Hq, hd), q, k, v)
+    assert_close(got[:, :nq], block.rope_bwd(dq, 10000.0).reshape(T, nq), "dq rotated (bf16)", tol=5e-3)
+    assert_close(got[:, nq:], block.rope_bwd(dk, 10000.0).reshape(T, nr - nq), "dk rotated (bf16)", tol=5e-3)
+
+
 @pytest.mark.parametrize("hd", [64, 128])
 def test_rope_f32_to_bf16_backward(hd):
     """The rotation by -theta of fp32 gradients, rounded to bf16 once."""
