@@ -241,7 +241,6 @@ def attention_probe(torch, mt, cfg, S, B=1, dq_form=0):
     lse = torch.zeros(Hq * T, device="cuda")
     work = torch.zeros(int(mt.lib.mt_k_attn_bwd_work_bytes(B, S, Hq, Hkv, hd)), dtype=torch.uint8, device="cuda")
     dqkv = torch.zeros(T, ld, dtype=torch.int16, device="cuda")
-    dqk32 = torch.zeros(T, ld, dtype=torch.float32, device="cuda")
     tab = torch.zeros(S * hd, dtype=torch.float32, device="cuda")
     base = [10000.0]   # the first call computes the RoPE table, later ones reuse it
     st = torch.cuda.current_stream()
@@ -251,10 +250,14 @@ def attention_probe(torch, mt, cfg, S, B=1, dq_form=0):
         mt.check(mt.lib.mt_k_attn_fwd(qkv.data_ptr(), ld, o.data_ptr(), nq, lse.data_ptr(), B, S, Hq, Hkv, hd, None, s),
                  "attn_fwd")
 
-    def bwd():  # as the step runs it: dQ rotated back in the dQ kernel (bf16), dK in fp32
+    def bwd():
+        # as the step runs it: dQ and dK rotated back where they are finished
+        # (bf16 out), and, after the first (untimed) call, the maxima of |dO|
+        # and |v| already in the scratch, as the step's O dX product and
+        # rotation leave them (no maxima pass)
         mt.check(mt.lib.mt_k_attn_bwd_rope(qkv.data_ptr(), ld, o.data_ptr(), do.data_ptr(), nq, lse.data_ptr(),
-                                           work.data_ptr(), dqkv.data_ptr(), ld, B, S, Hq, Hkv, hd, dqk32.data_ptr(),
-                                           ld, 0, dq_form, None, tab.data_ptr(), base[0], s),
+                                           work.data_ptr(), dqkv.data_ptr(), ld, B, S, Hq, Hkv, hd, None, 0, 0,
+                                           dq_form, None, tab.data_ptr(), base[0], 0 if base[0] else 1, s),
                  "attn_bwd")
         base[0] = 0.0
     fl = 4.0 * B * Hq * hd * S * (S + 1) / 2

@@ -104,6 +104,20 @@ int mt_k_rope(void* qkv, int64_t ld, void* table, int32_t T, int32_t S, int32_t 
 int mt_k_qkv_rope_cvt(const void* in, int64_t ldin, void* out, int64_t ldout, void* out_bf16, int64_t ld_bf16,
                       void* table, int32_t T, int32_t S, int32_t n_rot_heads, int32_t n_heads, int32_t hd, float base,
                       void* fp16_ovf, void* stream);
+/* The producers' side of the attention backward's scale 2^k (the form the
+ * step runs, so that the backward needs no pass of its own over dO and v):
+ * mt_k_gemm_amax is mt_k_gemm with epilogue 0 (bf16 out) that also adds the
+ * maximum of the stored |C| values to the partial maxima of |dO| in `amax`
+ * (words 64 i, i < 16, float bit patterns, atomic max); it takes only shapes
+ * the direct form runs (MT_E_INVAL otherwise) and never splits.
+ * mt_k_qkv_rope_cvt_vmax is mt_k_qkv_rope_cvt that adds max |v| of the fp16
+ * heads past n_rot_heads to the partial maxima of |v| (words 64 (16 + i)).
+ * amax: 8192 bytes, 256-byte aligned, zeroed by the caller. */
+int mt_k_gemm_amax(int32_t layout, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                   int32_t M, int32_t N, int32_t K, void* amax, void* stream);
+int mt_k_qkv_rope_cvt_vmax(const void* in, int64_t ldin, void* out, int64_t ldout, void* table, int32_t T, int32_t S,
+                           int32_t n_rot_heads, int32_t n_heads, int32_t hd, float base, void* fp16_ovf, void* amax,
+                           void* stream);
 /* y[i] = fp16(x[i]) for bf16 x, n a multiple of 8. */
 int mt_k_bf16_to_f16(const void* x, void* y, int64_t n, void* fp16_ovf, void* stream);
 
@@ -154,11 +168,14 @@ int mt_k_attn_bwd(const void* qkv, int64_t ld, const void* o, const void* dout, 
  * not written (may be NULL).  The rotation uses mt_k_rope's angles
  * (positions restart every S tokens), its table ([S x hd/2] float2) computed
  * into `table` for base > 0, or taken as a previous call left it for
- * base = 0. */
+ * base = 0.  amax_ready != 0: the maxima words in `work` already hold the
+ * maxima of this dO and v (left by a previous call on the same inputs), so
+ * the maxima pass is skipped, as in the step, where the O dX product and the
+ * recompute's rotation add them while they write dO and v. */
 int mt_k_attn_bwd_rope(const void* qkv, int64_t ld, const void* o, const void* dout, int64_t ldo, const void* lse,
                        void* work, void* dqkv, int64_t ldd, int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t hd,
                        void* dqk32, int64_t ld32, int32_t head_splits, int32_t dq_form, void* fp16_ovf, void* table,
-                       float base, void* stream);
+                       float base, int32_t amax_ready, void* stream);
 /* Rotary embedding of the first n_rot_heads heads of fp32 in [T x ldin]
  * (same angles and table as mt_k_rope; dir -1 rotates by -theta, the
  * backward), written as bf16 to out [T x ldout] with one rounding. */

@@ -100,6 +100,16 @@ int mt_k_gemm_split_plan(int64_t M, int64_t N, int64_t K, int64_t ws_bytes, int3
     return MT_OK;
 }
 
+int mt_k_gemm_amax(int32_t layout, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                   int32_t M, int32_t N, int32_t K, void* amax, void* stream) {
+    if (layout < 0 || layout > 2) MT_FAIL(MT_E_INVAL, "bad layout");
+    mt::GemmArgs a{A, lda, B, ldb, C, ldc, nullptr, 0, nullptr, 0, M, N, K};
+    a.amax = static_cast<uint32_t*>(amax);
+    const hipError_t e = mt::gemm(mt::GemmLayout(layout), mt::EPI_BF16_AMAX, a, S_(stream));
+    if (e == hipErrorNotSupported) MT_FAIL(MT_E_INVAL, "gemm_amax: the direct form does not take this shape");
+    return kst(e, "gemm_amax");
+}
+
 int mt_k_rmsnorm_fwd(const void* x, int32_t x_f32, const void* gamma, void* n, void* n_f16, void* rstd, int32_t T,
                      int32_t d, float eps, void* fp16_ovf, void* stream) {
     return kst(mt::rmsnorm_fwd(x, x_f32 != 0, U16(gamma), U16(n), n_f16 ? U16(n_f16) : nullptr, F32(rstd), T, d, eps,
@@ -133,6 +143,19 @@ int mt_k_rope(void* qkv, int64_t ld, void* table, int32_t T, int32_t S, int32_t 
     if (e != hipSuccess) return kst(e, "rope_table");
     return kst(mt::rope_apply(U16(qkv), ld, static_cast<float2*>(table), T, S, n_rot_heads, hd, dir, S_(stream)),
                "rope_apply");
+}
+
+int mt_k_qkv_rope_cvt_vmax(const void* in, int64_t ldin, void* out, int64_t ldout, void* table, int32_t T, int32_t S,
+                           int32_t n_rot_heads, int32_t n_heads, int32_t hd, float base, void* fp16_ovf, void* amax,
+                           void* stream) {
+    if (!amax || (reinterpret_cast<uintptr_t>(amax) & 255)) MT_FAIL(MT_E_INVAL, "qkv_rope_cvt_vmax: bad amax");
+    if (S <= 0 || (hd & 15)) MT_FAIL(MT_E_INVAL, "qkv_rope_cvt_vmax: bad shape");
+    hipError_t e = mt::rope_table(static_cast<float2*>(table), S, hd, base, S_(stream));
+    if (e != hipSuccess) return kst(e, "rope_table");
+    return kst(mt::qkv_rope_cvt(F32(in), ldin, U16(out), ldout, nullptr, 0, static_cast<float2*>(table), T, S,
+                                n_rot_heads, n_heads, hd, S_(stream), static_cast<uint32_t*>(fp16_ovf),
+                                static_cast<uint32_t*>(amax)),
+               "qkv_rope_cvt_vmax");
 }
 
 int mt_k_qkv_rope_cvt(const void* in, int64_t ldin, void* out, int64_t ldout, void* out_bf16, int64_t ld_bf16,
@@ -193,7 +216,7 @@ int mt_k_attn_bwd(const void* qkv, int64_t ld, const void* o, const void* dout, 
 int mt_k_attn_bwd_rope(const void* qkv, int64_t ld, const void* o, const void* dout, int64_t ldo, const void* lse,
                        void* work, void* dqkv, int64_t ldd, int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t hd,
                        void* dqk32, int64_t ld32, int32_t head_splits, int32_t dq_form, void* fp16_ovf, void* table,
-                       float base, void* stream) {
+                       float base, int32_t amax_ready, void* stream) {
     if (!table || (reinterpret_cast<uintptr_t>(table) & 15)) MT_FAIL(MT_E_INVAL, "attn_bwd_rope: bad table");
     if (!work || (reinterpret_cast<uintptr_t>(work) & 255)) MT_FAIL(MT_E_INVAL, "attn_bwd: work must be 256-byte aligned");
     if (head_splits < 0) MT_FAIL(MT_E_INVAL, "attn_bwd: head_splits must be >= 0");
@@ -211,6 +234,7 @@ int mt_k_attn_bwd_rope(const void* qkv, int64_t ld, const void* o, const void* d
                       B, S, Hq, Hkv, hd, F32(dqk32), ld32, static_cast<uint32_t*>(fp16_ovf)};
     a.splits = head_splits;
     a.rope_tab = static_cast<const float2*>(table);
+    a.amax_ready = amax_ready != 0;
     mt::attn_bwd_carve(work, B, S, Hq, Hkv, hd, a, dq_form != 1);
     return kst(mt::attn_bwd(a, S_(stream)), "attn_bwd_rope");
 }

@@ -353,7 +353,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_k(AttnArgs a, int n_qt, int q
 // atomics on one word, or on words of one line, serialise (about 11 ns each
 // measured: 20 us for 1152 blocks).  The reads here are uniform, so they are
 // scalar loads.
-constexpr int AMAX_W = 16, AMAX_LINE = 64;  // partial maxima per quantity; words per line
+constexpr int AMAX_W = ATTN_AMAX_PARTS, AMAX_LINE = ATTN_AMAX_LINE;  // partial maxima per quantity; words per line
 constexpr int AMAX_U = 8;                    // 16-byte loads in flight per lane of the maxima kernel
 static_assert(2 * AMAX_W * AMAX_LINE * 4 == ATTN_AMAX_BYTES, "maxima scratch size");
 __device__ __forceinline__ float grad_scale(const uint32_t* amax, int hd) {
@@ -1249,14 +1249,16 @@ hipError_t attn_bwd(const AttnBwdArgs& a, hipStream_t s) {
     const int64_t ck_do = T * a.Hq * a.hd / 8, ck_v = T * a.Hkv * a.hd / 8, per_block = 256 * AMAX_U;
     const int nb_v = int(std::min<int64_t>(256, (ck_v + per_block - 1) / per_block));
     const int nb_do = int(std::min<int64_t>(2048 - nb_v, (ck_do + per_block - 1) / per_block));
-    hipError_t e = fill_zero(a.amax, ATTN_AMAX_BYTES, s);
-    if (e != hipSuccess) return e;
+    if (!a.amax_ready) {
+        const hipError_t e = fill_zero(a.amax, ATTN_AMAX_BYTES, s);
+        if (e != hipSuccess) return e;
+    }
     // stored-dS form: dS must cover every key row and 128-query block
     const bool use_ds = a.ds != nullptr;
     if (use_ds && (a.ds_ld < (int64_t(a.S) + 127) / 128 * 128 || (a.ds_ld & 127))) return hipErrorInvalidValue;
     auto run = [&](auto hd_) {
         constexpr int HD = decltype(hd_)::value;
-        attn_amax_k<HD><<<nb_do + nb_v, 256, 0, s>>>(a, nb_do);
+        if (!a.amax_ready) attn_amax_k<HD><<<nb_do + nb_v, 256, 0, s>>>(a, nb_do);
         attn_prep_k<HD><<<np, 256, 0, s>>>(a);
         if (!use_ds) attn_dq_k<HD><<<gq, 256, 0, s>>>(a, n_qt, n_qt <= 256);
         attn_dkdv_k<HD><<<gk, 512, 0, s>>>(a, n_kt, ns, kt_slow);

@@ -33,7 +33,9 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_k(const TX* __restrict__ x,
                                                      const uint4* __restrict__ gamma,
                                                      uint4* __restrict__ n, uint4* __restrict__ n16,
                                                      float* __restrict__ rstd, int T, int d, float eps,
-                                                     uint32_t* __restrict__ ovf) {
+                                                     uint32_t* __restrict__ ovf, uint4* __restrict__ clear) {
+    if (clear && blockIdx.x == 0)  // words the caller needs zeroed before later kernels of the stream
+        for (int i = threadIdx.x; i < int(ATTN_AMAX_BYTES / 16); i += 256) clear[i] = make_uint4(0, 0, 0, 0);
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= T) return;
@@ -322,8 +324,9 @@ __device__ __forceinline__ uint4 h8_to_bf8(const uint4& v) {
 __global__ void qkv_rope_cvt_k(const float* __restrict__ in, int64_t ldin, uint16_t* __restrict__ out,
                                int64_t ldout, uint16_t* __restrict__ outb, int64_t ldb,
                                const float2* __restrict__ tab, int T, int S, int nrot, int nall, int hd,
-                               uint32_t* __restrict__ ovf) {
+                               uint32_t* __restrict__ ovf, uint32_t* __restrict__ vmax) {
     const int half = hd >> 1, per_head = half >> 3;
+    float vm = 0.f;  // max |v| of this lane's (fp16) values
     const int64_t n_rot_items = int64_t(T) * nrot * per_head;
     const int64_t n_v_items = int64_t(T) * (nall - nrot) * (hd >> 3);
     const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -371,8 +374,26 @@ __global__ void qkv_rope_cvt_k(const float* __restrict__ in, int64_t ldin, uint1
         const uint4 h8 = pack8h_sat(f, nov);
         *reinterpret_cast<uint4*>(out + int64_t(t) * ldout + col) = h8;
         if (outb) *reinterpret_cast<uint4*>(outb + int64_t(t) * ldb + col) = h8_to_bf8(h8);
+        if (vmax) {
+            float g[8];
+            unpack8h(h8, g);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) vm = fmaxf(vm, fabsf(g[k]));
+        }
     }
     count_ovf(ovf, nov);
+    if (vmax) {  // uniform: every thread of the block takes part; one atomic max per block
+        __shared__ float wm[4];
+        vm = wave_max(vm);
+        if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = vm;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const float m = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+            if (m > 0.f)
+                atomicMax(vmax + ATTN_AMAX_V_OFFSET + (blockIdx.x % ATTN_AMAX_PARTS) * ATTN_AMAX_LINE,
+                          __float_as_uint(m));
+        }
+    }
 }
 
 __global__ void bf16_to_f16_k(const uint4* __restrict__ in, uint4* __restrict__ out, int64_t n8,
@@ -642,10 +663,12 @@ inline unsigned blocks(int64_t n, int b) { return unsigned((n + b - 1) / b); }
 }  // namespace
 
 hipError_t rmsnorm_fwd(const void* x, bool x_f32, const uint16_t* gamma, uint16_t* n, uint16_t* n_f16,
-                       float* rstd, int T, int d, float eps, hipStream_t s, uint32_t* ovf) {
+                       float* rstd, int T, int d, float eps, hipStream_t s, uint32_t* ovf, uint32_t* clear_amax) {
     if (T < 0 || d <= 0 || (d & 7) || !al16(x) || !al16(gamma) || !al16(n) || (n_f16 && !al16(n_f16)))
         return hipErrorInvalidValue;
-    if (T == 0) return hipSuccess;
+    if (clear_amax && !al16(clear_amax)) return hipErrorInvalidValue;
+    if (T == 0) return clear_amax ? fill_zero(clear_amax, ATTN_AMAX_BYTES, s) : hipSuccess;
+    uint4* clr = reinterpret_cast<uint4*>(clear_amax);
     const uint4* g = reinterpret_cast<const uint4*>(gamma);
     uint4* nv = reinterpret_cast<uint4*>(n);
     uint4* nh = reinterpret_cast<uint4*>(n_f16);
@@ -655,10 +678,10 @@ hipError_t rmsnorm_fwd(const void* x, bool x_f32, const uint16_t* gamma, uint16_
         constexpr int CPL = decltype(cpl_)::value;
         if (x_f32)
             rmsnorm_fwd_k<float, CPL><<<blocks(T, 4), 256, 0, s>>>(static_cast<const float*>(x), g, nv, nh, rstd, T, d,
-                                                                   eps, ovf);
+                                                                   eps, ovf, clr);
         else
             rmsnorm_fwd_k<uint16_t, CPL><<<blocks(T, 4), 256, 0, s>>>(static_cast<const uint16_t*>(x), g, nv, nh, rstd,
-                                                                      T, d, eps, ovf);
+                                                                      T, d, eps, ovf, clr);
     };
     if (need <= 1) run(std::integral_constant<int, 1>{});
     else if (need <= 2) run(std::integral_constant<int, 2>{});
@@ -682,7 +705,7 @@ hipError_t rope_f32_to_bf16(const float* in, int64_t ldin, uint16_t* out, int64_
 
 hipError_t qkv_rope_cvt(const float* in, int64_t ldin, uint16_t* out, int64_t ldout, uint16_t* outb, int64_t ldb,
                         const float2* tab, int T, int S, int n_rot_heads, int n_heads, int hd, hipStream_t s,
-                        uint32_t* ovf) {
+                        uint32_t* ovf, uint32_t* vmax) {
     if (T < 0 || S <= 0 || n_rot_heads < 0 || n_heads < n_rot_heads || (hd & 15) || (ldin & 3) || (ldout & 7) ||
         ldin < int64_t(n_heads) * hd || ldout < int64_t(n_heads) * hd || !al16(in) || !al16(out))
         return hipErrorInvalidValue;
@@ -690,7 +713,7 @@ hipError_t qkv_rope_cvt(const float* in, int64_t ldin, uint16_t* out, int64_t ld
     if (T == 0) return hipSuccess;
     const int64_t n = int64_t(T) * n_rot_heads * (hd / 16) + int64_t(T) * (n_heads - n_rot_heads) * (hd / 8);
     qkv_rope_cvt_k<<<blocks(n, 256), 256, 0, s>>>(in, ldin, out, ldout, outb, ldb, tab, T, S, n_rot_heads, n_heads,
-                                                   hd, ovf);
+                                                   hd, ovf, vmax);
     return hipGetLastError();
 }
 

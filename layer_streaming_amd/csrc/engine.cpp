@@ -1142,17 +1142,23 @@ hipError_t Ctx::fwd_layer(const LayerView& w, const uint16_t* x, uint16_t* y, in
     // products run on the fp16 MFMA and o is fp16, and so are the operands of
     // the O product (Wo converted like Wqkv).  Every fp16 value is range
     // guarded (saturated and counted in ws.ovf).
+    // In the recompute (need_y false) this first kernel also clears the
+    // attention backward's maxima words: the rotation below adds max |v| to
+    // them and the backward's O dX product max |dO|.
     HIPR(site(S_RMS1_FWD, [&] {
-        return rmsnorm_fwd(x, false, w.g1, ws.n1, ws.n1h, ws.rstd1, T, d, sh.rms_eps, s, ws.ovf);
+        return rmsnorm_fwd(x, false, w.g1, ws.n1, ws.n1h, ws.rstd1, T, d, sh.rms_eps, s, ws.ovf,
+                           need_y ? nullptr : ws.amax);
     }));
     HIPR(site(S_GEMM_QKV, [&] {
         HIPR(bf16_to_f16(w.wqkv, ws.w16, int64_t(nqkv) * d, s, ws.ovf));
         GemmArgs a{ws.n1h, d, ws.w16, d, ws.qkv32, nqkv, nullptr, 0, nullptr, 0, T, nqkv, d};
         return gemm(GEMM_NT, EPI_F32_F16IN, split_ws(a, ws), s);
     }));
+    // In the recompute the rotation also takes max |v| for the attention
+    // backward's scale.
     HIPR(site(S_ROPE_FWD, [&] {
         return qkv_rope_cvt(ws.qkv32, nqkv, ws.qkv, nqkv, nullptr, 0, ws.rope_tab, T, S, sh.n_heads + sh.n_kv_heads,
-                            sh.n_heads + 2 * sh.n_kv_heads, sh.head_dim, s, ws.ovf);
+                            sh.n_heads + 2 * sh.n_kv_heads, sh.head_dim, s, ws.ovf, need_y ? nullptr : ws.amax);
     }));
     if (!attn_restored) {
         HIPR(site(S_ATTN_FWD, [&] {
@@ -1204,7 +1210,19 @@ hipError_t Ctx::bwd_layer(const LayerView& w, const LayerView& g, const uint16_t
         return rmsnorm_bwd(ws.dn, ws.h1, true, w.g2, ws.rstd2, dy, ws.dh1, g.g2, ws.partial, T, d, s);
     }));
     // attention
-    HIPR(site(S_GEMM_O_DX, [&] { return gemm_nn_t(ws.dh1, d, w.wo, nq, ws.dout, nq, T, nq, d); }));
+    // dO = dh1 Wo, with max |dO| added to the maxima words where the direct
+    // form runs it; else the attention backward takes both maxima itself.
+    bool amax_ready = false;
+    HIPR(site(S_GEMM_O_DX, [&] {
+        GemmArgs a{ws.dh1, d, w.wo, nq, ws.dout, nq, nullptr, 0, nullptr, 0, T, nq, d};
+        a.amax = ws.amax;
+        const hipError_t e = gemm_direct_checked(GEMM_NN, EPI_BF16_AMAX, a, st_c);
+        if (e != hipErrorNotSupported) {
+            amax_ready = e == hipSuccess;
+            return e;
+        }
+        return gemm_nn_t(ws.dh1, d, w.wo, nq, ws.dout, nq, T, nq, d);
+    }));
     // o is fp16: rounded to bf16 for the bf16 product
     HIPR(site(S_GEMM_O_DW, [&] { return gemm_tn_t(ws.dh1, d, ws.oa[ob], nq, g.wo, nq, d, nq, T, true); }));
     // The attention backward on the fp16 operands of the recomputed forward:
@@ -1217,6 +1235,7 @@ hipError_t Ctx::bwd_layer(const LayerView& w, const LayerView& g, const uint16_t
                       B, S, sh.n_heads, sh.n_kv_heads, sh.head_dim, nullptr, 0, ws.ovf,
                       reinterpret_cast<float*>(ws.tA), part, 0};
         a.rope_tab = ws.rope_tab;
+        a.amax_ready = amax_ready;
         // the stored-dS form of dQ where the shape takes it (the region after
         // the partials; the workspace was sized for the largest batch x seq)
         const int64_t dsb = attn_ds_bytes(B, S, sh.n_heads);

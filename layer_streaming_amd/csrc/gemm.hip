@@ -315,7 +315,8 @@ static hipError_t gemm_check(GemmLayout lay, GemmEpi epi, const GemmArgs& a) {
         return hipErrorInvalidValue;
     if (epi == EPI_BF16_ACCF32 && (!a.Cacc || a.ldacc < a.N)) return hipErrorInvalidValue;
     if ((epi == EPI_F32_F16IN || epi == EPI_F32_F16IN_RESID) && lay != GEMM_NT) return hipErrorInvalidValue;
-    if (int(epi) < 0 || int(epi) > int(EPI_F32_F16IN_RESID)) return hipErrorInvalidValue;
+    if (int(epi) < 0 || int(epi) > int(EPI_BF16_AMAX)) return hipErrorInvalidValue;
+    if (epi == EPI_BF16_AMAX && (!a.amax || (reinterpret_cast<uintptr_t>(a.amax) & 255))) return hipErrorInvalidValue;
     if (a.b_f16 && (lay != GEMM_TN || epi != EPI_BF16)) return hipErrorInvalidValue;
     return hipSuccess;
 }
@@ -333,6 +334,7 @@ hipError_t gemm(GemmLayout lay, GemmEpi epi, const GemmArgs& a, hipStream_t s) {
         if (e != hipErrorNotSupported) return e;
     }
     if (a.b_f16) return hipErrorNotSupported;  // only the direct form converts B
+    if (epi == EPI_BF16_AMAX) return hipErrorNotSupported;  // only the direct form takes the maxima
     switch (lay) {
         case GEMM_NT: return launch_layout<true, true>(epi, a, s);
         case GEMM_NN: return launch_layout<true, false>(epi, a, s);

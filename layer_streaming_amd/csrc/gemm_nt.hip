@@ -286,6 +286,8 @@ __device__ __forceinline__ void staged_store(const GemmArgs& p, const f32x16_t (
     constexpr int P = (TM * TN * 4 + CAP - 1) / CAP;   // passes
     constexpr int FMP = FM / P, RP = FMP * 32, CPR = TN / 4;
     static_assert(FM % P == 0 && RP * CPR * 16 <= CAP && CPR >= 16 && 64 % CPR == 0, "staging layout");
+    static_assert(EPI != EPI_BF16_AMAX || MT_NT_ST8, "the maxima ride on the 8-column bf16 stores");
+    float amx = 0.f;  // EPI_BF16_AMAX: max |stored value| of this lane
     static_for<0, P>([&](auto pass_) {
         constexpr int pass = decltype(pass_)::value;
 #pragma unroll
@@ -300,7 +302,7 @@ __device__ __forceinline__ void staged_store(const GemmArgs& p, const f32x16_t (
                     st[r * CPR + (c ^ (r & 15))] = make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
                 }
         }
-        if constexpr (EPI == EPI_BF16 && MT_NT_ST8) {
+        if constexpr ((EPI == EPI_BF16 || EPI == EPI_BF16_AMAX) && MT_NT_ST8) {
             // bf16 out, no epilogue operand: 8 columns (16 bytes) per lane
 #pragma unroll
             for (int it = 0; it < RP * CPR / 128; ++it) {
@@ -310,14 +312,22 @@ __device__ __forceinline__ void staged_store(const GemmArgs& p, const f32x16_t (
                 const float4 w1 = st[r * CPR + ((c + 1) ^ (r & 15))];
                 const int row = row0 + pass * RP + r, col = col0 + c * 4;
                 if (row < p.M && col < p.N) {
+                    const uint4 v = make_uint4(pack2(w0.x, w0.y), pack2(w0.z, w0.w), pack2(w1.x, w1.y),
+                                               pack2(w1.z, w1.w));
                     if (col + 8 <= p.N && (p.ldc & 7) == 0) {
-                        const uint4 v = make_uint4(pack2(w0.x, w0.y), pack2(w0.z, w0.w), pack2(w1.x, w1.y),
-                                                   pack2(w1.z, w1.w));
                         *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.C) + int64_t(row) * p.ldc + col) = v;
                     } else {
                         const float v0[4] = {w0.x, w0.y, w0.z, w0.w}, v1[4] = {w1.x, w1.y, w1.z, w1.w};
-                        store4<EPI>(p, row, col, v0);
-                        if (col + 4 < p.N) store4<EPI>(p, row, col + 4, v1);
+                        store4<EPI_BF16>(p, row, col, v0);
+                        if (col + 4 < p.N) store4<EPI_BF16>(p, row, col + 4, v1);
+                    }
+                    if constexpr (EPI == EPI_BF16_AMAX) {
+                        // max |value| over the stored (bf16) columns
+                        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                        for (int q = 0; q < 8; ++q)
+                            if (col + q < p.N)
+                                amx = fmaxf(amx, fabsf(q & 1 ? bfhi(wv[q >> 1]) : bflo(wv[q >> 1])));
                     }
                 }
             }
@@ -335,6 +345,17 @@ __device__ __forceinline__ void staged_store(const GemmArgs& p, const f32x16_t (
             }
         }
     });
+    if constexpr (EPI == EPI_BF16_AMAX) {  // one atomic max per block into its partial maximum
+        __shared__ float wm[16];
+        amx = wave_max(amx);
+        if (lane == 0) wm[threadIdx.x >> 6] = amx;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            float m = 0.f;
+            for (int w = 0; w < int(blockDim.x >> 6); ++w) m = fmaxf(m, wm[w]);
+            if (m > 0.f) atomicMax(p.amax + (blockIdx.x % ATTN_AMAX_PARTS) * ATTN_AMAX_LINE, __float_as_uint(m));
+        }
+    }
 }
 
 template <int BM, int BN, int WM, int WN, int EPI>
@@ -471,6 +492,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_nt_k(GemmArgs p, int tiles_
                                                     n0 + wn * TN);
     }
 #else
+    static_assert(EPI != EPI_BF16_AMAX, "the maxima ride on the staged epilogue");
     const int ml = lane & 31, nq = (lane >> 5) * 4;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -891,8 +913,10 @@ hipError_t launch(GemmEpi epi, const GemmArgs& a, hipStream_t s) {
     const dim3 block(WM * WN * 64);
     GemmSplit sp{tm * tn, 1, (a.K + 63) / 64};
     if constexpr (K64 && BM == 256 && BN == 256) {
-        const hipError_t e = split_for(a, tm, tn, sp);
-        if (e != hipSuccess) return e;
+        if (epi != EPI_BF16_AMAX) {  // the maxima are taken in the whole-tile epilogue only
+            const hipError_t e = split_for(a, tm, tn, sp);
+            if (e != hipSuccess) return e;
+        }
     }
     const dim3 grid = K64 ? split_grid(tm, tn, sp) : dim3(tm * tn);
     switch (epi) {
@@ -932,6 +956,10 @@ hipError_t launch(GemmEpi epi, const GemmArgs& a, hipStream_t s) {
             if constexpr (K64) gemm_nt64_k<BM, BN, WM, WN, EPI_F32_F16IN_RESID><<<grid, block, 0, s>>>(a, tm, tn, sp);
             else gemm_nt_k<BM, BN, WM, WN, EPI_F32_F16IN_RESID><<<grid, block, 0, s>>>(a, tm, tn);
             break;
+        case EPI_BF16_AMAX:
+            if constexpr (K64) gemm_nt64_k<BM, BN, WM, WN, EPI_BF16_AMAX><<<grid, block, 0, s>>>(a, tm, tn, sp);
+            else gemm_nt_k<BM, BN, WM, WN, EPI_BF16_AMAX><<<grid, block, 0, s>>>(a, tm, tn);
+            break;
         default: return hipErrorInvalidValue;
     }
     const hipError_t e = hipGetLastError();
@@ -947,10 +975,10 @@ hipError_t launch_kmajor(GemmEpi epi, const GemmArgs& a, hipStream_t s) {
     const int tm = (a.M + 255) / 256, tn = (a.N + 255) / 256;
     const dim3 block(WM * WN * 64);
     if (a.b_f16 && !(TA && TB && epi == EPI_BF16)) return hipErrorNotSupported;
-    if (epi != EPI_BF16 && epi != EPI_F32 && epi != EPI_F32_ACC && epi != EPI_BF16_ACCF32)
+    if (epi != EPI_BF16 && epi != EPI_F32 && epi != EPI_F32_ACC && epi != EPI_BF16_ACCF32 && epi != EPI_BF16_AMAX)
         return hipErrorNotSupported;
-    GemmSplit sp;
-    {
+    GemmSplit sp{tm * tn, 1, (a.K + 63) / 64};
+    if (epi != EPI_BF16_AMAX) {  // the maxima are taken in the whole-tile epilogue only
         const hipError_t e = split_for(a, tm, tn, sp);
         if (e != hipSuccess) return e;
     }
@@ -964,6 +992,9 @@ hipError_t launch_kmajor(GemmEpi epi, const GemmArgs& a, hipStream_t s) {
             case EPI_F32: gemm_nt64_k<256, 256, WM, WN, EPI_F32, TA, TB><<<grid, block, 0, s>>>(a, tm, tn, sp); break;
             case EPI_F32_ACC:
                 gemm_nt64_k<256, 256, WM, WN, EPI_F32_ACC, TA, TB><<<grid, block, 0, s>>>(a, tm, tn, sp);
+                break;
+            case EPI_BF16_AMAX:
+                gemm_nt64_k<256, 256, WM, WN, EPI_BF16_AMAX, TA, TB><<<grid, block, 0, s>>>(a, tm, tn, sp);
                 break;
             default:
                 gemm_nt64_k<256, 256, WM, WN, EPI_BF16_ACCF32, TA, TB><<<grid, block, 0, s>>>(a, tm, tn, sp);

@@ -25,6 +25,8 @@ enum GemmEpi {
     EPI_BF16_RESID32 = 6,// C(bf16) = acc + R(f32)
     EPI_F32_F16IN = 7,   // operands fp16 (not bf16), C(f32) = acc; NT layout only
     EPI_F32_F16IN_RESID = 8,  // operands fp16, C(f32) = acc + R(bf16); NT layout only
+    EPI_BF16_AMAX = 9,   // C(bf16) = acc, and max |C| (of the stored bf16 values) into the partial maxima at
+                         // amax (the attention backward's max |dO|); the direct form only, never split
 };
 struct GemmArgs {
     const void* A; int64_t lda;
@@ -40,6 +42,7 @@ struct GemmArgs {
     float* ws = nullptr;
     uint64_t ws_bytes = 0;
     int force_splits = 0;             // > 0: split the tail this many ways (tests); 0: gemm_split_plan decides
+    uint32_t* amax = nullptr;         // EPI_BF16_AMAX: the partial maxima words (ATTN_AMAX_PARTS, one per line)
 };
 // How a direct-form product on 256 x 256 tiles is cut: the first n_full tiles
 // run whole; each later tile runs as `splits` blocks over consecutive ranges
@@ -68,8 +71,12 @@ hipError_t gemm_direct_checked(GemmLayout lay, GemmEpi epi, const GemmArgs& a, h
 // n and gamma bf16; n_f16 (may be null) receives the same values in fp16.
 // ovf (may be null): counter of fp16 values out of range (saturated to
 // +-65504), the range guard of every fp16 operand the kernels write.
+// clear_amax (may be null, 16-byte aligned): ATTN_AMAX_BYTES zeroed by the
+// kernel's first block (the recompute's first kernel clears the attention
+// backward's maxima words before its producers add to them).
 hipError_t rmsnorm_fwd(const void* x, bool x_f32, const uint16_t* gamma, uint16_t* n, uint16_t* n_f16,
-                       float* rstd, int T, int d, float eps, hipStream_t s, uint32_t* ovf = nullptr);
+                       float* rstd, int T, int d, float eps, hipStream_t s, uint32_t* ovf = nullptr,
+                       uint32_t* clear_amax = nullptr);
 // dx = resid + rstd*(g - nh*mean(g*nh)), g = dn*gamma, nh = x*rstd (resid may be null);
 // dgamma = sum_t dn*nh written as bf16 (two-stage, fixed order).  `partial` is
 // fp32 scratch of rmsnorm_bwd_partial_elems(T, d) elements.
@@ -94,17 +101,21 @@ hipError_t rope_table(float2* tab, int S, int hd, float base, hipStream_t s);
 hipError_t rope_apply(uint16_t* qkv, int64_t ld, const float2* tab, int T, int S, int n_rot_heads,
                       int hd, int dir, hipStream_t s);
 // The same rotation of the first n_rot_heads heads of fp32 in [T x ldin],
-// written as bf16 to out [T x ldout] (one rounding): the attention backward's
-// dQ, dK rotated back by -theta (dir = -1).
+// written as bf16 to out [T x ldout] (one rounding), dir = -1 for a gradient
+// rotated back by -theta (the attention backward folds this rotation into
+// its own kernels; this one serves the kernel tests).
 hipError_t rope_f32_to_bf16(const float* in, int64_t ldin, uint16_t* out, int64_t ldout, const float2* tab, int T,
                             int S, int n_rot_heads, int hd, int dir, hipStream_t s);
 // From the fp32 QKV projection in [T x ldin] (n_heads heads of hd): rotate the
 // first n_rot_heads (q and k), and write every head as fp16 (saturated and
 // counted in ovf) into out [T x ldout] (the attention operand buffer); outb
 // (may be null) [T x ldb, ldb >= n_heads*hd] gets the same heads in bf16.
+// vmax (may be null): the partial maxima of |v| (the heads past n_rot_heads,
+// as stored in fp16) are added to it, one atomic max per wave (see
+// ATTN_AMAX_V_OFFSET; the caller zeroes the words).
 hipError_t qkv_rope_cvt(const float* in, int64_t ldin, uint16_t* out, int64_t ldout, uint16_t* outb, int64_t ldb,
                         const float2* tab, int T, int S, int n_rot_heads, int n_heads, int hd, hipStream_t s,
-                        uint32_t* ovf = nullptr);
+                        uint32_t* ovf = nullptr, uint32_t* vmax = nullptr);
 // Elementwise bf16 -> fp16 (n a multiple of 8), saturated and counted in ovf.
 hipError_t bf16_to_f16(const uint16_t* in, uint16_t* out, int64_t n, hipStream_t s, uint32_t* ovf = nullptr);
 
@@ -130,6 +141,11 @@ hipError_t attn_fwd(const AttnArgs& a, hipStream_t s);
 // Bytes of the attention backward's maxima scratch: 16 partial maxima of
 // |dO| and 16 of |v|, each in its own 256-byte line.
 constexpr int64_t ATTN_AMAX_BYTES = 8192;
+constexpr int ATTN_AMAX_PARTS = 16, ATTN_AMAX_LINE = 64;  // partial maxima per quantity; uint32 words per line
+// Where a producer adds to the partial maxima (float bit patterns, atomic
+// max): block b of the producer of dO into word (b % PARTS) * LINE, of v into
+// word (PARTS + b % PARTS) * LINE.
+constexpr int ATTN_AMAX_V_OFFSET = ATTN_AMAX_PARTS * ATTN_AMAX_LINE;
 struct AttnBwdArgs {
     const uint16_t* qkv; int64_t ld;  // fp16 q, k, v as the forward used them
     const uint16_t* o; const uint16_t* dout; int64_t ldo;  // o fp16, dout bf16
@@ -162,6 +178,10 @@ struct AttnBwdArgs {
     // kernel or the split reduction) and written to dqkv in bf16, rounded
     // once; dqk32 is not used.
     const float2* rope_tab = nullptr;
+    // The partial maxima of |dO| and |v| are already in amax, added where dO
+    // and v were written (the O dX product, the recompute's rotation): the
+    // maxima pass is skipped.
+    bool amax_ready = false;
 };
 // Query-head splits the dK/dV pass takes for a shape: automatic (req 0:
 // enough blocks for two per CU, at most Hq/Hkv) or at most req, reduced to

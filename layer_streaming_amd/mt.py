@@ -98,6 +98,10 @@ _SIGS = {
     "mt_k_gemm_split": (C.c_int, [C.c_int32, C.c_int32, _P, C.c_int64, _P, C.c_int64, _P, C.c_int64, _P, C.c_int64,
                                   _P, C.c_int64, C.c_int32, C.c_int32, C.c_int32, _P, C.c_int64, C.c_int32, _P]),
     "mt_k_gemm_split_plan": (C.c_int, [C.c_int64, C.c_int64, C.c_int64, C.c_int64, _P, _P, _P]),
+    "mt_k_gemm_amax": (C.c_int, [C.c_int32, _P, C.c_int64, _P, C.c_int64, _P, C.c_int64, C.c_int32, C.c_int32,
+                                 C.c_int32, _P, _P]),
+    "mt_k_qkv_rope_cvt_vmax": (C.c_int, [_P, C.c_int64, _P, C.c_int64, _P, C.c_int32, C.c_int32, C.c_int32,
+                                         C.c_int32, C.c_int32, C.c_float, _P, _P, _P]),
     "mt_k_rmsnorm_fwd": (C.c_int, [_P, C.c_int32, _P, _P, _P, _P, C.c_int32, C.c_int32, C.c_float, _P, _P]),
     "mt_k_rmsnorm_bwd_scratch_elems": (C.c_int64, [C.c_int32, C.c_int32]),
     "mt_k_rmsnorm_bwd": (C.c_int, [_P, _P, C.c_int32, _P, _P, _P, _P, _P, _P, C.c_int32, C.c_int32, _P]),
@@ -114,7 +118,7 @@ _SIGS = {
                                 C.c_int32, C.c_int32, C.c_int32, _P, C.c_int64, C.c_int32, C.c_int32, _P, _P]),
     "mt_k_attn_bwd_rope": (C.c_int, [_P, C.c_int64, _P, _P, C.c_int64, _P, _P, _P, C.c_int64, C.c_int32, C.c_int32,
                                      C.c_int32, C.c_int32, C.c_int32, _P, C.c_int64, C.c_int32, C.c_int32, _P, _P,
-                                     C.c_float, _P]),
+                                     C.c_float, C.c_int32, _P]),
     "mt_k_rope_f32_bf16": (C.c_int, [_P, C.c_int64, _P, C.c_int64, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                      C.c_float, C.c_int32, _P]),
     "mt_k_ce": (C.c_int, [_P, _P, _P, _P, C.c_int32, C.c_int32, C.c_float, _P]),

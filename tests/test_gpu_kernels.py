@@ -443,6 +443,80 @@ def test_gemm_tail_split_refuses_small_scratch():
     assert rc == mt.MT_E_INVAL
 
 
+# The attention backward's scale from its producers (the step's form): the
+# O dX product's epilogue adds max |dO| of the values it stores, the
+# recompute's rotation max |v| of the fp16 v it stores, each into 16 partial
+# maxima (float bit patterns) one 256-byte line apart.
+def _amax_words():
+    return torch.zeros(2048, dtype=torch.int32, device="cuda")
+
+
+def _partial_max(words, first):
+    w = words.cpu().numpy().view(np.uint32)[(16 * first + np.arange(16)) * 64]
+    return float(np.max(w.view(np.float32)))
+
+
+@pytest.mark.parametrize("layout,M,N,K,std", [(1, 4104, 3592, 520, 1.0), (1, 8192, 3584, 3584, 1e-4),
+                                              (0, 4104, 4044, 200, 30.0), (0, 200, 136, 72, 1.0)])
+def test_gemm_amax_epilogue(layout, M, N, K, std):
+    """bf16 output bit-identical to the plain epilogue; max |C| exact (the max
+    over the stored bf16 values, ragged columns included, none past N): NN on
+    the 64-deep form (the O dX shape among them), NT with a last 8-column chunk
+    cut by N and rows not 16-byte aligned (the 4-column stores), NT on the
+    32-deep form of small grids."""
+    log(f"gemm with max |C| layout={layout} M={M} N={N} K={K} std={std}")
+    a_shape = (M, K)
+    b_shape = (N, K) if layout == 0 else (K, N)
+    A = synth.bf16_exact_normal(RNG, a_shape, std=std)
+    B = synth.bf16_exact_normal(RNG, b_shape)
+    dA, dB = dev_bits(A), dev_bits(B)
+    ldc = N + 8
+    C1 = torch.full((M, ldc), 0x7F80, dtype=torch.int16, device="cuda")   # +inf past N: must stay out of the max
+    C0 = dev_zeros_bits((M, ldc))
+    words = _amax_words()
+    s = _stream()
+    mt.check(mt.lib.mt_k_gemm_amax(layout, dA.data_ptr(), K, dB.data_ptr(), b_shape[1], C1.data_ptr(), ldc, M, N, K,
+                                   words.data_ptr(), s), "gemm_amax")
+    mt.check(mt.lib.mt_k_gemm(layout, 0, dA.data_ptr(), K, dB.data_ptr(), b_shape[1], C0.data_ptr(), ldc, None, 0,
+                              None, 0, M, N, K, s), "gemm")
+    _sync()
+    c1 = C1.cpu().numpy()
+    assert np.array_equal(c1[:, :N], C0.cpu().numpy()[:, :N]), "values differ from the plain epilogue"
+    want = float(np.max(np.abs(widen(c1[:, :N].view(np.uint16)))))
+    assert _partial_max(words, 0) == want
+    assert _partial_max(words, 1) == 0.0, "|v| words touched"
+    if layout == 1:  # NN grids below 120 tiles of 256 x 256 are refused (no direct form takes them)
+        assert mt.lib.mt_k_gemm_amax(layout, dA.data_ptr(), K, dB.data_ptr(), b_shape[1], C1.data_ptr(), ldc, 200,
+                                     136, K, words.data_ptr(), s) == mt.MT_E_INVAL
+
+
+@pytest.mark.parametrize("hd,S", [(128, 1024), (64, 100)])
+def test_qkv_rope_cvt_vmax(hd, S):
+    """max |v| over the fp16 v heads the rotation stores, exactly; fp16 output
+    bit-identical to the plain entry."""
+    hq, hkv, B = 4, 2, 3
+    log(f"qkv_rope_cvt with max |v| hd={hd} S={S}")
+    ld = (hq + 2 * hkv) * hd
+    T = B * S
+    x = RNG.standard_normal((T, ld)).astype(np.float32)
+    x[:, (hq + hkv) * hd:] *= 3.0
+    dx = torch.from_numpy(x).cuda()
+    out = dev_zeros_bits((T, ld))
+    out0 = dev_zeros_bits((T, ld))
+    tab = torch.zeros(S * hd, dtype=torch.float32, device="cuda")
+    words = _amax_words()
+    s = _stream()
+    mt.check(mt.lib.mt_k_qkv_rope_cvt_vmax(dx.data_ptr(), ld, out.data_ptr(), ld, tab.data_ptr(), T, S, hq + hkv,
+                                           hq + 2 * hkv, hd, 10000.0, None, words.data_ptr(), s))
+    mt.check(mt.lib.mt_k_qkv_rope_cvt(dx.data_ptr(), ld, out0.data_ptr(), ld, None, 0, tab.data_ptr(), T, S,
+                                      hq + hkv, hq + 2 * hkv, hd, 10000.0, None, s))
+    _sync()
+    assert torch.equal(out, out0)
+    v = out.cpu().numpy().view(np.uint16)[:, (hq + hkv) * hd:].view(np.float16).astype(np.float32)
+    assert _partial_max(words, 1) == float(np.max(np.abs(v)))
+    assert _partial_max(words, 0) == 0.0, "|dO| words touched"
+
+
 # --------------------------------------------------------------- RMSNorm --
 @pytest.mark.parametrize("T,d,x_f32", [(37, 256, 0), (130, 3584, 0), (9, 8192, 0), (1, 64, 0), (130, 3584, 1),
                                        (21, 256, 1)])
@@ -789,8 +863,14 @@ def test_attention_bwd_rope_fused(B, S, Hq, Hkv, hd, dq_form, splits):
     g_fu = dev_zeros_bits((T, ld))
     mt.check(mt.lib.mt_k_attn_bwd_rope(d_qkv.data_ptr(), ld, d_o.data_ptr(), d_do.data_ptr(), nq, lse.data_ptr(),
                                        work.data_ptr(), g_fu.data_ptr(), ld, B, S, Hq, Hkv, hd, None, 0, splits,
-                                       dq_form, ovf.data_ptr(), tab.data_ptr(), 10000.0, s))
+                                       dq_form, ovf.data_ptr(), tab.data_ptr(), 10000.0, 0, s))
+    # again with the maxima left in the scratch by the call before (no maxima pass): bit-identical
+    g_fu2 = dev_zeros_bits((T, ld))
+    mt.check(mt.lib.mt_k_attn_bwd_rope(d_qkv.data_ptr(), ld, d_o.data_ptr(), d_do.data_ptr(), nq, lse.data_ptr(),
+                                       work.data_ptr(), g_fu2.data_ptr(), ld, B, S, Hq, Hkv, hd, None, 0, splits,
+                                       dq_form, ovf.data_ptr(), tab.data_ptr(), 0.0, 1, s))
     _sync()
+    assert torch.equal(g_fu, g_fu2), "maxima taken before: results differ"
     assert ovf[0].item() == 0
     gf = g_fu.cpu().numpy()
     assert np.array_equal(gf[:, nr:], g_un.cpu().numpy()[:, nr:]), "dV changed"
