@@ -128,8 +128,12 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_k(const uint4* __restrict__ d
         const uint4* dnr = dn + int64_t(row) * nv;
         const TX* xr = x + int64_t(row) * d;
         const uint4* rr_ = resid ? resid + int64_t(row) * nv : nullptr;
-        // the residual's loads go out with the others unless the row is wide
-        constexpr bool EARLY_Q = NCL <= 4;
+        // the residual's loads go out with the others up to 7 chunks per lane
+        // (d <= 3584: 209 / 229 VGPRs for bf16 / fp32 x, still two waves per
+        // SIMD; one memory round trip per row instead of two, 52.8 -> 50.9 and
+        // 65.5 -> 60.7 us at T 8192, d 3584); wider rows load it after the
+        // row's reduction, keeping the registers below 256
+        constexpr bool EARLY_Q = NCL <= 7;
         uint4 a[NCL], q[NCL], xv[NCL][2];
 #pragma unroll
         for (int j = 0; j < NCL; ++j) {
