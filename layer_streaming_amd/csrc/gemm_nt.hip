@@ -312,22 +312,24 @@ __device__ __forceinline__ void staged_store(const GemmArgs& p, const f32x16_t (
                 const float4 w1 = st[r * CPR + ((c + 1) ^ (r & 15))];
                 const int row = row0 + pass * RP + r, col = col0 + c * 4;
                 if (row < p.M && col < p.N) {
-                    const uint4 v = make_uint4(pack2(w0.x, w0.y), pack2(w0.z, w0.w), pack2(w1.x, w1.y),
-                                               pack2(w1.z, w1.w));
                     if (col + 8 <= p.N && (p.ldc & 7) == 0) {
+                        const uint4 v = make_uint4(pack2(w0.x, w0.y), pack2(w0.z, w0.w), pack2(w1.x, w1.y),
+                                                   pack2(w1.z, w1.w));
                         *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.C) + int64_t(row) * p.ldc + col) = v;
+                        if constexpr (EPI == EPI_BF16_AMAX) {  // max |value| of the stored bf16 values
+                            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) amx = fmaxf(amx, fmaxf(fabsf(bflo(wv[q])), fabsf(bfhi(wv[q]))));
+                        }
                     } else {
                         const float v0[4] = {w0.x, w0.y, w0.z, w0.w}, v1[4] = {w1.x, w1.y, w1.z, w1.w};
                         store4<EPI_BF16>(p, row, col, v0);
                         if (col + 4 < p.N) store4<EPI_BF16>(p, row, col + 4, v1);
-                    }
-                    if constexpr (EPI == EPI_BF16_AMAX) {
-                        // max |value| over the stored (bf16) columns
-                        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+                        if constexpr (EPI == EPI_BF16_AMAX) {  // the columns stored, rounded as stored
 #pragma unroll
-                        for (int q = 0; q < 8; ++q)
-                            if (col + q < p.N)
-                                amx = fmaxf(amx, fabsf(q & 1 ? bfhi(wv[q >> 1]) : bflo(wv[q >> 1])));
+                            for (int q = 0; q < 8; ++q)
+                                if (col + q < p.N) amx = fmaxf(amx, fabsf(bf2f(f2bf(q < 4 ? v0[q] : v1[q - 4]))));
+                        }
                     }
                 }
             }
