@@ -393,3 +393,15 @@ def test_gemm_tail_split_plan():
     # no scratch, no split; scratch too small for any split, no split
     assert _split_plan(T, d, 2 * F, 0)[1] == 1
     assert _split_plan(T, d, 2 * F, 1 << 20)[1] == 1
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark runs on one GPU: --gpus N > 1 exits with status 2 and a
+    message before anything touches a GPU."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr and r.stdout == ""
