@@ -432,6 +432,44 @@ def test_gemm_tail_split_epilogues():
     assert_close(c16r.cpu().numpy()[:, :N], ref16 + Rv, "C f16 operands + R", tol=1e-5)
 
 
+def test_gemm_tail_split_kmajor_accumulate():
+    """The split k-major forms with the accumulating epilogues the chunked LM
+    head runs: NN with fp32 out then fp32 accumulate (dX over vocabulary
+    chunks), TN with fp32 accumulate and bf16 from an fp32 partial (dE_out)."""
+    s = _stream()
+    M, N, K = 4104, 4360, 1000       # NN: 17 x 18 = 306 tiles, 50 split
+    log(f"gemm tail split NN accumulate M={M} N={N} K={K}")
+    A = synth.bf16_exact_normal(RNG, (M, K))
+    B = synth.bf16_exact_normal(RNG, (K, N))
+    ref = A.astype(np.float64) @ B.astype(np.float64)
+    dA, dB = dev_bits(A), dev_bits(B)
+    ws = torch.empty(50 * 4 * 65536, dtype=torch.float32, device="cuda")
+    c32 = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+    for epi in (2, 3):
+        mt.check(mt.lib.mt_k_gemm_split(1, epi, dA.data_ptr(), K, dB.data_ptr(), N, c32.data_ptr(), N, None, 0, None,
+                                        0, M, N, K, ws.data_ptr(), ws.numel() * 4, 4, s), f"gemm split NN epi {epi}")
+    _sync()
+    assert_close(c32.cpu().numpy(), 2 * ref, "NN C f32 += (split)", tol=1e-5)
+    M2, N2, K2 = 4104, 4040, 997     # TN: 17 x 16 = 272 tiles, 16 split
+    log(f"gemm tail split TN accumulate M={M2} N={N2} K={K2}")
+    A2 = synth.bf16_exact_normal(RNG, (K2, M2))
+    B2 = synth.bf16_exact_normal(RNG, (K2, N2))
+    ref2 = A2.T.astype(np.float64) @ B2.astype(np.float64)
+    dA2, dB2 = dev_bits(A2), dev_bits(B2)
+    acc = torch.zeros((M2, N2), dtype=torch.float32, device="cuda")
+    mt.check(mt.lib.mt_k_gemm_split(2, 2, dA2.data_ptr(), M2, dB2.data_ptr(), N2, acc.data_ptr(), N2, None, 0, None, 0,
+                                    M2, N2, K2, ws.data_ptr(), ws.numel() * 4, 3, s), "gemm split TN f32")
+    mt.check(mt.lib.mt_k_gemm_split(2, 3, dA2.data_ptr(), M2, dB2.data_ptr(), N2, acc.data_ptr(), N2, None, 0, None, 0,
+                                    M2, N2, K2, ws.data_ptr(), ws.numel() * 4, 3, s), "gemm split TN f32 +=")
+    dC = dev_zeros_bits((M2, N2))
+    mt.check(mt.lib.mt_k_gemm_split(2, 4, dA2.data_ptr(), M2, dB2.data_ptr(), N2, dC.data_ptr(), N2, None, 0,
+                                    acc.data_ptr(), N2, M2, N2, K2, ws.data_ptr(), ws.numel() * 4, 3, s),
+             "gemm split TN bf16 from f32")
+    _sync()
+    assert_close(acc.cpu().numpy(), 2 * ref2, "TN C f32 += (split)", tol=1e-5)
+    assert_close(host_f32(dC), 3 * ref2, "TN C bf16 from f32 partial (split)")
+
+
 def test_gemm_tail_split_refuses_small_scratch():
     M, N, K = 3080, 3000, 1000
     dA = dev_zeros_bits((M, K))
